@@ -1,0 +1,223 @@
+"""Plain decoder-only transformer in float64 (test infrastructure only).
+
+The model DEX wraps is an ordinary Llama-style decoder ("Depth Exploration for
+LLM Decoding", Section 2.1 treats it as a stack of L layers; Section 3.4 and
+Appendix C.2 state that every depth is decoded by the same final norm and LM
+head). Per layer l = 1..L, for a token at absolute position p:
+
+    a = RMSNorm(h) * g_attn,   RMSNorm(h) = h / sqrt(mean(h^2) + eps)
+    Q, K, V = a Wq^T, a Wk^T, a Wv^T          (split into heads of size hd)
+    Q, K rotated by RoPE at p: pairs (i, i + hd/2), angle p * base^(-2i/hd)
+    per query head h (kv head h // (n_heads / n_kv_heads)):
+        o_h = softmax(Q_h K^T / sqrt(hd)) V   over keys at positions <= p
+    h = h + o Wo^T
+    f = RMSNorm(h) * g_ffn
+    h = h + (SiLU(f Wg^T) * (f Wu^T)) Wd^T
+
+Depth-l logits: z_l = (RMSNorm(h_l) * g_final) W_head^T.
+
+Storage-dtype weights (bf16 or fp32) are upcast exactly to float64; all
+arithmetic is float64.
+"""
+
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import numpy as np
+
+
+def _f64(t) -> np.ndarray:
+    """torch tensor (any float dtype) or array -> float64 ndarray (exact upcast)."""
+    if hasattr(t, "detach"):
+        import torch
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+@dataclass
+class LayerW:
+    attn_norm: np.ndarray
+    wq: np.ndarray
+    wk: np.ndarray
+    wv: np.ndarray
+    wo: np.ndarray
+    ffn_norm: np.ndarray
+    w_gate: np.ndarray
+    w_up: np.ndarray
+    w_down: np.ndarray
+
+
+class PlainModel:
+    def __init__(self, cfg, weights):
+        """``cfg`` needs n_layers, d_model, n_heads, n_kv_heads, head_dim,
+        d_ffn, vocab, rope_base, eps; ``weights`` is the dict produced by
+        ``synthetic.weights.generate``."""
+        self.L = cfg.n_layers
+        self.d = cfg.d_model
+        self.nq = cfg.n_heads
+        self.nkv = cfg.n_kv_heads
+        self.hd = cfg.head_dim
+        self.V = cfg.vocab
+        self.eps = float(cfg.eps)
+        self.base = float(cfg.rope_base)
+        self.embed = _f64(weights["embed"])
+        self.layers: List[LayerW] = []
+        for lw in weights["layers"]:
+            self.layers.append(LayerW(**{k: _f64(lw[k]) for k in (
+                "attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")}))
+        self.final_norm = _f64(weights["final_norm"])
+        self.head = self.embed if weights["lm_head"] is weights["embed"] else _f64(weights["lm_head"])
+
+    # -- elementary pieces ------------------------------------------------
+    def rmsnorm(self, x: np.ndarray, g: np.ndarray) -> np.ndarray:
+        return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + self.eps) * g
+
+    def rope(self, x: np.ndarray, pos: np.ndarray) -> np.ndarray:
+        """x: [n, heads, hd]; pos: [n] absolute positions."""
+        half = self.hd // 2
+        inv = self.base ** (-2.0 * np.arange(half, dtype=np.float64) / self.hd)
+        ang = pos.astype(np.float64)[:, None] * inv[None, :]          # [n, half]
+        c = np.cos(ang)[:, None, :]
+        s = np.sin(ang)[:, None, :]
+        x1, x2 = x[..., :half], x[..., half:]
+        return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+    def attend(self, q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
+        """One query row. q: [nq, hd]; K, V: [n_keys, nkv, hd] -> [nq * hd]."""
+        rep = self.nq // self.nkv
+        out = np.empty((self.nq, self.hd))
+        for h in range(self.nq):
+            kh = K[:, h // rep, :]
+            vh = V[:, h // rep, :]
+            s = kh @ q[h] / np.sqrt(self.hd)
+            s = s - s.max()
+            p = np.exp(s)
+            p /= p.sum()
+            out[h] = p @ vh
+        return out.reshape(-1)
+
+    def logits(self, h: np.ndarray) -> np.ndarray:
+        """Shared exit head: h [..., d] -> [..., V]."""
+        return self.rmsnorm(h, self.final_norm) @ self.head.T
+
+    # -- forward passes ---------------------------------------------------
+    def prefill(self, tokens: Sequence[int]):
+        """Full causal forward of ``tokens`` at positions 0..n-1.
+
+        Returns (K, V, hiddens): K, V as lists over layers of [n, nkv, hd];
+        hiddens [L+1, n, d] (hiddens[l] = residual stream after l layers).
+        """
+        n = len(tokens)
+        pos = np.arange(n)
+        h = self.embed[np.asarray(tokens, dtype=np.int64)]
+        Ks, Vs, hs = [], [], [h.copy()]
+        for lw in self.layers:
+            a = self.rmsnorm(h, lw.attn_norm)
+            q = self.rope((a @ lw.wq.T).reshape(n, self.nq, self.hd), pos)
+            k = self.rope((a @ lw.wk.T).reshape(n, self.nkv, self.hd), pos)
+            v = (a @ lw.wv.T).reshape(n, self.nkv, self.hd)
+            o = np.stack([self.attend(q[i], k[:i + 1], v[:i + 1]) for i in range(n)]) if n else \
+                np.zeros((0, self.nq * self.hd))
+            h = h + o @ lw.wo.T
+            f = self.rmsnorm(h, lw.ffn_norm)
+            g = f @ lw.w_gate.T
+            h = h + ((g / (1.0 + np.exp(-g))) * (f @ lw.w_up.T)) @ lw.w_down.T
+            Ks.append(k)
+            Vs.append(v)
+            hs.append(h.copy())
+        return Ks, Vs, np.stack(hs)
+
+    def extend(self, tokens: Sequence[int], positions: Sequence[int], past) -> tuple:
+        """Forward independent single-token rows, each with its own past keys.
+
+        ``past(i, l)`` returns (K, V) arrays [n_past, nkv, hd] of the keys row i
+        attends to at layer l (positions < its own). Rows do not see each
+        other. Returns (hiddens [n, L+1, d], K [n, L, nkv, hd], V [n, L, nkv, hd]).
+        """
+        n = len(tokens)
+        pos = np.asarray(positions, dtype=np.int64)
+        h = self.embed[np.asarray(tokens, dtype=np.int64)]
+        hs = [h.copy()]
+        kn = np.empty((n, self.L, self.nkv, self.hd))
+        vn = np.empty((n, self.L, self.nkv, self.hd))
+        for l, lw in enumerate(self.layers):
+            a = self.rmsnorm(h, lw.attn_norm)
+            q = self.rope((a @ lw.wq.T).reshape(n, self.nq, self.hd), pos)
+            k = self.rope((a @ lw.wk.T).reshape(n, self.nkv, self.hd), pos)
+            v = (a @ lw.wv.T).reshape(n, self.nkv, self.hd)
+            kn[:, l], vn[:, l] = k, v
+            o = np.empty((n, self.nq * self.hd))
+            for i in range(n):
+                pk, pv = past(i, l)
+                o[i] = self.attend(q[i], np.concatenate([pk, k[i:i + 1]]),
+                                   np.concatenate([pv, v[i:i + 1]]))
+            h = h + o @ lw.wo.T
+            f = self.rmsnorm(h, lw.ffn_norm)
+            g = f @ lw.w_gate.T
+            h = h + ((g / (1.0 + np.exp(-g))) * (f @ lw.w_up.T)) @ lw.w_down.T
+            hs.append(h.copy())
+        return np.stack(hs, axis=1), kn, vn
+
+
+class SlotEvaluator:
+    """Per-depth logits of the plain model for branch contexts.
+
+    A *slot* is the tuple of tokens that follow the committed KV cache: its
+    first element is the anchor token (at position C, the committed length)
+    and element m sits at position C + m. The slot's candidate predicts
+    position C + len(slot). Results are memoised per slot; every slot's proper
+    prefixes must have been evaluated before it (true for both plain
+    autoregressive decoding and the DEX lattice, where a position child is
+    created only after its parent slot).
+    """
+
+    def __init__(self, model: PlainModel):
+        self.m = model
+
+    def begin(self, prompt: Sequence[int]):
+        """Cache prompt[:-1]; the last prompt token becomes the anchor."""
+        K, V, _ = self.m.prefill(list(prompt[:-1]))
+        self.K = [k for k in K]       # per layer [C, nkv, hd]
+        self.V = [v for v in V]
+        self.C = len(prompt) - 1
+        self.memo = {}                # slot -> (hiddens [L+1, d], K [L,nkv,hd], V)
+
+    def eval_slots(self, slots: Sequence[tuple]):
+        todo = [s for s in dict.fromkeys(slots) if s not in self.memo]
+        if not todo:
+            return
+        for s in todo:
+            for m in range(1, len(s)):
+                assert s[:m] in self.memo, "slot evaluated before its prefix"
+
+        def past(i, l):
+            s = todo[i]
+            ks = [self.K[l]] + [self.memo[s[:m]][1][l][None] for m in range(1, len(s))]
+            vs = [self.V[l]] + [self.memo[s[:m]][2][l][None] for m in range(1, len(s))]
+            return np.concatenate(ks), np.concatenate(vs)
+
+        hs, kn, vn = self.m.extend([s[-1] for s in todo],
+                                   [self.C + len(s) - 1 for s in todo], past)
+        for i, s in enumerate(todo):
+            self.memo[s] = (hs[i], kn[i], vn[i])
+
+    def logits(self, slot: tuple, depth: int) -> np.ndarray:
+        """Logits after ``depth`` layers for the slot's last token."""
+        return self.m.logits(self.memo[slot][0][depth])
+
+    def commit(self, y: int):
+        """The anchor token's KV joins the cache; ``y`` becomes the new anchor.
+
+        Memo entries are kept only for slots that continue (anchor, y, ...),
+        re-keyed by dropping the old anchor.
+        """
+        anchor = [s for s in self.memo if len(s) == 1]
+        assert len(anchor) == 1
+        a = anchor[0]
+        _, k, v = self.memo[a]
+        for l in range(self.m.L):
+            self.K[l] = np.concatenate([self.K[l], k[l][None]])
+            self.V[l] = np.concatenate([self.V[l], v[l][None]])
+        self.C += 1
+        self.memo = {s[1:]: val for s, val in self.memo.items()
+                     if len(s) >= 2 and s[0] == a[0] and s[1] == y}
