@@ -1,0 +1,179 @@
+/*
+ * dex.h - C ABI of the Depth Exploration Decoding (DEX) lattice-step library
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is "Depth Exploration for LLM Decoding" (arXiv 2606.29223):
+ * a decoder of L layers is cut into N stages at the exploration depths
+ * X = {d_0 < ... < d_{N-1} = L} (Section 2.3, Definition 4); each stage is a
+ * depth explorer (Section 3.1). One call of dex_step runs one round of
+ * Algorithm 1 for every live sequence: every node of the depth-position
+ * lattice created in that round runs its stage (expand), every new node is
+ * decoded by the shared final norm and LM head with depth-coupled sampling
+ * (Section 3.3, Algorithm 2), and a sequence whose anchor path reached the
+ * final depth commits exactly the final-depth token and collapses the lattice
+ * onto the shallowest matching branch (Section 3.2, "Commit process" and
+ * "Finite-state control and collapse").
+ *
+ * Conventions
+ *  - Every function returns DEX_OK (0) or a negative dex_status. No exception
+ *    crosses the ABI. dex_last_error gives a message for the last failure.
+ *  - Device pointers are HIP device addresses on the current device. Host
+ *    pointers are ordinary process memory.
+ *  - Weight tensors are row-major [out_features][in_features] in the model's
+ *    storage type (float for DEX_DTYPE_F32, bfloat16 bits for
+ *    DEX_DTYPE_BF16). The caller owns them; dex_create copies them into its
+ *    own packed layout inside the workspace, after which the caller may free
+ *    them.
+ *  - The workspace (size from dex_workspace_bytes) is a caller-owned device
+ *    buffer that the context uses until dex_destroy.
+ *  - A context is bound to one HIP stream (passed as void*, a hipStream_t) and
+ *    is not thread-safe. Calls that compute enqueue on that stream; dex_step,
+ *    dex_ar_step and dex_prefill synchronise it before returning.
+ *  - After DEX_EHIP the context is poisoned: only dex_destroy and
+ *    dex_last_error are accepted.
+ */
+#ifndef DEX_H_
+#define DEX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DEX_OK = 0,
+  DEX_EINVAL = -1, /* invalid argument: shapes, exploration set, tokens, sizes */
+  DEX_ENOSPC = -2, /* workspace or output buffer too small, context too long */
+  DEX_ESTATE = -3, /* call not valid in the current state (no prefill, all done, mixed modes) */
+  DEX_EHIP = -4    /* a HIP runtime call failed; the context is poisoned */
+} dex_status;
+
+typedef enum { DEX_DTYPE_F32 = 0, DEX_DTYPE_BF16 = 1 } dex_dtype;
+typedef enum { DEX_GREEDY = 0, DEX_SAMPLE = 1 } dex_mode;
+
+/* Decoder shape: pre-RMSNorm layers with rotary attention (rotate-half pairs
+ * (i, i + head_dim/2), angle position * rope_base^(-2i/head_dim)) and a SwiGLU
+ * feed-forward block; the same final norm and LM head decode every depth
+ * (Section 3.4 and Appendix C.2 of the paper). n_heads must be a multiple of
+ * n_kv_heads; head_dim is 64 or 128. */
+typedef struct {
+  int32_t n_layers;   /* L */
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t d_ffn;
+  int32_t vocab;
+  float rope_base;
+  float rms_eps;
+  int32_t tied_head;  /* 1: the LM head is the embedding matrix */
+  int32_t dtype;      /* dex_dtype: storage of weights and KV */
+} dex_model_config;
+
+/* Device pointers, row-major [out][in]. Per-layer entries are host arrays of
+ * n_layers device pointers. Norm weights are vectors of d_model. */
+typedef struct {
+  const void* tok_embed;           /* [vocab][d_model] */
+  const void* const* attn_norm;    /* [L] -> [d_model] */
+  const void* const* wq;           /* [L] -> [n_heads*head_dim][d_model] */
+  const void* const* wk;           /* [L] -> [n_kv_heads*head_dim][d_model] */
+  const void* const* wv;           /* [L] -> [n_kv_heads*head_dim][d_model] */
+  const void* const* wo;           /* [L] -> [d_model][n_heads*head_dim] */
+  const void* const* ffn_norm;     /* [L] -> [d_model] */
+  const void* const* w_gate;       /* [L] -> [d_ffn][d_model] */
+  const void* const* w_up;         /* [L] -> [d_ffn][d_model] */
+  const void* const* w_down;       /* [L] -> [d_model][d_ffn] */
+  const void* final_norm;          /* [d_model] */
+  const void* lm_head;             /* [vocab][d_model]; ignored when tied_head */
+} dex_weights;
+
+typedef struct {
+  int32_t mode;            /* dex_mode */
+  float temperature;       /* sampling: the rule takes argmax(z / temperature + g) */
+  int32_t decs;            /* 1: depth-coupled sampling masks shallower candidates of the slot chain */
+  int32_t max_batch;       /* sequences per context, 1..64 */
+  int32_t max_context;     /* prompt + generated tokens per sequence */
+  int32_t max_new_tokens;  /* T: a sequence stops after T commits */
+  /* Sampling only: device float32 Gumbel(0,1) rows [max_batch][gumbel_rows][vocab];
+   * row (b, j) is the noise for target position prompt_len_b + j, shared by
+   * every node predicting that position (one row per slot, shared across
+   * depths: Appendix C.1). Needs gumbel_rows >= max_new_tokens + N - 1. */
+  const float* gumbel;
+  int32_t gumbel_rows;
+  int32_t debug;           /* bit 0: keep the final-depth logits of each sequence's last commit */
+} dex_options;
+
+/* One committed token (Algorithm 1, validate_and_commit). */
+typedef struct {
+  int32_t seq;       /* sequence index */
+  int32_t position;  /* absolute position of the token */
+  int32_t token;     /* y = u_{N-1}, the final-depth reference */
+  int32_t branch;    /* b: shallowest anchor branch whose candidate equals y (N-1 if none) */
+  int32_t layers;    /* d_b: layers the token consumed on its critical path */
+} dex_commit;
+
+typedef struct dex_ctx dex_ctx;
+
+/* Device bytes needed by dex_create for this shape, exploration set and
+ * options. Pure: touches no device. X (host, n_x entries) must be strictly
+ * increasing with X[n_x-1] == cfg->n_layers and, in this build, uniformly
+ * spaced (d_k = (k+1) * L / n_x). Errors: DEX_EINVAL. */
+int dex_workspace_bytes(const dex_model_config* cfg, const int32_t* X, int32_t n_x,
+                        const dex_options* opt, size_t* out_bytes);
+
+/* Validates the configuration, packs the weights into the workspace and
+ * builds the RoPE table. L must equal cfg->n_layers. Enqueues on `stream`
+ * and synchronises it. Errors: DEX_EINVAL (bad shapes or X, null pointers),
+ * DEX_ENOSPC (ws_bytes too small), DEX_EHIP. On success *out owns a host
+ * struct released by dex_destroy. */
+int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t* X, int32_t n_x,
+               int32_t L, const dex_options* opt, void* d_workspace, size_t ws_bytes, void* stream,
+               dex_ctx** out);
+
+/* Resets every sequence and runs the prompts through all layers: positions
+ * 0..len-2 of each prompt fill the committed KV cache; the last prompt token
+ * becomes the anchor of the first cycle (FSM state 0). `tokens` holds the
+ * prompts back to back (host int32), `lens` their lengths (host, n_seqs).
+ * Errors: DEX_EINVAL (n_seqs outside 1..max_batch, len < 1, token outside
+ * [0, vocab)), DEX_ENOSPC (len + max_new_tokens > max_context), DEX_EHIP. */
+int dex_prefill(dex_ctx* ctx, int32_t n_seqs, const int32_t* tokens, const int32_t* lens);
+
+/* One lattice round for every live sequence (expand, decode with DECS,
+ * commit and collapse where the anchor path reached the final explorer).
+ * Writes at most one record per sequence into `out` (host, capacity cap) and
+ * their count into *n_out. Errors: DEX_ESTATE (no prefill, every sequence
+ * done, or the context was stepped with dex_ar_step), DEX_ENOSPC (cap < live
+ * sequences), DEX_EHIP. */
+int dex_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
+
+/* Plain autoregressive decoding with the same kernels: one full-depth token
+ * per live sequence per call (branch = 0, layers = L). The reference that DEX
+ * must reproduce bit for bit. Errors as dex_step (DEX_ESTATE if the context
+ * was stepped with dex_step since the last prefill). */
+int dex_ar_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
+
+/* For sequence `seq`'s last commit: the anchor-path candidates u_0..u_{N-1}
+ * and their top-1 minus top-2 margins (host arrays of N, either may be NULL),
+ * and, when options.debug bit 0 is set, the final-depth logits (host array of
+ * vocab floats, may be NULL). For dex_ar_step only u[0] and margins[0] are
+ * set. Errors: DEX_EINVAL (seq out of range, logits requested without debug),
+ * DEX_ESTATE (no commit yet), DEX_EHIP. */
+int dex_debug_anchor(dex_ctx* ctx, int32_t seq, int32_t* u, float* margins, float* logits);
+
+/* Per-step counters of the last dex_step / dex_ar_step: rows run at each
+ * explorer (host array of N int32, may be NULL) and the total row count. */
+int dex_last_step_rows(const dex_ctx* ctx, int32_t* rows_per_stage, int32_t* total_rows);
+
+void dex_destroy(dex_ctx* ctx);
+
+/* Message for the last failure on ctx (or of the last failed dex_create when
+ * ctx is NULL). Owned by the library; valid until the next call. */
+const char* dex_last_error(const dex_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DEX_H_ */

@@ -1,0 +1,60 @@
+"""Build libdex.so (the HIP lattice-step library) for gfx950 with hipcc.
+
+Usage: python -m lossless_depth_adaptive_amd.build  (or build() from Python).
+The shared library lands next to this file; it is git-ignored but travels with
+the source tree.
+"""
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(HERE, "libdex.so")
+SOURCES = ["gemm.hip", "layer.hip", "lattice.hip", "dex_capi.hip"]
+ARCH = os.environ.get("DEX_OFFLOAD_ARCH", "gfx950")
+
+# Packed fp32 VALU forms are disabled for every device compile.
+FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _hipcc():
+    for c in ("/opt/rocm/bin/hipcc", "hipcc"):
+        if os.path.exists(c) or c == "hipcc":
+            return c
+
+
+def _compile(src: str, outdir: str) -> str:
+    obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
+    return obj
+
+
+def build(verbose: bool = True) -> str:
+    outdir = os.path.join(HERE, "_build")
+    os.makedirs(outdir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, outdir), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB}")
+    return LIB
+
+
+if __name__ == "__main__":
+    build()
+    sys.exit(0)

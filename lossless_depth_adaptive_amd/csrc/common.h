@@ -1,0 +1,117 @@
+// Shared device/host definitions of the DEX lattice-step library (gfx950).
+//
+// Storage types: T is either float (fp32 models) or bf16_t (bfloat16 bits in
+// an unsigned short). The residual stream is always fp32; GEMM activations,
+// weights and KV use T; every accumulation is fp32.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dex {
+
+constexpr int kMaxN = 10;            // explorers supported (2^10 - 1 lattice nodes)
+constexpr int kWave = 64;
+constexpr int kGemmThreads = 512;    // 8 waves: fixed 8-way split of K
+constexpr int kKSplit = 8;
+constexpr int kMaxMB = 4;            // 16-row MFMA blocks per GEMM group (<= 64 rows)
+constexpr int kMaxGroups = 48;       // GEMM groups per launch
+constexpr int kAttnTile = 64;        // keys per attention tile (absolute positions)
+constexpr int kAttnChunk = 512;      // keys per split-KV chunk (absolute positions)
+constexpr int kAttnUnits = 32;       // (row, query head) units per attention work item
+constexpr int kAttnThreads = 256;
+
+typedef unsigned short bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+// One lattice (or autoregressive, or prefill) row of a step.
+struct RowInfo {
+  int seq;          // sequence index
+  int phys;         // physical node slot of the sequence (token, margin, explore KV)
+  int hrow;         // row of the fp32 hidden pool holding this row's residual stream
+  int stage;        // explorer index j (layer j*S + lambda at layer slot lambda)
+  int pos;          // absolute position of the row's input token
+  int tok;          // token id to embed, or -1 when the row continues a hidden state
+  int ncommit;      // keys read from the committed cache: positions [0, ncommit)
+  int n_anc;        // explore-buffer keys at positions ncommit .. ncommit+n_anc-1
+  int anc[kMaxN];   // physical slots holding those keys (same stage)
+  int n_mask;       // tokens masked by depth-coupled sampling
+  int mask[kMaxN];  // the masked token ids
+  int final_;       // 1 for the final-depth reference node
+  int grow;         // Gumbel row: target position minus the prompt length
+  int kv_commit;    // 1: write this row's K/V into the committed cache at pos
+};
+
+// Per-sequence plan of one lattice step, written by the host.
+struct SeqPlan {
+  int live;         // sequence takes part in this step
+  int q;            // FSM state: rounds completed by the current tree
+  int C;            // committed KV length
+  int commit;       // the round reaches the final explorer (q + 1 == N)
+  int prompt_len;
+  int base[kMaxN];  // first row index of this sequence's rows at each stage
+};
+
+struct GemmGroup {
+  const void* w;    // packed weights of this group
+  int row0;         // first row (activations A[row0 ...], row info rows[row0 ...])
+  int m;            // rows, 1..64
+};
+
+enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+
+struct GemmArgs {
+  GemmGroup g[kMaxGroups];
+  int ngroups;
+  int K;            // reduction length (multiple of 8 * k-step)
+  int N;            // output columns (multiple of 16)
+  const void* a;    // activations [rows][K] (T)
+  float* out;       // EPI_STORE: [rows][N] fp32; EPI_HEAD: debug logits [seq][N] or null
+  void* act;        // EPI_SWIGLU: [rows][N/2] (T)
+  float* hidden;    // EPI_RESID: hidden pool [*][N]
+  const RowInfo* rows;
+  // EPI_HEAD
+  int mode;         // 0 greedy, 1 sample
+  float tau;
+  const float* gumbel;   // [batch][gumbel_rows][N]
+  int gumbel_rows;
+  float* part;      // [rows][N/16][3] partial top-2 per 16-column tile
+};
+
+struct AttnItem {
+  int row0;         // first row
+  int nrows;        // rows (all of one sequence and one layer)
+  int stage;        // explorer of the rows; layer = stage * smul + lam
+  int max_keys;     // max over the rows of ncommit + n_anc
+};
+
+struct ModelDims {
+  int L, d, nq, nkv, hd, F, V;
+  int S;            // layers per stage
+  int N;            // explorers
+  int P;            // lattice node slots per sequence (2^N - 1)
+  int B;            // max sequences
+  int Cmax;         // max context
+  float eps;
+};
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((unsigned)v) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  unsigned u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// Host-visible kernel launchers (defined in the .hip files).
+struct Launch {
+  hipStream_t stream;
+};
+
+}  // namespace dex

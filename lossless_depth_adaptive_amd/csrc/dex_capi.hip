@@ -1,0 +1,749 @@
+// Host side of the DEX lattice-step library: the C ABI declared in
+// include/dex.h, workspace carving, weight packing, prefill, and the launch
+// sequence of one lattice round ("Depth Exploration for LLM Decoding",
+// Algorithm 1: expand -> DECS -> insert -> commit and collapse, or advance).
+//
+// The host owns the FSM counters of each sequence (state q, committed length
+// C, commits made); the device owns everything that depends on token values
+// (node map, candidates, KV, hidden states). A sequence in state q runs the
+// 2^q new nodes of its tree: 2^(q-1-j) at explorer j < q and the anchor path's
+// node at explorer q, so the row counts of a round are known on the host
+// before launch, and the only device-to-host transfer per round is the commit
+// records (at most one per sequence).
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "dex.h"
+
+namespace dex {
+template <typename T>
+hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, int, int, int, int, hipStream_t);
+template <typename T>
+hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
+hipError_t launch_head_reduce(const float*, int, int, const RowInfo*, int, int*, float*, hipStream_t);
+template <typename T>
+hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, int, hipStream_t);
+template <typename T>
+hipError_t launch_rmsnorm(const float*, const RowInfo*, int, int, const float*, long long, int, int, void*, int,
+                          float, hipStream_t);
+template <typename T>
+hipError_t launch_rope_kv(const float*, const RowInfo*, int, int, const float*, const float*, float*, void*, void*,
+                          const ModelDims&, int, int, float, hipStream_t);
+template <typename T>
+hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, int, const float*, const void*, const void*,
+                            float*, void*, const ModelDims&, int, int, int, int, hipStream_t);
+hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
+                        hipStream_t);
+hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
+                         float*, const int*, int, int, hipStream_t);
+template <typename T>
+hipError_t launch_promote(const SeqPlan*, int, const int*, const void*, void*, const ModelDims&, hipStream_t);
+hipError_t launch_ar_rows(const SeqPlan*, int, RowInfo*, const int*, int, hipStream_t);
+hipError_t launch_ar_commit(const SeqPlan*, int, const int*, const float*, int*, int*, int*, float*, int, int,
+                            hipStream_t);
+hipError_t launch_reset(int*, int*, int*, int*, const int*, int, int, hipStream_t);
+}  // namespace dex
+
+using namespace dex;
+
+namespace {
+
+thread_local std::string g_create_error;
+constexpr int kPrefillRows = 512;
+
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+// Every buffer of the workspace, as byte offsets.
+struct WsPlan {
+  size_t embed, head, norms, cosT, sinT, kvc, exb, hidden;
+  size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
+  size_t rows, plans, items, A, qkv, q, attn_out, act, attn_part, head_part;
+  std::vector<size_t> wqkv, wo, wgu, wdown;
+  size_t total;
+  int Rmax, nchunk;
+};
+
+size_t esize(int dtype) { return dtype == DEX_DTYPE_BF16 ? 2 : 4; }
+
+int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex_options* o, std::string& err) {
+  if (!c || !X || !o) { err = "null argument"; return DEX_EINVAL; }
+  if (c->n_layers < 1 || c->d_model < 16 || c->n_heads < 1 || c->n_kv_heads < 1 || c->d_ffn < 8 || c->vocab < 16) {
+    err = "non-positive model dimension"; return DEX_EINVAL;
+  }
+  if (c->dtype != DEX_DTYPE_F32 && c->dtype != DEX_DTYPE_BF16) { err = "dtype must be F32 or BF16"; return DEX_EINVAL; }
+  if (c->head_dim != 64 && c->head_dim != 128) { err = "head_dim must be 64 or 128"; return DEX_EINVAL; }
+  if (c->n_heads % c->n_kv_heads) { err = "n_heads must be a multiple of n_kv_heads"; return DEX_EINVAL; }
+  if (c->n_heads / c->n_kv_heads > kAttnUnits) { err = "too many query heads per kv head"; return DEX_EINVAL; }
+  const int kstep = c->dtype == DEX_DTYPE_BF16 ? 32 : 16;
+  if (c->d_model % kstep || (c->n_heads * c->head_dim) % kstep || c->d_ffn % kstep) {
+    err = "d_model, n_heads*head_dim and d_ffn must be multiples of the MFMA k-step (32 bf16, 16 fp32)";
+    return DEX_EINVAL;
+  }
+  if (c->d_model % 16 || c->vocab % 16 || c->d_ffn % 8) { err = "d_model and vocab must be multiples of 16, d_ffn of 8"; return DEX_EINVAL; }
+  if (!(c->rms_eps > 0) || !(c->rope_base > 1)) { err = "rms_eps and rope_base must be positive"; return DEX_EINVAL; }
+  if (n_x < 1 || n_x > kMaxN) { err = "number of exploration depths must be 1..10"; return DEX_EINVAL; }
+  for (int k = 0; k < n_x; ++k) {
+    if (X[k] < 1 || (k > 0 && X[k] <= X[k - 1])) { err = "exploration set must be strictly increasing within [1, L]"; return DEX_EINVAL; }
+  }
+  if (X[n_x - 1] != c->n_layers) { err = "the last exploration depth must equal L"; return DEX_EINVAL; }
+  if (c->n_layers % n_x) { err = "L must be a multiple of the number of explorers"; return DEX_EINVAL; }
+  for (int k = 0; k < n_x; ++k)
+    if (X[k] != (k + 1) * (c->n_layers / n_x)) { err = "only uniformly spaced exploration sets are supported"; return DEX_EINVAL; }
+  if (o->max_batch < 1 || o->max_batch > 64) { err = "max_batch must be 1..64"; return DEX_EINVAL; }
+  if (o->max_context < 2) { err = "max_context must be at least 2"; return DEX_EINVAL; }
+  if (o->max_new_tokens < 1) { err = "max_new_tokens must be positive"; return DEX_EINVAL; }
+  if (o->mode != DEX_GREEDY && o->mode != DEX_SAMPLE) { err = "mode must be GREEDY or SAMPLE"; return DEX_EINVAL; }
+  if (o->mode == DEX_SAMPLE) {
+    if (!(o->temperature > 0)) { err = "temperature must be positive"; return DEX_EINVAL; }
+    if (!o->gumbel) { err = "sampling needs Gumbel rows"; return DEX_EINVAL; }
+    if (o->gumbel_rows < o->max_new_tokens + n_x - 1) { err = "gumbel_rows must be >= max_new_tokens + N - 1"; return DEX_EINVAL; }
+  }
+  return DEX_OK;
+}
+
+WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) {
+  WsPlan w;
+  Layout lay;
+  const size_t es = esize(c->dtype);
+  const size_t L = c->n_layers, d = c->d_model, nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim,
+               F = c->d_ffn, V = c->vocab, B = o->max_batch, Cmax = o->max_context;
+  const int N = n_x, S = c->n_layers / n_x, P = (1 << N) - 1;
+  w.Rmax = std::max(std::max((int)B << (N - 1), kPrefillRows), (int)B);
+  w.nchunk = (int)((Cmax + kAttnChunk - 1) / kAttnChunk);
+  const size_t R = w.Rmax;
+  w.embed = lay.take(V * d * es);
+  w.head = lay.take(V * d * es);
+  for (size_t l = 0; l < L; ++l) {
+    w.wqkv.push_back(lay.take((nq + 2 * nkv) * hd * d * es));
+    w.wo.push_back(lay.take(d * nq * hd * es));
+    w.wgu.push_back(lay.take(2 * F * d * es));
+    w.wdown.push_back(lay.take(d * F * es));
+  }
+  w.norms = lay.take((2 * L + 1) * d * 4);
+  w.cosT = lay.take(Cmax * (hd / 2) * 4);
+  w.sinT = lay.take(Cmax * (hd / 2) * 4);
+  w.kvc = lay.take(B * L * 2 * nkv * Cmax * hd * es);
+  w.exb = lay.take(B * P * S * 2 * nkv * hd * es);
+  w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
+  w.map = lay.take(B * P * 4);
+  w.cand = lay.take(B * P * 4);
+  w.margin = lay.take(B * P * 4);
+  w.freel = lay.take(B * P * 4);
+  w.cursor = lay.take(B * 4);
+  w.anchor = lay.take(B * 4);
+  w.anchors_in = lay.take(B * 4);
+  w.records = lay.take(B * 5 * 4);
+  w.promote = lay.take(B * kMaxN * 4);
+  w.dbg_u = lay.take(B * kMaxN * 4);
+  w.dbg_m = lay.take(B * kMaxN * 4);
+  w.Xd = lay.take(kMaxN * 4);
+  w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
+  w.rows = lay.take(R * sizeof(RowInfo));
+  w.plans = lay.take(B * sizeof(SeqPlan));
+  w.items = lay.take(R * sizeof(AttnItem));
+  w.A = lay.take(R * std::max(std::max(d, nq * hd), F) * es);
+  w.qkv = lay.take(R * (nq + 2 * nkv) * hd * 4);
+  w.q = lay.take(R * nq * hd * 4);
+  w.attn_out = lay.take(R * nq * hd * es);
+  w.act = lay.take(R * F * es);
+  w.attn_part = lay.take(R * nq * w.nchunk * (hd + 2) * 4);
+  w.head_part = lay.take(R * (V / 16) * 3 * 4);
+  w.total = lay.off;
+  return w;
+}
+
+}  // namespace
+
+struct dex_ctx {
+  dex_model_config cfg;
+  dex_options opt;
+  ModelDims D;
+  int N, S, L;
+  std::vector<int> X;
+  bool bf16;
+  hipStream_t st;
+  char* ws;
+  WsPlan wp;
+  // device views
+  float *norms, *cosT, *sinT, *hidden, *margin, *dbg_m, *dbg_logits, *qkv, *q, *attn_part, *head_part;
+  int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
+  RowInfo* rows;
+  SeqPlan* plans;
+  AttnItem* items;
+  void *kvc, *exb, *A, *attn_out, *act, *embed, *head;
+  // host state
+  int nseq = 0;
+  std::vector<int> q_, C_, commits_, plen_;
+  int mode_used = 0;  // 0 none since prefill, 1 lattice, 2 autoregressive
+  bool any_commit = false;
+  bool poisoned = false;
+  SeqPlan* h_plans = nullptr;
+  int* h_records = nullptr;
+  AttnItem* h_items = nullptr;
+  RowInfo* h_rows = nullptr;
+  std::string err;
+  int last_rows[kMaxN] = {0};
+  int last_total = 0;
+
+  void* at(size_t off) { return ws + off; }
+};
+
+#define HIPCHK(expr)                                                              \
+  do {                                                                            \
+    hipError_t e_ = (expr);                                                       \
+    if (e_ != hipSuccess) {                                                       \
+      ctx->err = std::string(#expr) + ": " + hipGetErrorString(e_);               \
+      ctx->poisoned = true;                                                       \
+      return DEX_EHIP;                                                            \
+    }                                                                             \
+  } while (0)
+
+namespace {
+
+template <typename T>
+int pack_weights(dex_ctx* ctx, const dex_weights* w) {
+  const int L = ctx->L, d = ctx->D.d, nq = ctx->D.nq, nkv = ctx->D.nkv, hd = ctx->D.hd, F = ctx->D.F, V = ctx->D.V;
+  hipStream_t st = ctx->st;
+  for (int l = 0; l < L; ++l) {
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wqkv[l]), w->wq[l], w->wk[l], w->wv[l], nq * hd, nkv * hd, nkv * hd, d, 1,
+                          (nq + 2 * nkv) * hd, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wo[l]), w->wo[l], nullptr, nullptr, d, 0, 0, nq * hd, 0, d, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wgu[l]), w->w_gate[l], w->w_up[l], nullptr, F, F, 0, d, 2, 2 * F, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wdown[l]), w->w_down[l], nullptr, nullptr, d, 0, 0, F, 0, d, st));
+  }
+  const void* hsrc = ctx->cfg.tied_head ? w->tok_embed : w->lm_head;
+  HIPCHK(launch_pack<T>(ctx->head, hsrc, nullptr, nullptr, V, 0, 0, d, 0, V, st));
+  HIPCHK(hipMemcpyAsync(ctx->embed, w->tok_embed, (size_t)V * d * sizeof(T), hipMemcpyDeviceToDevice, st));
+  // Norm weights to fp32, through the host (2L+1 vectors of d).
+  std::vector<T> tmp(d);
+  std::vector<float> nf((size_t)(2 * L + 1) * d);
+  for (int i = 0; i < 2 * L + 1; ++i) {
+    const void* src = i == 2 * L ? w->final_norm : (i % 2 == 0 ? w->attn_norm[i / 2] : w->ffn_norm[i / 2]);
+    HIPCHK(hipMemcpy(tmp.data(), src, d * sizeof(T), hipMemcpyDeviceToHost));
+    for (int k = 0; k < d; ++k) {
+      float f;
+      if (sizeof(T) == 2) {
+        const unsigned u = ((unsigned)((const unsigned short*)tmp.data())[k]) << 16;
+        std::memcpy(&f, &u, 4);
+      } else {
+        std::memcpy(&f, (const char*)tmp.data() + 4 * k, 4);
+      }
+      nf[(size_t)i * d + k] = f;
+    }
+  }
+  HIPCHK(hipMemcpy(ctx->norms, nf.data(), nf.size() * 4, hipMemcpyHostToDevice));
+  return DEX_OK;
+}
+
+// One pass of the layer stack over `nrows` rows already set up in ctx->rows.
+// groups_by_stage: for each stage, [row0, count) of its rows; lam_count layer
+// slots; smul = S for lattice rows (layer = stage*S + lam), 0 for autoregressive
+// and prefill rows (layer = lam).
+template <typename T>
+int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& stage_rows, int lam_count,
+               int smul, int nitems, int max_keys) {
+  const ModelDims& D = ctx->D;
+  hipStream_t st = ctx->st;
+  const int d = D.d, nq = D.nq, nkv = D.nkv, hd = D.hd, F = D.F;
+  const float qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+  // Groups are collected in a host list and launched kMaxGroups at a time.
+  std::vector<GemmGroup> glist;
+  auto groups_for = [&](int lam, const std::vector<size_t>& woff) {
+    glist.clear();
+    for (size_t j = 0; j < stage_rows.size(); ++j) {
+      const int r0 = stage_rows[j].first, cnt = stage_rows[j].second;
+      const int layer = (int)j * smul + lam;
+      for (int o = 0; o < cnt; o += 64) glist.push_back(GemmGroup{ctx->at(woff[layer]), r0 + o, std::min(64, cnt - o)});
+    }
+  };
+  auto run_gemm = [&](GemmArgs& ga, int epi) -> hipError_t {
+    for (size_t g0 = 0; g0 < glist.size(); g0 += kMaxGroups) {
+      ga.ngroups = (int)std::min(glist.size() - g0, (size_t)kMaxGroups);
+      for (int i = 0; i < ga.ngroups; ++i) ga.g[i] = glist[g0 + i];
+      const hipError_t e = launch_gemm<T>(ga, epi, st);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  };
+  for (int lam = 0; lam < lam_count; ++lam) {
+    HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms, 2LL * d, smul, lam, ctx->A, d, D.eps, st));
+    GemmArgs ga;
+    std::memset(&ga, 0, sizeof(ga));
+    ga.rows = ctx->rows;
+    ga.hidden = ctx->hidden;
+    groups_for(lam, ctx->wp.wqkv);
+    ga.K = d;
+    ga.N = (nq + 2 * nkv) * hd;
+    ga.a = ctx->A;
+    ga.out = ctx->qkv;
+    HIPCHK(run_gemm(ga, EPI_STORE));
+    HIPCHK(launch_rope_kv<T>(ctx->qkv, ctx->rows, 0, nrows, ctx->cosT, ctx->sinT, ctx->q, ctx->kvc, ctx->exb, D, smul,
+                             lam, qscale, st));
+    HIPCHK(launch_attention<T>(ctx->items, nitems, ctx->rows, 0, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_part,
+                               ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys, st));
+    groups_for(lam, ctx->wp.wo);
+    ga.K = nq * hd;
+    ga.N = d;
+    ga.a = ctx->attn_out;
+    HIPCHK(run_gemm(ga, EPI_RESID));
+    HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms + d, 2LL * d, smul, lam, ctx->A, d, D.eps, st));
+    groups_for(lam, ctx->wp.wgu);
+    ga.K = d;
+    ga.N = 2 * F;
+    ga.a = ctx->A;
+    ga.act = ctx->act;
+    HIPCHK(run_gemm(ga, EPI_SWIGLU));
+    groups_for(lam, ctx->wp.wdown);
+    ga.K = F;
+    ga.N = d;
+    ga.a = ctx->act;
+    HIPCHK(run_gemm(ga, EPI_RESID));
+  }
+  return DEX_OK;
+}
+
+template <typename T>
+int run_head(dex_ctx* ctx, int nrows) {
+  const ModelDims& D = ctx->D;
+  hipStream_t st = ctx->st;
+  HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms + (size_t)2 * ctx->L * D.d, 0, 0, 0, ctx->A,
+                           D.d, D.eps, st));
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.rows = ctx->rows;
+  ga.K = D.d;
+  ga.N = D.V;
+  ga.a = ctx->A;
+  ga.out = (ctx->opt.debug & 1) ? ctx->dbg_logits : nullptr;
+  ga.mode = ctx->opt.mode;
+  ga.tau = ctx->opt.temperature;
+  ga.gumbel = ctx->opt.gumbel;
+  ga.gumbel_rows = ctx->opt.gumbel_rows;
+  ga.part = ctx->head_part;
+  for (int r0 = 0; r0 < nrows; r0 += 64 * kMaxGroups) {
+    ga.ngroups = 0;
+    for (int o = r0; o < std::min(nrows, r0 + 64 * kMaxGroups); o += 64) {
+      ga.g[ga.ngroups].w = ctx->head;
+      ga.g[ga.ngroups].row0 = o;
+      ga.g[ga.ngroups].m = std::min(64, nrows - o);
+      ++ga.ngroups;
+    }
+    HIPCHK(launch_gemm<T>(ga, EPI_HEAD, st));
+  }
+  HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, nrows, ctx->rows, D.P, ctx->cand, ctx->margin, st));
+  return DEX_OK;
+}
+
+// One round (lattice) or one autoregressive token for every live sequence.
+template <typename T>
+int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out) {
+  const int N = ctx->N, B = ctx->nseq;
+  const int T_ = ctx->opt.max_new_tokens;
+  // Host plan: rows per (sequence, stage) from the FSM state alone.
+  std::vector<int> live(B), rows_seq_stage((size_t)B * N, 0);
+  int nlive = 0, ncommit = 0;
+  int stage_tot[kMaxN] = {0};
+  for (int s = 0; s < B; ++s) {
+    live[s] = ctx->commits_[s] < T_;
+    if (!live[s]) continue;
+    ++nlive;
+    const int q = ar ? 0 : ctx->q_[s];
+    for (int j = 0; j < N; ++j) {
+      int r = 0;
+      if (ar) r = j == 0 ? 1 : 0;
+      else if (j < q) r = 1 << (q - 1 - j);
+      else if (j == q) r = 1;
+      rows_seq_stage[(size_t)s * N + j] = r;
+      stage_tot[j] += r;
+    }
+  }
+  if (nlive == 0) {
+    ctx->err = "every sequence has reached max_new_tokens";
+    return DEX_ESTATE;
+  }
+  if (cap < nlive) {
+    ctx->err = "output capacity below the number of live sequences";
+    return DEX_ENOSPC;
+  }
+  int stage_off[kMaxN + 1];
+  stage_off[0] = 0;
+  for (int j = 0; j < N; ++j) stage_off[j + 1] = stage_off[j] + stage_tot[j];
+  const int R = stage_off[N];
+  std::vector<int> cursor(stage_off, stage_off + N);
+  for (int s = 0; s < B; ++s) {
+    SeqPlan& p = ctx->h_plans[s];
+    std::memset(&p, 0, sizeof(p));
+    p.live = live[s];
+    p.q = ar ? 0 : ctx->q_[s];
+    p.C = ctx->C_[s];
+    p.commit = live[s] && (ar || p.q + 1 == N);
+    p.prompt_len = ctx->plen_[s];
+    ncommit += p.commit;
+    for (int j = 0; j < N; ++j) {
+      p.base[j] = cursor[j];
+      cursor[j] += rows_seq_stage[(size_t)s * N + j];
+    }
+  }
+  // Attention work items: rows of one (sequence, stage), at most kAttnUnits units each.
+  const int rep = ctx->D.nq / ctx->D.nkv;
+  const int per_item = std::max(1, kAttnUnits / rep);
+  int nitems = 0, max_keys = 0;
+  for (int j = 0; j < N; ++j)
+    for (int s = 0; s < B; ++s) {
+      const int cnt = rows_seq_stage[(size_t)s * N + j];
+      const int mk = ctx->C_[s] + (ar ? 1 : (ctx->q_[s] - j + 1));
+      for (int o = 0; o < cnt; o += per_item) {
+        AttnItem& it = ctx->h_items[nitems++];
+        it.row0 = ctx->h_plans[s].base[j] + o;
+        it.nrows = std::min(per_item, cnt - o);
+        it.stage = j;
+        it.max_keys = mk;
+        max_keys = std::max(max_keys, mk);
+      }
+    }
+  hipStream_t st = ctx->st;
+  HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
+  HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
+  if (ar) HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
+  else HIPCHK(launch_sched(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
+                           ctx->D.P, ctx->opt.decs, st));
+  HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, stage_tot[0], ctx->hidden, ctx->D.d, st));
+  std::vector<std::pair<int, int>> stage_rows;
+  for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
+  int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys);
+  if (rc) return rc;
+  rc = run_head<T>(ctx, R);
+  if (rc) return rc;
+  if (ncommit) {
+    if (ar) {
+      HIPCHK(launch_ar_commit(ctx->plans, B, ctx->cand, ctx->margin, ctx->anchor, ctx->records, ctx->dbg_u, ctx->dbg_m,
+                              ctx->D.P, ctx->L, st));
+    } else {
+      HIPCHK(launch_commit(ctx->plans, B, ctx->map, ctx->cand, ctx->margin, ctx->freel, ctx->cursor, ctx->anchor,
+                           ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P, st));
+      HIPCHK(launch_promote<T>(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
+    }
+    HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));
+  }
+  HIPCHK(hipStreamSynchronize(st));
+  int n = 0;
+  for (int s = 0; s < B; ++s) {
+    if (!live[s]) continue;
+    if (ctx->h_plans[s].commit) {
+      const int* r = ctx->h_records + s * 5;
+      dex_commit c;
+      c.seq = r[0];
+      c.position = r[1];
+      c.token = r[2];
+      c.branch = r[3];
+      c.layers = r[4];
+      out[n++] = c;
+      ctx->C_[s] += 1;
+      ctx->commits_[s] += 1;
+      ctx->q_[s] = ar ? 0 : N - 1 - c.branch;
+    } else {
+      ctx->q_[s] += 1;
+    }
+  }
+  *n_out = n;
+  ctx->any_commit = ctx->any_commit || n > 0;
+  for (int j = 0; j < N; ++j) ctx->last_rows[j] = stage_tot[j];
+  ctx->last_total = R;
+  return DEX_OK;
+}
+
+template <typename T>
+int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* lens) {
+  hipStream_t st = ctx->st;
+  std::vector<int> anchors(n_seqs);
+  size_t off = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    anchors[s] = tokens[off + lens[s] - 1];
+    off += lens[s];
+  }
+  HIPCHK(hipMemcpy(ctx->anchors_in, anchors.data(), n_seqs * 4, hipMemcpyHostToDevice));
+  HIPCHK(launch_reset(ctx->map, ctx->freel, ctx->cursor, ctx->anchor, ctx->anchors_in, n_seqs, ctx->D.P, st));
+  const int base_h = ctx->opt.max_batch * ctx->D.P;
+  const int rep = ctx->D.nq / ctx->D.nkv;
+  const int per_item = std::max(1, kAttnUnits / rep);
+  off = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    const int npos = lens[s] - 1;  // positions 0..len-2 go to the committed cache
+    for (int p0 = 0; p0 < npos; p0 += kPrefillRows) {
+      const int R = std::min(kPrefillRows, npos - p0);
+      for (int i = 0; i < R; ++i) {
+        RowInfo& r = ctx->h_rows[i];
+        std::memset(&r, 0, sizeof(r));
+        r.seq = s;
+        r.phys = 0;
+        r.hrow = base_h + i;
+        r.stage = 0;
+        r.pos = p0 + i;
+        r.tok = tokens[off + p0 + i];
+        r.ncommit = p0 + i + 1;
+        r.kv_commit = 1;
+      }
+      int nitems = 0;
+      for (int o = 0; o < R; o += per_item) {
+        AttnItem& it = ctx->h_items[nitems++];
+        it.row0 = o;
+        it.nrows = std::min(per_item, R - o);
+        it.stage = 0;
+        it.max_keys = p0 + o + it.nrows;
+      }
+      HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
+      HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
+      HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->D.d, st));
+      std::vector<std::pair<int, int>> stage_rows = {{0, R}};
+      const int rc = run_layers<T>(ctx, R, stage_rows, ctx->L, 0, nitems, p0 + R);
+      if (rc) return rc;
+      HIPCHK(hipStreamSynchronize(st));  // host row buffers are reused by the next chunk
+    }
+    off += lens[s];
+  }
+  HIPCHK(hipStreamSynchronize(st));
+  return DEX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dex_workspace_bytes(const dex_model_config* cfg, const int32_t* X, int32_t n_x, const dex_options* opt,
+                        size_t* out_bytes) {
+  std::string err;
+  const int rc = validate(cfg, X, n_x, opt, err);
+  if (rc) {
+    g_create_error = err;
+    return rc;
+  }
+  if (!out_bytes) {
+    g_create_error = "null output";
+    return DEX_EINVAL;
+  }
+  *out_bytes = plan_workspace(cfg, n_x, opt).total;
+  return DEX_OK;
+}
+
+int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t* X, int32_t n_x, int32_t L,
+               const dex_options* opt, void* d_workspace, size_t ws_bytes, void* stream, dex_ctx** out) {
+  std::string err;
+  int rc = validate(cfg, X, n_x, opt, err);
+  if (!rc && (!w || !d_workspace || !out)) { err = "null weights, workspace or output"; rc = DEX_EINVAL; }
+  if (!rc && L != cfg->n_layers) { err = "L must equal cfg->n_layers"; rc = DEX_EINVAL; }
+  if (!rc) {
+    const bool tied = cfg->tied_head != 0;
+    bool ok = w->tok_embed && w->final_norm && (tied || w->lm_head) && w->attn_norm && w->wq && w->wk && w->wv &&
+              w->wo && w->ffn_norm && w->w_gate && w->w_up && w->w_down;
+    for (int l = 0; ok && l < cfg->n_layers; ++l)
+      ok = w->attn_norm[l] && w->wq[l] && w->wk[l] && w->wv[l] && w->wo[l] && w->ffn_norm[l] && w->w_gate[l] &&
+           w->w_up[l] && w->w_down[l];
+    if (!ok) { err = "null weight pointer"; rc = DEX_EINVAL; }
+  }
+  WsPlan wp;
+  if (!rc) {
+    wp = plan_workspace(cfg, n_x, opt);
+    if (ws_bytes < wp.total) {
+      char buf[160];
+      snprintf(buf, sizeof buf, "workspace too small: %zu < %zu bytes", ws_bytes, wp.total);
+      err = buf;
+      rc = DEX_ENOSPC;
+    }
+  }
+  if (rc) {
+    g_create_error = err;
+    return rc;
+  }
+  dex_ctx* ctx = new dex_ctx();
+  ctx->cfg = *cfg;
+  ctx->opt = *opt;
+  ctx->N = n_x;
+  ctx->L = cfg->n_layers;
+  ctx->S = cfg->n_layers / n_x;
+  ctx->X.assign(X, X + n_x);
+  ctx->bf16 = cfg->dtype == DEX_DTYPE_BF16;
+  ctx->st = (hipStream_t)stream;
+  ctx->ws = (char*)d_workspace;
+  ctx->wp = wp;
+  ModelDims& D = ctx->D;
+  D.L = cfg->n_layers;
+  D.d = cfg->d_model;
+  D.nq = cfg->n_heads;
+  D.nkv = cfg->n_kv_heads;
+  D.hd = cfg->head_dim;
+  D.F = cfg->d_ffn;
+  D.V = cfg->vocab;
+  D.S = ctx->S;
+  D.N = n_x;
+  D.P = (1 << n_x) - 1;
+  D.B = opt->max_batch;
+  D.Cmax = opt->max_context;
+  D.eps = cfg->rms_eps;
+  ctx->embed = ctx->at(wp.embed);
+  ctx->head = ctx->at(wp.head);
+  ctx->norms = (float*)ctx->at(wp.norms);
+  ctx->cosT = (float*)ctx->at(wp.cosT);
+  ctx->sinT = (float*)ctx->at(wp.sinT);
+  ctx->kvc = ctx->at(wp.kvc);
+  ctx->exb = ctx->at(wp.exb);
+  ctx->hidden = (float*)ctx->at(wp.hidden);
+  ctx->map = (int*)ctx->at(wp.map);
+  ctx->cand = (int*)ctx->at(wp.cand);
+  ctx->margin = (float*)ctx->at(wp.margin);
+  ctx->freel = (int*)ctx->at(wp.freel);
+  ctx->cursor = (int*)ctx->at(wp.cursor);
+  ctx->anchor = (int*)ctx->at(wp.anchor);
+  ctx->anchors_in = (int*)ctx->at(wp.anchors_in);
+  ctx->records = (int*)ctx->at(wp.records);
+  ctx->promote = (int*)ctx->at(wp.promote);
+  ctx->dbg_u = (int*)ctx->at(wp.dbg_u);
+  ctx->dbg_m = (float*)ctx->at(wp.dbg_m);
+  ctx->Xd = (int*)ctx->at(wp.Xd);
+  ctx->dbg_logits = (opt->debug & 1) ? (float*)ctx->at(wp.dbg_logits) : nullptr;
+  ctx->rows = (RowInfo*)ctx->at(wp.rows);
+  ctx->plans = (SeqPlan*)ctx->at(wp.plans);
+  ctx->items = (AttnItem*)ctx->at(wp.items);
+  ctx->A = ctx->at(wp.A);
+  ctx->qkv = (float*)ctx->at(wp.qkv);
+  ctx->q = (float*)ctx->at(wp.q);
+  ctx->attn_out = ctx->at(wp.attn_out);
+  ctx->act = ctx->at(wp.act);
+  ctx->attn_part = (float*)ctx->at(wp.attn_part);
+  ctx->head_part = (float*)ctx->at(wp.head_part);
+  auto fail = [&](int code) {
+    g_create_error = ctx->err;
+    dex_destroy(ctx);
+    return code;
+  };
+  if (hipHostMalloc((void**)&ctx->h_plans, sizeof(SeqPlan) * D.B) != hipSuccess ||
+      hipHostMalloc((void**)&ctx->h_records, 5 * 4 * D.B) != hipSuccess ||
+      hipHostMalloc((void**)&ctx->h_items, sizeof(AttnItem) * wp.Rmax) != hipSuccess ||
+      hipHostMalloc((void**)&ctx->h_rows, sizeof(RowInfo) * wp.Rmax) != hipSuccess) {
+    ctx->err = "hipHostMalloc failed";
+    return fail(DEX_EHIP);
+  }
+  rc = ctx->bf16 ? pack_weights<bf16_t>(ctx, w) : pack_weights<float>(ctx, w);
+  if (rc) return fail(rc);
+  // RoPE table: angle pos * base^(-2i/hd) in double, cos/sin rounded to float.
+  const int half = D.hd / 2;
+  std::vector<float> cs((size_t)D.Cmax * half), sn((size_t)D.Cmax * half);
+  for (int p = 0; p < D.Cmax; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double ang = (double)p * std::pow((double)cfg->rope_base, -2.0 * i / D.hd);
+      cs[(size_t)p * half + i] = (float)std::cos(ang);
+      sn[(size_t)p * half + i] = (float)std::sin(ang);
+    }
+  int xd[kMaxN] = {0};
+  for (int k = 0; k < n_x; ++k) xd[k] = X[k];
+  if (hipMemcpy(ctx->cosT, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->sinT, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->Xd, xd, sizeof(xd), hipMemcpyHostToDevice) != hipSuccess ||
+      hipStreamSynchronize(ctx->st) != hipSuccess) {
+    ctx->err = "upload of tables failed";
+    return fail(DEX_EHIP);
+  }
+  *out = ctx;
+  return DEX_OK;
+}
+
+int dex_prefill(dex_ctx* ctx, int32_t n_seqs, const int32_t* tokens, const int32_t* lens) {
+  if (!ctx) return DEX_EINVAL;
+  if (ctx->poisoned) return DEX_EHIP;
+  if (n_seqs < 1 || n_seqs > ctx->opt.max_batch || !tokens || !lens) {
+    ctx->err = "n_seqs must be 1..max_batch with non-null tokens and lens";
+    return DEX_EINVAL;
+  }
+  size_t total = 0;
+  for (int s = 0; s < n_seqs; ++s) {
+    if (lens[s] < 1) { ctx->err = "prompt length must be >= 1"; return DEX_EINVAL; }
+    if ((long long)lens[s] + ctx->opt.max_new_tokens + ctx->N > ctx->opt.max_context) {
+      ctx->err = "prompt length + max_new_tokens + N exceeds max_context";
+      return DEX_ENOSPC;
+    }
+    total += lens[s];
+  }
+  for (size_t i = 0; i < total; ++i)
+    if (tokens[i] < 0 || tokens[i] >= ctx->D.V) { ctx->err = "token id outside [0, vocab)"; return DEX_EINVAL; }
+  const int rc = ctx->bf16 ? run_prefill<bf16_t>(ctx, n_seqs, tokens, lens) : run_prefill<float>(ctx, n_seqs, tokens, lens);
+  if (rc) return rc;
+  ctx->nseq = n_seqs;
+  ctx->q_.assign(n_seqs, 0);
+  ctx->C_.assign(n_seqs, 0);
+  ctx->commits_.assign(n_seqs, 0);
+  ctx->plen_.assign(n_seqs, 0);
+  for (int s = 0; s < n_seqs; ++s) {
+    ctx->C_[s] = lens[s] - 1;
+    ctx->plen_[s] = lens[s];
+  }
+  ctx->mode_used = 0;
+  ctx->any_commit = false;
+  return DEX_OK;
+}
+
+static int step_common(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out) {
+  if (!ctx) return DEX_EINVAL;
+  if (ctx->poisoned) return DEX_EHIP;
+  if (!out || !n_out) { ctx->err = "null output"; return DEX_EINVAL; }
+  if (ctx->nseq == 0) { ctx->err = "no prefill"; return DEX_ESTATE; }
+  const int want = ar ? 2 : 1;
+  if (ctx->mode_used && ctx->mode_used != want) {
+    ctx->err = "lattice and autoregressive steps cannot be mixed after one prefill";
+    return DEX_ESTATE;
+  }
+  const int rc = ctx->bf16 ? run_step<bf16_t>(ctx, ar, out, cap, n_out) : run_step<float>(ctx, ar, out, cap, n_out);
+  if (rc == DEX_OK) ctx->mode_used = want;
+  return rc;
+}
+
+int dex_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out) { return step_common(ctx, false, out, cap, n_out); }
+
+int dex_ar_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out) { return step_common(ctx, true, out, cap, n_out); }
+
+int dex_debug_anchor(dex_ctx* ctx, int32_t seq, int32_t* u, float* margins, float* logits) {
+  if (!ctx) return DEX_EINVAL;
+  if (ctx->poisoned) return DEX_EHIP;
+  if (seq < 0 || seq >= ctx->nseq) { ctx->err = "seq out of range"; return DEX_EINVAL; }
+  if (logits && !(ctx->opt.debug & 1)) { ctx->err = "logits need options.debug bit 0"; return DEX_EINVAL; }
+  if (ctx->commits_[seq] == 0) { ctx->err = "sequence has no commit yet"; return DEX_ESTATE; }
+  const int n = ctx->mode_used == 2 ? 1 : ctx->N;
+  if (u) HIPCHK(hipMemcpy(u, ctx->dbg_u + seq * kMaxN, n * 4, hipMemcpyDeviceToHost));
+  if (margins) HIPCHK(hipMemcpy(margins, ctx->dbg_m + seq * kMaxN, n * 4, hipMemcpyDeviceToHost));
+  if (logits) HIPCHK(hipMemcpy(logits, ctx->dbg_logits + (size_t)seq * ctx->D.V, (size_t)ctx->D.V * 4, hipMemcpyDeviceToHost));
+  return DEX_OK;
+}
+
+int dex_last_step_rows(const dex_ctx* ctx, int32_t* rows_per_stage, int32_t* total_rows) {
+  if (!ctx) return DEX_EINVAL;
+  if (rows_per_stage)
+    for (int j = 0; j < ctx->N; ++j) rows_per_stage[j] = ctx->last_rows[j];
+  if (total_rows) *total_rows = ctx->last_total;
+  return DEX_OK;
+}
+
+void dex_destroy(dex_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->h_plans) (void)hipHostFree(ctx->h_plans);
+  if (ctx->h_records) (void)hipHostFree(ctx->h_records);
+  if (ctx->h_items) (void)hipHostFree(ctx->h_items);
+  if (ctx->h_rows) (void)hipHostFree(ctx->h_rows);
+  delete ctx;
+}
+
+const char* dex_last_error(const dex_ctx* ctx) {
+  if (!ctx) return g_create_error.c_str();
+  return ctx->err.c_str();
+}
+
+}  // extern "C"

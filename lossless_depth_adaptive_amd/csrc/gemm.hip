@@ -1,0 +1,324 @@
+// Weight packing and the grouped, batch-invariant MFMA GEMM of the lattice step.
+//
+// Every projection of a decoder layer (QKV, O, gate/up, down) and the shared
+// LM head is Y[m, n] = sum_k A[m, k] W[n, k] with W row-major [N, K]
+// ("Depth Exploration for LLM Decoding", Section 3.1: each explorer runs its
+// stage, Layers(d_{k-1}, d_k], on its node batch; here one launch runs layer
+// slot lambda of every stage that has rows, one weight group per stage).
+//
+// Batch invariance: the value of output (m, n) depends only on row m of A and
+// column n of W, never on how many rows share the launch or where the row
+// sits. The reduction order is fixed by K alone:
+//   * K is cut into k-steps of 32 (bf16) or 16 (fp32) elements, one MFMA
+//     v_mfma_f32_16x16x32_bf16 (or four v_mfma_f32_16x16x4_f32) per step;
+//   * the k-steps are split into 8 contiguous ranges, [KS*w/8, KS*(w+1)/8)
+//     for wave w, each accumulated from zero in increasing order;
+//   * the 8 partial sums are added in wave order 0..7.
+// So plain autoregressive decoding (one row) and a 2048-row lattice stage give
+// bit-identical rows.
+//
+// Memory layout: weights are repacked once (dex_create) into MFMA fragments.
+// Fragment (nb, ks) holds output columns 16nb..16nb+15 and k-step ks as 64
+// lanes x 16 bytes, lane l carrying column l%16 and elements
+// [ks*KSTEP + (l/16)*EPL, +EPL). A wave streaming its k range therefore reads
+// one contiguous 1 KiB per instruction.
+#include "common.h"
+
+namespace dex {
+
+template <typename T> struct Mfma;
+template <> struct Mfma<bf16_t> {
+  static constexpr int KSTEP = 32;
+  static constexpr int EPL = 8;
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    bf16x8_t av, bv;
+    __builtin_memcpy(&av, &a, 16);
+    __builtin_memcpy(&bv, &b, 16);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+  }
+};
+template <> struct Mfma<float> {
+  static constexpr int KSTEP = 16;
+  static constexpr int EPL = 4;
+  // Lane l supplies elements kbase + 4*(l/16) + i for i = 0..3; MFMA i reduces
+  // over the four lane groups, so the four MFMAs cover the 16 elements.
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Packing. mode 0: one source [N][K]. mode 1: rows of src0, src1, src2
+// concatenated (n0, n1, n2 rows). mode 2: SwiGLU interleave of gate (src0)
+// and up (src1), each [n0][K]: packed fragment nb holds gate rows 8nb..8nb+7
+// in columns 0..7 and up rows 8nb..8nb+7 in columns 8..15.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void pack_kernel(u32x4_t* __restrict__ dst, const T* __restrict__ s0, const T* __restrict__ s1,
+                            const T* __restrict__ s2, int n0, int n1, int n2, int K, int mode,
+                            long long total) {
+  constexpr int KSTEP = Mfma<T>::KSTEP, EPL = Mfma<T>::EPL;
+  const int KS = K / KSTEP;
+  for (long long idx = blockIdx.x * (long long)blockDim.x + threadIdx.x; idx < total;
+       idx += (long long)gridDim.x * blockDim.x) {
+    const int lane = (int)(idx & 63);
+    const long long t = idx >> 6;
+    const int ks = (int)(t % KS);
+    const long long nb = t / KS;
+    const int c = lane & 15;
+    const int k0 = ks * KSTEP + (lane >> 4) * EPL;
+    const T* src;
+    if (mode == 2) {
+      const long long r = nb * 8 + (c & 7);
+      src = (c < 8 ? s0 : s1) + r * K;
+    } else {
+      long long r = nb * 16 + c;
+      if (r < n0) src = s0 + r * K;
+      else if (r < (long long)n0 + n1) src = s1 + (r - n0) * K;
+      else src = s2 + (r - n0 - n1) * K;
+    }
+    dst[idx] = *(const u32x4_t*)(src + k0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Grouped GEMM. grid = (N/16 tiles, groups), block = 512 (8 waves = 8 k ranges).
+// ---------------------------------------------------------------------------
+template <typename T, int MB, int EPI>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args) {
+  constexpr int KSTEP = Mfma<T>::KSTEP;
+  constexpr int EPL = Mfma<T>::EPL;
+  constexpr int U = 4;
+  const int gi = blockIdx.y;
+  if (gi >= args.ngroups) return;
+  const GemmGroup G = args.g[gi];
+  const int tile = blockIdx.x;
+  const int ntiles = args.N >> 4;
+  const int K = args.K;
+  const int KS = K / KSTEP;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int kb = (KS * w) / kKSplit, ke = (KS * (w + 1)) / kKSplit;
+
+  const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile * KS * 64 + lane;
+  const T* A = (const T*)args.a + (size_t)G.row0 * K;
+  const int col16 = lane & 15;
+  const int kq = (lane >> 4) * EPL;
+
+  f32x4_t acc[MB];
+  const u32x4_t* ap[MB];
+  bool av[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r = mb * 16 + col16;
+    av[mb] = r < G.m;
+    ap[mb] = (const u32x4_t*)(A + (size_t)(av[mb] ? r : 0) * K + kq);
+  }
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+  int ks = kb;
+  for (; ks + U <= ke; ks += U) {
+    u32x4_t bv[U];
+    u32x4_t a[U][MB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) bv[u] = __builtin_nontemporal_load(wp + (size_t)(ks + u) * 64);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) a[u][mb] = av[mb] ? ap[mb][(ks + u) * (KSTEP / EPL)] : zero;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) Mfma<T>::mma(acc[mb], a[u][mb], bv[u]);
+  }
+  for (; ks < ke; ++ks) {
+    const u32x4_t b = __builtin_nontemporal_load(wp + (size_t)ks * 64);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const u32x4_t a = av[mb] ? ap[mb][ks * (KSTEP / EPL)] : zero;
+      Mfma<T>::mma(acc[mb], a, b);
+    }
+  }
+
+  // Partial tiles of the 8 k ranges, then their sum in wave order.
+  __shared__ float red[kKSplit][kMaxMB * 256];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[w][(mb * 16 + (lane >> 4) * 4 + r) * 16 + col16] = acc[mb][r];
+  __syncthreads();
+
+  constexpr int E = MB * 256;
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    for (int e = threadIdx.x; e < E; e += kGemmThreads) {
+      const int rl = e >> 4, c = e & 15;
+      if (rl >= G.m) continue;
+      float v = red[0][e];
+#pragma unroll
+      for (int q = 1; q < kKSplit; ++q) v += red[q][e];
+      const int row = G.row0 + rl;
+      const int n = tile * 16 + c;
+      if constexpr (EPI == EPI_STORE) {
+        args.out[(size_t)row * args.N + n] = v;
+      } else {
+        float* h = args.hidden + (size_t)args.rows[row].hrow * args.N + n;
+        *h = *h + v;
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    for (int e = threadIdx.x; e < MB * 128; e += kGemmThreads) {
+      const int rl = e >> 3, c = e & 7;
+      if (rl >= G.m) continue;
+      const int eg = rl * 16 + c, eu = eg + 8;
+      float g = red[0][eg], u = red[0][eu];
+#pragma unroll
+      for (int q = 1; q < kKSplit; ++q) {
+        g += red[q][eg];
+        u += red[q][eu];
+      }
+      const float s = g / (1.0f + expf(-g));
+      const int row = G.row0 + rl;
+      ((T*)args.act)[(size_t)row * (args.N >> 1) + tile * 8 + c] = from_f<T>(s * u);
+    }
+  } else {  // EPI_HEAD
+    __shared__ float sc[kMaxMB * 16][17];
+    for (int e = threadIdx.x; e < E; e += kGemmThreads) {
+      const int rl = e >> 4, c = e & 15;
+      if (rl >= G.m) continue;
+      float z = red[0][e];
+#pragma unroll
+      for (int q = 1; q < kKSplit; ++q) z += red[q][e];
+      const int row = G.row0 + rl;
+      const int n = tile * 16 + c;
+      const RowInfo& ri = args.rows[row];
+      if (args.out != nullptr && ri.final_) args.out[(size_t)ri.seq * args.N + n] = z;
+      float s = z;
+      if (!ri.final_) {
+        for (int i = 0; i < ri.n_mask; ++i)
+          if (ri.mask[i] == n) s = -INFINITY;
+      }
+      if (args.mode == 1)
+        s = s / args.tau +
+            args.gumbel[((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N + n];
+      sc[rl][c] = s;
+    }
+    __syncthreads();
+    for (int rl = threadIdx.x; rl < MB * 16; rl += kGemmThreads) {
+      if (rl >= G.m) continue;
+      float best = sc[rl][0], second = -INFINITY;
+      int bi = 0;
+      for (int c = 1; c < 16; ++c) {
+        const float s = sc[rl][c];
+        if (s > best) {
+          second = best;
+          best = s;
+          bi = c;
+        } else if (s > second) {
+          second = s;
+        }
+      }
+      float* p = args.part + ((size_t)(G.row0 + rl) * ntiles + tile) * 3;
+      p[0] = best;
+      p[1] = __int_as_float(tile * 16 + bi);
+      p[2] = second;
+    }
+  }
+}
+
+// Exact merge of two (best, index, second) summaries: ties keep the lower id.
+__device__ __forceinline__ void top2_merge(float& b, int& i, float& s, float b2, int i2, float s2) {
+  if (b2 > b || (b2 == b && i2 < i)) {
+    s = fmaxf(s2, b);
+    b = b2;
+    i = i2;
+  } else {
+    s = fmaxf(s, b2);
+  }
+}
+
+// One wave per row: reduce the per-tile summaries to the row's token and margin.
+__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int nrows,
+                                   const RowInfo* __restrict__ rows, int P, int* __restrict__ cand,
+                                   float* __restrict__ margin) {
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= nrows) return;
+  float b = -INFINITY, s = -INFINITY;
+  int i = 0x7fffffff;
+  for (int t = lane; t < ntiles; t += 64) {
+    const float* p = part + ((size_t)row * ntiles + t) * 3;
+    top2_merge(b, i, s, p[0], __float_as_int(p[1]), p[2]);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float b2 = __shfl_xor(b, off);
+    const int i2 = __shfl_xor(i, off);
+    const float s2 = __shfl_xor(s, off);
+    top2_merge(b, i, s, b2, i2, s2);
+  }
+  if (lane == 0) {
+    const RowInfo& ri = rows[row];
+    if (i < 0 || i >= ntiles * 16) i = 0;  // unreachable for finite logits; keeps token ids in range
+    cand[ri.seq * P + ri.phys] = i;
+    margin[ri.seq * P + ri.phys] = b - s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+template <typename T>
+hipError_t launch_pack(void* dst, const void* s0, const void* s1, const void* s2, int n0, int n1,
+                       int n2, int K, int mode, int Npacked, hipStream_t st) {
+  const long long total = (long long)(Npacked / 16) * (K / Mfma<T>::KSTEP) * 64;
+  const int threads = 256;
+  long long blocks = (total + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, st, (u32x4_t*)dst,
+                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1, n2, K, mode, total);
+  return hipGetLastError();
+}
+template hipError_t launch_pack<float>(void*, const void*, const void*, const void*, int, int, int,
+                                       int, int, int, hipStream_t);
+template hipError_t launch_pack<bf16_t>(void*, const void*, const void*, const void*, int, int, int,
+                                        int, int, int, hipStream_t);
+
+template <typename T, int EPI>
+static hipError_t launch_gemm_mb(const GemmArgs& a, int mb, hipStream_t st) {
+  dim3 grid(a.N / 16, a.ngroups);
+  switch (mb) {
+    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((gemm_kernel<T, 3, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((gemm_kernel<T, 4, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+
+// Runs one grouped GEMM; the MFMA row-block count is the largest group's.
+template <typename T>
+hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
+  int mmax = 1;
+  for (int i = 0; i < a.ngroups; ++i) mmax = a.g[i].m > mmax ? a.g[i].m : mmax;
+  const int mb = (mmax + 15) / 16;
+  switch (epi) {
+    case EPI_STORE: return launch_gemm_mb<T, EPI_STORE>(a, mb, st);
+    case EPI_RESID: return launch_gemm_mb<T, EPI_RESID>(a, mb, st);
+    case EPI_SWIGLU: return launch_gemm_mb<T, EPI_SWIGLU>(a, mb, st);
+    default: return launch_gemm_mb<T, EPI_HEAD>(a, mb, st);
+  }
+}
+template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
+template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
+
+hipError_t launch_head_reduce(const float* part, int ntiles, int nrows, const RowInfo* rows, int P,
+                              int* cand, float* margin, hipStream_t st) {
+  if (nrows == 0) return hipSuccess;
+  const int wpb = 4;
+  hipLaunchKernelGGL(head_reduce_kernel, dim3((nrows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, part,
+                     ntiles, nrows, rows, P, cand, margin);
+  return hipGetLastError();
+}
+
+}  // namespace dex

@@ -1,0 +1,273 @@
+// Lattice bookkeeping on the device: the round's row schedule (expand), the
+// commit rule with collapse, and promotion of the anchor path's KV into the
+// committed cache ("Depth Exploration for LLM Decoding", Algorithm 1 and
+// Section 3.2).
+//
+// Nodes of a sequence's tree use heap numbering: node i has depth child 2i+1
+// and position child 2i+2, so ETK_0's children are ETK_1 (depth) and ETK_2
+// (position) and state q holds nodes 0 .. 2^q - 2, as the paper's four-explorer
+// example states. The bits of i+1 after its leading 1 are the path from the
+// root (0 = depth move, 1 = position move), hence
+//   explorer (stage) = trailing zeros of i+1,
+//   position offset  = popcount(i+1) - 1,
+//   slot-chain root  = ((i+1) >> stage) - 1,  chain member at depth m = ((root+1) << m) - 1.
+// A node's data (candidate token, margin, explore KV) lives in a physical slot
+// of its sequence, reached through map[seq][heap index]; collapse re-points
+// the map instead of moving data.
+#include "common.h"
+
+namespace dex {
+
+__global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restrict__ rows,
+                             int* __restrict__ map, const int* __restrict__ cand,
+                             const int* __restrict__ freel, int* __restrict__ cursor,
+                             const int* __restrict__ anchor_tok, int N, int P, int decs) {
+  const int s = blockIdx.x;
+  const SeqPlan pl = plans[s];
+  if (!pl.live) return;
+  const int q = pl.q, nnew = 1 << q, first = nnew - 1;
+  const int cur = cursor[s];
+  int* mp = map + (size_t)s * P;
+  const int* cd = cand + (size_t)s * P;
+  for (int t = threadIdx.x; t < nnew; t += blockDim.x) {
+    const int n = first + t, n1 = n + 1;
+    const int depth = __builtin_ctz(n1);
+    const int posoff = __popc(n1) - 1;
+    const int phys = freel[(size_t)s * P + cur + t];
+    mp[n] = phys;
+    const int idx = depth < q ? (((n1 >> depth) - (1 << (q - depth)) - 1) >> 1) : 0;
+    RowInfo R;
+    R.seq = s;
+    R.phys = phys;
+    R.stage = depth;
+    R.pos = pl.C + posoff;
+    R.ncommit = pl.C;
+    R.kv_commit = 0;
+    R.final_ = depth == N - 1;
+    R.grow = pl.C + posoff + 1 - pl.prompt_len;
+    const int root = (n1 >> depth) - 1;
+    R.hrow = s * P + (depth == 0 ? phys : mp[root]);
+    R.tok = depth != 0 ? -1 : (n == 0 ? anchor_tok[s] : cd[mp[(n - 1) >> 1]]);
+    // Slot roots on the path (the tree root and every position move), in
+    // position order; their chain members at this stage hold the keys.
+    const int level = 31 - __builtin_clz(n1);
+    int cnt = 0;
+    for (int sh = level; sh >= 0; --sh) {
+      const int pfx = n1 >> sh;
+      if (pfx == 1 || (pfx & 1)) {
+        const int node = (pfx << depth) - 1;
+        R.anc[cnt++] = node == n ? phys : mp[node];
+      }
+    }
+    R.n_anc = cnt;
+    // Depth-coupled sampling: candidates of shallower members of the chain.
+    R.n_mask = 0;
+    if (decs && depth < N - 1) {
+      for (int m = 0; m < depth; ++m) R.mask[m] = cd[mp[((root + 1) << m) - 1]];
+      R.n_mask = depth;
+    }
+    rows[pl.base[depth] + idx] = R;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) cursor[s] = cur + nnew;
+}
+
+// Commit and collapse for every sequence whose round reached the final
+// explorer. u_j = candidate of anchor node 2^j - 1; the token is u_{N-1}; the
+// branch is the smallest j with u_j == u_{N-1}. The subtree under the branch's
+// position child (heap 2^(k+1)) becomes the new tree: relative node j at level
+// lv maps to old node (2^(k+1) + 1) 2^lv - 1 + (j + 1 - 2^lv), for the
+// 2^(N-1-k) - 1 nodes it holds. Free slots are rebuilt in increasing order.
+__global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict__ map,
+                              const int* __restrict__ cand, const float* __restrict__ margin,
+                              int* __restrict__ freel, int* __restrict__ cursor,
+                              int* __restrict__ anchor_tok, int* __restrict__ records,
+                              int* __restrict__ promote_src, int* __restrict__ dbg_u,
+                              float* __restrict__ dbg_m, const int* __restrict__ Xd, int N, int P) {
+  const int s = blockIdx.x;
+  const SeqPlan pl = plans[s];
+  if (!pl.live || !pl.commit) return;
+  __shared__ int u[kMaxN];
+  __shared__ int ksh;
+  __shared__ int nm[1 << (kMaxN - 1)];
+  __shared__ unsigned char used[1 << kMaxN];
+  int* mp = map + (size_t)s * P;
+  const int tid = threadIdx.x;
+  if (tid < N) {
+    const int p = mp[(1 << tid) - 1];
+    u[tid] = cand[(size_t)s * P + p];
+    promote_src[s * kMaxN + tid] = p;
+    dbg_u[s * kMaxN + tid] = u[tid];
+    dbg_m[s * kMaxN + tid] = margin[(size_t)s * P + p];
+  }
+  for (int p = tid; p < P; p += blockDim.x) used[p] = 0;
+  __syncthreads();
+  if (tid == 0) {
+    const int y = u[N - 1];
+    int k = N - 1;
+    for (int j = 0; j < N; ++j)
+      if (u[j] == y) {
+        k = j;
+        break;
+      }
+    int* rec = records + s * 5;
+    rec[0] = s;
+    rec[1] = pl.C + 1;
+    rec[2] = y;
+    rec[3] = k;
+    rec[4] = Xd[k];
+    anchor_tok[s] = y;
+    ksh = k;
+  }
+  __syncthreads();
+  const int k = ksh;
+  const int nk = (1 << (N - 1 - k)) - 1;
+  const int root = 1 << (k + 1);
+  for (int j = tid; j < nk; j += blockDim.x) {
+    const int lv = 31 - __builtin_clz(j + 1);
+    nm[j] = mp[((root + 1) << lv) - 1 + (j + 1 - (1 << lv))];
+  }
+  __syncthreads();
+  for (int j = tid; j < nk; j += blockDim.x) {
+    mp[j] = nm[j];
+    used[nm[j]] = 1;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int c = 0;
+    for (int p = 0; p < P; ++p)
+      if (!used[p]) freel[(size_t)s * P + c++] = p;
+    cursor[s] = 0;
+  }
+}
+
+// Copy the anchor path's K/V (node 2^j - 1 holds stage j) into the committed
+// cache at position C. grid = (sequences, layers).
+template <typename T>
+__global__ void promote_kernel(const SeqPlan* __restrict__ plans, const int* __restrict__ promote_src,
+                               const T* __restrict__ exb, T* __restrict__ kvc, ModelDims D) {
+  const int s = blockIdx.x, layer = blockIdx.y;
+  const SeqPlan pl = plans[s];
+  if (!pl.live || !pl.commit) return;
+  const int j = layer / D.S, lam = layer - j * D.S;
+  const int phys = promote_src[s * kMaxN + j];
+  const int n = 2 * D.nkv * D.hd;
+  for (int t = threadIdx.x; t < n; t += blockDim.x) {
+    const int kv = t / (D.nkv * D.hd);
+    const int rem = t - kv * D.nkv * D.hd;
+    const int h = rem / D.hd, i = rem - h * D.hd;
+    const T v = exb[((((size_t)s * D.P + phys) * D.S + lam) * 2 + kv) * D.nkv * D.hd + (size_t)h * D.hd + i];
+    kvc[((((size_t)s * D.L + layer) * 2 + kv) * D.nkv + h) * (size_t)D.Cmax * D.hd + (size_t)pl.C * D.hd + i] = v;
+  }
+}
+
+// Plain autoregressive rows: one full-depth row per live sequence.
+__global__ void ar_rows_kernel(const SeqPlan* __restrict__ plans, int nseq, RowInfo* __restrict__ rows,
+                               const int* __restrict__ anchor_tok, int P) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= nseq) return;
+  const SeqPlan pl = plans[s];
+  if (!pl.live) return;
+  RowInfo R;
+  R.seq = s;
+  R.phys = 0;
+  R.hrow = s * P;
+  R.stage = 0;
+  R.pos = pl.C;
+  R.tok = anchor_tok[s];
+  R.ncommit = pl.C + 1;
+  R.n_anc = 0;
+  R.n_mask = 0;
+  R.final_ = 1;
+  R.grow = pl.C + 1 - pl.prompt_len;
+  R.kv_commit = 1;
+  rows[pl.base[0]] = R;
+}
+
+__global__ void ar_commit_kernel(const SeqPlan* __restrict__ plans, int nseq, const int* __restrict__ cand,
+                                 const float* __restrict__ margin, int* __restrict__ anchor_tok,
+                                 int* __restrict__ records, int* __restrict__ dbg_u,
+                                 float* __restrict__ dbg_m, int P, int L) {
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= nseq) return;
+  const SeqPlan pl = plans[s];
+  if (!pl.live) return;
+  const int y = cand[(size_t)s * P];
+  int* rec = records + s * 5;
+  rec[0] = s;
+  rec[1] = pl.C + 1;
+  rec[2] = y;
+  rec[3] = 0;
+  rec[4] = L;
+  anchor_tok[s] = y;
+  dbg_u[s * kMaxN] = y;
+  dbg_m[s * kMaxN] = margin[(size_t)s * P];
+}
+
+// Reset one sequence's lattice: empty map, all slots free, anchor token.
+__global__ void reset_seq_kernel(int* __restrict__ map, int* __restrict__ freel, int* __restrict__ cursor,
+                                 int* __restrict__ anchor_tok, const int* __restrict__ anchors, int nseq,
+                                 int P) {
+  const int s = blockIdx.x;
+  if (s >= nseq) return;
+  for (int p = threadIdx.x; p < P; p += blockDim.x) {
+    freel[(size_t)s * P + p] = p;
+    map[(size_t)s * P + p] = -1;
+  }
+  if (threadIdx.x == 0) {
+    cursor[s] = 0;
+    anchor_tok[s] = anchors[s];
+  }
+}
+
+// ----------------------------------------------------------------------------
+hipError_t launch_sched(const SeqPlan* plans, int nseq, RowInfo* rows, int* map, const int* cand,
+                        const int* freel, int* cursor, const int* anchor_tok, int N, int P, int decs,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(sched_kernel, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
+                     anchor_tok, N, P, decs);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* cand, const float* margin,
+                         int* freel, int* cursor, int* anchor_tok, int* records, int* promote_src,
+                         int* dbg_u, float* dbg_m, const int* Xd, int N, int P, hipStream_t st) {
+  hipLaunchKernelGGL(commit_kernel, dim3(nseq), dim3(256), 0, st, plans, map, cand, margin, freel, cursor,
+                     anchor_tok, records, promote_src, dbg_u, dbg_m, Xd, N, P);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_promote(const SeqPlan* plans, int nseq, const int* promote_src, const void* exb, void* kvc,
+                          const ModelDims& D, hipStream_t st) {
+  hipLaunchKernelGGL(promote_kernel<T>, dim3(nseq, D.L), dim3(256), 0, st, plans, promote_src,
+                     (const T*)exb, (T*)kvc, D);
+  return hipGetLastError();
+}
+template hipError_t launch_promote<float>(const SeqPlan*, int, const int*, const void*, void*, const ModelDims&,
+                                          hipStream_t);
+template hipError_t launch_promote<bf16_t>(const SeqPlan*, int, const int*, const void*, void*,
+                                           const ModelDims&, hipStream_t);
+
+hipError_t launch_ar_rows(const SeqPlan* plans, int nseq, RowInfo* rows, const int* anchor_tok, int P,
+                          hipStream_t st) {
+  hipLaunchKernelGGL(ar_rows_kernel, dim3((nseq + 63) / 64), dim3(64), 0, st, plans, nseq, rows, anchor_tok, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_ar_commit(const SeqPlan* plans, int nseq, const int* cand, const float* margin,
+                            int* anchor_tok, int* records, int* dbg_u, float* dbg_m, int P, int L,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(ar_commit_kernel, dim3((nseq + 63) / 64), dim3(64), 0, st, plans, nseq, cand, margin,
+                     anchor_tok, records, dbg_u, dbg_m, P, L);
+  return hipGetLastError();
+}
+
+hipError_t launch_reset(int* map, int* freel, int* cursor, int* anchor_tok, const int* anchors, int nseq, int P,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(reset_seq_kernel, dim3(nseq), dim3(256), 0, st, map, freel, cursor, anchor_tok, anchors,
+                     nseq, P);
+  return hipGetLastError();
+}
+
+}  // namespace dex

@@ -1,0 +1,72 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function that
+include/dex.h declares, and dex_workspace_bytes (host-only) validates its
+arguments. No compute call is made."""
+
+import os
+import re
+
+import pytest
+
+from lossless_depth_adaptive_amd import dex as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "dex.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dex_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported():
+    lib = D.load_library()
+    names = _declared()
+    assert set(names) == set(D.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def _cfg(**kw):
+    base = dict(n_layers=8, d_model=256, n_heads=4, n_kv_heads=4, head_dim=64, d_ffn=1024, vocab=2048,
+                tied_head=True, dtype="f32")
+    base.update(kw)
+    return D.model_config(**base)
+
+
+def test_workspace_bytes_grows_with_batch_and_context():
+    a = D.workspace_bytes(_cfg(), [2, 4, 6, 8], D.options(max_batch=1, max_context=128, max_new_tokens=64))
+    b = D.workspace_bytes(_cfg(), [2, 4, 6, 8], D.options(max_batch=4, max_context=128, max_new_tokens=64))
+    c = D.workspace_bytes(_cfg(), [2, 4, 6, 8], D.options(max_batch=1, max_context=4096, max_new_tokens=64))
+    assert 0 < a < b and a < c
+
+
+@pytest.mark.parametrize("X,msg", [
+    ([2, 4, 6], "last exploration depth"),
+    ([4, 2, 6, 8], "strictly increasing"),
+    ([0, 8], "strictly increasing"),
+    ([1, 3, 8], "multiple of the number"),
+    ([3, 4, 8, 8], "strictly increasing"),
+    ([1, 2, 8, 8], "strictly increasing"),
+    ([2, 5, 6, 8], "uniformly spaced"),
+    (list(range(1, 12)), "1..10"),
+])
+def test_invalid_exploration_sets(X, msg):
+    with pytest.raises(D.DexError) as e:
+        D.workspace_bytes(_cfg(n_layers=8 if len(X) <= 8 else 11), X, D.options())
+    assert e.value.code == D.DEX_EINVAL
+    assert msg in str(e.value)
+
+
+@pytest.mark.parametrize("kw,opt", [
+    (dict(head_dim=96), {}),
+    (dict(n_kv_heads=3), {}),
+    (dict(vocab=2050), {}),
+    (dict(d_model=264), {}),
+    ({}, dict(max_batch=0)),
+    ({}, dict(max_batch=65)),
+    ({}, dict(mode="sample")),                 # sampling without Gumbel rows
+])
+def test_invalid_shapes_and_options(kw, opt):
+    with pytest.raises(D.DexError) as e:
+        D.workspace_bytes(_cfg(**kw), [2, 4, 6, 8], D.options(**opt))
+    assert e.value.code == D.DEX_EINVAL

@@ -1,0 +1,133 @@
+"""GPU parity of the HIP lattice step, through the C ABI.
+
+For each case:
+  * DEX (dex_step) and plain AR (dex_ar_step) on the GPU give the same token
+    stream and bit-identical final-depth logits at every commit: the lossless
+    invariant of "Depth Exploration for LLM Decoding", Section 3.2, checked at
+    the bit level (the kernels are batch-invariant);
+  * the oracle, forced onto the GPU's stream, agrees on every quantity whose
+    decision margin exceeds the gate: committed token, anchor candidates
+    u_0..u_{N-1}, selected branch and layers; final-depth logits agree within
+    the tolerance (1e-4 fp32; 3e-2 bf16 weights with fp32 accumulation).
+
+Shapes: the tiny fp32 workload at full size, its variants (sampling, untied
+head, DECS off, N = 1, 2, 8), and reduced-width versions of the 7B/13B/GQA
+workloads that keep their depth, exploration sets, batch structure and
+decoding modes. Full-size 7B runs are in test_gpu_fullsize.py.
+"""
+
+import numpy as np
+import pytest
+
+from oracle.decode import ar_decode
+from oracle.model import PlainModel, SlotEvaluator
+from synthetic import get_workload
+from synthetic.noise import gumbel_rows
+from synthetic.prompts import batch_prompts
+from synthetic.weights import generate
+
+pytestmark = pytest.mark.gpu
+
+tiny = get_workload("tiny_f32")
+small = dict(d_model=512, n_heads=4, n_kv_heads=4, d_ffn=1376, vocab=4096)
+
+CASES = {
+    "tiny": (tiny, dict(T=64)),
+    "tiny_sample": (tiny.scaled(mode="sample", seed_g=3001), dict(T=48)),
+    "tiny_untied_nodecs": (tiny.scaled(tied=False, gamma=0.8), dict(T=40, decs=False)),
+    "tiny_N1": (tiny.scaled(tied=False, gamma=0.8, X=(8,)), dict(T=24)),
+    "tiny_N2": (tiny.scaled(tied=False, gamma=0.8, X=(4, 8)), dict(T=32)),
+    "tiny_N8": (tiny.scaled(tied=False, gamma=0.8, X=tuple(range(1, 9))), dict(T=32)),
+    "llama7b_x4_narrow": (get_workload("llama7b_x4_greedy").scaled(prompt_len=80, **small), dict(T=40)),
+    "llama7b_x8_sample_narrow": (get_workload("llama7b_x8_sample").scaled(prompt_len=80, **small), dict(T=32)),
+    "llama13b_x8_b4_narrow": (get_workload("llama13b_x8_b8").scaled(
+        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4096, batch=4, prompt_len=48), dict(T=20)),
+    "qwen_gqa_x9_b4_narrow": (get_workload("qwen8b_x9_b16").scaled(
+        d_model=512, n_heads=4, n_kv_heads=2, d_ffn=1536, vocab=4096, batch=4, prompt_len=40), dict(T=16)),
+}
+
+
+def _run_case(name):
+    from tests.gpu_helpers import compare_with_oracle, device_weights, make_ctx, run
+    w, kw = CASES[name]
+    T = kw["T"]
+    decs = kw.get("decs", True)
+    N = len(w.X)
+    print(f"[case] {name} L={w.n_layers} d={w.d_model} X={w.X} batch={w.batch} mode={w.mode} T={T}", flush=True)
+    Wd = device_weights(w)
+    prompts = batch_prompts(w)
+    gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab) if w.mode == "sample" else None
+    gum_d = gum.cuda() if gum is not None else None
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d)
+    dex_recs, steps = run(ctx, prompts, T)
+    ctx.close()
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d)
+    ar_recs, ar_steps = run(ctx, prompts, T, ar=True)
+    ctx.close()
+    assert ar_steps == T
+    for s in range(w.batch):
+        assert [r["token"] for r in dex_recs[s]] == [r["token"] for r in ar_recs[s]], f"seq {s}: DEX != AR"
+        for a, b in zip(dex_recs[s], ar_recs[s]):
+            assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32)), \
+                f"seq {s} pos {a['position']}: final logits differ in bits"
+            assert a["position"] == b["position"]
+            assert a["layers"] == w.X[a["branch"]]
+    # round accounting: N rounds to the first commit, then b+1 rounds per commit
+    if w.batch == 1:
+        bs = [r["branch"] for r in dex_recs[0]]
+        assert steps == N + sum(b + 1 for b in bs[:-1])
+    # oracle, forced onto the GPU stream
+    m = PlainModel(w, generate(w))
+    fp32 = w.dtype == "f32"
+    gate, tol = (1e-3, 1e-4) if fp32 else (5e-2, 3e-2)
+    stats = []
+    for s in range(w.batch):
+        g = gum[s].numpy() if gum is not None else None
+        orc = ar_decode(SlotEvaluator(m), prompts[s], T, w.X, mode=w.mode, tau=w.tau, gumbel=g,
+                        decs=decs, forced=[r["token"] for r in dex_recs[s]], brute_ead=False,
+                        keep_logits=True)
+        stats.append(compare_with_oracle(dex_recs[s], orc, gate, tol, N))
+    print(f"[case] {name} steps={steps} oracle-compared tokens={sum(x['tokens'] for x in stats)} "
+          f"branches={sum(x['branches'] for x in stats)} worst logit err="
+          f"{max(x['worst_logit_err'] for x in stats):.3g}", flush=True)
+    total = sum(len(r) for r in dex_recs)
+    assert sum(x["tokens"] for x in stats) >= total // 4, "too few tokens passed the margin gate"
+    assert sum(x["branches"] for x in stats) >= total // 8, "too few branches passed the margin gate"
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_dex_parity(name):
+    _run_case(name)
+
+
+def test_error_codes_on_device():
+    from lossless_depth_adaptive_amd import dex as D
+    from tests.gpu_helpers import device_weights, make_ctx
+    w = tiny
+    Wd = device_weights(w)
+    ctx = make_ctx(w, Wd, 2, 4)
+    with pytest.raises(D.DexError) as e:
+        ctx.step()
+    assert e.value.code == D.DEX_ESTATE
+    with pytest.raises(D.DexError) as e:
+        ctx.prefill([[1, 2, 3]] * 3)                     # more sequences than max_batch
+    assert e.value.code == D.DEX_EINVAL
+    with pytest.raises(D.DexError) as e:
+        ctx.prefill([[1, 2, 99999]])                     # token outside the vocabulary
+    assert e.value.code == D.DEX_EINVAL
+    with pytest.raises(D.DexError) as e:
+        ctx.prefill([list(range(200))])                  # longer than max_context allows
+    assert e.value.code == D.DEX_ENOSPC
+    ctx.prefill([[5, 6, 7], [8]])                        # a one-token prompt is valid
+    recs = ctx.step()
+    assert recs == []                                    # first round never commits (N = 4)
+    with pytest.raises(D.DexError) as e:
+        ctx.ar_step()                                    # modes cannot be mixed
+    assert e.value.code == D.DEX_ESTATE
+    n = 0
+    while n < 8:
+        n += len(ctx.step())
+    with pytest.raises(D.DexError) as e:
+        ctx.step()                                       # both sequences are done
+    assert e.value.code == D.DEX_ESTATE
+    ctx.close()
