@@ -166,6 +166,30 @@ int dex_debug_anchor(dex_ctx* ctx, int32_t seq, int32_t* u, float* margins, floa
  * explorer (host array of N int32, may be NULL) and the total row count. */
 int dex_last_step_rows(const dex_ctx* ctx, int32_t* rows_per_stage, int32_t* total_rows);
 
+/* Kernel classes timed by dex_profile. */
+typedef enum {
+  DEX_PROF_GEMM = 0,     /* stage-batched layer GEMMs (QKV, O, gate/up, down) */
+  DEX_PROF_ATTN = 1,     /* lattice attention and its split-KV combine */
+  DEX_PROF_HEAD = 2,     /* exit head: LM-head GEMM with DECS/Gumbel epilogue, argmax reduce */
+  DEX_PROF_ROWOPS = 3,   /* embedding gather, RMSNorm, RoPE and K/V write */
+  DEX_PROF_LATTICE = 4,  /* schedule, commit/collapse, KV promotion */
+  DEX_PROF_NCLASS = 5
+} dex_prof_class;
+
+typedef struct {
+  double ms;        /* summed GPU time between HIP events around the class's launches */
+  int64_t launches; /* kernel launches timed */
+  double bytes;     /* algorithmic HBM bytes of those launches (each weight matrix, KV entry,
+                       activation row read or written once) */
+  double flops;     /* algorithmic floating-point operations */
+} dex_kernel_stats;
+
+/* Per-class timing of later dex_step / dex_ar_step calls with HIP events on
+ * the context's stream. enable = 1 turns it on, 0 off. When out is not NULL
+ * the stats gathered since the last call are copied into out[0..n-1]
+ * (n <= DEX_PROF_NCLASS) and reset. Errors: DEX_EINVAL (bad n), DEX_EHIP. */
+int dex_profile(dex_ctx* ctx, int32_t enable, dex_kernel_stats* out, int32_t n);
+
 void dex_destroy(dex_ctx* ctx);
 
 /* Message for the last failure on ctx (or of the last failed dex_create when

@@ -15,10 +15,8 @@ constexpr int kGemmThreads = 512;    // 8 waves: fixed 8-way split of K
 constexpr int kKSplit = 8;
 constexpr int kMaxMB = 4;            // 16-row MFMA blocks per GEMM group (<= 64 rows)
 constexpr int kMaxGroups = 48;       // GEMM groups per launch
-constexpr int kAttnTile = 64;        // keys per attention tile (absolute positions)
-constexpr int kAttnChunk = 512;      // keys per split-KV chunk (absolute positions)
-constexpr int kAttnUnits = 32;       // (row, query head) units per attention work item
-constexpr int kAttnThreads = 256;
+constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item
+constexpr int kAttnThreads = 512;    // 8 waves, one key tile each
 
 typedef unsigned short bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -66,9 +64,9 @@ struct GemmArgs {
   int ngroups;
   int K;            // reduction length (multiple of 8 * k-step)
   int N;            // output columns (multiple of 16)
-  const void* a;    // activations [rows][K] (T)
+  const void* a;    // activations [rows][K] (fp32)
   float* out;       // EPI_STORE: [rows][N] fp32; EPI_HEAD: debug logits [seq][N] or null
-  void* act;        // EPI_SWIGLU: [rows][N/2] (T)
+  void* act;        // EPI_SWIGLU: [rows][N/2] (fp32)
   float* hidden;    // EPI_RESID: hidden pool [*][N]
   const RowInfo* rows;
   // EPI_HEAD

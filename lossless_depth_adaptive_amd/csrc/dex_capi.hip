@@ -31,18 +31,16 @@ hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, int, hipS
 template <typename T>
 hipError_t launch_rmsnorm(const float*, const RowInfo*, int, int, const float*, long long, int, int, void*, int,
                           float, hipStream_t);
-template <typename T>
-hipError_t launch_rope_kv(const float*, const RowInfo*, int, int, const float*, const float*, float*, void*, void*,
+hipError_t launch_rope_kv(const float*, const RowInfo*, int, int, const float*, const float*, float*, float*, float*,
                           const ModelDims&, int, int, float, hipStream_t);
-template <typename T>
-hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, int, const float*, const void*, const void*,
-                            float*, void*, const ModelDims&, int, int, int, int, hipStream_t);
+int attn_chunk(int hd);
+hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, int, const float*, const float*, const float*,
+                            float*, float*, const ModelDims&, int, int, int, int, hipStream_t);
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
                         hipStream_t);
 hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
                          float*, const int*, int, int, hipStream_t);
-template <typename T>
-hipError_t launch_promote(const SeqPlan*, int, const int*, const void*, void*, const ModelDims&, hipStream_t);
+hipError_t launch_promote(const SeqPlan*, int, const int*, const float*, float*, const ModelDims&, hipStream_t);
 hipError_t launch_ar_rows(const SeqPlan*, int, RowInfo*, const int*, int, hipStream_t);
 hipError_t launch_ar_commit(const SeqPlan*, int, const int*, const float*, int*, int*, int*, float*, int, int,
                             hipStream_t);
@@ -121,7 +119,7 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
                F = c->d_ffn, V = c->vocab, B = o->max_batch, Cmax = o->max_context;
   const int N = n_x, S = c->n_layers / n_x, P = (1 << N) - 1;
   w.Rmax = std::max(std::max((int)B << (N - 1), kPrefillRows), (int)B);
-  w.nchunk = (int)((Cmax + kAttnChunk - 1) / kAttnChunk);
+  w.nchunk = (int)((Cmax + attn_chunk((int)hd) - 1) / attn_chunk((int)hd));
   const size_t R = w.Rmax;
   w.embed = lay.take(V * d * es);
   w.head = lay.take(V * d * es);
@@ -134,8 +132,8 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.norms = lay.take((2 * L + 1) * d * 4);
   w.cosT = lay.take(Cmax * (hd / 2) * 4);
   w.sinT = lay.take(Cmax * (hd / 2) * 4);
-  w.kvc = lay.take(B * L * 2 * nkv * Cmax * hd * es);
-  w.exb = lay.take(B * P * S * 2 * nkv * hd * es);
+  w.kvc = lay.take(B * L * 2 * nkv * Cmax * hd * 4);      // K/V are fp32
+  w.exb = lay.take(B * P * S * 2 * nkv * hd * 4);
   w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
   w.map = lay.take(B * P * 4);
   w.cand = lay.take(B * P * 4);
@@ -153,11 +151,11 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.rows = lay.take(R * sizeof(RowInfo));
   w.plans = lay.take(B * sizeof(SeqPlan));
   w.items = lay.take(R * sizeof(AttnItem));
-  w.A = lay.take(R * std::max(std::max(d, nq * hd), F) * es);
+  w.A = lay.take(R * std::max(std::max(d, nq * hd), F) * 4);
   w.qkv = lay.take(R * (nq + 2 * nkv) * hd * 4);
   w.q = lay.take(R * nq * hd * 4);
-  w.attn_out = lay.take(R * nq * hd * es);
-  w.act = lay.take(R * F * es);
+  w.attn_out = lay.take(R * nq * hd * 4);
+  w.act = lay.take(R * F * 4);
   w.attn_part = lay.take(R * nq * w.nchunk * (hd + 2) * 4);
   w.head_part = lay.take(R * (V / 16) * 3 * 4);
   w.total = lay.off;
@@ -182,7 +180,8 @@ struct dex_ctx {
   RowInfo* rows;
   SeqPlan* plans;
   AttnItem* items;
-  void *kvc, *exb, *A, *attn_out, *act, *embed, *head;
+  float *kvc, *exb;
+  void *A, *attn_out, *act, *embed, *head;
   // host state
   int nseq = 0;
   std::vector<int> q_, C_, commits_, plen_;
@@ -196,6 +195,16 @@ struct dex_ctx {
   std::string err;
   int last_rows[kMaxN] = {0};
   int last_total = 0;
+  // optional per-class timing with HIP events on the context's stream
+  struct Mark {
+    hipEvent_t a = nullptr, b = nullptr;
+    int cls = 0, launches = 0;
+    double bytes = 0, flops = 0;
+  };
+  bool prof = false;
+  std::vector<Mark> marks;
+  size_t nmarks = 0;
+  dex_kernel_stats stats[DEX_PROF_NCLASS] = {};
 
   void* at(size_t off) { return ws + off; }
 };
@@ -211,6 +220,46 @@ struct dex_ctx {
   } while (0)
 
 namespace {
+
+// Opens a timed region of class `cls`; returns its mark index or -1.
+int prof_begin(dex_ctx* ctx, int cls) {
+  if (!ctx->prof) return -1;
+  if (ctx->nmarks == ctx->marks.size()) {
+    dex_ctx::Mark m;
+    if (hipEventCreate(&m.a) != hipSuccess || hipEventCreate(&m.b) != hipSuccess) return -1;
+    ctx->marks.push_back(m);
+  }
+  dex_ctx::Mark& m = ctx->marks[ctx->nmarks];
+  m.cls = cls;
+  m.launches = 0;
+  m.bytes = m.flops = 0;
+  if (hipEventRecord(m.a, ctx->st) != hipSuccess) return -1;
+  return (int)ctx->nmarks++;
+}
+
+void prof_end(dex_ctx* ctx, int idx, int launches, double bytes, double flops) {
+  if (idx < 0) return;
+  dex_ctx::Mark& m = ctx->marks[idx];
+  m.launches = launches;
+  m.bytes = bytes;
+  m.flops = flops;
+  (void)hipEventRecord(m.b, ctx->st);
+}
+
+// After the stream has been synchronised: fold the marks into the stats.
+void prof_collect(dex_ctx* ctx) {
+  for (size_t i = 0; i < ctx->nmarks; ++i) {
+    dex_ctx::Mark& m = ctx->marks[i];
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, m.a, m.b) != hipSuccess) continue;
+    dex_kernel_stats& st = ctx->stats[m.cls];
+    st.ms += ms;
+    st.launches += m.launches;
+    st.bytes += m.bytes;
+    st.flops += m.flops;
+  }
+  ctx->nmarks = 0;
+}
 
 template <typename T>
 int pack_weights(dex_ctx* ctx, const dex_weights* w) {
@@ -253,7 +302,7 @@ int pack_weights(dex_ctx* ctx, const dex_weights* w) {
 // and prefill rows (layer = lam).
 template <typename T>
 int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& stage_rows, int lam_count,
-               int smul, int nitems, int max_keys) {
+               int smul, int nitems, int max_keys, double attn_bytes = 0, double attn_flops = 0) {
   const ModelDims& D = ctx->D;
   hipStream_t st = ctx->st;
   const int d = D.d, nq = D.nq, nkv = D.nkv, hd = D.hd, F = D.F;
@@ -268,17 +317,35 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
       for (int o = 0; o < cnt; o += 64) glist.push_back(GemmGroup{ctx->at(woff[layer]), r0 + o, std::min(64, cnt - o)});
     }
   };
+  const double es = sizeof(T);
   auto run_gemm = [&](GemmArgs& ga, int epi) -> hipError_t {
+    // algorithmic traffic: each distinct weight matrix once, activations in and out
+    double bytes = 0, flops = 0;
+    const void* lastw = nullptr;
+    for (const GemmGroup& g : glist) {
+      if (g.w != lastw) bytes += (double)ga.N * ga.K * es;
+      lastw = g.w;
+      bytes += (double)g.m * ga.K * 4;
+      bytes += epi == EPI_STORE ? (double)g.m * ga.N * 4 : epi == EPI_RESID ? 2.0 * g.m * ga.N * 4 : (double)g.m * ga.N / 2 * 4;
+      flops += 2.0 * g.m * ga.N * ga.K;
+    }
+    const int mk = prof_begin(ctx, DEX_PROF_GEMM);
+    int launches = 0;
     for (size_t g0 = 0; g0 < glist.size(); g0 += kMaxGroups) {
       ga.ngroups = (int)std::min(glist.size() - g0, (size_t)kMaxGroups);
       for (int i = 0; i < ga.ngroups; ++i) ga.g[i] = glist[g0 + i];
       const hipError_t e = launch_gemm<T>(ga, epi, st);
       if (e != hipSuccess) return e;
+      ++launches;
     }
+    prof_end(ctx, mk, launches, bytes, flops);
     return hipSuccess;
   };
+  const double rowop_bytes = (double)nrows * d * 8;            // one norm: hidden in, activations out
   for (int lam = 0; lam < lam_count; ++lam) {
+    int mk = prof_begin(ctx, DEX_PROF_ROWOPS);
     HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms, 2LL * d, smul, lam, ctx->A, d, D.eps, st));
+    prof_end(ctx, mk, 1, rowop_bytes, 3.0 * nrows * d);
     GemmArgs ga;
     std::memset(&ga, 0, sizeof(ga));
     ga.rows = ctx->rows;
@@ -289,16 +356,23 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     ga.a = ctx->A;
     ga.out = ctx->qkv;
     HIPCHK(run_gemm(ga, EPI_STORE));
-    HIPCHK(launch_rope_kv<T>(ctx->qkv, ctx->rows, 0, nrows, ctx->cosT, ctx->sinT, ctx->q, ctx->kvc, ctx->exb, D, smul,
+    mk = prof_begin(ctx, DEX_PROF_ROWOPS);
+    HIPCHK(launch_rope_kv(ctx->qkv, ctx->rows, 0, nrows, ctx->cosT, ctx->sinT, ctx->q, ctx->kvc, ctx->exb, D, smul,
                              lam, qscale, st));
-    HIPCHK(launch_attention<T>(ctx->items, nitems, ctx->rows, 0, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_part,
-                               ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys, st));
+    prof_end(ctx, mk, 1, (double)nrows * (nq + 2 * nkv) * hd * 4 + (double)nrows * nq * hd * 4 + 2.0 * nrows * nkv * hd * 4,
+             6.0 * nrows * (nq + nkv) * hd);
+    mk = prof_begin(ctx, DEX_PROF_ATTN);
+    HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, 0, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_part,
+                            (float*)ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys, st));
+    prof_end(ctx, mk, 2, attn_bytes, attn_flops);
     groups_for(lam, ctx->wp.wo);
     ga.K = nq * hd;
     ga.N = d;
     ga.a = ctx->attn_out;
     HIPCHK(run_gemm(ga, EPI_RESID));
+    mk = prof_begin(ctx, DEX_PROF_ROWOPS);
     HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms + d, 2LL * d, smul, lam, ctx->A, d, D.eps, st));
+    prof_end(ctx, mk, 1, rowop_bytes, 3.0 * nrows * d);
     groups_for(lam, ctx->wp.wgu);
     ga.K = d;
     ga.N = 2 * F;
@@ -332,7 +406,11 @@ int run_head(dex_ctx* ctx, int nrows) {
   ga.gumbel = ctx->opt.gumbel;
   ga.gumbel_rows = ctx->opt.gumbel_rows;
   ga.part = ctx->head_part;
+  const double es = sizeof(T);
+  const int mk = prof_begin(ctx, DEX_PROF_HEAD);
+  int launches = 1;
   for (int r0 = 0; r0 < nrows; r0 += 64 * kMaxGroups) {
+    ++launches;
     ga.ngroups = 0;
     for (int o = r0; o < std::min(nrows, r0 + 64 * kMaxGroups); o += 64) {
       ga.g[ga.ngroups].w = ctx->head;
@@ -343,6 +421,8 @@ int run_head(dex_ctx* ctx, int nrows) {
     HIPCHK(launch_gemm<T>(ga, EPI_HEAD, st));
   }
   HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, nrows, ctx->rows, D.P, ctx->cand, ctx->margin, st));
+  prof_end(ctx, mk, launches, (double)D.V * D.d * es + (double)nrows * D.d * 4 + (double)nrows * (D.V / 16) * 12 * 2,
+           2.0 * nrows * D.V * D.d);
   return DEX_OK;
 }
 
@@ -413,19 +493,43 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
         max_keys = std::max(max_keys, mk);
       }
     }
+  // Algorithmic attention traffic of one layer slot: each (sequence, stage)
+  // group reads its committed K/V once, each row its explore entries.
+  double attn_bytes = 0, attn_flops = 0;
+  if (ctx->prof) {
+    const double kvrow = 2.0 * ctx->D.nkv * ctx->D.hd * 4;
+    for (int s = 0; s < B; ++s) {
+      if (!live[s]) continue;
+      const int q = ar ? 0 : ctx->q_[s];
+      const int C = ctx->C_[s] + (ar ? 1 : 0);
+      for (int j = 0; j < N; ++j)
+        if (rows_seq_stage[(size_t)s * N + j]) attn_bytes += C * kvrow;
+      for (int n = (1 << q) - 1; n <= (1 << (q + 1)) - 2; ++n) {
+        const int anc = ar ? 0 : __builtin_popcount(n + 1);
+        attn_bytes += anc * kvrow + ctx->D.nq * ctx->D.hd * 8.0;
+        attn_flops += 4.0 * ctx->D.nq * ctx->D.hd * (C + anc);
+      }
+    }
+  }
   hipStream_t st = ctx->st;
+  int mk = prof_begin(ctx, DEX_PROF_LATTICE);
   HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
   if (ar) HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
   else HIPCHK(launch_sched(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
                            ctx->D.P, ctx->opt.decs, st));
+  prof_end(ctx, mk, 1, (double)R * sizeof(RowInfo), 0);
+  mk = prof_begin(ctx, DEX_PROF_ROWOPS);
   HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, stage_tot[0], ctx->hidden, ctx->D.d, st));
+  prof_end(ctx, mk, 1, (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
   std::vector<std::pair<int, int>> stage_rows;
   for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
-  int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys);
+  int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, attn_bytes,
+                         attn_flops);
   if (rc) return rc;
   rc = run_head<T>(ctx, R);
   if (rc) return rc;
+  mk = prof_begin(ctx, DEX_PROF_LATTICE);
   if (ncommit) {
     if (ar) {
       HIPCHK(launch_ar_commit(ctx->plans, B, ctx->cand, ctx->margin, ctx->anchor, ctx->records, ctx->dbg_u, ctx->dbg_m,
@@ -433,11 +537,14 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     } else {
       HIPCHK(launch_commit(ctx->plans, B, ctx->map, ctx->cand, ctx->margin, ctx->freel, ctx->cursor, ctx->anchor,
                            ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P, st));
-      HIPCHK(launch_promote<T>(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
+      HIPCHK(launch_promote(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
     }
     HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));
   }
+  prof_end(ctx, mk, ncommit ? (ar ? 1 : 2) : 0,
+           ar ? 0.0 : 2.0 * ncommit * ctx->L * 2.0 * ctx->D.nkv * ctx->D.hd * 4, 0);
   HIPCHK(hipStreamSynchronize(st));
+  prof_collect(ctx);
   int n = 0;
   for (int s = 0; s < B; ++s) {
     if (!live[s]) continue;
@@ -596,8 +703,8 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->norms = (float*)ctx->at(wp.norms);
   ctx->cosT = (float*)ctx->at(wp.cosT);
   ctx->sinT = (float*)ctx->at(wp.sinT);
-  ctx->kvc = ctx->at(wp.kvc);
-  ctx->exb = ctx->at(wp.exb);
+  ctx->kvc = (float*)ctx->at(wp.kvc);
+  ctx->exb = (float*)ctx->at(wp.exb);
   ctx->hidden = (float*)ctx->at(wp.hidden);
   ctx->map = (int*)ctx->at(wp.map);
   ctx->cand = (int*)ctx->at(wp.cand);
@@ -732,8 +839,27 @@ int dex_last_step_rows(const dex_ctx* ctx, int32_t* rows_per_stage, int32_t* tot
   return DEX_OK;
 }
 
+int dex_profile(dex_ctx* ctx, int32_t enable, dex_kernel_stats* out, int32_t n) {
+  if (!ctx) return DEX_EINVAL;
+  if (ctx->poisoned) return DEX_EHIP;
+  if (out && (n < 0 || n > DEX_PROF_NCLASS)) {
+    ctx->err = "n must be 0..DEX_PROF_NCLASS";
+    return DEX_EINVAL;
+  }
+  if (out) {
+    for (int i = 0; i < n; ++i) out[i] = ctx->stats[i];
+    for (int i = 0; i < DEX_PROF_NCLASS; ++i) ctx->stats[i] = dex_kernel_stats{};
+  }
+  ctx->prof = enable != 0;
+  return DEX_OK;
+}
+
 void dex_destroy(dex_ctx* ctx) {
   if (!ctx) return;
+  for (auto& m : ctx->marks) {
+    if (m.a) (void)hipEventDestroy(m.a);
+    if (m.b) (void)hipEventDestroy(m.b);
+  }
   if (ctx->h_plans) (void)hipHostFree(ctx->h_plans);
   if (ctx->h_records) (void)hipHostFree(ctx->h_records);
   if (ctx->h_items) (void)hipHostFree(ctx->h_items);

@@ -6,11 +6,16 @@
 // stage, Layers(d_{k-1}, d_k], on its node batch; here one launch runs layer
 // slot lambda of every stage that has rows, one weight group per stage).
 //
+// Activations A are fp32. For bf16 weights each A fragment is split in
+// registers into a bf16 high part and a bf16 remainder (a = hi + lo up to
+// 2^-16 relative), and both go through v_mfma_f32_16x16x32_bf16 against the
+// same weight fragment: products are as exact as fp32 activations would
+// give, at no extra weight traffic. fp32 weights use v_mfma_f32_16x16x4_f32.
+//
 // Batch invariance: the value of output (m, n) depends only on row m of A and
 // column n of W, never on how many rows share the launch or where the row
 // sits. The reduction order is fixed by K alone:
-//   * K is cut into k-steps of 32 (bf16) or 16 (fp32) elements, one MFMA
-//     v_mfma_f32_16x16x32_bf16 (or four v_mfma_f32_16x16x4_f32) per step;
+//   * K is cut into k-steps of 32 (bf16) or 16 (fp32) elements;
 //   * the k-steps are split into 8 contiguous ranges, [KS*w/8, KS*(w+1)/8)
 //     for wave w, each accumulated from zero in increasing order;
 //   * the 8 partial sums are added in wave order 0..7.
@@ -26,15 +31,29 @@
 
 namespace dex {
 
+// Per k-step: A fragment of a lane (AW 32-bit words of fp32 activations) and
+// the weight fragment (16 bytes) -> accumulate into acc.
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
   static constexpr int KSTEP = 32;
-  static constexpr int EPL = 8;
-  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
-    bf16x8_t av, bv;
-    __builtin_memcpy(&av, &a, 16);
+  static constexpr int EPL = 8;      // elements per lane per k-step
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a0, const u32x4_t& a1,
+                                             const u32x4_t& b) {
+    bf16x8_t hi, lo, bv;
+    const float f[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
+                        __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
+                        __uint_as_float(a1[2]), __uint_as_float(a1[3])};
+    unsigned short h[8], l[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      h[i] = f2bf(f[i]);
+      l[i] = f2bf(f[i] - bf2f(h[i]));
+    }
+    __builtin_memcpy(&hi, h, 16);
+    __builtin_memcpy(&lo, l, 16);
     __builtin_memcpy(&bv, &b, 16);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, bv, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, bv, acc, 0, 0, 0);
   }
 };
 template <> struct Mfma<float> {
@@ -42,7 +61,8 @@ template <> struct Mfma<float> {
   static constexpr int EPL = 4;
   // Lane l supplies elements kbase + 4*(l/16) + i for i = 0..3; MFMA i reduces
   // over the four lane groups, so the four MFMAs cover the 16 elements.
-  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t& b) {
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t&,
+                                             const u32x4_t& b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
@@ -103,9 +123,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   const int kb = (KS * w) / kKSplit, ke = (KS * (w + 1)) / kKSplit;
 
   const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile * KS * 64 + lane;
-  const T* A = (const T*)args.a + (size_t)G.row0 * K;
+  const float* A = (const float*)args.a + (size_t)G.row0 * K;
   const int col16 = lane & 15;
   const int kq = (lane >> 4) * EPL;
+  constexpr int AW = EPL / 4;          // 16-byte A loads per lane per k-step (fp32 activations)
 
   f32x4_t acc[MB];
   const u32x4_t* ap[MB];
@@ -121,24 +142,28 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   int ks = kb;
   for (; ks + U <= ke; ks += U) {
     u32x4_t bv[U];
-    u32x4_t a[U][MB];
+    u32x4_t a[U][MB][AW];
 #pragma unroll
     for (int u = 0; u < U; ++u) bv[u] = __builtin_nontemporal_load(wp + (size_t)(ks + u) * 64);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) a[u][mb] = av[mb] ? ap[mb][(ks + u) * (KSTEP / EPL)] : zero;
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int x = 0; x < AW; ++x) a[u][mb][x] = av[mb] ? ap[mb][(ks + u) * (KSTEP / 4) + x] : zero;
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) Mfma<T>::mma(acc[mb], a[u][mb], bv[u]);
+      for (int mb = 0; mb < MB; ++mb) Mfma<T>::mma(acc[mb], a[u][mb][0], a[u][mb][AW - 1], bv[u]);
   }
   for (; ks < ke; ++ks) {
     const u32x4_t b = __builtin_nontemporal_load(wp + (size_t)ks * 64);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      const u32x4_t a = av[mb] ? ap[mb][ks * (KSTEP / EPL)] : zero;
-      Mfma<T>::mma(acc[mb], a, b);
+      u32x4_t a[AW];
+#pragma unroll
+      for (int x = 0; x < AW; ++x) a[x] = av[mb] ? ap[mb][ks * (KSTEP / 4) + x] : zero;
+      Mfma<T>::mma(acc[mb], a[0], a[AW - 1], b);
     }
   }
 
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
       }
       const float s = g / (1.0f + expf(-g));
       const int row = G.row0 + rl;
-      ((T*)args.act)[(size_t)row * (args.N >> 1) + tile * 8 + c] = from_f<T>(s * u);
+      ((float*)args.act)[(size_t)row * (args.N >> 1) + tile * 8 + c] = s * u;
     }
   } else {  // EPI_HEAD
     __shared__ float sc[kMaxMB * 16][17];

@@ -143,9 +143,8 @@ __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict
 
 // Copy the anchor path's K/V (node 2^j - 1 holds stage j) into the committed
 // cache at position C. grid = (sequences, layers).
-template <typename T>
 __global__ void promote_kernel(const SeqPlan* __restrict__ plans, const int* __restrict__ promote_src,
-                               const T* __restrict__ exb, T* __restrict__ kvc, ModelDims D) {
+                               const float* __restrict__ exb, float* __restrict__ kvc, ModelDims D) {
   const int s = blockIdx.x, layer = blockIdx.y;
   const SeqPlan pl = plans[s];
   if (!pl.live || !pl.commit) return;
@@ -156,7 +155,7 @@ __global__ void promote_kernel(const SeqPlan* __restrict__ plans, const int* __r
     const int kv = t / (D.nkv * D.hd);
     const int rem = t - kv * D.nkv * D.hd;
     const int h = rem / D.hd, i = rem - h * D.hd;
-    const T v = exb[((((size_t)s * D.P + phys) * D.S + lam) * 2 + kv) * D.nkv * D.hd + (size_t)h * D.hd + i];
+    const float v = exb[((((size_t)s * D.P + phys) * D.S + lam) * 2 + kv) * D.nkv * D.hd + (size_t)h * D.hd + i];
     kvc[((((size_t)s * D.L + layer) * 2 + kv) * D.nkv + h) * (size_t)D.Cmax * D.hd + (size_t)pl.C * D.hd + i] = v;
   }
 }
@@ -237,17 +236,11 @@ hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* ca
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_promote(const SeqPlan* plans, int nseq, const int* promote_src, const void* exb, void* kvc,
+hipError_t launch_promote(const SeqPlan* plans, int nseq, const int* promote_src, const float* exb, float* kvc,
                           const ModelDims& D, hipStream_t st) {
-  hipLaunchKernelGGL(promote_kernel<T>, dim3(nseq, D.L), dim3(256), 0, st, plans, promote_src,
-                     (const T*)exb, (T*)kvc, D);
+  hipLaunchKernelGGL(promote_kernel, dim3(nseq, D.L), dim3(256), 0, st, plans, promote_src, exb, kvc, D);
   return hipGetLastError();
 }
-template hipError_t launch_promote<float>(const SeqPlan*, int, const int*, const void*, void*, const ModelDims&,
-                                          hipStream_t);
-template hipError_t launch_promote<bf16_t>(const SeqPlan*, int, const int*, const void*, void*,
-                                           const ModelDims&, hipStream_t);
 
 hipError_t launch_ar_rows(const SeqPlan* plans, int nseq, RowInfo* rows, const int* anchor_tok, int P,
                           hipStream_t st) {

@@ -24,7 +24,7 @@ __global__ void embed_kernel(const T* __restrict__ E, const RowInfo* __restrict_
 }
 
 // ----------------------------------------------------------------------------
-// RMSNorm: out = x / sqrt(mean(x^2) + eps) * g, rounded to the GEMM input type.
+// RMSNorm: out = x / sqrt(mean(x^2) + eps) * g (fp32 GEMM activations).
 // The weight g belongs to layer stage*smul + lam (smul = 0 gives one layer for
 // every row). Sum of squares: per-thread strided partials, a fixed xor
 // butterfly per wave, then the four waves in order.
@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
                                                       const RowInfo* __restrict__ rows, int row0,
                                                       const float* __restrict__ gbase,
                                                       long long gstride, int smul, int lam,
-                                                      T* __restrict__ out, int d, float eps) {
+                                                      float* __restrict__ out, int d, float eps) {
   const int row = row0 + blockIdx.x;
   const RowInfo& r = rows[row];
   const float* x = hidden + (size_t)r.hrow * d;
@@ -47,8 +47,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   __syncthreads();
   const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
   const float rs = 1.0f / sqrtf(tot / (float)d + eps);
-  T* o = out + (size_t)row * d;
-  for (int i = threadIdx.x; i < d; i += 256) o[i] = from_f<T>(x[i] * rs * g[i]);
+  float* o = out + (size_t)row * d;
+  for (int i = threadIdx.x; i < d; i += 256) o[i] = x[i] * rs * g[i];
 }
 
 // ----------------------------------------------------------------------------
@@ -56,14 +56,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // fp32. Rotation pairs (i, i + hd/2) by angle pos * base^(-2i/hd) from a
 // host-built table. Queries go to qout pre-multiplied by qscale
 // (log2(e)/sqrt(hd), so attention can use exp2). Keys and values are stored
-// in the storage type: into the committed cache at the row's position for
+// in fp32: into the committed cache at the row's position for
 // autoregressive and prefill rows, into the node's explore slot otherwise.
 // ----------------------------------------------------------------------------
-template <typename T>
 __global__ void rope_kv_kernel(const float* __restrict__ qkv, const RowInfo* __restrict__ rows,
                                int row0, const float* __restrict__ cosT,
                                const float* __restrict__ sinT, float* __restrict__ qout,
-                               T* __restrict__ kvc, T* __restrict__ exb, ModelDims D, int smul,
+                               float* __restrict__ kvc, float* __restrict__ exb, ModelDims D, int smul,
                                int lam, float qscale) {
   const int row = row0 + blockIdx.x;
   const RowInfo& r = rows[row];
@@ -91,15 +90,15 @@ __global__ void rope_kv_kernel(const float* __restrict__ qkv, const RowInfo* __r
       o1 = x1 * c - x2 * s;
       o2 = x2 * c + x1 * s;
     }
-    T* dst;
+    float* dst;
     if (r.kv_commit)
       dst = kvc + ((((size_t)r.seq * D.L + layer) * 2 + kv) * D.nkv + hh) * (size_t)D.Cmax * hd +
             (size_t)r.pos * hd;
     else
       dst = exb + ((((size_t)r.seq * D.P + r.phys) * D.S + lam) * 2 + kv) * (size_t)D.nkv * hd +
             (size_t)hh * hd;
-    dst[i] = from_f<T>(o1);
-    dst[i + half] = from_f<T>(o2);
+    dst[i] = o1;
+    dst[i + half] = o2;
   }
 }
 
@@ -108,65 +107,77 @@ __global__ void rope_kv_kernel(const float* __restrict__ qkv, const RowInfo* __r
 // binary expansion lets ancestry, KV entries and attention masks be indexed
 // consistently). A row attends to the committed cache [0, ncommit) and to the
 // explore-buffer entries of its ancestors at positions ncommit.. (its own
-// entry last). Keys are visited in absolute-position tiles of 64 and split-KV
-// chunks of 512 positions, whichever buffer holds them, so the reduction order
-// of a row depends only on its position. All rows of a work item share one
-// sequence and layer: committed K/V tiles are staged in LDS once for all of
-// them.
+// entry last). All rows of a work item share one sequence and layer. K and V
+// are fp32.
 //
-// Per (row, query head) unit and tile: s_j = q . k_j (sequential over the head
-// dimension), running max m, p_j = 2^(s_j - m), l = l*2^(m_old - m) +
-// butterfly-sum p, acc = acc*2^(m_old - m) + sum_j p_j v_j (j increasing).
-// grid = (items, kv heads, chunks), block = 256 (4 waves).
+// Reduction order, a function of key positions only (so a lattice node and
+// the same context decoded autoregressively agree bit for bit). With
+// HS = hd/64 lane groups per key and TK = 64/HS keys per tile:
+//   tile  = TK absolute positions [TK t, TK t + TK): lane group g of key j
+//           forms the partial dot product over dims [64g, 64g+64) with four
+//           interleaved sums added as (s0+s1)+(s2+s3), the groups then added
+//           in order; m = max; p_j = 2^(s_j - m); l = xor-butterfly sum of p_j;
+//           acc = sum_j p_j v_j in j order (even and odd j in two chains);
+//   chunk = 8 tiles, merged in tile order;
+//   row   = chunks merged in chunk order by attn_combine_kernel.
+// Queries arrive pre-multiplied by log2(e)/sqrt(hd).
+//
+// grid = (items, kv heads, chunks), block = 512: wave w owns tile 8c+w. The
+// wave loads its committed K rows and V columns into registers once and reuses
+// them for every (row, query head) unit of the item; explore entries are read
+// from the node slots directly.
 // ----------------------------------------------------------------------------
-template <typename T> struct Pair;
-template <> struct Pair<bf16_t> {
-  static constexpr int PAD = 2;
-  __device__ __forceinline__ static void ld(const bf16_t* p, int d, float& a, float& b) {
-    const unsigned w = *(const unsigned*)(p + d);
-    a = __uint_as_float(w << 16);
-    b = __uint_as_float(w & 0xFFFF0000u);
-  }
-};
-template <> struct Pair<float> {
-  static constexpr int PAD = 1;
-  __device__ __forceinline__ static void ld(const float* p, int d, float& a, float& b) {
-    a = p[d];
-    b = p[d + 1];
-  }
-};
+constexpr int kAttnWaves = kAttnThreads / 64;
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+// Sum over each group of `width` lanes (xor butterfly, fixed order).
+__device__ __forceinline__ float group_sum(float v, int width) {
+  for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   return v;
 }
 
-template <typename T, int HD>
+template <int HD> struct AttnGeom {
+  static constexpr int HS = HD / 64;              // lane groups per key
+  static constexpr int TK = 64 / HS;              // keys per tile
+  static constexpr int CHUNK = kAttnWaves * TK;   // keys per chunk
+};
+
+// Partial q . k over 64 dims held as 16 float4 words.
+template <typename Fetch>
+__device__ __forceinline__ float dot64(const float* __restrict__ qv, Fetch fetch) {
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const f32x4_t k = fetch(i);
+    s[0] = fmaf(qv[4 * i], k[0], s[0]);
+    s[1] = fmaf(qv[4 * i + 1], k[1], s[1]);
+    s[2] = fmaf(qv[4 * i + 2], k[2], s[2]);
+    s[3] = fmaf(qv[4 * i + 3], k[3], s[3]);
+  }
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
+template <int HD>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows,
-    const float* __restrict__ q, const T* __restrict__ kvc, const T* __restrict__ exb,
+    const float* __restrict__ q, const float* __restrict__ kvc, const float* __restrict__ exb,
     float* __restrict__ part, ModelDims D, int lam, int smul, int nchunk) {
-  constexpr int LD = HD + Pair<T>::PAD;           // LDS row stride (elements)
-  constexpr int UPW = kAttnUnits / 4;            // units per wave
-  constexpr int DPL = HD / 64;                   // output dims per lane
-  __shared__ T Ks[kAttnTile * LD];
-  __shared__ T Vs[kAttnTile * LD];
+  using G = AttnGeom<HD>;
+  constexpr int HS = G::HS, TK = G::TK, HP = HD + 2;
   __shared__ float qs[kAttnUnits][HD];
+  __shared__ float red[kAttnWaves][kAttnUnits][HP];
 
   const AttnItem it = items[blockIdx.x];
   const int h = blockIdx.y, c = blockIdx.z;
-  const int pb = c * kAttnChunk;
+  const int pb = c * G::CHUNK;
   if (pb >= it.max_keys) return;
-  const int pe = min(pb + kAttnChunk, it.max_keys);
   const int rep = D.nq / D.nkv;
   const int units = it.nrows * rep;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int seq = rows[it.row0].seq;
-
   int maxc = 0;
   for (int i = 0; i < it.nrows; ++i) maxc = max(maxc, rows[it.row0 + i].ncommit);
 
@@ -178,93 +189,128 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 
   const int layer = it.stage * smul + lam;
   const size_t cstride = (size_t)D.Cmax * HD;
-  const T* kc = kvc + (((size_t)seq * D.L + layer) * 2 + 0) * D.nkv * cstride + h * cstride;
-  const T* vc = kvc + (((size_t)seq * D.L + layer) * 2 + 1) * D.nkv * cstride + h * cstride;
-  const size_t xs_slot = (size_t)D.S * 2 * D.nkv * HD;   // explore elements per node slot
-  const T* xk = exb + (size_t)seq * D.P * xs_slot + (size_t)lam * 2 * D.nkv * HD + (size_t)h * HD;
-  const T* xv = xk + (size_t)D.nkv * HD;
+  const float* kc = kvc + (((size_t)seq * D.L + layer) * 2 + 0) * D.nkv * cstride + h * cstride;
+  const float* vc = kvc + (((size_t)seq * D.L + layer) * 2 + 1) * D.nkv * cstride + h * cstride;
+  const size_t xs_slot = (size_t)D.S * 2 * D.nkv * HD;   // explore floats per node slot
+  const float* xk = exb + (size_t)seq * D.P * xs_slot + (size_t)lam * 2 * D.nkv * HD + (size_t)h * HD;
+  const float* xv = xk + (size_t)D.nkv * HD;
 
-  float m[UPW], l[UPW], acc[UPW][DPL];
+  // This wave's tile: key j = lane % TK, dims [64 g, 64 g + 64) with g = lane / TK.
+  const int p0 = pb + TK * w;
+  const int j = lane % TK, g = lane / TK;
+  const int p = p0 + j;
+  f32x4_t kw[16];
+  float vw[TK][HS];
+  const int nk = max(0, min(TK, maxc - p0));
+  if (j < nk) {
+    const f32x4_t* kr = (const f32x4_t*)(kc + (size_t)p * HD + 64 * g);
 #pragma unroll
-  for (int i = 0; i < UPW; ++i) {
-    m[i] = -INFINITY;
-    l[i] = 0.f;
+    for (int i = 0; i < 16; ++i) kw[i] = kr[i];
+  } else {
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) acc[i][t] = 0.f;
+    for (int i = 0; i < 16; ++i) kw[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
+#pragma unroll
+  for (int jj = 0; jj < TK; ++jj)
+#pragma unroll
+    for (int e = 0; e < HS; ++e) vw[jj][e] = jj < nk ? vc[(size_t)(p0 + jj) * HD + lane * HS + e] : 0.f;
+  __syncthreads();
 
-  for (int p0 = pb; p0 < pe; p0 += kAttnTile) {
-    __syncthreads();
-    // Stage committed keys/values of this tile (32-bit words).
-    const int nld = max(0, min(kAttnTile, maxc - p0));
-    constexpr int WPR = HD * (int)sizeof(T) / 4;   // 32-bit words per row
-    for (int t = threadIdx.x; t < nld * WPR; t += kAttnThreads) {
-      const int j = t / WPR, wd = t - j * WPR;
-      const unsigned* ks = (const unsigned*)(kc + (size_t)(p0 + j) * HD);
-      const unsigned* vs = (const unsigned*)(vc + (size_t)(p0 + j) * HD);
-      ((unsigned*)(Ks + j * LD))[wd] = ks[wd];
-      ((unsigned*)(Vs + j * LD))[wd] = vs[wd];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < UPW; ++i) {
-      const int u = w + 4 * i;
-      if (u >= units) continue;
-      const RowInfo& R = rows[it.row0 + u / rep];
-      const int lim = R.ncommit + R.n_anc;
-      if (p0 >= lim) continue;
-      const int p = p0 + lane;
-      float s = -INFINITY;
-      if (p < lim) {
-        const T* kp = (p < R.ncommit) ? (Ks + lane * LD) : (xk + (size_t)R.anc[p - R.ncommit] * xs_slot);
-        float acc_s = 0.f;
-        for (int dd = 0; dd < HD; dd += 2) {
-          float k0, k1;
-          Pair<T>::ld(kp, dd, k0, k1);
-          acc_s = fmaf(qs[u][dd], k0, acc_s);
-          acc_s = fmaf(qs[u][dd + 1], k1, acc_s);
-        }
-        s = acc_s;
+  for (int u = 0; u < units; ++u) {
+    const RowInfo& R = rows[it.row0 + u / rep];
+    const int lim = R.ncommit + R.n_anc;
+    float* rd = red[w][u];
+    if (p0 >= lim) {
+      if (lane == 0) {
+        rd[HD] = -INFINITY;
+        rd[HD + 1] = 0.f;
       }
-      const float mt = wave_max(s);
-      const float mn = fmaxf(m[i], mt);
-      const float alpha = exp2f(m[i] - mn);
-      const float pj = (p < lim) ? exp2f(s - mn) : 0.f;
-      l[i] = l[i] * alpha + wave_sum(pj);
 #pragma unroll
-      for (int t = 0; t < DPL; ++t) acc[i][t] *= alpha;
-      const int nv = min(kAttnTile, lim - p0);
-      for (int jj = 0; jj < nv; ++jj) {
+      for (int e = 0; e < HS; ++e) rd[lane * HS + e] = 0.f;
+      continue;
+    }
+    const float* qv = qs[u] + 64 * g;
+    float sp = 0.f;
+    if (p < R.ncommit) {
+      sp = dot64(qv, [&](int i) { return kw[i]; });
+    } else if (p < lim) {
+      const f32x4_t* xr = (const f32x4_t*)(xk + (size_t)R.anc[p - R.ncommit] * xs_slot + 64 * g);
+      sp = dot64(qv, [&](int i) { return xr[i]; });
+    }
+    float s = sp;
+    if (HS == 2) {
+      const float other = __shfl_xor(sp, 32);
+      s = g == 0 ? sp + other : other + sp;
+    }
+    if (p >= lim) s = -INFINITY;
+    const float m = wave_max(s);
+    const float pj = p < lim ? exp2f(s - m) : 0.f;
+    const float l = group_sum(pj, TK);
+    float a0[HS], a1[HS];
+#pragma unroll
+    for (int e = 0; e < HS; ++e) a0[e] = a1[e] = 0.f;
+    const int nv = min(TK, lim - p0);
+#pragma unroll
+    for (int jj = 0; jj < TK; ++jj) {
+      if (jj < nv) {
         const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj));
         const int pp = p0 + jj;
-        const T* vp = (pp < R.ncommit) ? (Vs + jj * LD) : (xv + (size_t)R.anc[pp - R.ncommit] * xs_slot);
+        float v[HS];
+        if (pp < R.ncommit) {
 #pragma unroll
-        for (int t = 0; t < DPL; ++t) acc[i][t] = fmaf(pv, to_f<T>(vp[lane + 64 * t]), acc[i][t]);
+          for (int e = 0; e < HS; ++e) v[e] = vw[jj][e];
+        } else {
+          const float* xr = xv + (size_t)R.anc[pp - R.ncommit] * xs_slot + lane * HS;
+#pragma unroll
+          for (int e = 0; e < HS; ++e) v[e] = xr[e];
+        }
+#pragma unroll
+        for (int e = 0; e < HS; ++e) {
+          if (jj & 1) a1[e] = fmaf(pv, v[e], a1[e]);
+          else a0[e] = fmaf(pv, v[e], a0[e]);
+        }
       }
-      m[i] = mn;
+    }
+#pragma unroll
+    for (int e = 0; e < HS; ++e) rd[lane * HS + e] = a0[e] + a1[e];
+    if (lane == 0) {
+      rd[HD] = m;
+      rd[HD + 1] = l;
     }
   }
-#pragma unroll
-  for (int i = 0; i < UPW; ++i) {
-    const int u = w + 4 * i;
-    if (u >= units) continue;
+  __syncthreads();
+  // Merge the chunk's tiles in tile order; wave w takes units w, w+8, ...
+  for (int u = w; u < units; u += kAttnWaves) {
     const int row = it.row0 + u / rep, qh = h * rep + u % rep;
     const RowInfo& R = rows[row];
     if (pb >= R.ncommit + R.n_anc) continue;
-    float* o = part + (((size_t)row * D.nq + qh) * nchunk + c) * (HD + 2);
+    float M = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) o[lane + 64 * t] = acc[i][t];
+    for (int t = 0; t < kAttnWaves; ++t) M = fmaxf(M, red[t][u][HD]);
+    float Ls = 0.f, o[HS];
+#pragma unroll
+    for (int e = 0; e < HS; ++e) o[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < kAttnWaves; ++t) {
+      const float f = exp2f(red[t][u][HD] - M);
+      Ls = fmaf(red[t][u][HD + 1], f, Ls);
+#pragma unroll
+      for (int e = 0; e < HS; ++e) o[e] = fmaf(red[t][u][lane * HS + e], f, o[e]);
+    }
+    float* dst = part + (((size_t)row * D.nq + qh) * nchunk + c) * HP;
+#pragma unroll
+    for (int e = 0; e < HS; ++e) dst[lane * HS + e] = o[e];
     if (lane == 0) {
-      o[HD] = m[i];
-      o[HD + 1] = l[i];
+      dst[HD] = M;
+      dst[HD + 1] = Ls;
     }
   }
 }
 
 // Combine the split-KV chunks of a (row, head) in chunk order; one wave each.
-template <typename T, int HD>
+template <int HD>
 __global__ void attn_combine_kernel(const RowInfo* __restrict__ rows, int row0, int nrows,
-                                    const float* __restrict__ part, T* __restrict__ out, int nq,
+                                    const float* __restrict__ part, float* __restrict__ out, int nq,
                                     int nchunk) {
   constexpr int DPL = HD / 64;
   const int unit = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
@@ -273,7 +319,7 @@ __global__ void attn_combine_kernel(const RowInfo* __restrict__ rows, int row0, 
   const int row = row0 + unit / nq, qh = unit % nq;
   const RowInfo& R = rows[row];
   const int lim = R.ncommit + R.n_anc;
-  const int nc = (lim + kAttnChunk - 1) / kAttnChunk;
+  const int nc = (lim + AttnGeom<HD>::CHUNK - 1) / AttnGeom<HD>::CHUNK;
   const float* base = part + ((size_t)row * nq + qh) * nchunk * (HD + 2);
   float M = -INFINITY;
   for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * (HD + 2) + HD]);
@@ -285,12 +331,12 @@ __global__ void attn_combine_kernel(const RowInfo* __restrict__ rows, int row0, 
     const float f = exp2f(pc[HD] - M);
     Lsum = fmaf(pc[HD + 1], f, Lsum);
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) o[t] = fmaf(pc[lane + 64 * t], f, o[t]);
+    for (int t = 0; t < DPL; ++t) o[t] = fmaf(pc[lane * DPL + t], f, o[t]);
   }
   const float inv = 1.0f / Lsum;
-  T* dst = out + ((size_t)row * nq + qh) * HD;
+  float* dst = out + ((size_t)row * nq + qh) * HD;
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) dst[lane + 64 * t] = from_f<T>(o[t] * inv);
+  for (int t = 0; t < DPL; ++t) dst[lane * DPL + t] = o[t] * inv;
 }
 
 // ----------------------------------------------------------------------------
@@ -310,55 +356,49 @@ hipError_t launch_rmsnorm(const float* hidden, const RowInfo* rows, int row0, in
                           float eps, hipStream_t st) {
   if (nrows == 0) return hipSuccess;
   hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(nrows), dim3(256), 0, st, hidden, rows, row0, gbase,
-                     gstride, smul, lam, (T*)out, d, eps);
+                     gstride, smul, lam, (float*)out, d, eps);
   return hipGetLastError();
 }
 
-template <typename T>
 hipError_t launch_rope_kv(const float* qkv, const RowInfo* rows, int row0, int nrows, const float* cosT,
-                          const float* sinT, float* qout, void* kvc, void* exb, const ModelDims& D,
+                          const float* sinT, float* qout, float* kvc, float* exb, const ModelDims& D,
                           int smul, int lam, float qscale, hipStream_t st) {
   if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_kv_kernel<T>, dim3(nrows), dim3(256), 0, st, qkv, rows, row0, cosT, sinT,
-                     qout, (T*)kvc, (T*)exb, D, smul, lam, qscale);
+  hipLaunchKernelGGL(rope_kv_kernel, dim3(nrows), dim3(256), 0, st, qkv, rows, row0, cosT, sinT, qout, kvc, exb, D,
+                     smul, lam, qscale);
   return hipGetLastError();
 }
 
-template <typename T>
+int attn_chunk(int hd) { return hd == 128 ? AttnGeom<128>::CHUNK : AttnGeom<64>::CHUNK; }
+
 hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int row0, int nrows,
-                            const float* q, const void* kvc, const void* exb, float* part, void* out,
+                            const float* q, const float* kvc, const float* exb, float* part, float* out,
                             const ModelDims& D, int lam, int smul, int nchunk, int max_keys, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
-  const int nc = (max_keys + kAttnChunk - 1) / kAttnChunk;
+  const int nc = (max_keys + attn_chunk(D.hd) - 1) / attn_chunk(D.hd);
   dim3 grid(nitems, D.nkv, nc);
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_kernel<T, 128>), grid, dim3(kAttnThreads), 0, st, items, rows, q,
-                       (const T*)kvc, (const T*)exb, part, D, lam, smul, nchunk);
+    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D,
+                       lam, smul, nchunk);
   else
-    hipLaunchKernelGGL((attn_kernel<T, 64>), grid, dim3(kAttnThreads), 0, st, items, rows, q,
-                       (const T*)kvc, (const T*)exb, part, D, lam, smul, nchunk);
+    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D,
+                       lam, smul, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = nrows * D.nq, wpb = 4;
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<T, 128>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0,
-                       st, rows, row0, nrows, part, (T*)out, D.nq, nchunk);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0,
+                       st, rows, row0, nrows, part, out, D.nq, nchunk);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<T, 64>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0,
-                       st, rows, row0, nrows, part, (T*)out, D.nq, nchunk);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0,
+                       st, rows, row0, nrows, part, out, D.nq, nchunk);
   return hipGetLastError();
 }
 
 #define DEX_INST(T)                                                                                  \
   template hipError_t launch_embed<T>(const void*, const RowInfo*, int, int, float*, int, hipStream_t); \
   template hipError_t launch_rmsnorm<T>(const float*, const RowInfo*, int, int, const float*, long long, \
-                                        int, int, void*, int, float, hipStream_t);                   \
-  template hipError_t launch_rope_kv<T>(const float*, const RowInfo*, int, int, const float*,         \
-                                        const float*, float*, void*, void*, const ModelDims&, int, int, \
-                                        float, hipStream_t);                                          \
-  template hipError_t launch_attention<T>(const AttnItem*, int, const RowInfo*, int, int, const float*, \
-                                          const void*, const void*, float*, void*, const ModelDims&,  \
-                                          int, int, int, int, hipStream_t);
+                                        int, int, void*, int, float, hipStream_t);
 DEX_INST(float)
 DEX_INST(bf16_t)
 

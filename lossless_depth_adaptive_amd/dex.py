@@ -17,7 +17,8 @@ DEX_OK, DEX_EINVAL, DEX_ENOSPC, DEX_ESTATE, DEX_EHIP = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GREEDY, SAMPLE = 0, 1
 EXPORTED = ["dex_workspace_bytes", "dex_create", "dex_prefill", "dex_step", "dex_ar_step",
-            "dex_debug_anchor", "dex_last_step_rows", "dex_destroy", "dex_last_error"]
+            "dex_debug_anchor", "dex_last_step_rows", "dex_profile", "dex_destroy", "dex_last_error"]
+PROF_CLASSES = ["gemm", "attention", "exit_head", "row_ops", "lattice"]
 
 
 class ModelConfig(ctypes.Structure):
@@ -51,6 +52,11 @@ class Commit(ctypes.Structure):
                 ("branch", ctypes.c_int32), ("layers", ctypes.c_int32)]
 
 
+class KernelStats(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double), ("launches", ctypes.c_int64), ("bytes", ctypes.c_double),
+                ("flops", ctypes.c_double)]
+
+
 class DexError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"dex error {code}: {msg}")
@@ -77,6 +83,7 @@ def load_library() -> ctypes.CDLL:
     lib.dex_ar_step.argtypes = [vp, P(Commit), i32, P(i32)]
     lib.dex_debug_anchor.argtypes = [vp, i32, P(i32), P(ctypes.c_float), P(ctypes.c_float)]
     lib.dex_last_step_rows.argtypes = [vp, P(i32), P(i32)]
+    lib.dex_profile.argtypes = [vp, i32, P(KernelStats), i32]
     lib.dex_destroy.argtypes = [vp]
     lib.dex_destroy.restype = None
     lib.dex_last_error.argtypes = [vp]
@@ -194,6 +201,15 @@ class Dex:
         t = ctypes.c_int32(0)
         self._check(self.lib.dex_last_step_rows(self.ctx, r, ctypes.byref(t)))
         return list(r), t.value
+
+    def profile(self, enable: bool = True) -> dict:
+        """Turn per-class event timing on/off; returns (and resets) the stats
+        gathered since the previous call, keyed by class name."""
+        n = len(PROF_CLASSES)
+        st = (KernelStats * n)()
+        self._check(self.lib.dex_profile(self.ctx, int(bool(enable)), st, n))
+        return {PROF_CLASSES[i]: dict(ms=st[i].ms, launches=st[i].launches, bytes=st[i].bytes,
+                                      flops=st[i].flops) for i in range(n)}
 
     def close(self):
         if getattr(self, "ctx", None) is not None and self.ctx.value:
