@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--no-ar", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gemm_llama7b_x4_greedy.json"),
                     help="counter-derived HBM bytes per GEMM launch (from rocprofv3 --pmc runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the timed rounds (a known-size "
+                         "reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the DEX lattice step runs every explorer on a single device "
@@ -134,6 +137,14 @@ def main():
     ctx.prefill(prompts)
     t_prefill = time.perf_counter() - t0
     log(f"[gpu] prefill of {w.batch} x {w.prompt_len} tokens: {t_prefill * 1e3:.1f} ms")
+    if args.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[gpu] copy calibration: 1 GiB read + 1 GiB written")
     for _ in range(args.warmup):
         ctx.step()
     ctx.profile(True)

@@ -51,25 +51,58 @@ struct SeqPlan {
   int base[kMaxN];  // first row index of this sequence's rows at each stage
 };
 
-struct GemmGroup {
-  const void* w;    // packed weights of this group
-  int row0;         // first row (activations A[row0 ...], row info rows[row0 ...])
-  int m;            // rows, 1..64
+struct ModelDims {
+  int L, d, nq, nkv, hd, F, V;
+  int S;            // layers per stage
+  int N;            // explorers
+  int P;            // lattice node slots per sequence (2^N - 1)
+  int B;            // max sequences
+  int Cmax;         // max context
+  float eps;
 };
 
-enum Epilogue { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+struct GemmGroup {
+  const void* w;        // packed weights of this group
+  const float* gamma;   // EPI_RESID: RMSNorm weight of the row's next consumer (null: none)
+  int row0;             // first row (activations A[row0 ...], row info rows[row0 ...])
+  int m;                // rows, 1..64
+};
 
+enum Epilogue { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+
+// Residual-stream buffers, indexed by a row's hrow: the fp32 residual h, its
+// per-16-column sums of squares, and h multiplied elementwise by the RMSNorm
+// weight of its next consumer (xn: next QKV or gate/up GEMM; xh: the exit
+// head). A normalising GEMM reads xn or xh and scales its outputs by
+// rstd = 1/sqrt(mean(h^2) + eps), so RMSNorm costs no pass of its own.
 struct GemmArgs {
   GemmGroup g[kMaxGroups];
   int ngroups;
-  int K;            // reduction length (multiple of 8 * k-step)
+  int K;            // reduction length (multiple of the k-step)
   int N;            // output columns (multiple of 16)
-  const void* a;    // activations [rows][K] (fp32)
-  float* out;       // EPI_STORE: [rows][N] fp32; EPI_HEAD: debug logits [seq][N] or null
-  void* act;        // EPI_SWIGLU: [rows][N/2] (fp32)
-  float* hidden;    // EPI_RESID: hidden pool [*][N]
   const RowInfo* rows;
+  const void* a;    // EPI_RESID: activations [rows][K] (fp32)
+  const float* xin; // normalising epilogues: xn or xh, [*][K]
+  float* hidden;    // EPI_RESID: residual [*][N]
+  float* ssq;       // [*][d/16]: read by normalising epilogues, written by EPI_RESID
+  float* xn;        // EPI_RESID: h * gamma of the next consumer
+  float* xh;        // EPI_RESID: h * final-norm weight (when write_xh)
+  const float* gfinal;
+  int write_xh;
+  float eps;
+  // EPI_QKV
+  ModelDims dims;
+  const float* cosT;
+  const float* sinT;
+  float* qout;      // [rows][nq][hd], pre-scaled by qscale
+  float* kvc;       // committed K/V
+  float* exb;       // explore-buffer K/V
+  int smul, lam;    // layer = stage * smul + lam
+  float qscale;
+  // EPI_SWIGLU
+  void* act;        // [rows][N/2] (fp32)
   // EPI_HEAD
+  float* out;       // debug logits [seq][N] or null
   int mode;         // 0 greedy, 1 sample
   float tau;
   const float* gumbel;   // [batch][gumbel_rows][N]
@@ -82,16 +115,6 @@ struct AttnItem {
   int nrows;        // rows (all of one sequence and one layer)
   int stage;        // explorer of the rows; layer = stage * smul + lam
   int max_keys;     // max over the rows of ncommit + n_anc
-};
-
-struct ModelDims {
-  int L, d, nq, nkv, hd, F, V;
-  int S;            // layers per stage
-  int N;            // explorers
-  int P;            // lattice node slots per sequence (2^N - 1)
-  int B;            // max sequences
-  int Cmax;         // max context
-  float eps;
 };
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((unsigned)v) << 16); }

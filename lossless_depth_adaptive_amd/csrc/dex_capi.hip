@@ -22,22 +22,18 @@
 
 namespace dex {
 template <typename T>
-hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, int, int, int, int, hipStream_t);
+hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, int, int, int, int, int, hipStream_t);
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
 hipError_t launch_head_reduce(const float*, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
-hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, int, hipStream_t);
-template <typename T>
-hipError_t launch_rmsnorm(const float*, const RowInfo*, int, int, const float*, long long, int, int, void*, int,
-                          float, hipStream_t);
-hipError_t launch_rope_kv(const float*, const RowInfo*, int, int, const float*, const float*, float*, float*, float*,
-                          const ModelDims&, int, int, float, hipStream_t);
+hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
-hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, int, const float*, const float*, const float*,
+hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const float*, const float*, const float*,
                             float*, float*, const ModelDims&, int, int, int, int, hipStream_t);
+template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
-                        hipStream_t);
+                        const void*, float*, float*, float*, const float*, int, hipStream_t);
 hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
                          float*, const int*, int, int, hipStream_t);
 hipError_t launch_promote(const SeqPlan*, int, const int*, const float*, float*, const ModelDims&, hipStream_t);
@@ -65,9 +61,9 @@ struct Layout {
 
 // Every buffer of the workspace, as byte offsets.
 struct WsPlan {
-  size_t embed, head, norms, cosT, sinT, kvc, exb, hidden;
+  size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh;
   size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
-  size_t rows, plans, items, A, qkv, q, attn_out, act, attn_part, head_part;
+  size_t rows, plans, items, q, attn_out, act, attn_part, head_part, ssq;
   std::vector<size_t> wqkv, wo, wgu, wdown;
   size_t total;
   int Rmax, nchunk;
@@ -135,6 +131,8 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.kvc = lay.take(B * L * 2 * nkv * Cmax * hd * 4);      // K/V are fp32
   w.exb = lay.take(B * P * S * 2 * nkv * hd * 4);
   w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
+  w.xn = lay.take((B * P + kPrefillRows) * d * 4);
+  w.xh = lay.take((B * P + kPrefillRows) * d * 4);
   w.map = lay.take(B * P * 4);
   w.cand = lay.take(B * P * 4);
   w.margin = lay.take(B * P * 4);
@@ -151,9 +149,8 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.rows = lay.take(R * sizeof(RowInfo));
   w.plans = lay.take(B * sizeof(SeqPlan));
   w.items = lay.take(R * sizeof(AttnItem));
-  w.A = lay.take(R * std::max(std::max(d, nq * hd), F) * 4);
-  w.qkv = lay.take(R * (nq + 2 * nkv) * hd * 4);
   w.q = lay.take(R * nq * hd * 4);
+  w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
   w.attn_out = lay.take(R * nq * hd * 4);
   w.act = lay.take(R * F * 4);
   w.attn_part = lay.take(R * nq * w.nchunk * (hd + 2) * 4);
@@ -175,13 +172,13 @@ struct dex_ctx {
   char* ws;
   WsPlan wp;
   // device views
-  float *norms, *cosT, *sinT, *hidden, *margin, *dbg_m, *dbg_logits, *qkv, *q, *attn_part, *head_part;
+  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q, *attn_part, *head_part, *ssq;
   int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
   RowInfo* rows;
   SeqPlan* plans;
   AttnItem* items;
   float *kvc, *exb;
-  void *A, *attn_out, *act, *embed, *head;
+  void *attn_out, *act, *embed, *head;
   // host state
   int nseq = 0;
   std::vector<int> q_, C_, commits_, plen_;
@@ -267,13 +264,13 @@ int pack_weights(dex_ctx* ctx, const dex_weights* w) {
   hipStream_t st = ctx->st;
   for (int l = 0; l < L; ++l) {
     HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wqkv[l]), w->wq[l], w->wk[l], w->wv[l], nq * hd, nkv * hd, nkv * hd, d, 1,
-                          (nq + 2 * nkv) * hd, st));
-    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wo[l]), w->wo[l], nullptr, nullptr, d, 0, 0, nq * hd, 0, d, st));
-    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wgu[l]), w->w_gate[l], w->w_up[l], nullptr, F, F, 0, d, 2, 2 * F, st));
-    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wdown[l]), w->w_down[l], nullptr, nullptr, d, 0, 0, F, 0, d, st));
+                          (nq + 2 * nkv) * hd, hd, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wo[l]), w->wo[l], nullptr, nullptr, d, 0, 0, nq * hd, 0, d, hd, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wgu[l]), w->w_gate[l], w->w_up[l], nullptr, F, F, 0, d, 2, 2 * F, hd, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wdown[l]), w->w_down[l], nullptr, nullptr, d, 0, 0, F, 0, d, hd, st));
   }
   const void* hsrc = ctx->cfg.tied_head ? w->tok_embed : w->lm_head;
-  HIPCHK(launch_pack<T>(ctx->head, hsrc, nullptr, nullptr, V, 0, 0, d, 0, V, st));
+  HIPCHK(launch_pack<T>(ctx->head, hsrc, nullptr, nullptr, V, 0, 0, d, 0, V, hd, st));
   HIPCHK(hipMemcpyAsync(ctx->embed, w->tok_embed, (size_t)V * d * sizeof(T), hipMemcpyDeviceToDevice, st));
   // Norm weights to fp32, through the host (2L+1 vectors of d).
   std::vector<T> tmp(d);
@@ -297,27 +294,34 @@ int pack_weights(dex_ctx* ctx, const dex_weights* w) {
 }
 
 // One pass of the layer stack over `nrows` rows already set up in ctx->rows.
-// groups_by_stage: for each stage, [row0, count) of its rows; lam_count layer
+// stage_rows: for each stage, [row0, count) of its rows; lam_count layer
 // slots; smul = S for lattice rows (layer = stage*S + lam), 0 for autoregressive
-// and prefill rows (layer = lam).
+// and prefill rows (layer = lam). Per layer slot: QKV GEMM (fused RMSNorm,
+// RoPE, K/V write) -> attention -> O GEMM (+ residual) -> gate/up GEMM (fused
+// RMSNorm, SwiGLU) -> down GEMM (+ residual).
 template <typename T>
 int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& stage_rows, int lam_count,
-               int smul, int nitems, int max_keys, double attn_bytes = 0, double attn_flops = 0) {
+               int smul, int nitems, int max_keys, bool want_xh, double attn_bytes = 0, double attn_flops = 0) {
   const ModelDims& D = ctx->D;
   hipStream_t st = ctx->st;
   const int d = D.d, nq = D.nq, nkv = D.nkv, hd = D.hd, F = D.F;
-  const float qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+  const double es = sizeof(T);
   // Groups are collected in a host list and launched kMaxGroups at a time.
   std::vector<GemmGroup> glist;
-  auto groups_for = [&](int lam, const std::vector<size_t>& woff) {
+  // gamma_of(layer): RMSNorm weight the residual-add epilogue folds into xn
+  // for the row's next consumer (null: no consumer).
+  auto groups_for = [&](int lam, const std::vector<size_t>& woff, int next_norm) {
     glist.clear();
     for (size_t j = 0; j < stage_rows.size(); ++j) {
       const int r0 = stage_rows[j].first, cnt = stage_rows[j].second;
       const int layer = (int)j * smul + lam;
-      for (int o = 0; o < cnt; o += 64) glist.push_back(GemmGroup{ctx->at(woff[layer]), r0 + o, std::min(64, cnt - o)});
+      const float* gamma = nullptr;
+      if (next_norm == 1) gamma = ctx->norms + (size_t)layer * 2 * d + d;                    // this layer's FFN norm
+      if (next_norm == 2 && layer + 1 < ctx->L) gamma = ctx->norms + (size_t)(layer + 1) * 2 * d;  // next attention norm
+      for (int o = 0; o < cnt; o += 64)
+        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o)});
     }
   };
-  const double es = sizeof(T);
   auto run_gemm = [&](GemmArgs& ga, int epi) -> hipError_t {
     // algorithmic traffic: each distinct weight matrix once, activations in and out
     double bytes = 0, flops = 0;
@@ -326,7 +330,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
       if (g.w != lastw) bytes += (double)ga.N * ga.K * es;
       lastw = g.w;
       bytes += (double)g.m * ga.K * 4;
-      bytes += epi == EPI_STORE ? (double)g.m * ga.N * 4 : epi == EPI_RESID ? 2.0 * g.m * ga.N * 4 : (double)g.m * ga.N / 2 * 4;
+      bytes += epi == EPI_QKV ? (double)g.m * ga.N * 4 : epi == EPI_RESID ? 2.0 * g.m * ga.N * 4 : (double)g.m * ga.N / 2 * 4;
       flops += 2.0 * g.m * ga.N * ga.K;
     }
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
@@ -341,65 +345,69 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     prof_end(ctx, mk, launches, bytes, flops);
     return hipSuccess;
   };
-  const double rowop_bytes = (double)nrows * d * 8;            // one norm: hidden in, activations out
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.rows = ctx->rows;
+  ga.hidden = ctx->hidden;
+  ga.ssq = ctx->ssq;
+  ga.xn = ctx->xn;
+  ga.xh = ctx->xh;
+  ga.xin = ctx->xn;
+  ga.gfinal = ctx->norms + (size_t)2 * ctx->L * d;
+  ga.eps = D.eps;
+  ga.dims = D;
+  ga.cosT = ctx->cosT;
+  ga.sinT = ctx->sinT;
+  ga.qout = ctx->q;
+  ga.kvc = ctx->kvc;
+  ga.exb = ctx->exb;
+  ga.smul = smul;
+  ga.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+  ga.act = ctx->act;
   for (int lam = 0; lam < lam_count; ++lam) {
-    int mk = prof_begin(ctx, DEX_PROF_ROWOPS);
-    HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms, 2LL * d, smul, lam, ctx->A, d, D.eps, st));
-    prof_end(ctx, mk, 1, rowop_bytes, 3.0 * nrows * d);
-    GemmArgs ga;
-    std::memset(&ga, 0, sizeof(ga));
-    ga.rows = ctx->rows;
-    ga.hidden = ctx->hidden;
-    groups_for(lam, ctx->wp.wqkv);
+    ga.lam = lam;
+    ga.write_xh = 0;
+    groups_for(lam, ctx->wp.wqkv, 0);
     ga.K = d;
     ga.N = (nq + 2 * nkv) * hd;
-    ga.a = ctx->A;
-    ga.out = ctx->qkv;
-    HIPCHK(run_gemm(ga, EPI_STORE));
-    mk = prof_begin(ctx, DEX_PROF_ROWOPS);
-    HIPCHK(launch_rope_kv(ctx->qkv, ctx->rows, 0, nrows, ctx->cosT, ctx->sinT, ctx->q, ctx->kvc, ctx->exb, D, smul,
-                             lam, qscale, st));
-    prof_end(ctx, mk, 1, (double)nrows * (nq + 2 * nkv) * hd * 4 + (double)nrows * nq * hd * 4 + 2.0 * nrows * nkv * hd * 4,
-             6.0 * nrows * (nq + nkv) * hd);
-    mk = prof_begin(ctx, DEX_PROF_ATTN);
-    HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, 0, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_part,
+    HIPCHK(run_gemm(ga, EPI_QKV));
+    int mk = prof_begin(ctx, DEX_PROF_ATTN);
+    HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_part,
                             (float*)ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
-    groups_for(lam, ctx->wp.wo);
+    groups_for(lam, ctx->wp.wo, 1);
     ga.K = nq * hd;
     ga.N = d;
     ga.a = ctx->attn_out;
     HIPCHK(run_gemm(ga, EPI_RESID));
-    mk = prof_begin(ctx, DEX_PROF_ROWOPS);
-    HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms + d, 2LL * d, smul, lam, ctx->A, d, D.eps, st));
-    prof_end(ctx, mk, 1, rowop_bytes, 3.0 * nrows * d);
-    groups_for(lam, ctx->wp.wgu);
+    groups_for(lam, ctx->wp.wgu, 0);
     ga.K = d;
     ga.N = 2 * F;
-    ga.a = ctx->A;
-    ga.act = ctx->act;
     HIPCHK(run_gemm(ga, EPI_SWIGLU));
-    groups_for(lam, ctx->wp.wdown);
+    groups_for(lam, ctx->wp.wdown, 2);
     ga.K = F;
     ga.N = d;
     ga.a = ctx->act;
+    ga.write_xh = want_xh && lam == lam_count - 1;
     HIPCHK(run_gemm(ga, EPI_RESID));
   }
   return DEX_OK;
 }
 
+// Exit head for every row: final RMSNorm (fused), LM head, DECS mask and
+// Gumbel perturbation in the GEMM epilogue, then the per-row argmax reduce.
 template <typename T>
 int run_head(dex_ctx* ctx, int nrows) {
   const ModelDims& D = ctx->D;
   hipStream_t st = ctx->st;
-  HIPCHK(launch_rmsnorm<T>(ctx->hidden, ctx->rows, 0, nrows, ctx->norms + (size_t)2 * ctx->L * D.d, 0, 0, 0, ctx->A,
-                           D.d, D.eps, st));
   GemmArgs ga;
   std::memset(&ga, 0, sizeof(ga));
   ga.rows = ctx->rows;
+  ga.xin = ctx->xh;
+  ga.ssq = ctx->ssq;
+  ga.eps = D.eps;
   ga.K = D.d;
   ga.N = D.V;
-  ga.a = ctx->A;
   ga.out = (ctx->opt.debug & 1) ? ctx->dbg_logits : nullptr;
   ga.mode = ctx->opt.mode;
   ga.tau = ctx->opt.temperature;
@@ -414,6 +422,7 @@ int run_head(dex_ctx* ctx, int nrows) {
     ga.ngroups = 0;
     for (int o = r0; o < std::min(nrows, r0 + 64 * kMaxGroups); o += 64) {
       ga.g[ga.ngroups].w = ctx->head;
+      ga.g[ga.ngroups].gamma = nullptr;
       ga.g[ga.ngroups].row0 = o;
       ga.g[ga.ngroups].m = std::min(64, nrows - o);
       ++ga.ngroups;
@@ -515,17 +524,19 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   int mk = prof_begin(ctx, DEX_PROF_LATTICE);
   HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
   HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
-  if (ar) HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
-  else HIPCHK(launch_sched(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
-                           ctx->D.P, ctx->opt.decs, st));
-  prof_end(ctx, mk, 1, (double)R * sizeof(RowInfo), 0);
-  mk = prof_begin(ctx, DEX_PROF_ROWOPS);
-  HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, stage_tot[0], ctx->hidden, ctx->D.d, st));
-  prof_end(ctx, mk, 1, (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
+  if (ar) {
+    HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
+    HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
+  } else {
+    HIPCHK(launch_sched<T>(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
+                           ctx->D.P, ctx->opt.decs, ctx->embed, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d,
+                           st));
+  }
+  prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
   std::vector<std::pair<int, int>> stage_rows;
   for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
-  int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, attn_bytes,
-                         attn_flops);
+  int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, true,
+                         attn_bytes, attn_flops);
   if (rc) return rc;
   rc = run_head<T>(ctx, R);
   if (rc) return rc;
@@ -612,9 +623,9 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
       }
       HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
       HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
-      HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->D.d, st));
+      HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
       std::vector<std::pair<int, int>> stage_rows = {{0, R}};
-      const int rc = run_layers<T>(ctx, R, stage_rows, ctx->L, 0, nitems, p0 + R);
+      const int rc = run_layers<T>(ctx, R, stage_rows, ctx->L, 0, nitems, p0 + R, false);
       if (rc) return rc;
       HIPCHK(hipStreamSynchronize(st));  // host row buffers are reused by the next chunk
     }
@@ -706,6 +717,8 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->kvc = (float*)ctx->at(wp.kvc);
   ctx->exb = (float*)ctx->at(wp.exb);
   ctx->hidden = (float*)ctx->at(wp.hidden);
+  ctx->xn = (float*)ctx->at(wp.xn);
+  ctx->xh = (float*)ctx->at(wp.xh);
   ctx->map = (int*)ctx->at(wp.map);
   ctx->cand = (int*)ctx->at(wp.cand);
   ctx->margin = (float*)ctx->at(wp.margin);
@@ -722,9 +735,8 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->rows = (RowInfo*)ctx->at(wp.rows);
   ctx->plans = (SeqPlan*)ctx->at(wp.plans);
   ctx->items = (AttnItem*)ctx->at(wp.items);
-  ctx->A = ctx->at(wp.A);
-  ctx->qkv = (float*)ctx->at(wp.qkv);
   ctx->q = (float*)ctx->at(wp.q);
+  ctx->ssq = (float*)ctx->at(wp.ssq);
   ctx->attn_out = ctx->at(wp.attn_out);
   ctx->act = ctx->at(wp.act);
   ctx->attn_part = (float*)ctx->at(wp.attn_part);

@@ -1,4 +1,6 @@
-// Weight packing and the grouped, batch-invariant MFMA GEMM of the lattice step.
+// Weight packing and the grouped, batch-invariant MFMA GEMM of the lattice step,
+// with RMSNorm fused in front and RoPE/K-V write, residual add, SwiGLU or the
+// DECS exit head fused behind.
 //
 // Every projection of a decoder layer (QKV, O, gate/up, down) and the shared
 // LM head is Y[m, n] = sum_k A[m, k] W[n, k] with W row-major [N, K]
@@ -11,6 +13,13 @@
 // 2^-16 relative), and both go through v_mfma_f32_16x16x32_bf16 against the
 // same weight fragment: products are as exact as fp32 activations would
 // give, at no extra weight traffic. fp32 weights use v_mfma_f32_16x16x4_f32.
+//
+// Fused RMSNorm: the producer of a residual row (embedding or a residual-add
+// epilogue) writes, per 16-column tile, the residual h, h * g for the row's
+// next normalising consumer (g its RMSNorm weight), and the tile's sum of
+// squares. The consumer streams h * g as its A operand and multiplies each
+// output by rstd = 1/sqrt(sum_t ssq[t] / d + eps), the sum taken lane-strided
+// in tile order and closed by a fixed butterfly.
 //
 // Batch invariance: the value of output (m, n) depends only on row m of A and
 // column n of W, never on how many rows share the launch or where the row
@@ -26,23 +35,21 @@
 // Fragment (nb, ks) holds output columns 16nb..16nb+15 and k-step ks as 64
 // lanes x 16 bytes, lane l carrying column l%16 and elements
 // [ks*KSTEP + (l/16)*EPL, +EPL). A wave streaming its k range therefore reads
-// one contiguous 1 KiB per instruction.
+// one contiguous 1 KiB per instruction. Column order inside a 16-column tile is
+// chosen for the epilogue: SwiGLU tiles hold 8 gate and the matching 8 up
+// columns; query/key tiles hold 8 rotary pairs (i, i + hd/2).
 #include "common.h"
 
 namespace dex {
 
-// Per k-step: A fragment of a lane (AW 32-bit words of fp32 activations) and
-// the weight fragment (16 bytes) -> accumulate into acc.
+// Per k-step: A fragment of a lane (fp32 activations) and the weight fragment
+// (16 bytes) -> accumulate into acc.
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
   static constexpr int KSTEP = 32;
   static constexpr int EPL = 8;      // elements per lane per k-step
-  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a0, const u32x4_t& a1,
-                                             const u32x4_t& b) {
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const float* f, const u32x4_t& b) {
     bf16x8_t hi, lo, bv;
-    const float f[8] = {__uint_as_float(a0[0]), __uint_as_float(a0[1]), __uint_as_float(a0[2]),
-                        __uint_as_float(a0[3]), __uint_as_float(a1[0]), __uint_as_float(a1[1]),
-                        __uint_as_float(a1[2]), __uint_as_float(a1[3])};
     unsigned short h[8], l[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -61,24 +68,33 @@ template <> struct Mfma<float> {
   static constexpr int EPL = 4;
   // Lane l supplies elements kbase + 4*(l/16) + i for i = 0..3; MFMA i reduces
   // over the four lane groups, so the four MFMAs cover the 16 elements.
-  __device__ __forceinline__ static void mma(f32x4_t& acc, const u32x4_t& a, const u32x4_t&,
-                                             const u32x4_t& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), acc, 0, 0, 0);
+  __device__ __forceinline__ static void mma(f32x4_t& acc, const float* f, const u32x4_t& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[0], __uint_as_float(b[0]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[1], __uint_as_float(b[1]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[2], __uint_as_float(b[2]), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(f[3], __uint_as_float(b[3]), acc, 0, 0, 0);
   }
 };
 
+// Sum of squares of 16 consecutive values, in order.
+__device__ __forceinline__ float ssq16(const float* v) {
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 16; ++c) s = fmaf(v[c], v[c], s);
+  return s;
+}
+
 // ---------------------------------------------------------------------------
-// Packing. mode 0: one source [N][K]. mode 1: rows of src0, src1, src2
-// concatenated (n0, n1, n2 rows). mode 2: SwiGLU interleave of gate (src0)
-// and up (src1), each [n0][K]: packed fragment nb holds gate rows 8nb..8nb+7
-// in columns 0..7 and up rows 8nb..8nb+7 in columns 8..15.
+// Packing. mode 0: one source [N][K]. mode 1: QKV, rows of src0 (queries),
+// src1 (keys), src2 (values) with n0, n1, n2 rows; query and key heads are
+// permuted so that tile u of a head holds dims 8u..8u+7 in columns 0..7 and
+// their rotary partners 8u+hd/2.. in columns 8..15 (hd = head_dim). mode 2:
+// SwiGLU, gate (src0) and up (src1), each [n0][K]: packed tile nb holds gate
+// rows 8nb..8nb+7 in columns 0..7 and up rows 8nb..8nb+7 in columns 8..15.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void pack_kernel(u32x4_t* __restrict__ dst, const T* __restrict__ s0, const T* __restrict__ s1,
-                            const T* __restrict__ s2, int n0, int n1, int n2, int K, int mode,
+                            const T* __restrict__ s2, int n0, int n1, int n2, int K, int mode, int hd,
                             long long total) {
   constexpr int KSTEP = Mfma<T>::KSTEP, EPL = Mfma<T>::EPL;
   const int KS = K / KSTEP;
@@ -96,6 +112,12 @@ __global__ void pack_kernel(u32x4_t* __restrict__ dst, const T* __restrict__ s0,
       src = (c < 8 ? s0 : s1) + r * K;
     } else {
       long long r = nb * 16 + c;
+      if (mode == 1 && r < (long long)n0 + n1) {
+        const long long head = r / hd;
+        const int within = (int)(r - head * hd), u = within >> 4;
+        const int dim = c < 8 ? 8 * u + c : 8 * u + (c - 8) + hd / 2;
+        r = head * hd + dim;
+      }
       if (r < n0) src = s0 + r * K;
       else if (r < (long long)n0 + n1) src = s1 + (r - n0) * K;
       else src = s2 + (r - n0 - n1) * K;
@@ -111,7 +133,9 @@ template <typename T, int MB, int EPI>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args) {
   constexpr int KSTEP = Mfma<T>::KSTEP;
   constexpr int EPL = Mfma<T>::EPL;
+  constexpr int AW = EPL / 4;          // 16-byte A loads per lane per k-step (fp32 activations)
   constexpr int U = 4;
+  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
   const int gi = blockIdx.y;
   if (gi >= args.ngroups) return;
   const GemmGroup G = args.g[gi];
@@ -121,13 +145,13 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   const int KS = K / KSTEP;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int kb = (KS * w) / kKSplit, ke = (KS * (w + 1)) / kKSplit;
-
-  const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile * KS * 64 + lane;
-  const float* A = (const float*)args.a + (size_t)G.row0 * K;
   const int col16 = lane & 15;
   const int kq = (lane >> 4) * EPL;
-  constexpr int AW = EPL / 4;          // 16-byte A loads per lane per k-step (fp32 activations)
 
+  __shared__ float red[kKSplit][kMaxMB * 256];
+  __shared__ float rs_sh[kMaxMB * 16];
+
+  const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile * KS * 64 + lane;
   f32x4_t acc[MB];
   const u32x4_t* ap[MB];
   bool av[MB];
@@ -136,85 +160,146 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
     acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int r = mb * 16 + col16;
     av[mb] = r < G.m;
-    ap[mb] = (const u32x4_t*)(A + (size_t)(av[mb] ? r : 0) * K + kq);
+    const int rr = av[mb] ? r : 0;
+    const float* base = NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
+                             : (const float*)args.a + (size_t)(G.row0 + rr) * K;
+    ap[mb] = (const u32x4_t*)(base + kq);
   }
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+
+  auto load_a = [&](int k, int mb, float* f) {
+#pragma unroll
+    for (int x = 0; x < AW; ++x) {
+      const u32x4_t v = av[mb] ? ap[mb][k * (KSTEP / 4) + x] : zero;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[4 * x + e] = __uint_as_float(v[e]);
+    }
+  };
+
+  // Every load of U k-steps is issued before the MFMAs that consume them.
   int ks = kb;
   for (; ks + U <= ke; ks += U) {
     u32x4_t bv[U];
-    u32x4_t a[U][MB][AW];
+    float a[U][MB][EPL];
 #pragma unroll
     for (int u = 0; u < U; ++u) bv[u] = __builtin_nontemporal_load(wp + (size_t)(ks + u) * 64);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int x = 0; x < AW; ++x) a[u][mb][x] = av[mb] ? ap[mb][(ks + u) * (KSTEP / 4) + x] : zero;
+      for (int mb = 0; mb < MB; ++mb) load_a(ks + u, mb, a[u][mb]);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) Mfma<T>::mma(acc[mb], a[u][mb][0], a[u][mb][AW - 1], bv[u]);
+      for (int mb = 0; mb < MB; ++mb) Mfma<T>::mma(acc[mb], a[u][mb], bv[u]);
   }
   for (; ks < ke; ++ks) {
     const u32x4_t b = __builtin_nontemporal_load(wp + (size_t)ks * 64);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      u32x4_t a[AW];
-#pragma unroll
-      for (int x = 0; x < AW; ++x) a[x] = av[mb] ? ap[mb][ks * (KSTEP / 4) + x] : zero;
-      Mfma<T>::mma(acc[mb], a[0], a[AW - 1], b);
+      float a[EPL];
+      load_a(ks, mb, a);
+      Mfma<T>::mma(acc[mb], a, b);
+    }
+  }
+
+  // rstd of each row of a normalising GEMM, from the producer's tile sums.
+  if constexpr (NORM) {
+    const int nt = K >> 4;
+    for (int rl = w; rl < G.m; rl += kKSplit) {
+      const float* sq = args.ssq + (size_t)args.rows[G.row0 + rl].hrow * nt;
+      float s = 0.f;
+      for (int t = lane; t < nt; t += 64) s += sq[t];
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) rs_sh[rl] = 1.0f / sqrtf(s / (float)K + args.eps);
     }
   }
 
   // Partial tiles of the 8 k ranges, then their sum in wave order.
-  __shared__ float red[kKSplit][kMaxMB * 256];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) red[w][(mb * 16 + (lane >> 4) * 4 + r) * 16 + col16] = acc[mb][r];
   __syncthreads();
+  auto total = [&](int e) {
+    float v = red[0][e];
+#pragma unroll
+    for (int q = 1; q < kKSplit; ++q) v += red[q][e];
+    return v;
+  };
 
   constexpr int E = MB * 256;
-  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+  if constexpr (EPI == EPI_RESID) {
+    // h += y for the tile's 16 columns; h * g for the next consumer (and the
+    // exit head at a stage's end); then the tile's sum of squares.
+    __shared__ float hs[kMaxMB * 16][16];
     for (int e = threadIdx.x; e < E; e += kGemmThreads) {
       const int rl = e >> 4, c = e & 15;
       if (rl >= G.m) continue;
-      float v = red[0][e];
-#pragma unroll
-      for (int q = 1; q < kKSplit; ++q) v += red[q][e];
-      const int row = G.row0 + rl;
-      const int n = tile * 16 + c;
-      if constexpr (EPI == EPI_STORE) {
-        args.out[(size_t)row * args.N + n] = v;
-      } else {
-        float* h = args.hidden + (size_t)args.rows[row].hrow * args.N + n;
-        *h = *h + v;
-      }
+      const size_t o = (size_t)args.rows[G.row0 + rl].hrow * args.N + tile * 16 + c;
+      const float nv = args.hidden[o] + total(e);
+      args.hidden[o] = nv;
+      if (G.gamma) args.xn[o] = nv * G.gamma[tile * 16 + c];
+      if (args.write_xh) args.xh[o] = nv * args.gfinal[tile * 16 + c];
+      hs[rl][c] = nv;
     }
+    __syncthreads();
+    for (int rl = threadIdx.x; rl < G.m; rl += kGemmThreads)
+      args.ssq[(size_t)args.rows[G.row0 + rl].hrow * ntiles + tile] = ssq16(hs[rl]);
   } else if constexpr (EPI == EPI_SWIGLU) {
     for (int e = threadIdx.x; e < MB * 128; e += kGemmThreads) {
       const int rl = e >> 3, c = e & 7;
       if (rl >= G.m) continue;
-      const int eg = rl * 16 + c, eu = eg + 8;
-      float g = red[0][eg], u = red[0][eu];
-#pragma unroll
-      for (int q = 1; q < kKSplit; ++q) {
-        g += red[q][eg];
-        u += red[q][eu];
-      }
+      const float g = total(rl * 16 + c) * rs_sh[rl], u = total(rl * 16 + c + 8) * rs_sh[rl];
       const float s = g / (1.0f + expf(-g));
+      ((float*)args.act)[(size_t)(G.row0 + rl) * (args.N >> 1) + tile * 8 + c] = s * u;
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    // RoPE on query/key pairs (columns c, c+8), K/V into the committed cache
+    // (autoregressive and prefill rows) or the node's explore slot.
+    const ModelDims& D = args.dims;
+    const int hd = D.hd, tph = hd >> 4;
+    const int head = tile / tph, u = tile - head * tph;
+    for (int e = threadIdx.x; e < MB * 128; e += kGemmThreads) {
+      const int rl = e >> 3, c = e & 7;
+      if (rl >= G.m) continue;
       const int row = G.row0 + rl;
-      ((float*)args.act)[(size_t)row * (args.N >> 1) + tile * 8 + c] = s * u;
+      const RowInfo& R = args.rows[row];
+      const float x1 = total(rl * 16 + c) * rs_sh[rl], x2 = total(rl * 16 + c + 8) * rs_sh[rl];
+      const int layer = R.stage * args.smul + args.lam;
+      float* kvdst = nullptr;
+      int kv = 0;
+      if (head >= D.nq) {
+        kv = head < D.nq + D.nkv ? 0 : 1;
+        const int hh = head - D.nq - kv * D.nkv;
+        kvdst = R.kv_commit
+                    ? args.kvc + ((((size_t)R.seq * D.L + layer) * 2 + kv) * D.nkv + hh) * (size_t)D.Cmax * hd +
+                          (size_t)R.pos * hd
+                    : args.exb + ((((size_t)R.seq * D.P + R.phys) * D.S + args.lam) * 2 + kv) * (size_t)D.nkv * hd +
+                          (size_t)hh * hd;
+      }
+      if (kv == 1) {                         // values: natural column order
+        kvdst[16 * u + c] = x1;
+        kvdst[16 * u + c + 8] = x2;
+        continue;
+      }
+      const int i = 8 * u + c;
+      const float cs = args.cosT[(size_t)R.pos * (hd >> 1) + i], sn = args.sinT[(size_t)R.pos * (hd >> 1) + i];
+      const float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
+      if (head < D.nq) {
+        float* qd = args.qout + ((size_t)row * D.nq + head) * hd;
+        qd[i] = o1 * args.qscale;
+        qd[i + (hd >> 1)] = o2 * args.qscale;
+      } else {
+        kvdst[i] = o1;
+        kvdst[i + (hd >> 1)] = o2;
+      }
     }
   } else {  // EPI_HEAD
     __shared__ float sc[kMaxMB * 16][17];
     for (int e = threadIdx.x; e < E; e += kGemmThreads) {
       const int rl = e >> 4, c = e & 15;
       if (rl >= G.m) continue;
-      float z = red[0][e];
-#pragma unroll
-      for (int q = 1; q < kKSplit; ++q) z += red[q][e];
+      const float z = total(e) * rs_sh[rl];
       const int row = G.row0 + rl;
       const int n = tile * 16 + c;
       const RowInfo& ri = args.rows[row];
@@ -225,8 +310,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
           if (ri.mask[i] == n) s = -INFINITY;
       }
       if (args.mode == 1)
-        s = s / args.tau +
-            args.gumbel[((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N + n];
+        s = s / args.tau + args.gumbel[((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N + n];
       sc[rl][c] = s;
     }
     __syncthreads();
@@ -290,24 +374,48 @@ __global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, i
   }
 }
 
+// Embedding gather for rows with tok >= 0 (prefill and autoregressive rows):
+// h = E[tok] in fp32, xn = h * g0 (first layer's attention-norm weight) and the
+// per-16-column sums of squares.
+template <typename T>
+__global__ void embed_kernel(const T* __restrict__ E, const RowInfo* __restrict__ rows, int row0,
+                             float* __restrict__ hidden, float* __restrict__ xn, float* __restrict__ ssq,
+                             const float* __restrict__ g0, int d) {
+  const RowInfo& r = rows[row0 + blockIdx.x];
+  if (r.tok < 0) return;
+  const T* e = E + (size_t)r.tok * d;
+  const size_t base = (size_t)r.hrow * d;
+  for (int t = threadIdx.x; t < d / 16; t += blockDim.x) {
+    float v[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = to_f<T>(e[16 * t + c]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      hidden[base + 16 * t + c] = v[c];
+      xn[base + 16 * t + c] = v[c] * g0[16 * t + c];
+    }
+    ssq[(size_t)r.hrow * (d / 16) + t] = ssq16(v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_pack(void* dst, const void* s0, const void* s1, const void* s2, int n0, int n1,
-                       int n2, int K, int mode, int Npacked, hipStream_t st) {
+                       int n2, int K, int mode, int Npacked, int hd, hipStream_t st) {
   const long long total = (long long)(Npacked / 16) * (K / Mfma<T>::KSTEP) * 64;
   const int threads = 256;
   long long blocks = (total + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(pack_kernel<T>, dim3((unsigned)blocks), dim3(threads), 0, st, (u32x4_t*)dst,
-                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1, n2, K, mode, total);
+                     (const T*)s0, (const T*)s1, (const T*)s2, n0, n1, n2, K, mode, hd, total);
   return hipGetLastError();
 }
 template hipError_t launch_pack<float>(void*, const void*, const void*, const void*, int, int, int,
-                                       int, int, int, hipStream_t);
+                                       int, int, int, int, hipStream_t);
 template hipError_t launch_pack<bf16_t>(void*, const void*, const void*, const void*, int, int, int,
-                                        int, int, int, hipStream_t);
+                                        int, int, int, int, hipStream_t);
 
 template <typename T, int EPI>
 static hipError_t launch_gemm_mb(const GemmArgs& a, int mb, hipStream_t st) {
@@ -328,7 +436,7 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   for (int i = 0; i < a.ngroups; ++i) mmax = a.g[i].m > mmax ? a.g[i].m : mmax;
   const int mb = (mmax + 15) / 16;
   switch (epi) {
-    case EPI_STORE: return launch_gemm_mb<T, EPI_STORE>(a, mb, st);
+    case EPI_QKV: return launch_gemm_mb<T, EPI_QKV>(a, mb, st);
     case EPI_RESID: return launch_gemm_mb<T, EPI_RESID>(a, mb, st);
     case EPI_SWIGLU: return launch_gemm_mb<T, EPI_SWIGLU>(a, mb, st);
     default: return launch_gemm_mb<T, EPI_HEAD>(a, mb, st);
@@ -345,5 +453,17 @@ hipError_t launch_head_reduce(const float* part, int ntiles, int nrows, const Ro
                      ntiles, nrows, rows, P, cand, margin);
   return hipGetLastError();
 }
+
+template <typename T>
+hipError_t launch_embed(const void* E, const RowInfo* rows, int row0, int nrows, float* hidden, float* xn,
+                        float* ssq, const float* g0, int d, hipStream_t st) {
+  if (nrows == 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_kernel<T>, dim3(nrows), dim3(256), 0, st, (const T*)E, rows, row0, hidden, xn, ssq, g0, d);
+  return hipGetLastError();
+}
+template hipError_t launch_embed<float>(const void*, const RowInfo*, int, int, float*, float*, float*, const float*,
+                                        int, hipStream_t);
+template hipError_t launch_embed<bf16_t>(const void*, const RowInfo*, int, int, float*, float*, float*, const float*,
+                                         int, hipStream_t);
 
 }  // namespace dex

@@ -18,15 +18,28 @@
 
 namespace dex {
 
+// Expand: one workgroup per live sequence builds the row of every node the
+// round creates (2^q of them at state q) and gathers the embedding of the rows
+// that start a slot (explorer 0): residual, residual times the first layer's
+// attention-norm weight, and per-16-column sums of squares (the inputs of the
+// fused RMSNorm of the next GEMM).
+template <typename T>
 __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restrict__ rows,
                              int* __restrict__ map, const int* __restrict__ cand,
                              const int* __restrict__ freel, int* __restrict__ cursor,
-                             const int* __restrict__ anchor_tok, int N, int P, int decs) {
+                             const int* __restrict__ anchor_tok, int N, int P, int decs,
+                             const T* __restrict__ E, float* __restrict__ hidden, float* __restrict__ xn,
+                             float* __restrict__ ssq, const float* __restrict__ g0, int d) {
   const int s = blockIdx.x;
   const SeqPlan pl = plans[s];
   if (!pl.live) return;
   const int q = pl.q, nnew = 1 << q, first = nnew - 1;
   const int cur = cursor[s];
+  __shared__ int nemb;
+  __shared__ int emb_h[1 << (kMaxN - 1)];
+  __shared__ int emb_t[1 << (kMaxN - 1)];
+  if (threadIdx.x == 0) nemb = 0;
+  __syncthreads();
   int* mp = map + (size_t)s * P;
   const int* cd = cand + (size_t)s * P;
   for (int t = threadIdx.x; t < nnew; t += blockDim.x) {
@@ -67,9 +80,31 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
       R.n_mask = depth;
     }
     rows[pl.base[depth] + idx] = R;
+    if (R.tok >= 0) {
+      const int e = atomicAdd(&nemb, 1);
+      emb_h[e] = R.hrow;
+      emb_t[e] = R.tok;
+    }
   }
   __syncthreads();
   if (threadIdx.x == 0) cursor[s] = cur + nnew;
+  const int nt = d >> 4;
+  for (int x = threadIdx.x; x < nemb * nt; x += blockDim.x) {
+    const int e = x / nt, t = x - e * nt;
+    const T* src = E + (size_t)emb_t[e] * d + 16 * t;
+    float* h = hidden + (size_t)emb_h[e] * d + 16 * t;
+    float* xr = xn + (size_t)emb_h[e] * d + 16 * t;
+    float v[16], ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) v[c] = to_f<T>(src[c]);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      h[c] = v[c];
+      xr[c] = v[c] * g0[16 * t + c];
+      ss = fmaf(v[c], v[c], ss);
+    }
+    ssq[(size_t)emb_h[e] * nt + t] = ss;
+  }
 }
 
 // Commit and collapse for every sequence whose round reached the final
@@ -220,13 +255,21 @@ __global__ void reset_seq_kernel(int* __restrict__ map, int* __restrict__ freel,
 }
 
 // ----------------------------------------------------------------------------
+template <typename T>
 hipError_t launch_sched(const SeqPlan* plans, int nseq, RowInfo* rows, int* map, const int* cand,
                         const int* freel, int* cursor, const int* anchor_tok, int N, int P, int decs,
+                        const void* E, float* hidden, float* xn, float* ssq, const float* g0, int d,
                         hipStream_t st) {
-  hipLaunchKernelGGL(sched_kernel, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
-                     anchor_tok, N, P, decs);
+  hipLaunchKernelGGL(sched_kernel<T>, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
+                     anchor_tok, N, P, decs, (const T*)E, hidden, xn, ssq, g0, d);
   return hipGetLastError();
 }
+template hipError_t launch_sched<float>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
+                                        const int*, int, int, int, const void*, float*, float*, float*, const float*,
+                                        int, hipStream_t);
+template hipError_t launch_sched<bf16_t>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
+                                         const int*, int, int, int, const void*, float*, float*, float*, const float*,
+                                         int, hipStream_t);
 
 hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* cand, const float* margin,
                          int* freel, int* cursor, int* anchor_tok, int* records, int* promote_src,

@@ -1,106 +1,11 @@
-// Per-row layer kernels of the lattice step: embedding gather, RMSNorm,
-// RoPE with the K/V write, and lattice attention with its split-KV combine.
+// Lattice attention of the lattice step.
 //
-// Every kernel computes a row from that row's own inputs in a fixed order, so a
-// node of the depth-position lattice and the same context decoded
-// autoregressively produce identical bits.
+// Every row is computed from that row's own inputs in a fixed order, so a node
+// of the depth-position lattice and the same context decoded autoregressively
+// produce identical bits.
 #include "common.h"
 
 namespace dex {
-
-// ----------------------------------------------------------------------------
-// Embedding: rows that start a slot (explorer 0, "Depth Exploration for LLM
-// Decoding", Section 3.2: a position expansion starts the next token position
-// from E_0) load E[tok] into their fp32 residual stream.
-// ----------------------------------------------------------------------------
-template <typename T>
-__global__ void embed_kernel(const T* __restrict__ E, const RowInfo* __restrict__ rows, int row0,
-                             float* __restrict__ hidden, int d) {
-  const RowInfo& r = rows[row0 + blockIdx.x];
-  if (r.tok < 0) return;
-  const T* e = E + (size_t)r.tok * d;
-  float* h = hidden + (size_t)r.hrow * d;
-  for (int i = threadIdx.x; i < d; i += blockDim.x) h[i] = to_f<T>(e[i]);
-}
-
-// ----------------------------------------------------------------------------
-// RMSNorm: out = x / sqrt(mean(x^2) + eps) * g (fp32 GEMM activations).
-// The weight g belongs to layer stage*smul + lam (smul = 0 gives one layer for
-// every row). Sum of squares: per-thread strided partials, a fixed xor
-// butterfly per wave, then the four waves in order.
-// ----------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ hidden,
-                                                      const RowInfo* __restrict__ rows, int row0,
-                                                      const float* __restrict__ gbase,
-                                                      long long gstride, int smul, int lam,
-                                                      float* __restrict__ out, int d, float eps) {
-  const int row = row0 + blockIdx.x;
-  const RowInfo& r = rows[row];
-  const float* x = hidden + (size_t)r.hrow * d;
-  const float* g = gbase + (size_t)(r.stage * smul + lam) * gstride;
-  float ss = 0.f;
-  for (int i = threadIdx.x; i < d; i += 256) ss = fmaf(x[i], x[i], ss);
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-  __shared__ float wsum[4];
-  if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
-  const float rs = 1.0f / sqrtf(tot / (float)d + eps);
-  float* o = out + (size_t)row * d;
-  for (int i = threadIdx.x; i < d; i += 256) o[i] = x[i] * rs * g[i];
-}
-
-// ----------------------------------------------------------------------------
-// RoPE and K/V write. Input: the QKV projection [rows][(nq + 2nkv) * hd] in
-// fp32. Rotation pairs (i, i + hd/2) by angle pos * base^(-2i/hd) from a
-// host-built table. Queries go to qout pre-multiplied by qscale
-// (log2(e)/sqrt(hd), so attention can use exp2). Keys and values are stored
-// in fp32: into the committed cache at the row's position for
-// autoregressive and prefill rows, into the node's explore slot otherwise.
-// ----------------------------------------------------------------------------
-__global__ void rope_kv_kernel(const float* __restrict__ qkv, const RowInfo* __restrict__ rows,
-                               int row0, const float* __restrict__ cosT,
-                               const float* __restrict__ sinT, float* __restrict__ qout,
-                               float* __restrict__ kvc, float* __restrict__ exb, ModelDims D, int smul,
-                               int lam, float qscale) {
-  const int row = row0 + blockIdx.x;
-  const RowInfo& r = rows[row];
-  const int hd = D.hd, half = hd >> 1;
-  const int nh = D.nq + 2 * D.nkv;
-  const float* src = qkv + (size_t)row * nh * hd;
-  const float* cs = cosT + (size_t)r.pos * half;
-  const float* sn = sinT + (size_t)r.pos * half;
-  const int layer = r.stage * smul + lam;
-  for (int t = threadIdx.x; t < nh * half; t += blockDim.x) {
-    const int h = t / half, i = t - h * half;
-    const float x1 = src[h * hd + i], x2 = src[h * hd + i + half];
-    if (h < D.nq) {
-      const float c = cs[i], s = sn[i];
-      float* q = qout + ((size_t)row * D.nq + h) * hd;
-      q[i] = (x1 * c - x2 * s) * qscale;
-      q[i + half] = (x2 * c + x1 * s) * qscale;
-      continue;
-    }
-    const int kv = (h < D.nq + D.nkv) ? 0 : 1;
-    const int hh = h - D.nq - kv * D.nkv;
-    float o1 = x1, o2 = x2;
-    if (kv == 0) {
-      const float c = cs[i], s = sn[i];
-      o1 = x1 * c - x2 * s;
-      o2 = x2 * c + x1 * s;
-    }
-    float* dst;
-    if (r.kv_commit)
-      dst = kvc + ((((size_t)r.seq * D.L + layer) * 2 + kv) * D.nkv + hh) * (size_t)D.Cmax * hd +
-            (size_t)r.pos * hd;
-    else
-      dst = exb + ((((size_t)r.seq * D.P + r.phys) * D.S + lam) * 2 + kv) * (size_t)D.nkv * hd +
-            (size_t)hh * hd;
-    dst[i] = o1;
-    dst[i + half] = o2;
-  }
-}
 
 // ----------------------------------------------------------------------------
 // Lattice attention ("Depth Exploration for LLM Decoding", Section 3.2: the
@@ -309,97 +214,62 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 
 // Combine the split-KV chunks of a (row, head) in chunk order; one wave each.
 template <int HD>
-__global__ void attn_combine_kernel(const RowInfo* __restrict__ rows, int row0, int nrows,
-                                    const float* __restrict__ part, float* __restrict__ out, int nq,
-                                    int nchunk) {
-  constexpr int DPL = HD / 64;
+__global__ void attn_combine_kernel(const RowInfo* __restrict__ rows, int nrows, const float* __restrict__ part,
+                                    float* __restrict__ out, int nq, int nchunk) {
+  using G = AttnGeom<HD>;
+  constexpr int HS = G::HS, HP = HD + 2;
   const int unit = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (unit >= nrows * nq) return;
-  const int row = row0 + unit / nq, qh = unit % nq;
+  const int row = unit / nq, qh = unit % nq;
   const RowInfo& R = rows[row];
-  const int lim = R.ncommit + R.n_anc;
-  const int nc = (lim + AttnGeom<HD>::CHUNK - 1) / AttnGeom<HD>::CHUNK;
-  const float* base = part + ((size_t)row * nq + qh) * nchunk * (HD + 2);
+  const int nc = (R.ncommit + R.n_anc + G::CHUNK - 1) / G::CHUNK;
+  const float* base = part + ((size_t)row * nq + qh) * nchunk * HP;
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * (HD + 2) + HD]);
-  float Lsum = 0.f, o[DPL];
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * HP + HD]);
+  float Ls = 0.f, o[HS];
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) o[t] = 0.f;
+  for (int e = 0; e < HS; ++e) o[e] = 0.f;
   for (int c = 0; c < nc; ++c) {
-    const float* pc = base + c * (HD + 2);
+    const float* pc = base + c * HP;
     const float f = exp2f(pc[HD] - M);
-    Lsum = fmaf(pc[HD + 1], f, Lsum);
+    Ls = fmaf(pc[HD + 1], f, Ls);
 #pragma unroll
-    for (int t = 0; t < DPL; ++t) o[t] = fmaf(pc[lane * DPL + t], f, o[t]);
+    for (int e = 0; e < HS; ++e) o[e] = fmaf(pc[lane * HS + e], f, o[e]);
   }
-  const float inv = 1.0f / Lsum;
+  const float inv = 1.0f / Ls;
   float* dst = out + ((size_t)row * nq + qh) * HD;
 #pragma unroll
-  for (int t = 0; t < DPL; ++t) dst[lane * DPL + t] = o[t] * inv;
+  for (int e = 0; e < HS; ++e) dst[lane * HS + e] = o[e] * inv;
 }
 
 // ----------------------------------------------------------------------------
-// Host launchers
+// Host launcher
 // ----------------------------------------------------------------------------
-template <typename T>
-hipError_t launch_embed(const void* E, const RowInfo* rows, int row0, int nrows, float* hidden, int d,
-                        hipStream_t st) {
-  if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(embed_kernel<T>, dim3(nrows), dim3(256), 0, st, (const T*)E, rows, row0, hidden, d);
-  return hipGetLastError();
-}
-
-template <typename T>
-hipError_t launch_rmsnorm(const float* hidden, const RowInfo* rows, int row0, int nrows,
-                          const float* gbase, long long gstride, int smul, int lam, void* out, int d,
-                          float eps, hipStream_t st) {
-  if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rmsnorm_kernel<T>, dim3(nrows), dim3(256), 0, st, hidden, rows, row0, gbase,
-                     gstride, smul, lam, (float*)out, d, eps);
-  return hipGetLastError();
-}
-
-hipError_t launch_rope_kv(const float* qkv, const RowInfo* rows, int row0, int nrows, const float* cosT,
-                          const float* sinT, float* qout, float* kvc, float* exb, const ModelDims& D,
-                          int smul, int lam, float qscale, hipStream_t st) {
-  if (nrows == 0) return hipSuccess;
-  hipLaunchKernelGGL(rope_kv_kernel, dim3(nrows), dim3(256), 0, st, qkv, rows, row0, cosT, sinT, qout, kvc, exb, D,
-                     smul, lam, qscale);
-  return hipGetLastError();
-}
-
 int attn_chunk(int hd) { return hd == 128 ? AttnGeom<128>::CHUNK : AttnGeom<64>::CHUNK; }
 
-hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int row0, int nrows,
-                            const float* q, const float* kvc, const float* exb, float* part, float* out,
-                            const ModelDims& D, int lam, int smul, int nchunk, int max_keys, hipStream_t st) {
+hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int nrows, const float* q,
+                            const float* kvc, const float* exb, float* part, float* out, const ModelDims& D,
+                            int lam, int smul, int nchunk, int max_keys, hipStream_t st) {
   if (nitems == 0) return hipSuccess;
   const int nc = (max_keys + attn_chunk(D.hd) - 1) / attn_chunk(D.hd);
   dim3 grid(nitems, D.nkv, nc);
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D,
-                       lam, smul, nchunk);
+    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D, lam,
+                       smul, nchunk);
   else
-    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D,
-                       lam, smul, nchunk);
+    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D, lam,
+                       smul, nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int units = nrows * D.nq, wpb = 4;
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0,
-                       st, rows, row0, nrows, part, out, D.nq, nchunk);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0, st, rows,
+                       nrows, part, out, D.nq, nchunk);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0,
-                       st, rows, row0, nrows, part, out, D.nq, nchunk);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0, st, rows,
+                       nrows, part, out, D.nq, nchunk);
   return hipGetLastError();
 }
-
-#define DEX_INST(T)                                                                                  \
-  template hipError_t launch_embed<T>(const void*, const RowInfo*, int, int, float*, int, hipStream_t); \
-  template hipError_t launch_rmsnorm<T>(const float*, const RowInfo*, int, int, const float*, long long, \
-                                        int, int, void*, int, float, hipStream_t);
-DEX_INST(float)
-DEX_INST(bf16_t)
 
 }  // namespace dex
