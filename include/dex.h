@@ -168,11 +168,13 @@ int dex_last_step_rows(const dex_ctx* ctx, int32_t* rows_per_stage, int32_t* tot
 
 /* Kernel classes timed by dex_profile. */
 typedef enum {
-  DEX_PROF_GEMM = 0,     /* stage-batched layer GEMMs (QKV, O, gate/up, down) */
+  DEX_PROF_GEMM = 0,     /* stage-batched layer GEMMs (QKV with RMSNorm, RoPE, K/V write; O with
+                            residual; gate/up with RMSNorm and SwiGLU; down with residual) */
   DEX_PROF_ATTN = 1,     /* lattice attention and its split-KV combine */
   DEX_PROF_HEAD = 2,     /* exit head: LM-head GEMM with DECS/Gumbel epilogue, argmax reduce */
-  DEX_PROF_ROWOPS = 3,   /* embedding gather, RMSNorm, RoPE and K/V write */
-  DEX_PROF_LATTICE = 4,  /* schedule, commit/collapse, KV promotion */
+  DEX_PROF_ROWOPS = 3,   /* standalone per-row kernels (none at present: RMSNorm, RoPE with the
+                            K/V write and the embedding gather run fused in other classes) */
+  DEX_PROF_LATTICE = 4,  /* schedule with embedding, commit/collapse, KV promotion */
   DEX_PROF_NCLASS = 5
 } dex_prof_class;
 

@@ -1,0 +1,124 @@
+"""Summaries of rocprofv3 result databases (rocpd SQLite) for the lattice step.
+
+  python -m lossless_depth_adaptive_amd.profsum trace RESULTS.db
+      Per-kernel statistics of the decode window (from the first schedule or
+      autoregressive-row kernel to the end of the trace): calls, mean and
+      total duration, share, plus the mean over every layer-GEMM dispatch.
+
+  python -m lossless_depth_adaptive_amd.profsum traffic --fetch F.db --write W.db \
+        --bench-json BENCH.json --out traffic.json
+      HBM bytes of the layer GEMMs from the FETCH_SIZE and WRITE_SIZE counter
+      runs (KiB per dispatch), each scaled by what the same counter reads for a
+      1 GiB device-to-device copy in the same process (bench.py
+      --copy-calibration), summed over the decode window's GEMM dispatches and
+      divided by their count; compared with the algorithmic bytes per launch
+      the library reported for the same rounds (bench.py run with --warmup 0).
+"""
+
+import argparse
+import json
+import sqlite3
+import sys
+
+GIB = 1 << 30
+
+
+def _short(name: str) -> str:
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def _dispatches(db):
+    cur = sqlite3.connect(db).cursor()
+    return cur.execute("select name, start, end, duration from kernels order by start").fetchall()
+
+
+def decode_window(rows):
+    for i, r in enumerate(rows):
+        if "sched_kernel" in r[0] or "ar_rows_kernel" in r[0]:
+            return rows[i:]
+    return []
+
+
+def trace_summary(db: str) -> str:
+    rows = [r for r in decode_window(_dispatches(db)) if "dex::" in r[0]]
+    if not rows:
+        return "no decode-window dispatches found\n"
+    stats = {}
+    for name, s, e, d in rows:
+        stats.setdefault(_short(name), []).append(d)
+    total = sum(sum(v) for v in stats.values())
+    span = rows[-1][2] - rows[0][1]
+    out = [f"decode window: {len(rows)} dispatches, {total / 1e6:.2f} ms in kernels, {span / 1e6:.2f} ms wall",
+           f"{'kernel':<52} {'calls':>7} {'mean_us':>10} {'total_ms':>10} {'share':>7}"]
+    for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{k:<52} {len(v):>7} {sum(v) / len(v) / 1e3:>10.2f} {sum(v) / 1e6:>10.2f} "
+                   f"{100.0 * sum(v) / total:>6.1f}%")
+    g = [d for k, v in stats.items() if k.startswith("dex::gemm_kernel") for d in v]
+    out.append(f"layer+head GEMM dispatches: {len(g)}, mean {sum(g) / len(g) / 1e3:.2f} us")
+    lg = [d for k, v in stats.items() if k.startswith("dex::gemm_kernel") and not k.endswith(", 3>") for d in v]
+    out.append(f"layer GEMM dispatches (exit head excluded): {len(lg)}, mean {sum(lg) / len(lg) / 1e3:.2f} us")
+    return "\n".join(out) + "\n"
+
+
+def _counters(db, counter):
+    cur = sqlite3.connect(db).cursor()
+    return cur.execute("select dispatch_id, kernel_name, value from counters_collection where counter_name = ? "
+                       "order by dispatch_id", (counter,)).fetchall()
+
+
+def _calibration(rows):
+    """Counter reading of the 1 GiB copy: the dispatch right after the fill."""
+    for i, (_, name, _) in enumerate(rows):
+        if "FillFunctor<float>" in name and i + 1 < len(rows):
+            return rows[i + 1][2]
+    raise SystemExit("calibration copy not found (run bench.py with --copy-calibration)")
+
+
+def _gemm_window(rows):
+    start = next(i for i, r in enumerate(rows) if "sched_kernel" in r[1] or "ar_rows_kernel" in r[1])
+    return [r for r in rows[start:] if "dex::gemm_kernel" in r[1] and not _short(r[1]).endswith(", 3>")]
+
+
+def traffic(fetch_db, write_db, bench_json, workload=None):
+    f, w = _counters(fetch_db, "FETCH_SIZE"), _counters(write_db, "WRITE_SIZE")
+    f_scale = GIB / (_calibration(f) * 1024.0)
+    w_scale = GIB / (_calibration(w) * 1024.0)
+    fg, wg = _gemm_window(f), _gemm_window(w)
+    fetch = sum(v for _, _, v in fg) * 1024.0 * f_scale
+    write = sum(v for _, _, v in wg) * 1024.0 * w_scale
+    bench = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    rl = bench["roofline"]
+    n = len(fg)
+    return dict(workload=workload or bench["config"]["workload"], launches=n,
+                fetch_bytes_per_launch=fetch / n, write_bytes_per_launch=write / max(1, len(wg)),
+                bytes_per_launch=fetch / n + write / max(1, len(wg)),
+                algorithmic_bytes_per_launch=rl["algorithmic_bytes_per_launch"],
+                fetch_scale=f_scale, write_scale=w_scale,
+                note="layer GEMM launches (exit head excluded) of the decode window; counters in KiB per "
+                     "dispatch scaled by a 1 GiB copy read/write in the same process")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    r = sub.add_parser("traffic")
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--bench-json", required=True)
+    r.add_argument("--workload")
+    r.add_argument("--out")
+    a = ap.parse_args(argv)
+    if a.cmd == "trace":
+        sys.stdout.write(trace_summary(a.db))
+    else:
+        res = traffic(a.fetch, a.write, a.bench_json, a.workload)
+        txt = json.dumps(res, indent=2)
+        if a.out:
+            open(a.out, "w").write(txt + "\n")
+        print(txt)
+
+
+if __name__ == "__main__":
+    main()
