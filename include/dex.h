@@ -102,7 +102,10 @@ typedef struct {
    * depths: Appendix C.1). Needs gumbel_rows >= max_new_tokens + N - 1. */
   const float* gumbel;
   int32_t gumbel_rows;
-  int32_t debug;           /* bit 0: keep the final-depth logits of each sequence's last commit */
+  int32_t debug;           /* bit 0: keep the final-depth logits of each sequence's last commit;
+                              bit 1: launch every round eagerly (no HIP-graph replay). By default a
+                              round whose plan (FSM states, commit flags, attention chunk count) was
+                              seen before is captured once into a HIP graph and replayed. */
 } dex_options;
 
 /* One committed token (Algorithm 1, validate_and_commit). */

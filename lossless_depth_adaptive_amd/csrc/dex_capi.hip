@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "common.h"
@@ -49,6 +50,7 @@ namespace {
 
 thread_local std::string g_create_error;
 constexpr int kPrefillRows = 512;
+constexpr size_t kMaxGraphs = 256;
 
 struct Layout {
   size_t off = 0;
@@ -198,9 +200,17 @@ struct dex_ctx {
     int cls = 0, launches = 0;
     double bytes = 0, flops = 0;
   };
+  hipStream_t cap_st = nullptr;   // private stream that round graphs are captured on
   bool prof = false;
   std::vector<Mark> marks;
   size_t nmarks = 0;
+  // HIP graphs of whole rounds, keyed by the round's plan
+  struct GraphEntry {
+    hipGraphExec_t exec = nullptr;
+    std::vector<Mark> marks;
+  };
+  std::unordered_map<std::string, GraphEntry> graphs;
+  std::unordered_map<std::string, int> graph_seen;
   dex_kernel_stats stats[DEX_PROF_NCLASS] = {};
 
   void* at(size_t off) { return ws + off; }
@@ -521,39 +531,104 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     }
   }
   hipStream_t st = ctx->st;
-  int mk = prof_begin(ctx, DEX_PROF_LATTICE);
-  HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
-  HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
-  if (ar) {
-    HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
-    HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
-  } else {
-    HIPCHK(launch_sched<T>(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
-                           ctx->D.P, ctx->opt.decs, ctx->embed, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d,
-                           st));
-  }
-  prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
-  std::vector<std::pair<int, int>> stage_rows;
-  for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
-  int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, true,
-                         attn_bytes, attn_flops);
-  if (rc) return rc;
-  rc = run_head<T>(ctx, R);
-  if (rc) return rc;
-  mk = prof_begin(ctx, DEX_PROF_LATTICE);
-  if (ncommit) {
+  // Everything the round enqueues; run eagerly, or captured into a HIP graph
+  // and replayed when the same plan (FSM states, commit flags, attention chunk
+  // count, profiling) comes back. Plans and items are re-read from the pinned
+  // host buffers at every replay.
+  auto enqueue = [&]() -> int {
+    hipStream_t st = ctx->st;
+    int mk = prof_begin(ctx, DEX_PROF_LATTICE);
+    HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
     if (ar) {
-      HIPCHK(launch_ar_commit(ctx->plans, B, ctx->cand, ctx->margin, ctx->anchor, ctx->records, ctx->dbg_u, ctx->dbg_m,
-                              ctx->D.P, ctx->L, st));
+      HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
+      HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
     } else {
-      HIPCHK(launch_commit(ctx->plans, B, ctx->map, ctx->cand, ctx->margin, ctx->freel, ctx->cursor, ctx->anchor,
-                           ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P, st));
-      HIPCHK(launch_promote(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
+      HIPCHK(launch_sched<T>(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
+                             ctx->D.P, ctx->opt.decs, ctx->embed, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms,
+                             ctx->D.d, st));
     }
-    HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));
+    prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
+    std::vector<std::pair<int, int>> stage_rows;
+    for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
+    int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, true,
+                           attn_bytes, attn_flops);
+    if (rc) return rc;
+    rc = run_head<T>(ctx, R);
+    if (rc) return rc;
+    mk = prof_begin(ctx, DEX_PROF_LATTICE);
+    if (ncommit) {
+      if (ar) {
+        HIPCHK(launch_ar_commit(ctx->plans, B, ctx->cand, ctx->margin, ctx->anchor, ctx->records, ctx->dbg_u,
+                                ctx->dbg_m, ctx->D.P, ctx->L, st));
+      } else {
+        HIPCHK(launch_commit(ctx->plans, B, ctx->map, ctx->cand, ctx->margin, ctx->freel, ctx->cursor, ctx->anchor,
+                             ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P, st));
+        HIPCHK(launch_promote(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
+      }
+      HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));
+    }
+    prof_end(ctx, mk, ncommit ? (ar ? 1 : 2) : 0,
+             ar ? 0.0 : 2.0 * ncommit * ctx->L * 2.0 * ctx->D.nkv * ctx->D.hd * 4, 0);
+    return DEX_OK;
+  };
+  const bool graphs = !(ctx->opt.debug & 2);
+  std::string key;
+  if (graphs) {
+    key.reserve(16 + 3 * B);
+    key += ar ? 'A' : 'D';
+    key += ctx->prof ? 'P' : '-';
+    key += std::to_string((max_keys + attn_chunk(ctx->D.hd) - 1) / attn_chunk(ctx->D.hd));
+    key += ':';
+    for (int s = 0; s < B; ++s) {
+      key += (char)('a' + (live[s] ? ctx->h_plans[s].q : 31));
+      key += ctx->h_plans[s].commit ? 'c' : '.';
+    }
   }
-  prof_end(ctx, mk, ncommit ? (ar ? 1 : 2) : 0,
-           ar ? 0.0 : 2.0 * ncommit * ctx->L * 2.0 * ctx->D.nkv * ctx->D.hd * 4, 0);
+  auto found = graphs ? ctx->graphs.find(key) : ctx->graphs.end();
+  if (found != ctx->graphs.end()) {
+    // Replay: restore the timing marks the capture recorded; attention bytes
+    // change with the committed length and are refreshed from this round.
+    dex_ctx::GraphEntry& ge = found->second;
+    for (size_t i = 0; i < ge.marks.size(); ++i) {
+      ctx->marks[i].cls = ge.marks[i].cls;
+      ctx->marks[i].launches = ge.marks[i].launches;
+      ctx->marks[i].bytes = ge.marks[i].cls == DEX_PROF_ATTN ? attn_bytes : ge.marks[i].bytes;
+      ctx->marks[i].flops = ge.marks[i].cls == DEX_PROF_ATTN ? attn_flops : ge.marks[i].flops;
+    }
+    ctx->nmarks = ge.marks.size();
+    HIPCHK(hipGraphLaunch(ge.exec, st));
+  } else if (graphs && ++ctx->graph_seen[key] >= 2 && ctx->graphs.size() < kMaxGraphs) {
+    // Capture on the library's own stream (the caller's may be the legacy
+    // default stream, which cannot be captured), launch on the caller's.
+    HIPCHK(hipStreamBeginCapture(ctx->cap_st, hipStreamCaptureModeThreadLocal));
+    ctx->st = ctx->cap_st;
+    const int rc = enqueue();
+    ctx->st = st;
+    hipGraph_t g = nullptr;
+    const hipError_t e = hipStreamEndCapture(ctx->cap_st, &g);
+    if (rc != DEX_OK || e != hipSuccess) {
+      if (g) (void)hipGraphDestroy(g);
+      if (rc == DEX_OK) {
+        ctx->err = std::string("hipStreamEndCapture: ") + hipGetErrorString(e);
+        ctx->poisoned = true;
+        return DEX_EHIP;
+      }
+      return rc;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t ei = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    HIPCHK(ei);
+    dex_ctx::GraphEntry ge;
+    ge.exec = exec;
+    ge.marks.assign(ctx->marks.begin(), ctx->marks.begin() + ctx->nmarks);
+    ctx->graphs.emplace(key, std::move(ge));
+    HIPCHK(hipGraphLaunch(exec, st));
+  } else {
+    const int rc = enqueue();
+    if (rc) return rc;
+  }
   HIPCHK(hipStreamSynchronize(st));
   prof_collect(ctx);
   int n = 0;
@@ -746,11 +821,12 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
     dex_destroy(ctx);
     return code;
   };
-  if (hipHostMalloc((void**)&ctx->h_plans, sizeof(SeqPlan) * D.B) != hipSuccess ||
+  if (hipStreamCreateWithFlags(&ctx->cap_st, hipStreamNonBlocking) != hipSuccess ||
+      hipHostMalloc((void**)&ctx->h_plans, sizeof(SeqPlan) * D.B) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_records, 5 * 4 * D.B) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_items, sizeof(AttnItem) * wp.Rmax) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_rows, sizeof(RowInfo) * wp.Rmax) != hipSuccess) {
-    ctx->err = "hipHostMalloc failed";
+    ctx->err = "stream creation or hipHostMalloc failed";
     return fail(DEX_EHIP);
   }
   rc = ctx->bf16 ? pack_weights<bf16_t>(ctx, w) : pack_weights<float>(ctx, w);
@@ -868,6 +944,8 @@ int dex_profile(dex_ctx* ctx, int32_t enable, dex_kernel_stats* out, int32_t n) 
 
 void dex_destroy(dex_ctx* ctx) {
   if (!ctx) return;
+  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second.exec);
+  if (ctx->cap_st) (void)hipStreamDestroy(ctx->cap_st);
   for (auto& m : ctx->marks) {
     if (m.a) (void)hipEventDestroy(m.a);
     if (m.b) (void)hipEventDestroy(m.b);

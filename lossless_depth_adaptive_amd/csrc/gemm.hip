@@ -127,19 +127,24 @@ __global__ void pack_kernel(u32x4_t* __restrict__ dst, const T* __restrict__ s0,
 }
 
 // ---------------------------------------------------------------------------
-// Grouped GEMM. grid = (N/16 tiles, groups), block = 512 (8 waves = 8 k ranges).
+// Grouped GEMM. grid = (N/(16 NB) tile blocks, groups), block = 512 (8 waves =
+// the 8 k ranges). A workgroup covers NB adjacent 16-column tiles and reuses
+// each activation fragment for all of them.
 // ---------------------------------------------------------------------------
-template <typename T, int MB, int EPI>
+#ifndef DEX_GEMM_U
+#define DEX_GEMM_U 4
+#endif
+template <typename T, int MB, int NB, int EPI>
 __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args) {
   constexpr int KSTEP = Mfma<T>::KSTEP;
   constexpr int EPL = Mfma<T>::EPL;
   constexpr int AW = EPL / 4;          // 16-byte A loads per lane per k-step (fp32 activations)
-  constexpr int U = 4;
+  constexpr int U = DEX_GEMM_U;        // k-steps of loads in flight per wave
   constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
   const int gi = blockIdx.y;
   if (gi >= args.ngroups) return;
   const GemmGroup G = args.g[gi];
-  const int tile = blockIdx.x;
+  const int tile0 = blockIdx.x * NB;
   const int ntiles = args.N >> 4;
   const int K = args.K;
   const int KS = K / KSTEP;
@@ -148,16 +153,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   const int col16 = lane & 15;
   const int kq = (lane >> 4) * EPL;
 
-  __shared__ float red[kKSplit][kMaxMB * 256];
-  __shared__ float rs_sh[kMaxMB * 16];
+  __shared__ float red[kKSplit][NB][MB * 256];
+  __shared__ float rs_sh[MB * 16];
 
-  const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile * KS * 64 + lane;
-  f32x4_t acc[MB];
+  const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile0 * KS * 64 + lane;
+  f32x4_t acc[MB][NB];
   const u32x4_t* ap[MB];
   bool av[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    acc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int r = mb * 16 + col16;
     av[mb] = r < G.m;
     const int rr = av[mb] ? r : 0;
@@ -175,14 +181,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
       for (int e = 0; e < 4; ++e) f[4 * x + e] = __uint_as_float(v[e]);
     }
   };
+  auto load_b = [&](int k, int nb) { return __builtin_nontemporal_load(wp + ((size_t)nb * KS + k) * 64); };
 
   // Every load of U k-steps is issued before the MFMAs that consume them.
   int ks = kb;
   for (; ks + U <= ke; ks += U) {
-    u32x4_t bv[U];
+    u32x4_t bv[U][NB];
     float a[U][MB][EPL];
 #pragma unroll
-    for (int u = 0; u < U; ++u) bv[u] = __builtin_nontemporal_load(wp + (size_t)(ks + u) * 64);
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) bv[u][nb] = load_b(ks + u, nb);
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
@@ -190,15 +199,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) Mfma<T>::mma(acc[mb], a[u][mb], bv[u]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) Mfma<T>::mma(acc[mb][nb], a[u][mb], bv[u][nb]);
   }
   for (; ks < ke; ++ks) {
-    const u32x4_t b = __builtin_nontemporal_load(wp + (size_t)ks * 64);
+    u32x4_t b[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) b[nb] = load_b(ks, nb);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       float a[EPL];
       load_a(ks, mb, a);
-      Mfma<T>::mma(acc[mb], a, b);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) Mfma<T>::mma(acc[mb][nb], a, b[nb]);
     }
   }
 
@@ -218,12 +232,16 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[w][(mb * 16 + (lane >> 4) * 4 + r) * 16 + col16] = acc[mb][r];
-  __syncthreads();
-  auto total = [&](int e) {
-    float v = red[0][e];
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int q = 1; q < kKSplit; ++q) v += red[q][e];
+      for (int r = 0; r < 4; ++r) red[w][nb][(mb * 16 + (lane >> 4) * 4 + r) * 16 + col16] = acc[mb][nb][r];
+  __syncthreads();
+  for (int nb = 0; nb < NB; ++nb) {
+  const int tile = tile0 + nb;
+  auto total = [&](int e) {
+    float v = red[0][nb][e];
+#pragma unroll
+    for (int q = 1; q < kKSplit; ++q) v += red[q][nb][e];
     return v;
   };
 
@@ -231,7 +249,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   if constexpr (EPI == EPI_RESID) {
     // h += y for the tile's 16 columns; h * g for the next consumer (and the
     // exit head at a stage's end); then the tile's sum of squares.
-    __shared__ float hs[kMaxMB * 16][16];
+    __shared__ float hs[MB * 16][16];
     for (int e = threadIdx.x; e < E; e += kGemmThreads) {
       const int rl = e >> 4, c = e & 15;
       if (rl >= G.m) continue;
@@ -295,7 +313,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
       }
     }
   } else {  // EPI_HEAD
-    __shared__ float sc[kMaxMB * 16][17];
+    __shared__ float sc[MB * 16][17];
     for (int e = threadIdx.x; e < E; e += kGemmThreads) {
       const int rl = e >> 4, c = e & 15;
       if (rl >= G.m) continue;
@@ -333,6 +351,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
       p[1] = __int_as_float(tile * 16 + bi);
       p[2] = second;
     }
+  }
+  if (NB > 1) __syncthreads();
   }
 }
 
@@ -417,16 +437,25 @@ template hipError_t launch_pack<float>(void*, const void*, const void*, const vo
 template hipError_t launch_pack<bf16_t>(void*, const void*, const void*, const void*, int, int, int,
                                         int, int, int, int, hipStream_t);
 
-template <typename T, int EPI>
+#ifndef DEX_GEMM_NB
+#define DEX_GEMM_NB 1
+#endif
+template <typename T, int NB, int EPI>
 static hipError_t launch_gemm_mb(const GemmArgs& a, int mb, hipStream_t st) {
-  dim3 grid(a.N / 16, a.ngroups);
+  dim3 grid(a.N / (16 * NB), a.ngroups);
   switch (mb) {
-    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((gemm_kernel<T, 3, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<T, 4, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((gemm_kernel<T, 1, NB, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((gemm_kernel<T, 2, NB, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((gemm_kernel<T, 3, NB, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((gemm_kernel<T, 4, NB, EPI>), grid, dim3(kGemmThreads), 0, st, a); break;
   }
   return hipGetLastError();
+}
+
+template <typename T, int EPI>
+static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
+  if (DEX_GEMM_NB > 1 && (a.N / 16) % DEX_GEMM_NB == 0) return launch_gemm_mb<T, DEX_GEMM_NB, EPI>(a, mb, st);
+  return launch_gemm_mb<T, 1, EPI>(a, mb, st);
 }
 
 // Runs one grouped GEMM; the MFMA row-block count is the largest group's.
@@ -436,10 +465,10 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
   for (int i = 0; i < a.ngroups; ++i) mmax = a.g[i].m > mmax ? a.g[i].m : mmax;
   const int mb = (mmax + 15) / 16;
   switch (epi) {
-    case EPI_QKV: return launch_gemm_mb<T, EPI_QKV>(a, mb, st);
-    case EPI_RESID: return launch_gemm_mb<T, EPI_RESID>(a, mb, st);
-    case EPI_SWIGLU: return launch_gemm_mb<T, EPI_SWIGLU>(a, mb, st);
-    default: return launch_gemm_mb<T, EPI_HEAD>(a, mb, st);
+    case EPI_QKV: return launch_gemm_nb<T, EPI_QKV>(a, mb, st);
+    case EPI_RESID: return launch_gemm_nb<T, EPI_RESID>(a, mb, st);
+    case EPI_SWIGLU: return launch_gemm_nb<T, EPI_SWIGLU>(a, mb, st);
+    default: return launch_gemm_nb<T, EPI_HEAD>(a, mb, st);
   }
 }
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);

@@ -11,7 +11,8 @@ import os
 from typing import Dict, List, Optional, Sequence
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libdex.so")
+# The in-tree build; DEX_LIBRARY may name another build of the same sources.
+LIB_PATH = os.environ.get("DEX_LIBRARY") or os.path.join(HERE, "libdex.so")
 
 DEX_OK, DEX_EINVAL, DEX_ENOSPC, DEX_ESTATE, DEX_EHIP = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
@@ -106,12 +107,14 @@ def model_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab,
 
 
 def options(mode="greedy", temperature=1.0, decs=True, max_batch=1, max_context=1024,
-            max_new_tokens=256, gumbel=None, debug=False) -> Options:
-    """``gumbel``: CUDA float32 tensor [max_batch, rows, vocab] or None."""
+            max_new_tokens=256, gumbel=None, debug=False, graphs=True) -> Options:
+    """``gumbel``: CUDA float32 tensor [max_batch, rows, vocab] or None. ``debug`` keeps the
+    final-depth logits of each last commit; ``graphs=False`` launches every round eagerly."""
     return Options(SAMPLE if mode == "sample" else GREEDY, float(temperature), int(bool(decs)),
                    max_batch, max_context, max_new_tokens,
                    None if gumbel is None else gumbel.data_ptr(),
-                   0 if gumbel is None else gumbel.shape[1], int(bool(debug)))
+                   0 if gumbel is None else gumbel.shape[1],
+                   int(bool(debug)) | (0 if graphs else 2))
 
 
 def workspace_bytes(cfg: ModelConfig, X: Sequence[int], opt: Options) -> int:

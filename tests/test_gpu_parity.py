@@ -131,3 +131,30 @@ def test_error_codes_on_device():
         ctx.step()                                       # both sequences are done
     assert e.value.code == D.DEX_ESTATE
     ctx.close()
+
+
+@pytest.mark.parametrize("name", ["llama7b_x4_narrow", "llama13b_x8_b4_narrow"])
+def test_graph_replay_matches_eager(name):
+    """Rounds replayed from captured HIP graphs (the default) give the same
+    commits and the same final-depth logit bits as rounds launched eagerly,
+    for DEX and for plain AR; each replay is checked, with eager host work and
+    synchronisations between replays."""
+    from tests.gpu_helpers import device_weights, make_ctx, run
+    w, kw = CASES[name]
+    T = kw["T"]
+    Wd = device_weights(w)
+    prompts = batch_prompts(w)
+    gum = gumbel_rows(w.seed_g, w.batch, T + len(w.X), w.vocab).cuda() if w.mode == "sample" else None
+    for ar in (False, True):
+        res = []
+        for graphs in (False, True):
+            ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum, graphs=graphs)
+            res.append(run(ctx, prompts, T, ar=ar)[0])
+            ctx.close()
+        for s in range(w.batch):
+            eager, graph = res[0][s], res[1][s]
+            assert [(r["token"], r["branch"], r["position"]) for r in eager] == \
+                   [(r["token"], r["branch"], r["position"]) for r in graph]
+            for a, b in zip(eager, graph):
+                assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+                assert a["u"] == b["u"]
