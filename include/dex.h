@@ -190,7 +190,9 @@ typedef struct {
 } dex_kernel_stats;
 
 /* Per-class timing of later dex_step / dex_ar_step calls with HIP events on
- * the context's stream. enable = 1 turns it on, 0 off. When out is not NULL
+ * the context's stream. enable = 1 turns it on, 0 off. While it is on, rounds
+ * run eagerly (no graph replay): event records inside a replayed graph do not
+ * bracket the kernels between them. When out is not NULL
  * the stats gathered since the last call are copied into out[0..n-1]
  * (n <= DEX_PROF_NCLASS) and reset. Errors: DEX_EINVAL (bad n), DEX_EHIP. */
 int dex_profile(dex_ctx* ctx, int32_t enable, dex_kernel_stats* out, int32_t n);

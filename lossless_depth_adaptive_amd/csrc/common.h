@@ -15,8 +15,10 @@ constexpr int kGemmThreads = 512;    // 8 waves: fixed 8-way split of K
 constexpr int kKSplit = 8;
 constexpr int kMaxMB = 4;            // 16-row MFMA blocks per GEMM group (<= 64 rows)
 constexpr int kMaxGroups = 48;       // GEMM groups per launch
-constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item
-constexpr int kAttnThreads = 512;    // 8 waves, one key tile each
+constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item (one MFMA tile)
+constexpr int kKvTile = 32;          // positions per K/V cache tile = keys per attention chunk
+constexpr int kAttnSC = 4;           // chunks per attention super-chunk
+constexpr int kAttnSCKeys = kKvTile * kAttnSC;
 
 typedef unsigned short bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -58,6 +60,7 @@ struct ModelDims {
   int P;            // lattice node slots per sequence (2^N - 1)
   int B;            // max sequences
   int Cmax;         // max context
+  int Cs;           // committed-cache positions per (sequence, layer, kv head): Cmax rounded up to kKvTile
   float eps;
 };
 
@@ -95,8 +98,8 @@ struct GemmArgs {
   const float* cosT;
   const float* sinT;
   float* qout;      // [rows][nq][hd], pre-scaled by qscale
-  float* kvc;       // committed K/V
-  float* exb;       // explore-buffer K/V
+  bf16_t* kvc;      // committed K/V (tiles of (hi, lo) pairs)
+  bf16_t* exb;      // explore-buffer K/V
   int smul, lam;    // layer = stage * smul + lam
   float qscale;
   // EPI_SWIGLU
@@ -112,10 +115,37 @@ struct GemmArgs {
 
 struct AttnItem {
   int row0;         // first row
-  int nrows;        // rows (all of one sequence and one layer)
+  int nrows;        // rows (all of one sequence and one layer), nrows * (nq / nkv) <= kAttnUnits
   int stage;        // explorer of the rows; layer = stage * smul + lam
   int max_keys;     // max over the rows of ncommit + n_anc
+  int xc0, xc1;     // chunks [xc0, xc1] may hold explore keys of some row (xc0 = -1: none);
+                    // every row's explore keys lie in them
 };
+
+// K/V storage. Every K or V value x is kept as a bfloat16 pair (hi, lo) with
+// hi = bf16(x) and lo = bf16(x - hi), both round-to-nearest-even, so that the
+// attention products run on bf16 MFMA with about 2^-17 relative error.
+//
+// Committed cache: per (sequence, layer, kv head) a run of Cs / kKvTile tiles
+// of 32 positions, 128 * hd bf16 each:
+//   K plane pl (0 hi, 1 lo): [pl][hd / 8][slot][8] at offset pl * 32 hd, with
+//     position k of the tile at slot 16 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3);
+//   V plane pl: [pl][hd][32 positions] at offset 64 hd + pl * 32 hd.
+// Explore entry of one (sequence, node slot, layer slot, kv head): 4 hd bf16,
+//   K hi, K lo, V hi, V lo, each [hd].
+__host__ __device__ inline int kv_slot(int k) { return 16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
+__host__ __device__ inline size_t kv_head_base(const ModelDims& D, int seq, int layer, int h) {
+  return (((size_t)seq * D.L + layer) * D.nkv + h) * (size_t)D.Cs * D.hd * 4;
+}
+__host__ __device__ inline size_t kv_elem(int hd, int pos, int kv, int plane, int d) {
+  const size_t tile = (size_t)(pos / kKvTile) * 128 * hd;
+  const int k = pos % kKvTile;
+  return kv == 0 ? tile + (size_t)plane * 32 * hd + (d >> 3) * 256 + kv_slot(k) * 8 + (d & 7)
+                 : tile + 64 * (size_t)hd + (size_t)plane * 32 * hd + (size_t)d * 32 + k;
+}
+__host__ __device__ inline size_t ex_base(const ModelDims& D, int seq, int phys, int lam, int h) {
+  return ((((size_t)seq * D.P + phys) * D.S + lam) * D.nkv + h) * 4 * (size_t)D.hd;
+}
 
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((unsigned)v) << 16); }
 __device__ __forceinline__ bf16_t f2bf(float f) {
@@ -129,6 +159,11 @@ template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+// The (hi, lo) bfloat16 pair of x described above.
+__device__ __forceinline__ void split_bf(float x, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
 
 // Host-visible kernel launchers (defined in the .hip files).
 struct Launch {

@@ -30,14 +30,15 @@ hipError_t launch_head_reduce(const float*, int, int, const RowInfo*, int, int*,
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
-hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const float*, const float*, const float*,
-                            float*, float*, const ModelDims&, int, int, int, int, hipStream_t);
+int attn_mix_slots();
+hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const float*, const bf16_t*, const bf16_t*,
+                            float*, float*, float*, const ModelDims&, int, int, int, int, int, hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
                         const void*, float*, float*, float*, const float*, int, hipStream_t);
 hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
                          float*, const int*, int, int, hipStream_t);
-hipError_t launch_promote(const SeqPlan*, int, const int*, const float*, float*, const ModelDims&, hipStream_t);
+hipError_t launch_promote(const SeqPlan*, int, const int*, const bf16_t*, bf16_t*, const ModelDims&, hipStream_t);
 hipError_t launch_ar_rows(const SeqPlan*, int, RowInfo*, const int*, int, hipStream_t);
 hipError_t launch_ar_commit(const SeqPlan*, int, const int*, const float*, int*, int*, int*, float*, int, int,
                             hipStream_t);
@@ -65,7 +66,7 @@ struct Layout {
 struct WsPlan {
   size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh;
   size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
-  size_t rows, plans, items, q, attn_out, act, attn_part, head_part, ssq;
+  size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq;
   std::vector<size_t> wqkv, wo, wgu, wdown;
   size_t total;
   int Rmax, nchunk;
@@ -118,6 +119,7 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   const int N = n_x, S = c->n_layers / n_x, P = (1 << N) - 1;
   w.Rmax = std::max(std::max((int)B << (N - 1), kPrefillRows), (int)B);
   w.nchunk = (int)((Cmax + attn_chunk((int)hd) - 1) / attn_chunk((int)hd));
+  const size_t Cs = (Cmax + kKvTile - 1) / kKvTile * kKvTile;
   const size_t R = w.Rmax;
   w.embed = lay.take(V * d * es);
   w.head = lay.take(V * d * es);
@@ -130,8 +132,8 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.norms = lay.take((2 * L + 1) * d * 4);
   w.cosT = lay.take(Cmax * (hd / 2) * 4);
   w.sinT = lay.take(Cmax * (hd / 2) * 4);
-  w.kvc = lay.take(B * L * 2 * nkv * Cmax * hd * 4);      // K/V are fp32
-  w.exb = lay.take(B * P * S * 2 * nkv * hd * 4);
+  w.kvc = lay.take(B * L * nkv * Cs * hd * 8);            // K and V as bf16 (hi, lo) pairs
+  w.exb = lay.take(B * P * S * nkv * hd * 8);
   w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
   w.xn = lay.take((B * P + kPrefillRows) * d * 4);
   w.xh = lay.take((B * P + kPrefillRows) * d * 4);
@@ -155,7 +157,8 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
   w.attn_out = lay.take(R * nq * hd * 4);
   w.act = lay.take(R * F * 4);
-  w.attn_part = lay.take(R * nq * w.nchunk * (hd + 2) * 4);
+  w.attn_part = lay.take(R * nq * w.nchunk * (hd + 4) * 4);
+  w.attn_tail = lay.take(R * nq * attn_mix_slots() * (hd + 4) * 4);
   w.head_part = lay.take(R * (V / 16) * 3 * 4);
   w.total = lay.off;
   return w;
@@ -174,12 +177,12 @@ struct dex_ctx {
   char* ws;
   WsPlan wp;
   // device views
-  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q, *attn_part, *head_part, *ssq;
+  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q, *attn_part, *attn_tail, *head_part, *ssq;
   int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
   RowInfo* rows;
   SeqPlan* plans;
   AttnItem* items;
-  float *kvc, *exb;
+  bf16_t *kvc, *exb;
   void *attn_out, *act, *embed, *head;
   // host state
   int nseq = 0;
@@ -202,14 +205,11 @@ struct dex_ctx {
   };
   hipStream_t cap_st = nullptr;   // private stream that round graphs are captured on
   bool prof = false;
+  int attn_umax = 1;              // most units in one attention item of the current round
   std::vector<Mark> marks;
   size_t nmarks = 0;
   // HIP graphs of whole rounds, keyed by the round's plan
-  struct GraphEntry {
-    hipGraphExec_t exec = nullptr;
-    std::vector<Mark> marks;
-  };
-  std::unordered_map<std::string, GraphEntry> graphs;
+  std::unordered_map<std::string, hipGraphExec_t> graphs;
   std::unordered_map<std::string, int> graph_seen;
   dex_kernel_stats stats[DEX_PROF_NCLASS] = {};
 
@@ -382,8 +382,9 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     ga.N = (nq + 2 * nkv) * hd;
     HIPCHK(run_gemm(ga, EPI_QKV));
     int mk = prof_begin(ctx, DEX_PROF_ATTN);
-    HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_part,
-                            (float*)ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys, st));
+    HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail,
+                            ctx->attn_part, (float*)ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys,
+                            smul != 0 ? ctx->attn_umax : 0, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
     groups_for(lam, ctx->wp.wo, 1);
     ga.K = nq * hd;
@@ -499,6 +500,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   const int rep = ctx->D.nq / ctx->D.nkv;
   const int per_item = std::max(1, kAttnUnits / rep);
   int nitems = 0, max_keys = 0;
+  ctx->attn_umax = 1;
   for (int j = 0; j < N; ++j)
     for (int s = 0; s < B; ++s) {
       const int cnt = rows_seq_stage[(size_t)s * N + j];
@@ -509,7 +511,11 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
         it.nrows = std::min(per_item, cnt - o);
         it.stage = j;
         it.max_keys = mk;
+        // lattice rows: explore keys at [C, mk), at most two chunks
+        it.xc0 = ar ? -1 : ctx->C_[s] / kKvTile;
+        it.xc1 = ar ? -1 : (mk - 1) / kKvTile;
         max_keys = std::max(max_keys, mk);
+        ctx->attn_umax = std::max(ctx->attn_umax, it.nrows * rep);
       }
     }
   // Algorithmic attention traffic of one layer slot: each (sequence, stage)
@@ -572,12 +578,13 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
              ar ? 0.0 : 2.0 * ncommit * ctx->L * 2.0 * ctx->D.nkv * ctx->D.hd * 4, 0);
     return DEX_OK;
   };
-  const bool graphs = !(ctx->opt.debug & 2);
+  // Timed rounds run eagerly: an event recorded inside a replayed graph does
+  // not wait for the kernel before it, so it cannot time that kernel.
+  const bool graphs = !(ctx->opt.debug & 2) && !ctx->prof;
   std::string key;
   if (graphs) {
     key.reserve(16 + 3 * B);
     key += ar ? 'A' : 'D';
-    key += ctx->prof ? 'P' : '-';
     key += std::to_string((max_keys + attn_chunk(ctx->D.hd) - 1) / attn_chunk(ctx->D.hd));
     key += ':';
     for (int s = 0; s < B; ++s) {
@@ -587,17 +594,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   }
   auto found = graphs ? ctx->graphs.find(key) : ctx->graphs.end();
   if (found != ctx->graphs.end()) {
-    // Replay: restore the timing marks the capture recorded; attention bytes
-    // change with the committed length and are refreshed from this round.
-    dex_ctx::GraphEntry& ge = found->second;
-    for (size_t i = 0; i < ge.marks.size(); ++i) {
-      ctx->marks[i].cls = ge.marks[i].cls;
-      ctx->marks[i].launches = ge.marks[i].launches;
-      ctx->marks[i].bytes = ge.marks[i].cls == DEX_PROF_ATTN ? attn_bytes : ge.marks[i].bytes;
-      ctx->marks[i].flops = ge.marks[i].cls == DEX_PROF_ATTN ? attn_flops : ge.marks[i].flops;
-    }
-    ctx->nmarks = ge.marks.size();
-    HIPCHK(hipGraphLaunch(ge.exec, st));
+    HIPCHK(hipGraphLaunch(found->second, st));
   } else if (graphs && ++ctx->graph_seen[key] >= 2 && ctx->graphs.size() < kMaxGraphs) {
     // Capture on the library's own stream (the caller's may be the legacy
     // default stream, which cannot be captured), launch on the caller's.
@@ -620,10 +617,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     const hipError_t ei = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
     (void)hipGraphDestroy(g);
     HIPCHK(ei);
-    dex_ctx::GraphEntry ge;
-    ge.exec = exec;
-    ge.marks.assign(ctx->marks.begin(), ctx->marks.begin() + ctx->nmarks);
-    ctx->graphs.emplace(key, std::move(ge));
+    ctx->graphs.emplace(key, exec);
     HIPCHK(hipGraphLaunch(exec, st));
   } else {
     const int rc = enqueue();
@@ -695,6 +689,7 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         it.nrows = std::min(per_item, R - o);
         it.stage = 0;
         it.max_keys = p0 + o + it.nrows;
+        it.xc0 = it.xc1 = -1;
       }
       HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
       HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
@@ -783,14 +778,15 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   D.P = (1 << n_x) - 1;
   D.B = opt->max_batch;
   D.Cmax = opt->max_context;
+  D.Cs = (D.Cmax + kKvTile - 1) / kKvTile * kKvTile;
   D.eps = cfg->rms_eps;
   ctx->embed = ctx->at(wp.embed);
   ctx->head = ctx->at(wp.head);
   ctx->norms = (float*)ctx->at(wp.norms);
   ctx->cosT = (float*)ctx->at(wp.cosT);
   ctx->sinT = (float*)ctx->at(wp.sinT);
-  ctx->kvc = (float*)ctx->at(wp.kvc);
-  ctx->exb = (float*)ctx->at(wp.exb);
+  ctx->kvc = (bf16_t*)ctx->at(wp.kvc);
+  ctx->exb = (bf16_t*)ctx->at(wp.exb);
   ctx->hidden = (float*)ctx->at(wp.hidden);
   ctx->xn = (float*)ctx->at(wp.xn);
   ctx->xh = (float*)ctx->at(wp.xh);
@@ -815,6 +811,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->attn_out = ctx->at(wp.attn_out);
   ctx->act = ctx->at(wp.act);
   ctx->attn_part = (float*)ctx->at(wp.attn_part);
+  ctx->attn_tail = (float*)ctx->at(wp.attn_tail);
   ctx->head_part = (float*)ctx->at(wp.head_part);
   auto fail = [&](int code) {
     g_create_error = ctx->err;
@@ -944,7 +941,7 @@ int dex_profile(dex_ctx* ctx, int32_t enable, dex_kernel_stats* out, int32_t n) 
 
 void dex_destroy(dex_ctx* ctx) {
   if (!ctx) return;
-  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second.exec);
+  for (auto& kv : ctx->graphs) (void)hipGraphExecDestroy(kv.second);
   if (ctx->cap_st) (void)hipStreamDestroy(ctx->cap_st);
   for (auto& m : ctx->marks) {
     if (m.a) (void)hipEventDestroy(m.a);

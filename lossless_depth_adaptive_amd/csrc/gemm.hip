@@ -284,20 +284,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
       const RowInfo& R = args.rows[row];
       const float x1 = total(rl * 16 + c) * rs_sh[rl], x2 = total(rl * 16 + c + 8) * rs_sh[rl];
       const int layer = R.stage * args.smul + args.lam;
-      float* kvdst = nullptr;
+      // K/V go out as (hi, lo) bf16 pairs: committed tile or explore entry.
+      bf16_t* kvbase = nullptr;
       int kv = 0;
       if (head >= D.nq) {
         kv = head < D.nq + D.nkv ? 0 : 1;
         const int hh = head - D.nq - kv * D.nkv;
-        kvdst = R.kv_commit
-                    ? args.kvc + ((((size_t)R.seq * D.L + layer) * 2 + kv) * D.nkv + hh) * (size_t)D.Cmax * hd +
-                          (size_t)R.pos * hd
-                    : args.exb + ((((size_t)R.seq * D.P + R.phys) * D.S + args.lam) * 2 + kv) * (size_t)D.nkv * hd +
-                          (size_t)hh * hd;
+        kvbase = R.kv_commit ? args.kvc + kv_head_base(D, R.seq, layer, hh)
+                             : args.exb + ex_base(D, R.seq, R.phys, args.lam, hh) + (size_t)kv * 2 * hd;
       }
+      auto put = [&](int dd, float v) {
+        bf16_t hi, lo;
+        split_bf(v, hi, lo);
+        if (R.kv_commit) {
+          kvbase[kv_elem(hd, R.pos, kv, 0, dd)] = hi;
+          kvbase[kv_elem(hd, R.pos, kv, 1, dd)] = lo;
+        } else {
+          kvbase[dd] = hi;
+          kvbase[hd + dd] = lo;
+        }
+      };
       if (kv == 1) {                         // values: natural column order
-        kvdst[16 * u + c] = x1;
-        kvdst[16 * u + c + 8] = x2;
+        put(16 * u + c, x1);
+        put(16 * u + c + 8, x2);
         continue;
       }
       const int i = 8 * u + c;
@@ -308,8 +317,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
         qd[i] = o1 * args.qscale;
         qd[i + (hd >> 1)] = o2 * args.qscale;
       } else {
-        kvdst[i] = o1;
-        kvdst[i + (hd >> 1)] = o2;
+        put(i, o1);
+        put(i + (hd >> 1), o2);
       }
     }
   } else {  // EPI_HEAD

@@ -177,21 +177,19 @@ __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict
 }
 
 // Copy the anchor path's K/V (node 2^j - 1 holds stage j) into the committed
-// cache at position C. grid = (sequences, layers).
+// cache at position C. grid = (sequences, layers, kv heads).
 __global__ void promote_kernel(const SeqPlan* __restrict__ plans, const int* __restrict__ promote_src,
-                               const float* __restrict__ exb, float* __restrict__ kvc, ModelDims D) {
-  const int s = blockIdx.x, layer = blockIdx.y;
+                               const bf16_t* __restrict__ exb, bf16_t* __restrict__ kvc, ModelDims D) {
+  const int s = blockIdx.x, layer = blockIdx.y, h = blockIdx.z;
   const SeqPlan pl = plans[s];
   if (!pl.live || !pl.commit) return;
   const int j = layer / D.S, lam = layer - j * D.S;
   const int phys = promote_src[s * kMaxN + j];
-  const int n = 2 * D.nkv * D.hd;
-  for (int t = threadIdx.x; t < n; t += blockDim.x) {
-    const int kv = t / (D.nkv * D.hd);
-    const int rem = t - kv * D.nkv * D.hd;
-    const int h = rem / D.hd, i = rem - h * D.hd;
-    const float v = exb[((((size_t)s * D.P + phys) * D.S + lam) * 2 + kv) * D.nkv * D.hd + (size_t)h * D.hd + i];
-    kvc[((((size_t)s * D.L + layer) * 2 + kv) * D.nkv + h) * (size_t)D.Cmax * D.hd + (size_t)pl.C * D.hd + i] = v;
+  const bf16_t* src = exb + ex_base(D, s, phys, lam, h);
+  bf16_t* dst = kvc + kv_head_base(D, s, layer, h);
+  for (int t = threadIdx.x; t < 4 * D.hd; t += blockDim.x) {   // K hi, K lo, V hi, V lo, each [hd]
+    const int kv = t / (2 * D.hd), plane = (t / D.hd) & 1, i = t % D.hd;
+    dst[kv_elem(D.hd, pl.C, kv, plane, i)] = src[t];
   }
 }
 
@@ -279,9 +277,9 @@ hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* ca
   return hipGetLastError();
 }
 
-hipError_t launch_promote(const SeqPlan* plans, int nseq, const int* promote_src, const float* exb, float* kvc,
+hipError_t launch_promote(const SeqPlan* plans, int nseq, const int* promote_src, const bf16_t* exb, bf16_t* kvc,
                           const ModelDims& D, hipStream_t st) {
-  hipLaunchKernelGGL(promote_kernel, dim3(nseq, D.L), dim3(256), 0, st, plans, promote_src, exb, kvc, D);
+  hipLaunchKernelGGL(promote_kernel, dim3(nseq, D.L, D.nkv), dim3(256), 0, st, plans, promote_src, exb, kvc, D);
   return hipGetLastError();
 }
 

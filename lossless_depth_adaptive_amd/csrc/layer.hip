@@ -12,263 +12,491 @@ namespace dex {
 // binary expansion lets ancestry, KV entries and attention masks be indexed
 // consistently). A row attends to the committed cache [0, ncommit) and to the
 // explore-buffer entries of its ancestors at positions ncommit.. (its own
-// entry last). All rows of a work item share one sequence and layer. K and V
-// are fp32.
+// entry last). All rows of a work item share one sequence and layer.
+//
+// Products run on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with every fp32
+// operand split into a bf16 pair: a.b is taken as hi.hi + hi.lo + lo.hi.
+// A work item is one MFMA tile of up to 16 units (row, query head) of one kv
+// head. Scores come out transposed, S^T = K Q^T: lane (g, n) = (lane / 16,
+// lane % 16) holds unit n's scores for keys 8g .. 8g+7 of a 32-key chunk, which
+// is exactly the B operand of the value product O^T = V^T P^T. The K tile
+// layout (see common.h) puts those keys in MFMA row order, the V planes are
+// stored transposed, so every operand is one 16-byte load and each load
+// instruction of the wave covers whole contiguous runs.
 //
 // Reduction order, a function of key positions only (so a lattice node and
-// the same context decoded autoregressively agree bit for bit). With
-// HS = hd/64 lane groups per key and TK = 64/HS keys per tile:
-//   tile  = TK absolute positions [TK t, TK t + TK): lane group g of key j
-//           forms the partial dot product over dims [64g, 64g+64) with four
-//           interleaved sums added as (s0+s1)+(s2+s3), the groups then added
-//           in order; m = max; p_j = 2^(s_j - m); l = xor-butterfly sum of p_j;
-//           acc = sum_j p_j v_j in j order (even and odd j in two chains);
-//   chunk = 8 tiles, merged in tile order;
-//   row   = chunks merged in chunk order by attn_combine_kernel.
+// the same context decoded autoregressively agree bit for bit):
+//   chunk       = 32 positions [32c, 32c + 32): scores by the MFMA chain over
+//                 32-dim steps in order; m = max; p = 2^(s - m); l = sum of
+//                 p (each lane's eight in key order, then lanes g^1, g^2 by
+//                 butterfly); acc = V^T P^T by one MFMA chain;
+//   super-chunk = kAttnSC chunks folded left to right (fold below);
+//   row         = super-chunks folded left to right by attn_combine_kernel.
 // Queries arrive pre-multiplied by log2(e)/sqrt(hd).
 //
-// grid = (items, kv heads, chunks), block = 512: wave w owns tile 8c+w. The
-// wave loads its committed K rows and V columns into registers once and reuses
-// them for every (row, query head) unit of the item; explore entries are read
-// from the node slots directly.
+// A chunk in which some row reads explore entries (positions it does not share
+// with the tile's other rows; the host marks them as chunks xc0..xc1 of the
+// item, at most two since a row has at most N explore keys) is computed once
+// per unit, with that unit's keys gathered into the same operand layout; every
+// other chunk is computed once for the whole tile with keys past a unit's limit
+// masked. Both give a unit the same operand values in the same MFMA order, hence
+// the same bits. The per-unit chunks are latency-bound, so they run as extra
+// blocks of the same launch, overlapping the bandwidth-bound shared chunks; the
+// super-chunks that hold them are folded by the combine kernel.
 // ----------------------------------------------------------------------------
-constexpr int kAttnWaves = kAttnThreads / 64;
 
-__device__ __forceinline__ float wave_max(float v) {
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-  return v;
-}
-// Sum over each group of `width` lanes (xor butterfly, fixed order).
-__device__ __forceinline__ float group_sum(float v, int width) {
-  for (int off = width >> 1; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
 }
 
-template <int HD> struct AttnGeom {
-  static constexpr int HS = HD / 64;              // lane groups per key
-  static constexpr int TK = 64 / HS;              // keys per tile
-  static constexpr int CHUNK = kAttnWaves * TK;   // keys per chunk
+// acc += A B^T over one 32-element k step, operands split into (hi, lo).
+__device__ __forceinline__ f32x4_t mma3(f32x4_t acc, const u32x4_t& ah, const u32x4_t& al, const u32x4_t& bh,
+                                        const u32x4_t& bl) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bh), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ah), as_bf16x8(bl), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(al), as_bf16x8(bh), acc, 0, 0, 0);
+  return acc;
+}
+
+__device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16_t h0, l0, h1, l1;
+    split_bf(x[2 * i], h0, l0);
+    split_bf(x[2 * i + 1], h1, l1);
+    hi[i] = (unsigned)h0 | ((unsigned)h1 << 16);
+    lo[i] = (unsigned)l0 | ((unsigned)l1 << 16);
+  }
+}
+
+// Fold partial (m, l, a) into state (M, L, A); both describe non-empty key sets.
+template <int NA>
+__device__ __forceinline__ void fold(float& M, float& L, float* A, float m, float l, const float* a) {
+  const float Mn = fmaxf(M, m);
+  const float al = exp2f(M - Mn), be = exp2f(m - Mn);
+  L = fmaf(l, be, L * al);
+#pragma unroll
+  for (int k = 0; k < NA; ++k) A[k] = fmaf(a[k], be, A[k] * al);
+  M = Mn;
+}
+
+// One 32-key chunk for the tile. qsrc(s, hi, lo): this lane's query operand
+// (unit n, dims 32s + 8g .. 32s + 8g + 7); ksrc(t, s, hi, lo): its K operand for
+// row block t (0, 1) and 32-dim step s; vsrc(b, hi, lo): its V^T operand for
+// output dims [16b, 16b + 16). valid8 bit i: key 8g + i counts for this lane's
+// unit. Out: acc[b][r] = the unit's unnormalised output at dim 16b + 4g + r,
+// and the chunk's m and l (m = -inf when no key counts).
+template <int HD, typename QSrc, typename KSrc, typename VSrc>
+__device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, unsigned valid8, f32x4_t* acc,
+                                              float& m, float& l) {
+  constexpr int NS = HD / 32, NB = HD / 16;
+  f32x4_t st[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4_t kh, kl, qh, ql;
+      ksrc(t, s, kh, kl);
+      qsrc(s, qh, ql);
+      st[t] = mma3(st[t], kh, kl, qh, ql);
+    }
+  }
+  float sv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sv[i] = (valid8 >> i) & 1 ? st[i >> 2][i & 3] : -INFINITY;
+  float mx = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float msafe = mx == -INFINITY ? 0.f : mx;
+  float p[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) p[i] = (valid8 >> i) & 1 ? exp2f(sv[i] - msafe) : 0.f;
+  float ls = p[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) ls += p[i];
+  ls += __shfl_xor(ls, 16);
+  ls += __shfl_xor(ls, 32);
+  m = mx;
+  l = ls;
+  u32x4_t ph, pl;
+  split8(p, ph, pl);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    u32x4_t vh, vl;
+    vsrc(b, vh, vl);
+    acc[b] = mma3(f32x4_t{0.f, 0.f, 0.f, 0.f}, vh, vl, ph, pl);
+  }
+}
+
+constexpr int kMixSlots = 2 * kAttnSC;   // chunk slots of the (at most two) mixed super-chunks
+
+// Whether super-chunk sc of the item holds a per-unit (explore) chunk.
+__device__ __forceinline__ bool sc_mixed(const AttnItem& it, int sc) {
+  return it.xc0 >= 0 && (sc == it.xc0 / kAttnSC || sc == it.xc1 / kAttnSC);
+}
+
+// Store the chunk partial of unit n held by lanes (g, n) to dst[hd + 2].
+template <int HD>
+__device__ __forceinline__ void store_partial(float* dst, const f32x4_t* acc, float m, float l, int g) {
+#pragma unroll
+  for (int b = 0; b < HD / 16; ++b) *(f32x4_t*)(dst + 16 * b + 4 * g) = acc[b];
+  if (g == 0) {
+    dst[HD] = m;
+    dst[HD + 1] = l;
+  }
+}
+
+// LDS of one attention block: the shared-chunk role's query tile and chunk
+// partials, or the per-unit role's explore values.
+template <int HD> struct AttnSmem {
+  union {
+    struct {
+      float red[kAttnSC][kAttnUnits][HD + 2];
+      bf16_t qsh[2][kAttnUnits][HD + 8];   // queries as (hi, lo), rows padded by 16 bytes
+    } m;
+    bf16_t ev[kAttnSC][kMaxN][2 * HD];      // per wave: V hi, V lo of the unit's explore entries
+  };
 };
 
-// Partial q . k over 64 dims held as 16 float4 words.
-template <typename Fetch>
-__device__ __forceinline__ float dot64(const float* __restrict__ qv, Fetch fetch) {
-  float s[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const f32x4_t k = fetch(i);
-    s[0] = fmaf(qv[4 * i], k[0], s[0]);
-    s[1] = fmaf(qv[4 * i + 1], k[1], s[1]);
-    s[2] = fmaf(qv[4 * i + 2], k[2], s[2]);
-    s[3] = fmaf(qv[4 * i + 3], k[3], s[3]);
+// Per-unit role: wave w computes chunk c (one of xc0, xc1) for unit u of the
+// item with that unit's own keys, into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
+template <int HD>
+__device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int c, int u,
+                                const RowInfo* __restrict__ rows, const float* __restrict__ q,
+                                const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
+                                float* __restrict__ mix, const ModelDims& D, int lam, int smul) {
+  constexpr int NB = HD / 16, HP = HD + 4;
+  const int rep = D.nq / D.nkv, units = it.nrows * rep;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int p0 = c * kKvTile;
+  const int row = it.row0 + min(u, units - 1) / rep, qhd = h * rep + u % rep;
+  const RowInfo& Ru = rows[row];
+  const int ncu = Ru.ncommit, limu = Ru.ncommit + Ru.n_anc;
+  const bool active = u < units && c <= it.xc1 && p0 < limu;
+  const size_t eslot = (size_t)D.S * D.nkv * 4 * HD;  // bf16 between node slots
+  const bf16_t* eb = exb + ex_base(D, Ru.seq, 0, lam, h);
+  bf16_t (*ev)[2 * HD] = sm.ev[w];
+  if (active) {
+    for (int t = lane; t < (limu - ncu) * (HD / 4); t += 64) {
+      const int j = t / (HD / 4), o = 8 * (t % (HD / 4));
+      *(u32x4_t*)&ev[j][o] = *(const u32x4_t*)(eb + Ru.anc[j] * eslot + 2 * HD + o);
+    }
   }
-  return (s[0] + s[1]) + (s[2] + s[3]);
+  __syncthreads();
+  if (!active) return;
+  const int layer = it.stage * smul + lam;
+  const bf16_t* tb = kvc + kv_head_base(D, Ru.seq, layer, h) + (size_t)c * 128 * HD;
+  const float* qr = q + ((size_t)row * D.nq + qhd) * HD;
+  // Every column of the query operand carries unit u; column u is kept.
+  auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
+    const f32x4_t a = *(const f32x4_t*)(qr + 32 * s + 8 * g), b = *(const f32x4_t*)(qr + 32 * s + 8 * g + 4);
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    split8(x, qh, ql);
+  };
+  auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
+    const int p = p0 + 8 * (n >> 2) + 4 * t + (n & 3);
+    const bf16_t* kp;
+    size_t lo_off;
+    if (p < ncu) {
+      kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
+      lo_off = 32 * HD;
+    } else if (p < limu) {
+      kp = eb + Ru.anc[p - ncu] * eslot + 8 * (4 * s + g);
+      lo_off = HD;
+    } else {
+      kh = kl = u32x4_t{0u, 0u, 0u, 0u};
+      return;
+    }
+    kh = *(const u32x4_t*)kp;
+    kl = *(const u32x4_t*)(kp + lo_off);
+  };
+  auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
+    const int pb = p0 + 8 * g, dd = 16 * b + n;
+    if (pb < ncu) {
+      const bf16_t* vp = tb + 64 * HD + dd * 32 + 8 * g;
+      vh = *(const u32x4_t*)vp;
+      vl = *(const u32x4_t*)(vp + 32 * HD);
+    } else {
+      vh = vl = u32x4_t{0u, 0u, 0u, 0u};
+    }
+    if (pb + 7 < ncu) return;
+    // Positions from ncu on: the explore entry's value, or 0 past the limit.
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int p = pb + i;
+      if (p < ncu) continue;
+      const unsigned hv = p < limu ? ev[p - ncu][dd] : 0u, lv = p < limu ? ev[p - ncu][HD + dd] : 0u;
+      const int sh = 16 * (i & 1);
+      const unsigned keep = ~(0xFFFFu << sh);
+      vh[i >> 1] = (vh[i >> 1] & keep) | (hv << sh);
+      vl[i >> 1] = (vl[i >> 1] & keep) | (lv << sh);
+    }
+  };
+  unsigned valid8 = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < limu ? 1u : 0u) << i;
+  f32x4_t acc[NB];
+  float m, l;
+  chunk_partial<HD>(qsrc, ksrc, vsrc, valid8, acc, m, l);
+  if (n == u)
+    store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP, acc,
+                      m, l, g);
 }
 
+// Shared role: wave w takes chunk kAttnSC * sc + w of the tile. In a
+// super-chunk without per-unit chunks the block folds the chunks per unit and
+// writes the super-chunk state part[row][qh][sc] = (acc[hd], m, l); in one with
+// them, its other chunks go to the mix slots for the combine kernel to fold.
 template <int HD>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
-    const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows,
-    const float* __restrict__ q, const float* __restrict__ kvc, const float* __restrict__ exb,
-    float* __restrict__ part, ModelDims D, int lam, int smul, int nchunk) {
-  using G = AttnGeom<HD>;
-  constexpr int HS = G::HS, TK = G::TK, HP = HD + 2;
-  __shared__ float qs[kAttnUnits][HD];
-  __shared__ float red[kAttnWaves][kAttnUnits][HP];
-
-  const AttnItem it = items[blockIdx.x];
-  const int h = blockIdx.y, c = blockIdx.z;
-  const int pb = c * G::CHUNK;
-  if (pb >= it.max_keys) return;
-  const int rep = D.nq / D.nkv;
-  const int units = it.nrows * rep;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int seq = rows[it.row0].seq;
-  int maxc = 0;
-  for (int i = 0; i < it.nrows; ++i) maxc = max(maxc, rows[it.row0 + i].ncommit);
-
-  for (int t = threadIdx.x; t < units * HD; t += kAttnThreads) {
-    const int u = t / HD, dd = t - u * HD;
-    const int row = it.row0 + u / rep, qh = h * rep + u % rep;
-    qs[u][dd] = q[((size_t)row * D.nq + qh) * HD + dd];
-  }
-
+__device__ void attn_shared_chunks(AttnSmem<HD>& sm, const AttnItem& it, int h, int sc,
+                                   const RowInfo* __restrict__ rows, const float* __restrict__ q,
+                                   const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
+                                   const ModelDims& D, int lam, int smul, int nsc_max) {
+  constexpr int NB = HD / 16, HP = HD + 4;
+  auto& red = sm.m.red;
+  auto& qsh = sm.m.qsh;
+  const int rep = D.nq / D.nkv, units = it.nrows * rep;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int layer = it.stage * smul + lam;
-  const size_t cstride = (size_t)D.Cmax * HD;
-  const float* kc = kvc + (((size_t)seq * D.L + layer) * 2 + 0) * D.nkv * cstride + h * cstride;
-  const float* vc = kvc + (((size_t)seq * D.L + layer) * 2 + 1) * D.nkv * cstride + h * cstride;
-  const size_t xs_slot = (size_t)D.S * 2 * D.nkv * HD;   // explore floats per node slot
-  const float* xk = exb + (size_t)seq * D.P * xs_slot + (size_t)lam * 2 * D.nkv * HD + (size_t)h * HD;
-  const float* xv = xk + (size_t)D.nkv * HD;
-
-  // This wave's tile: key j = lane % TK, dims [64 g, 64 g + 64) with g = lane / TK.
-  const int p0 = pb + TK * w;
-  const int j = lane % TK, g = lane / TK;
-  const int p = p0 + j;
-  f32x4_t kw[16];
-  float vw[TK][HS];
-  const int nk = max(0, min(TK, maxc - p0));
-  if (j < nk) {
-    const f32x4_t* kr = (const f32x4_t*)(kc + (size_t)p * HD + 64 * g);
+  const int seq = rows[it.row0].seq;
+  for (int t = threadIdx.x; t < kAttnUnits * HD / 8; t += 64 * kAttnSC) {
+    const int u = t / (HD / 8), d8 = 8 * (t % (HD / 8));
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (u < units) {
+      const float* qr = q + ((size_t)(it.row0 + u / rep) * D.nq + h * rep + u % rep) * HD + d8;
+      const f32x4_t a = *(const f32x4_t*)qr, b = *(const f32x4_t*)(qr + 4);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) kw[i] = kr[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) kw[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+      }
+    }
+    u32x4_t hi, lo;
+    split8(x, hi, lo);
+    *(u32x4_t*)&qsh[0][u][d8] = hi;
+    *(u32x4_t*)&qsh[1][u][d8] = lo;
   }
-#pragma unroll
-  for (int jj = 0; jj < TK; ++jj)
-#pragma unroll
-    for (int e = 0; e < HS; ++e) vw[jj][e] = jj < nk ? vc[(size_t)(p0 + jj) * HD + lane * HS + e] : 0.f;
+  // This lane's unit n: key limit (0 past the tile).
+  int lim = 0;
+  if (n < units) {
+    const RowInfo& R = rows[it.row0 + n / rep];
+    lim = R.ncommit + R.n_anc;
+  }
+  // Positions past every unit's limit may hold stale or never-written values:
+  // their V elements are zeroed so that p = 0 contributes exact zeros.
+  int vlim = lim;
+  for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
+  const int c = sc * kAttnSC + w, p0 = c * kKvTile;
+  const bool unit_chunk = it.xc0 >= 0 && c >= it.xc0 && c <= it.xc1;
+  const bool to_mix = sc_mixed(it, sc);
   __syncthreads();
 
-  for (int u = 0; u < units; ++u) {
-    const RowInfo& R = rows[it.row0 + u / rep];
-    const int lim = R.ncommit + R.n_anc;
-    float* rd = red[w][u];
-    if (p0 >= lim) {
-      if (lane == 0) {
-        rd[HD] = -INFINITY;
-        rd[HD + 1] = 0.f;
-      }
+  const bf16_t* tb = kvc + kv_head_base(D, seq, layer, h) + (size_t)c * 128 * HD;
+  if (!unit_chunk && p0 < vlim) {
+    auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
+      qh = *(const u32x4_t*)&qsh[0][n][32 * s + 8 * g];
+      ql = *(const u32x4_t*)&qsh[1][n][32 * s + 8 * g];
+    };
+    auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
+      const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
+      kh = *(const u32x4_t*)kp;
+      kl = *(const u32x4_t*)(kp + 32 * HD);
+    };
+    auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
+      const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
+      vh = *(const u32x4_t*)vp;
+      vl = *(const u32x4_t*)(vp + 32 * HD);
+      const int nv = vlim - (p0 + 8 * g);   // keys of this lane's eight below some limit
+      if (nv < 8) {
 #pragma unroll
-      for (int e = 0; e < HS; ++e) rd[lane * HS + e] = 0.f;
-      continue;
-    }
-    const float* qv = qs[u] + 64 * g;
-    float sp = 0.f;
-    if (p < R.ncommit) {
-      sp = dot64(qv, [&](int i) { return kw[i]; });
-    } else if (p < lim) {
-      const f32x4_t* xr = (const f32x4_t*)(xk + (size_t)R.anc[p - R.ncommit] * xs_slot + 64 * g);
-      sp = dot64(qv, [&](int i) { return xr[i]; });
-    }
-    float s = sp;
-    if (HS == 2) {
-      const float other = __shfl_xor(sp, 32);
-      s = g == 0 ? sp + other : other + sp;
-    }
-    if (p >= lim) s = -INFINITY;
-    const float m = wave_max(s);
-    const float pj = p < lim ? exp2f(s - m) : 0.f;
-    const float l = group_sum(pj, TK);
-    float a0[HS], a1[HS];
-#pragma unroll
-    for (int e = 0; e < HS; ++e) a0[e] = a1[e] = 0.f;
-    const int nv = min(TK, lim - p0);
-#pragma unroll
-    for (int jj = 0; jj < TK; ++jj) {
-      if (jj < nv) {
-        const float pv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pj), jj));
-        const int pp = p0 + jj;
-        float v[HS];
-        if (pp < R.ncommit) {
-#pragma unroll
-          for (int e = 0; e < HS; ++e) v[e] = vw[jj][e];
-        } else {
-          const float* xr = xv + (size_t)R.anc[pp - R.ncommit] * xs_slot + lane * HS;
-#pragma unroll
-          for (int e = 0; e < HS; ++e) v[e] = xr[e];
+        for (int i = 0; i < 4; ++i) {
+          const unsigned keep = (2 * i + 1 < nv ? 0xFFFF0000u : 0u) | (2 * i < nv ? 0xFFFFu : 0u);
+          vh[i] &= keep;
+          vl[i] &= keep;
         }
+      }
+    };
+    unsigned valid8 = 0;
 #pragma unroll
-        for (int e = 0; e < HS; ++e) {
-          if (jj & 1) a1[e] = fmaf(pv, v[e], a1[e]);
-          else a0[e] = fmaf(pv, v[e], a0[e]);
+    for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim ? 1u : 0u) << i;
+    f32x4_t acc[NB];
+    float m, l;
+    chunk_partial<HD>(qsrc, ksrc, vsrc, valid8, acc, m, l);
+    if (n < units && p0 < lim) {
+      if (to_mix) {
+        const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
+        store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
+                          acc, m, l, g);
+      } else {
+        float* rd = red[w][n];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rd[16 * b + 4 * g + r] = acc[b][r];
+        if (g == 0) {
+          rd[HD] = m;
+          rd[HD + 1] = l;
         }
       }
     }
-#pragma unroll
-    for (int e = 0; e < HS; ++e) rd[lane * HS + e] = a0[e] + a1[e];
-    if (lane == 0) {
-      rd[HD] = m;
-      rd[HD + 1] = l;
-    }
   }
+  if (to_mix) return;
   __syncthreads();
-  // Merge the chunk's tiles in tile order; wave w takes units w, w+8, ...
-  for (int u = w; u < units; u += kAttnWaves) {
+
+  // Fold the super-chunk's chunks per unit: thread (unit, sixteenth of hd).
+  constexpr int NA = HD / 16;
+  const int fu = threadIdx.x >> 4, fs = threadIdx.x & 15;
+  if (fu >= units) return;
+  const int row = it.row0 + fu / rep, qhd = h * rep + fu % rep;
+  const RowInfo& R = rows[row];
+  const int flim = R.ncommit + R.n_anc;
+  const int cb = sc * kAttnSC;
+  if (cb * kKvTile >= flim) return;
+  float M = red[0][fu][HD], L = red[0][fu][HD + 1], A[NA];
+#pragma unroll
+  for (int k = 0; k < NA; ++k) A[k] = red[0][fu][NA * fs + k];
+  for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < flim; ++ww) {
+    float a[NA];
+#pragma unroll
+    for (int k = 0; k < NA; ++k) a[k] = red[ww][fu][NA * fs + k];
+    fold<NA>(M, L, A, red[ww][fu][HD], red[ww][fu][HD + 1], a);
+  }
+  float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP;
+#pragma unroll
+  for (int k = 0; k < NA; k += 4) *(f32x4_t*)(dst + NA * fs + k) = f32x4_t{A[k], A[k + 1], A[k + 2], A[k + 3]};
+  if (fs == 0) {
+    dst[HD] = M;
+    dst[HD + 1] = L;
+  }
+}
+
+// One launch, block = kAttnSC waves. Blocks [0, ntail): per-unit chunks,
+// index = ((item * nkv + h) * 2 + j) * nquad + quad -> chunk xc0 + j, unit
+// kAttnSC * quad + wave. Blocks from ntail: shared chunks, index =
+// (item * nkv + h) * nsc + sc.
+template <int HD>
+__global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
+    const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
+    const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb, float* __restrict__ mix,
+    float* __restrict__ part, ModelDims D, int lam, int smul, int nsc_max, int ntail, int nquad, int nsc) {
+  __shared__ AttnSmem<HD> sm;
+  int b = blockIdx.x;
+  if (b < ntail) {
+    const int quad = b % nquad;
+    b /= nquad;
+    const int j = b % 2;
+    b /= 2;
+    const AttnItem it = items[b / D.nkv];
+    if (it.xc0 < 0) return;
+    attn_unit_chunk<HD>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * quad + (threadIdx.x >> 6), rows, q, kvc, exb, mix, D,
+                        lam, smul);
+    return;
+  }
+  b -= ntail;
+  const int sc = b % nsc;
+  b /= nsc;
+  const AttnItem it = items[b / D.nkv];
+  if (sc * kAttnSCKeys >= it.max_keys) return;
+  attn_shared_chunks<HD>(sm, it, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, smul, nsc_max);
+}
+
+// Fold the super-chunk states of each (row, query head) of an item in order
+// and normalise. Super-chunks holding per-unit chunks are first folded here
+// from their chunk partials, exactly as attn_kernel folds the others.
+// grid = (items, kv heads), block = 4 waves, one unit at a time per wave.
+template <int HD>
+__global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows,
+                                    const float* __restrict__ mix, const float* __restrict__ part,
+                                    float* __restrict__ out, int nq, int nkv, int nsc_max) {
+  constexpr int HS = HD / 64, HP = HD + 4;
+  const AttnItem it = items[blockIdx.x];
+  const int h = blockIdx.y, rep = nq / nkv, units = it.nrows * rep;
+  const int lane = threadIdx.x & 63;
+  for (int u = threadIdx.x >> 6; u < units; u += blockDim.x >> 6) {
     const int row = it.row0 + u / rep, qh = h * rep + u % rep;
     const RowInfo& R = rows[row];
-    if (pb >= R.ncommit + R.n_anc) continue;
-    float M = -INFINITY;
+    const int lim = R.ncommit + R.n_anc;
+    const int nsc = (lim + kAttnSCKeys - 1) / kAttnSCKeys;
+    const float* base = part + ((size_t)row * nq + qh) * nsc_max * HP;
+    const float* mbase = mix + ((size_t)row * nq + qh) * kMixSlots * HP;
+    float M = 0.f, L = 0.f, A[HS];
+    for (int sc = 0; sc < nsc; ++sc) {
+      float ms, ls, as[HS];
+      if (sc_mixed(it, sc)) {
+        const int cb = sc * kAttnSC;
+        const float* pc = mbase + (cb - kAttnSC * (it.xc0 / kAttnSC)) * HP;
+        ms = pc[HD];
+        ls = pc[HD + 1];
 #pragma unroll
-    for (int t = 0; t < kAttnWaves; ++t) M = fmaxf(M, red[t][u][HD]);
-    float Ls = 0.f, o[HS];
+        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
+        for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < lim; ++ww) {
+          const float* pw = pc + ww * HP;
+          float a[HS];
 #pragma unroll
-    for (int e = 0; e < HS; ++e) o[e] = 0.f;
+          for (int e = 0; e < HS; ++e) a[e] = pw[lane * HS + e];
+          fold<HS>(ms, ls, as, pw[HD], pw[HD + 1], a);
+        }
+      } else {
+        const float* pc = base + sc * HP;
+        ms = pc[HD];
+        ls = pc[HD + 1];
 #pragma unroll
-    for (int t = 0; t < kAttnWaves; ++t) {
-      const float f = exp2f(red[t][u][HD] - M);
-      Ls = fmaf(red[t][u][HD + 1], f, Ls);
+        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
+      }
+      if (sc == 0) {
+        M = ms;
+        L = ls;
 #pragma unroll
-      for (int e = 0; e < HS; ++e) o[e] = fmaf(red[t][u][lane * HS + e], f, o[e]);
+        for (int e = 0; e < HS; ++e) A[e] = as[e];
+      } else {
+        fold<HS>(M, L, A, ms, ls, as);
+      }
     }
-    float* dst = part + (((size_t)row * D.nq + qh) * nchunk + c) * HP;
+    const float inv = 1.0f / L;
+    float* dst = out + ((size_t)row * nq + qh) * HD;
 #pragma unroll
-    for (int e = 0; e < HS; ++e) dst[lane * HS + e] = o[e];
-    if (lane == 0) {
-      dst[HD] = M;
-      dst[HD + 1] = Ls;
-    }
+    for (int e = 0; e < HS; ++e) dst[lane * HS + e] = A[e] * inv;
   }
-}
-
-// Combine the split-KV chunks of a (row, head) in chunk order; one wave each.
-template <int HD>
-__global__ void attn_combine_kernel(const RowInfo* __restrict__ rows, int nrows, const float* __restrict__ part,
-                                    float* __restrict__ out, int nq, int nchunk) {
-  using G = AttnGeom<HD>;
-  constexpr int HS = G::HS, HP = HD + 2;
-  const int unit = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (unit >= nrows * nq) return;
-  const int row = unit / nq, qh = unit % nq;
-  const RowInfo& R = rows[row];
-  const int nc = (R.ncommit + R.n_anc + G::CHUNK - 1) / G::CHUNK;
-  const float* base = part + ((size_t)row * nq + qh) * nchunk * HP;
-  float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * HP + HD]);
-  float Ls = 0.f, o[HS];
-#pragma unroll
-  for (int e = 0; e < HS; ++e) o[e] = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float* pc = base + c * HP;
-    const float f = exp2f(pc[HD] - M);
-    Ls = fmaf(pc[HD + 1], f, Ls);
-#pragma unroll
-    for (int e = 0; e < HS; ++e) o[e] = fmaf(pc[lane * HS + e], f, o[e]);
-  }
-  const float inv = 1.0f / Ls;
-  float* dst = out + ((size_t)row * nq + qh) * HD;
-#pragma unroll
-  for (int e = 0; e < HS; ++e) dst[lane * HS + e] = o[e] * inv;
 }
 
 // ----------------------------------------------------------------------------
 // Host launcher
 // ----------------------------------------------------------------------------
-int attn_chunk(int hd) { return hd == 128 ? AttnGeom<128>::CHUNK : AttnGeom<64>::CHUNK; }
+int attn_chunk(int) { return kAttnSCKeys; }
+int attn_mix_slots() { return kMixSlots; }
 
+// umax: most units of an item whose rows read explore-buffer keys (lattice
+// rows), 0 when no row does.
 hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int nrows, const float* q,
-                            const float* kvc, const float* exb, float* part, float* out, const ModelDims& D,
-                            int lam, int smul, int nchunk, int max_keys, hipStream_t st) {
+                            const bf16_t* kvc, const bf16_t* exb, float* mix, float* part, float* out,
+                            const ModelDims& D, int lam, int smul, int nsc_max, int max_keys, int umax,
+                            hipStream_t st) {
+  (void)nrows;
   if (nitems == 0) return hipSuccess;
-  const int nc = (max_keys + attn_chunk(D.hd) - 1) / attn_chunk(D.hd);
-  dim3 grid(nitems, D.nkv, nc);
+  const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
+  if (nsc > nsc_max || umax > kAttnUnits) return hipErrorInvalidValue;
+  const int nquad = (umax + kAttnSC - 1) / kAttnSC;
+  const int ntail = nitems * D.nkv * 2 * nquad;
+  const dim3 grid(ntail + nitems * D.nkv * nsc);
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D, lam,
-                       smul, nchunk);
+    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, exb, mix, part, D,
+                       lam, smul, nsc_max, ntail, nquad, nsc);
   else
-    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(kAttnThreads), 0, st, items, rows, q, kvc, exb, part, D, lam,
-                       smul, nchunk);
+    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, exb, mix, part, D,
+                       lam, smul, nsc_max, ntail, nquad, nsc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int units = nrows * D.nq, wpb = 4;
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0, st, rows,
-                       nrows, part, out, D.nq, nchunk);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
+                       out, D.nq, D.nkv, nsc_max);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3((units + wpb - 1) / wpb), dim3(64 * wpb), 0, st, rows,
-                       nrows, part, out, D.nq, nchunk);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
+                       out, D.nq, D.nkv, nsc_max);
   return hipGetLastError();
 }
 
