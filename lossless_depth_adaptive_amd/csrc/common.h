@@ -120,6 +120,8 @@ struct AttnItem {
   int max_keys;     // max over the rows of ncommit + n_anc
   int xc0, xc1;     // chunks [xc0, xc1] may hold explore keys of some row (xc0 = -1: none);
                     // every row's explore keys lie in them
+  int lead;         // items (this one and the next lead - 1, same sequence and stage) the
+                    // attention block of this item covers; 0: covered by an earlier item
 };
 
 // K/V storage. Every K or V value x is kept as a bfloat16 pair (hi, lo) with

@@ -26,13 +26,15 @@ template <typename T>
 hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, int, int, int, int, int, hipStream_t);
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
+template <typename T>
+hipError_t launch_gemm_wide(const GemmArgs&, int, hipStream_t);
 hipError_t launch_head_reduce(const float*, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
 int attn_mix_slots();
 hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const float*, const bf16_t*, const bf16_t*,
-                            float*, float*, float*, const ModelDims&, int, int, int, int, int, hipStream_t);
+                            float*, float*, float*, const ModelDims&, int, int, int, int, int, bool, hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
                         const void*, float*, float*, float*, const float*, int, hipStream_t);
@@ -206,6 +208,7 @@ struct dex_ctx {
   hipStream_t cap_st = nullptr;   // private stream that round graphs are captured on
   bool prof = false;
   int attn_umax = 1;              // most units in one attention item of the current round
+  bool attn_groups = false;       // some attention item of the current pass leads a group of several
   std::vector<Mark> marks;
   size_t nmarks = 0;
   // HIP graphs of whole rounds, keyed by the round's plan
@@ -227,6 +230,39 @@ struct dex_ctx {
   } while (0)
 
 namespace {
+
+// Attention blocks: the items of one (sequence, stage) are covered in groups of
+// up to kAttnSC consecutive items; item i of n leads a group of this size (0:
+// inside a group).
+int attn_lead(int i, int n) { return i % kAttnSC ? 0 : std::min(kAttnSC, n - i); }
+
+// Groups of at least this many rows go to the wide GEMM kernel, the others to
+// the split-k kernel (both give a row the same bits).
+#ifndef DEX_WIDE_ROWS
+#define DEX_WIDE_ROWS 32
+#endif
+constexpr int kWideRows = DEX_WIDE_ROWS;
+
+// Launches grouped GEMMs over `groups` (kMaxGroups per launch, wide and
+// split-k groups apart); ga carries everything else. Counts launches.
+template <typename T>
+hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, hipStream_t st,
+                         int* launches) {
+  for (int wide = 0; wide < 2; ++wide) {
+    ga.ngroups = 0;
+    for (size_t i = 0; i <= groups.size(); ++i) {
+      const bool flush = i == groups.size() || ga.ngroups == kMaxGroups;
+      if (flush && ga.ngroups) {
+        const hipError_t e = wide ? launch_gemm_wide<T>(ga, epi, st) : launch_gemm<T>(ga, epi, st);
+        if (e != hipSuccess) return e;
+        ++*launches;
+        ga.ngroups = 0;
+      }
+      if (i < groups.size() && (groups[i].m >= kWideRows) == (wide == 1)) ga.g[ga.ngroups++] = groups[i];
+    }
+  }
+  return hipSuccess;
+}
 
 // Opens a timed region of class `cls`; returns its mark index or -1.
 int prof_begin(dex_ctx* ctx, int cls) {
@@ -345,13 +381,8 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     }
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
     int launches = 0;
-    for (size_t g0 = 0; g0 < glist.size(); g0 += kMaxGroups) {
-      ga.ngroups = (int)std::min(glist.size() - g0, (size_t)kMaxGroups);
-      for (int i = 0; i < ga.ngroups; ++i) ga.g[i] = glist[g0 + i];
-      const hipError_t e = launch_gemm<T>(ga, epi, st);
-      if (e != hipSuccess) return e;
-      ++launches;
-    }
+    const hipError_t e = launch_groups<T>(ga, glist, epi, st, &launches);
+    if (e != hipSuccess) return e;
     prof_end(ctx, mk, launches, bytes, flops);
     return hipSuccess;
   };
@@ -384,7 +415,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     int mk = prof_begin(ctx, DEX_PROF_ATTN);
     HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail,
                             ctx->attn_part, (float*)ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys,
-                            smul != 0 ? ctx->attn_umax : 0, st));
+                            smul != 0 ? ctx->attn_umax : 0, ctx->attn_groups, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
     groups_for(lam, ctx->wp.wo, 1);
     ga.K = nq * hd;
@@ -428,18 +459,9 @@ int run_head(dex_ctx* ctx, int nrows) {
   const double es = sizeof(T);
   const int mk = prof_begin(ctx, DEX_PROF_HEAD);
   int launches = 1;
-  for (int r0 = 0; r0 < nrows; r0 += 64 * kMaxGroups) {
-    ++launches;
-    ga.ngroups = 0;
-    for (int o = r0; o < std::min(nrows, r0 + 64 * kMaxGroups); o += 64) {
-      ga.g[ga.ngroups].w = ctx->head;
-      ga.g[ga.ngroups].gamma = nullptr;
-      ga.g[ga.ngroups].row0 = o;
-      ga.g[ga.ngroups].m = std::min(64, nrows - o);
-      ++ga.ngroups;
-    }
-    HIPCHK(launch_gemm<T>(ga, EPI_HEAD, st));
-  }
+  std::vector<GemmGroup> groups;
+  for (int o = 0; o < nrows; o += 64) groups.push_back(GemmGroup{ctx->head, nullptr, o, std::min(64, nrows - o)});
+  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, st, &launches));
   HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, nrows, ctx->rows, D.P, ctx->cand, ctx->margin, st));
   prof_end(ctx, mk, launches, (double)D.V * D.d * es + (double)nrows * D.d * 4 + (double)nrows * (D.V / 16) * 12 * 2,
            2.0 * nrows * D.V * D.d);
@@ -501,6 +523,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   const int per_item = std::max(1, kAttnUnits / rep);
   int nitems = 0, max_keys = 0;
   ctx->attn_umax = 1;
+  ctx->attn_groups = false;
   for (int j = 0; j < N; ++j)
     for (int s = 0; s < B; ++s) {
       const int cnt = rows_seq_stage[(size_t)s * N + j];
@@ -514,6 +537,8 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
         // lattice rows: explore keys at [C, mk), at most two chunks
         it.xc0 = ar ? -1 : ctx->C_[s] / kKvTile;
         it.xc1 = ar ? -1 : (mk - 1) / kKvTile;
+        it.lead = attn_lead(o / per_item, (cnt + per_item - 1) / per_item);
+        ctx->attn_groups |= it.lead > 1;
         max_keys = std::max(max_keys, mk);
         ctx->attn_umax = std::max(ctx->attn_umax, it.nrows * rep);
       }
@@ -683,6 +708,7 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         r.kv_commit = 1;
       }
       int nitems = 0;
+      ctx->attn_groups = false;
       for (int o = 0; o < R; o += per_item) {
         AttnItem& it = ctx->h_items[nitems++];
         it.row0 = o;
@@ -690,6 +716,8 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         it.stage = 0;
         it.max_keys = p0 + o + it.nrows;
         it.xc0 = it.xc1 = -1;
+        it.lead = attn_lead(o / per_item, (R + per_item - 1) / per_item);
+        ctx->attn_groups |= it.lead > 1;
       }
       HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
       HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));

@@ -127,6 +127,131 @@ __global__ void pack_kernel(u32x4_t* __restrict__ dst, const T* __restrict__ s0,
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue of one 16-column output tile for rows [0, G.m) of group G. val(rl, c)
+// is the GEMM output of row rl, tile column c (before rstd); rs[rl] the row's
+// rstd (normalising epilogues); scr is LDS scratch of ROWS x 17 floats. All NT
+// threads of the block call it (it synchronises).
+template <int EPI, int NT, int ROWS, typename Val>
+__device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGroup& G, int tile, Val val,
+                                              const float* rs, float (*scr)[17]) {
+  const int ntiles = args.N >> 4;
+  constexpr int E = ROWS * 16;
+  if constexpr (EPI == EPI_RESID) {
+    // h += y for the tile's 16 columns; h * g for the next consumer (and the
+    // exit head at a stage's end); then the tile's sum of squares.
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int rl = e >> 4, c = e & 15;
+      if (rl >= G.m) continue;
+      const size_t o = (size_t)args.rows[G.row0 + rl].hrow * args.N + tile * 16 + c;
+      const float nv = args.hidden[o] + val(rl, c);
+      args.hidden[o] = nv;
+      if (G.gamma) args.xn[o] = nv * G.gamma[tile * 16 + c];
+      if (args.write_xh) args.xh[o] = nv * args.gfinal[tile * 16 + c];
+      scr[rl][c] = nv;
+    }
+    __syncthreads();
+    for (int rl = threadIdx.x; rl < G.m; rl += NT)
+      args.ssq[(size_t)args.rows[G.row0 + rl].hrow * ntiles + tile] = ssq16(scr[rl]);
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    for (int e = threadIdx.x; e < ROWS * 8; e += NT) {
+      const int rl = e >> 3, c = e & 7;
+      if (rl >= G.m) continue;
+      const float g = val(rl, c) * rs[rl], u = val(rl, c + 8) * rs[rl];
+      const float s = g / (1.0f + expf(-g));
+      ((float*)args.act)[(size_t)(G.row0 + rl) * (args.N >> 1) + tile * 8 + c] = s * u;
+    }
+  } else if constexpr (EPI == EPI_QKV) {
+    // RoPE on query/key pairs (columns c, c+8), K/V into the committed cache
+    // (autoregressive and prefill rows) or the node's explore slot.
+    const ModelDims& D = args.dims;
+    const int hd = D.hd, tph = hd >> 4;
+    const int head = tile / tph, u = tile - head * tph;
+    for (int e = threadIdx.x; e < ROWS * 8; e += NT) {
+      const int rl = e >> 3, c = e & 7;
+      if (rl >= G.m) continue;
+      const int row = G.row0 + rl;
+      const RowInfo& R = args.rows[row];
+      const float x1 = val(rl, c) * rs[rl], x2 = val(rl, c + 8) * rs[rl];
+      const int layer = R.stage * args.smul + args.lam;
+      // K/V go out as (hi, lo) bf16 pairs: committed tile or explore entry.
+      bf16_t* kvbase = nullptr;
+      int kv = 0;
+      if (head >= D.nq) {
+        kv = head < D.nq + D.nkv ? 0 : 1;
+        const int hh = head - D.nq - kv * D.nkv;
+        kvbase = R.kv_commit ? args.kvc + kv_head_base(D, R.seq, layer, hh)
+                             : args.exb + ex_base(D, R.seq, R.phys, args.lam, hh) + (size_t)kv * 2 * hd;
+      }
+      auto put = [&](int dd, float v) {
+        bf16_t hi, lo;
+        split_bf(v, hi, lo);
+        if (R.kv_commit) {
+          kvbase[kv_elem(hd, R.pos, kv, 0, dd)] = hi;
+          kvbase[kv_elem(hd, R.pos, kv, 1, dd)] = lo;
+        } else {
+          kvbase[dd] = hi;
+          kvbase[hd + dd] = lo;
+        }
+      };
+      if (kv == 1) {                         // values: natural column order
+        put(16 * u + c, x1);
+        put(16 * u + c + 8, x2);
+        continue;
+      }
+      const int i = 8 * u + c;
+      const float cs = args.cosT[(size_t)R.pos * (hd >> 1) + i], sn = args.sinT[(size_t)R.pos * (hd >> 1) + i];
+      const float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
+      if (head < D.nq) {
+        float* qd = args.qout + ((size_t)row * D.nq + head) * hd;
+        qd[i] = o1 * args.qscale;
+        qd[i + (hd >> 1)] = o2 * args.qscale;
+      } else {
+        put(i, o1);
+        put(i + (hd >> 1), o2);
+      }
+    }
+  } else {  // EPI_HEAD
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int rl = e >> 4, c = e & 15;
+      if (rl >= G.m) continue;
+      const float z = val(rl, c) * rs[rl];
+      const int row = G.row0 + rl;
+      const int n = tile * 16 + c;
+      const RowInfo& ri = args.rows[row];
+      if (args.out != nullptr && ri.final_) args.out[(size_t)ri.seq * args.N + n] = z;
+      float s = z;
+      if (!ri.final_) {
+        for (int i = 0; i < ri.n_mask; ++i)
+          if (ri.mask[i] == n) s = -INFINITY;
+      }
+      if (args.mode == 1)
+        s = s / args.tau + args.gumbel[((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N + n];
+      scr[rl][c] = s;
+    }
+    __syncthreads();
+    for (int rl = threadIdx.x; rl < ROWS; rl += NT) {
+      if (rl >= G.m) continue;
+      float best = scr[rl][0], second = -INFINITY;
+      int bi = 0;
+      for (int c = 1; c < 16; ++c) {
+        const float s = scr[rl][c];
+        if (s > best) {
+          second = best;
+          best = s;
+          bi = c;
+        } else if (s > second) {
+          second = s;
+        }
+      }
+      float* p = args.part + ((size_t)(G.row0 + rl) * ntiles + tile) * 3;
+      p[0] = best;
+      p[1] = __int_as_float(tile * 16 + bi);
+      p[2] = second;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Grouped GEMM. grid = (N/(16 NB) tile blocks, groups), block = 512 (8 waves =
 // the 8 k ranges). A workgroup covers NB adjacent 16-column tiles and reuses
 // each activation fragment for all of them.
@@ -155,6 +280,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 
   __shared__ float red[kKSplit][NB][MB * 256];
   __shared__ float rs_sh[MB * 16];
+  __shared__ float scr[MB * 16][17];
 
   const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile0 * KS * 64 + lane;
   f32x4_t acc[MB][NB];
@@ -237,131 +363,151 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
       for (int r = 0; r < 4; ++r) red[w][nb][(mb * 16 + (lane >> 4) * 4 + r) * 16 + col16] = acc[mb][nb][r];
   __syncthreads();
   for (int nb = 0; nb < NB; ++nb) {
-  const int tile = tile0 + nb;
-  auto total = [&](int e) {
-    float v = red[0][nb][e];
+    auto total = [&](int rl, int c) {
+      const int e = rl * 16 + c;
+      float v = red[0][nb][e];
 #pragma unroll
-    for (int q = 1; q < kKSplit; ++q) v += red[q][nb][e];
-    return v;
+      for (int q = 1; q < kKSplit; ++q) v += red[q][nb][e];
+      return v;
+    };
+    epilogue_tile<EPI, kGemmThreads, MB * 16>(args, G, tile0 + nb, total, rs_sh, scr);
+    if (NB > 1) __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Wide GEMM for groups of many rows. grid = (ceil(N / 256), groups), block = 4
+// waves; a block computes 64 rows x 16 column tiles, wave w the tiles
+// 4w .. 4w+3. The group's activation k-step (64 rows x KSTEP, fp32) is staged
+// in LDS once for the four waves; weight fragments stream from HBM as in
+// gemm_kernel. Each output is reduced exactly as there: the 8 k ranges
+// [KS r/8, KS (r+1)/8) are accumulated from zero by the same MFMA chain, in
+// order, and summed in range order, so a row gets the same bits from either
+// kernel and from any grouping.
+// ---------------------------------------------------------------------------
+constexpr int kWideThreads = 256;
+constexpr int kWideWT = 4;                       // 16-column tiles per wave
+constexpr int kWideBT = 4 * kWideWT;             // per block
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
+  constexpr int KSTEP = Mfma<T>::KSTEP, EPL = Mfma<T>::EPL;
+  constexpr int NA4 = 64 * KSTEP / 4 / kWideThreads;   // 16-byte A loads per thread per k-step
+  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
+  const int gi = blockIdx.y;
+  if (gi >= args.ngroups) return;
+  const GemmGroup G = args.g[gi];
+  const int ntiles = args.N >> 4;
+  const int tb0 = blockIdx.x * kWideBT;
+  const int K = args.K, KS = K / KSTEP;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int col16 = lane & 15, kq = (lane >> 4) * EPL;
+  const int t0 = tb0 + w * kWideWT;
+
+  struct Stage { float a[2][64][KSTEP + 4]; };
+  struct Out { float t[64][kWideBT * 16 + 4]; };
+  __shared__ union { Stage s; Out o; } sm;
+  __shared__ float rs_sh[64];
+  __shared__ float scr[64][17];
+
+  // This thread's A loads: float4 index i -> row i / (KSTEP / 4), quad i % (KSTEP / 4).
+  const float* asrc[NA4];
+  bool aval[NA4];
+#pragma unroll
+  for (int x = 0; x < NA4; ++x) {
+    const int i = threadIdx.x + x * kWideThreads, r = i / (KSTEP / 4), qd = i % (KSTEP / 4);
+    aval[x] = r < G.m;
+    const int rr = aval[x] ? r : 0;
+    const float* base = NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
+                             : (const float*)args.a + (size_t)(G.row0 + rr) * K;
+    asrc[x] = base + 4 * qd;
+  }
+  auto load_a = [&](int ks, f32x4_t* v) {
+#pragma unroll
+    for (int x = 0; x < NA4; ++x)
+      v[x] = aval[x] ? *(const f32x4_t*)(asrc[x] + (size_t)ks * KSTEP) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  };
+  auto store_a = [&](int buf, const f32x4_t* v) {
+#pragma unroll
+    for (int x = 0; x < NA4; ++x) {
+      const int i = threadIdx.x + x * kWideThreads, r = i / (KSTEP / 4), qd = i % (KSTEP / 4);
+      *(f32x4_t*)&sm.s.a[buf][r][4 * qd] = v[x];
+    }
+  };
+  const u32x4_t* wp = (const u32x4_t*)G.w + lane;
+  bool bval[kWideWT];
+#pragma unroll
+  for (int nb = 0; nb < kWideWT; ++nb) bval[nb] = t0 + nb < ntiles;
+  auto load_b = [&](int ks, u32x4_t* b) {
+#pragma unroll
+    for (int nb = 0; nb < kWideWT; ++nb)
+      b[nb] = bval[nb] ? __builtin_nontemporal_load(wp + ((size_t)(t0 + nb) * KS + ks) * 64) : u32x4_t{0u, 0u, 0u, 0u};
   };
 
-  constexpr int E = MB * 256;
-  if constexpr (EPI == EPI_RESID) {
-    // h += y for the tile's 16 columns; h * g for the next consumer (and the
-    // exit head at a stage's end); then the tile's sum of squares.
-    __shared__ float hs[MB * 16][16];
-    for (int e = threadIdx.x; e < E; e += kGemmThreads) {
-      const int rl = e >> 4, c = e & 15;
-      if (rl >= G.m) continue;
-      const size_t o = (size_t)args.rows[G.row0 + rl].hrow * args.N + tile * 16 + c;
-      const float nv = args.hidden[o] + total(e);
-      args.hidden[o] = nv;
-      if (G.gamma) args.xn[o] = nv * G.gamma[tile * 16 + c];
-      if (args.write_xh) args.xh[o] = nv * args.gfinal[tile * 16 + c];
-      hs[rl][c] = nv;
+  f32x4_t acc[4][kWideWT], tot[4][kWideWT];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kWideWT; ++nb) acc[mb][nb] = tot[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t apre[NA4];
+  u32x4_t bcur[kWideWT], bnext[kWideWT];
+  load_a(0, apre);
+  load_b(0, bcur);
+  int range = 0, rend = KS / kKSplit;
+  for (int ks = 0; ks < KS; ++ks) {
+    const int buf = ks & 1;
+    store_a(buf, apre);
+    if (ks + 1 < KS) {
+      load_a(ks + 1, apre);
+      load_b(ks + 1, bnext);
     }
     __syncthreads();
-    for (int rl = threadIdx.x; rl < G.m; rl += kGemmThreads)
-      args.ssq[(size_t)args.rows[G.row0 + rl].hrow * ntiles + tile] = ssq16(hs[rl]);
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    for (int e = threadIdx.x; e < MB * 128; e += kGemmThreads) {
-      const int rl = e >> 3, c = e & 7;
-      if (rl >= G.m) continue;
-      const float g = total(rl * 16 + c) * rs_sh[rl], u = total(rl * 16 + c + 8) * rs_sh[rl];
-      const float s = g / (1.0f + expf(-g));
-      ((float*)args.act)[(size_t)(G.row0 + rl) * (args.N >> 1) + tile * 8 + c] = s * u;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      float a[EPL];
+      const float* ar = &sm.s.a[buf][mb * 16 + col16][kq];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a[e] = ar[e];
+#pragma unroll
+      for (int nb = 0; nb < kWideWT; ++nb) Mfma<T>::mma(acc[mb][nb], a, bcur[nb]);
     }
-  } else if constexpr (EPI == EPI_QKV) {
-    // RoPE on query/key pairs (columns c, c+8), K/V into the committed cache
-    // (autoregressive and prefill rows) or the node's explore slot.
-    const ModelDims& D = args.dims;
-    const int hd = D.hd, tph = hd >> 4;
-    const int head = tile / tph, u = tile - head * tph;
-    for (int e = threadIdx.x; e < MB * 128; e += kGemmThreads) {
-      const int rl = e >> 3, c = e & 7;
-      if (rl >= G.m) continue;
-      const int row = G.row0 + rl;
-      const RowInfo& R = args.rows[row];
-      const float x1 = total(rl * 16 + c) * rs_sh[rl], x2 = total(rl * 16 + c + 8) * rs_sh[rl];
-      const int layer = R.stage * args.smul + args.lam;
-      // K/V go out as (hi, lo) bf16 pairs: committed tile or explore entry.
-      bf16_t* kvbase = nullptr;
-      int kv = 0;
-      if (head >= D.nq) {
-        kv = head < D.nq + D.nkv ? 0 : 1;
-        const int hh = head - D.nq - kv * D.nkv;
-        kvbase = R.kv_commit ? args.kvc + kv_head_base(D, R.seq, layer, hh)
-                             : args.exb + ex_base(D, R.seq, R.phys, args.lam, hh) + (size_t)kv * 2 * hd;
-      }
-      auto put = [&](int dd, float v) {
-        bf16_t hi, lo;
-        split_bf(v, hi, lo);
-        if (R.kv_commit) {
-          kvbase[kv_elem(hd, R.pos, kv, 0, dd)] = hi;
-          kvbase[kv_elem(hd, R.pos, kv, 1, dd)] = lo;
-        } else {
-          kvbase[dd] = hi;
-          kvbase[hd + dd] = lo;
+#pragma unroll
+    for (int nb = 0; nb < kWideWT; ++nb) bcur[nb] = bnext[nb];
+    if (ks + 1 == rend) {   // end of k range `range`: add its partial in range order
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < kWideWT; ++nb) {
+          tot[mb][nb] = range == 0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
+          acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-      };
-      if (kv == 1) {                         // values: natural column order
-        put(16 * u + c, x1);
-        put(16 * u + c + 8, x2);
-        continue;
-      }
-      const int i = 8 * u + c;
-      const float cs = args.cosT[(size_t)R.pos * (hd >> 1) + i], sn = args.sinT[(size_t)R.pos * (hd >> 1) + i];
-      const float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
-      if (head < D.nq) {
-        float* qd = args.qout + ((size_t)row * D.nq + head) * hd;
-        qd[i] = o1 * args.qscale;
-        qd[i + (hd >> 1)] = o2 * args.qscale;
-      } else {
-        put(i, o1);
-        put(i + (hd >> 1), o2);
-      }
-    }
-  } else {  // EPI_HEAD
-    __shared__ float sc[MB * 16][17];
-    for (int e = threadIdx.x; e < E; e += kGemmThreads) {
-      const int rl = e >> 4, c = e & 15;
-      if (rl >= G.m) continue;
-      const float z = total(e) * rs_sh[rl];
-      const int row = G.row0 + rl;
-      const int n = tile * 16 + c;
-      const RowInfo& ri = args.rows[row];
-      if (args.out != nullptr && ri.final_) args.out[(size_t)ri.seq * args.N + n] = z;
-      float s = z;
-      if (!ri.final_) {
-        for (int i = 0; i < ri.n_mask; ++i)
-          if (ri.mask[i] == n) s = -INFINITY;
-      }
-      if (args.mode == 1)
-        s = s / args.tau + args.gumbel[((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N + n];
-      sc[rl][c] = s;
-    }
-    __syncthreads();
-    for (int rl = threadIdx.x; rl < MB * 16; rl += kGemmThreads) {
-      if (rl >= G.m) continue;
-      float best = sc[rl][0], second = -INFINITY;
-      int bi = 0;
-      for (int c = 1; c < 16; ++c) {
-        const float s = sc[rl][c];
-        if (s > best) {
-          second = best;
-          best = s;
-          bi = c;
-        } else if (s > second) {
-          second = s;
-        }
-      }
-      float* p = args.part + ((size_t)(G.row0 + rl) * ntiles + tile) * 3;
-      p[0] = best;
-      p[1] = __int_as_float(tile * 16 + bi);
-      p[2] = second;
+      ++range;
+      rend = (KS * (range + 1)) / kKSplit;
     }
   }
-  if (NB > 1) __syncthreads();
+
+  if constexpr (NORM) {
+    const int nt = K >> 4;
+    for (int rl = w; rl < G.m; rl += kWideThreads / 64) {
+      const float* sq = args.ssq + (size_t)args.rows[G.row0 + rl].hrow * nt;
+      float s = 0.f;
+      for (int t = lane; t < nt; t += 64) s += sq[t];
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) rs_sh[rl] = 1.0f / sqrtf(s / (float)K + args.eps);
+    }
+  }
+  __syncthreads();   // the last k-step's LDS reads are done before the outputs overwrite them
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kWideWT; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + (lane >> 4) * 4 + r][(w * kWideWT + nb) * 16 + col16] = tot[mb][nb][r];
+  __syncthreads();
+  for (int tl = 0; tl < kWideBT && tb0 + tl < ntiles; ++tl) {
+    epilogue_tile<EPI, kWideThreads, 64>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
+                                         rs_sh, scr);
+    __syncthreads();
   }
 }
 
@@ -466,6 +612,21 @@ static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
   if (DEX_GEMM_NB > 1 && (a.N / 16) % DEX_GEMM_NB == 0) return launch_gemm_mb<T, DEX_GEMM_NB, EPI>(a, mb, st);
   return launch_gemm_mb<T, 1, EPI>(a, mb, st);
 }
+
+// Runs one grouped GEMM on the wide kernel (every group has many rows).
+template <typename T>
+hipError_t launch_gemm_wide(const GemmArgs& a, int epi, hipStream_t st) {
+  const dim3 grid((a.N / 16 + kWideBT - 1) / kWideBT, a.ngroups);
+  switch (epi) {
+    case EPI_QKV: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_QKV>), grid, dim3(kWideThreads), 0, st, a); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_RESID>), grid, dim3(kWideThreads), 0, st, a); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_SWIGLU>), grid, dim3(kWideThreads), 0, st, a); break;
+    default: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_HEAD>), grid, dim3(kWideThreads), 0, st, a); break;
+  }
+  return hipGetLastError();
+}
+template hipError_t launch_gemm_wide<float>(const GemmArgs&, int, hipStream_t);
+template hipError_t launch_gemm_wide<bf16_t>(const GemmArgs&, int, hipStream_t);
 
 // Runs one grouped GEMM; the MFMA row-block count is the largest group's.
 template <typename T>

@@ -160,8 +160,46 @@ template <int HD> struct AttnSmem {
       bf16_t qsh[2][kAttnUnits][HD + 8];   // queries as (hi, lo), rows padded by 16 bytes
     } m;
     bf16_t ev[kAttnSC][kMaxN][2 * HD];      // per wave: V hi, V lo of the unit's explore entries
+    bf16_t qt[kAttnSC][2][kAttnUnits][HD + 8];  // per wave: its tile's queries as (hi, lo)
   };
 };
+
+template <int NB>
+__device__ __forceinline__ void fold4(float& M, float& L, f32x4_t* A, float m, float l, const f32x4_t* a) {
+  const float Mn = fmaxf(M, m);
+  const float al = exp2f(M - Mn), be = exp2f(m - Mn);
+  L = fmaf(l, be, L * al);
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) A[b][r] = fmaf(a[b][r], be, A[b][r] * al);
+  M = Mn;
+}
+
+// Queries of a tile of units, split into (hi, lo), into LDS rows padded by 16
+// bytes. Threads t0, t0 + step, ... share the work.
+template <int HD>
+__device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], const AttnItem& it, int h,
+                                            const float* __restrict__ q, const ModelDims& D, int t0, int step) {
+  const int rep = D.nq / D.nkv, units = it.nrows * rep;
+  for (int t = t0; t < kAttnUnits * HD / 8; t += step) {
+    const int u = t / (HD / 8), d8 = 8 * (t % (HD / 8));
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (u < units) {
+      const float* qr = q + ((size_t)(it.row0 + u / rep) * D.nq + h * rep + u % rep) * HD + d8;
+      const f32x4_t a = *(const f32x4_t*)qr, b = *(const f32x4_t*)(qr + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[i] = a[i];
+        x[4 + i] = b[i];
+      }
+    }
+    u32x4_t hi, lo;
+    split8(x, hi, lo);
+    *(u32x4_t*)&dst[0][u][d8] = hi;
+    *(u32x4_t*)&dst[1][u][d8] = lo;
+  }
+}
 
 // Per-unit role: wave w computes chunk c (one of xc0, xc1) for unit u of the
 // item with that unit's own keys, into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
@@ -264,23 +302,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD>& sm, const AttnItem& it, int h, 
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int layer = it.stage * smul + lam;
   const int seq = rows[it.row0].seq;
-  for (int t = threadIdx.x; t < kAttnUnits * HD / 8; t += 64 * kAttnSC) {
-    const int u = t / (HD / 8), d8 = 8 * (t % (HD / 8));
-    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (u < units) {
-      const float* qr = q + ((size_t)(it.row0 + u / rep) * D.nq + h * rep + u % rep) * HD + d8;
-      const f32x4_t a = *(const f32x4_t*)qr, b = *(const f32x4_t*)(qr + 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[i] = a[i];
-        x[4 + i] = b[i];
-      }
-    }
-    u32x4_t hi, lo;
-    split8(x, hi, lo);
-    *(u32x4_t*)&qsh[0][u][d8] = hi;
-    *(u32x4_t*)&qsh[1][u][d8] = lo;
-  }
+  load_q_tile<HD>(qsh, it, h, q, D, threadIdx.x, 64 * kAttnSC);
   // This lane's unit n: key limit (0 past the tile).
   int lim = 0;
   if (n < units) {
@@ -375,10 +397,96 @@ __device__ void attn_shared_chunks(AttnSmem<HD>& sm, const AttnItem& it, int h, 
   }
 }
 
+// Tile role: wave w takes unit tile (item) first + w of a group of items of one
+// sequence and stage, and runs the super-chunk's chunks itself, folding them in
+// registers in the same order as attn_shared_chunks. The waves read the same
+// K/V chunks, so the group costs one pass over them from HBM.
+template <int HD>
+__device__ void attn_tile_chunks(AttnSmem<HD>& sm, const AttnItem* __restrict__ items, int first, int count, int h,
+                                 int sc, const RowInfo* __restrict__ rows, const float* __restrict__ q,
+                                 const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
+                                 const ModelDims& D, int lam, int smul, int nsc_max) {
+  constexpr int NB = HD / 16, HP = HD + 4;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const AttnItem it = items[first + min(w, count - 1)];
+  const bool active = w < count;
+  const int rep = D.nq / D.nkv, units = active ? it.nrows * rep : 0;
+  if (active) load_q_tile<HD>(sm.qt[w], it, h, q, D, lane, 64);
+  int lim = 0;
+  if (n < units) {
+    const RowInfo& R = rows[it.row0 + n / rep];
+    lim = R.ncommit + R.n_anc;
+  }
+  int vlim = lim;
+  for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
+  __syncthreads();
+  if (!active) return;
+  const int layer = it.stage * smul + lam;
+  const bf16_t* hb = kvc + kv_head_base(D, rows[it.row0].seq, layer, h);
+  const bool to_mix = sc_mixed(it, sc);
+  bf16_t (*qt)[kAttnUnits][HD + 8] = sm.qt[w];
+  float Ms = 0.f, Ls = 0.f;
+  f32x4_t As[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) As[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+  for (int k = 0; k < kAttnSC; ++k) {
+    const int c = sc * kAttnSC + k, p0 = c * kKvTile;
+    if (p0 >= vlim) break;
+    if (it.xc0 >= 0 && c >= it.xc0 && c <= it.xc1) continue;
+    const bf16_t* tb = hb + (size_t)c * 128 * HD;
+    auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
+      qh = *(const u32x4_t*)&qt[0][n][32 * s + 8 * g];
+      ql = *(const u32x4_t*)&qt[1][n][32 * s + 8 * g];
+    };
+    auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
+      const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
+      kh = *(const u32x4_t*)kp;
+      kl = *(const u32x4_t*)(kp + 32 * HD);
+    };
+    auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
+      const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
+      vh = *(const u32x4_t*)vp;
+      vl = *(const u32x4_t*)(vp + 32 * HD);
+      const int nv = vlim - (p0 + 8 * g);
+      if (nv < 8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const unsigned keep = (2 * i + 1 < nv ? 0xFFFF0000u : 0u) | (2 * i < nv ? 0xFFFFu : 0u);
+          vh[i] &= keep;
+          vl[i] &= keep;
+        }
+      }
+    };
+    unsigned valid8 = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim ? 1u : 0u) << i;
+    f32x4_t acc[NB];
+    float m, l;
+    chunk_partial<HD>(qsrc, ksrc, vsrc, valid8, acc, m, l);
+    if (n >= units || p0 >= lim) continue;
+    if (to_mix) {
+      const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
+      store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP, acc,
+                        m, l, g);
+    } else if (k == 0) {
+      Ms = m;
+      Ls = l;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) As[b] = acc[b];
+    } else {
+      fold4<NB>(Ms, Ls, As, m, l, acc);
+    }
+  }
+  if (to_mix || n >= units || sc * kAttnSCKeys >= lim) return;
+  const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
+  store_partial<HD>(part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP, As, Ms, Ls, g);
+}
+
 // One launch, block = kAttnSC waves. Blocks [0, ntail): per-unit chunks,
 // index = ((item * nkv + h) * 2 + j) * nquad + quad -> chunk xc0 + j, unit
-// kAttnSC * quad + wave. Blocks from ntail: shared chunks, index =
-// (item * nkv + h) * nsc + sc.
+// kAttnSC * quad + wave. Blocks from ntail: index = (item * nkv + h) * nsc + sc,
+// shared role for items that form a group of their own.
 template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
@@ -400,9 +508,24 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   b -= ntail;
   const int sc = b % nsc;
   b /= nsc;
-  const AttnItem it = items[b / D.nkv];
-  if (sc * kAttnSCKeys >= it.max_keys) return;
+  const int ii = b / D.nkv;
+  const AttnItem it = items[ii];
+  if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys) return;
   attn_shared_chunks<HD>(sm, it, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, smul, nsc_max);
+}
+
+// Groups of several items (tile role). grid = (items, kv heads, super-chunks);
+// blocks of items that do not lead such a group return at once.
+template <int HD>
+__global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
+    const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
+    const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam,
+    int smul, int nsc_max) {
+  __shared__ AttnSmem<HD> sm;
+  const int ii = blockIdx.x, sc = blockIdx.z;
+  const AttnItem it = items[ii];
+  if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys) return;
+  attn_tile_chunks<HD>(sm, items, ii, it.lead, blockIdx.y, sc, rows, q, kvc, mix, part, D, lam, smul, nsc_max);
 }
 
 // Fold the super-chunk states of each (row, query head) of an item in order
@@ -471,10 +594,10 @@ int attn_chunk(int) { return kAttnSCKeys; }
 int attn_mix_slots() { return kMixSlots; }
 
 // umax: most units of an item whose rows read explore-buffer keys (lattice
-// rows), 0 when no row does.
+// rows), 0 when no row does; groups: some item leads a group of several.
 hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int nrows, const float* q,
                             const bf16_t* kvc, const bf16_t* exb, float* mix, float* part, float* out,
-                            const ModelDims& D, int lam, int smul, int nsc_max, int max_keys, int umax,
+                            const ModelDims& D, int lam, int smul, int nsc_max, int max_keys, int umax, bool groups,
                             hipStream_t st) {
   (void)nrows;
   if (nitems == 0) return hipSuccess;
@@ -491,6 +614,17 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* ro
                        lam, smul, nsc_max, ntail, nquad, nsc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (groups) {
+    const dim3 ggrid(nitems, D.nkv, nsc);
+    if (D.hd == 128)
+      hipLaunchKernelGGL((attn_group_kernel<128>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
+                         D, lam, smul, nsc_max);
+    else
+      hipLaunchKernelGGL((attn_group_kernel<64>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
+                         D, lam, smul, nsc_max);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (D.hd == 128)
     hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
                        out, D.nq, D.nkv, nsc_max);
