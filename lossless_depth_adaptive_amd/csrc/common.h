@@ -15,6 +15,7 @@ constexpr int kGemmThreads = 512;    // 8 waves: fixed 8-way split of K
 constexpr int kKSplit = 8;
 constexpr int kMaxMB = 4;            // 16-row MFMA blocks per GEMM group (<= 64 rows)
 constexpr int kMaxGroups = 48;       // GEMM groups per launch
+constexpr int kSplitRows = 512;      // rows of one split-range wide GEMM launch
 constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item (one MFMA tile)
 constexpr int kKvTile = 32;          // positions per K/V cache tile = keys per attention chunk
 constexpr int kAttnSC = 4;           // chunks per attention super-chunk
@@ -69,6 +70,7 @@ struct GemmGroup {
   const float* gamma;   // EPI_RESID: RMSNorm weight of the row's next consumer (null: none)
   int row0;             // first row (activations A[row0 ...], row info rows[row0 ...])
   int m;                // rows, 1..64
+  int srow;             // split-range wide GEMM: the group's first row in the partial-sum scratch
 };
 
 enum Epilogue { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
@@ -111,6 +113,8 @@ struct GemmArgs {
   const float* gumbel;   // [batch][gumbel_rows][N]
   int gumbel_rows;
   float* part;      // [rows][N/16][3] partial top-2 per 16-column tile
+  // split-range wide GEMM: per k range r, scratch rows [r][kSplitRows][N] (fp32)
+  float* split;
 };
 
 struct AttnItem {

@@ -17,6 +17,7 @@
 #include <string>
 #include <unordered_map>
 #include <vector>
+#include <type_traits>
 
 #include "common.h"
 #include "dex.h"
@@ -26,8 +27,7 @@ template <typename T>
 hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, int, int, int, int, int, hipStream_t);
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
-template <typename T>
-hipError_t launch_gemm_wide(const GemmArgs&, int, hipStream_t);
+hipError_t launch_gemm_wide(const GemmArgs&, int, bool, hipStream_t);
 hipError_t launch_head_reduce(const float*, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
@@ -68,10 +68,10 @@ struct Layout {
 struct WsPlan {
   size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh;
   size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
-  size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq;
+  size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq, gemm_split;
   std::vector<size_t> wqkv, wo, wgu, wdown;
   size_t total;
-  int Rmax, nchunk;
+  int Rmax, nchunk, split_cols;
 };
 
 size_t esize(int dtype) { return dtype == DEX_DTYPE_BF16 ? 2 : 4; }
@@ -161,6 +161,8 @@ WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) 
   w.act = lay.take(R * F * 4);
   w.attn_part = lay.take(R * nq * w.nchunk * (hd + 4) * 4);
   w.attn_tail = lay.take(R * nq * attn_mix_slots() * (hd + 4) * 4);
+  w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
+  w.gemm_split = lay.take((size_t)kKSplit * kSplitRows * w.split_cols * 4);
   w.head_part = lay.take(R * (V / 16) * 3 * 4);
   w.total = lay.off;
   return w;
@@ -179,7 +181,7 @@ struct dex_ctx {
   char* ws;
   WsPlan wp;
   // device views
-  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q, *attn_part, *attn_tail, *head_part, *ssq;
+  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q, *attn_part, *attn_tail, *head_part, *ssq, *gemm_split;
   int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
   RowInfo* rows;
   SeqPlan* plans;
@@ -244,21 +246,40 @@ int attn_lead(int i, int n) { return i % kAttnSC ? 0 : std::min(kAttnSC, n - i);
 constexpr int kWideRows = DEX_WIDE_ROWS;
 
 // Launches grouped GEMMs over `groups` (kMaxGroups per launch, wide and
-// split-k groups apart); ga carries everything else. Counts launches.
+// split-k groups apart; wide ones only with bf16 weights); ga carries
+// everything else. A wide launch that would have few blocks runs split by k
+// range when its rows fit the scratch (split_cols: the scratch's row length).
+// Counts launches.
 template <typename T>
-hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, hipStream_t st,
-                         int* launches) {
+hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, int split_cols,
+                         hipStream_t st, int* launches) {
   for (int wide = 0; wide < 2; ++wide) {
     ga.ngroups = 0;
+    int rows = 0;
     for (size_t i = 0; i <= groups.size(); ++i) {
+      const bool is_wide = std::is_same<T, bf16_t>::value && i < groups.size() && groups[i].m >= kWideRows;
+      const bool mine = i < groups.size() && is_wide == (wide == 1);
       const bool flush = i == groups.size() || ga.ngroups == kMaxGroups;
       if (flush && ga.ngroups) {
-        const hipError_t e = wide ? launch_gemm_wide<T>(ga, epi, st) : launch_gemm<T>(ga, epi, st);
+        hipError_t e;
+        if (wide) {
+          const int blocks = ga.ngroups * ((ga.N / 16 + 7) / 8);
+          const bool split = blocks < 512 && rows <= kSplitRows && ga.N <= split_cols;
+          e = launch_gemm_wide(ga, epi, split, st);
+          *launches += split ? 2 : 1;
+        } else {
+          e = launch_gemm<T>(ga, epi, st);
+          ++*launches;
+        }
         if (e != hipSuccess) return e;
-        ++*launches;
         ga.ngroups = 0;
+        rows = 0;
       }
-      if (i < groups.size() && (groups[i].m >= kWideRows) == (wide == 1)) ga.g[ga.ngroups++] = groups[i];
+      if (mine) {
+        ga.g[ga.ngroups] = groups[i];
+        ga.g[ga.ngroups++].srow = rows;
+        rows += groups[i].m;
+      }
     }
   }
   return hipSuccess;
@@ -365,7 +386,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
       if (next_norm == 1) gamma = ctx->norms + (size_t)layer * 2 * d + d;                    // this layer's FFN norm
       if (next_norm == 2 && layer + 1 < ctx->L) gamma = ctx->norms + (size_t)(layer + 1) * 2 * d;  // next attention norm
       for (int o = 0; o < cnt; o += 64)
-        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o)});
+        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o), 0});
     }
   };
   auto run_gemm = [&](GemmArgs& ga, int epi) -> hipError_t {
@@ -381,7 +402,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     }
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
     int launches = 0;
-    const hipError_t e = launch_groups<T>(ga, glist, epi, st, &launches);
+    const hipError_t e = launch_groups<T>(ga, glist, epi, ctx->wp.split_cols, st, &launches);
     if (e != hipSuccess) return e;
     prof_end(ctx, mk, launches, bytes, flops);
     return hipSuccess;
@@ -404,6 +425,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
   ga.exb = ctx->exb;
   ga.smul = smul;
   ga.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
+  ga.split = ctx->gemm_split;
   ga.act = ctx->act;
   for (int lam = 0; lam < lam_count; ++lam) {
     ga.lam = lam;
@@ -460,8 +482,9 @@ int run_head(dex_ctx* ctx, int nrows) {
   const int mk = prof_begin(ctx, DEX_PROF_HEAD);
   int launches = 1;
   std::vector<GemmGroup> groups;
-  for (int o = 0; o < nrows; o += 64) groups.push_back(GemmGroup{ctx->head, nullptr, o, std::min(64, nrows - o)});
-  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, st, &launches));
+  for (int o = 0; o < nrows; o += 64) groups.push_back(GemmGroup{ctx->head, nullptr, o, std::min(64, nrows - o), 0});
+  ga.split = ctx->gemm_split;
+  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches));
   HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, nrows, ctx->rows, D.P, ctx->cand, ctx->margin, st));
   prof_end(ctx, mk, launches, (double)D.V * D.d * es + (double)nrows * D.d * 4 + (double)nrows * (D.V / 16) * 12 * 2,
            2.0 * nrows * D.V * D.d);
@@ -840,6 +863,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->act = ctx->at(wp.act);
   ctx->attn_part = (float*)ctx->at(wp.attn_part);
   ctx->attn_tail = (float*)ctx->at(wp.attn_tail);
+  ctx->gemm_split = (float*)ctx->at(wp.gemm_split);
   ctx->head_part = (float*)ctx->at(wp.head_part);
   auto fail = [&](int code) {
     g_create_error = ctx->err;

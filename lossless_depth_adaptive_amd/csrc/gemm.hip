@@ -376,72 +376,85 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 }
 
 // ---------------------------------------------------------------------------
-// Wide GEMM for groups of many rows. grid = (ceil(N / 256), groups), block = 4
-// waves; a block computes 64 rows x 16 column tiles, wave w the tiles
-// 4w .. 4w+3. The group's activation k-step (64 rows x KSTEP, fp32) is staged
-// in LDS once for the four waves; weight fragments stream from HBM as in
-// gemm_kernel. Each output is reduced exactly as there: the 8 k ranges
-// [KS r/8, KS (r+1)/8) are accumulated from zero by the same MFMA chain, in
+// Wide GEMM for groups of many rows (bf16 weights). grid = (groups,
+// ceil(N / (64 kWideWT)), 1 or 8 k ranges), block = 4 waves; a block computes
+// 64 rows x 4 kWideWT column tiles, wave w the tiles kWideWT w ... Each k-step's activations (64
+// rows x 32, fp32) are split once into bf16 (hi, lo) in an LDS stage shared by
+// the four waves; loads run kWideD k-steps ahead in registers. Each output is
+// reduced exactly as in gemm_kernel: the 8 k ranges [KS r/8, KS (r+1)/8) are
+// accumulated from zero by the same MFMA chain (hi then lo per k-step), in
 // order, and summed in range order, so a row gets the same bits from either
-// kernel and from any grouping.
+// kernel and from any grouping. SPLIT: the block takes k range blockIdx.z
+// only and leaves its partial in args.split for gemm_split_reduce_kernel.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
-constexpr int kWideWT = 4;                       // 16-column tiles per wave
+constexpr int kWideWT = 2;                       // 16-column tiles per wave
 constexpr int kWideBT = 4 * kWideWT;             // per block
+constexpr int kWideD = 3;                        // k-steps of loads in flight
+constexpr int kWideAP = 40;                      // LDS row pitch of a stage (bf16)
 
-template <typename T, int EPI>
+template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
-  constexpr int KSTEP = Mfma<T>::KSTEP, EPL = Mfma<T>::EPL;
-  constexpr int NA4 = 64 * KSTEP / 4 / kWideThreads;   // 16-byte A loads per thread per k-step
+  constexpr int KSTEP = 32;
   constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
-  const int gi = blockIdx.y;
+  const int gi = blockIdx.x;
   if (gi >= args.ngroups) return;
   const GemmGroup G = args.g[gi];
   const int ntiles = args.N >> 4;
-  const int tb0 = blockIdx.x * kWideBT;
+  const int tb0 = blockIdx.y * kWideBT;
   const int K = args.K, KS = K / KSTEP;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int col16 = lane & 15, kq = (lane >> 4) * EPL;
+  const int col16 = lane & 15, kg = lane >> 4;
   const int t0 = tb0 + w * kWideWT;
 
-  struct Stage { float a[2][64][KSTEP + 4]; };
+  struct Stage { bf16_t hi[2][64][kWideAP], lo[2][64][kWideAP]; };
   struct Out { float t[64][kWideBT * 16 + 4]; };
   __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[64];
   __shared__ float scr[64][17];
 
-  // This thread's A loads: float4 index i -> row i / (KSTEP / 4), quad i % (KSTEP / 4).
-  const float* asrc[NA4];
-  bool aval[NA4];
+  // A loads of this thread: rows ar and ar + 32, columns 4 aq .. 4 aq + 3.
+  const int ar = threadIdx.x >> 3, aq = threadIdx.x & 7;
+  const float* asrc[2];
+  bool aval[2];
 #pragma unroll
-  for (int x = 0; x < NA4; ++x) {
-    const int i = threadIdx.x + x * kWideThreads, r = i / (KSTEP / 4), qd = i % (KSTEP / 4);
+  for (int x = 0; x < 2; ++x) {
+    const int r = ar + 32 * x;
     aval[x] = r < G.m;
     const int rr = aval[x] ? r : 0;
     const float* base = NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
                              : (const float*)args.a + (size_t)(G.row0 + rr) * K;
-    asrc[x] = base + 4 * qd;
+    asrc[x] = base + 4 * aq;
   }
-  auto load_a = [&](int ks, f32x4_t* v) {
-#pragma unroll
-    for (int x = 0; x < NA4; ++x)
-      v[x] = aval[x] ? *(const f32x4_t*)(asrc[x] + (size_t)ks * KSTEP) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-  };
-  auto store_a = [&](int buf, const f32x4_t* v) {
-#pragma unroll
-    for (int x = 0; x < NA4; ++x) {
-      const int i = threadIdx.x + x * kWideThreads, r = i / (KSTEP / 4), qd = i % (KSTEP / 4);
-      *(f32x4_t*)&sm.s.a[buf][r][4 * qd] = v[x];
-    }
-  };
   const u32x4_t* wp = (const u32x4_t*)G.w + lane;
   bool bval[kWideWT];
 #pragma unroll
   for (int nb = 0; nb < kWideWT; ++nb) bval[nb] = t0 + nb < ntiles;
-  auto load_b = [&](int ks, u32x4_t* b) {
+
+  struct Pre {
+    f32x4_t a[2];
+    u32x4_t b[kWideWT];
+  };
+  auto load = [&](int ks, Pre& p) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      p.a[x] = aval[x] ? *(const f32x4_t*)(asrc[x] + (size_t)ks * KSTEP) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < kWideWT; ++nb)
-      b[nb] = bval[nb] ? __builtin_nontemporal_load(wp + ((size_t)(t0 + nb) * KS + ks) * 64) : u32x4_t{0u, 0u, 0u, 0u};
+      p.b[nb] = bval[nb] ? __builtin_nontemporal_load(wp + ((size_t)(t0 + nb) * KS + ks) * 64)
+                         : u32x4_t{0u, 0u, 0u, 0u};
+  };
+  auto stage_a = [&](int buf, const Pre& p) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      bf16_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) split_bf(p.a[x][e], h[e], l[e]);
+      unsigned hv[2] = {(unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16)};
+      unsigned lv[2] = {(unsigned)l[0] | ((unsigned)l[1] << 16), (unsigned)l[2] | ((unsigned)l[3] << 16)};
+      __builtin_memcpy(&sm.s.hi[buf][ar + 32 * x][4 * aq], hv, 8);
+      __builtin_memcpy(&sm.s.lo[buf][ar + 32 * x][4 * aq], lv, 8);
+    }
   };
 
   f32x4_t acc[4][kWideWT], tot[4][kWideWT];
@@ -449,43 +462,66 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < kWideWT; ++nb) acc[mb][nb] = tot[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  f32x4_t apre[NA4];
-  u32x4_t bcur[kWideWT], bnext[kWideWT];
-  load_a(0, apre);
-  load_b(0, bcur);
-  int range = 0, rend = KS / kKSplit;
-  for (int ks = 0; ks < KS; ++ks) {
-    const int buf = ks & 1;
-    store_a(buf, apre);
-    if (ks + 1 < KS) {
-      load_a(ks + 1, apre);
-      load_b(ks + 1, bnext);
-    }
-    __syncthreads();
+
+  const int kbeg = SPLIT ? (KS * (int)blockIdx.z) / kKSplit : 0;
+  const int kend = SPLIT ? (KS * ((int)blockIdx.z + 1)) / kKSplit : KS;
+  Pre pre[kWideD];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
-      float a[EPL];
-      const float* ar = &sm.s.a[buf][mb * 16 + col16][kq];
+  for (int j = 0; j < kWideD; ++j)
+    if (kbeg + j < kend) load(kbeg + j, pre[j]);
+  int range = 0, rend = SPLIT ? kend : KS / kKSplit;
+  for (int k0 = kbeg; k0 < kend; k0 += kWideD) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) a[e] = ar[e];
+    for (int j = 0; j < kWideD; ++j) {
+      const int ks = k0 + j;
+      if (ks >= kend) break;
+      const int buf = ks & 1;
+      stage_a(buf, pre[j]);
+      u32x4_t bcur[kWideWT];
 #pragma unroll
-      for (int nb = 0; nb < kWideWT; ++nb) Mfma<T>::mma(acc[mb][nb], a, bcur[nb]);
-    }
+      for (int nb = 0; nb < kWideWT; ++nb) bcur[nb] = pre[j].b[nb];
+      if (ks + kWideD < kend) load(ks + kWideD, pre[j]);
+      __syncthreads();
 #pragma unroll
-    for (int nb = 0; nb < kWideWT; ++nb) bcur[nb] = bnext[nb];
-    if (ks + 1 == rend) {   // end of k range `range`: add its partial in range order
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb) {
+        bf16x8_t ah, al;
+        __builtin_memcpy(&ah, &sm.s.hi[buf][mb * 16 + col16][8 * kg], 16);
+        __builtin_memcpy(&al, &sm.s.lo[buf][mb * 16 + col16][8 * kg], 16);
 #pragma unroll
         for (int nb = 0; nb < kWideWT; ++nb) {
-          tot[mb][nb] = range == 0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
-          acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          bf16x8_t bv;
+          __builtin_memcpy(&bv, &bcur[nb], 16);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[mb][nb], 0, 0, 0);
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[mb][nb], 0, 0, 0);
         }
-      ++range;
-      rend = (KS * (range + 1)) / kKSplit;
+      }
+      if (ks + 1 == rend) {   // end of k range `range`: add its partial in range order
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < kWideWT; ++nb) {
+            tot[mb][nb] = range == 0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
+            acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        ++range;
+        rend = (KS * (range + 1)) / kKSplit;
+      }
     }
   }
 
+  if constexpr (SPLIT) {
+    float* dst = args.split + ((size_t)blockIdx.z * kSplitRows + G.srow) * args.N;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kWideWT; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rl = mb * 16 + kg * 4 + r;
+          if (rl < G.m && t0 + nb < ntiles) dst[(size_t)rl * args.N + (t0 + nb) * 16 + col16] = tot[mb][nb][r];
+        }
+    return;
+  }
   if constexpr (NORM) {
     const int nt = K >> 4;
     for (int rl = w; rl < G.m; rl += kWideThreads / 64) {
@@ -502,13 +538,47 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 #pragma unroll
     for (int nb = 0; nb < kWideWT; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + (lane >> 4) * 4 + r][(w * kWideWT + nb) * 16 + col16] = tot[mb][nb][r];
+      for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * kWideWT + nb) * 16 + col16] = tot[mb][nb][r];
   __syncthreads();
   for (int tl = 0; tl < kWideBT && tb0 + tl < ntiles; ++tl) {
     epilogue_tile<EPI, kWideThreads, 64>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
                                          rs_sh, scr);
     __syncthreads();
   }
+}
+
+// Sum of a split-range wide GEMM's 8 range partials, in range order, then the
+// epilogue. grid = (groups, N/16 tiles), block = 256.
+template <int EPI>
+__global__ __launch_bounds__(kWideThreads) void gemm_split_reduce_kernel(const GemmArgs args) {
+  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
+  const GemmGroup G = args.g[blockIdx.x];
+  const int tile = blockIdx.y;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ float val[64][17];
+  __shared__ float rs_sh[64];
+  __shared__ float scr[64][17];
+  const size_t rstride = (size_t)kSplitRows * args.N;
+  for (int e = threadIdx.x; e < G.m * 16; e += kWideThreads) {
+    const int rl = e >> 4, c = e & 15;
+    const float* p = args.split + (size_t)(G.srow + rl) * args.N + tile * 16 + c;
+    float v = p[0];
+#pragma unroll
+    for (int q = 1; q < kKSplit; ++q) v += p[q * rstride];
+    val[rl][c] = v;
+  }
+  if constexpr (NORM) {
+    const int K = args.K, nt = K >> 4;
+    for (int rl = w; rl < G.m; rl += kWideThreads / 64) {
+      const float* sq = args.ssq + (size_t)args.rows[G.row0 + rl].hrow * nt;
+      float s = 0.f;
+      for (int t = lane; t < nt; t += 64) s += sq[t];
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) rs_sh[rl] = 1.0f / sqrtf(s / (float)K + args.eps);
+    }
+  }
+  __syncthreads();
+  epilogue_tile<EPI, kWideThreads, 64>(args, G, tile, [&](int rl, int c) { return val[rl][c]; }, rs_sh, scr);
 }
 
 // Exact merge of two (best, index, second) summaries: ties keep the lower id.
@@ -613,20 +683,28 @@ static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
   return launch_gemm_mb<T, 1, EPI>(a, mb, st);
 }
 
-// Runs one grouped GEMM on the wide kernel (every group has many rows).
-template <typename T>
-hipError_t launch_gemm_wide(const GemmArgs& a, int epi, hipStream_t st) {
-  const dim3 grid((a.N / 16 + kWideBT - 1) / kWideBT, a.ngroups);
+template <int EPI, bool SPLIT>
+static void wide_launch(const GemmArgs& a, hipStream_t st) {
+  const dim3 grid(a.ngroups, (a.N / 16 + kWideBT - 1) / kWideBT, SPLIT ? kKSplit : 1);
+  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT>), grid, dim3(kWideThreads), 0, st, a);
+  if (SPLIT) {
+    hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3(a.ngroups, a.N / 16), dim3(kWideThreads), 0, st, a);
+  }
+}
+
+// Runs one grouped GEMM with bf16 weights on the wide kernel (every group has
+// many rows). split: one block per k range, partial sums through args.split
+// (groups' srow set, rows < kSplitRows), then their in-order sum and the
+// epilogue.
+hipError_t launch_gemm_wide(const GemmArgs& a, int epi, bool split, hipStream_t st) {
   switch (epi) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_QKV>), grid, dim3(kWideThreads), 0, st, a); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_RESID>), grid, dim3(kWideThreads), 0, st, a); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_SWIGLU>), grid, dim3(kWideThreads), 0, st, a); break;
-    default: hipLaunchKernelGGL((gemm_wide_kernel<T, EPI_HEAD>), grid, dim3(kWideThreads), 0, st, a); break;
+    case EPI_QKV: split ? wide_launch<EPI_QKV, true>(a, st) : wide_launch<EPI_QKV, false>(a, st); break;
+    case EPI_RESID: split ? wide_launch<EPI_RESID, true>(a, st) : wide_launch<EPI_RESID, false>(a, st); break;
+    case EPI_SWIGLU: split ? wide_launch<EPI_SWIGLU, true>(a, st) : wide_launch<EPI_SWIGLU, false>(a, st); break;
+    default: split ? wide_launch<EPI_HEAD, true>(a, st) : wide_launch<EPI_HEAD, false>(a, st); break;
   }
   return hipGetLastError();
 }
-template hipError_t launch_gemm_wide<float>(const GemmArgs&, int, hipStream_t);
-template hipError_t launch_gemm_wide<bf16_t>(const GemmArgs&, int, hipStream_t);
 
 // Runs one grouped GEMM; the MFMA row-block count is the largest group's.
 template <typename T>
