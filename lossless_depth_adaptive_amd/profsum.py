@@ -10,9 +10,11 @@
       HBM bytes of the layer GEMMs from the FETCH_SIZE and WRITE_SIZE counter
       runs (KiB per dispatch), each scaled by what the same counter reads for a
       1 GiB device-to-device copy in the same process (bench.py
-      --copy-calibration), summed over the decode window's GEMM dispatches and
-      divided by their count; compared with the algorithmic bytes per launch
-      the library reported for the same rounds (bench.py run with --warmup 0).
+      --copy-calibration), summed over the layer-GEMM dispatches of the rounds
+      bench.py timed with HIP events (the last roofline.launches of the decode
+      window; run bench.py with --no-ar) and divided by their count; compared
+      with the algorithmic bytes per launch the library reported for the same
+      rounds.
 """
 
 import argparse
@@ -83,19 +85,19 @@ def traffic(fetch_db, write_db, bench_json, workload=None):
     f, w = _counters(fetch_db, "FETCH_SIZE"), _counters(write_db, "WRITE_SIZE")
     f_scale = GIB / (_calibration(f) * 1024.0)
     w_scale = GIB / (_calibration(w) * 1024.0)
-    fg, wg = _gemm_window(f), _gemm_window(w)
-    fetch = sum(v for _, _, v in fg) * 1024.0 * f_scale
-    write = sum(v for _, _, v in wg) * 1024.0 * w_scale
     bench = json.loads(open(bench_json).read().strip().splitlines()[-1])
     rl = bench["roofline"]
-    n = len(fg)
+    n = rl["launches"]
+    fg, wg = _gemm_window(f)[-n:], _gemm_window(w)[-n:]
+    fetch = sum(v for _, _, v in fg) * 1024.0 * f_scale
+    write = sum(v for _, _, v in wg) * 1024.0 * w_scale
     return dict(workload=workload or bench["config"]["workload"], launches=n,
                 fetch_bytes_per_launch=fetch / n, write_bytes_per_launch=write / max(1, len(wg)),
                 bytes_per_launch=fetch / n + write / max(1, len(wg)),
                 algorithmic_bytes_per_launch=rl["algorithmic_bytes_per_launch"],
                 fetch_scale=f_scale, write_scale=w_scale,
-                note="layer GEMM launches (exit head excluded) of the decode window; counters in KiB per "
-                     "dispatch scaled by a 1 GiB copy read/write in the same process")
+                note="layer GEMM launches (exit head excluded) of the HIP-event-timed rounds; counters in KiB "
+                     "per dispatch scaled by a 1 GiB copy read/write in the same process")
 
 
 def main(argv=None):
