@@ -153,22 +153,38 @@ __host__ __device__ inline size_t ex_base(const ModelDims& D, int seq, int phys,
   return ((((size_t)seq * D.P + phys) * D.S + lam) * D.nkv + h) * 4 * (size_t)D.hd;
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(((unsigned)v) << 16); }
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  unsigned u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// Two floats to packed bfloat16 (a in the low half), round-to-nearest-even
+// (v_cvt_pk_bf16_f32). Every float-to-bf16 rounding of the library goes
+// through here, so all kernels round identically.
+__device__ __forceinline__ unsigned f2bf2(float a, float b) {
+  const f32x2_t f = {a, b};
+  const bf16x2_t v = __builtin_convertvector(f, bf16x2_t);
+  unsigned u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(f2bf2(f, 0.f) & 0xFFFFu); }
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
 template <typename T> __device__ __forceinline__ T from_f(float v);
 template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+// The (hi, lo) bfloat16 pairs of two values, packed (a in the low halves).
+__device__ __forceinline__ void split_bf2(float a, float b, unsigned& hi, unsigned& lo) {
+  hi = f2bf2(a, b);
+  lo = f2bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
 // The (hi, lo) bfloat16 pair of x described above.
 __device__ __forceinline__ void split_bf(float x, bf16_t& hi, bf16_t& lo) {
-  hi = f2bf(x);
-  lo = f2bf(x - bf2f(hi));
+  unsigned h, l;
+  split_bf2(x, 0.f, h, l);
+  hi = (bf16_t)(h & 0xFFFFu);
+  lo = (bf16_t)(l & 0xFFFFu);
 }
 
 // Host-visible kernel launchers (defined in the .hip files).

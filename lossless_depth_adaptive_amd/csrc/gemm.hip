@@ -49,13 +49,10 @@ template <> struct Mfma<bf16_t> {
   static constexpr int KSTEP = 32;
   static constexpr int EPL = 8;      // elements per lane per k-step
   __device__ __forceinline__ static void mma(f32x4_t& acc, const float* f, const u32x4_t& b) {
-    bf16x8_t hi, lo, bv;
-    unsigned short h[8], l[8];
+    unsigned h[4], l[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      h[i] = f2bf(f[i]);
-      l[i] = f2bf(f[i] - bf2f(h[i]));
-    }
+    for (int i = 0; i < 4; ++i) split_bf2(f[2 * i], f[2 * i + 1], h[i], l[i]);
+    bf16x8_t hi, lo, bv;
     __builtin_memcpy(&hi, h, 16);
     __builtin_memcpy(&lo, l, 16);
     __builtin_memcpy(&bv, &b, 16);
@@ -386,6 +383,8 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 // order, and summed in range order, so a row gets the same bits from either
 // kernel and from any grouping. SPLIT: the block takes k range blockIdx.z
 // only and leaves its partial in args.split for gemm_split_reduce_kernel.
+// Weight loads are ordinary (cached) loads: the row groups of a stage read
+// the same tile at about the same time and should meet in L2.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
 constexpr int kWideWT = 2;                       // 16-column tiles per wave
@@ -441,17 +440,14 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
       p.a[x] = aval[x] ? *(const f32x4_t*)(asrc[x] + (size_t)ks * KSTEP) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nb = 0; nb < kWideWT; ++nb)
-      p.b[nb] = bval[nb] ? __builtin_nontemporal_load(wp + ((size_t)(t0 + nb) * KS + ks) * 64)
-                         : u32x4_t{0u, 0u, 0u, 0u};
+      p.b[nb] = bval[nb] ? wp[((size_t)(t0 + nb) * KS + ks) * 64] : u32x4_t{0u, 0u, 0u, 0u};
   };
   auto stage_a = [&](int buf, const Pre& p) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      bf16_t h[4], l[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) split_bf(p.a[x][e], h[e], l[e]);
-      unsigned hv[2] = {(unsigned)h[0] | ((unsigned)h[1] << 16), (unsigned)h[2] | ((unsigned)h[3] << 16)};
-      unsigned lv[2] = {(unsigned)l[0] | ((unsigned)l[1] << 16), (unsigned)l[2] | ((unsigned)l[3] << 16)};
+      unsigned hv[2], lv[2];
+      split_bf2(p.a[x][0], p.a[x][1], hv[0], lv[0]);
+      split_bf2(p.a[x][2], p.a[x][3], hv[1], lv[1]);
       __builtin_memcpy(&sm.s.hi[buf][ar + 32 * x][4 * aq], hv, 8);
       __builtin_memcpy(&sm.s.lo[buf][ar + 32 * x][4 * aq], lv, 8);
     }

@@ -63,11 +63,10 @@ __device__ __forceinline__ f32x4_t mma3(f32x4_t acc, const u32x4_t& ah, const u3
 __device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    bf16_t h0, l0, h1, l1;
-    split_bf(x[2 * i], h0, l0);
-    split_bf(x[2 * i + 1], h1, l1);
-    hi[i] = (unsigned)h0 | ((unsigned)h1 << 16);
-    lo[i] = (unsigned)l0 | ((unsigned)l1 << 16);
+    unsigned h, l;
+    split_bf2(x[2 * i], x[2 * i + 1], h, l);
+    hi[i] = h;
+    lo[i] = l;
   }
 }
 
