@@ -120,11 +120,21 @@ def _subtree(n: Node) -> List[Node]:
 
 def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = "greedy",
                tau: float = 1.0, gumbel=None, decs: bool = True,
-               forced: Optional[Sequence[int]] = None, stats: Optional[dict] = None) -> List[dict]:
+               forced: Optional[Sequence[int]] = None, stats: Optional[dict] = None,
+               single_exit: bool = False) -> List[dict]:
     """DEX decoding of T tokens. Returns one record per commit:
     token, b, layers (= d_b), u (anchor candidates), margins, rounds (rounds
     since the previous commit). ``stats`` (optional dict) receives per-round
-    node counts per explorer under "rows_per_round"."""
+    node counts per explorer under "rows_per_round".
+
+    single_exit: the single-exit ablation of "Depth Exploration for LLM
+    Decoding", Section 4 (Figure 4, right-top): intermediate depth branches
+    are disabled, so only the first and the final explorer expose candidates.
+    Reading: a node of an intermediate explorer is still computed (the chain
+    must reach the final depth) but does not exit, so it proposes no token and
+    has no position child; the commit keeps branch 0 when u_0 matches and the
+    final depth otherwise. Unmasked candidates follow (no shallower proposal
+    exists in a chain)."""
     N, P = len(X), len(prompt)
     ev.begin(list(prompt))
     anchor_tok = int(prompt[-1])
@@ -136,7 +146,7 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
     rows_log, nodes_log = [], []
     while len(recs) < T:
         tree = _subtree(root) if root is not None else []
-        assert len(tree) == 2 ** q - 1, "state q must hold 2^q - 1 nodes"
+        assert len(tree) == (q * (q + 1) // 2 if single_exit else 2 ** q - 1), "nodes held at state q"
         # expand
         if q == 0:
             root = Node(etk=0, slot=(anchor_tok,), k=0, prior=[], round=rnd)
@@ -150,6 +160,8 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
                              parent=f.etk, kind="depth")
                     f.depth_child = c
                     new.append(c)
+                if f.cand is None:
+                    continue                           # a node that did not exit
                 c = Node(etk=0, slot=f.slot + (f.cand,), k=0, prior=[], round=rnd,
                          parent=f.etk, kind="position")
                 f.pos_child = c
@@ -157,12 +169,18 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
             for c in new:
                 c.etk = etk
                 etk += 1
-        assert len(new) == 2 ** q, "a round at state q creates 2^q nodes"
+        if single_exit:
+            assert len(new) == q + 1, "a single-exit round at state q creates q + 1 nodes"
+        else:
+            assert len(new) == 2 ** q, "a round at state q creates 2^q nodes"
         ev.eval_slots([n.slot for n in new])
         # DECS + insert
         for n in new:
             final = n.k == N - 1
-            masked = [] if (final or not decs) else [p.cand for p in n.prior]
+            if single_exit and 0 < n.k < N - 1:
+                n.cand, n.margin = None, None
+                continue
+            masked = [] if (final or not decs) else [p.cand for p in n.prior if p.cand is not None]
             g = _gumbel_row(gumbel, ev.C + len(n.slot), P, mode)
             n.cand, n.margin, _ = decode(ev.logits(n.slot, X[n.k]), masked, mode, tau, g)
         rows_log.append([sum(1 for n in new if n.k == j) for j in range(N)])

@@ -145,3 +145,53 @@ def test_every_layer_explored_reaches_the_ead_oracle():
         assert ceil_x(r["ead_stab"], X) == r["ead_stab"]
         assert r["layers"] <= r["ead_stab"]
         assert r["layers"] == r["ead"]
+
+
+def _single_exit_expected(ar, X):
+    """Branch of the single-exit ablation, from the AR driver alone: the first
+    depth when its unmasked proposal is the committed token, else the final."""
+    N = len(X)
+    return [0 if r["cand_by_depth"][X[0] - 1] == r["token"] else N - 1 for r in ar]
+
+
+@pytest.mark.parametrize("N", [2, 3, 4, 6])
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_scripted_single_exit(N, mode):
+    """Single-exit ablation ("Depth Exploration for LLM Decoding", Section 4,
+    Figure 4 right-top): lossless; branch 0 exactly when the first depth's
+    proposal is the committed token, else the final depth; one node per
+    explorer 0..q in the round at state q; b + 1 rounds per commit."""
+    L = 12
+    X = sorted(set([round(L * (k + 1) / N) for k in range(N)]))
+    V = 13
+    prompt = [2, 7, 1, 8]
+    T = 60
+    G = np.random.default_rng(10 + N).gumbel(size=(T + N + 2, V)) if mode == "sample" else None
+    ar = ar_decode(ScriptedEvaluator(V, L, salt=N), prompt, T, X, mode=mode, tau=0.8, gumbel=G)
+    st = {}
+    dx = dex_decode(ScriptedEvaluator(V, L, salt=N), prompt, T, X, mode=mode, tau=0.8, gumbel=G,
+                    stats=st, single_exit=True)
+    assert [r["token"] for r in dx] == [r["token"] for r in ar]
+    bs = [r["b"] for r in dx]
+    assert bs == _single_exit_expected(ar, X)
+    assert [r["layers"] for r in dx] == [X[b] for b in bs]
+    assert set(bs) == ({0, N - 1} if N > 1 else {0}), "scripted model must hit and miss the first depth"
+    assert [r["rounds"] for r in dx] == [N] + [b + 1 for b in bs[:-1]]
+    for rows in st["rows_per_round"]:
+        k = sum(rows)
+        assert rows == [1] * k + [0] * (N - k)
+
+
+@pytest.mark.parametrize("variant", [
+    ("tiny_f32", dict(), 40),
+    ("tiny_f32", dict(mode="sample", tau=1.0, seed_g=3001), 40),
+])
+def test_real_model_single_exit(variant):
+    name, kw, T = variant
+    w, m = _real(name, **kw)
+    p = prompt_ids(w.prompt_dist, w.vocab, w.prompt_len, w.seed_p, 0)
+    G = gumbel_rows(w.seed_g, 1, T + len(w.X) + 1, w.vocab).numpy()[0] if w.mode == "sample" else None
+    ar = ar_decode(SlotEvaluator(m), p, T, w.X, mode=w.mode, tau=w.tau, gumbel=G)
+    dx = dex_decode(SlotEvaluator(m), p, T, w.X, mode=w.mode, tau=w.tau, gumbel=G, single_exit=True)
+    assert [r["token"] for r in dx] == [r["token"] for r in ar]
+    assert [r["b"] for r in dx] == _single_exit_expected(ar, w.X)
