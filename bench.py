@@ -43,7 +43,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, Wd, prompts, commits):
+def cpu_baseline(w, Wd, prompts, commits, variant="dex"):
     """Time the oracle's DEX decoder (oracle/decode.py, as it stands) on the
     first ``commits`` commits of sequence 0, excluding its prefill."""
     import numpy as np
@@ -80,7 +80,8 @@ def cpu_baseline(w, Wd, prompts, commits):
 
     g = gumbel_rows(w.seed_g, 1, commits + len(w.X), w.vocab)[0].numpy() if w.mode == "sample" else None
     t2 = time.time()
-    recs = dex_decode(Prefilled(ev), prompts[0], commits, w.X, mode=w.mode, tau=w.tau, gumbel=g)
+    recs = dex_decode(Prefilled(ev), prompts[0], commits, w.X, mode=w.mode, tau=w.tau, gumbel=g,
+                      decs=variant != "vanilla", single_exit=variant == "single_exit")
     t_dec = time.time() - t2
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else 1
@@ -99,6 +100,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b_x4_greedy")
     ap.add_argument("--cpu-commits", type=int, default=6)
+    ap.add_argument("--variant", choices=["dex", "single_exit", "vanilla"], default="dex",
+                    help="dex: full depth exploration with DECS; single_exit: only the first and final "
+                         "explorers propose (ablation of Section 4, Figure 4 right-top); vanilla: DECS off "
+                         "(Figure 4 right-bottom)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ar", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gemm_llama7b_x4_greedy.json"),
@@ -134,7 +139,8 @@ def main():
     cfg = D.model_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.d_ffn, w.vocab,
                          w.rope_base, w.eps, w.tied, w.dtype)
     max_ctx = w.prompt_len + T + N + 8
-    opt = D.options(w.mode, w.tau, True, w.batch, max_ctx, T, gum, False)
+    opt = D.options(w.mode, w.tau, args.variant != "vanilla", w.batch, max_ctx, T, gum, False,
+                    single_exit=args.variant == "single_exit")
     ctx = D.Dex(cfg, Wd, w.X, opt)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -212,7 +218,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, Wd, prompts, args.cpu_commits)
+        cpu = cpu_baseline(w, Wd, prompts, args.cpu_commits, args.variant)
 
     layers = [c["layers"] for c in commits]
     out = {
@@ -229,7 +235,8 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded random-init weights and prompts)",
         "config": {"workload": w.name, "layers": w.n_layers, "d_model": w.d_model, "X": list(w.X),
-                   "batch": w.batch, "prompt_len": w.prompt_len, "max_new_tokens": T, "mode": w.mode},
+                   "batch": w.batch, "prompt_len": w.prompt_len, "max_new_tokens": T, "mode": w.mode,
+                   "variant": args.variant},
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "tokens"},
         "dex": {"commits": len(commits), "mean_layers_per_token": round(float(np.mean(layers)), 3) if layers else None,

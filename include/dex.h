@@ -106,6 +106,11 @@ typedef struct {
                               bit 1: launch every round eagerly (no HIP-graph replay). By default a
                               round whose plan (FSM states, commit flags, attention chunk count) was
                               seen before is captured once into a HIP graph and replayed. */
+  int32_t single_exit;     /* 1: the single-exit ablation ("Depth Exploration for LLM Decoding",
+                              Section 4, Figure 4 right-top): only explorers 0 and N-1 exit; the
+                              intermediate ones run without proposing, so only explorer-0 nodes
+                              spawn position children and a commit keeps branch 0 or N-1. The
+                              round at state q has one row per explorer 0..q. 0: full DEX. */
 } dex_options;
 
 /* One committed token (Algorithm 1, validate_and_commit). */

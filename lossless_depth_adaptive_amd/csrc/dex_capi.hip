@@ -28,7 +28,7 @@ hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, i
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
 hipError_t launch_gemm_wide(const GemmArgs&, int, bool, hipStream_t);
-hipError_t launch_head_reduce(const float*, int, int, const RowInfo*, int, int*, float*, hipStream_t);
+hipError_t launch_head_reduce(const float*, int, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
@@ -37,9 +37,9 @@ hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const flo
                             float*, float*, float*, const ModelDims&, int, int, int, int, int, bool, hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
-                        const void*, float*, float*, float*, const float*, int, hipStream_t);
+                        const void*, float*, float*, float*, const float*, int, int, hipStream_t);
 hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
-                         float*, const int*, int, int, hipStream_t);
+                         float*, const int*, int, int, int, hipStream_t);
 hipError_t launch_promote(const SeqPlan*, int, const int*, const bf16_t*, bf16_t*, const ModelDims&, hipStream_t);
 hipError_t launch_ar_rows(const SeqPlan*, int, RowInfo*, const int*, int, hipStream_t);
 hipError_t launch_ar_commit(const SeqPlan*, int, const int*, const float*, int*, int*, int*, float*, int, int,
@@ -104,6 +104,7 @@ int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex
   if (o->max_context < 2) { err = "max_context must be at least 2"; return DEX_EINVAL; }
   if (o->max_new_tokens < 1) { err = "max_new_tokens must be positive"; return DEX_EINVAL; }
   if (o->mode != DEX_GREEDY && o->mode != DEX_SAMPLE) { err = "mode must be GREEDY or SAMPLE"; return DEX_EINVAL; }
+  if (o->single_exit != 0 && o->single_exit != 1) { err = "single_exit must be 0 or 1"; return DEX_EINVAL; }
   if (o->mode == DEX_SAMPLE) {
     if (!(o->temperature > 0)) { err = "temperature must be positive"; return DEX_EINVAL; }
     if (!o->gumbel) { err = "sampling needs Gumbel rows"; return DEX_EINVAL; }
@@ -237,6 +238,13 @@ namespace {
 // up to kAttnSC consecutive items; item i of n leads a group of this size (0:
 // inside a group).
 int attn_lead(int i, int n) { return i % kAttnSC ? 0 : std::min(kAttnSC, n - i); }
+
+// Single-exit ablation: heap node n exists when its path is position moves
+// followed by depth moves (n + 1 = (2^(a+1) - 1) 2^b).
+bool single_exit_node(int n) {
+  const unsigned t = (unsigned)(n + 1) >> __builtin_ctz(n + 1);
+  return (t & (t + 1)) == 0;
+}
 
 // Groups of at least this many rows go to the wide GEMM kernel, the others to
 // the split-k kernel (both give a row the same bits).
@@ -458,10 +466,11 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
   return DEX_OK;
 }
 
-// Exit head for every row: final RMSNorm (fused), LM head, DECS mask and
-// Gumbel perturbation in the GEMM epilogue, then the per-row argmax reduce.
+// Exit head for the rows of `ranges` (first row, count): final RMSNorm
+// (fused), LM head, DECS mask and Gumbel perturbation in the GEMM epilogue,
+// then the per-row argmax reduce.
 template <typename T>
-int run_head(dex_ctx* ctx, int nrows) {
+int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
   const ModelDims& D = ctx->D;
   hipStream_t st = ctx->st;
   GemmArgs ga;
@@ -480,12 +489,20 @@ int run_head(dex_ctx* ctx, int nrows) {
   ga.part = ctx->head_part;
   const double es = sizeof(T);
   const int mk = prof_begin(ctx, DEX_PROF_HEAD);
-  int launches = 1;
+  int launches = 0, nrows = 0;
   std::vector<GemmGroup> groups;
-  for (int o = 0; o < nrows; o += 64) groups.push_back(GemmGroup{ctx->head, nullptr, o, std::min(64, nrows - o), 0});
+  for (const auto& rg : ranges) {
+    for (int o = 0; o < rg.second; o += 64)
+      groups.push_back(GemmGroup{ctx->head, nullptr, rg.first + o, std::min(64, rg.second - o), 0});
+    nrows += rg.second;
+  }
   ga.split = ctx->gemm_split;
   HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches));
-  HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, nrows, ctx->rows, D.P, ctx->cand, ctx->margin, st));
+  for (const auto& rg : ranges) {
+    HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, rg.first, rg.second, ctx->rows, D.P, ctx->cand, ctx->margin,
+                              st));
+    ++launches;
+  }
   prof_end(ctx, mk, launches, (double)D.V * D.d * es + (double)nrows * D.d * 4 + (double)nrows * (D.V / 16) * 12 * 2,
            2.0 * nrows * D.V * D.d);
   return DEX_OK;
@@ -508,6 +525,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     for (int j = 0; j < N; ++j) {
       int r = 0;
       if (ar) r = j == 0 ? 1 : 0;
+      else if (ctx->opt.single_exit) r = j <= q ? 1 : 0;   // one node per explorer 0..q
       else if (j < q) r = 1 << (q - 1 - j);
       else if (j == q) r = 1;
       rows_seq_stage[(size_t)s * N + j] = r;
@@ -578,6 +596,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       for (int j = 0; j < N; ++j)
         if (rows_seq_stage[(size_t)s * N + j]) attn_bytes += C * kvrow;
       for (int n = (1 << q) - 1; n <= (1 << (q + 1)) - 2; ++n) {
+        if (ctx->opt.single_exit && !single_exit_node(n)) continue;
         const int anc = ar ? 0 : __builtin_popcount(n + 1);
         attn_bytes += anc * kvrow + ctx->D.nq * ctx->D.hd * 8.0;
         attn_flops += 4.0 * ctx->D.nq * ctx->D.hd * (C + anc);
@@ -600,7 +619,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     } else {
       HIPCHK(launch_sched<T>(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
                              ctx->D.P, ctx->opt.decs, ctx->embed, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms,
-                             ctx->D.d, st));
+                             ctx->D.d, ctx->opt.single_exit, st));
     }
     prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
     std::vector<std::pair<int, int>> stage_rows;
@@ -608,7 +627,15 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, true,
                            attn_bytes, attn_flops);
     if (rc) return rc;
-    rc = run_head<T>(ctx, R);
+    // Every row exits, except intermediate explorers in the single-exit ablation.
+    std::vector<std::pair<int, int>> exits;
+    if (!ar && ctx->opt.single_exit && N > 1) {
+      if (stage_tot[0]) exits.push_back({stage_off[0], stage_tot[0]});
+      if (stage_tot[N - 1]) exits.push_back({stage_off[N - 1], stage_tot[N - 1]});
+    } else {
+      exits.push_back({0, R});
+    }
+    rc = run_head<T>(ctx, exits);
     if (rc) return rc;
     mk = prof_begin(ctx, DEX_PROF_LATTICE);
     if (ncommit) {
@@ -617,7 +644,8 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
                                 ctx->dbg_m, ctx->D.P, ctx->L, st));
       } else {
         HIPCHK(launch_commit(ctx->plans, B, ctx->map, ctx->cand, ctx->margin, ctx->freel, ctx->cursor, ctx->anchor,
-                             ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P, st));
+                             ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P,
+                             ctx->opt.single_exit, st));
         HIPCHK(launch_promote(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
       }
       HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));

@@ -588,13 +588,15 @@ __device__ __forceinline__ void top2_merge(float& b, int& i, float& s, float b2,
   }
 }
 
-// One wave per row: reduce the per-tile summaries to the row's token and margin.
-__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int nrows,
+// One wave per row of [row0, row0 + nrows): reduce the per-tile summaries to
+// the row's token and margin.
+__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int row0, int nrows,
                                    const RowInfo* __restrict__ rows, int P, int* __restrict__ cand,
                                    float* __restrict__ margin) {
-  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (row >= nrows) return;
+  if (idx >= nrows) return;
+  const int row = row0 + idx;
   float b = -INFINITY, s = -INFINITY;
   int i = 0x7fffffff;
   for (int t = lane; t < ntiles; t += 64) {
@@ -718,12 +720,12 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
 
-hipError_t launch_head_reduce(const float* part, int ntiles, int nrows, const RowInfo* rows, int P,
+hipError_t launch_head_reduce(const float* part, int ntiles, int row0, int nrows, const RowInfo* rows, int P,
                               int* cand, float* margin, hipStream_t st) {
   if (nrows == 0) return hipSuccess;
   const int wpb = 4;
   hipLaunchKernelGGL(head_reduce_kernel, dim3((nrows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, part,
-                     ntiles, nrows, rows, P, cand, margin);
+                     ntiles, row0, nrows, rows, P, cand, margin);
   return hipGetLastError();
 }
 

@@ -23,17 +23,22 @@ namespace dex {
 // that start a slot (explorer 0): residual, residual times the first layer's
 // attention-norm weight, and per-16-column sums of squares (the inputs of the
 // fused RMSNorm of the next GEMM).
+// Single-exit ablation ("Depth Exploration for LLM Decoding", Section 4,
+// Figure 4 right-top): only explorer-0 nodes spawn position children, so the
+// round's nodes are those whose path is a run of position moves followed by
+// depth moves, n + 1 = (2^(a+1) - 1) 2^(q-a) for a = 0..q: one per explorer,
+// none of them masked.
 template <typename T>
 __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restrict__ rows,
                              int* __restrict__ map, const int* __restrict__ cand,
                              const int* __restrict__ freel, int* __restrict__ cursor,
                              const int* __restrict__ anchor_tok, int N, int P, int decs,
                              const T* __restrict__ E, float* __restrict__ hidden, float* __restrict__ xn,
-                             float* __restrict__ ssq, const float* __restrict__ g0, int d) {
+                             float* __restrict__ ssq, const float* __restrict__ g0, int d, int single_exit) {
   const int s = blockIdx.x;
   const SeqPlan pl = plans[s];
   if (!pl.live) return;
-  const int q = pl.q, nnew = 1 << q, first = nnew - 1;
+  const int q = pl.q, nnew = single_exit ? q + 1 : 1 << q, first = (1 << q) - 1;
   const int cur = cursor[s];
   __shared__ int nemb;
   __shared__ int emb_h[1 << (kMaxN - 1)];
@@ -43,12 +48,12 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
   int* mp = map + (size_t)s * P;
   const int* cd = cand + (size_t)s * P;
   for (int t = threadIdx.x; t < nnew; t += blockDim.x) {
-    const int n = first + t, n1 = n + 1;
+    const int n = single_exit ? (((2 << t) - 1) << (q - t)) - 1 : first + t, n1 = n + 1;
     const int depth = __builtin_ctz(n1);
     const int posoff = __popc(n1) - 1;
     const int phys = freel[(size_t)s * P + cur + t];
     mp[n] = phys;
-    const int idx = depth < q ? (((n1 >> depth) - (1 << (q - depth)) - 1) >> 1) : 0;
+    const int idx = single_exit || depth >= q ? 0 : (((n1 >> depth) - (1 << (q - depth)) - 1) >> 1);
     RowInfo R;
     R.seq = s;
     R.phys = phys;
@@ -75,7 +80,7 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
     R.n_anc = cnt;
     // Depth-coupled sampling: candidates of shallower members of the chain.
     R.n_mask = 0;
-    if (decs && depth < N - 1) {
+    if (decs && !single_exit && depth < N - 1) {
       for (int m = 0; m < depth; ++m) R.mask[m] = cd[mp[((root + 1) << m) - 1]];
       R.n_mask = depth;
     }
@@ -113,12 +118,15 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
 // position child (heap 2^(k+1)) becomes the new tree: relative node j at level
 // lv maps to old node (2^(k+1) + 1) 2^lv - 1 + (j + 1 - 2^lv), for the
 // 2^(N-1-k) - 1 nodes it holds. Free slots are rebuilt in increasing order.
+// Single-exit ablation: only u_0 and u_{N-1} exist (branch 0 or N-1), and only
+// the kept subtree's single-exit nodes hold slots.
 __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict__ map,
                               const int* __restrict__ cand, const float* __restrict__ margin,
                               int* __restrict__ freel, int* __restrict__ cursor,
                               int* __restrict__ anchor_tok, int* __restrict__ records,
                               int* __restrict__ promote_src, int* __restrict__ dbg_u,
-                              float* __restrict__ dbg_m, const int* __restrict__ Xd, int N, int P) {
+                              float* __restrict__ dbg_m, const int* __restrict__ Xd, int N, int P,
+                              int single_exit) {
   const int s = blockIdx.x;
   const SeqPlan pl = plans[s];
   if (!pl.live || !pl.commit) return;
@@ -130,10 +138,11 @@ __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict
   const int tid = threadIdx.x;
   if (tid < N) {
     const int p = mp[(1 << tid) - 1];
-    u[tid] = cand[(size_t)s * P + p];
+    const bool exits = !single_exit || tid == 0 || tid == N - 1;
+    u[tid] = exits ? cand[(size_t)s * P + p] : -1;
     promote_src[s * kMaxN + tid] = p;
     dbg_u[s * kMaxN + tid] = u[tid];
-    dbg_m[s * kMaxN + tid] = margin[(size_t)s * P + p];
+    dbg_m[s * kMaxN + tid] = exits ? margin[(size_t)s * P + p] : 0.f;
   }
   for (int p = tid; p < P; p += blockDim.x) used[p] = 0;
   __syncthreads();
@@ -160,12 +169,14 @@ __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict
   const int root = 1 << (k + 1);
   for (int j = tid; j < nk; j += blockDim.x) {
     const int lv = 31 - __builtin_clz(j + 1);
-    nm[j] = mp[((root + 1) << lv) - 1 + (j + 1 - (1 << lv))];
+    const unsigned t = (unsigned)(j + 1) >> __builtin_ctz(j + 1);
+    const bool held = !single_exit || (t & (t + 1)) == 0;
+    nm[j] = held ? mp[((root + 1) << lv) - 1 + (j + 1 - (1 << lv))] : -1;
   }
   __syncthreads();
   for (int j = tid; j < nk; j += blockDim.x) {
     mp[j] = nm[j];
-    used[nm[j]] = 1;
+    if (nm[j] >= 0) used[nm[j]] = 1;
   }
   __syncthreads();
   if (tid == 0) {
@@ -257,23 +268,23 @@ template <typename T>
 hipError_t launch_sched(const SeqPlan* plans, int nseq, RowInfo* rows, int* map, const int* cand,
                         const int* freel, int* cursor, const int* anchor_tok, int N, int P, int decs,
                         const void* E, float* hidden, float* xn, float* ssq, const float* g0, int d,
-                        hipStream_t st) {
+                        int single_exit, hipStream_t st) {
   hipLaunchKernelGGL(sched_kernel<T>, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
-                     anchor_tok, N, P, decs, (const T*)E, hidden, xn, ssq, g0, d);
+                     anchor_tok, N, P, decs, (const T*)E, hidden, xn, ssq, g0, d, single_exit);
   return hipGetLastError();
 }
 template hipError_t launch_sched<float>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
                                         const int*, int, int, int, const void*, float*, float*, float*, const float*,
-                                        int, hipStream_t);
+                                        int, int, hipStream_t);
 template hipError_t launch_sched<bf16_t>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
                                          const int*, int, int, int, const void*, float*, float*, float*, const float*,
-                                         int, hipStream_t);
+                                         int, int, hipStream_t);
 
 hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* cand, const float* margin,
                          int* freel, int* cursor, int* anchor_tok, int* records, int* promote_src,
-                         int* dbg_u, float* dbg_m, const int* Xd, int N, int P, hipStream_t st) {
+                         int* dbg_u, float* dbg_m, const int* Xd, int N, int P, int single_exit, hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3(nseq), dim3(256), 0, st, plans, map, cand, margin, freel, cursor,
-                     anchor_tok, records, promote_src, dbg_u, dbg_m, Xd, N, P);
+                     anchor_tok, records, promote_src, dbg_u, dbg_m, Xd, N, P, single_exit);
   return hipGetLastError();
 }
 

@@ -14,7 +14,8 @@ def device_weights(w):
     return generate(w, device="cuda")
 
 
-def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, gumbel=None, graphs=True):
+def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, gumbel=None, graphs=True,
+             single_exit=False):
     X = list(X or w.X)
     cfg = D.model_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.d_ffn,
                          w.vocab, w.rope_base, w.eps, w.tied, w.dtype)
@@ -22,7 +23,7 @@ def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, g
         max_context = w.prompt_len + T + len(X) + 8
     if w.mode == "sample" and gumbel is None:
         gumbel = gumbel_rows(w.seed_g, batch, T + len(X), w.vocab).cuda()
-    opt = D.options(w.mode, w.tau, decs, batch, max_context, T, gumbel, debug, graphs)
+    opt = D.options(w.mode, w.tau, decs, batch, max_context, T, gumbel, debug, graphs, single_exit)
     ctx = D.Dex(cfg, Wd, X, opt)
     ctx._gumbel = gumbel
     return ctx

@@ -100,6 +100,52 @@ def test_dex_parity(name):
     _run_case(name)
 
 
+@pytest.mark.parametrize("name", ["tiny", "tiny_sample", "llama7b_x8_sample_narrow", "qwen_gqa_x9_b4_narrow"])
+def test_single_exit_parity(name):
+    """Single-exit ablation ("Depth Exploration for LLM Decoding", Section 4,
+    Figure 4 right-top): the GPU stream equals GPU AR bit for bit; the branch
+    is 0 or N-1, and (where the oracle's first-depth and final decisions clear
+    the gate) 0 exactly when the first depth's unmasked proposal is the
+    committed token; N rounds to the first commit, then b + 1 per commit."""
+    from tests.gpu_helpers import device_weights, make_ctx, run
+    w, kw = CASES[name]
+    T = kw["T"]
+    N = len(w.X)
+    print(f"[case] single-exit {name} X={w.X} batch={w.batch} mode={w.mode} T={T}", flush=True)
+    Wd = device_weights(w)
+    prompts = batch_prompts(w)
+    gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab) if w.mode == "sample" else None
+    gum_d = gum.cuda() if gum is not None else None
+    ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum_d, single_exit=True)
+    se_recs, steps = run(ctx, prompts, T)
+    ctx.close()
+    ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum_d)
+    ar_recs, _ = run(ctx, prompts, T, ar=True)
+    ctx.close()
+    for s in range(w.batch):
+        assert [r["token"] for r in se_recs[s]] == [r["token"] for r in ar_recs[s]], f"seq {s}: single-exit != AR"
+        for a, b in zip(se_recs[s], ar_recs[s]):
+            assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+            assert a["branch"] in (0, N - 1) and a["layers"] == w.X[a["branch"]]
+    if w.batch == 1:
+        bs = [r["branch"] for r in se_recs[0]]
+        assert steps == N + sum(b + 1 for b in bs[:-1])
+    m = PlainModel(w, generate(w))
+    gate = 1e-3 if w.dtype == "f32" else 5e-2
+    checked = 0
+    for s in range(w.batch):
+        g = gum[s].numpy() if gum is not None else None
+        orc = ar_decode(SlotEvaluator(m), prompts[s], T, w.X, mode=w.mode, tau=w.tau, gumbel=g, decs=False,
+                        forced=[r["token"] for r in se_recs[s]], brute_ead=False)
+        for gr, o in zip(se_recs[s], orc):
+            if o["final_margin"] > gate and o["margins"][0] > gate:
+                assert gr["branch"] == (0 if o["u"][0] == o["token"] else N - 1), (gr, o["u"][0], o["token"])
+                checked += 1
+    total = sum(len(r) for r in se_recs)
+    print(f"[case] single-exit {name} steps={steps} branches checked={checked}/{total}", flush=True)
+    assert checked >= total // 4
+
+
 def test_error_codes_on_device():
     from lossless_depth_adaptive_amd import dex as D
     from tests.gpu_helpers import device_weights, make_ctx
