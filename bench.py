@@ -100,6 +100,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama7b_x4_greedy")
     ap.add_argument("--cpu-commits", type=int, default=6)
+    ap.add_argument("--X", default=None,
+                    help="comma-separated exploration set replacing the workload's (e.g. 4,12,20,32: stages "
+                         "of unequal length; the exploration-resolution study of Section 4)")
     ap.add_argument("--variant", choices=["dex", "single_exit", "vanilla"], default="dex",
                     help="dex: full depth exploration with DECS; single_exit: only the first and final "
                          "explorers propose (ablation of Section 4, Figure 4 right-top); vanilla: DECS off "
@@ -128,6 +131,8 @@ def main():
 
     torch.cuda.set_device(0)
     w = get_workload(args.workload)
+    if args.X:
+        w = w.scaled(X=tuple(int(x) for x in args.X.split(",")))
     N = len(w.X)
     T = max(w.gen, args.warmup + 2 * args.steps)
     t0 = time.time()

@@ -56,14 +56,22 @@ struct SeqPlan {
 
 struct ModelDims {
   int L, d, nq, nkv, hd, F, V;
-  int S;            // layers per stage
+  int S;            // layers of the longest stage (explore-buffer layer slots per node)
   int N;            // explorers
   int P;            // lattice node slots per sequence (2^N - 1)
   int B;            // max sequences
   int Cmax;         // max context
   int Cs;           // committed-cache positions per (sequence, layer, kv head): Cmax rounded up to kKvTile
   float eps;
+  int lfirst[kMaxN + 1];   // explorer j runs layers [lfirst[j], lfirst[j+1]) (d_{j-1} .. d_j - 1); lfirst[N] = L
 };
+
+// Layer of slot lam for a row of explorer `stage`: lattice rows run their
+// stage's layers, autoregressive and prefill rows (lattice = 0) every layer.
+__host__ __device__ inline int layer_of(const ModelDims& D, int lattice, int stage, int lam) {
+  return lattice ? D.lfirst[stage] + lam : lam;
+}
+__host__ __device__ inline int stage_len(const ModelDims& D, int j) { return D.lfirst[j + 1] - D.lfirst[j]; }
 
 struct GemmGroup {
   const void* w;        // packed weights of this group
@@ -71,6 +79,7 @@ struct GemmGroup {
   int row0;             // first row (activations A[row0 ...], row info rows[row0 ...])
   int m;                // rows, 1..64
   int srow;             // split-range wide GEMM: the group's first row in the partial-sum scratch
+  int xh;               // EPI_RESID: also write h * final-norm weight (the rows end their stage here)
 };
 
 enum Epilogue { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
@@ -91,9 +100,8 @@ struct GemmArgs {
   float* hidden;    // EPI_RESID: residual [*][N]
   float* ssq;       // [*][d/16]: read by normalising epilogues, written by EPI_RESID
   float* xn;        // EPI_RESID: h * gamma of the next consumer
-  float* xh;        // EPI_RESID: h * final-norm weight (when write_xh)
+  float* xh;        // EPI_RESID: h * final-norm weight (groups with xh set)
   const float* gfinal;
-  int write_xh;
   float eps;
   // EPI_QKV
   ModelDims dims;
@@ -102,7 +110,7 @@ struct GemmArgs {
   float* qout;      // [rows][nq][hd], pre-scaled by qscale
   bf16_t* kvc;      // committed K/V (tiles of (hi, lo) pairs)
   bf16_t* exb;      // explore-buffer K/V
-  int smul, lam;    // layer = stage * smul + lam
+  int lattice, lam;  // layer slot lam; layer = layer_of(dims, lattice, row's stage, lam)
   float qscale;
   // EPI_SWIGLU
   void* act;        // [rows][N/2] (fp32)
@@ -120,7 +128,7 @@ struct GemmArgs {
 struct AttnItem {
   int row0;         // first row
   int nrows;        // rows (all of one sequence and one layer), nrows * (nq / nkv) <= kAttnUnits
-  int stage;        // explorer of the rows; layer = stage * smul + lam
+  int stage;        // explorer of the rows; layer = layer_of(D, lattice, stage, lam)
   int max_keys;     // max over the rows of ncommit + n_anc
   int xc0, xc1;     // chunks [xc0, xc1] may hold explore keys of some row (xc0 = -1: none);
                     // every row's explore keys lie in them

@@ -97,9 +97,6 @@ int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex
     if (X[k] < 1 || (k > 0 && X[k] <= X[k - 1])) { err = "exploration set must be strictly increasing within [1, L]"; return DEX_EINVAL; }
   }
   if (X[n_x - 1] != c->n_layers) { err = "the last exploration depth must equal L"; return DEX_EINVAL; }
-  if (c->n_layers % n_x) { err = "L must be a multiple of the number of explorers"; return DEX_EINVAL; }
-  for (int k = 0; k < n_x; ++k)
-    if (X[k] != (k + 1) * (c->n_layers / n_x)) { err = "only uniformly spaced exploration sets are supported"; return DEX_EINVAL; }
   if (o->max_batch < 1 || o->max_batch > 64) { err = "max_batch must be 1..64"; return DEX_EINVAL; }
   if (o->max_context < 2) { err = "max_context must be at least 2"; return DEX_EINVAL; }
   if (o->max_new_tokens < 1) { err = "max_new_tokens must be positive"; return DEX_EINVAL; }
@@ -113,13 +110,20 @@ int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex
   return DEX_OK;
 }
 
-WsPlan plan_workspace(const dex_model_config* c, int n_x, const dex_options* o) {
+// Layers of the longest stage: max over j of d_j - d_{j-1} (d_{-1} = 0).
+int longest_stage(const int32_t* X, int n_x) {
+  int s = 0;
+  for (int j = 0; j < n_x; ++j) s = std::max(s, X[j] - (j ? X[j - 1] : 0));
+  return s;
+}
+
+WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, const dex_options* o) {
   WsPlan w;
   Layout lay;
   const size_t es = esize(c->dtype);
   const size_t L = c->n_layers, d = c->d_model, nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim,
                F = c->d_ffn, V = c->vocab, B = o->max_batch, Cmax = o->max_context;
-  const int N = n_x, S = c->n_layers / n_x, P = (1 << N) - 1;
+  const int N = n_x, S = longest_stage(X, n_x), P = (1 << N) - 1;
   w.Rmax = std::max(std::max((int)B << (N - 1), kPrefillRows), (int)B);
   w.nchunk = (int)((Cmax + attn_chunk((int)hd) - 1) / attn_chunk((int)hd));
   const size_t Cs = (Cmax + kKvTile - 1) / kKvTile * kKvTile;
@@ -370,31 +374,40 @@ int pack_weights(dex_ctx* ctx, const dex_weights* w) {
 
 // One pass of the layer stack over `nrows` rows already set up in ctx->rows.
 // stage_rows: for each stage, [row0, count) of its rows; lam_count layer
-// slots; smul = S for lattice rows (layer = stage*S + lam), 0 for autoregressive
-// and prefill rows (layer = lam). Per layer slot: QKV GEMM (fused RMSNorm,
-// RoPE, K/V write) -> attention -> O GEMM (+ residual) -> gate/up GEMM (fused
-// RMSNorm, SwiGLU) -> down GEMM (+ residual).
+// slots; lattice != 0 for lattice rows (stage j runs layers lfirst[j] ..
+// lfirst[j+1] - 1, so it takes part in slots lam < its length), 0 for
+// autoregressive and prefill rows (one stage, layer = lam). want_xh: rows
+// write h * final-norm weight after their last layer (exit head input).
+// attn_stage_bytes/flops: algorithmic attention traffic of one layer slot per
+// stage. Per layer slot: QKV GEMM (fused RMSNorm, RoPE, K/V write) ->
+// attention -> O GEMM (+ residual) -> gate/up GEMM (fused RMSNorm, SwiGLU) ->
+// down GEMM (+ residual).
 template <typename T>
 int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& stage_rows, int lam_count,
-               int smul, int nitems, int max_keys, bool want_xh, double attn_bytes = 0, double attn_flops = 0) {
+               int lattice, int nitems, int max_keys, bool want_xh,
+               const std::vector<double>& attn_stage_bytes = {}, const std::vector<double>& attn_stage_flops = {}) {
   const ModelDims& D = ctx->D;
   hipStream_t st = ctx->st;
   const int d = D.d, nq = D.nq, nkv = D.nkv, hd = D.hd, F = D.F;
   const double es = sizeof(T);
+  auto len_of = [&](size_t j) { return lattice ? stage_len(D, (int)j) : lam_count; };
   // Groups are collected in a host list and launched kMaxGroups at a time.
   std::vector<GemmGroup> glist;
-  // gamma_of(layer): RMSNorm weight the residual-add epilogue folds into xn
-  // for the row's next consumer (null: no consumer).
-  auto groups_for = [&](int lam, const std::vector<size_t>& woff, int next_norm) {
+  // next_norm: RMSNorm weight the residual-add epilogue folds into xn for the
+  // row's next consumer (1: this layer's FFN norm, 2: the next layer's
+  // attention norm); xh_at_end: the rows' last layer also writes xh.
+  auto groups_for = [&](int lam, const std::vector<size_t>& woff, int next_norm, bool xh_at_end) {
     glist.clear();
     for (size_t j = 0; j < stage_rows.size(); ++j) {
       const int r0 = stage_rows[j].first, cnt = stage_rows[j].second;
-      const int layer = (int)j * smul + lam;
+      if (lam >= len_of(j)) continue;
+      const int layer = layer_of(D, lattice, (int)j, lam);
       const float* gamma = nullptr;
       if (next_norm == 1) gamma = ctx->norms + (size_t)layer * 2 * d + d;                    // this layer's FFN norm
       if (next_norm == 2 && layer + 1 < ctx->L) gamma = ctx->norms + (size_t)(layer + 1) * 2 * d;  // next attention norm
+      const int xh = xh_at_end && lam == len_of(j) - 1;
       for (int o = 0; o < cnt; o += 64)
-        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o), 0});
+        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o), 0, xh});
     }
   };
   auto run_gemm = [&](GemmArgs& ga, int epi) -> hipError_t {
@@ -431,36 +444,40 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
   ga.qout = ctx->q;
   ga.kvc = ctx->kvc;
   ga.exb = ctx->exb;
-  ga.smul = smul;
+  ga.lattice = lattice;
   ga.qscale = (float)(1.4426950408889634 / std::sqrt((double)hd));
   ga.split = ctx->gemm_split;
   ga.act = ctx->act;
   for (int lam = 0; lam < lam_count; ++lam) {
     ga.lam = lam;
-    ga.write_xh = 0;
-    groups_for(lam, ctx->wp.wqkv, 0);
+    groups_for(lam, ctx->wp.wqkv, 0, false);
     ga.K = d;
     ga.N = (nq + 2 * nkv) * hd;
     HIPCHK(run_gemm(ga, EPI_QKV));
+    double attn_bytes = 0, attn_flops = 0;
+    for (size_t j = 0; j < attn_stage_bytes.size(); ++j)
+      if (lam < len_of(j)) {
+        attn_bytes += attn_stage_bytes[j];
+        attn_flops += attn_stage_flops[j];
+      }
     int mk = prof_begin(ctx, DEX_PROF_ATTN);
     HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail,
-                            ctx->attn_part, (float*)ctx->attn_out, D, lam, smul, ctx->wp.nchunk, max_keys,
-                            smul != 0 ? ctx->attn_umax : 0, ctx->attn_groups, st));
+                            ctx->attn_part, (float*)ctx->attn_out, D, lam, lattice, ctx->wp.nchunk, max_keys,
+                            lattice != 0 ? ctx->attn_umax : 0, ctx->attn_groups, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
-    groups_for(lam, ctx->wp.wo, 1);
+    groups_for(lam, ctx->wp.wo, 1, false);
     ga.K = nq * hd;
     ga.N = d;
     ga.a = ctx->attn_out;
     HIPCHK(run_gemm(ga, EPI_RESID));
-    groups_for(lam, ctx->wp.wgu, 0);
+    groups_for(lam, ctx->wp.wgu, 0, false);
     ga.K = d;
     ga.N = 2 * F;
     HIPCHK(run_gemm(ga, EPI_SWIGLU));
-    groups_for(lam, ctx->wp.wdown, 2);
+    groups_for(lam, ctx->wp.wdown, 2, want_xh);
     ga.K = F;
     ga.N = d;
     ga.a = ctx->act;
-    ga.write_xh = want_xh && lam == lam_count - 1;
     HIPCHK(run_gemm(ga, EPI_RESID));
   }
   return DEX_OK;
@@ -584,9 +601,10 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
         ctx->attn_umax = std::max(ctx->attn_umax, it.nrows * rep);
       }
     }
-  // Algorithmic attention traffic of one layer slot: each (sequence, stage)
-  // group reads its committed K/V once, each row its explore entries.
-  double attn_bytes = 0, attn_flops = 0;
+  // Algorithmic attention traffic of one layer slot, per stage: each
+  // (sequence, stage) group reads its committed K/V once, each row its
+  // explore entries.
+  std::vector<double> attn_bytes(N, 0.0), attn_flops(N, 0.0);
   if (ctx->prof) {
     const double kvrow = 2.0 * ctx->D.nkv * ctx->D.hd * 4;
     for (int s = 0; s < B; ++s) {
@@ -594,12 +612,13 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       const int q = ar ? 0 : ctx->q_[s];
       const int C = ctx->C_[s] + (ar ? 1 : 0);
       for (int j = 0; j < N; ++j)
-        if (rows_seq_stage[(size_t)s * N + j]) attn_bytes += C * kvrow;
+        if (rows_seq_stage[(size_t)s * N + j]) attn_bytes[j] += C * kvrow;
       for (int n = (1 << q) - 1; n <= (1 << (q + 1)) - 2; ++n) {
-        if (ctx->opt.single_exit && !single_exit_node(n)) continue;
+        if (!ar && ctx->opt.single_exit && !single_exit_node(n)) continue;
         const int anc = ar ? 0 : __builtin_popcount(n + 1);
-        attn_bytes += anc * kvrow + ctx->D.nq * ctx->D.hd * 8.0;
-        attn_flops += 4.0 * ctx->D.nq * ctx->D.hd * (C + anc);
+        const int j = ar ? 0 : __builtin_ctz(n + 1);
+        attn_bytes[j] += anc * kvrow + ctx->D.nq * ctx->D.hd * 8.0;
+        attn_flops[j] += 4.0 * ctx->D.nq * ctx->D.hd * (C + anc);
       }
     }
   }
@@ -624,7 +643,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
     std::vector<std::pair<int, int>> stage_rows;
     for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
-    int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : ctx->S, nitems, max_keys, true,
+    int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : 1, nitems, max_keys, true,
                            attn_bytes, attn_flops);
     if (rc) return rc;
     // Every row exits, except intermediate explorers in the single-exit ablation.
@@ -800,7 +819,7 @@ int dex_workspace_bytes(const dex_model_config* cfg, const int32_t* X, int32_t n
     g_create_error = "null output";
     return DEX_EINVAL;
   }
-  *out_bytes = plan_workspace(cfg, n_x, opt).total;
+  *out_bytes = plan_workspace(cfg, X, n_x, opt).total;
   return DEX_OK;
 }
 
@@ -821,7 +840,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   }
   WsPlan wp;
   if (!rc) {
-    wp = plan_workspace(cfg, n_x, opt);
+    wp = plan_workspace(cfg, X, n_x, opt);
     if (ws_bytes < wp.total) {
       char buf[160];
       snprintf(buf, sizeof buf, "workspace too small: %zu < %zu bytes", ws_bytes, wp.total);
@@ -838,7 +857,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->opt = *opt;
   ctx->N = n_x;
   ctx->L = cfg->n_layers;
-  ctx->S = cfg->n_layers / n_x;
+  ctx->S = longest_stage(X, n_x);
   ctx->X.assign(X, X + n_x);
   ctx->bf16 = cfg->dtype == DEX_DTYPE_BF16;
   ctx->st = (hipStream_t)stream;
@@ -853,6 +872,8 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   D.F = cfg->d_ffn;
   D.V = cfg->vocab;
   D.S = ctx->S;
+  D.lfirst[0] = 0;
+  for (int j = 0; j < n_x; ++j) D.lfirst[j + 1] = X[j];
   D.N = n_x;
   D.P = (1 << n_x) - 1;
   D.B = opt->max_batch;

@@ -143,7 +143,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGr
       const float nv = args.hidden[o] + val(rl, c);
       args.hidden[o] = nv;
       if (G.gamma) args.xn[o] = nv * G.gamma[tile * 16 + c];
-      if (args.write_xh) args.xh[o] = nv * args.gfinal[tile * 16 + c];
+      if (G.xh) args.xh[o] = nv * args.gfinal[tile * 16 + c];
       scr[rl][c] = nv;
     }
     __syncthreads();
@@ -169,7 +169,7 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGr
       const int row = G.row0 + rl;
       const RowInfo& R = args.rows[row];
       const float x1 = val(rl, c) * rs[rl], x2 = val(rl, c + 8) * rs[rl];
-      const int layer = R.stage * args.smul + args.lam;
+      const int layer = layer_of(D, args.lattice, R.stage, args.lam);
       // K/V go out as (hi, lo) bf16 pairs: committed tile or explore entry.
       bf16_t* kvbase = nullptr;
       int kv = 0;

@@ -194,7 +194,9 @@ __global__ void promote_kernel(const SeqPlan* __restrict__ plans, const int* __r
   const int s = blockIdx.x, layer = blockIdx.y, h = blockIdx.z;
   const SeqPlan pl = plans[s];
   if (!pl.live || !pl.commit) return;
-  const int j = layer / D.S, lam = layer - j * D.S;
+  int j = 0;
+  while (D.lfirst[j + 1] <= layer) ++j;
+  const int lam = layer - D.lfirst[j];
   const int phys = promote_src[s * kMaxN + j];
   const bf16_t* src = exb + ex_base(D, s, phys, lam, h);
   bf16_t* dst = kvc + kv_head_base(D, s, layer, h);

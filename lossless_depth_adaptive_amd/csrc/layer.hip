@@ -206,7 +206,7 @@ template <int HD>
 __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int c, int u,
                                 const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                 const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
-                                float* __restrict__ mix, const ModelDims& D, int lam, int smul) {
+                                float* __restrict__ mix, const ModelDims& D, int lam, int lattice) {
   constexpr int NB = HD / 16, HP = HD + 4;
   const int rep = D.nq / D.nkv, units = it.nrows * rep;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
@@ -226,7 +226,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int
   }
   __syncthreads();
   if (!active) return;
-  const int layer = it.stage * smul + lam;
+  const int layer = layer_of(D, lattice, it.stage, lam);
   const bf16_t* tb = kvc + kv_head_base(D, Ru.seq, layer, h) + (size_t)c * 128 * HD;
   const float* qr = q + ((size_t)row * D.nq + qhd) * HD;
   // Every column of the query operand carries unit u; column u is kept.
@@ -293,13 +293,13 @@ template <int HD>
 __device__ void attn_shared_chunks(AttnSmem<HD>& sm, const AttnItem& it, int h, int sc,
                                    const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                    const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
-                                   const ModelDims& D, int lam, int smul, int nsc_max) {
+                                   const ModelDims& D, int lam, int lattice, int nsc_max) {
   constexpr int NB = HD / 16, HP = HD + 4;
   auto& red = sm.m.red;
   auto& qsh = sm.m.qsh;
   const int rep = D.nq / D.nkv, units = it.nrows * rep;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const int layer = it.stage * smul + lam;
+  const int layer = layer_of(D, lattice, it.stage, lam);
   const int seq = rows[it.row0].seq;
   load_q_tile<HD>(qsh, it, h, q, D, threadIdx.x, 64 * kAttnSC);
   // This lane's unit n: key limit (0 past the tile).
@@ -404,7 +404,7 @@ template <int HD>
 __device__ void attn_tile_chunks(AttnSmem<HD>& sm, const AttnItem* __restrict__ items, int first, int count, int h,
                                  int sc, const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                  const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
-                                 const ModelDims& D, int lam, int smul, int nsc_max) {
+                                 const ModelDims& D, int lam, int lattice, int nsc_max) {
   constexpr int NB = HD / 16, HP = HD + 4;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const AttnItem it = items[first + min(w, count - 1)];
@@ -420,7 +420,7 @@ __device__ void attn_tile_chunks(AttnSmem<HD>& sm, const AttnItem* __restrict__ 
   for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
   __syncthreads();
   if (!active) return;
-  const int layer = it.stage * smul + lam;
+  const int layer = layer_of(D, lattice, it.stage, lam);
   const bf16_t* hb = kvc + kv_head_base(D, rows[it.row0].seq, layer, h);
   const bool to_mix = sc_mixed(it, sc);
   bf16_t (*qt)[kAttnUnits][HD + 8] = sm.qt[w];
@@ -490,7 +490,7 @@ template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
     const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb, float* __restrict__ mix,
-    float* __restrict__ part, ModelDims D, int lam, int smul, int nsc_max, int ntail, int nquad, int nsc) {
+    float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail, int nquad, int nsc) {
   __shared__ AttnSmem<HD> sm;
   int b = blockIdx.x;
   if (b < ntail) {
@@ -499,9 +499,9 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const int j = b % 2;
     b /= 2;
     const AttnItem it = items[b / D.nkv];
-    if (it.xc0 < 0) return;
+    if (it.xc0 < 0 || (lattice && lam >= stage_len(D, it.stage))) return;
     attn_unit_chunk<HD>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * quad + (threadIdx.x >> 6), rows, q, kvc, exb, mix, D,
-                        lam, smul);
+                        lam, lattice);
     return;
   }
   b -= ntail;
@@ -509,8 +509,8 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   b /= nsc;
   const int ii = b / D.nkv;
   const AttnItem it = items[ii];
-  if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys) return;
-  attn_shared_chunks<HD>(sm, it, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, smul, nsc_max);
+  if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
+  attn_shared_chunks<HD>(sm, it, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
 // Groups of several items (tile role). grid = (items, kv heads, super-chunks);
@@ -519,12 +519,12 @@ template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
     const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam,
-    int smul, int nsc_max) {
+    int lattice, int nsc_max) {
   __shared__ AttnSmem<HD> sm;
   const int ii = blockIdx.x, sc = blockIdx.z;
   const AttnItem it = items[ii];
-  if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys) return;
-  attn_tile_chunks<HD>(sm, items, ii, it.lead, blockIdx.y, sc, rows, q, kvc, mix, part, D, lam, smul, nsc_max);
+  if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
+  attn_tile_chunks<HD>(sm, items, ii, it.lead, blockIdx.y, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
 // Fold the super-chunk states of each (row, query head) of an item in order
@@ -534,10 +534,11 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
 template <int HD>
 __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows,
                                     const float* __restrict__ mix, const float* __restrict__ part,
-                                    float* __restrict__ out, int nq, int nkv, int nsc_max) {
+                                    float* __restrict__ out, ModelDims D, int lam, int lattice, int nsc_max) {
   constexpr int HS = HD / 64, HP = HD + 4;
   const AttnItem it = items[blockIdx.x];
-  const int h = blockIdx.y, rep = nq / nkv, units = it.nrows * rep;
+  if (lattice && lam >= stage_len(D, it.stage)) return;
+  const int nq = D.nq, h = blockIdx.y, rep = nq / D.nkv, units = it.nrows * rep;
   const int lane = threadIdx.x & 63;
   for (int u = threadIdx.x >> 6; u < units; u += blockDim.x >> 6) {
     const int row = it.row0 + u / rep, qh = h * rep + u % rep;
@@ -596,7 +597,7 @@ int attn_mix_slots() { return kMixSlots; }
 // rows), 0 when no row does; groups: some item leads a group of several.
 hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int nrows, const float* q,
                             const bf16_t* kvc, const bf16_t* exb, float* mix, float* part, float* out,
-                            const ModelDims& D, int lam, int smul, int nsc_max, int max_keys, int umax, bool groups,
+                            const ModelDims& D, int lam, int lattice, int nsc_max, int max_keys, int umax, bool groups,
                             hipStream_t st) {
   (void)nrows;
   if (nitems == 0) return hipSuccess;
@@ -607,29 +608,29 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* ro
   const dim3 grid(ntail + nitems * D.nkv * nsc);
   if (D.hd == 128)
     hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, exb, mix, part, D,
-                       lam, smul, nsc_max, ntail, nquad, nsc);
+                       lam, lattice, nsc_max, ntail, nquad, nsc);
   else
     hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, exb, mix, part, D,
-                       lam, smul, nsc_max, ntail, nquad, nsc);
+                       lam, lattice, nsc_max, ntail, nquad, nsc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (groups) {
     const dim3 ggrid(nitems, D.nkv, nsc);
     if (D.hd == 128)
       hipLaunchKernelGGL((attn_group_kernel<128>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
-                         D, lam, smul, nsc_max);
+                         D, lam, lattice, nsc_max);
     else
       hipLaunchKernelGGL((attn_group_kernel<64>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
-                         D, lam, smul, nsc_max);
+                         D, lam, lattice, nsc_max);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (D.hd == 128)
     hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
-                       out, D.nq, D.nkv, nsc_max);
+                       out, D, lam, lattice, nsc_max);
   else
     hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
-                       out, D.nq, D.nkv, nsc_max);
+                       out, D, lam, lattice, nsc_max);
   return hipGetLastError();
 }
 

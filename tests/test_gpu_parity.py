@@ -11,7 +11,8 @@ For each case:
     the tolerance (1e-4 fp32; 3e-2 bf16 weights with fp32 accumulation).
 
 Shapes: the tiny fp32 workload at full size, its variants (sampling, untied
-head, DECS off, N = 1, 2, 8), and reduced-width versions of the 7B/13B/GQA
+head, DECS off, N = 1, 2, 8, stages of unequal length), and reduced-width
+versions of the 7B/13B/GQA
 workloads that keep their depth, exploration sets, batch structure and
 decoding modes. Full-size 7B runs are in test_gpu_fullsize.py.
 """
@@ -38,6 +39,11 @@ CASES = {
     "tiny_N1": (tiny.scaled(tied=False, gamma=0.8, X=(8,)), dict(T=24)),
     "tiny_N2": (tiny.scaled(tied=False, gamma=0.8, X=(4, 8)), dict(T=32)),
     "tiny_N8": (tiny.scaled(tied=False, gamma=0.8, X=tuple(range(1, 9))), dict(T=32)),
+    # stages of unequal length (exploration-resolution study, Section 4)
+    "tiny_nonuniform": (tiny.scaled(tied=False, gamma=0.8, X=(1, 3, 8)), dict(T=40)),
+    "tiny_nonuniform_sample": (tiny.scaled(mode="sample", seed_g=3001, X=(2, 5, 6, 8)), dict(T=40)),
+    "llama7b_nonuniform_narrow": (get_workload("llama7b_x4_greedy").scaled(prompt_len=80, X=(4, 12, 16, 32), **small),
+                                  dict(T=32)),
     "llama7b_x4_narrow": (get_workload("llama7b_x4_greedy").scaled(prompt_len=80, **small), dict(T=40)),
     "llama7b_x8_sample_narrow": (get_workload("llama7b_x8_sample").scaled(prompt_len=80, **small), dict(T=32)),
     "llama13b_x8_b4_narrow": (get_workload("llama13b_x8_b8").scaled(
