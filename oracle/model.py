@@ -16,6 +16,13 @@ head). Per layer l = 1..L, for a token at absolute position p:
 
 Depth-l logits: z_l = (RMSNorm(h_l) * g_final) W_head^T.
 
+Inducing adapters (Section 3.4, Appendix C.2), optional, at non-final
+exploration depths l only: the proposal at depth l is decoded from
+    h~_l = h_l + alpha_l (W2_l SiLU(W1_l (RMSNorm(h_l) * g_l) + b1_l) + b2_l)
+(two linear layers with biases, an RMSNorm scale g_l and a scalar gate; the
+activation is the backbone's, SiLU). The residual stream itself is not
+changed, and the final depth never has an adapter.
+
 Storage-dtype weights (bf16 or fp32) are upcast exactly to float64; all
 arithmetic is float64.
 """
@@ -48,10 +55,11 @@ class LayerW:
 
 
 class PlainModel:
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, adapters=None):
         """``cfg`` needs n_layers, d_model, n_heads, n_kv_heads, head_dim,
         d_ffn, vocab, rope_base, eps; ``weights`` is the dict produced by
-        ``synthetic.weights.generate``."""
+        ``synthetic.weights.generate``; ``adapters`` (optional) maps a depth
+        l < L to a dict w1, b1, w2, b2, norm, alpha."""
         self.L = cfg.n_layers
         self.d = cfg.d_model
         self.nq = cfg.n_heads
@@ -67,6 +75,10 @@ class PlainModel:
                 "attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")}))
         self.final_norm = _f64(weights["final_norm"])
         self.head = self.embed if weights["lm_head"] is weights["embed"] else _f64(weights["lm_head"])
+        self.adapters = {}
+        for l, a in (adapters or {}).items():
+            assert 1 <= l < self.L, "adapters sit at non-final depths"
+            self.adapters[int(l)] = {k: (float(v) if k == "alpha" else _f64(v)) for k, v in a.items()}
 
     # -- elementary pieces ------------------------------------------------
     def rmsnorm(self, x: np.ndarray, g: np.ndarray) -> np.ndarray:
@@ -99,6 +111,18 @@ class PlainModel:
     def logits(self, h: np.ndarray) -> np.ndarray:
         """Shared exit head: h [..., d] -> [..., V]."""
         return self.rmsnorm(h, self.final_norm) @ self.head.T
+
+    def adapter_delta(self, h: np.ndarray, depth: int) -> np.ndarray:
+        """Delta h of the adapter at ``depth`` (zero where there is none)."""
+        a = self.adapters.get(int(depth))
+        if a is None:
+            return np.zeros_like(h)
+        u = self.rmsnorm(h, a["norm"]) @ a["w1"].T + a["b1"]
+        return a["alpha"] * ((u / (1.0 + np.exp(-u))) @ a["w2"].T + a["b2"])
+
+    def exit_logits(self, h: np.ndarray, depth: int) -> np.ndarray:
+        """Logits of a proposal made after ``depth`` layers (adapter applied)."""
+        return self.logits(h + self.adapter_delta(h, depth))
 
     # -- forward passes ---------------------------------------------------
     def prefill(self, tokens: Sequence[int]):
@@ -202,8 +226,9 @@ class SlotEvaluator:
             self.memo[s] = (hs[i], kn[i], vn[i])
 
     def logits(self, slot: tuple, depth: int) -> np.ndarray:
-        """Logits after ``depth`` layers for the slot's last token."""
-        return self.m.logits(self.memo[slot][0][depth])
+        """Logits after ``depth`` layers for the slot's last token (through the
+        depth's inducing adapter when the model has one)."""
+        return self.m.exit_logits(self.memo[slot][0][depth], depth)
 
     def commit(self, y: int):
         """The anchor token's KV joins the cache; ``y`` becomes the new anchor.
