@@ -43,7 +43,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, Wd, prompts, commits, variant="dex"):
+def cpu_baseline(w, Wd, prompts, commits, variant="dex", adapter_alpha=None):
     """Time the oracle's DEX decoder (oracle/decode.py, as it stands) on the
     first ``commits`` commits of sequence 0, excluding its prefill."""
     import numpy as np
@@ -58,7 +58,11 @@ def cpu_baseline(w, Wd, prompts, commits, variant="dex"):
     Wc = {"embed": Wd["embed"].cpu(), "final_norm": Wd["final_norm"].cpu(),
           "layers": [{k: v.cpu() for k, v in l.items()} for l in Wd["layers"]]}
     Wc["lm_head"] = Wc["embed"] if w.tied else Wd["lm_head"].cpu()
-    model = PlainModel(w, Wc)
+    ads = None
+    if adapter_alpha is not None:
+        from synthetic.adapters import generate_adapters
+        ads = dict(zip(w.X[:-1], generate_adapters(w, adapter_alpha)))
+    model = PlainModel(w, Wc, adapters=ads)
     del Wc
     log(f"[cpu] weights on host in fp64 after {time.time() - t0:.1f}s")
     ev = SlotEvaluator(model)
@@ -103,6 +107,9 @@ def main():
     ap.add_argument("--X", default=None,
                     help="comma-separated exploration set replacing the workload's (e.g. 4,12,20,32: stages "
                          "of unequal length; the exploration-resolution study of Section 4)")
+    ap.add_argument("--adapter-alpha", type=float, default=None,
+                    help="attach seeded inducing adapters (m = 2 d_model) with this gate at the non-final depths "
+                         "(Section 3.4, Appendix C.2); the pages initialise alpha to 1e-3")
     ap.add_argument("--variant", choices=["dex", "single_exit", "vanilla"], default="dex",
                     help="dex: full depth exploration with DECS; single_exit: only the first and final "
                          "explorers propose (ablation of Section 4, Figure 4 right-top); vanilla: DECS off "
@@ -141,12 +148,16 @@ def main():
     log(f"[gpu] {w.name}: weights generated on device in {time.time() - t0:.1f}s")
     prompts = batch_prompts(w)
     gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab).cuda() if w.mode == "sample" else None
+    ads = None
+    if args.adapter_alpha is not None:
+        from synthetic.adapters import adapter_hidden, generate_adapters
+        ads = generate_adapters(w, args.adapter_alpha, device="cuda")
     cfg = D.model_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.d_ffn, w.vocab,
-                         w.rope_base, w.eps, w.tied, w.dtype)
+                         w.rope_base, w.eps, w.tied, w.dtype, adapter_hidden=adapter_hidden(w) if ads else 0)
     max_ctx = w.prompt_len + T + N + 8
     opt = D.options(w.mode, w.tau, args.variant != "vanilla", w.batch, max_ctx, T, gum, False,
                     single_exit=args.variant == "single_exit")
-    ctx = D.Dex(cfg, Wd, w.X, opt)
+    ctx = D.Dex(cfg, Wd, w.X, opt, adapters=ads)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ctx.prefill(prompts)
@@ -206,7 +217,7 @@ def main():
 
     ar = None
     if not args.no_ar:
-        ctx = D.Dex(cfg, Wd, w.X, opt)
+        ctx = D.Dex(cfg, Wd, w.X, opt, adapters=ads)
         ctx.prefill(prompts)
         k_ar = min(64, T)
         for _ in range(4):
@@ -223,7 +234,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, Wd, prompts, args.cpu_commits, args.variant)
+        cpu = cpu_baseline(w, Wd, prompts, args.cpu_commits, args.variant, args.adapter_alpha)
 
     layers = [c["layers"] for c in commits]
     out = {
@@ -241,7 +252,7 @@ def main():
         "data": "synthetic (seeded random-init weights and prompts)",
         "config": {"workload": w.name, "layers": w.n_layers, "d_model": w.d_model, "X": list(w.X),
                    "batch": w.batch, "prompt_len": w.prompt_len, "max_new_tokens": T, "mode": w.mode,
-                   "variant": args.variant},
+                   "variant": args.variant, "adapter_alpha": args.adapter_alpha},
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "tokens"},
         "dex": {"commits": len(commits), "mean_layers_per_token": round(float(np.mean(layers)), 3) if layers else None,

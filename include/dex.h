@@ -70,6 +70,9 @@ typedef struct {
   float rms_eps;
   int32_t tied_head;  /* 1: the LM head is the embedding matrix */
   int32_t dtype;      /* dex_dtype: storage of weights and KV */
+  int32_t adapter_hidden; /* m of the inducing adapters at the non-final exploration depths
+                             ("Depth Exploration for LLM Decoding", Section 3.4, Appendix C.2);
+                             0: no adapters. Multiple of 32 (bf16) or 16 (fp32). */
 } dex_model_config;
 
 /* Device pointers, row-major [out][in]. Per-layer entries are host arrays of
@@ -87,6 +90,16 @@ typedef struct {
   const void* const* w_down;       /* [L] -> [d_model][d_ffn] */
   const void* final_norm;          /* [d_model] */
   const void* lm_head;             /* [vocab][d_model]; ignored when tied_head */
+  /* Inducing adapters, read when adapter_hidden > 0: host arrays of N-1 device
+   * pointers, one per non-final explorer k, storage dtype. A proposal of
+   * explorer k is decoded from h + alpha_k (w2_k SiLU(w1_k (RMSNorm(h) * norm_k)
+   * + b1_k) + b2_k); the residual stream and the final explorer are unchanged. */
+  const void* const* adapter_w1;    /* [N-1] -> [m][d_model] */
+  const void* const* adapter_b1;    /* [N-1] -> [m] */
+  const void* const* adapter_w2;    /* [N-1] -> [d_model][m] */
+  const void* const* adapter_b2;    /* [N-1] -> [d_model] */
+  const void* const* adapter_norm;  /* [N-1] -> [d_model] */
+  const float* adapter_alpha;       /* host [N-1] */
 } dex_weights;
 
 typedef struct {

@@ -80,9 +80,14 @@ struct GemmGroup {
   int m;                // rows, 1..64
   int srow;             // split-range wide GEMM: the group's first row in the partial-sum scratch
   int xh;               // EPI_RESID: also write h * final-norm weight (the rows end their stage here)
+  const float* bias;    // EPI_ADAPT1 / EPI_ADAPT2: b1 / b2 of the group's adapter
+  float alpha;          // EPI_ADAPT2: the adapter's gate
+  const float* anorm;   // EPI_RESID: also write h * this adapter norm weight (null: none)
 };
 
-enum Epilogue { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3 };
+enum Epilogue { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_ADAPT1 = 4, EPI_ADAPT2 = 5 };
+// Epilogues whose A operand is a normalised residual (h * g, scaled by rstd).
+constexpr bool epi_norm(int e) { return e == EPI_QKV || e == EPI_SWIGLU || e == EPI_HEAD || e == EPI_ADAPT1; }
 
 // Residual-stream buffers, indexed by a row's hrow: the fp32 residual h, its
 // per-16-column sums of squares, and h multiplied elementwise by the RMSNorm
@@ -100,7 +105,9 @@ struct GemmArgs {
   float* hidden;    // EPI_RESID: residual [*][N]
   float* ssq;       // [*][d/16]: read by normalising epilogues, written by EPI_RESID
   float* xn;        // EPI_RESID: h * gamma of the next consumer
-  float* xh;        // EPI_RESID: h * final-norm weight (groups with xh set)
+  float* xh;        // EPI_RESID: h * final-norm weight (groups with xh set); EPI_ADAPT2: h~ * weight
+  float* xa;        // EPI_RESID: h * adapter norm weight (groups with anorm set)
+  float* ssq_head;  // [*][d/16] sums of squares of the exit head's input (h, or h~ for adapted rows)
   const float* gfinal;
   float eps;
   // EPI_QKV

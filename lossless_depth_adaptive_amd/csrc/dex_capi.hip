@@ -11,6 +11,7 @@
 // before launch, and the only device-to-host transfer per round is the commit
 // records (at most one per sequence).
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -66,7 +67,8 @@ struct Layout {
 
 // Every buffer of the workspace, as byte offsets.
 struct WsPlan {
-  size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh;
+  size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh, xa, ssq_head, ad_vec;
+  std::vector<size_t> wad1, wad2;  // packed inducing adapters, one per non-final explorer
   size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
   size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq, gemm_split;
   std::vector<size_t> wqkv, wo, wgu, wdown;
@@ -93,6 +95,10 @@ int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex
   if (c->d_model % 16 || c->vocab % 16 || c->d_ffn % 8) { err = "d_model and vocab must be multiples of 16, d_ffn of 8"; return DEX_EINVAL; }
   if (!(c->rms_eps > 0) || !(c->rope_base > 1)) { err = "rms_eps and rope_base must be positive"; return DEX_EINVAL; }
   if (n_x < 1 || n_x > kMaxN) { err = "number of exploration depths must be 1..10"; return DEX_EINVAL; }
+  if (c->adapter_hidden < 0 || c->adapter_hidden % (c->dtype == DEX_DTYPE_BF16 ? 32 : 16)) {
+    err = "adapter_hidden must be 0 or a positive multiple of the MFMA k-step (32 bf16, 16 fp32)";
+    return DEX_EINVAL;
+  }
   for (int k = 0; k < n_x; ++k) {
     if (X[k] < 1 || (k > 0 && X[k] <= X[k - 1])) { err = "exploration set must be strictly increasing within [1, L]"; return DEX_EINVAL; }
   }
@@ -137,6 +143,12 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
     w.wdown.push_back(lay.take(d * F * es));
   }
   w.norms = lay.take((2 * L + 1) * d * 4);
+  const size_t m = c->adapter_hidden;
+  for (int k = 0; m && k < N - 1; ++k) {
+    w.wad1.push_back(lay.take(m * d * es));
+    w.wad2.push_back(lay.take(d * m * es));
+  }
+  w.ad_vec = lay.take(m ? (size_t)(N - 1) * (m + 2 * d) * 4 : 0);   // per adapter: b1 [m], b2 [d], norm [d]
   w.cosT = lay.take(Cmax * (hd / 2) * 4);
   w.sinT = lay.take(Cmax * (hd / 2) * 4);
   w.kvc = lay.take(B * L * nkv * Cs * hd * 8);            // K and V as bf16 (hi, lo) pairs
@@ -144,6 +156,8 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
   w.xn = lay.take((B * P + kPrefillRows) * d * 4);
   w.xh = lay.take((B * P + kPrefillRows) * d * 4);
+  w.xa = lay.take(m ? (B * P + kPrefillRows) * d * 4 : 0);
+  w.ssq_head = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
   w.map = lay.take(B * P * 4);
   w.cand = lay.take(B * P * 4);
   w.margin = lay.take(B * P * 4);
@@ -163,7 +177,7 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.q = lay.take(R * nq * hd * 4);
   w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
   w.attn_out = lay.take(R * nq * hd * 4);
-  w.act = lay.take(R * F * 4);
+  w.act = lay.take(R * std::max(F, m) * 4);
   w.attn_part = lay.take(R * nq * w.nchunk * (hd + 4) * 4);
   w.attn_tail = lay.take(R * nq * attn_mix_slots() * (hd + 4) * 4);
   w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
@@ -186,7 +200,10 @@ struct dex_ctx {
   char* ws;
   WsPlan wp;
   // device views
-  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q, *attn_part, *attn_tail, *head_part, *ssq, *gemm_split;
+  float *ad_vec = nullptr, *xa = nullptr, *ssq_head = nullptr;
+  std::vector<float> ad_alpha;    // inducing-adapter gates (host), one per non-final explorer
+  float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q;
+  float *attn_part, *attn_tail, *head_part, *ssq, *gemm_split;
   int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
   RowInfo* rows;
   SeqPlan* plans;
@@ -369,6 +386,86 @@ int pack_weights(dex_ctx* ctx, const dex_weights* w) {
     }
   }
   HIPCHK(hipMemcpy(ctx->norms, nf.data(), nf.size() * 4, hipMemcpyHostToDevice));
+  // Inducing adapters: W1, W2 packed like any layer matrix; b1, b2 and the
+  // norm weight to fp32 through the host.
+  const int m = ctx->cfg.adapter_hidden;
+  for (int k = 0; m && k < ctx->N - 1; ++k) {
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wad1[k]), w->adapter_w1[k], nullptr, nullptr, m, 0, 0, d, 0, m, hd, st));
+    HIPCHK(launch_pack<T>(ctx->at(ctx->wp.wad2[k]), w->adapter_w2[k], nullptr, nullptr, d, 0, 0, m, 0, d, hd, st));
+    const void* srcs[3] = {w->adapter_b1[k], w->adapter_b2[k], w->adapter_norm[k]};
+    const int lens[3] = {m, d, d};
+    std::vector<T> t2((size_t)m);
+    std::vector<float> f2;
+    for (int v = 0; v < 3; ++v) {
+      HIPCHK(hipMemcpy(t2.data(), srcs[v], lens[v] * sizeof(T), hipMemcpyDeviceToHost));
+      for (int i = 0; i < lens[v]; ++i) {
+        float f;
+        if (sizeof(T) == 2) {
+          const unsigned u = ((unsigned)((const unsigned short*)t2.data())[i]) << 16;
+          std::memcpy(&f, &u, 4);
+        } else {
+          std::memcpy(&f, (const char*)t2.data() + 4 * i, 4);
+        }
+        f2.push_back(f);
+      }
+    }
+    HIPCHK(hipMemcpy(ctx->ad_vec + (size_t)k * (m + 2 * d), f2.data(), f2.size() * 4, hipMemcpyHostToDevice));
+    ctx->ad_alpha.push_back(w->adapter_alpha[k]);
+  }
+  return DEX_OK;
+}
+
+// Adapter vectors of explorer k in the workspace: b1 [m], b2 [d], norm [d].
+const float* ad_b1(dex_ctx* ctx, int k) { return ctx->ad_vec + (size_t)k * (ctx->cfg.adapter_hidden + 2 * ctx->D.d); }
+const float* ad_b2(dex_ctx* ctx, int k) { return ad_b1(ctx, k) + ctx->cfg.adapter_hidden; }
+const float* ad_norm(dex_ctx* ctx, int k) { return ad_b2(ctx, k) + ctx->D.d; }
+
+// Inducing adapters on the exit rows of non-final explorers: `ranges` holds
+// (explorer, first row, count). ADAPT1: SiLU(W1 (RMSNorm(h) * g) + b1) into
+// the activation buffer; ADAPT2: h~ = h + alpha (W2 a + b2) becomes the exit
+// head's input (xh, ssq_head).
+template <typename T>
+int run_adapters(dex_ctx* ctx, const std::vector<std::array<int, 3>>& ranges) {
+  if (ranges.empty()) return DEX_OK;
+  const ModelDims& D = ctx->D;
+  hipStream_t st = ctx->st;
+  const int m = ctx->cfg.adapter_hidden;
+  GemmArgs ga;
+  std::memset(&ga, 0, sizeof(ga));
+  ga.rows = ctx->rows;
+  ga.hidden = ctx->hidden;
+  ga.ssq = ctx->ssq;
+  ga.ssq_head = ctx->ssq_head;
+  ga.xin = ctx->xa;
+  ga.xh = ctx->xh;
+  ga.gfinal = ctx->norms + (size_t)2 * ctx->L * D.d;
+  ga.eps = D.eps;
+  ga.act = ctx->act;
+  ga.a = ctx->act;
+  ga.split = ctx->gemm_split;
+  const double es = sizeof(T);
+  double bytes = 0, flops = 0;
+  int nrows = 0;
+  for (int pass = 0; pass < 2; ++pass) {
+    std::vector<GemmGroup> groups;
+    for (const auto& rg : ranges) {
+      const int k = rg[0];
+      for (int o = 0; o < rg[2]; o += 64) {
+        GemmGroup g{ctx->at(pass ? ctx->wp.wad2[k] : ctx->wp.wad1[k]), nullptr, rg[1] + o, std::min(64, rg[2] - o),
+                    0, 0, pass ? ad_b2(ctx, k) : ad_b1(ctx, k), ctx->ad_alpha[k], nullptr};
+        groups.push_back(g);
+      }
+      if (pass == 0) nrows += rg[2];
+    }
+    ga.K = pass ? m : D.d;
+    ga.N = pass ? D.d : m;
+    const int mk = prof_begin(ctx, DEX_PROF_GEMM);
+    int launches = 0;
+    HIPCHK(launch_groups<T>(ga, groups, pass ? EPI_ADAPT2 : EPI_ADAPT1, ctx->wp.split_cols, st, &launches));
+    bytes = (double)ranges.size() * m * D.d * es + (double)nrows * (m + D.d) * 4 * (pass ? 2 : 1);
+    flops = 2.0 * nrows * m * D.d;
+    prof_end(ctx, mk, launches, bytes, flops);
+  }
   return DEX_OK;
 }
 
@@ -406,8 +503,12 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
       if (next_norm == 1) gamma = ctx->norms + (size_t)layer * 2 * d + d;                    // this layer's FFN norm
       if (next_norm == 2 && layer + 1 < ctx->L) gamma = ctx->norms + (size_t)(layer + 1) * 2 * d;  // next attention norm
       const int xh = xh_at_end && lam == len_of(j) - 1;
+      // rows of a non-final explorer that exits also feed its inducing adapter
+      const bool adapted = xh && lattice && ctx->cfg.adapter_hidden > 0 && (int)j < ctx->N - 1 &&
+                           (!ctx->opt.single_exit || j == 0);
       for (int o = 0; o < cnt; o += 64)
-        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o), 0, xh});
+        glist.push_back(GemmGroup{ctx->at(woff[layer]), gamma, r0 + o, std::min(64, cnt - o), 0, xh, nullptr, 0.f,
+                                  adapted ? ad_norm(ctx, (int)j) : nullptr});
     }
   };
   auto run_gemm = [&](GemmArgs& ga, int epi) -> hipError_t {
@@ -435,6 +536,8 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
   ga.ssq = ctx->ssq;
   ga.xn = ctx->xn;
   ga.xh = ctx->xh;
+  ga.xa = ctx->xa;
+  ga.ssq_head = ctx->ssq_head;
   ga.xin = ctx->xn;
   ga.gfinal = ctx->norms + (size_t)2 * ctx->L * d;
   ga.eps = D.eps;
@@ -494,7 +597,7 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
   std::memset(&ga, 0, sizeof(ga));
   ga.rows = ctx->rows;
   ga.xin = ctx->xh;
-  ga.ssq = ctx->ssq;
+  ga.ssq = ctx->ssq_head;
   ga.eps = D.eps;
   ga.K = D.d;
   ga.N = D.V;
@@ -646,6 +749,14 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : 1, nitems, max_keys, true,
                            attn_bytes, attn_flops);
     if (rc) return rc;
+    // Inducing adapters on the exit rows of non-final explorers.
+    if (!ar && ctx->cfg.adapter_hidden > 0) {
+      std::vector<std::array<int, 3>> ad;
+      for (int j = 0; j < N - 1; ++j)
+        if (stage_tot[j] && (!ctx->opt.single_exit || j == 0)) ad.push_back({j, stage_off[j], stage_tot[j]});
+      rc = run_adapters<T>(ctx, ad);
+      if (rc) return rc;
+    }
     // Every row exits, except intermediate explorers in the single-exit ablation.
     std::vector<std::pair<int, int>> exits;
     if (!ar && ctx->opt.single_exit && N > 1) {
@@ -836,6 +947,11 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
     for (int l = 0; ok && l < cfg->n_layers; ++l)
       ok = w->attn_norm[l] && w->wq[l] && w->wk[l] && w->wv[l] && w->wo[l] && w->ffn_norm[l] && w->w_gate[l] &&
            w->w_up[l] && w->w_down[l];
+    if (ok && cfg->adapter_hidden > 0) {
+      ok = w->adapter_w1 && w->adapter_b1 && w->adapter_w2 && w->adapter_b2 && w->adapter_norm && w->adapter_alpha;
+      for (int k = 0; ok && k < n_x - 1; ++k)
+        ok = w->adapter_w1[k] && w->adapter_b1[k] && w->adapter_w2[k] && w->adapter_b2[k] && w->adapter_norm[k];
+    }
     if (!ok) { err = "null weight pointer"; rc = DEX_EINVAL; }
   }
   WsPlan wp;
@@ -890,6 +1006,9 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->hidden = (float*)ctx->at(wp.hidden);
   ctx->xn = (float*)ctx->at(wp.xn);
   ctx->xh = (float*)ctx->at(wp.xh);
+  ctx->xa = (float*)ctx->at(wp.xa);
+  ctx->ssq_head = (float*)ctx->at(wp.ssq_head);
+  ctx->ad_vec = (float*)ctx->at(wp.ad_vec);
   ctx->map = (int*)ctx->at(wp.map);
   ctx->cand = (int*)ctx->at(wp.cand);
   ctx->margin = (float*)ctx->at(wp.margin);

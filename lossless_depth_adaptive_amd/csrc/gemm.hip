@@ -144,11 +144,39 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGr
       args.hidden[o] = nv;
       if (G.gamma) args.xn[o] = nv * G.gamma[tile * 16 + c];
       if (G.xh) args.xh[o] = nv * args.gfinal[tile * 16 + c];
+      if (G.anorm) args.xa[o] = nv * G.anorm[tile * 16 + c];
       scr[rl][c] = nv;
     }
     __syncthreads();
+    for (int rl = threadIdx.x; rl < G.m; rl += NT) {
+      const size_t so = (size_t)args.rows[G.row0 + rl].hrow * ntiles + tile;
+      const float v = ssq16(scr[rl]);
+      args.ssq[so] = v;
+      if (G.xh) args.ssq_head[so] = v;
+    }
+  } else if constexpr (EPI == EPI_ADAPT1) {
+    // Inducing adapter, first layer: SiLU(W1 (RMSNorm(h) * g) + b1).
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int rl = e >> 4, c = e & 15;
+      if (rl >= G.m) continue;
+      const float u = val(rl, c) * rs[rl] + G.bias[tile * 16 + c];
+      ((float*)args.act)[(size_t)(G.row0 + rl) * args.N + tile * 16 + c] = u / (1.0f + expf(-u));
+    }
+  } else if constexpr (EPI == EPI_ADAPT2) {
+    // Inducing adapter, second layer: h~ = h + alpha (W2 a + b2) is the exit
+    // head's input (times the final-norm weight) and its tile sums of squares;
+    // the residual stream keeps h.
+    for (int e = threadIdx.x; e < E; e += NT) {
+      const int rl = e >> 4, c = e & 15;
+      if (rl >= G.m) continue;
+      const size_t o = (size_t)args.rows[G.row0 + rl].hrow * args.N + tile * 16 + c;
+      const float ht = args.hidden[o] + G.alpha * (val(rl, c) + G.bias[tile * 16 + c]);
+      args.xh[o] = ht * args.gfinal[tile * 16 + c];
+      scr[rl][c] = ht;
+    }
+    __syncthreads();
     for (int rl = threadIdx.x; rl < G.m; rl += NT)
-      args.ssq[(size_t)args.rows[G.row0 + rl].hrow * ntiles + tile] = ssq16(scr[rl]);
+      args.ssq_head[(size_t)args.rows[G.row0 + rl].hrow * ntiles + tile] = ssq16(scr[rl]);
   } else if constexpr (EPI == EPI_SWIGLU) {
     for (int e = threadIdx.x; e < ROWS * 8; e += NT) {
       const int rl = e >> 3, c = e & 7;
@@ -262,7 +290,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   constexpr int EPL = Mfma<T>::EPL;
   constexpr int AW = EPL / 4;          // 16-byte A loads per lane per k-step (fp32 activations)
   constexpr int U = DEX_GEMM_U;        // k-steps of loads in flight per wave
-  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
+  constexpr bool NORM = epi_norm(EPI);
   const int gi = blockIdx.y;
   if (gi >= args.ngroups) return;
   const GemmGroup G = args.g[gi];
@@ -395,7 +423,7 @@ constexpr int kWideAP = 40;                      // LDS row pitch of a stage (bf
 template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
   constexpr int KSTEP = 32;
-  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
+  constexpr bool NORM = epi_norm(EPI);
   const int gi = blockIdx.x;
   if (gi >= args.ngroups) return;
   const GemmGroup G = args.g[gi];
@@ -547,7 +575,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 // epilogue. grid = (groups, N/16 tiles), block = 256.
 template <int EPI>
 __global__ __launch_bounds__(kWideThreads) void gemm_split_reduce_kernel(const GemmArgs args) {
-  constexpr bool NORM = EPI == EPI_QKV || EPI == EPI_SWIGLU || EPI == EPI_HEAD;
+  constexpr bool NORM = epi_norm(EPI);
   const GemmGroup G = args.g[blockIdx.x];
   const int tile = blockIdx.y;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -699,6 +727,8 @@ hipError_t launch_gemm_wide(const GemmArgs& a, int epi, bool split, hipStream_t 
     case EPI_QKV: split ? wide_launch<EPI_QKV, true>(a, st) : wide_launch<EPI_QKV, false>(a, st); break;
     case EPI_RESID: split ? wide_launch<EPI_RESID, true>(a, st) : wide_launch<EPI_RESID, false>(a, st); break;
     case EPI_SWIGLU: split ? wide_launch<EPI_SWIGLU, true>(a, st) : wide_launch<EPI_SWIGLU, false>(a, st); break;
+    case EPI_ADAPT1: split ? wide_launch<EPI_ADAPT1, true>(a, st) : wide_launch<EPI_ADAPT1, false>(a, st); break;
+    case EPI_ADAPT2: split ? wide_launch<EPI_ADAPT2, true>(a, st) : wide_launch<EPI_ADAPT2, false>(a, st); break;
     default: split ? wide_launch<EPI_HEAD, true>(a, st) : wide_launch<EPI_HEAD, false>(a, st); break;
   }
   return hipGetLastError();
@@ -714,6 +744,8 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
     case EPI_QKV: return launch_gemm_nb<T, EPI_QKV>(a, mb, st);
     case EPI_RESID: return launch_gemm_nb<T, EPI_RESID>(a, mb, st);
     case EPI_SWIGLU: return launch_gemm_nb<T, EPI_SWIGLU>(a, mb, st);
+    case EPI_ADAPT1: return launch_gemm_nb<T, EPI_ADAPT1>(a, mb, st);
+    case EPI_ADAPT2: return launch_gemm_nb<T, EPI_ADAPT2>(a, mb, st);
     default: return launch_gemm_nb<T, EPI_HEAD>(a, mb, st);
   }
 }

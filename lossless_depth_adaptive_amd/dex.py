@@ -28,7 +28,7 @@ class ModelConfig(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("d_ffn", ctypes.c_int32),
                 ("vocab", ctypes.c_int32), ("rope_base", ctypes.c_float),
                 ("rms_eps", ctypes.c_float), ("tied_head", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("adapter_hidden", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -37,7 +37,9 @@ _PP = ctypes.POINTER(ctypes.c_void_p)
 class Weights(ctypes.Structure):
     _fields_ = [("tok_embed", ctypes.c_void_p), ("attn_norm", _PP), ("wq", _PP), ("wk", _PP),
                 ("wv", _PP), ("wo", _PP), ("ffn_norm", _PP), ("w_gate", _PP), ("w_up", _PP),
-                ("w_down", _PP), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p)]
+                ("w_down", _PP), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("adapter_w1", _PP), ("adapter_b1", _PP), ("adapter_w2", _PP), ("adapter_b2", _PP),
+                ("adapter_norm", _PP), ("adapter_alpha", ctypes.POINTER(ctypes.c_float))]
 
 
 class Options(ctypes.Structure):
@@ -101,9 +103,11 @@ def _i32_array(vals: Sequence[int]):
 
 
 def model_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, rope_base=10000.0,
-                 rms_eps=1e-5, tied_head=False, dtype="bf16") -> ModelConfig:
+                 rms_eps=1e-5, tied_head=False, dtype="bf16", adapter_hidden=0) -> ModelConfig:
+    """``adapter_hidden``: m of the inducing adapters (0: none)."""
     return ModelConfig(n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, rope_base,
-                       rms_eps, int(bool(tied_head)), DTYPE_BF16 if dtype == "bf16" else DTYPE_F32)
+                       rms_eps, int(bool(tied_head)), DTYPE_BF16 if dtype == "bf16" else DTYPE_F32,
+                       int(adapter_hidden))
 
 
 def options(mode="greedy", temperature=1.0, decs=True, max_batch=1, max_context=1024,
@@ -135,10 +139,12 @@ class Dex:
     ``attn_norm, wq, wk, wv, wo, ffn_norm, w_gate, w_up, w_down``),
     ``final_norm`` and ``lm_head``: CUDA tensors in the storage dtype,
     row-major [out, in]. The library packs them into its workspace.
+    ``adapters`` (needed when cfg.adapter_hidden > 0): one dict per non-final
+    explorer with CUDA tensors ``w1, b1, w2, b2, norm`` and a float ``alpha``.
     """
 
     def __init__(self, cfg: ModelConfig, weights: Dict, X: Sequence[int], opt: Options,
-                 stream=None, device="cuda"):
+                 stream=None, device="cuda", adapters=None):
         import torch
         self.lib = load_library()
         self.cfg, self.opt, self.X = cfg, opt, list(X)
@@ -156,6 +162,20 @@ class Dex:
         w = Weights(weights["embed"].data_ptr(), arr("attn_norm"), arr("wq"), arr("wk"), arr("wv"),
                     arr("wo"), arr("ffn_norm"), arr("w_gate"), arr("w_up"), arr("w_down"),
                     weights["final_norm"].data_ptr(), weights["lm_head"].data_ptr())
+        if cfg.adapter_hidden:
+            if adapters is None or len(adapters) != self.N - 1:
+                raise ValueError("adapter_hidden > 0 needs one adapter per non-final explorer")
+
+            def aarr(key):
+                a = (ctypes.c_void_p * len(adapters))(*[ad[key].data_ptr() for ad in adapters])
+                self._keep.append(a)
+                return ctypes.cast(a, _PP)
+
+            alpha = (ctypes.c_float * len(adapters))(*[float(ad["alpha"]) for ad in adapters])
+            self._keep.append(alpha)
+            w.adapter_w1, w.adapter_b1, w.adapter_w2 = aarr("w1"), aarr("b1"), aarr("w2")
+            w.adapter_b2, w.adapter_norm = aarr("b2"), aarr("norm")
+            w.adapter_alpha = ctypes.cast(alpha, ctypes.POINTER(ctypes.c_float))
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         ctx = ctypes.c_void_p(None)
         rc = self.lib.dex_create(ctypes.byref(cfg), ctypes.byref(w), _i32_array(X), len(X), L,

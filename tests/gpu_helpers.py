@@ -15,17 +15,20 @@ def device_weights(w):
 
 
 def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, gumbel=None, graphs=True,
-             single_exit=False):
+             single_exit=False, adapters=None):
+    """``adapters``: device adapter dicts (synthetic.adapters layout) or None."""
     X = list(X or w.X)
+    m = adapters[0]["w1"].shape[0] if adapters else 0
     cfg = D.model_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.d_ffn,
-                         w.vocab, w.rope_base, w.eps, w.tied, w.dtype)
+                         w.vocab, w.rope_base, w.eps, w.tied, w.dtype, adapter_hidden=m)
     if max_context is None:
         max_context = w.prompt_len + T + len(X) + 8
     if w.mode == "sample" and gumbel is None:
         gumbel = gumbel_rows(w.seed_g, batch, T + len(X), w.vocab).cuda()
     opt = D.options(w.mode, w.tau, decs, batch, max_context, T, gumbel, debug, graphs, single_exit)
-    ctx = D.Dex(cfg, Wd, X, opt)
+    ctx = D.Dex(cfg, Wd, X, opt, adapters=adapters)
     ctx._gumbel = gumbel
+    ctx._adapters = adapters
     return ctx
 
 

@@ -11,7 +11,8 @@ For each case:
     the tolerance (1e-4 fp32; 3e-2 bf16 weights with fp32 accumulation).
 
 Shapes: the tiny fp32 workload at full size, its variants (sampling, untied
-head, DECS off, N = 1, 2, 8, stages of unequal length), and reduced-width
+head, DECS off, N = 1, 2, 8, stages of unequal length, inducing adapters), and
+reduced-width
 versions of the 7B/13B/GQA
 workloads that keep their depth, exploration sets, batch structure and
 decoding modes. Full-size 7B runs are in test_gpu_fullsize.py.
@@ -23,6 +24,7 @@ import pytest
 from oracle.decode import ar_decode
 from oracle.model import PlainModel, SlotEvaluator
 from synthetic import get_workload
+from synthetic.adapters import generate_adapters
 from synthetic.noise import gumbel_rows
 from synthetic.prompts import batch_prompts
 from synthetic.weights import generate
@@ -44,6 +46,13 @@ CASES = {
     "tiny_nonuniform_sample": (tiny.scaled(mode="sample", seed_g=3001, X=(2, 5, 6, 8)), dict(T=40)),
     "llama7b_nonuniform_narrow": (get_workload("llama7b_x4_greedy").scaled(prompt_len=80, X=(4, 12, 16, 32), **small),
                                   dict(T=32)),
+    # inducing adapters at the non-final depths (Section 3.4, Appendix C.2); alpha
+    # well above the pages' 1e-3 initial value so that they change proposals
+    "tiny_adapters": (tiny.scaled(tied=False, gamma=0.8), dict(T=40, adapter_alpha=0.5)),
+    "tiny_adapters_sample": (tiny.scaled(mode="sample", seed_g=3001), dict(T=40, adapter_alpha=0.5)),
+    "llama13b_x8_b4_adapters_narrow": (get_workload("llama13b_x8_b8").scaled(
+        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4096, batch=4, prompt_len=48),
+        dict(T=20, adapter_alpha=0.5)),
     "llama7b_x4_narrow": (get_workload("llama7b_x4_greedy").scaled(prompt_len=80, **small), dict(T=40)),
     "llama7b_x8_sample_narrow": (get_workload("llama7b_x8_sample").scaled(prompt_len=80, **small), dict(T=32)),
     "llama13b_x8_b4_narrow": (get_workload("llama13b_x8_b8").scaled(
@@ -64,10 +73,12 @@ def _run_case(name):
     prompts = batch_prompts(w)
     gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab) if w.mode == "sample" else None
     gum_d = gum.cuda() if gum is not None else None
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d)
+    alpha = kw.get("adapter_alpha")
+    ads_d = generate_adapters(w, alpha, device="cuda") if alpha is not None else None
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d)
     dex_recs, steps = run(ctx, prompts, T)
     ctx.close()
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d)
     ar_recs, ar_steps = run(ctx, prompts, T, ar=True)
     ctx.close()
     assert ar_steps == T
@@ -83,7 +94,8 @@ def _run_case(name):
         bs = [r["branch"] for r in dex_recs[0]]
         assert steps == N + sum(b + 1 for b in bs[:-1])
     # oracle, forced onto the GPU stream
-    m = PlainModel(w, generate(w))
+    ads = dict(zip(w.X[:-1], generate_adapters(w, alpha))) if alpha is not None else None
+    m = PlainModel(w, generate(w), adapters=ads)
     fp32 = w.dtype == "f32"
     gate, tol = (1e-3, 1e-4) if fp32 else (5e-2, 3e-2)
     stats = []
