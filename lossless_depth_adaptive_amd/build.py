@@ -23,6 +23,11 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
 
+# The GEMM and attention kernels keep their MFMA accumulators in ordinary
+# VGPRs: the compiler otherwise rotates them through AGPRs with copies in every
+# k-step, or spills into AGPRs.
+SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in ("gemm.hip", "layer.hip")}
+
 
 def _hipcc():
     for c in ("/opt/rocm/bin/hipcc", "hipcc"):
@@ -32,7 +37,7 @@ def _hipcc():
 
 def _compile(src: str, outdir: str) -> str:
     obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
   const int ntiles = args.N >> 4;
   const int K = args.K;
   const int KS = K / KSTEP;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int kb = (KS * w) / kKSplit, ke = (KS * (w + 1)) / kKSplit;
   const int col16 = lane & 15;
   const int kq = (lane >> 4) * EPL;
@@ -309,6 +309,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 
   const u32x4_t* wp = (const u32x4_t*)G.w + (size_t)tile0 * KS * 64 + lane;
   f32x4_t acc[MB][NB];
+  // Rows past the group's end are not loaded (masked lanes fetch nothing).
   const u32x4_t* ap[MB];
   bool av[MB];
 #pragma unroll
@@ -401,140 +402,161 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 }
 
 // ---------------------------------------------------------------------------
-// Wide GEMM for groups of many rows (bf16 weights). grid = (groups,
-// ceil(N / (64 kWideWT)), 1 or 8 k ranges), block = 4 waves; a block computes
-// 64 rows x 4 kWideWT column tiles, wave w the tiles kWideWT w ... Each k-step's activations (64
-// rows x 32, fp32) are split once into bf16 (hi, lo) in an LDS stage shared by
-// the four waves; loads run kWideD k-steps ahead in registers. Each output is
-// reduced exactly as in gemm_kernel: the 8 k ranges [KS r/8, KS (r+1)/8) are
-// accumulated from zero by the same MFMA chain (hi then lo per k-step), in
-// order, and summed in range order, so a row gets the same bits from either
-// kernel and from any grouping. SPLIT: the block takes k range blockIdx.z
-// only and leaves its partial in args.split for gemm_split_reduce_kernel.
-// Weight loads are ordinary (cached) loads: the row groups of a stage read
-// the same tile at about the same time and should meet in L2.
+// Wide GEMM for groups of many rows (bf16 weights). 1-D grid of (group, column
+// block[, k range]) blocks, block = 4 waves; a block computes 64 rows x
+// kWideBT column tiles, wave w the kWideWT tiles from kWideWT w. Each k-step's
+// activations (64 rows x 32, fp32) are split once into bf16 (hi, lo) and
+// stored in LDS in MFMA operand order, shared by the four waves; global loads
+// run two k-steps ahead in registers. Each output is reduced exactly as in
+// gemm_kernel: the 8 k ranges [KS r/8, KS (r+1)/8) are accumulated from zero
+// by the same MFMA chain (hi then lo per k-step), in order, and summed in
+// range order, so a row gets the same bits from either kernel and from any
+// grouping. SPLIT: the block takes one k range only and leaves its partial in
+// args.split for gemm_split_reduce_kernel.
+// Blocks that read the same weight tile (the row groups of one column block)
+// are given consecutive logical ids on one XCD, so the tile is fetched into
+// that XCD's L2 once.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
-constexpr int kWideWT = 2;                       // 16-column tiles per wave
+#ifndef DEX_WIDE_WT
+#define DEX_WIDE_WT 4
+#endif
+constexpr int kWideWT = DEX_WIDE_WT;             // 16-column tiles per wave
 constexpr int kWideBT = 4 * kWideWT;             // per block
-constexpr int kWideD = 3;                        // k-steps of loads in flight
-constexpr int kWideAP = 40;                      // LDS row pitch of a stage (bf16)
+
+// Logical block of hardware block b out of nb: the hardware hands blocks to
+// the 8 XCDs round-robin, and XCD x gets a contiguous run of logical ids.
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+  const int x = b & 7, k = b >> 3, q = nb >> 3, rem = nb & 7;
+  return x * q + (x < rem ? x : rem) + k;
+}
 
 template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
   constexpr int KSTEP = 32;
   constexpr bool NORM = epi_norm(EPI);
-  const int gi = blockIdx.x;
-  if (gi >= args.ngroups) return;
-  const GemmGroup G = args.g[gi];
   const int ntiles = args.N >> 4;
-  const int tb0 = blockIdx.y * kWideBT;
+  const int ncb = (ntiles + kWideBT - 1) / kWideBT;
+  const int nblk = args.ngroups * ncb * (SPLIT ? kKSplit : 1);
+  const int lb = xcd_block(blockIdx.x, nblk);
+  const int gi = lb % args.ngroups;
+  const int cb = (lb / args.ngroups) % ncb;
+  const int z = SPLIT ? lb / (args.ngroups * ncb) : 0;
+  const GemmGroup G = args.g[gi];
+  const int tb0 = cb * kWideBT;
   const int K = args.K, KS = K / KSTEP;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col16 = lane & 15, kg = lane >> 4;
   const int t0 = tb0 + w * kWideWT;
 
-  struct Stage { bf16_t hi[2][64][kWideAP], lo[2][64][kWideAP]; };
-  struct Out { float t[64][kWideBT * 16 + 4]; };
+  // f[buf][part][mb][lane]: part 0 (hi) / 1 (lo) of row 16 mb + (lane & 15),
+  // k 8 (lane >> 4) .. +7 of the k-step, the A operand of lane `lane`.
+  struct Stage { u32x4_t f[2][2][4][64]; };
+  struct Out { float t[SPLIT ? 1 : 64][kWideBT * 16 + 4]; };   // the split form stores from registers
   __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[64];
-  __shared__ float scr[64][17];
+  __shared__ float scr[SPLIT ? 1 : 64][17];
 
-  // A loads of this thread: rows ar and ar + 32, columns 4 aq .. 4 aq + 3.
-  const int ar = threadIdx.x >> 3, aq = threadIdx.x & 7;
-  const float* asrc[2];
-  bool aval[2];
+  // Thread (w, lane) converts the fragment that lane `lane` of row block w
+  // reads. Rows past the group's end repeat its first row and tiles past N the
+  // last tile: their outputs are never stored.
+  const int ar = 16 * w + col16;
+  const int rr = ar < G.m ? ar : 0;
+  const float* asrc = (NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
+                            : (const float*)args.a + (size_t)(G.row0 + rr) * K) + 8 * kg;
+  const u32x4_t* bsrc[kWideWT];
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int r = ar + 32 * x;
-    aval[x] = r < G.m;
-    const int rr = aval[x] ? r : 0;
-    const float* base = NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
-                             : (const float*)args.a + (size_t)(G.row0 + rr) * K;
-    asrc[x] = base + 4 * aq;
+  for (int nb = 0; nb < kWideWT; ++nb) {
+    const int t = t0 + nb < ntiles ? t0 + nb : ntiles - 1;
+    bsrc[nb] = (const u32x4_t*)G.w + (size_t)t * KS * 64 + lane;
   }
-  const u32x4_t* wp = (const u32x4_t*)G.w + lane;
-  bool bval[kWideWT];
-#pragma unroll
-  for (int nb = 0; nb < kWideWT; ++nb) bval[nb] = t0 + nb < ntiles;
 
   struct Pre {
     f32x4_t a[2];
     u32x4_t b[kWideWT];
   };
-  auto load = [&](int ks, Pre& p) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x)
-      p.a[x] = aval[x] ? *(const f32x4_t*)(asrc[x] + (size_t)ks * KSTEP) : f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int nb = 0; nb < kWideWT; ++nb)
-      p.b[nb] = bval[nb] ? wp[((size_t)(t0 + nb) * KS + ks) * 64] : u32x4_t{0u, 0u, 0u, 0u};
+  auto load_a = [&](int ks, Pre& p) {
+    ks = ks < KS ? ks : KS - 1;
+    const f32x4_t* ap = (const f32x4_t*)(asrc + (size_t)ks * KSTEP);
+    p.a[0] = ap[0];
+    p.a[1] = ap[1];
   };
-  auto stage_a = [&](int buf, const Pre& p) {
+  auto load_b = [&](int ks, Pre& p) {
+    ks = ks < KS ? ks : KS - 1;
+#pragma unroll
+    for (int nb = 0; nb < kWideWT; ++nb) p.b[nb] = bsrc[nb][(size_t)ks * 64];
+  };
+  // One k-step from the registers of p, which then take k-step ks + 2: the
+  // activation loads go out once p.a is staged, the weight loads once the
+  // MFMAs have read p.b.
+  auto step = [&](int ks, Pre& p, f32x4_t (&acc)[4][kWideWT]) {
+    const int buf = ks & 1;
+    u32x4_t hv, lv;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      unsigned hv[2], lv[2];
-      split_bf2(p.a[x][0], p.a[x][1], hv[0], lv[0]);
-      split_bf2(p.a[x][2], p.a[x][3], hv[1], lv[1]);
-      __builtin_memcpy(&sm.s.hi[buf][ar + 32 * x][4 * aq], hv, 8);
-      __builtin_memcpy(&sm.s.lo[buf][ar + 32 * x][4 * aq], lv, 8);
+      unsigned h0, l0, h1, l1;
+      split_bf2(p.a[x][0], p.a[x][1], h0, l0);
+      split_bf2(p.a[x][2], p.a[x][3], h1, l1);
+      hv[2 * x] = h0;
+      hv[2 * x + 1] = h1;
+      lv[2 * x] = l0;
+      lv[2 * x + 1] = l1;
     }
+    sm.s.f[buf][0][w][lane] = hv;
+    sm.s.f[buf][1][w][lane] = lv;
+    load_a(ks + 2, p);
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      const u32x4_t ahu = sm.s.f[buf][0][mb][lane], alu = sm.s.f[buf][1][mb][lane];
+      bf16x8_t ah, al;
+      __builtin_memcpy(&ah, &ahu, 16);
+      __builtin_memcpy(&al, &alu, 16);
+#pragma unroll
+      for (int nb = 0; nb < kWideWT; ++nb) {
+        bf16x8_t bv;
+        __builtin_memcpy(&bv, &p.b[nb], 16);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[mb][nb], 0, 0, 0);
+      }
+    }
+    load_b(ks + 2, p);
   };
 
-  f32x4_t acc[4][kWideWT], tot[4][kWideWT];
+  f32x4_t tot[4][kWideWT];
+  const int r0 = SPLIT ? z : 0, r1 = SPLIT ? z + 1 : kKSplit;
+  int ks = (KS * r0) / kKSplit;
+  Pre p0, p1;
+  load_a(ks, p0);
+  load_b(ks, p0);
+  load_a(ks + 1, p1);
+  load_b(ks + 1, p1);
+  for (int r = r0; r < r1; ++r) {
+    const int re = (KS * (r + 1)) / kKSplit;
+    f32x4_t acc[4][kWideWT];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kWideWT; ++nb) acc[mb][nb] = tot[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int kbeg = SPLIT ? (KS * (int)blockIdx.z) / kKSplit : 0;
-  const int kend = SPLIT ? (KS * ((int)blockIdx.z + 1)) / kKSplit : KS;
-  Pre pre[kWideD];
-#pragma unroll
-  for (int j = 0; j < kWideD; ++j)
-    if (kbeg + j < kend) load(kbeg + j, pre[j]);
-  int range = 0, rend = SPLIT ? kend : KS / kKSplit;
-  for (int k0 = kbeg; k0 < kend; k0 += kWideD) {
-#pragma unroll
-    for (int j = 0; j < kWideD; ++j) {
-      const int ks = k0 + j;
-      if (ks >= kend) break;
-      const int buf = ks & 1;
-      stage_a(buf, pre[j]);
-      u32x4_t bcur[kWideWT];
-#pragma unroll
-      for (int nb = 0; nb < kWideWT; ++nb) bcur[nb] = pre[j].b[nb];
-      if (ks + kWideD < kend) load(ks + kWideD, pre[j]);
-      __syncthreads();
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        bf16x8_t ah, al;
-        __builtin_memcpy(&ah, &sm.s.hi[buf][mb * 16 + col16][8 * kg], 16);
-        __builtin_memcpy(&al, &sm.s.lo[buf][mb * 16 + col16][8 * kg], 16);
-#pragma unroll
-        for (int nb = 0; nb < kWideWT; ++nb) {
-          bf16x8_t bv;
-          __builtin_memcpy(&bv, &bcur[nb], 16);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[mb][nb], 0, 0, 0);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[mb][nb], 0, 0, 0);
-        }
-      }
-      if (ks + 1 == rend) {   // end of k range `range`: add its partial in range order
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < kWideWT; ++nb) {
-            tot[mb][nb] = range == 0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
-            acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          }
-        ++range;
-        rend = (KS * (range + 1)) / kKSplit;
-      }
+      for (int nb = 0; nb < kWideWT; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (; ks + 2 <= re; ks += 2) {
+      step(ks, p0, acc);
+      step(ks + 1, p1, acc);
     }
+    if (ks < re) {   // odd range length: p1 holds the next k-step
+      step(ks, p0, acc);
+      ++ks;
+      const Pre t = p0;
+      p0 = p1;
+      p1 = t;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kWideWT; ++nb) tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
   }
 
   if constexpr (SPLIT) {
-    float* dst = args.split + ((size_t)blockIdx.z * kSplitRows + G.srow) * args.N;
+    float* dst = args.split + ((size_t)z * kSplitRows + G.srow) * args.N;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -711,7 +733,8 @@ static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
 
 template <int EPI, bool SPLIT>
 static void wide_launch(const GemmArgs& a, hipStream_t st) {
-  const dim3 grid(a.ngroups, (a.N / 16 + kWideBT - 1) / kWideBT, SPLIT ? kKSplit : 1);
+  const int ncb = (a.N / 16 + kWideBT - 1) / kWideBT;
+  const dim3 grid(a.ngroups * ncb * (SPLIT ? kKSplit : 1));
   hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT>), grid, dim3(kWideThreads), 0, st, a);
   if (SPLIT) {
     hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3(a.ngroups, a.N / 16), dim3(kWideThreads), 0, st, a);

@@ -84,23 +84,38 @@ __device__ __forceinline__ void fold(float& M, float& L, float* A, float m, floa
 // One 32-key chunk for the tile. qsrc(s, hi, lo): this lane's query operand
 // (unit n, dims 32s + 8g .. 32s + 8g + 7); ksrc(t, s, hi, lo): its K operand for
 // row block t (0, 1) and 32-dim step s; vsrc(b, hi, lo): its V^T operand for
-// output dims [16b, 16b + 16). valid8 bit i: key 8g + i counts for this lane's
-// unit. Out: acc[b][r] = the unit's unnormalised output at dim 16b + 4g + r,
-// and the chunk's m and l (m = -inf when no key counts).
-template <int HD, typename QSrc, typename KSrc, typename VSrc>
-__device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, unsigned valid8, f32x4_t* acc,
-                                              float& m, float& l) {
+// output dims [16b, 16b + 16), as loaded; vpost(b, hi, lo) then fixes it up
+// (masks, gathered values) once the loads have landed. valid8 bit i: key
+// 8g + i counts for this lane's unit. Out: acc[b][r] = the unit's unnormalised
+// output at dim 16b + 4g + r, and the chunk's m and l (m = -inf when no key
+// counts). EAGER: all K and V loads of the chunk are issued before the first
+// MFMA, so the chunk costs one memory latency (at the price of registers);
+// otherwise each operand is loaded where it is used. The arithmetic is the
+// same either way.
+template <int HD, bool EAGER, typename QSrc, typename KSrc, typename VSrc, typename VPost>
+__device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, VPost vpost, unsigned valid8,
+                                              f32x4_t* acc, float& m, float& l) {
   constexpr int NS = HD / 32, NB = HD / 16;
+  u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
+  if constexpr (EAGER) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ksrc(t, s, kh[t][s], kl[t][s]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) vsrc(b, vh[b], vl[b]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   f32x4_t st[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     st[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      u32x4_t kh, kl, qh, ql;
-      ksrc(t, s, kh, kl);
+      u32x4_t qh, ql;
+      if constexpr (!EAGER) ksrc(t, s, kh[t][s], kl[t][s]);
       qsrc(s, qh, ql);
-      st[t] = mma3(st[t], kh, kl, qh, ql);
+      st[t] = mma3(st[t], kh[t][s], kl[t][s], qh, ql);
     }
   }
   float sv[8];
@@ -126,9 +141,23 @@ __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, u
   split8(p, ph, pl);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    u32x4_t vh, vl;
-    vsrc(b, vh, vl);
-    acc[b] = mma3(f32x4_t{0.f, 0.f, 0.f, 0.f}, vh, vl, ph, pl);
+    if constexpr (!EAGER) vsrc(b, vh[b], vl[b]);
+    vpost(b, vh[b], vl[b]);
+    acc[b] = mma3(f32x4_t{0.f, 0.f, 0.f, 0.f}, vh[b], vl[b], ph, pl);
+  }
+}
+
+// V^T operand fix-up of the shared chunks: positions at or past vlim (the
+// largest key limit of the tile) may hold stale or never-written values; their
+// elements are zeroed so that p = 0 contributes exact zeros.
+__device__ __forceinline__ void mask_v(u32x4_t& vh, u32x4_t& vl, int nv) {
+  if (nv < 8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned keep = (2 * i + 1 < nv ? 0xFFFF0000u : 0u) | (2 * i < nv ? 0xFFFFu : 0u);
+      vh[i] &= keep;
+      vl[i] &= keep;
+    }
   }
 }
 
@@ -261,6 +290,9 @@ __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int
     } else {
       vh = vl = u32x4_t{0u, 0u, 0u, 0u};
     }
+  };
+  auto vpost = [&](int b, u32x4_t& vh, u32x4_t& vl) {
+    const int pb = p0 + 8 * g, dd = 16 * b + n;
     if (pb + 7 < ncu) return;
     // Positions from ncu on: the explore entry's value, or 0 past the limit.
 #pragma unroll
@@ -279,7 +311,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int
   for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < limu ? 1u : 0u) << i;
   f32x4_t acc[NB];
   float m, l;
-  chunk_partial<HD>(qsrc, ksrc, vsrc, valid8, acc, m, l);
+  chunk_partial<HD, false>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
   if (n == u)
     store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP, acc,
                       m, l, g);
@@ -332,22 +364,14 @@ __device__ void attn_shared_chunks(AttnSmem<HD>& sm, const AttnItem& it, int h, 
       const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
       vh = *(const u32x4_t*)vp;
       vl = *(const u32x4_t*)(vp + 32 * HD);
-      const int nv = vlim - (p0 + 8 * g);   // keys of this lane's eight below some limit
-      if (nv < 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned keep = (2 * i + 1 < nv ? 0xFFFF0000u : 0u) | (2 * i < nv ? 0xFFFFu : 0u);
-          vh[i] &= keep;
-          vl[i] &= keep;
-        }
-      }
     };
+    auto vpost = [&](int, u32x4_t& vh, u32x4_t& vl) { mask_v(vh, vl, vlim - (p0 + 8 * g)); };
     unsigned valid8 = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim ? 1u : 0u) << i;
     f32x4_t acc[NB];
     float m, l;
-    chunk_partial<HD>(qsrc, ksrc, vsrc, valid8, acc, m, l);
+    chunk_partial<HD, true>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
     if (n < units && p0 < lim) {
       if (to_mix) {
         const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
@@ -447,22 +471,14 @@ __device__ void attn_tile_chunks(AttnSmem<HD>& sm, const AttnItem* __restrict__ 
       const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
       vh = *(const u32x4_t*)vp;
       vl = *(const u32x4_t*)(vp + 32 * HD);
-      const int nv = vlim - (p0 + 8 * g);
-      if (nv < 8) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned keep = (2 * i + 1 < nv ? 0xFFFF0000u : 0u) | (2 * i < nv ? 0xFFFFu : 0u);
-          vh[i] &= keep;
-          vl[i] &= keep;
-        }
-      }
     };
+    auto vpost = [&](int, u32x4_t& vh, u32x4_t& vl) { mask_v(vh, vl, vlim - (p0 + 8 * g)); };
     unsigned valid8 = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim ? 1u : 0u) << i;
     f32x4_t acc[NB];
     float m, l;
-    chunk_partial<HD>(qsrc, ksrc, vsrc, valid8, acc, m, l);
+    chunk_partial<HD, true>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
     if (n >= units || p0 >= lim) continue;
     if (to_mix) {
       const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
