@@ -121,7 +121,7 @@ def _subtree(n: Node) -> List[Node]:
 def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = "greedy",
                tau: float = 1.0, gumbel=None, decs: bool = True,
                forced: Optional[Sequence[int]] = None, stats: Optional[dict] = None,
-               single_exit: bool = False) -> List[dict]:
+               single_exit: bool = False, branch_cap: int = 0) -> List[dict]:
     """DEX decoding of T tokens. Returns one record per commit:
     token, b, layers (= d_b), u (anchor candidates), margins, rounds (rounds
     since the previous commit). ``stats`` (optional dict) receives per-round
@@ -134,7 +134,16 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
     must reach the final depth) but does not exit, so it proposes no token and
     has no position child; the commit keeps branch 0 when u_0 matches and the
     final depth otherwise. Unmasked candidates follow (no shallower proposal
-    exists in a chain)."""
+    exists in a chain).
+
+    branch_cap: a pruned lattice (the sparse lattice named as future work in
+    Section 6). The pages give no policy; the one taken here is structural:
+    only nodes of explorers j < branch_cap spawn position children (0: no
+    pruning). Depth children are never pruned, so every anchor chain still
+    reaches the final depth and the commit rule is unchanged: the output stays
+    the plain model's. A commit whose branch b has no position child (b >=
+    branch_cap) keeps nothing, and a fresh tree starts from the new anchor,
+    as after the final branch."""
     N, P = len(X), len(prompt)
     ev.begin(list(prompt))
     anchor_tok = int(prompt[-1])
@@ -145,8 +154,10 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
     since = 0
     rows_log, nodes_log = [], []
     while len(recs) < T:
+        pruned = 0 < branch_cap < N
         tree = _subtree(root) if root is not None else []
-        assert len(tree) == (q * (q + 1) // 2 if single_exit else 2 ** q - 1), "nodes held at state q"
+        if not pruned:
+            assert len(tree) == (q * (q + 1) // 2 if single_exit else 2 ** q - 1), "nodes held at state q"
         # expand
         if q == 0:
             root = Node(etk=0, slot=(anchor_tok,), k=0, prior=[], round=rnd)
@@ -162,6 +173,8 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
                     new.append(c)
                 if f.cand is None:
                     continue                           # a node that did not exit
+                if pruned and f.k >= branch_cap:
+                    continue                           # pruned: no position branch from this explorer
                 c = Node(etk=0, slot=f.slot + (f.cand,), k=0, prior=[], round=rnd,
                          parent=f.etk, kind="position")
                 f.pos_child = c
@@ -171,7 +184,7 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
                 etk += 1
         if single_exit:
             assert len(new) == q + 1, "a single-exit round at state q creates q + 1 nodes"
-        else:
+        elif not pruned:
             assert len(new) == 2 ** q, "a round at state q creates 2^q nodes"
         ev.eval_slots([n.slot for n in new])
         # DECS + insert
@@ -206,7 +219,7 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
             break
         # collapse
         ev.commit(y)
-        if b < N - 1:
+        if b < N - 1 and chain[b].pos_child is not None:
             root = chain[b].pos_child
             assert root.slot == (anchor_tok, y)
             kept = sorted(_subtree(root), key=lambda n: n.etk)
