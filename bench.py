@@ -43,7 +43,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, Wd, prompts, commits, variant="dex", adapter_alpha=None):
+def cpu_baseline(w, Wd, prompts, commits, variant="dex", adapter_alpha=None, branch_cap=0):
     """Time the oracle's DEX decoder (oracle/decode.py, as it stands) on the
     first ``commits`` commits of sequence 0, excluding its prefill."""
     import numpy as np
@@ -85,7 +85,8 @@ def cpu_baseline(w, Wd, prompts, commits, variant="dex", adapter_alpha=None):
     g = gumbel_rows(w.seed_g, 1, commits + len(w.X), w.vocab)[0].numpy() if w.mode == "sample" else None
     t2 = time.time()
     recs = dex_decode(Prefilled(ev), prompts[0], commits, w.X, mode=w.mode, tau=w.tau, gumbel=g,
-                      decs=variant != "vanilla", single_exit=variant == "single_exit")
+                      decs=variant != "vanilla", single_exit=variant == "single_exit",
+                      branch_cap=branch_cap if variant == "pruned" else 0)
     t_dec = time.time() - t2
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else 1
@@ -110,10 +111,13 @@ def main():
     ap.add_argument("--adapter-alpha", type=float, default=None,
                     help="attach seeded inducing adapters (m = 2 d_model) with this gate at the non-final depths "
                          "(Section 3.4, Appendix C.2); the pages initialise alpha to 1e-3")
-    ap.add_argument("--variant", choices=["dex", "single_exit", "vanilla"], default="dex",
+    ap.add_argument("--variant", choices=["dex", "single_exit", "vanilla", "pruned"], default="dex",
                     help="dex: full depth exploration with DECS; single_exit: only the first and final "
                          "explorers propose (ablation of Section 4, Figure 4 right-top); vanilla: DECS off "
-                         "(Figure 4 right-bottom)")
+                         "(Figure 4 right-bottom); pruned: only explorers below --branch-cap spawn "
+                         "position children (the sparse lattice of Section 6)")
+    ap.add_argument("--branch-cap", type=int, default=2,
+                    help="pruned variant: position children only from explorers j < this cap")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ar", action="store_true")
     ap.add_argument("--traffic", default=os.path.join(ROOT, "profiles", "traffic_gemm_llama7b_x4_greedy.json"),
@@ -155,8 +159,9 @@ def main():
     cfg = D.model_config(w.n_layers, w.d_model, w.n_heads, w.n_kv_heads, w.head_dim, w.d_ffn, w.vocab,
                          w.rope_base, w.eps, w.tied, w.dtype, adapter_hidden=adapter_hidden(w) if ads else 0)
     max_ctx = w.prompt_len + T + N + 8
+    branch_cap = args.branch_cap if args.variant == "pruned" else 0
     opt = D.options(w.mode, w.tau, args.variant != "vanilla", w.batch, max_ctx, T, gum, False,
-                    single_exit=args.variant == "single_exit")
+                    single_exit=args.variant == "single_exit", branch_cap=branch_cap)
     ctx = D.Dex(cfg, Wd, w.X, opt, adapters=ads)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -234,7 +239,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, Wd, prompts, args.cpu_commits, args.variant, args.adapter_alpha)
+        cpu = cpu_baseline(w, Wd, prompts, args.cpu_commits, args.variant, args.adapter_alpha, branch_cap)
 
     layers = [c["layers"] for c in commits]
     out = {
@@ -252,7 +257,8 @@ def main():
         "data": "synthetic (seeded random-init weights and prompts)",
         "config": {"workload": w.name, "layers": w.n_layers, "d_model": w.d_model, "X": list(w.X),
                    "batch": w.batch, "prompt_len": w.prompt_len, "max_new_tokens": T, "mode": w.mode,
-                   "variant": args.variant, "adapter_alpha": args.adapter_alpha},
+                   "variant": args.variant, "adapter_alpha": args.adapter_alpha,
+                   "branch_cap": branch_cap or None},
         "roofline": roofline,
         "cpu_baseline": None if cpu is None else {k: v for k, v in cpu.items() if k != "tokens"},
         "dex": {"commits": len(commits), "mean_layers_per_token": round(float(np.mean(layers)), 3) if layers else None,

@@ -124,6 +124,15 @@ typedef struct {
                               intermediate ones run without proposing, so only explorer-0 nodes
                               spawn position children and a commit keeps branch 0 or N-1. The
                               round at state q has one row per explorer 0..q. 0: full DEX. */
+  int32_t branch_cap;      /* Pruned lattice (the sparse lattice the same paper names as future work,
+                              Section 6; the policy is this library's): only nodes of explorers
+                              j < branch_cap spawn position children, so a round creates only the
+                              nodes whose root path has no run of branch_cap or more depth moves
+                              before a position move. Depth children are never pruned and the
+                              commit rule is unchanged, so the output is still the plain model's;
+                              a commit with branch b >= branch_cap keeps nothing and the next tree
+                              starts fresh. 0 (or N): no pruning. Range 0..N; not combined with
+                              single_exit (which already implies the cap-1 node set). */
 } dex_options;
 
 /* One committed token (Algorithm 1, validate_and_commit). */

@@ -133,6 +133,7 @@ struct GemmArgs {
 };
 
 struct AttnItem {
+  int seq;          // sequence of the rows
   int row0;         // first row
   int nrows;        // rows (all of one sequence and one layer), nrows * (nq / nkv) <= kAttnUnits
   int stage;        // explorer of the rows; layer = layer_of(D, lattice, stage, lam)
@@ -142,6 +143,26 @@ struct AttnItem {
   int lead;         // items (this one and the next lead - 1, same sequence and stage) the
                     // attention block of this item covers; 0: covered by an earlier item
 };
+
+// Pruned lattice: whether heap node n (n1 = n + 1) is created when only nodes
+// of explorers below `cap` spawn position children (cap 0: every node). The
+// bits of n1 after its leading 1 are the node's path from the root (0 = depth
+// move, 1 = position move); a position move leaves a node whose explorer is
+// the number of depth moves since the previous position move (or the root),
+// so the node exists when every run of 0s followed by a 1 is shorter than cap.
+// The trailing 0s (the node's own explorer) are not constrained. cap = 1 gives
+// the single-exit node set n1 = (2^(a+1) - 1) 2^b.
+__host__ __device__ inline bool node_held(unsigned n1, int cap) {
+  if (cap <= 0) return true;
+  unsigned t = n1 >> __builtin_ctz(n1);   // odd: ends with the last position move
+  while (t > 1) {
+    t >>= 1;                              // that move
+    const int z = __builtin_ctz(t);       // depth moves before it
+    if (z >= cap) return false;
+    t >>= z;
+  }
+  return true;
+}
 
 // K/V storage. Every K or V value x is kept as a bfloat16 pair (hi, lo) with
 // hi = bf16(x) and lo = bf16(x - hi), both round-to-nearest-even, so that the

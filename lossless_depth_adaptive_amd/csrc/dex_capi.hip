@@ -38,9 +38,9 @@ hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const flo
                             float*, float*, float*, const ModelDims&, int, int, int, int, int, bool, hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
-                        const void*, float*, float*, float*, const float*, int, int, hipStream_t);
+                        const void*, float*, float*, float*, const float*, int, int, int, hipStream_t);
 hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
-                         float*, const int*, int, int, int, hipStream_t);
+                         float*, const int*, int, int, int, int, hipStream_t);
 hipError_t launch_promote(const SeqPlan*, int, const int*, const bf16_t*, bf16_t*, const ModelDims&, hipStream_t);
 hipError_t launch_ar_rows(const SeqPlan*, int, RowInfo*, const int*, int, hipStream_t);
 hipError_t launch_ar_commit(const SeqPlan*, int, const int*, const float*, int*, int*, int*, float*, int, int,
@@ -108,6 +108,8 @@ int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex
   if (o->max_new_tokens < 1) { err = "max_new_tokens must be positive"; return DEX_EINVAL; }
   if (o->mode != DEX_GREEDY && o->mode != DEX_SAMPLE) { err = "mode must be GREEDY or SAMPLE"; return DEX_EINVAL; }
   if (o->single_exit != 0 && o->single_exit != 1) { err = "single_exit must be 0 or 1"; return DEX_EINVAL; }
+  if (o->branch_cap < 0 || o->branch_cap > n_x) { err = "branch_cap must be 0..N"; return DEX_EINVAL; }
+  if (o->single_exit && o->branch_cap) { err = "branch_cap and single_exit cannot be combined"; return DEX_EINVAL; }
   if (o->mode == DEX_SAMPLE) {
     if (!(o->temperature > 0)) { err = "temperature must be positive"; return DEX_EINVAL; }
     if (!o->gumbel) { err = "sampling needs Gumbel rows"; return DEX_EINVAL; }
@@ -260,11 +262,11 @@ namespace {
 // inside a group).
 int attn_lead(int i, int n) { return i % kAttnSC ? 0 : std::min(kAttnSC, n - i); }
 
-// Single-exit ablation: heap node n exists when its path is position moves
-// followed by depth moves (n + 1 = (2^(a+1) - 1) 2^b).
-bool single_exit_node(int n) {
-  const unsigned t = (unsigned)(n + 1) >> __builtin_ctz(n + 1);
-  return (t & (t + 1)) == 0;
+// Node cap of the lattice (node_held): 1 for the single-exit ablation, the
+// pruned lattice's branch_cap below N, else 0 (every node).
+int node_cap(const dex_options& o, int N) {
+  if (o.single_exit) return 1;
+  return o.branch_cap > 0 && o.branch_cap < N ? o.branch_cap : 0;
 }
 
 // Groups of at least this many rows go to the wide GEMM kernel, the others to
@@ -633,6 +635,7 @@ template <typename T>
 int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out) {
   const int N = ctx->N, B = ctx->nseq;
   const int T_ = ctx->opt.max_new_tokens;
+  const int ncap = node_cap(ctx->opt, N);
   // Host plan: rows per (sequence, stage) from the FSM state alone.
   std::vector<int> live(B), rows_seq_stage((size_t)B * N, 0);
   int nlive = 0, ncommit = 0;
@@ -642,13 +645,14 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     if (!live[s]) continue;
     ++nlive;
     const int q = ar ? 0 : ctx->q_[s];
+    if (!ar && ncap) {   // pruned lattice (single-exit: one node per explorer 0..q)
+      for (int n = (1 << q) - 1; n <= (1 << (q + 1)) - 2; ++n)
+        if (node_held(n + 1, ncap)) ++rows_seq_stage[(size_t)s * N + __builtin_ctz(n + 1)];
+    }
     for (int j = 0; j < N; ++j) {
-      int r = 0;
+      int& r = rows_seq_stage[(size_t)s * N + j];
       if (ar) r = j == 0 ? 1 : 0;
-      else if (ctx->opt.single_exit) r = j <= q ? 1 : 0;   // one node per explorer 0..q
-      else if (j < q) r = 1 << (q - 1 - j);
-      else if (j == q) r = 1;
-      rows_seq_stage[(size_t)s * N + j] = r;
+      else if (!ncap) r = j < q ? 1 << (q - 1 - j) : (j == q ? 1 : 0);   // full lattice
       stage_tot[j] += r;
     }
   }
@@ -691,6 +695,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       const int mk = ctx->C_[s] + (ar ? 1 : (ctx->q_[s] - j + 1));
       for (int o = 0; o < cnt; o += per_item) {
         AttnItem& it = ctx->h_items[nitems++];
+        it.seq = s;
         it.row0 = ctx->h_plans[s].base[j] + o;
         it.nrows = std::min(per_item, cnt - o);
         it.stage = j;
@@ -717,7 +722,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       for (int j = 0; j < N; ++j)
         if (rows_seq_stage[(size_t)s * N + j]) attn_bytes[j] += C * kvrow;
       for (int n = (1 << q) - 1; n <= (1 << (q + 1)) - 2; ++n) {
-        if (!ar && ctx->opt.single_exit && !single_exit_node(n)) continue;
+        if (!ar && ncap && !node_held(n + 1, ncap)) continue;
         const int anc = ar ? 0 : __builtin_popcount(n + 1);
         const int j = ar ? 0 : __builtin_ctz(n + 1);
         attn_bytes[j] += anc * kvrow + ctx->D.nq * ctx->D.hd * 8.0;
@@ -741,7 +746,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     } else {
       HIPCHK(launch_sched<T>(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
                              ctx->D.P, ctx->opt.decs, ctx->embed, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms,
-                             ctx->D.d, ctx->opt.single_exit, st));
+                             ctx->D.d, ctx->opt.single_exit, ncap, st));
     }
     prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
     std::vector<std::pair<int, int>> stage_rows;
@@ -775,7 +780,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       } else {
         HIPCHK(launch_commit(ctx->plans, B, ctx->map, ctx->cand, ctx->margin, ctx->freel, ctx->cursor, ctx->anchor,
                              ctx->records, ctx->promote, ctx->dbg_u, ctx->dbg_m, ctx->Xd, N, ctx->D.P,
-                             ctx->opt.single_exit, st));
+                             ctx->opt.single_exit, ncap, st));
         HIPCHK(launch_promote(ctx->plans, B, ctx->promote, ctx->exb, ctx->kvc, ctx->D, st));
       }
       HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));
@@ -845,7 +850,8 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       out[n++] = c;
       ctx->C_[s] += 1;
       ctx->commits_[s] += 1;
-      ctx->q_[s] = ar ? 0 : N - 1 - c.branch;
+      // the kept subtree has done N - 1 - b rounds; a pruned branch kept nothing
+      ctx->q_[s] = ar || (ncap && c.branch >= ncap) ? 0 : N - 1 - c.branch;
     } else {
       ctx->q_[s] += 1;
     }
@@ -892,6 +898,7 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
       ctx->attn_groups = false;
       for (int o = 0; o < R; o += per_item) {
         AttnItem& it = ctx->h_items[nitems++];
+        it.seq = s;
         it.row0 = o;
         it.nrows = std::min(per_item, R - o);
         it.stage = 0;

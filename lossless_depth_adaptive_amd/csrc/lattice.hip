@@ -23,22 +23,28 @@ namespace dex {
 // that start a slot (explorer 0): residual, residual times the first layer's
 // attention-norm weight, and per-16-column sums of squares (the inputs of the
 // fused RMSNorm of the next GEMM).
-// Single-exit ablation ("Depth Exploration for LLM Decoding", Section 4,
-// Figure 4 right-top): only explorer-0 nodes spawn position children, so the
-// round's nodes are those whose path is a run of position moves followed by
-// depth moves, n + 1 = (2^(a+1) - 1) 2^(q-a) for a = 0..q: one per explorer,
-// none of them masked.
+// Pruned lattice (cap > 0): only the nodes node_held keeps are created; each
+// takes the next free slot in heap order and the next row of its explorer.
+// The single-exit ablation ("Depth Exploration for LLM Decoding", Section 4,
+// Figure 4 right-top) has the cap-1 node set, n + 1 = (2^(a+1) - 1) 2^(q-a)
+// for a = 0..q (one per explorer), and no masks.
 template <typename T>
 __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restrict__ rows,
                              int* __restrict__ map, const int* __restrict__ cand,
                              const int* __restrict__ freel, int* __restrict__ cursor,
                              const int* __restrict__ anchor_tok, int N, int P, int decs,
                              const T* __restrict__ E, float* __restrict__ hidden, float* __restrict__ xn,
-                             float* __restrict__ ssq, const float* __restrict__ g0, int d, int single_exit) {
+                             float* __restrict__ ssq, const float* __restrict__ g0, int d, int single_exit,
+                             int cap) {
   const int s = blockIdx.x;
   const SeqPlan pl = plans[s];
   if (!pl.live) return;
-  const int q = pl.q, nnew = single_exit ? q + 1 : 1 << q, first = (1 << q) - 1;
+  const int q = pl.q, first = (1 << q) - 1, total = 1 << q;
+  int nnew = total;
+  if (cap) {
+    nnew = 0;
+    for (int t = 0; t < total; ++t) nnew += node_held(first + t + 1, cap);
+  }
   const int cur = cursor[s];
   __shared__ int nemb;
   __shared__ int emb_h[1 << (kMaxN - 1)];
@@ -47,13 +53,25 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
   __syncthreads();
   int* mp = map + (size_t)s * P;
   const int* cd = cand + (size_t)s * P;
-  for (int t = threadIdx.x; t < nnew; t += blockDim.x) {
-    const int n = single_exit ? (((2 << t) - 1) << (q - t)) - 1 : first + t, n1 = n + 1;
+  for (int t = threadIdx.x; t < total; t += blockDim.x) {
+    const int n = first + t, n1 = n + 1;
+    if (cap && !node_held(n1, cap)) continue;
     const int depth = __builtin_ctz(n1);
     const int posoff = __popc(n1) - 1;
-    const int phys = freel[(size_t)s * P + cur + t];
+    // rank: kept nodes of the round before n; idx: those of n's explorer
+    int rank = t, idx = depth >= q ? 0 : (((n1 >> depth) - (1 << (q - depth)) - 1) >> 1);
+    if (cap) {
+      rank = idx = 0;
+      for (int t2 = 0; t2 < t; ++t2) {
+        const unsigned m1 = first + t2 + 1;
+        if (node_held(m1, cap)) {
+          ++rank;
+          idx += __builtin_ctz(m1) == depth;
+        }
+      }
+    }
+    const int phys = freel[(size_t)s * P + cur + rank];
     mp[n] = phys;
-    const int idx = single_exit || depth >= q ? 0 : (((n1 >> depth) - (1 << (q - depth)) - 1) >> 1);
     RowInfo R;
     R.seq = s;
     R.phys = phys;
@@ -118,15 +136,18 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
 // position child (heap 2^(k+1)) becomes the new tree: relative node j at level
 // lv maps to old node (2^(k+1) + 1) 2^lv - 1 + (j + 1 - 2^lv), for the
 // 2^(N-1-k) - 1 nodes it holds. Free slots are rebuilt in increasing order.
-// Single-exit ablation: only u_0 and u_{N-1} exist (branch 0 or N-1), and only
-// the kept subtree's single-exit nodes hold slots.
+// Pruned lattice (cap > 0): only the kept subtree's nodes that node_held keeps
+// hold slots (the subtree's own numbering gives the same answer as the old
+// tree's, since its root's path is k < cap depth moves and one position
+// move), and a branch k >= cap had no position child: nothing is kept.
+// Single-exit ablation (cap 1): only u_0 and u_{N-1} exist (branch 0 or N-1).
 __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict__ map,
                               const int* __restrict__ cand, const float* __restrict__ margin,
                               int* __restrict__ freel, int* __restrict__ cursor,
                               int* __restrict__ anchor_tok, int* __restrict__ records,
                               int* __restrict__ promote_src, int* __restrict__ dbg_u,
                               float* __restrict__ dbg_m, const int* __restrict__ Xd, int N, int P,
-                              int single_exit) {
+                              int single_exit, int cap) {
   const int s = blockIdx.x;
   const SeqPlan pl = plans[s];
   if (!pl.live || !pl.commit) return;
@@ -165,13 +186,11 @@ __global__ void commit_kernel(const SeqPlan* __restrict__ plans, int* __restrict
   }
   __syncthreads();
   const int k = ksh;
-  const int nk = (1 << (N - 1 - k)) - 1;
+  const int nk = cap && k >= cap ? 0 : (1 << (N - 1 - k)) - 1;
   const int root = 1 << (k + 1);
   for (int j = tid; j < nk; j += blockDim.x) {
     const int lv = 31 - __builtin_clz(j + 1);
-    const unsigned t = (unsigned)(j + 1) >> __builtin_ctz(j + 1);
-    const bool held = !single_exit || (t & (t + 1)) == 0;
-    nm[j] = held ? mp[((root + 1) << lv) - 1 + (j + 1 - (1 << lv))] : -1;
+    nm[j] = node_held(j + 1, cap) ? mp[((root + 1) << lv) - 1 + (j + 1 - (1 << lv))] : -1;
   }
   __syncthreads();
   for (int j = tid; j < nk; j += blockDim.x) {
@@ -270,23 +289,24 @@ template <typename T>
 hipError_t launch_sched(const SeqPlan* plans, int nseq, RowInfo* rows, int* map, const int* cand,
                         const int* freel, int* cursor, const int* anchor_tok, int N, int P, int decs,
                         const void* E, float* hidden, float* xn, float* ssq, const float* g0, int d,
-                        int single_exit, hipStream_t st) {
+                        int single_exit, int cap, hipStream_t st) {
   hipLaunchKernelGGL(sched_kernel<T>, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
-                     anchor_tok, N, P, decs, (const T*)E, hidden, xn, ssq, g0, d, single_exit);
+                     anchor_tok, N, P, decs, (const T*)E, hidden, xn, ssq, g0, d, single_exit, cap);
   return hipGetLastError();
 }
 template hipError_t launch_sched<float>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
                                         const int*, int, int, int, const void*, float*, float*, float*, const float*,
-                                        int, int, hipStream_t);
+                                        int, int, int, hipStream_t);
 template hipError_t launch_sched<bf16_t>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
                                          const int*, int, int, int, const void*, float*, float*, float*, const float*,
-                                         int, int, hipStream_t);
+                                         int, int, int, hipStream_t);
 
 hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* cand, const float* margin,
                          int* freel, int* cursor, int* anchor_tok, int* records, int* promote_src,
-                         int* dbg_u, float* dbg_m, const int* Xd, int N, int P, int single_exit, hipStream_t st) {
+                         int* dbg_u, float* dbg_m, const int* Xd, int N, int P, int single_exit, int cap,
+                         hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3(nseq), dim3(256), 0, st, plans, map, cand, margin, freel, cursor,
-                     anchor_tok, records, promote_src, dbg_u, dbg_m, Xd, N, P, single_exit);
+                     anchor_tok, records, promote_src, dbg_u, dbg_m, Xd, N, P, single_exit, cap);
   return hipGetLastError();
 }
 

@@ -179,42 +179,29 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4_t* acc, fl
   }
 }
 
-// LDS of one attention block: the shared-chunk role's query tile and chunk
-// partials, or the per-unit role's explore values.
-template <int HD> struct AttnSmem {
+// LDS of one attention block: the shared-chunk role's query tiles (up to
+// MAXT) and chunk partials, or the per-unit role's explore values.
+template <int HD, int MAXT> struct AttnSmem {
   union {
     struct {
       float red[kAttnSC][kAttnUnits][HD + 2];
-      bf16_t qsh[2][kAttnUnits][HD + 8];   // queries as (hi, lo), rows padded by 16 bytes
+      bf16_t qsh[MAXT][2][kAttnUnits][HD + 8];   // queries as (hi, lo), rows padded by 16 bytes
     } m;
     bf16_t ev[kAttnSC][kMaxN][2 * HD];      // per wave: V hi, V lo of the unit's explore entries
-    bf16_t qt[kAttnSC][2][kAttnUnits][HD + 8];  // per wave: its tile's queries as (hi, lo)
   };
 };
 
-template <int NB>
-__device__ __forceinline__ void fold4(float& M, float& L, f32x4_t* A, float m, float l, const f32x4_t* a) {
-  const float Mn = fmaxf(M, m);
-  const float al = exp2f(M - Mn), be = exp2f(m - Mn);
-  L = fmaf(l, be, L * al);
-#pragma unroll
-  for (int b = 0; b < NB; ++b)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) A[b][r] = fmaf(a[b][r], be, A[b][r] * al);
-  M = Mn;
-}
-
-// Queries of a tile of units, split into (hi, lo), into LDS rows padded by 16
-// bytes. Threads t0, t0 + step, ... share the work.
+// Queries of a tile of `units` units from row row0 on, split into (hi, lo),
+// into LDS rows padded by 16 bytes. Threads t0, t0 + step, ... share the work.
 template <int HD>
-__device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], const AttnItem& it, int h,
+__device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], int row0, int units, int h,
                                             const float* __restrict__ q, const ModelDims& D, int t0, int step) {
-  const int rep = D.nq / D.nkv, units = it.nrows * rep;
+  const int rep = D.nq / D.nkv;
   for (int t = t0; t < kAttnUnits * HD / 8; t += step) {
     const int u = t / (HD / 8), d8 = 8 * (t % (HD / 8));
     float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (u < units) {
-      const float* qr = q + ((size_t)(it.row0 + u / rep) * D.nq + h * rep + u % rep) * HD + d8;
+      const float* qr = q + ((size_t)(row0 + u / rep) * D.nq + h * rep + u % rep) * HD + d8;
       const f32x4_t a = *(const f32x4_t*)qr, b = *(const f32x4_t*)(qr + 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -232,7 +219,7 @@ __device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], c
 // Per-unit role: wave w computes chunk c (one of xc0, xc1) for unit u of the
 // item with that unit's own keys, into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
 template <int HD>
-__device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int c, int u,
+__device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, int c, int u,
                                 const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                 const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
                                 float* __restrict__ mix, const ModelDims& D, int lam, int lattice) {
@@ -245,7 +232,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int
   const int ncu = Ru.ncommit, limu = Ru.ncommit + Ru.n_anc;
   const bool active = u < units && c <= it.xc1 && p0 < limu;
   const size_t eslot = (size_t)D.S * D.nkv * 4 * HD;  // bf16 between node slots
-  const bf16_t* eb = exb + ex_base(D, Ru.seq, 0, lam, h);
+  const bf16_t* eb = exb + ex_base(D, it.seq, 0, lam, h);
   bf16_t (*ev)[2 * HD] = sm.ev[w];
   if (active) {
     for (int t = lane; t < (limu - ncu) * (HD / 4); t += 64) {
@@ -256,7 +243,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int
   __syncthreads();
   if (!active) return;
   const int layer = layer_of(D, lattice, it.stage, lam);
-  const bf16_t* tb = kvc + kv_head_base(D, Ru.seq, layer, h) + (size_t)c * 128 * HD;
+  const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 128 * HD;
   const float* qr = q + ((size_t)row * D.nq + qhd) * HD;
   // Every column of the query operand carries unit u; column u is kept.
   auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
@@ -317,185 +304,156 @@ __device__ void attn_unit_chunk(AttnSmem<HD>& sm, const AttnItem& it, int h, int
                       m, l, g);
 }
 
-// Shared role: wave w takes chunk kAttnSC * sc + w of the tile. In a
-// super-chunk without per-unit chunks the block folds the chunks per unit and
-// writes the super-chunk state part[row][qh][sc] = (acc[hd], m, l); in one with
-// them, its other chunks go to the mix slots for the combine kernel to fold.
-template <int HD>
-__device__ void attn_shared_chunks(AttnSmem<HD>& sm, const AttnItem& it, int h, int sc,
-                                   const RowInfo* __restrict__ rows, const float* __restrict__ q,
+// Shared role: wave w takes chunk kAttnSC * sc + w for the `count` unit tiles
+// (items first, first + 1, ...) of one sequence and stage, loading its K/V once
+// for all of them. Per tile, in a super-chunk without per-unit chunks the block
+// folds the chunks per unit and writes the super-chunk state
+// part[row][qh][sc] = (acc[hd], m, l); in one with them, the tile's chunks go
+// to the mix slots for the combine kernel to fold.
+template <int HD, int MAXT>
+__device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __restrict__ items, int first, int count,
+                                   int h, int sc, const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                    const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
                                    const ModelDims& D, int lam, int lattice, int nsc_max) {
-  constexpr int NB = HD / 16, HP = HD + 4;
+  constexpr int NB = HD / 16, NS = HD / 32, HP = HD + 4;
   auto& red = sm.m.red;
-  auto& qsh = sm.m.qsh;
-  const int rep = D.nq / D.nkv, units = it.nrows * rep;
+  const int rep = D.nq / D.nkv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const int layer = layer_of(D, lattice, it.stage, lam);
-  const int seq = rows[it.row0].seq;
-  load_q_tile<HD>(qsh, it, h, q, D, threadIdx.x, 64 * kAttnSC);
-  // This lane's unit n: key limit (0 past the tile).
-  int lim = 0;
-  if (n < units) {
-    const RowInfo& R = rows[it.row0 + n / rep];
-    lim = R.ncommit + R.n_anc;
+  const AttnItem it0 = items[first];   // the tiles share sequence, stage and explore chunks
+  const int layer = layer_of(D, lattice, it0.stage, lam);
+  // Every tile's rows and key limits up front: lane n's unit (lim) and fold
+  // thread fu's unit (flim). Loads of one kind are issued together.
+  const int fu = threadIdx.x >> 4, fs = threadIdx.x & 15;
+  int row0[MAXT], units[MAXT], lim[MAXT], flim[MAXT];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    row0[t] = t < count ? items[first + t].row0 : 0;
+    units[t] = t < count ? items[first + t].nrows * rep : 0;
   }
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    lim[t] = 0;
+    flim[t] = 0;
+    if (n < units[t]) {
+      const RowInfo& R = rows[row0[t] + n / rep];
+      lim[t] = R.ncommit + R.n_anc;
+    }
+    if (fu < units[t]) {
+      const RowInfo& R = rows[row0[t] + fu / rep];
+      flim[t] = R.ncommit + R.n_anc;
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t)
+    if (t < count) load_q_tile<HD>(sm.m.qsh[t], row0[t], units[t], h, q, D, threadIdx.x, 64 * kAttnSC);
   // Positions past every unit's limit may hold stale or never-written values:
-  // their V elements are zeroed so that p = 0 contributes exact zeros.
-  int vlim = lim;
+  // their V elements are zeroed so that p = 0 contributes exact zeros. (Below
+  // that limit every position holds a written key, so a unit with a smaller
+  // limit gets exact zeros there as well.)
+  int vlim = 0;
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) vlim = max(vlim, lim[t]);
   for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
   const int c = sc * kAttnSC + w, p0 = c * kKvTile;
-  const bool unit_chunk = it.xc0 >= 0 && c >= it.xc0 && c <= it.xc1;
-  const bool to_mix = sc_mixed(it, sc);
+  const bool unit_chunk = it0.xc0 >= 0 && c >= it0.xc0 && c <= it0.xc1;
+  const bool to_mix = sc_mixed(it0, sc);
+  const bool work = !unit_chunk && p0 < vlim;
   __syncthreads();
 
-  const bf16_t* tb = kvc + kv_head_base(D, seq, layer, h) + (size_t)c * 128 * HD;
-  if (!unit_chunk && p0 < vlim) {
-    auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
-      qh = *(const u32x4_t*)&qsh[0][n][32 * s + 8 * g];
-      ql = *(const u32x4_t*)&qsh[1][n][32 * s + 8 * g];
-    };
-    auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
-      const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
-      kh = *(const u32x4_t*)kp;
-      kl = *(const u32x4_t*)(kp + 32 * HD);
-    };
-    auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
+  // The chunk's K and V operands, every load issued before the first use.
+  const bf16_t* tb = kvc + kv_head_base(D, it0.seq, layer, h) + (size_t)c * 128 * HD;
+  u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
+  if (work) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
+        kh[t][s] = *(const u32x4_t*)kp;
+        kl[t][s] = *(const u32x4_t*)(kp + 32 * HD);
+      }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
       const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
-      vh = *(const u32x4_t*)vp;
-      vl = *(const u32x4_t*)(vp + 32 * HD);
-    };
-    auto vpost = [&](int, u32x4_t& vh, u32x4_t& vl) { mask_v(vh, vl, vlim - (p0 + 8 * g)); };
-    unsigned valid8 = 0;
+      vh[b] = *(const u32x4_t*)vp;
+      vl[b] = *(const u32x4_t*)(vp + 32 * HD);
+    }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim ? 1u : 0u) << i;
-    f32x4_t acc[NB];
-    float m, l;
-    chunk_partial<HD, true>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
-    if (n < units && p0 < lim) {
-      if (to_mix) {
-        const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
-        store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
-                          acc, m, l, g);
-      } else {
-        float* rd = red[w][n];
+    for (int b = 0; b < NB; ++b) mask_v(vh[b], vl[b], vlim - (p0 + 8 * g));
+  }
+
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+  for (int t = 0; t < MAXT; ++t) {
+    if (t >= count) break;
+    if (work) {
+      auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
+        qh = *(const u32x4_t*)&sm.m.qsh[t][0][n][32 * s + 8 * g];
+        ql = *(const u32x4_t*)&sm.m.qsh[t][1][n][32 * s + 8 * g];
+      };
+      auto ksrc = [&](int tt, int s, u32x4_t& a, u32x4_t& b) {
+        a = kh[tt][s];
+        b = kl[tt][s];
+      };
+      auto vsrc = [&](int b, u32x4_t& a, u32x4_t& bb) {
+        a = vh[b];
+        bb = vl[b];
+      };
+      auto vpost = [&](int, u32x4_t&, u32x4_t&) {};
+      unsigned valid8 = 0;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) rd[16 * b + 4 * g + r] = acc[b][r];
-        if (g == 0) {
-          rd[HD] = m;
-          rd[HD + 1] = l;
+      for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim[t] ? 1u : 0u) << i;
+      f32x4_t acc[NB];
+      float m, l;
+      chunk_partial<HD, false>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
+      if (n < units[t] && p0 < lim[t]) {
+        if (to_mix) {
+          const int row = row0[t] + n / rep, qhd = h * rep + n % rep;
+          store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it0.xc0 / kAttnSC)) * HP,
+                            acc, m, l, g);
+        } else {
+          float* rd = red[w][n];
+#pragma unroll
+          for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rd[16 * b + 4 * g + r] = acc[b][r];
+          if (g == 0) {
+            rd[HD] = m;
+            rd[HD + 1] = l;
+          }
         }
       }
     }
-  }
-  if (to_mix) return;
-  __syncthreads();
+    if (to_mix) continue;
+    __syncthreads();
 
-  // Fold the super-chunk's chunks per unit: thread (unit, sixteenth of hd).
-  constexpr int NA = HD / 16;
-  const int fu = threadIdx.x >> 4, fs = threadIdx.x & 15;
-  if (fu >= units) return;
-  const int row = it.row0 + fu / rep, qhd = h * rep + fu % rep;
-  const RowInfo& R = rows[row];
-  const int flim = R.ncommit + R.n_anc;
-  const int cb = sc * kAttnSC;
-  if (cb * kKvTile >= flim) return;
-  float M = red[0][fu][HD], L = red[0][fu][HD + 1], A[NA];
+    // Fold the super-chunk's chunks per unit: thread (unit, sixteenth of hd).
+    constexpr int NA = HD / 16;
+    if (fu < units[t]) {
+      const int row = row0[t] + fu / rep, qhd = h * rep + fu % rep;
+      const int cb = sc * kAttnSC;
+      if (cb * kKvTile < flim[t]) {
+        float M = red[0][fu][HD], L = red[0][fu][HD + 1], A[NA];
 #pragma unroll
-  for (int k = 0; k < NA; ++k) A[k] = red[0][fu][NA * fs + k];
-  for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < flim; ++ww) {
-    float a[NA];
+        for (int k = 0; k < NA; ++k) A[k] = red[0][fu][NA * fs + k];
+        for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < flim[t]; ++ww) {
+          float a[NA];
 #pragma unroll
-    for (int k = 0; k < NA; ++k) a[k] = red[ww][fu][NA * fs + k];
-    fold<NA>(M, L, A, red[ww][fu][HD], red[ww][fu][HD + 1], a);
-  }
-  float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP;
+          for (int k = 0; k < NA; ++k) a[k] = red[ww][fu][NA * fs + k];
+          fold<NA>(M, L, A, red[ww][fu][HD], red[ww][fu][HD + 1], a);
+        }
+        float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP;
 #pragma unroll
-  for (int k = 0; k < NA; k += 4) *(f32x4_t*)(dst + NA * fs + k) = f32x4_t{A[k], A[k + 1], A[k + 2], A[k + 3]};
-  if (fs == 0) {
-    dst[HD] = M;
-    dst[HD + 1] = L;
-  }
-}
-
-// Tile role: wave w takes unit tile (item) first + w of a group of items of one
-// sequence and stage, and runs the super-chunk's chunks itself, folding them in
-// registers in the same order as attn_shared_chunks. The waves read the same
-// K/V chunks, so the group costs one pass over them from HBM.
-template <int HD>
-__device__ void attn_tile_chunks(AttnSmem<HD>& sm, const AttnItem* __restrict__ items, int first, int count, int h,
-                                 int sc, const RowInfo* __restrict__ rows, const float* __restrict__ q,
-                                 const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
-                                 const ModelDims& D, int lam, int lattice, int nsc_max) {
-  constexpr int NB = HD / 16, HP = HD + 4;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-  const AttnItem it = items[first + min(w, count - 1)];
-  const bool active = w < count;
-  const int rep = D.nq / D.nkv, units = active ? it.nrows * rep : 0;
-  if (active) load_q_tile<HD>(sm.qt[w], it, h, q, D, lane, 64);
-  int lim = 0;
-  if (n < units) {
-    const RowInfo& R = rows[it.row0 + n / rep];
-    lim = R.ncommit + R.n_anc;
-  }
-  int vlim = lim;
-  for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
-  __syncthreads();
-  if (!active) return;
-  const int layer = layer_of(D, lattice, it.stage, lam);
-  const bf16_t* hb = kvc + kv_head_base(D, rows[it.row0].seq, layer, h);
-  const bool to_mix = sc_mixed(it, sc);
-  bf16_t (*qt)[kAttnUnits][HD + 8] = sm.qt[w];
-  float Ms = 0.f, Ls = 0.f;
-  f32x4_t As[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) As[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-  for (int k = 0; k < kAttnSC; ++k) {
-    const int c = sc * kAttnSC + k, p0 = c * kKvTile;
-    if (p0 >= vlim) break;
-    if (it.xc0 >= 0 && c >= it.xc0 && c <= it.xc1) continue;
-    const bf16_t* tb = hb + (size_t)c * 128 * HD;
-    auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
-      qh = *(const u32x4_t*)&qt[0][n][32 * s + 8 * g];
-      ql = *(const u32x4_t*)&qt[1][n][32 * s + 8 * g];
-    };
-    auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
-      const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
-      kh = *(const u32x4_t*)kp;
-      kl = *(const u32x4_t*)(kp + 32 * HD);
-    };
-    auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
-      const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
-      vh = *(const u32x4_t*)vp;
-      vl = *(const u32x4_t*)(vp + 32 * HD);
-    };
-    auto vpost = [&](int, u32x4_t& vh, u32x4_t& vl) { mask_v(vh, vl, vlim - (p0 + 8 * g)); };
-    unsigned valid8 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim ? 1u : 0u) << i;
-    f32x4_t acc[NB];
-    float m, l;
-    chunk_partial<HD, true>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
-    if (n >= units || p0 >= lim) continue;
-    if (to_mix) {
-      const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
-      store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP, acc,
-                        m, l, g);
-    } else if (k == 0) {
-      Ms = m;
-      Ls = l;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) As[b] = acc[b];
-    } else {
-      fold4<NB>(Ms, Ls, As, m, l, acc);
+        for (int k = 0; k < NA; k += 4)
+          *(f32x4_t*)(dst + NA * fs + k) = f32x4_t{A[k], A[k + 1], A[k + 2], A[k + 3]};
+        if (fs == 0) {
+          dst[HD] = M;
+          dst[HD + 1] = L;
+        }
+      }
     }
+    if (t + 1 < count) __syncthreads();   // the fold has read red before the next tile writes it
   }
-  if (to_mix || n >= units || sc * kAttnSCKeys >= lim) return;
-  const int row = it.row0 + n / rep, qhd = h * rep + n % rep;
-  store_partial<HD>(part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP, As, Ms, Ls, g);
 }
 
 // One launch, block = kAttnSC waves. Blocks [0, ntail): per-unit chunks,
@@ -507,7 +465,7 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
     const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb, float* __restrict__ mix,
     float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail, int nquad, int nsc) {
-  __shared__ AttnSmem<HD> sm;
+  __shared__ AttnSmem<HD, 1> sm;
   int b = blockIdx.x;
   if (b < ntail) {
     const int quad = b % nquad;
@@ -526,21 +484,25 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   const int ii = b / D.nkv;
   const AttnItem it = items[ii];
   if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD>(sm, it, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
+  attn_shared_chunks<HD, 1>(sm, items, ii, 1, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
-// Groups of several items (tile role). grid = (items, kv heads, super-chunks);
-// blocks of items that do not lead such a group return at once.
+// Groups of several items: the shared role over up to kAttnSC tiles. 1-D grid,
+// index = (item * nkv + h) * nsc + sc: consecutive blocks walk consecutive
+// super-chunks of one (item, kv head), so the blocks in flight stream a few
+// contiguous K/V regions. Blocks of items that do not lead a group return at
+// once.
 template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
     const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam,
-    int lattice, int nsc_max) {
-  __shared__ AttnSmem<HD> sm;
-  const int ii = blockIdx.x, sc = blockIdx.z;
+    int lattice, int nsc_max, int nsc) {
+  __shared__ AttnSmem<HD, kAttnSC> sm;
+  const int sc = blockIdx.x % nsc, ih = blockIdx.x / nsc;
+  const int ii = ih / D.nkv, h = ih % D.nkv;
   const AttnItem it = items[ii];
   if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_tile_chunks<HD>(sm, items, ii, it.lead, blockIdx.y, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
+  attn_shared_chunks<HD, kAttnSC>(sm, items, ii, it.lead, h, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
 // Fold the super-chunk states of each (row, query head) of an item in order
@@ -564,36 +526,51 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
     const float* base = part + ((size_t)row * nq + qh) * nsc_max * HP;
     const float* mbase = mix + ((size_t)row * nq + qh) * kMixSlots * HP;
     float M = 0.f, L = 0.f, A[HS];
-    for (int sc = 0; sc < nsc; ++sc) {
-      float ms, ls, as[HS];
-      if (sc_mixed(it, sc)) {
-        const int cb = sc * kAttnSC;
-        const float* pc = mbase + (cb - kAttnSC * (it.xc0 / kAttnSC)) * HP;
-        ms = pc[HD];
-        ls = pc[HD + 1];
+    // Super-chunk states are loaded kPF at a time, then folded in order.
+    constexpr int kPF = 16;
+    for (int sc0 = 0; sc0 < nsc; sc0 += kPF) {
+      float bm[kPF], bl[kPF], ba[kPF][HS];
 #pragma unroll
-        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
-        for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < lim; ++ww) {
-          const float* pw = pc + ww * HP;
-          float a[HS];
+      for (int j = 0; j < kPF; ++j) {
+        const int sc = sc0 + j;
+        if (sc < nsc && !sc_mixed(it, sc)) {
+          const float* pc = base + sc * HP;
+          bm[j] = pc[HD];
+          bl[j] = pc[HD + 1];
 #pragma unroll
-          for (int e = 0; e < HS; ++e) a[e] = pw[lane * HS + e];
-          fold<HS>(ms, ls, as, pw[HD], pw[HD + 1], a);
+          for (int e = 0; e < HS; ++e) ba[j][e] = pc[lane * HS + e];
         }
-      } else {
-        const float* pc = base + sc * HP;
-        ms = pc[HD];
-        ls = pc[HD + 1];
-#pragma unroll
-        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
       }
-      if (sc == 0) {
-        M = ms;
-        L = ls;
 #pragma unroll
-        for (int e = 0; e < HS; ++e) A[e] = as[e];
-      } else {
-        fold<HS>(M, L, A, ms, ls, as);
+      for (int j = 0; j < kPF; ++j) {
+        const int sc = sc0 + j;
+        if (sc >= nsc) break;
+        float ms = bm[j], ls = bl[j], as[HS];
+#pragma unroll
+        for (int e = 0; e < HS; ++e) as[e] = ba[j][e];
+        if (sc_mixed(it, sc)) {
+          const int cb = sc * kAttnSC;
+          const float* pc = mbase + (cb - kAttnSC * (it.xc0 / kAttnSC)) * HP;
+          ms = pc[HD];
+          ls = pc[HD + 1];
+#pragma unroll
+          for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
+          for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < lim; ++ww) {
+            const float* pw = pc + ww * HP;
+            float a[HS];
+#pragma unroll
+            for (int e = 0; e < HS; ++e) a[e] = pw[lane * HS + e];
+            fold<HS>(ms, ls, as, pw[HD], pw[HD + 1], a);
+          }
+        }
+        if (sc == 0) {
+          M = ms;
+          L = ls;
+#pragma unroll
+          for (int e = 0; e < HS; ++e) A[e] = as[e];
+        } else {
+          fold<HS>(M, L, A, ms, ls, as);
+        }
       }
     }
     const float inv = 1.0f / L;
@@ -631,13 +608,13 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* ro
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (groups) {
-    const dim3 ggrid(nitems, D.nkv, nsc);
+    const dim3 ggrid(nitems * D.nkv * nsc);
     if (D.hd == 128)
       hipLaunchKernelGGL((attn_group_kernel<128>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
-                         D, lam, lattice, nsc_max);
+                         D, lam, lattice, nsc_max, nsc);
     else
       hipLaunchKernelGGL((attn_group_kernel<64>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
-                         D, lam, lattice, nsc_max);
+                         D, lam, lattice, nsc_max, nsc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -75,8 +75,18 @@ def test_non_uniform_exploration_sets(X):
     ({}, dict(max_batch=0)),
     ({}, dict(max_batch=65)),
     ({}, dict(mode="sample")),                 # sampling without Gumbel rows
+    ({}, dict(branch_cap=-1)),
+    ({}, dict(branch_cap=5)),                  # above N = 4
+    ({}, dict(branch_cap=2, single_exit=True)),
 ])
 def test_invalid_shapes_and_options(kw, opt):
     with pytest.raises(D.DexError) as e:
         D.workspace_bytes(_cfg(**kw), [2, 4, 6, 8], D.options(**opt))
     assert e.value.code == D.DEX_EINVAL
+
+
+@pytest.mark.parametrize("cap", [0, 1, 2, 3, 4])
+def test_branch_cap_accepted(cap):
+    """The pruned lattice's cap is 0..N; it needs no workspace of its own."""
+    assert D.workspace_bytes(_cfg(), [2, 4, 6, 8], D.options(branch_cap=cap)) == \
+        D.workspace_bytes(_cfg(), [2, 4, 6, 8], D.options())

@@ -164,6 +164,45 @@ def test_single_exit_parity(name):
     assert checked >= total // 4
 
 
+@pytest.mark.parametrize("name,cap", [("tiny", 1), ("tiny_sample", 2), ("llama7b_x8_sample_narrow", 3),
+                                      ("qwen_gqa_x9_b4_narrow", 2), ("llama13b_x8_b4_narrow", 4)])
+def test_pruned_parity(name, cap):
+    """Pruned lattice (only explorers j < cap spawn position children): the GPU
+    stream equals GPU AR bit for bit, and the branch and layers of every
+    commit equal the full lattice's (they are a function of the committed
+    prefix); N rounds to the first commit, then b + 1 rounds after a kept
+    branch (b < cap) and N after a pruned one."""
+    from tests.gpu_helpers import device_weights, make_ctx, run
+    w, kw = CASES[name]
+    T = kw["T"]
+    N = len(w.X)
+    print(f"[case] pruned {name} cap={cap} X={w.X} batch={w.batch} mode={w.mode} T={T}", flush=True)
+    Wd = device_weights(w)
+    prompts = batch_prompts(w)
+    gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab) if w.mode == "sample" else None
+    gum_d = gum.cuda() if gum is not None else None
+    ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum_d, branch_cap=cap)
+    pr_recs, steps = run(ctx, prompts, T)
+    ctx.close()
+    ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum_d)
+    full_recs, _ = run(ctx, prompts, T)
+    ctx.close()
+    ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum_d)
+    ar_recs, _ = run(ctx, prompts, T, ar=True)
+    ctx.close()
+    for s in range(w.batch):
+        assert [r["token"] for r in pr_recs[s]] == [r["token"] for r in ar_recs[s]], f"seq {s}: pruned != AR"
+        for a, b in zip(pr_recs[s], ar_recs[s]):
+            assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+        assert [(r["branch"], r["layers"]) for r in pr_recs[s]] == [(r["branch"], r["layers"]) for r in full_recs[s]]
+    if w.batch == 1:
+        bs = [r["branch"] for r in pr_recs[0]]
+        assert steps == N + sum(b + 1 if b < cap else N for b in bs[:-1])
+    kept = sum(1 for s in range(w.batch) for r in pr_recs[s][:-1] if r["branch"] < cap)
+    pruned = sum(1 for s in range(w.batch) for r in pr_recs[s][:-1] if cap <= r["branch"] < N - 1)
+    print(f"[case] pruned {name} cap={cap} steps={steps} kept={kept} pruned-branch commits={pruned}", flush=True)
+
+
 def test_error_codes_on_device():
     from lossless_depth_adaptive_amd import dex as D
     from tests.gpu_helpers import device_weights, make_ctx
