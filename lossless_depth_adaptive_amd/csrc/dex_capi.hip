@@ -270,9 +270,13 @@ int node_cap(const dex_options& o, int N) {
 }
 
 // Groups of at least this many rows go to the wide GEMM kernel, the others to
-// the split-k kernel (both give a row the same bits).
+// the split-k kernel (both give a row the same bits). The split-k kernel
+// re-reads every row's activations for each 16-column tile, so its time grows
+// with the rows: on four 7B/13B-shaped weights it wins only below about 8 rows
+// (at 16 rows the wide kernel is 1.4-2x faster). A wide launch of fewer than
+// 256 blocks (d x d and down projections) runs split by k range.
 #ifndef DEX_WIDE_ROWS
-#define DEX_WIDE_ROWS 32
+#define DEX_WIDE_ROWS 8
 #endif
 constexpr int kWideRows = DEX_WIDE_ROWS;
 
@@ -294,8 +298,8 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
       if (flush && ga.ngroups) {
         hipError_t e;
         if (wide) {
-          const int blocks = ga.ngroups * ((ga.N / 16 + 7) / 8);
-          const bool split = blocks < 512 && rows <= kSplitRows && ga.N <= split_cols;
+          const int blocks = ga.ngroups * ((ga.N / 16 + kWideBT - 1) / kWideBT);
+          const bool split = blocks < 256 && rows <= kSplitRows && ga.N <= split_cols;
           e = launch_gemm_wide(ga, epi, split, st);
           *launches += split ? 2 : 1;
         } else {

@@ -418,11 +418,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 // that XCD's L2 once.
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
-#ifndef DEX_WIDE_WT
-#define DEX_WIDE_WT 4
-#endif
-constexpr int kWideWT = DEX_WIDE_WT;             // 16-column tiles per wave
-constexpr int kWideBT = 4 * kWideWT;             // per block
 
 // Logical block of hardware block b out of nb: the hardware hands blocks to
 // the 8 XCDs round-robin, and XCD x gets a contiguous run of logical ids.
