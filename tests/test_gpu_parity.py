@@ -59,7 +59,25 @@ CASES = {
         d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4096, batch=4, prompt_len=48), dict(T=20)),
     "qwen_gqa_x9_b4_narrow": (get_workload("qwen8b_x9_b16").scaled(
         d_model=512, n_heads=4, n_kv_heads=2, d_ffn=1536, vocab=4096, batch=4, prompt_len=40), dict(T=16)),
+    # edge cases: the most explorers the library takes (10, so 1023 lattice nodes per
+    # sequence), prompt lengths around the 32-position K/V tile in one batch (a one-token
+    # prompt included), and a wide batch
+    "tiny_N10": (tiny.scaled(tied=False, gamma=0.8, n_layers=10, X=tuple(range(1, 11))), dict(T=16)),
+    "tiny_ragged_b4": (tiny.scaled(mode="sample", seed_g=3001, batch=4), dict(T=24, lens=[1, 31, 33, 64])),
+    "tiny_b64": (tiny.scaled(batch=64), dict(T=6)),
 }
+
+
+def _prompts(w, kw):
+    """The workload's prompts, or prompts of the given per-sequence lengths."""
+    lens = kw.get("lens")
+    if lens is None:
+        return batch_prompts(w)
+    return [batch_prompts(w, length=n)[b] for b, n in enumerate(lens)]
+
+
+def _max_context(w, kw):
+    return max(len(p) for p in _prompts(w, kw)) + kw["T"] + len(w.X) + 8
 
 
 def _run_case(name):
@@ -70,15 +88,16 @@ def _run_case(name):
     N = len(w.X)
     print(f"[case] {name} L={w.n_layers} d={w.d_model} X={w.X} batch={w.batch} mode={w.mode} T={T}", flush=True)
     Wd = device_weights(w)
-    prompts = batch_prompts(w)
+    prompts = _prompts(w, kw)
+    mc = _max_context(w, kw)
     gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab) if w.mode == "sample" else None
     gum_d = gum.cuda() if gum is not None else None
     alpha = kw.get("adapter_alpha")
     ads_d = generate_adapters(w, alpha, device="cuda") if alpha is not None else None
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc)
     dex_recs, steps = run(ctx, prompts, T)
     ctx.close()
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc)
     ar_recs, ar_steps = run(ctx, prompts, T, ar=True)
     ctx.close()
     assert ar_steps == T
