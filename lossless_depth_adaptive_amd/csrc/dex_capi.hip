@@ -911,6 +911,11 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         it.lead = attn_lead(o / per_item, (R + per_item - 1) / per_item);
         ctx->attn_groups |= it.lead > 1;
       }
+      // A group's blocks skip super-chunks past its first item's max_keys:
+      // make that the group's largest (causal rows further down need more).
+      for (int i = 0; i < nitems; ++i)
+        for (int k = 1; k < ctx->h_items[i].lead; ++k)
+          ctx->h_items[i].max_keys = std::max(ctx->h_items[i].max_keys, ctx->h_items[i + k].max_keys);
       HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
       HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
       HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
