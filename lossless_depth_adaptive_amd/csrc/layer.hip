@@ -216,21 +216,25 @@ __device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], i
   }
 }
 
-// Per-unit role: wave w computes chunk c (one of xc0, xc1) for unit u of the
-// item with that unit's own keys, into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
+// Per-row role: wave w computes chunk c (one of xc0, xc1) for row rr of the
+// item with that row's own keys, for all rep = nq / nkv query heads of kv head
+// h at once (MFMA column n carries query head h rep + n; the others repeat a
+// query and are not stored), into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
+// A column's result depends only on its own query, so each unit gets the bits
+// it gets in a shared tile.
 template <int HD>
-__device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, int c, int u,
+__device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, int c, int rr,
                                 const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                 const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
                                 float* __restrict__ mix, const ModelDims& D, int lam, int lattice) {
   constexpr int NB = HD / 16, HP = HD + 4;
-  const int rep = D.nq / D.nkv, units = it.nrows * rep;
+  const int rep = D.nq / D.nkv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int p0 = c * kKvTile;
-  const int row = it.row0 + min(u, units - 1) / rep, qhd = h * rep + u % rep;
+  const int row = it.row0 + min(rr, it.nrows - 1);
   const RowInfo& Ru = rows[row];
   const int ncu = Ru.ncommit, limu = Ru.ncommit + Ru.n_anc;
-  const bool active = u < units && c <= it.xc1 && p0 < limu;
+  const bool active = rr < it.nrows && c <= it.xc1 && p0 < limu;
   const size_t eslot = (size_t)D.S * D.nkv * 4 * HD;  // bf16 between node slots
   const bf16_t* eb = exb + ex_base(D, it.seq, 0, lam, h);
   bf16_t (*ev)[2 * HD] = sm.ev[w];
@@ -244,8 +248,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
   if (!active) return;
   const int layer = layer_of(D, lattice, it.stage, lam);
   const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 128 * HD;
-  const float* qr = q + ((size_t)row * D.nq + qhd) * HD;
-  // Every column of the query operand carries unit u; column u is kept.
+  const float* qr = q + ((size_t)row * D.nq + h * rep + min(n, rep - 1)) * HD;
   auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
     const f32x4_t a = *(const f32x4_t*)(qr + 32 * s + 8 * g), b = *(const f32x4_t*)(qr + 32 * s + 8 * g + 4);
     const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -299,9 +302,9 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
   f32x4_t acc[NB];
   float m, l;
   chunk_partial<HD, false>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
-  if (n == u)
-    store_partial<HD>(mix + (((size_t)row * D.nq + qhd) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP, acc,
-                      m, l, g);
+  if (n < rep)
+    store_partial<HD>(mix + (((size_t)row * D.nq + h * rep + n) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
+                      acc, m, l, g);
 }
 
 // Shared role: wave w takes chunk kAttnSC * sc + w for the `count` unit tiles
@@ -456,8 +459,8 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
   }
 }
 
-// One launch, block = kAttnSC waves. Blocks [0, ntail): per-unit chunks,
-// index = ((item * nkv + h) * 2 + j) * nquad + quad -> chunk xc0 + j, unit
+// One launch, block = kAttnSC waves. Blocks [0, ntail): per-row chunks,
+// index = ((item * nkv + h) * 2 + j) * nquad + quad -> chunk xc0 + j, row
 // kAttnSC * quad + wave. Blocks from ntail: index = (item * nkv + h) * nsc + sc,
 // shared role for items that form a group of their own.
 template <int HD>
@@ -596,7 +599,8 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* ro
   if (nitems == 0) return hipSuccess;
   const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
   if (nsc > nsc_max || umax > kAttnUnits) return hipErrorInvalidValue;
-  const int nquad = (umax + kAttnSC - 1) / kAttnSC;
+  const int rep = D.nq / D.nkv, rmax = (umax + rep - 1) / rep;   // most rows of an item
+  const int nquad = (rmax + kAttnSC - 1) / kAttnSC;
   const int ntail = nitems * D.nkv * 2 * nquad;
   const dim3 grid(ntail + nitems * D.nkv * nsc);
   if (D.hd == 128)
