@@ -23,7 +23,11 @@ constexpr int kWideWT = DEX_WIDE_WT;  // wide GEMM: 16-column tiles per wave
 constexpr int kWideBT = 4 * kWideWT;  // wide GEMM: 16-column tiles per block (4 waves)
 constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item (one MFMA tile)
 constexpr int kKvTile = 32;          // positions per K/V cache tile = keys per attention chunk
-constexpr int kAttnSC = 4;           // chunks per attention super-chunk
+#ifndef DEX_ATTN_SC
+#define DEX_ATTN_SC 4
+#endif
+constexpr int kAttnSC = DEX_ATTN_SC;  // chunks per attention super-chunk (= waves per attention block)
+constexpr int kAttnGroup = 4;        // unit tiles (items) of one sequence and stage per grouped attention block
 constexpr int kAttnSCKeys = kKvTile * kAttnSC;
 
 typedef unsigned short bf16_t;

@@ -258,9 +258,9 @@ struct dex_ctx {
 namespace {
 
 // Attention blocks: the items of one (sequence, stage) are covered in groups of
-// up to kAttnSC consecutive items; item i of n leads a group of this size (0:
+// up to kAttnGroup consecutive items; item i of n leads a group of this size (0:
 // inside a group).
-int attn_lead(int i, int n) { return i % kAttnSC ? 0 : std::min(kAttnSC, n - i); }
+int attn_lead(int i, int n) { return i % kAttnGroup ? 0 : std::min(kAttnGroup, n - i); }
 
 // Node cap of the lattice (node_held): 1 for the single-exit ablation, the
 // pruned lattice's branch_cap below N, else 0 (every node).

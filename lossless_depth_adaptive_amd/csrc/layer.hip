@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   attn_shared_chunks<HD, 1>(sm, items, ii, 1, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
-// Groups of several items: the shared role over up to kAttnSC tiles. 1-D grid,
+// Groups of several items: the shared role over up to kAttnGroup tiles. 1-D grid,
 // index = (item * nkv + h) * nsc + sc: consecutive blocks walk consecutive
 // super-chunks of one (item, kv head), so the blocks in flight stream a few
 // contiguous K/V regions. Blocks of items that do not lead a group return at
@@ -500,12 +500,12 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
     const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
     const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam,
     int lattice, int nsc_max, int nsc) {
-  __shared__ AttnSmem<HD, kAttnSC> sm;
+  __shared__ AttnSmem<HD, kAttnGroup> sm;
   const int sc = blockIdx.x % nsc, ih = blockIdx.x / nsc;
   const int ii = ih / D.nkv, h = ih % D.nkv;
   const AttnItem it = items[ii];
   if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD, kAttnSC>(sm, items, ii, it.lead, h, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
+  attn_shared_chunks<HD, kAttnGroup>(sm, items, ii, it.lead, h, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
 // Fold the super-chunk states of each (row, query head) of an item in order
