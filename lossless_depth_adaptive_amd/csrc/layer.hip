@@ -37,12 +37,13 @@ namespace dex {
 // A chunk in which some row reads explore entries (positions it does not share
 // with the tile's other rows; the host marks them as chunks xc0..xc1 of the
 // item, at most two since a row has at most N explore keys) is computed once
-// per unit, with that unit's keys gathered into the same operand layout; every
-// other chunk is computed once for the whole tile with keys past a unit's limit
-// masked. Both give a unit the same operand values in the same MFMA order, hence
-// the same bits. The per-unit chunks are latency-bound, so they run as extra
-// blocks of the same launch, overlapping the bandwidth-bound shared chunks; the
-// super-chunks that hold them are folded by the combine kernel.
+// per row, with that row's keys gathered into the same operand layout and its
+// query heads of the kv head as the MFMA columns; every other chunk is computed
+// once for the whole tile with keys past a unit's limit masked. Both give a
+// unit the same operand values in the same MFMA order, hence the same bits.
+// The per-row chunks are latency-bound, so they run as extra blocks of the same
+// launch, overlapping the bandwidth-bound shared chunks; the super-chunks that
+// hold them are folded by the combine kernel.
 // ----------------------------------------------------------------------------
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
@@ -163,7 +164,7 @@ __device__ __forceinline__ void mask_v(u32x4_t& vh, u32x4_t& vl, int nv) {
 
 constexpr int kMixSlots = 2 * kAttnSC;   // chunk slots of the (at most two) mixed super-chunks
 
-// Whether super-chunk sc of the item holds a per-unit (explore) chunk.
+// Whether super-chunk sc of the item holds a per-row (explore) chunk.
 __device__ __forceinline__ bool sc_mixed(const AttnItem& it, int sc) {
   return it.xc0 >= 0 && (sc == it.xc0 / kAttnSC || sc == it.xc1 / kAttnSC);
 }
@@ -180,7 +181,7 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4_t* acc, fl
 }
 
 // LDS of one attention block: the shared-chunk role's query tiles (up to
-// MAXT) and chunk partials, or the per-unit role's explore values.
+// MAXT) and chunk partials, or the per-row role's explore values.
 template <int HD, int MAXT> struct AttnSmem {
   union {
     struct {
@@ -309,7 +310,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
 
 // Shared role: wave w takes chunk kAttnSC * sc + w for the `count` unit tiles
 // (items first, first + 1, ...) of one sequence and stage, loading its K/V once
-// for all of them. Per tile, in a super-chunk without per-unit chunks the block
+// for all of them. Per tile, in a super-chunk without per-row chunks the block
 // folds the chunks per unit and writes the super-chunk state
 // part[row][qh][sc] = (acc[hd], m, l); in one with them, the tile's chunks go
 // to the mix slots for the combine kernel to fold.
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
 }
 
 // Fold the super-chunk states of each (row, query head) of an item in order
-// and normalise. Super-chunks holding per-unit chunks are first folded here
+// and normalise. Super-chunks holding per-row chunks are first folded here
 // from their chunk partials, exactly as attn_kernel folds the others.
 // grid = (items, kv heads), block = 4 waves, one unit at a time per wave.
 template <int HD>
