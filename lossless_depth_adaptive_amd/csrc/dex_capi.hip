@@ -28,7 +28,7 @@ template <typename T>
 hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, int, int, int, int, int, hipStream_t);
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
-hipError_t launch_gemm_wide(const GemmArgs&, int, bool, hipStream_t);
+hipError_t launch_gemm_wide(const GemmArgs&, int, int, hipStream_t);
 hipError_t launch_head_reduce(const float*, int, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
@@ -273,8 +273,10 @@ int node_cap(const dex_options& o, int N) {
 // the split-k kernel (both give a row the same bits). The split-k kernel
 // re-reads every row's activations for each 16-column tile, so its time grows
 // with the rows: on four 7B/13B-shaped weights it wins only below about 8 rows
-// (at 16 rows the wide kernel is 1.4-2x faster). A wide launch of fewer than
-// 256 blocks (d x d and down projections) runs split by k range.
+// (at 16 rows the wide kernel is 1.4-2x faster). A wide launch that would
+// have fewer than 384 blocks at 4 column tiles per wave runs 2 tiles per wave
+// (7B gate/up and QKV: 8-15% faster), and one of fewer than 128 blocks (d x d
+// and down projections) runs split by k range.
 #ifndef DEX_WIDE_ROWS
 #define DEX_WIDE_ROWS 8
 #endif
@@ -298,10 +300,14 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
       if (flush && ga.ngroups) {
         hipError_t e;
         if (wide) {
-          const int blocks = ga.ngroups * ((ga.N / 16 + kWideBT - 1) / kWideBT);
-          const bool split = blocks < 256 && rows <= kSplitRows && ga.N <= split_cols;
-          e = launch_gemm_wide(ga, epi, split, st);
-          *launches += split ? 2 : 1;
+          // blocks at 4 tiles per wave: many -> as they are; a medium launch
+          // -> 2 tiles per wave (twice the blocks); few -> split by k range
+          const int blocks4 = ga.ngroups * ((ga.N / 16 + 15) / 16);
+          int shape = WIDE_T4;
+          if (blocks4 < 128 && rows <= kSplitRows && ga.N <= split_cols) shape = WIDE_SPLIT;
+          else if (blocks4 < 384) shape = WIDE_T2;
+          e = launch_gemm_wide(ga, epi, shape, st);
+          *launches += shape == WIDE_SPLIT ? 2 : 1;
         } else {
           e = launch_gemm<T>(ga, epi, st);
           ++*launches;

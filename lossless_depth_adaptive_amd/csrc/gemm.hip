@@ -403,8 +403,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 
 // ---------------------------------------------------------------------------
 // Wide GEMM for groups of many rows (bf16 weights). 1-D grid of (group, column
-// block[, k range]) blocks, block = 4 waves; a block computes 64 rows x
-// kWideBT column tiles, wave w the kWideWT tiles from kWideWT w. Each k-step's
+// block[, k range]) blocks, block = 4 waves; a block computes 64 rows x 4 WT
+// column tiles, wave w the WT tiles from WT w (WT does not change any output's
+// bits, only the block count). Each k-step's
 // activations (64 rows x 32, fp32) are split once into bf16 (hi, lo) and
 // stored in LDS in MFMA operand order, shared by the four waves; global loads
 // run two k-steps ahead in registers. Each output is reduced exactly as in
@@ -426,28 +427,29 @@ __device__ __forceinline__ int xcd_block(int b, int nb) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
-template <int EPI, bool SPLIT>
+template <int EPI, bool SPLIT, int WT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
+  constexpr int BT = 4 * WT;   // 16-column tiles per block
   constexpr int KSTEP = 32;
   constexpr bool NORM = epi_norm(EPI);
   const int ntiles = args.N >> 4;
-  const int ncb = (ntiles + kWideBT - 1) / kWideBT;
+  const int ncb = (ntiles + BT - 1) / BT;
   const int nblk = args.ngroups * ncb * (SPLIT ? kKSplit : 1);
   const int lb = xcd_block(blockIdx.x, nblk);
   const int gi = lb % args.ngroups;
   const int cb = (lb / args.ngroups) % ncb;
   const int z = SPLIT ? lb / (args.ngroups * ncb) : 0;
   const GemmGroup G = args.g[gi];
-  const int tb0 = cb * kWideBT;
+  const int tb0 = cb * BT;
   const int K = args.K, KS = K / KSTEP;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col16 = lane & 15, kg = lane >> 4;
-  const int t0 = tb0 + w * kWideWT;
+  const int t0 = tb0 + w * WT;
 
   // f[buf][part][mb][lane]: part 0 (hi) / 1 (lo) of row 16 mb + (lane & 15),
   // k 8 (lane >> 4) .. +7 of the k-step, the A operand of lane `lane`.
   struct Stage { u32x4_t f[2][2][4][64]; };
-  struct Out { float t[SPLIT ? 1 : 64][kWideBT * 16 + 4]; };   // the split form stores from registers
+  struct Out { float t[SPLIT ? 1 : 64][BT * 16 + 4]; };   // the split form stores from registers
   __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[64];
   __shared__ float scr[SPLIT ? 1 : 64][17];
@@ -459,16 +461,16 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   const int rr = ar < G.m ? ar : 0;
   const float* asrc = (NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
                             : (const float*)args.a + (size_t)(G.row0 + rr) * K) + 8 * kg;
-  const u32x4_t* bsrc[kWideWT];
+  const u32x4_t* bsrc[WT];
 #pragma unroll
-  for (int nb = 0; nb < kWideWT; ++nb) {
+  for (int nb = 0; nb < WT; ++nb) {
     const int t = t0 + nb < ntiles ? t0 + nb : ntiles - 1;
     bsrc[nb] = (const u32x4_t*)G.w + (size_t)t * KS * 64 + lane;
   }
 
   struct Pre {
     f32x4_t a[2];
-    u32x4_t b[kWideWT];
+    u32x4_t b[WT];
   };
   auto load_a = [&](int ks, Pre& p) {
     ks = ks < KS ? ks : KS - 1;
@@ -479,12 +481,12 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   auto load_b = [&](int ks, Pre& p) {
     ks = ks < KS ? ks : KS - 1;
 #pragma unroll
-    for (int nb = 0; nb < kWideWT; ++nb) p.b[nb] = bsrc[nb][(size_t)ks * 64];
+    for (int nb = 0; nb < WT; ++nb) p.b[nb] = bsrc[nb][(size_t)ks * 64];
   };
   // One k-step from the registers of p, which then take k-step ks + 2: the
   // activation loads go out once p.a is staged, the weight loads once the
   // MFMAs have read p.b.
-  auto step = [&](int ks, Pre& p, f32x4_t (&acc)[4][kWideWT]) {
+  auto step = [&](int ks, Pre& p, f32x4_t (&acc)[4][WT]) {
     const int buf = ks & 1;
     u32x4_t hv, lv;
 #pragma unroll
@@ -508,7 +510,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
       __builtin_memcpy(&ah, &ahu, 16);
       __builtin_memcpy(&al, &alu, 16);
 #pragma unroll
-      for (int nb = 0; nb < kWideWT; ++nb) {
+      for (int nb = 0; nb < WT; ++nb) {
         bf16x8_t bv;
         __builtin_memcpy(&bv, &p.b[nb], 16);
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[mb][nb], 0, 0, 0);
@@ -518,7 +520,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
     load_b(ks + 2, p);
   };
 
-  f32x4_t tot[4][kWideWT];
+  f32x4_t tot[4][WT];
   const int r0 = SPLIT ? z : 0, r1 = SPLIT ? z + 1 : kKSplit;
   int ks = (KS * r0) / kKSplit;
   Pre p0, p1;
@@ -528,11 +530,11 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   load_b(ks + 1, p1);
   for (int r = r0; r < r1; ++r) {
     const int re = (KS * (r + 1)) / kKSplit;
-    f32x4_t acc[4][kWideWT];
+    f32x4_t acc[4][WT];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kWideWT; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < WT; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (; ks + 2 <= re; ks += 2) {
       step(ks, p0, acc);
       step(ks + 1, p1, acc);
@@ -547,7 +549,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kWideWT; ++nb) tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
+      for (int nb = 0; nb < WT; ++nb) tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
   }
 
   if constexpr (SPLIT) {
@@ -555,7 +557,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < kWideWT; ++nb)
+      for (int nb = 0; nb < WT; ++nb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int rl = mb * 16 + kg * 4 + r;
@@ -577,11 +579,11 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < kWideWT; ++nb)
+    for (int nb = 0; nb < WT; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * kWideWT + nb) * 16 + col16] = tot[mb][nb][r];
+      for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * WT + nb) * 16 + col16] = tot[mb][nb][r];
   __syncthreads();
-  for (int tl = 0; tl < kWideBT && tb0 + tl < ntiles; ++tl) {
+  for (int tl = 0; tl < BT && tb0 + tl < ntiles; ++tl) {
     epilogue_tile<EPI, kWideThreads, 64>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
                                          rs_sh, scr);
     __syncthreads();
@@ -726,11 +728,11 @@ static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
   return launch_gemm_mb<T, 1, EPI>(a, mb, st);
 }
 
-template <int EPI, bool SPLIT>
+template <int EPI, bool SPLIT, int WT>
 static void wide_launch(const GemmArgs& a, hipStream_t st) {
-  const int ncb = (a.N / 16 + kWideBT - 1) / kWideBT;
+  const int ncb = (a.N / 16 + 4 * WT - 1) / (4 * WT);
   const dim3 grid(a.ngroups * ncb * (SPLIT ? kKSplit : 1));
-  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT>), grid, dim3(kWideThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT, WT>), grid, dim3(kWideThreads), 0, st, a);
   if (SPLIT) {
     hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3(a.ngroups, a.N / 16), dim3(kWideThreads), 0, st, a);
   }
@@ -740,14 +742,23 @@ static void wide_launch(const GemmArgs& a, hipStream_t st) {
 // many rows). split: one block per k range, partial sums through args.split
 // (groups' srow set, rows < kSplitRows), then their in-order sum and the
 // epilogue.
-hipError_t launch_gemm_wide(const GemmArgs& a, int epi, bool split, hipStream_t st) {
+// Launch shapes of the wide kernel: 4 tiles per wave, unsplit or split by k
+// range, or 2 tiles per wave unsplit (twice the blocks for medium launches).
+template <int EPI>
+static void wide_launch_shape(const GemmArgs& a, int shape, hipStream_t st) {
+  if (shape == WIDE_SPLIT) wide_launch<EPI, true, 4>(a, st);
+  else if (shape == WIDE_T2) wide_launch<EPI, false, 2>(a, st);
+  else wide_launch<EPI, false, 4>(a, st);
+}
+
+hipError_t launch_gemm_wide(const GemmArgs& a, int epi, int shape, hipStream_t st) {
   switch (epi) {
-    case EPI_QKV: split ? wide_launch<EPI_QKV, true>(a, st) : wide_launch<EPI_QKV, false>(a, st); break;
-    case EPI_RESID: split ? wide_launch<EPI_RESID, true>(a, st) : wide_launch<EPI_RESID, false>(a, st); break;
-    case EPI_SWIGLU: split ? wide_launch<EPI_SWIGLU, true>(a, st) : wide_launch<EPI_SWIGLU, false>(a, st); break;
-    case EPI_ADAPT1: split ? wide_launch<EPI_ADAPT1, true>(a, st) : wide_launch<EPI_ADAPT1, false>(a, st); break;
-    case EPI_ADAPT2: split ? wide_launch<EPI_ADAPT2, true>(a, st) : wide_launch<EPI_ADAPT2, false>(a, st); break;
-    default: split ? wide_launch<EPI_HEAD, true>(a, st) : wide_launch<EPI_HEAD, false>(a, st); break;
+    case EPI_QKV: wide_launch_shape<EPI_QKV>(a, shape, st); break;
+    case EPI_RESID: wide_launch_shape<EPI_RESID>(a, shape, st); break;
+    case EPI_SWIGLU: wide_launch_shape<EPI_SWIGLU>(a, shape, st); break;
+    case EPI_ADAPT1: wide_launch_shape<EPI_ADAPT1>(a, shape, st); break;
+    case EPI_ADAPT2: wide_launch_shape<EPI_ADAPT2>(a, shape, st); break;
+    default: wide_launch_shape<EPI_HEAD>(a, shape, st); break;
   }
   return hipGetLastError();
 }
