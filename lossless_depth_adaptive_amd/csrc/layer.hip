@@ -185,7 +185,7 @@ __device__ __forceinline__ void store_partial(float* dst, const f32x4_t* acc, fl
 template <int HD, int MAXT> struct AttnSmem {
   union {
     struct {
-      float red[kAttnSC][kAttnUnits][HD + 2];
+      alignas(16) float red[kAttnSC][kAttnUnits][HD + 4];   // chunk partials; rows 16-byte aligned
       bf16_t qsh[MAXT][2][kAttnUnits][HD + 8];   // queries as (hi, lo), rows padded by 16 bytes
     } m;
     bf16_t ev[kAttnSC][kMaxN][2 * HD];      // per wave: V hi, V lo of the unit's explore entries
@@ -418,9 +418,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
         } else {
           float* rd = red[w][n];
 #pragma unroll
-          for (int b = 0; b < NB; ++b)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rd[16 * b + 4 * g + r] = acc[b][r];
+          for (int b = 0; b < NB; ++b) *(f32x4_t*)(rd + 16 * b + 4 * g) = acc[b];
           if (g == 0) {
             rd[HD] = m;
             rd[HD + 1] = l;
@@ -431,25 +429,36 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
     if (to_mix) continue;
     __syncthreads();
 
-    // Fold the super-chunk's chunks per unit: thread (unit, sixteenth of hd).
-    constexpr int NA = HD / 16;
+    // Fold the super-chunk's chunks per unit: thread (unit, fs) takes the
+    // element quads 4 fs + 64 q (the fold is element-wise, so the split does
+    // not change any bits), which keeps a wave's 16-byte LDS reads on distinct
+    // banks.
+    constexpr int NA = HD / 16, NQ = NA / 4;
     if (fu < units[t]) {
       const int row = row0[t] + fu / rep, qhd = h * rep + fu % rep;
       const int cb = sc * kAttnSC;
       if (cb * kKvTile < flim[t]) {
         float M = red[0][fu][HD], L = red[0][fu][HD + 1], A[NA];
 #pragma unroll
-        for (int k = 0; k < NA; ++k) A[k] = red[0][fu][NA * fs + k];
+        for (int q4 = 0; q4 < NQ; ++q4) {
+          const f32x4_t v = *(const f32x4_t*)&red[0][fu][4 * fs + 64 * q4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) A[4 * q4 + e] = v[e];
+        }
         for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < flim[t]; ++ww) {
           float a[NA];
 #pragma unroll
-          for (int k = 0; k < NA; ++k) a[k] = red[ww][fu][NA * fs + k];
+          for (int q4 = 0; q4 < NQ; ++q4) {
+            const f32x4_t v = *(const f32x4_t*)&red[ww][fu][4 * fs + 64 * q4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) a[4 * q4 + e] = v[e];
+          }
           fold<NA>(M, L, A, red[ww][fu][HD], red[ww][fu][HD + 1], a);
         }
         float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP;
 #pragma unroll
-        for (int k = 0; k < NA; k += 4)
-          *(f32x4_t*)(dst + NA * fs + k) = f32x4_t{A[k], A[k + 1], A[k + 2], A[k + 3]};
+        for (int q4 = 0; q4 < NQ; ++q4)
+          *(f32x4_t*)(dst + 4 * fs + 64 * q4) = f32x4_t{A[4 * q4], A[4 * q4 + 1], A[4 * q4 + 2], A[4 * q4 + 3]};
         if (fs == 0) {
           dst[HD] = M;
           dst[HD + 1] = L;
@@ -530,51 +539,36 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
     const float* base = part + ((size_t)row * nq + qh) * nsc_max * HP;
     const float* mbase = mix + ((size_t)row * nq + qh) * kMixSlots * HP;
     float M = 0.f, L = 0.f, A[HS];
-    // Super-chunk states are loaded kPF at a time, then folded in order.
-    constexpr int kPF = 16;
-    for (int sc0 = 0; sc0 < nsc; sc0 += kPF) {
-      float bm[kPF], bl[kPF], ba[kPF][HS];
+    for (int sc = 0; sc < nsc; ++sc) {
+      float ms, ls, as[HS];
+      if (sc_mixed(it, sc)) {
+        const int cb = sc * kAttnSC;
+        const float* pc = mbase + (cb - kAttnSC * (it.xc0 / kAttnSC)) * HP;
+        ms = pc[HD];
+        ls = pc[HD + 1];
 #pragma unroll
-      for (int j = 0; j < kPF; ++j) {
-        const int sc = sc0 + j;
-        if (sc < nsc && !sc_mixed(it, sc)) {
-          const float* pc = base + sc * HP;
-          bm[j] = pc[HD];
-          bl[j] = pc[HD + 1];
+        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
+        for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < lim; ++ww) {
+          const float* pw = pc + ww * HP;
+          float a[HS];
 #pragma unroll
-          for (int e = 0; e < HS; ++e) ba[j][e] = pc[lane * HS + e];
+          for (int e = 0; e < HS; ++e) a[e] = pw[lane * HS + e];
+          fold<HS>(ms, ls, as, pw[HD], pw[HD + 1], a);
         }
+      } else {
+        const float* pc = base + sc * HP;
+        ms = pc[HD];
+        ls = pc[HD + 1];
+#pragma unroll
+        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
       }
+      if (sc == 0) {
+        M = ms;
+        L = ls;
 #pragma unroll
-      for (int j = 0; j < kPF; ++j) {
-        const int sc = sc0 + j;
-        if (sc >= nsc) break;
-        float ms = bm[j], ls = bl[j], as[HS];
-#pragma unroll
-        for (int e = 0; e < HS; ++e) as[e] = ba[j][e];
-        if (sc_mixed(it, sc)) {
-          const int cb = sc * kAttnSC;
-          const float* pc = mbase + (cb - kAttnSC * (it.xc0 / kAttnSC)) * HP;
-          ms = pc[HD];
-          ls = pc[HD + 1];
-#pragma unroll
-          for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
-          for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < lim; ++ww) {
-            const float* pw = pc + ww * HP;
-            float a[HS];
-#pragma unroll
-            for (int e = 0; e < HS; ++e) a[e] = pw[lane * HS + e];
-            fold<HS>(ms, ls, as, pw[HD], pw[HD + 1], a);
-          }
-        }
-        if (sc == 0) {
-          M = ms;
-          L = ls;
-#pragma unroll
-          for (int e = 0; e < HS; ++e) A[e] = as[e];
-        } else {
-          fold<HS>(M, L, A, ms, ls, as);
-        }
+        for (int e = 0; e < HS; ++e) A[e] = as[e];
+      } else {
+        fold<HS>(M, L, A, ms, ls, as);
       }
     }
     const float inv = 1.0f / L;
