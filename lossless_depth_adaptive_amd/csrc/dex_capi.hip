@@ -34,8 +34,8 @@ template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
 int attn_mix_slots();
-hipError_t launch_attention(const AttnItem*, int, const RowInfo*, int, const float*, const bf16_t*, const bf16_t*,
-                            float*, float*, float*, const ModelDims&, int, int, int, int, int, bool, hipStream_t);
+hipError_t launch_attention(const AttnItem*, int, const int*, int, int, const RowInfo*, int, const float*, const bf16_t*,
+                            const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
                         const void*, float*, float*, float*, const float*, int, int, int, hipStream_t);
@@ -175,7 +175,7 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
   w.rows = lay.take(R * sizeof(RowInfo));
   w.plans = lay.take(B * sizeof(SeqPlan));
-  w.items = lay.take(R * sizeof(AttnItem));
+  w.items = lay.take(R * (sizeof(AttnItem) + 4));   // items, then the attention block list (R ints)
   w.q = lay.take(R * nq * hd * 4);
   w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
   w.attn_out = lay.take(R * nq * hd * 4);
@@ -210,6 +210,7 @@ struct dex_ctx {
   RowInfo* rows;
   SeqPlan* plans;
   AttnItem* items;
+  int* item_list;   // attention block list: single items, then group leads (after the Rmax items)
   bf16_t *kvc, *exb;
   void *attn_out, *act, *embed, *head;
   // host state
@@ -221,6 +222,7 @@ struct dex_ctx {
   SeqPlan* h_plans = nullptr;
   int* h_records = nullptr;
   AttnItem* h_items = nullptr;
+  int* h_item_list = nullptr;     // attention block list (after the Rmax items of h_items)
   RowInfo* h_rows = nullptr;
   std::string err;
   int last_rows[kMaxN] = {0};
@@ -234,7 +236,8 @@ struct dex_ctx {
   hipStream_t cap_st = nullptr;   // private stream that round graphs are captured on
   bool prof = false;
   int attn_umax = 1;              // most units in one attention item of the current round
-  bool attn_groups = false;       // some attention item of the current pass leads a group of several
+  int attn_single = 0;            // attention items of the current pass that form a group of their own
+  int attn_groups = 0;            // attention items of the current pass that lead a group of several
   std::vector<Mark> marks;
   size_t nmarks = 0;
   // HIP graphs of whole rounds, keyed by the round's plan
@@ -261,6 +264,20 @@ namespace {
 // up to kAttnGroup consecutive items; item i of n leads a group of this size (0:
 // inside a group).
 int attn_lead(int i, int n) { return i % kAttnGroup ? 0 : std::min(kAttnGroup, n - i); }
+
+// Attention block list of the pass's first nitems items: the items that form a
+// group of their own (the shared-role blocks of attn_kernel), then the items
+// that lead a group of several (attn_group_kernel), so that neither launch
+// has blocks for items covered by another.
+void attn_block_list(dex_ctx* ctx, int nitems) {
+  int n1 = 0, ng = 0;
+  for (int i = 0; i < nitems; ++i)
+    if (ctx->h_items[i].lead == 1) ctx->h_item_list[n1++] = i;
+  for (int i = 0; i < nitems; ++i)
+    if (ctx->h_items[i].lead > 1) ctx->h_item_list[n1 + ng++] = i;
+  ctx->attn_single = n1;
+  ctx->attn_groups = ng;
+}
 
 // Node cap of the lattice (node_held): 1 for the single-exit ablation, the
 // pruned lattice's branch_cap below N, else 0 (every node).
@@ -576,9 +593,9 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
         attn_flops += attn_stage_flops[j];
       }
     int mk = prof_begin(ctx, DEX_PROF_ATTN);
-    HIPCHK(launch_attention(ctx->items, nitems, ctx->rows, nrows, ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail,
-                            ctx->attn_part, (float*)ctx->attn_out, D, lam, lattice, ctx->wp.nchunk, max_keys,
-                            lattice != 0 ? ctx->attn_umax : 0, ctx->attn_groups, st));
+    HIPCHK(launch_attention(ctx->items, nitems, ctx->item_list, ctx->attn_single, ctx->attn_groups, ctx->rows, nrows,
+                            ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail, ctx->attn_part, (float*)ctx->attn_out, D, lam,
+                            lattice, ctx->wp.nchunk, max_keys, lattice != 0 ? ctx->attn_umax : 0, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
     groups_for(lam, ctx->wp.wo, 1, false);
     ga.K = nq * hd;
@@ -698,7 +715,6 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   const int per_item = std::max(1, kAttnUnits / rep);
   int nitems = 0, max_keys = 0;
   ctx->attn_umax = 1;
-  ctx->attn_groups = false;
   for (int j = 0; j < N; ++j)
     for (int s = 0; s < B; ++s) {
       const int cnt = rows_seq_stage[(size_t)s * N + j];
@@ -714,11 +730,11 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
         it.xc0 = ar ? -1 : ctx->C_[s] / kKvTile;
         it.xc1 = ar ? -1 : (mk - 1) / kKvTile;
         it.lead = attn_lead(o / per_item, (cnt + per_item - 1) / per_item);
-        ctx->attn_groups |= it.lead > 1;
         max_keys = std::max(max_keys, mk);
         ctx->attn_umax = std::max(ctx->attn_umax, it.nrows * rep);
       }
     }
+  attn_block_list(ctx, nitems);
   // Algorithmic attention traffic of one layer slot, per stage: each
   // (sequence, stage) group reads its committed K/V once, each row its
   // explore entries.
@@ -750,6 +766,9 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     int mk = prof_begin(ctx, DEX_PROF_LATTICE);
     HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
     HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
+    if (ctx->attn_single + ctx->attn_groups)
+      HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list, (ctx->attn_single + ctx->attn_groups) * sizeof(int),
+                            hipMemcpyHostToDevice, st));
     if (ar) {
       HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
       HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
@@ -905,7 +924,6 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         r.kv_commit = 1;
       }
       int nitems = 0;
-      ctx->attn_groups = false;
       for (int o = 0; o < R; o += per_item) {
         AttnItem& it = ctx->h_items[nitems++];
         it.seq = s;
@@ -915,7 +933,6 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         it.max_keys = p0 + o + it.nrows;
         it.xc0 = it.xc1 = -1;
         it.lead = attn_lead(o / per_item, (R + per_item - 1) / per_item);
-        ctx->attn_groups |= it.lead > 1;
       }
       // A group's blocks skip super-chunks past its first item's max_keys:
       // make that the group's largest (causal rows further down need more).
@@ -923,7 +940,10 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
         for (int k = 1; k < ctx->h_items[i].lead; ++k)
           ctx->h_items[i].max_keys = std::max(ctx->h_items[i].max_keys, ctx->h_items[i + k].max_keys);
       HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
+      attn_block_list(ctx, nitems);
       HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
+      HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list, (ctx->attn_single + ctx->attn_groups) * sizeof(int),
+                            hipMemcpyHostToDevice, st));
       HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
       std::vector<std::pair<int, int>> stage_rows = {{0, R}};
       const int rc = run_layers<T>(ctx, R, stage_rows, ctx->L, 0, nitems, p0 + R, false);
@@ -1047,6 +1067,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->rows = (RowInfo*)ctx->at(wp.rows);
   ctx->plans = (SeqPlan*)ctx->at(wp.plans);
   ctx->items = (AttnItem*)ctx->at(wp.items);
+  ctx->item_list = (int*)(ctx->items + wp.Rmax);
   ctx->q = (float*)ctx->at(wp.q);
   ctx->ssq = (float*)ctx->at(wp.ssq);
   ctx->attn_out = ctx->at(wp.attn_out);
@@ -1063,11 +1084,12 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   if (hipStreamCreateWithFlags(&ctx->cap_st, hipStreamNonBlocking) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_plans, sizeof(SeqPlan) * D.B) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_records, 5 * 4 * D.B) != hipSuccess ||
-      hipHostMalloc((void**)&ctx->h_items, sizeof(AttnItem) * wp.Rmax) != hipSuccess ||
+      hipHostMalloc((void**)&ctx->h_items, (sizeof(AttnItem) + 4) * wp.Rmax) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_rows, sizeof(RowInfo) * wp.Rmax) != hipSuccess) {
     ctx->err = "stream creation or hipHostMalloc failed";
     return fail(DEX_EHIP);
   }
+  ctx->h_item_list = (int*)(ctx->h_items + wp.Rmax);
   rc = ctx->bf16 ? pack_weights<bf16_t>(ctx, w) : pack_weights<float>(ctx, w);
   if (rc) return fail(rc);
   // RoPE table: angle pos * base^(-2i/hd) in double, cos/sin rounded to float.

@@ -471,13 +471,15 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 
 // One launch, block = kAttnSC waves. Blocks [0, ntail): per-row chunks,
 // index = ((item * nkv + h) * 2 + j) * nquad + quad -> chunk xc0 + j, row
-// kAttnSC * quad + wave. Blocks from ntail: index = (item * nkv + h) * nsc + sc,
-// shared role for items that form a group of their own.
+// kAttnSC * quad + wave. Blocks from ntail: index = (k * nkv + h) * nsc + sc,
+// shared role for item list[k], the k-th of the items that form a group of
+// their own.
 template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
-    const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
-    const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb, float* __restrict__ mix,
-    float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail, int nquad, int nsc) {
+    const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
+    const float* __restrict__ q, const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
+    float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail,
+    int nquad, int nsc) {
   __shared__ AttnSmem<HD, 1> sm;
   int b = blockIdx.x;
   if (b < ntail) {
@@ -494,25 +496,24 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   b -= ntail;
   const int sc = b % nsc;
   b /= nsc;
-  const int ii = b / D.nkv;
+  const int ii = list[b / D.nkv];
   const AttnItem it = items[ii];
   if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
   attn_shared_chunks<HD, 1>(sm, items, ii, 1, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
 }
 
 // Groups of several items: the shared role over up to kAttnGroup tiles. 1-D grid,
-// index = (item * nkv + h) * nsc + sc: consecutive blocks walk consecutive
-// super-chunks of one (item, kv head), so the blocks in flight stream a few
-// contiguous K/V regions. Blocks of items that do not lead a group return at
-// once.
+// index = (k * nkv + h) * nsc + sc for the group led by item list[k]:
+// consecutive blocks walk consecutive super-chunks of one (group, kv head), so
+// the blocks in flight stream a few contiguous K/V regions.
 template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
-    const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows, const float* __restrict__ q,
-    const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam,
-    int lattice, int nsc_max, int nsc) {
+    const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
+    const float* __restrict__ q, const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
+    ModelDims D, int lam, int lattice, int nsc_max, int nsc) {
   __shared__ AttnSmem<HD, kAttnGroup> sm;
   const int sc = blockIdx.x % nsc, ih = blockIdx.x / nsc;
-  const int ii = ih / D.nkv, h = ih % D.nkv;
+  const int ii = list[ih / D.nkv], h = ih % D.nkv;
   const AttnItem it = items[ii];
   if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
   attn_shared_chunks<HD, kAttnGroup>(sm, items, ii, it.lead, h, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
@@ -584,36 +585,41 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
 int attn_chunk(int) { return kAttnSCKeys; }
 int attn_mix_slots() { return kMixSlots; }
 
-// umax: most units of an item whose rows read explore-buffer keys (lattice
-// rows), 0 when no row does; groups: some item leads a group of several.
-hipError_t launch_attention(const AttnItem* items, int nitems, const RowInfo* rows, int nrows, const float* q,
-                            const bf16_t* kvc, const bf16_t* exb, float* mix, float* part, float* out,
-                            const ModelDims& D, int lam, int lattice, int nsc_max, int max_keys, int umax, bool groups,
-                            hipStream_t st) {
+// list: the nsingle items that form a group of their own, then the ngroups
+// items that lead a group of several. umax: most units of an item whose rows
+// read explore-buffer keys (lattice rows), 0 when no row does.
+hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups,
+                            const RowInfo* rows, int nrows, const float* q, const bf16_t* kvc, const bf16_t* exb,
+                            float* mix, float* part, float* out, const ModelDims& D, int lam, int lattice, int nsc_max,
+                            int max_keys, int umax, hipStream_t st) {
   (void)nrows;
   if (nitems == 0) return hipSuccess;
   const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
-  if (nsc > nsc_max || umax > kAttnUnits) return hipErrorInvalidValue;
+  if (nsc > nsc_max || umax > kAttnUnits || nsingle < 0 || ngroups < 0 || nsingle + ngroups > nitems)
+    return hipErrorInvalidValue;
   const int rep = D.nq / D.nkv, rmax = (umax + rep - 1) / rep;   // most rows of an item
   const int nquad = (rmax + kAttnSC - 1) / kAttnSC;
   const int ntail = nitems * D.nkv * 2 * nquad;
-  const dim3 grid(ntail + nitems * D.nkv * nsc);
-  if (D.hd == 128)
-    hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, exb, mix, part, D,
-                       lam, lattice, nsc_max, ntail, nquad, nsc);
-  else
-    hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, exb, mix, part, D,
-                       lam, lattice, nsc_max, ntail, nquad, nsc);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (groups) {
-    const dim3 ggrid(nitems * D.nkv * nsc);
+  const dim3 grid(ntail + nsingle * D.nkv * nsc);
+  hipError_t e = hipSuccess;
+  if (grid.x > 0) {
     if (D.hd == 128)
-      hipLaunchKernelGGL((attn_group_kernel<128>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
-                         D, lam, lattice, nsc_max, nsc);
+      hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
+                         part, D, lam, lattice, nsc_max, ntail, nquad, nsc);
     else
-      hipLaunchKernelGGL((attn_group_kernel<64>), ggrid, dim3(64 * kAttnSC), 0, st, items, rows, q, kvc, mix, part,
-                         D, lam, lattice, nsc_max, nsc);
+      hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
+                         part, D, lam, lattice, nsc_max, ntail, nquad, nsc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (ngroups > 0 && nsc > 0) {
+    const dim3 ggrid(ngroups * D.nkv * nsc);
+    if (D.hd == 128)
+      hipLaunchKernelGGL((attn_group_kernel<128>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle, rows, q,
+                         kvc, mix, part, D, lam, lattice, nsc_max, nsc);
+    else
+      hipLaunchKernelGGL((attn_group_kernel<64>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle, rows, q,
+                         kvc, mix, part, D, lam, lattice, nsc_max, nsc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
