@@ -151,6 +151,13 @@ struct AttnItem {
                     // attention block of this item covers; 0: covered by an earlier item
 };
 
+// Logical block of hardware block b out of nb: the hardware hands blocks to
+// the 8 XCDs round-robin, and XCD x gets a contiguous run of logical ids.
+__device__ __forceinline__ int xcd_block(int b, int nb) {
+  const int x = b & 7, k = b >> 3, q = nb >> 3, rem = nb & 7;
+  return x * q + (x < rem ? x : rem) + k;
+}
+
 // Pruned lattice: whether heap node n (n1 = n + 1) is created when only nodes
 // of explorers below `cap` spawn position children (cap 0: every node). The
 // bits of n1 after its leading 1 are the node's path from the root (0 = depth

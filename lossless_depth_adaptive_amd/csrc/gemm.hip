@@ -420,13 +420,6 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
 
-// Logical block of hardware block b out of nb: the hardware hands blocks to
-// the 8 XCDs round-robin, and XCD x gets a contiguous run of logical ids.
-__device__ __forceinline__ int xcd_block(int b, int nb) {
-  const int x = b & 7, k = b >> 3, q = nb >> 3, rem = nb & 7;
-  return x * q + (x < rem ? x : rem) + k;
-}
-
 template <int EPI, bool SPLIT, int WT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
   constexpr int BT = 4 * WT;   // 16-column tiles per block

@@ -503,16 +503,20 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
 }
 
 // Groups of several items: the shared role over up to kAttnGroup tiles. 1-D grid,
-// index = (k * nkv + h) * nsc + sc for the group led by item list[k]:
-// consecutive blocks walk consecutive super-chunks of one (group, kv head), so
-// the blocks in flight stream a few contiguous K/V regions.
+// logical index (xcd_block) = (k * nkv + h) * nsc + sc for the group led by
+// item list[k]: each XCD walks consecutive super-chunks of one (group, kv head),
+// so the blocks in flight stream a few contiguous K/V regions and neighbouring
+// super-chunk records are written from one L2. (The single-item launch keeps
+// the hardware order: there the remap made the per-row blocks pile up on the
+// first XCDs.)
 template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
     const float* __restrict__ q, const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
     ModelDims D, int lam, int lattice, int nsc_max, int nsc) {
   __shared__ AttnSmem<HD, kAttnGroup> sm;
-  const int sc = blockIdx.x % nsc, ih = blockIdx.x / nsc;
+  const int lb = xcd_block(blockIdx.x, gridDim.x);   // an XCD takes consecutive super-chunks of one group
+  const int sc = lb % nsc, ih = lb / nsc;
   const int ii = list[ih / D.nkv], h = ih % D.nkv;
   const AttnItem it = items[ii];
   if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
