@@ -118,7 +118,11 @@ typedef struct {
   int32_t debug;           /* bit 0: keep the final-depth logits of each sequence's last commit;
                               bit 1: launch every round eagerly (no HIP-graph replay). By default a
                               round whose plan (FSM states, commit flags, attention chunk count) was
-                              seen before is captured once into a HIP graph and replayed. */
+                              seen before is captured once into a HIP graph and replayed;
+                              bit 2: grouped attention blocks always run whole spans of key
+                              positions (by default a launch does so only when that still fills
+                              the GPU). The results are the same bits either way; the bit lets
+                              small inputs exercise the span path. */
   int32_t single_exit;     /* 1: the single-exit ablation ("Depth Exploration for LLM Decoding",
                               Section 4, Figure 4 right-top): only explorers 0 and N-1 exit; the
                               intermediate ones run without proposing, so only explorer-0 nodes

@@ -35,7 +35,8 @@ hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, f
 int attn_chunk(int hd);
 int attn_mix_slots();
 hipError_t launch_attention(const AttnItem*, int, const int*, int, int, const RowInfo*, int, const float*, const bf16_t*,
-                            const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, hipStream_t);
+                            const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, bool,
+                            hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
                         const void*, float*, float*, float*, const float*, int, int, int, hipStream_t);
@@ -595,7 +596,8 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     int mk = prof_begin(ctx, DEX_PROF_ATTN);
     HIPCHK(launch_attention(ctx->items, nitems, ctx->item_list, ctx->attn_single, ctx->attn_groups, ctx->rows, nrows,
                             ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail, ctx->attn_part, (float*)ctx->attn_out, D, lam,
-                            lattice, ctx->wp.nchunk, max_keys, lattice != 0 ? ctx->attn_umax : 0, st));
+                            lattice, ctx->wp.nchunk, max_keys, lattice != 0 ? ctx->attn_umax : 0,
+                            (ctx->opt.debug & 4) != 0, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
     groups_for(lam, ctx->wp.wo, 1, false);
     ga.K = nq * hd;

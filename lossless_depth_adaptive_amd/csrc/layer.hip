@@ -163,6 +163,10 @@ __device__ __forceinline__ void mask_v(u32x4_t& vh, u32x4_t& vl, int nv) {
 }
 
 constexpr int kMixSlots = 2 * kAttnSC;   // chunk slots of the (at most two) mixed super-chunks
+// Super-chunks per span: a row's super-chunk states are folded left to right
+// within each span of kAttnSpan, and the span states left to right.
+constexpr int kAttnSpan = 16;
+constexpr int kSpanBlocks = 512;   // grouped blocks that fill the chip (two per CU)
 
 // Whether super-chunk sc of the item holds a per-row (explore) chunk.
 __device__ __forceinline__ bool sc_mixed(const AttnItem& it, int sc) {
@@ -308,17 +312,24 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
                       acc, m, l, g);
 }
 
-// Shared role: wave w takes chunk kAttnSC * sc + w for the `count` unit tiles
-// (items first, first + 1, ...) of one sequence and stage, loading its K/V once
-// for all of them. Per tile, in a super-chunk without per-row chunks the block
-// folds the chunks per unit and writes the super-chunk state
-// part[row][qh][sc] = (acc[hd], m, l); in one with them, the tile's chunks go
-// to the mix slots for the combine kernel to fold.
-template <int HD, int MAXT>
+// Shared role over super-chunks sc0 .. sc1 - 1, in order: for each, wave w
+// takes chunk kAttnSC * sc + w for the `count` unit tiles (items first,
+// first + 1, ...) of one sequence and stage, loading its K/V once for all of
+// them. Per tile, in a super-chunk without per-row chunks the block folds the
+// chunks per unit into the super-chunk state (acc[hd], m, l); in one with them,
+// the tile's chunks go to the mix slots for the combine kernel to fold. SPAN
+// false: one super-chunk, its state written to part[row][qh][sc]. SPAN true:
+// the super-chunks of span `span` (kAttnSpan of them from sc0 = kAttnSpan
+// span); the fold threads fold the states into the span state in registers
+// (the first as it is, each later one that holds keys of the unit by the fold)
+// and write it to part[row][qh][span]. Super-chunks with per-row chunks come
+// last in a row's keys, so the span state covers the ones before them.
+template <int HD, int MAXT, bool SPAN>
 __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __restrict__ items, int first, int count,
-                                   int h, int sc, const RowInfo* __restrict__ rows, const float* __restrict__ q,
-                                   const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
-                                   const ModelDims& D, int lam, int lattice, int nsc_max) {
+                                   int h, int sc0, int sc1, int span, const RowInfo* __restrict__ rows,
+                                   const float* __restrict__ q, const bf16_t* __restrict__ kvc,
+                                   float* __restrict__ mix, float* __restrict__ part, const ModelDims& D, int lam,
+                                   int lattice, int nsc_max) {
   constexpr int NB = HD / 16, NS = HD / 32, HP = HD + 4;
   auto& red = sm.m.red;
   const int rep = D.nq / D.nkv;
@@ -358,11 +369,23 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) vlim = max(vlim, lim[t]);
   for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
+  __syncthreads();
+
+  // Span state of fold thread fu's unit per tile (elements 4 fs + 64 q + e).
+  constexpr int NA = HD / 16, NQ = NA / 4;
+  float PM[MAXT], PL[MAXT], PA[MAXT][NA];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    PM[t] = PL[t] = 0.f;
+#pragma unroll
+    for (int e = 0; e < NA; ++e) PA[t][e] = 0.f;
+  }
+
+  for (int sc = sc0; sc < sc1; ++sc) {
   const int c = sc * kAttnSC + w, p0 = c * kKvTile;
   const bool unit_chunk = it0.xc0 >= 0 && c >= it0.xc0 && c <= it0.xc1;
   const bool to_mix = sc_mixed(it0, sc);
   const bool work = !unit_chunk && p0 < vlim;
-  __syncthreads();
 
   // The chunk's K and V operands, every load issued before the first use.
   const bf16_t* tb = kvc + kv_head_base(D, it0.seq, layer, h) + (size_t)c * 128 * HD;
@@ -433,7 +456,6 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
     // element quads 4 fs + 64 q (the fold is element-wise, so the split does
     // not change any bits), which keeps a wave's 16-byte LDS reads on distinct
     // banks.
-    constexpr int NA = HD / 16, NQ = NA / 4;
     if (fu < units[t]) {
       const int row = row0[t] + fu / rep, qhd = h * rep + fu % rep;
       const int cb = sc * kAttnSC;
@@ -455,17 +477,52 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
           }
           fold<NA>(M, L, A, red[ww][fu][HD], red[ww][fu][HD + 1], a);
         }
-        float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP;
+        if constexpr (SPAN) {
+          // Selects, not branches, keep the span state in one set of registers.
+          float Mf = PM[t], Lf = PL[t], Af[NA];
 #pragma unroll
-        for (int q4 = 0; q4 < NQ; ++q4)
-          *(f32x4_t*)(dst + 4 * fs + 64 * q4) = f32x4_t{A[4 * q4], A[4 * q4 + 1], A[4 * q4 + 2], A[4 * q4 + 3]};
-        if (fs == 0) {
-          dst[HD] = M;
-          dst[HD + 1] = L;
+          for (int e = 0; e < NA; ++e) Af[e] = PA[t][e];
+          fold<NA>(Mf, Lf, Af, M, L, A);
+          const bool firstsc = sc == sc0;
+          PM[t] = firstsc ? M : Mf;
+          PL[t] = firstsc ? L : Lf;
+#pragma unroll
+          for (int e = 0; e < NA; ++e) PA[t][e] = firstsc ? A[e] : Af[e];
+        } else {
+          float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + sc) * HP;
+#pragma unroll
+          for (int q4 = 0; q4 < NQ; ++q4)
+            *(f32x4_t*)(dst + 4 * fs + 64 * q4) = f32x4_t{A[4 * q4], A[4 * q4 + 1], A[4 * q4 + 2], A[4 * q4 + 3]};
+          if (fs == 0) {
+            dst[HD] = M;
+            dst[HD + 1] = L;
+          }
         }
       }
     }
-    if (t + 1 < count) __syncthreads();   // the fold has read red before the next tile writes it
+    if (SPAN || t + 1 < count) __syncthreads();   // the fold has read red before it is written again
+  }
+  }
+
+  if constexpr (SPAN) {
+    if (!sc_mixed(it0, sc0)) {
+#pragma unroll
+      for (int t = 0; t < MAXT; ++t) {
+        if (t >= count) break;
+        if (fu < units[t] && sc0 * kAttnSCKeys < flim[t]) {
+          const int row = row0[t] + fu / rep, qhd = h * rep + fu % rep;
+          float* dst = part + (((size_t)row * D.nq + qhd) * nsc_max + span) * HP;
+#pragma unroll
+          for (int q4 = 0; q4 < NQ; ++q4)
+            *(f32x4_t*)(dst + 4 * fs + 64 * q4) =
+                f32x4_t{PA[t][4 * q4], PA[t][4 * q4 + 1], PA[t][4 * q4 + 2], PA[t][4 * q4 + 3]};
+          if (fs == 0) {
+            dst[HD] = PM[t];
+            dst[HD + 1] = PL[t];
+          }
+        }
+      }
+    }
   }
 }
 
@@ -499,42 +556,58 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   const int ii = list[b / D.nkv];
   const AttnItem it = items[ii];
   if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD, 1>(sm, items, ii, 1, b % D.nkv, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
+  attn_shared_chunks<HD, 1, false>(sm, items, ii, 1, b % D.nkv, sc, sc + 1, 0, rows, q, kvc, mix, part, D, lam,
+                                   lattice, nsc_max);
 }
 
-// Groups of several items: the shared role over up to kAttnGroup tiles. 1-D grid,
-// logical index (xcd_block) = (k * nkv + h) * nsc + sc for the group led by
-// item list[k]: each XCD walks consecutive super-chunks of one (group, kv head),
-// so the blocks in flight stream a few contiguous K/V regions and neighbouring
-// super-chunk records are written from one L2. (The single-item launch keeps
-// the hardware order: there the remap made the per-row blocks pile up on the
-// first XCDs.)
-template <int HD>
-__global__ __launch_bounds__(64 * kAttnSC) void attn_group_kernel(
+// Groups of several items: the shared role over up to kAttnGroup tiles. SPAN:
+// block (group, h, span) runs the super-chunks of one span and writes span
+// states; otherwise block (group, h, sc) runs one super-chunk and writes its
+// state, and the combine kernel folds those into span states in the same
+// order (the launch picks SPAN when it has blocks enough to fill the chip).
+// 1-D grid, logical index (xcd_block) = (k * nkv + h) * nb + b for the group
+// led by item list[k]: each XCD walks consecutive super-chunks or spans of one
+// (group, kv head), so the blocks in flight stream a few contiguous K/V
+// regions. (The single-item launch keeps the hardware order: there the remap
+// made the per-row blocks pile up on the first XCDs.)
+template <int HD, bool SPAN>
+__global__ __launch_bounds__(64 * kAttnSC) __attribute__((amdgpu_waves_per_eu(2))) void attn_group_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
     const float* __restrict__ q, const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
-    ModelDims D, int lam, int lattice, int nsc_max, int nsc) {
+    ModelDims D, int lam, int lattice, int nsc_max, int nb) {
   __shared__ AttnSmem<HD, kAttnGroup> sm;
-  const int lb = xcd_block(blockIdx.x, gridDim.x);   // an XCD takes consecutive super-chunks of one group
-  const int sc = lb % nsc, ih = lb / nsc;
+  const int lb = xcd_block(blockIdx.x, gridDim.x);
+  const int bi = lb % nb, ih = lb / nb;
   const int ii = list[ih / D.nkv], h = ih % D.nkv;
   const AttnItem it = items[ii];
-  if (it.lead < 2 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD, kAttnGroup>(sm, items, ii, it.lead, h, sc, rows, q, kvc, mix, part, D, lam, lattice, nsc_max);
+  const int nsc = (it.max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
+  const int sc0 = SPAN ? bi * kAttnSpan : bi, sc1 = SPAN ? min(sc0 + kAttnSpan, nsc) : sc0 + 1;
+  if (it.lead < 2 || sc0 >= nsc || (lattice && lam >= stage_len(D, it.stage))) return;
+  attn_shared_chunks<HD, kAttnGroup, SPAN>(sm, items, ii, it.lead, h, sc0, sc1, bi, rows, q, kvc, mix, part, D, lam,
+                                           lattice, nsc_max);
 }
 
-// Fold the super-chunk states of each (row, query head) of an item in order
-// and normalise. Super-chunks holding per-row chunks are first folded here
-// from their chunk partials, exactly as attn_kernel folds the others.
-// grid = (items, kv heads), block = 4 waves, one unit at a time per wave.
+// Fold the states of each (row, query head) of an item and normalise: within
+// each span of kAttnSpan super-chunks the super-chunk states left to right,
+// then the span states left to right. An item of a group (lead != 1) has its
+// span states from attn_group_kernel when it ran spans (span_states),
+// covering each span's super-chunks up to the first one with per-row chunks;
+// otherwise an item has one state per super-chunk (from attn_kernel or
+// attn_group_kernel), folded here the same way. Super-chunks with
+// per-row chunks (the last ones of a row) are folded here from their chunk
+// partials, exactly as attn_kernel folds the others, and join their span's
+// fold in order. grid = (items, kv heads), block = 4 waves, one unit at a
+// time per wave.
 template <int HD>
 __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows,
                                     const float* __restrict__ mix, const float* __restrict__ part,
-                                    float* __restrict__ out, ModelDims D, int lam, int lattice, int nsc_max) {
+                                    float* __restrict__ out, ModelDims D, int lam, int lattice, int nsc_max,
+                                    int span_states) {
   constexpr int HS = HD / 64, HP = HD + 4;
   const AttnItem it = items[blockIdx.x];
   if (lattice && lam >= stage_len(D, it.stage)) return;
   const int nq = D.nq, h = blockIdx.y, rep = nq / D.nkv, units = it.nrows * rep;
+  const bool grouped = span_states && it.lead != 1;
   const int lane = threadIdx.x & 63;
   for (int u = threadIdx.x >> 6; u < units; u += blockDim.x >> 6) {
     const int row = it.row0 + u / rep, qh = h * rep + u % rep;
@@ -544,30 +617,56 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
     const float* base = part + ((size_t)row * nq + qh) * nsc_max * HP;
     const float* mbase = mix + ((size_t)row * nq + qh) * kMixSlots * HP;
     float M = 0.f, L = 0.f, A[HS];
-    for (int sc = 0; sc < nsc; ++sc) {
-      float ms, ls, as[HS];
-      if (sc_mixed(it, sc)) {
+    for (int k = 0; k * kAttnSpan < nsc; ++k) {
+      const int lo = k * kAttnSpan, hi = min(lo + kAttnSpan, nsc);
+      float ms = 0.f, ls = 0.f, as[HS];
+      bool have = false;
+      // Folds state (m, l, a) into the span state.
+      auto join = [&](float m, float l, const float* a) {
+        if (have) {
+          fold<HS>(ms, ls, as, m, l, a);
+        } else {
+          ms = m;
+          ls = l;
+#pragma unroll
+          for (int e = 0; e < HS; ++e) as[e] = a[e];
+          have = true;
+        }
+      };
+      if (grouped) {
+        if (!sc_mixed(it, lo)) {
+          const float* pc = base + k * HP;
+          float a[HS];
+#pragma unroll
+          for (int e = 0; e < HS; ++e) a[e] = pc[lane * HS + e];
+          join(pc[HD], pc[HD + 1], a);
+        }
+      } else {
+        for (int sc = lo; sc < hi && !sc_mixed(it, sc); ++sc) {
+          const float* pc = base + sc * HP;
+          float a[HS];
+#pragma unroll
+          for (int e = 0; e < HS; ++e) a[e] = pc[lane * HS + e];
+          join(pc[HD], pc[HD + 1], a);
+        }
+      }
+      for (int sc = lo; sc < hi; ++sc) {
+        if (!sc_mixed(it, sc)) continue;
         const int cb = sc * kAttnSC;
         const float* pc = mbase + (cb - kAttnSC * (it.xc0 / kAttnSC)) * HP;
-        ms = pc[HD];
-        ls = pc[HD + 1];
+        float mm = pc[HD], lm = pc[HD + 1], am[HS];
 #pragma unroll
-        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
+        for (int e = 0; e < HS; ++e) am[e] = pc[lane * HS + e];
         for (int ww = 1; ww < kAttnSC && (cb + ww) * kKvTile < lim; ++ww) {
           const float* pw = pc + ww * HP;
           float a[HS];
 #pragma unroll
           for (int e = 0; e < HS; ++e) a[e] = pw[lane * HS + e];
-          fold<HS>(ms, ls, as, pw[HD], pw[HD + 1], a);
+          fold<HS>(mm, lm, am, pw[HD], pw[HD + 1], a);
         }
-      } else {
-        const float* pc = base + sc * HP;
-        ms = pc[HD];
-        ls = pc[HD + 1];
-#pragma unroll
-        for (int e = 0; e < HS; ++e) as[e] = pc[lane * HS + e];
+        join(mm, lm, am);
       }
-      if (sc == 0) {
+      if (k == 0) {
         M = ms;
         L = ls;
 #pragma unroll
@@ -591,11 +690,12 @@ int attn_mix_slots() { return kMixSlots; }
 
 // list: the nsingle items that form a group of their own, then the ngroups
 // items that lead a group of several. umax: most units of an item whose rows
-// read explore-buffer keys (lattice rows), 0 when no row does.
+// read explore-buffer keys (lattice rows), 0 when no row does. span: grouped
+// blocks run whole spans whatever their count.
 hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups,
                             const RowInfo* rows, int nrows, const float* q, const bf16_t* kvc, const bf16_t* exb,
                             float* mix, float* part, float* out, const ModelDims& D, int lam, int lattice, int nsc_max,
-                            int max_keys, int umax, hipStream_t st) {
+                            int max_keys, int umax, bool span, hipStream_t st) {
   (void)nrows;
   if (nitems == 0) return hipSuccess;
   const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
@@ -616,23 +716,37 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // Grouped blocks run whole spans when that still gives the chip a block for
+  // every slot (two per CU), else one super-chunk each.
+  const int nspan = (nsc + kAttnSpan - 1) / kAttnSpan;
+  const int span_states = ngroups > 0 && (span || ngroups * D.nkv * nspan >= kSpanBlocks);
   if (ngroups > 0 && nsc > 0) {
-    const dim3 ggrid(ngroups * D.nkv * nsc);
-    if (D.hd == 128)
-      hipLaunchKernelGGL((attn_group_kernel<128>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle, rows, q,
-                         kvc, mix, part, D, lam, lattice, nsc_max, nsc);
-    else
-      hipLaunchKernelGGL((attn_group_kernel<64>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle, rows, q,
-                         kvc, mix, part, D, lam, lattice, nsc_max, nsc);
+    const int nb = span_states ? nspan : nsc;
+    const dim3 ggrid(ngroups * D.nkv * nb);
+    if (D.hd == 128) {
+      if (span_states)
+        hipLaunchKernelGGL((attn_group_kernel<128, true>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
+                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
+      else
+        hipLaunchKernelGGL((attn_group_kernel<128, false>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
+                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
+    } else {
+      if (span_states)
+        hipLaunchKernelGGL((attn_group_kernel<64, true>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
+                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
+      else
+        hipLaunchKernelGGL((attn_group_kernel<64, false>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
+                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
+    }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (D.hd == 128)
     hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
-                       out, D, lam, lattice, nsc_max);
+                       out, D, lam, lattice, nsc_max, span_states);
   else
     hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
-                       out, D, lam, lattice, nsc_max);
+                       out, D, lam, lattice, nsc_max, span_states);
   return hipGetLastError();
 }
 

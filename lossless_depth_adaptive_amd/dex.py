@@ -113,16 +113,18 @@ def model_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab,
 
 def options(mode="greedy", temperature=1.0, decs=True, max_batch=1, max_context=1024,
             max_new_tokens=256, gumbel=None, debug=False, graphs=True, single_exit=False,
-            branch_cap=0) -> Options:
+            branch_cap=0, span_attention=False) -> Options:
     """``gumbel``: CUDA float32 tensor [max_batch, rows, vocab] or None. ``debug`` keeps the
     final-depth logits of each last commit; ``graphs=False`` launches every round eagerly;
     ``single_exit`` selects the single-exit ablation; ``branch_cap`` > 0 the pruned lattice
-    (position children only from explorers below it)."""
+    (position children only from explorers below it); ``span_attention`` makes grouped
+    attention blocks always run whole spans (same results; for tests)."""
     return Options(SAMPLE if mode == "sample" else GREEDY, float(temperature), int(bool(decs)),
                    max_batch, max_context, max_new_tokens,
                    None if gumbel is None else gumbel.data_ptr(),
                    0 if gumbel is None else gumbel.shape[1],
-                   int(bool(debug)) | (0 if graphs else 2), int(bool(single_exit)), int(branch_cap))
+                   int(bool(debug)) | (0 if graphs else 2) | (4 if span_attention else 0),
+                   int(bool(single_exit)), int(branch_cap))
 
 
 def workspace_bytes(cfg: ModelConfig, X: Sequence[int], opt: Options) -> int:

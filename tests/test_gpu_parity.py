@@ -34,6 +34,8 @@ pytestmark = pytest.mark.gpu
 tiny = get_workload("tiny_f32")
 small = dict(d_model=512, n_heads=4, n_kv_heads=4, d_ffn=1376, vocab=4096)
 
+qwen_long = get_workload("qwen8b_x9_b16").scaled(d_model=512, n_heads=4, n_kv_heads=2, d_ffn=1536, vocab=4096,
+                                                  batch=1, prompt_len=2030, n_layers=18, X=tuple(range(2, 19, 2)))
 CASES = {
     "tiny": (tiny, dict(T=64)),
     "tiny_sample": (tiny.scaled(mode="sample", seed_g=3001), dict(T=48)),
@@ -65,6 +67,15 @@ CASES = {
     "tiny_N10": (tiny.scaled(tied=False, gamma=0.8, n_layers=10, X=tuple(range(1, 11))), dict(T=16)),
     "tiny_ragged_b4": (tiny.scaled(mode="sample", seed_g=3001, batch=4), dict(T=24, lens=[1, 31, 33, 64])),
     "tiny_b64": (tiny.scaled(batch=64), dict(T=6)),
+    # grouped attention forced to run whole spans (span=True; by default only launches
+    # that fill the GPU do), and contexts that cross the first span boundary (2048 keys)
+    # while decoding, so that a row folds two spans and the explore keys sit first in
+    # the second span for some rounds and later in it for others
+    "qwen_gqa_x9_b4_narrow_span": (get_workload("qwen8b_x9_b16").scaled(
+        d_model=512, n_heads=4, n_kv_heads=2, d_ffn=1536, vocab=4096, batch=4, prompt_len=40),
+        dict(T=16, span=True)),
+    "qwen_gqa_long": (qwen_long, dict(T=32)),
+    "qwen_gqa_long_span": (qwen_long, dict(T=32, span=True)),
 }
 
 
@@ -94,10 +105,11 @@ def _run_case(name):
     gum_d = gum.cuda() if gum is not None else None
     alpha = kw.get("adapter_alpha")
     ads_d = generate_adapters(w, alpha, device="cuda") if alpha is not None else None
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc)
+    span = kw.get("span", False)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span)
     dex_recs, steps = run(ctx, prompts, T)
     ctx.close()
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span)
     ar_recs, ar_steps = run(ctx, prompts, T, ar=True)
     ctx.close()
     assert ar_steps == T
