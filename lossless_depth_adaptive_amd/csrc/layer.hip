@@ -31,7 +31,9 @@ namespace dex {
 //                 p (each lane's eight in key order, then lanes g^1, g^2 by
 //                 butterfly); acc = V^T P^T by one MFMA chain;
 //   super-chunk = kAttnSC chunks folded left to right (fold below);
-//   row         = super-chunks folded left to right by attn_combine_kernel.
+//   span        = kAttnSpan super-chunks folded left to right (by a grouped
+//                 block, or by attn_combine_kernel from super-chunk states);
+//   row         = spans folded left to right by attn_combine_kernel.
 // Queries arrive pre-multiplied by log2(e)/sqrt(hd).
 //
 // A chunk in which some row reads explore entries (positions it does not share
