@@ -73,11 +73,16 @@ __device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo)
   }
 }
 
+// 2^x by the hardware instruction (v_exp_f32): results below 2^-126 come out
+// as zero rather than subnormal, which saves the range fix-up exp2f adds
+// around it. Every softmax weight and fold factor takes this one path.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Fold partial (m, l, a) into state (M, L, A); both describe non-empty key sets.
 template <int NA>
 __device__ __forceinline__ void fold(float& M, float& L, float* A, float m, float l, const float* a) {
   const float Mn = fmaxf(M, m);
-  const float al = exp2f(M - Mn), be = exp2f(m - Mn);
+  const float al = exp2_hw(M - Mn), be = exp2_hw(m - Mn);
   L = fmaf(l, be, L * al);
 #pragma unroll
   for (int k = 0; k < NA; ++k) A[k] = fmaf(a[k], be, A[k] * al);
@@ -132,7 +137,7 @@ __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, V
   const float msafe = mx == -INFINITY ? 0.f : mx;
   float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = (valid8 >> i) & 1 ? exp2f(sv[i] - msafe) : 0.f;
+  for (int i = 0; i < 8; ++i) p[i] = (valid8 >> i) & 1 ? exp2_hw(sv[i] - msafe) : 0.f;
   float ls = p[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) ls += p[i];
@@ -335,7 +340,8 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
   constexpr int NB = HD / 16, NS = HD / 32, HP = HD + 4;
   auto& red = sm.m.red;
   const int rep = D.nq / D.nkv;
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4,
+            n = lane & 15;
   const AttnItem it0 = items[first];   // the tiles share sequence, stage and explore chunks
   const int layer = layer_of(D, lattice, it0.stage, lam);
   // Every tile's rows and key limits up front: lane n's unit (lim) and fold
@@ -371,6 +377,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) vlim = max(vlim, lim[t]);
   for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
+  vlim = __builtin_amdgcn_readfirstlane(vlim);   // the same in every lane
   __syncthreads();
 
   // Span state of fold thread fu's unit per tile (elements 4 fs + 64 q + e).
@@ -408,8 +415,9 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
       vl[b] = *(const u32x4_t*)(vp + 32 * HD);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if (p0 + kKvTile > vlim)   // only a chunk that reaches past every limit needs the V mask
 #pragma unroll
-    for (int b = 0; b < NB; ++b) mask_v(vh[b], vl[b], vlim - (p0 + 8 * g));
+      for (int b = 0; b < NB; ++b) mask_v(vh[b], vl[b], vlim - (p0 + 8 * g));
   }
 
 #pragma unroll
