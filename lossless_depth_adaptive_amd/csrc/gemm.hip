@@ -408,7 +408,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 // bits, only the block count). Each k-step's
 // activations (64 rows x 32, fp32) are split once into bf16 (hi, lo) and
 // stored in LDS in MFMA operand order, shared by the four waves; global loads
-// run two k-steps ahead in registers. Each output is reduced exactly as in
+// run three k-steps ahead in registers. Each output is reduced exactly as in
 // gemm_kernel: the 8 k ranges [KS r/8, KS (r+1)/8) are accumulated from zero
 // by the same MFMA chain (hi then lo per k-step), in order, and summed in
 // range order, so a row gets the same bits from either kernel and from any
@@ -476,7 +476,8 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 #pragma unroll
     for (int nb = 0; nb < WT; ++nb) p.b[nb] = bsrc[nb][(size_t)ks * 64];
   };
-  // One k-step from the registers of p, which then take k-step ks + 2: the
+  // One k-step from the registers of p, which then take k-step ks + 3 (three
+  // register sets, so each load has two k-steps of MFMAs to land in): the
   // activation loads go out once p.a is staged, the weight loads once the
   // MFMAs have read p.b.
   auto step = [&](int ks, Pre& p, f32x4_t (&acc)[4][WT]) {
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
     }
     sm.s.f[buf][0][w][lane] = hv;
     sm.s.f[buf][1][w][lane] = lv;
-    load_a(ks + 2, p);
+    load_a(ks + 3, p);
     __syncthreads();
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
@@ -510,39 +511,57 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[mb][nb], 0, 0, 0);
       }
     }
-    load_b(ks + 2, p);
+    load_b(ks + 3, p);
   };
 
-  f32x4_t tot[4][WT];
+  // The k ranges in order: acc takes one range, tot the range sums (the first
+  // as it is, the next ones added in order); the loop walks every k-step of
+  // the block's ranges with the three register sets in turn.
+  f32x4_t tot[4][WT], acc[4][WT];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < WT; ++nb) acc[mb][nb] = tot[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int r0 = SPLIT ? z : 0, r1 = SPLIT ? z + 1 : kKSplit;
   int ks = (KS * r0) / kKSplit;
-  Pre p0, p1;
+  const int kend = (KS * r1) / kKSplit;
+  int r = r0, rend = (KS * (r0 + 1)) / kKSplit;
+  Pre p0, p1, p2;
   load_a(ks, p0);
   load_b(ks, p0);
   load_a(ks + 1, p1);
   load_b(ks + 1, p1);
-  for (int r = r0; r < r1; ++r) {
-    const int re = (KS * (r + 1)) / kKSplit;
-    f32x4_t acc[4][WT];
+  load_a(ks + 2, p2);
+  load_b(ks + 2, p2);
+  auto close = [&](int k) {
+    if (k + 1 == rend) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < WT; ++nb) acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (; ks + 2 <= re; ks += 2) {
-      step(ks, p0, acc);
-      step(ks + 1, p1, acc);
+        for (int nb = 0; nb < WT; ++nb) {
+          tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
+          acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+      ++r;
+      rend = (KS * (r + 1)) / kKSplit;
     }
-    if (ks < re) {   // odd range length: p1 holds the next k-step
-      step(ks, p0, acc);
-      ++ks;
-      const Pre t = p0;
-      p0 = p1;
-      p1 = t;
-    }
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < WT; ++nb) tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
+  };
+  for (; ks + 3 <= kend; ks += 3) {
+    step(ks, p0, acc);
+    close(ks);
+    step(ks + 1, p1, acc);
+    close(ks + 1);
+    step(ks + 2, p2, acc);
+    close(ks + 2);
+  }
+  if (ks < kend) {
+    step(ks, p0, acc);
+    close(ks);
+    ++ks;
+  }
+  if (ks < kend) {
+    step(ks, p1, acc);
+    close(ks);
   }
 
   if constexpr (SPLIT) {
