@@ -35,8 +35,8 @@ hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, f
 int attn_chunk(int hd);
 int attn_mix_slots();
 hipError_t launch_attention(const AttnItem*, int, const int*, int, int, const RowInfo*, int, const float*, const bf16_t*,
-                            const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, bool,
-                            hipStream_t);
+                            const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, int,
+                            bool, hipStream_t);
 template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
                         const void*, float*, float*, float*, const float*, int, int, int, hipStream_t);
@@ -237,6 +237,7 @@ struct dex_ctx {
   hipStream_t cap_st = nullptr;   // private stream that round graphs are captured on
   bool prof = false;
   int attn_umax = 1;              // most units in one attention item of the current round
+  int attn_nj = 0;                // most chunks holding explore keys in one item of the round (0 to 2)
   int attn_single = 0;            // attention items of the current pass that form a group of their own
   int attn_groups = 0;            // attention items of the current pass that lead a group of several
   std::vector<Mark> marks;
@@ -597,7 +598,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     HIPCHK(launch_attention(ctx->items, nitems, ctx->item_list, ctx->attn_single, ctx->attn_groups, ctx->rows, nrows,
                             ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail, ctx->attn_part, (float*)ctx->attn_out, D, lam,
                             lattice, ctx->wp.nchunk, max_keys, lattice != 0 ? ctx->attn_umax : 0,
-                            (ctx->opt.debug & 4) != 0, st));
+                            lattice != 0 ? ctx->attn_nj : 0, (ctx->opt.debug & 4) != 0, st));
     prof_end(ctx, mk, 2, attn_bytes, attn_flops);
     groups_for(lam, ctx->wp.wo, 1, false);
     ga.K = nq * hd;
@@ -717,6 +718,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   const int per_item = std::max(1, kAttnUnits / rep);
   int nitems = 0, max_keys = 0;
   ctx->attn_umax = 1;
+  ctx->attn_nj = 0;
   for (int j = 0; j < N; ++j)
     for (int s = 0; s < B; ++s) {
       const int cnt = rows_seq_stage[(size_t)s * N + j];
@@ -731,6 +733,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
         // lattice rows: explore keys at [C, mk), at most two chunks
         it.xc0 = ar ? -1 : ctx->C_[s] / kKvTile;
         it.xc1 = ar ? -1 : (mk - 1) / kKvTile;
+        if (!ar) ctx->attn_nj = std::max(ctx->attn_nj, it.xc1 - it.xc0 + 1);
         it.lead = attn_lead(o / per_item, (cnt + per_item - 1) / per_item);
         max_keys = std::max(max_keys, mk);
         ctx->attn_umax = std::max(ctx->attn_umax, it.nrows * rep);
@@ -829,6 +832,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     key += ar ? 'A' : 'D';
     key += std::to_string((max_keys + attn_chunk(ctx->D.hd) - 1) / attn_chunk(ctx->D.hd));
     key += ':';
+    key += (char)('0' + ctx->attn_nj);   // per-row chunk slots of the attention launch
     for (int s = 0; s < B; ++s) {
       key += (char)('a' + (live[s] ? ctx->h_plans[s].q : 31));
       key += ctx->h_plans[s].commit ? 'c' : '.';
