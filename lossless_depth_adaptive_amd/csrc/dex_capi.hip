@@ -34,7 +34,8 @@ template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
 int attn_mix_slots();
-hipError_t launch_attention(const AttnItem*, int, const int*, int, int, const RowInfo*, int, const float*, const bf16_t*,
+hipError_t launch_attention(const AttnItem*, int, const int*, int, int, int, const RowInfo*, int, const float*,
+                            const bf16_t*,
                             const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, int,
                             bool, hipStream_t);
 template <typename T>
@@ -176,7 +177,7 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
   w.rows = lay.take(R * sizeof(RowInfo));
   w.plans = lay.take(B * sizeof(SeqPlan));
-  w.items = lay.take(R * (sizeof(AttnItem) + 4));   // items, then the attention block list (R ints)
+  w.items = lay.take(R * (sizeof(AttnItem) + 12));   // items, then the attention block lists (3 R ints)
   w.q = lay.take(R * nq * hd * 4);
   w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
   w.attn_out = lay.take(R * nq * hd * 4);
@@ -240,6 +241,7 @@ struct dex_ctx {
   int attn_nj = 0;                // most chunks holding explore keys in one item of the round (0 to 2)
   int attn_single = 0;            // attention items of the current pass that form a group of their own
   int attn_groups = 0;            // attention items of the current pass that lead a group of several
+  int attn_tails = 0;             // (item, 4-row quarter) entries of the per-row attention chunks
   std::vector<Mark> marks;
   size_t nmarks = 0;
   // HIP graphs of whole rounds, keyed by the round's plan
@@ -267,18 +269,24 @@ namespace {
 // inside a group).
 int attn_lead(int i, int n) { return i % kAttnGroup ? 0 : std::min(kAttnGroup, n - i); }
 
-// Attention block list of the pass's first nitems items: the items that form a
-// group of their own (the shared-role blocks of attn_kernel), then the items
-// that lead a group of several (attn_group_kernel), so that neither launch
-// has blocks for items covered by another.
+// Attention block lists of the pass's first nitems items: the items that form
+// a group of their own (the shared-role blocks of attn_kernel), then the items
+// that lead a group of several (attn_group_kernel), then, for items whose rows
+// read explore keys, one entry 4 item + q per quarter q of the item's rows
+// (the per-row chunk blocks of attn_kernel, kAttnSC rows each), so that no
+// launch has blocks without work.
 void attn_block_list(dex_ctx* ctx, int nitems) {
-  int n1 = 0, ng = 0;
+  int n1 = 0, ng = 0, nt = 0;
   for (int i = 0; i < nitems; ++i)
     if (ctx->h_items[i].lead == 1) ctx->h_item_list[n1++] = i;
   for (int i = 0; i < nitems; ++i)
     if (ctx->h_items[i].lead > 1) ctx->h_item_list[n1 + ng++] = i;
+  for (int i = 0; i < nitems; ++i)
+    if (ctx->h_items[i].xc0 >= 0)
+      for (int qt = 0; qt * kAttnSC < ctx->h_items[i].nrows; ++qt) ctx->h_item_list[n1 + ng + nt++] = 4 * i + qt;
   ctx->attn_single = n1;
   ctx->attn_groups = ng;
+  ctx->attn_tails = nt;
 }
 
 // Node cap of the lattice (node_held): 1 for the single-exit ablation, the
@@ -595,7 +603,8 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
         attn_flops += attn_stage_flops[j];
       }
     int mk = prof_begin(ctx, DEX_PROF_ATTN);
-    HIPCHK(launch_attention(ctx->items, nitems, ctx->item_list, ctx->attn_single, ctx->attn_groups, ctx->rows, nrows,
+    HIPCHK(launch_attention(ctx->items, nitems, ctx->item_list, ctx->attn_single, ctx->attn_groups,
+                            lattice != 0 ? ctx->attn_tails : 0, ctx->rows, nrows,
                             ctx->q, ctx->kvc, ctx->exb, ctx->attn_tail, ctx->attn_part, (float*)ctx->attn_out, D, lam,
                             lattice, ctx->wp.nchunk, max_keys, lattice != 0 ? ctx->attn_umax : 0,
                             lattice != 0 ? ctx->attn_nj : 0, (ctx->opt.debug & 4) != 0, st));
@@ -771,9 +780,8 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     int mk = prof_begin(ctx, DEX_PROF_LATTICE);
     HIPCHK(hipMemcpyAsync(ctx->plans, ctx->h_plans, B * sizeof(SeqPlan), hipMemcpyHostToDevice, st));
     HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
-    if (ctx->attn_single + ctx->attn_groups)
-      HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list, (ctx->attn_single + ctx->attn_groups) * sizeof(int),
-                            hipMemcpyHostToDevice, st));
+    const int nlist = ctx->attn_single + ctx->attn_groups + ctx->attn_tails;
+    if (nlist) HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list, nlist * sizeof(int), hipMemcpyHostToDevice, st));
     if (ar) {
       HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
       HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
@@ -948,7 +956,8 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
       HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
       attn_block_list(ctx, nitems);
       HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
-      HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list, (ctx->attn_single + ctx->attn_groups) * sizeof(int),
+      HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list,
+                            (ctx->attn_single + ctx->attn_groups + ctx->attn_tails) * sizeof(int),
                             hipMemcpyHostToDevice, st));
       HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
       std::vector<std::pair<int, int>> stage_rows = {{0, R}};
@@ -1090,7 +1099,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   if (hipStreamCreateWithFlags(&ctx->cap_st, hipStreamNonBlocking) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_plans, sizeof(SeqPlan) * D.B) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_records, 5 * 4 * D.B) != hipSuccess ||
-      hipHostMalloc((void**)&ctx->h_items, (sizeof(AttnItem) + 4) * wp.Rmax) != hipSuccess ||
+      hipHostMalloc((void**)&ctx->h_items, (sizeof(AttnItem) + 12) * wp.Rmax) != hipSuccess ||
       hipHostMalloc((void**)&ctx->h_rows, sizeof(RowInfo) * wp.Rmax) != hipSuccess) {
     ctx->err = "stream creation or hipHostMalloc failed";
     return fail(DEX_EHIP);

@@ -537,8 +537,9 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 }
 
 // One launch, block = kAttnSC waves. Blocks [0, ntail): per-row chunks,
-// index = ((item * nkv + h) * nj + j) * nquad + quad -> chunk xc0 + j, row
-// kAttnSC * quad + wave (nj: the most chunks with explore keys in one item). Blocks from ntail: index = (k * nkv + h) * nsc + sc,
+// index = (e * nkv + h) * nj + j for tail entry tlist[e] = 4 item + quad ->
+// chunk xc0 + j, row kAttnSC * quad + wave (nj: the most chunks with explore
+// keys in one item). Blocks from ntail: index = (k * nkv + h) * nsc + sc,
 // shared role for item list[k], the k-th of the items that form a group of
 // their own.
 template <int HD>
@@ -546,18 +547,17 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
     const float* __restrict__ q, const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
     float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail,
-    int nquad, int nj, int nsc) {
+    const int* __restrict__ tlist, int nj, int nsc) {
   __shared__ AttnSmem<HD, 1> sm;
   int b = blockIdx.x;
   if (b < ntail) {
-    const int quad = b % nquad;
-    b /= nquad;
     const int j = b % nj;
     b /= nj;
-    const AttnItem it = items[b / D.nkv];
+    const int e = tlist[b / D.nkv];
+    const AttnItem it = items[e >> 2];
     if (it.xc0 < 0 || (lattice && lam >= stage_len(D, it.stage))) return;
-    attn_unit_chunk<HD>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * quad + (threadIdx.x >> 6), rows, q, kvc, exb, mix, D,
-                        lam, lattice);
+    attn_unit_chunk<HD>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * (e & 3) + (threadIdx.x >> 6), rows, q, kvc, exb, mix,
+                        D, lam, lattice);
     return;
   }
   b -= ntail;
@@ -699,11 +699,13 @@ int attn_chunk(int) { return kAttnSCKeys; }
 int attn_mix_slots() { return kMixSlots; }
 
 // list: the nsingle items that form a group of their own, then the ngroups
-// items that lead a group of several. umax: most units of an item whose rows
+// items that lead a group of several, then ntails entries 4 item + quad of
+// the 4-row quarters of items whose rows read explore keys (0 when none do).
+// umax: most units of an item whose rows
 // read explore-buffer keys (lattice rows), 0 when no row does; nj: the most
 // chunks holding explore keys in one item (xc1 - xc0 + 1, at most 2). span:
 // grouped blocks run whole spans whatever their count.
-hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups,
+hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups, int ntails,
                             const RowInfo* rows, int nrows, const float* q, const bf16_t* kvc, const bf16_t* exb,
                             float* mix, float* part, float* out, const ModelDims& D, int lam, int lattice, int nsc_max,
                             int max_keys, int umax, int nj, bool span, hipStream_t st) {
@@ -711,20 +713,18 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, 
   if (nitems == 0) return hipSuccess;
   const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
   if (nsc > nsc_max || umax > kAttnUnits || nsingle < 0 || ngroups < 0 || nsingle + ngroups > nitems || nj < 0 ||
-      nj > 2 || (umax > 0 && nj == 0))
+      nj > 2 || ntails < 0 || ntails > 4 * nitems || (ntails > 0 && nj == 0))
     return hipErrorInvalidValue;
-  const int rep = D.nq / D.nkv, rmax = (umax + rep - 1) / rep;   // most rows of an item
-  const int nquad = (rmax + kAttnSC - 1) / kAttnSC;
-  const int ntail = nitems * D.nkv * nj * nquad;
+  const int ntail = ntails * D.nkv * nj;
   const dim3 grid(ntail + nsingle * D.nkv * nsc);
   hipError_t e = hipSuccess;
   if (grid.x > 0) {
     if (D.hd == 128)
       hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
-                         part, D, lam, lattice, nsc_max, ntail, nquad, nj, nsc);
+                         part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nsc);
     else
       hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
-                         part, D, lam, lattice, nsc_max, ntail, nquad, nj, nsc);
+                         part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nsc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
