@@ -74,6 +74,7 @@ CASES = {
     "qwen_gqa_x9_b4_narrow_span": (get_workload("qwen8b_x9_b16").scaled(
         d_model=512, n_heads=4, n_kv_heads=2, d_ffn=1536, vocab=4096, batch=4, prompt_len=40),
         dict(T=16, span=True)),
+    "tiny_N8_span": (tiny.scaled(tied=False, gamma=0.8, X=tuple(range(1, 9))), dict(T=32, span=True)),
     "qwen_gqa_long": (qwen_long, dict(T=32)),
     "qwen_gqa_long_span": (qwen_long, dict(T=32, span=True)),
 }
