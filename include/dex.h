@@ -117,8 +117,9 @@ typedef struct {
   int32_t gumbel_rows;
   int32_t debug;           /* bit 0: keep the final-depth logits of each sequence's last commit;
                               bit 1: launch every round eagerly (no HIP-graph replay). By default a
-                              round whose plan (FSM states, commit flags, attention chunk count) was
-                              seen before is captured once into a HIP graph and replayed;
+                              round whose plan (FSM states, commit flags, attention chunk count,
+                              explore-chunk slots) was seen before is captured once into a HIP graph
+                              and replayed;
                               bit 2: grouped attention blocks always run whole spans of key
                               positions (by default a launch does so only when that still fills
                               the GPU). The results are the same bits either way; the bit lets

@@ -773,8 +773,9 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   hipStream_t st = ctx->st;
   // Everything the round enqueues; run eagerly, or captured into a HIP graph
   // and replayed when the same plan (FSM states, commit flags, attention chunk
-  // count, profiling) comes back. Plans and items are re-read from the pinned
-  // host buffers at every replay.
+  // count, explore-chunk slots, profiling) comes back. Plans, items and the
+  // attention block lists are re-read from the pinned host buffers at every
+  // replay.
   auto enqueue = [&]() -> int {
     hipStream_t st = ctx->st;
     int mk = prof_begin(ctx, DEX_PROF_LATTICE);
