@@ -112,7 +112,8 @@ typedef struct {
   /* Sampling only: device float32 Gumbel(0,1) rows [max_batch][gumbel_rows][vocab];
    * row (b, j) is the noise for target position prompt_len_b + j, shared by
    * every node predicting that position (one row per slot, shared across
-   * depths: Appendix C.1). Needs gumbel_rows >= max_new_tokens + N - 1. */
+   * depths: Appendix C.1). Needs gumbel_rows >= max_new_tokens + N - 1 and a
+   * 16-byte aligned pointer (the exit head reads the rows four floats at a time). */
   const float* gumbel;
   int32_t gumbel_rows;
   int32_t debug;           /* bit 0: keep the final-depth logits of each sequence's last commit;

@@ -12,6 +12,7 @@
 // records (at most one per sequence).
 #include <algorithm>
 #include <array>
+#include <cstdint>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -115,6 +116,7 @@ int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex
   if (o->mode == DEX_SAMPLE) {
     if (!(o->temperature > 0)) { err = "temperature must be positive"; return DEX_EINVAL; }
     if (!o->gumbel) { err = "sampling needs Gumbel rows"; return DEX_EINVAL; }
+    if (((uintptr_t)o->gumbel & 15) != 0) { err = "gumbel must be 16-byte aligned"; return DEX_EINVAL; }
     if (o->gumbel_rows < o->max_new_tokens + n_x - 1) { err = "gumbel_rows must be >= max_new_tokens + N - 1"; return DEX_EINVAL; }
   }
   return DEX_OK;

@@ -420,6 +420,79 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args)
 // ---------------------------------------------------------------------------
 constexpr int kWideThreads = 256;
 
+// Exit-head epilogue of a wide block: t holds the block's BT tiles for its 64
+// rows (before rstd). Lane l of each of the NW waves takes row l, and wave w
+// the tiles w, w + NW, ...: the row's data is read once, and each tile's 16
+// columns are scanned in column order exactly as in epilogue_tile (same mask,
+// noise and top-2 arithmetic, so the summaries carry the same bits). With a
+// row per lane and a row pitch of 4 banks, the 16-byte LDS reads of a wave
+// fall on distinct banks.
+template <int BT, int NW>
+__device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0,
+                                                   const float (*t)[BT * 16 + 4], const float* rs) {
+  const int ntiles = args.N >> 4;
+  const int rl = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (rl >= G.m) return;
+  const RowInfo& ri = args.rows[G.row0 + rl];
+  const bool fin = ri.final_ != 0;
+  const float rsl = rs[rl];
+  float* outp = args.out != nullptr && fin ? args.out + (size_t)ri.seq * args.N : nullptr;
+  const float* gum = args.mode == 1 ? args.gumbel + ((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N : nullptr;
+  // Whether a masked token falls in the block's columns at all (a row masks at
+  // most N - 1 tokens, so nearly every block has none).
+  const int nm = fin ? 0 : ri.n_mask;
+  bool hit = false;
+  for (int i = 0; i < nm; ++i) hit |= ri.mask[i] >= tb0 * 16 && ri.mask[i] < (tb0 + BT) * 16;
+  float* part = args.part + ((size_t)(G.row0 + rl) * ntiles) * 3;
+  for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
+    const int n0 = (tb0 + tl) * 16;
+    float s[16];
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+      const float4 v = *(const float4*)&t[rl][tl * 16 + c];
+      s[c] = v.x * rsl;
+      s[c + 1] = v.y * rsl;
+      s[c + 2] = v.z * rsl;
+      s[c + 3] = v.w * rsl;
+    }
+    if (outp != nullptr) {
+#pragma unroll
+      for (int c = 0; c < 16; c += 4) *(float4*)(outp + n0 + c) = float4{s[c], s[c + 1], s[c + 2], s[c + 3]};
+    }
+    if (hit) {
+      for (int i = 0; i < nm; ++i) {
+        const int m = ri.mask[i] - n0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (m == c) s[c] = -INFINITY;
+      }
+    }
+    if (gum != nullptr) {
+#pragma unroll
+      for (int c = 0; c < 16; c += 4) {
+        const float4 g = *(const float4*)(gum + n0 + c);
+        s[c] = s[c] / args.tau + g.x;
+        s[c + 1] = s[c + 1] / args.tau + g.y;
+        s[c + 2] = s[c + 2] / args.tau + g.z;
+        s[c + 3] = s[c + 3] / args.tau + g.w;
+      }
+    }
+    float best = s[0], second = -INFINITY;
+    int bi = 0;
+#pragma unroll
+    for (int c = 1; c < 16; ++c) {
+      const bool gt = s[c] > best;
+      second = gt ? best : (s[c] > second ? s[c] : second);
+      bi = gt ? c : bi;
+      best = gt ? s[c] : best;
+    }
+    float* p = part + (size_t)(tb0 + tl) * 3;
+    p[0] = best;
+    p[1] = __int_as_float(n0 + bi);
+    p[2] = second;
+  }
+}
+
 template <int EPI, bool SPLIT, int WT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
   constexpr int BT = 4 * WT;   // 16-column tiles per block
@@ -445,7 +518,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   struct Out { float t[SPLIT ? 1 : 64][BT * 16 + 4]; };   // the split form stores from registers
   __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[64];
-  __shared__ float scr[SPLIT ? 1 : 64][17];
+  __shared__ float scr[SPLIT || EPI == EPI_HEAD ? 1 : 64][17];
 
   // Thread (w, lane) converts the fragment that lane `lane` of row block w
   // reads. Rows past the group's end repeat its first row and tiles past N the
@@ -595,10 +668,14 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
 #pragma unroll
       for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * WT + nb) * 16 + col16] = tot[mb][nb][r];
   __syncthreads();
-  for (int tl = 0; tl < BT && tb0 + tl < ntiles; ++tl) {
-    epilogue_tile<EPI, kWideThreads, 64>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
-                                         rs_sh, scr);
-    __syncthreads();
+  if constexpr (EPI == EPI_HEAD) {
+    head_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
+  } else {
+    for (int tl = 0; tl < BT && tb0 + tl < ntiles; ++tl) {
+      epilogue_tile<EPI, kWideThreads, 64>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
+                                           rs_sh, scr);
+      __syncthreads();
+    }
   }
 }
 

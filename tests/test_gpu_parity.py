@@ -67,6 +67,10 @@ CASES = {
     "tiny_N10": (tiny.scaled(tied=False, gamma=0.8, n_layers=10, X=tuple(range(1, 11))), dict(T=16)),
     "tiny_ragged_b4": (tiny.scaled(mode="sample", seed_g=3001, batch=4), dict(T=24, lens=[1, 31, 33, 64])),
     "tiny_b64": (tiny.scaled(batch=64), dict(T=6)),
+    # sixteen sampled sequences: the exit-head groups hold 8 rows or more, so the
+    # bf16 exit head runs on the wide GEMM with depth-coupled masks and noise
+    "llama13b_x8_b16_sample_narrow": (get_workload("llama13b_x8_b8").scaled(
+        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4096, batch=16, prompt_len=48), dict(T=12)),
     # grouped attention forced to run whole spans (span=True; by default only launches
     # that fill the GPU do), and contexts that cross the first span boundary (2048 keys)
     # while decoding, so that a row folds two spans and the explore keys sit first in
