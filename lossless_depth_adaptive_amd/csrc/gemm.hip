@@ -493,6 +493,61 @@ __device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const G
   }
 }
 
+// Residual epilogue of a wide block, in the same lane layout: lane l of wave w
+// adds row l's outputs of tiles w, w + NW, ... into the residual stream. The
+// residual reads of all of the lane's tiles go out before the first is used
+// (one memory latency per block instead of one per tile). Per element and per
+// tile sum of squares the arithmetic is epilogue_tile's, so the bits are too.
+template <int BT, int NW>
+__device__ __forceinline__ void resid_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0,
+                                                    const float (*t)[BT * 16 + 4]) {
+  constexpr int TPW = BT / NW;   // tiles per wave
+  const int ntiles = args.N >> 4;
+  const int rl = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (rl >= G.m) return;
+  const size_t rbase = (size_t)args.rows[G.row0 + rl].hrow * args.N;
+  float4 h[TPW][4];
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tile = tb0 + w + j * NW;
+    if (tile < ntiles) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) h[j][q] = *(const float4*)(args.hidden + rbase + tile * 16 + 4 * q);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < TPW; ++j) {
+    const int tl = w + j * NW, tile = tb0 + tl;
+    if (tile >= ntiles) break;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 y = *(const float4*)&t[rl][tl * 16 + 4 * q];
+      v[4 * q] = h[j][q].x + y.x;
+      v[4 * q + 1] = h[j][q].y + y.y;
+      v[4 * q + 2] = h[j][q].z + y.z;
+      v[4 * q + 3] = h[j][q].w + y.w;
+    }
+    const size_t o = rbase + tile * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *(float4*)(args.hidden + o + 4 * q) = float4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    auto scaled = [&](float* dst, const float* g) {
+      float u[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) u[c] = v[c] * g[tile * 16 + c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) *(float4*)(dst + o + 4 * q) = float4{u[4 * q], u[4 * q + 1], u[4 * q + 2], u[4 * q + 3]};
+    };
+    if (G.gamma) scaled(args.xn, G.gamma);
+    if (G.xh) scaled(args.xh, args.gfinal);
+    if (G.anorm) scaled(args.xa, G.anorm);
+    const float s = ssq16(v);
+    const size_t so = (size_t)args.rows[G.row0 + rl].hrow * ntiles + tile;
+    args.ssq[so] = s;
+    if (G.xh) args.ssq_head[so] = s;
+  }
+}
+
 template <int EPI, bool SPLIT, int WT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
   constexpr int BT = 4 * WT;   // 16-column tiles per block
@@ -518,7 +573,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   struct Out { float t[SPLIT ? 1 : 64][BT * 16 + 4]; };   // the split form stores from registers
   __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[64];
-  __shared__ float scr[SPLIT || EPI == EPI_HEAD ? 1 : 64][17];
+  __shared__ float scr[SPLIT || EPI != EPI_ADAPT2 ? 1 : 64][17];
 
   // Thread (w, lane) converts the fragment that lane `lane` of row block w
   // reads. Rows past the group's end repeat its first row and tiles past N the
@@ -670,11 +725,14 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   __syncthreads();
   if constexpr (EPI == EPI_HEAD) {
     head_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
+  } else if constexpr (EPI == EPI_RESID) {
+    resid_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t);
   } else {
+    // Only the adapter's second layer uses scr, so only it waits between tiles.
     for (int tl = 0; tl < BT && tb0 + tl < ntiles; ++tl) {
       epilogue_tile<EPI, kWideThreads, 64>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
                                            rs_sh, scr);
-      __syncthreads();
+      if constexpr (EPI == EPI_ADAPT2) __syncthreads();
     }
   }
 }
