@@ -123,6 +123,15 @@ __global__ void pack_kernel(u32x4_t* __restrict__ dst, const T* __restrict__ s0,
   }
 }
 
+// Rotary rotation of the pair (x1, x2) by the angle of cosine cs and sine sn,
+// with its roundings spelled out (a product, then a fused multiply-add), so
+// that every epilogue form gives the same bits whatever the compiler would
+// contract.
+__device__ __forceinline__ void rope_pair(float x1, float x2, float cs, float sn, float& o1, float& o2) {
+  o1 = fmaf(x1, cs, -(x2 * sn));
+  o2 = fmaf(x2, cs, x1 * sn);
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue of one 16-column output tile for rows [0, G.m) of group G. val(rl, c)
 // is the GEMM output of row rl, tile column c (before rstd); rs[rl] the row's
@@ -225,7 +234,8 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGr
       }
       const int i = 8 * u + c;
       const float cs = args.cosT[(size_t)R.pos * (hd >> 1) + i], sn = args.sinT[(size_t)R.pos * (hd >> 1) + i];
-      const float o1 = x1 * cs - x2 * sn, o2 = x2 * cs + x1 * sn;
+      float o1, o2;
+      rope_pair(x1, x2, cs, sn, o1, o2);
       if (head < D.nq) {
         float* qd = args.qout + ((size_t)row * D.nq + head) * hd;
         qd[i] = o1 * args.qscale;
@@ -498,6 +508,94 @@ __device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const G
 // residual reads of all of the lane's tiles go out before the first is used
 // (one memory latency per block instead of one per tile). Per element and per
 // tile sum of squares the arithmetic is epilogue_tile's, so the bits are too.
+// Query/key/value epilogue of a wide block, in the same lane layout: lane l of
+// wave w takes row l's tiles w, w + NW, ... (a tile lies in one head), with
+// the row's data read once. Per element the arithmetic is epilogue_tile's;
+// key and explore-buffer runs of 8 or 16 dims go out as 16-byte stores.
+template <int BT, int NW>
+__device__ __forceinline__ void qkv_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0,
+                                                  const float (*t)[BT * 16 + 4], const float* rs) {
+  const ModelDims& D = args.dims;
+  const int hd = D.hd, tph = hd >> 4, half = hd >> 1;
+  const int ntiles = args.N >> 4;
+  const int rl = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (rl >= G.m) return;
+  const int row = G.row0 + rl;
+  const RowInfo& R = args.rows[row];
+  const int seq = R.seq, phys = R.phys, pos = R.pos;
+  const bool commit = R.kv_commit != 0;
+  const int layer = layer_of(D, args.lattice, R.stage, args.lam);
+  const float rsl = rs[rl];
+  const float* cosr = args.cosT + (size_t)pos * half;
+  const float* sinr = args.sinT + (size_t)pos * half;
+  // 8 consecutive values as (hi, lo) bf16 runs at hp and lp (16-byte aligned).
+  auto put8 = [](bf16_t* hp, bf16_t* lp, const float* v) {
+    u32x4_t h, l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      unsigned hk, lk;
+      split_bf2(v[2 * k], v[2 * k + 1], hk, lk);
+      h[k] = hk;
+      l[k] = lk;
+    }
+    *(u32x4_t*)hp = h;
+    *(u32x4_t*)lp = l;
+  };
+  for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
+    const int tile = tb0 + tl;
+    const int head = tile / tph, u = tile - head * tph;
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 v = *(const float4*)&t[rl][tl * 16 + 4 * q];
+      x[4 * q] = v.x * rsl;
+      x[4 * q + 1] = v.y * rsl;
+      x[4 * q + 2] = v.z * rsl;
+      x[4 * q + 3] = v.w * rsl;
+    }
+    if (head >= D.nq + D.nkv) {   // values: dims 16u .. 16u + 15 in column order
+      const int hh = head - D.nq - D.nkv;
+      if (commit) {
+        bf16_t* base = args.kvc + kv_head_base(D, seq, layer, hh);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          bf16_t hi, lo;
+          split_bf(x[c], hi, lo);
+          base[kv_elem(hd, pos, 1, 0, 16 * u + c)] = hi;
+          base[kv_elem(hd, pos, 1, 1, 16 * u + c)] = lo;
+        }
+      } else {
+        bf16_t* base = args.exb + ex_base(D, seq, phys, args.lam, hh) + 2 * (size_t)hd + 16 * u;
+        put8(base, base + hd, x);
+        put8(base + 8, base + hd + 8, x + 8);
+      }
+      continue;
+    }
+    float o1[8], o2[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) rope_pair(x[c], x[c + 8], cosr[8 * u + c], sinr[8 * u + c], o1[c], o2[c]);
+    if (head < D.nq) {
+      float* qd = args.qout + ((size_t)row * D.nq + head) * hd + 8 * u;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        qd[c] = o1[c] * args.qscale;
+        qd[c + half] = o2[c] * args.qscale;
+      }
+    } else {
+      const int hh = head - D.nq;
+      if (commit) {
+        bf16_t* base = args.kvc + kv_head_base(D, seq, layer, hh);
+        put8(base + kv_elem(hd, pos, 0, 0, 8 * u), base + kv_elem(hd, pos, 0, 1, 8 * u), o1);
+        put8(base + kv_elem(hd, pos, 0, 0, 8 * u + half), base + kv_elem(hd, pos, 0, 1, 8 * u + half), o2);
+      } else {
+        bf16_t* base = args.exb + ex_base(D, seq, phys, args.lam, hh) + 8 * u;
+        put8(base, base + hd, o1);
+        put8(base + half, base + hd + half, o2);
+      }
+    }
+  }
+}
+
 template <int BT, int NW>
 __device__ __forceinline__ void resid_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0,
                                                     const float (*t)[BT * 16 + 4]) {
@@ -727,6 +825,8 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
     head_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
   } else if constexpr (EPI == EPI_RESID) {
     resid_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t);
+  } else if constexpr (EPI == EPI_QKV) {
+    qkv_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
   } else {
     // Only the adapter's second layer uses scr, so only it waits between tiles.
     for (int tl = 0; tl < BT && tb0 + tl < ntiles; ++tl) {
