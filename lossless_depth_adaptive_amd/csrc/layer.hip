@@ -536,12 +536,12 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
   }
 }
 
-// One launch, block = kAttnSC waves. Blocks [0, ntail): per-row chunks,
-// index = (e * nkv + h) * nj + j for tail entry tlist[e] = 4 item + quad ->
-// chunk xc0 + j, row kAttnSC * quad + wave (nj: the most chunks with explore
-// keys in one item). Blocks from ntail: index = (k * nkv + h) * nsc + sc,
-// shared role for item list[k], the k-th of the items that form a group of
-// their own.
+// One launch, block = kAttnSC waves. Logical blocks [0, ntail): per-row
+// chunks, index = (e * nkv + h) * nj + j for tail entry tlist[e] = 4 item +
+// quad -> chunk xc0 + j, row kAttnSC * quad + wave (nj: the most chunks with
+// explore keys in one item). Logical blocks from ntail: index = (k * nkv + h)
+// * nsc + sc, shared role for item list[k], the k-th of the items that form a
+// group of their own.
 template <int HD>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
@@ -549,7 +549,14 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail,
     const int* __restrict__ tlist, int nj, int nsc) {
   __shared__ AttnSmem<HD, 1> sm;
-  int b = blockIdx.x;
+  // Hardware block x -> logical index b: the per-row blocks are spread evenly
+  // among the shared ones (x takes per-row block floor(x ntail / grid) when
+  // that count steps at x), so that latency-bound and streaming blocks share
+  // the CUs for the whole launch instead of running one after the other.
+  const int total = gridDim.x;
+  const int t0 = (int)((long long)blockIdx.x * ntail / total);
+  const int t1 = (int)((long long)(blockIdx.x + 1) * ntail / total);
+  int b = t1 > t0 ? t0 : ntail + (blockIdx.x - t0);
   if (b < ntail) {
     const int j = b % nj;
     b /= nj;
