@@ -174,6 +174,7 @@ constexpr int kMixSlots = 2 * kAttnSC;   // chunk slots of the (at most two) mix
 // within each span of kAttnSpan, and the span states left to right.
 constexpr int kAttnSpan = 16;
 constexpr int kSpanBlocks = 512;   // grouped blocks that fill the chip (two per CU)
+constexpr int kSpreadBlocks = 4096;   // attn_kernel launches that spread their per-row blocks
 
 // Whether super-chunk sc of the item holds a per-row (explore) chunk.
 __device__ __forceinline__ bool sc_mixed(const AttnItem& it, int sc) {
@@ -549,14 +550,16 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail,
     const int* __restrict__ tlist, int nj, int nsc) {
   __shared__ AttnSmem<HD, 1> sm;
-  // Hardware block x -> logical index b: the per-row blocks are spread evenly
-  // among the shared ones (x takes per-row block floor(x ntail / grid) when
-  // that count steps at x), so that latency-bound and streaming blocks share
-  // the CUs for the whole launch instead of running one after the other.
+  // Hardware block x -> logical index b. In a launch of kSpreadBlocks blocks
+  // or more the per-row blocks are spread evenly among the shared ones (x
+  // takes per-row block floor(x ntail / grid) when that count steps at x), so
+  // that latency-bound and streaming blocks share the CUs for the whole
+  // launch; a smaller launch, a few blocks per CU, keeps the per-row blocks
+  // first, so its longest blocks start first.
   const int total = gridDim.x;
   const int t0 = (int)((long long)blockIdx.x * ntail / total);
   const int t1 = (int)((long long)(blockIdx.x + 1) * ntail / total);
-  int b = t1 > t0 ? t0 : ntail + (blockIdx.x - t0);
+  int b = total < kSpreadBlocks ? (int)blockIdx.x : (t1 > t0 ? t0 : ntail + (blockIdx.x - t0));
   if (b < ntail) {
     const int j = b % nj;
     b /= nj;
