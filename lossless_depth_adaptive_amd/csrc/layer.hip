@@ -662,7 +662,25 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
           join(pc[HD], pc[HD + 1], a);
         }
       } else {
-        for (int sc = lo; sc < hi && !sc_mixed(it, sc); ++sc) {
+        // The super-chunk states up to the first mixed one, read four at a
+        // time ahead of their (in-order) folds.
+        int end = lo;
+        while (end < hi && !sc_mixed(it, end)) ++end;
+        int sc = lo;
+        for (; sc + 4 <= end; sc += 4) {
+          float a4[4][HS], m4[4], l4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float* pc = base + (sc + j) * HP;
+#pragma unroll
+            for (int e = 0; e < HS; ++e) a4[j][e] = pc[lane * HS + e];
+            m4[j] = pc[HD];
+            l4[j] = pc[HD + 1];
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) join(m4[j], l4[j], a4[j]);
+        }
+        for (; sc < end; ++sc) {
           const float* pc = base + sc * HP;
           float a[HS];
 #pragma unroll
