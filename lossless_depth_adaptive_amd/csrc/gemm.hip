@@ -294,8 +294,11 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGr
 #ifndef DEX_GEMM_U
 #define DEX_GEMM_U 4
 #endif
+// Blocks of one row block (the decode-bound shape) are held to 64 VGPRs, so a
+// CU keeps four blocks (32 waves) and their loads in flight instead of three.
 template <typename T, int MB, int NB, int EPI>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(const GemmArgs args) {
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 8 : 1))) void gemm_kernel(
+    const GemmArgs args) {
   constexpr int KSTEP = Mfma<T>::KSTEP;
   constexpr int EPL = Mfma<T>::EPL;
   constexpr int AW = EPL / 4;          // 16-byte A loads per lane per k-step (fp32 activations)
