@@ -85,6 +85,25 @@ def test_invalid_shapes_and_options(kw, opt):
     assert e.value.code == D.DEX_EINVAL
 
 
+def test_gumbel_rows_alignment():
+    """The exit head reads Gumbel rows four floats at a time: a pointer that is
+    not 16-byte aligned is refused before any GPU work, an aligned one is
+    accepted (only the pointer is checked here; nothing reads the rows)."""
+    import torch
+    cfg = _cfg()
+    rows = 64 + 4
+    buf = torch.zeros(1 * rows * cfg.vocab + 4, dtype=torch.float32)
+    ok = buf[: rows * cfg.vocab].view(1, rows, cfg.vocab)
+    bad = buf[1: 1 + rows * cfg.vocab].view(1, rows, cfg.vocab)
+    assert ok.data_ptr() % 16 == 0 and bad.data_ptr() % 16 == 4
+    opt = dict(mode="sample", max_batch=1, max_new_tokens=64)
+    assert D.workspace_bytes(cfg, [2, 4, 6, 8], D.options(gumbel=ok, **opt)) > 0
+    with pytest.raises(D.DexError) as e:
+        D.workspace_bytes(cfg, [2, 4, 6, 8], D.options(gumbel=bad, **opt))
+    assert e.value.code == D.DEX_EINVAL
+    assert "16-byte aligned" in str(e.value)
+
+
 @pytest.mark.parametrize("cap", [0, 1, 2, 3, 4])
 def test_branch_cap_accepted(cap):
     """The pruned lattice's cap is 0..N; it needs no workspace of its own."""
