@@ -131,7 +131,8 @@ typedef struct {
                               spawn position children and a commit keeps branch 0 or N-1. The
                               round at state q has one row per explorer 0..q. 0: full DEX. */
   int32_t branch_cap;      /* Pruned lattice (the sparse lattice the same paper names as future work,
-                              Section 6; the policy is this library's): only nodes of explorers
+                              Appendix E, "Expansion growth and overhead"; the policy is this
+                              library's): only nodes of explorers
                               j < branch_cap spawn position children, so a round creates only the
                               nodes whose root path has no run of branch_cap or more depth moves
                               before a position move. Depth children are never pruned and the
@@ -153,9 +154,10 @@ typedef struct {
 typedef struct dex_ctx dex_ctx;
 
 /* Device bytes needed by dex_create for this shape, exploration set and
- * options. Pure: touches no device. X (host, n_x entries) must be strictly
- * increasing with X[n_x-1] == cfg->n_layers and, in this build, uniformly
- * spaced (d_k = (k+1) * L / n_x). Errors: DEX_EINVAL. */
+ * options. Pure: touches no device. X (host, n_x entries, 1 <= n_x <= 10)
+ * must be strictly increasing with X[0] >= 1 and X[n_x-1] == cfg->n_layers
+ * (Definition 4 of the paper); the stages between consecutive depths may have
+ * unequal lengths. Errors: DEX_EINVAL. */
 int dex_workspace_bytes(const dex_model_config* cfg, const int32_t* X, int32_t n_x,
                         const dex_options* opt, size_t* out_bytes);
 
@@ -168,9 +170,12 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
                int32_t L, const dex_options* opt, void* d_workspace, size_t ws_bytes, void* stream,
                dex_ctx** out);
 
-/* Resets every sequence and runs the prompts through all layers: positions
- * 0..len-2 of each prompt fill the committed KV cache; the last prompt token
- * becomes the anchor of the first cycle (FSM state 0). `tokens` holds the
+/* Algorithm 1's initialisation ("Depth Exploration for LLM Decoding",
+ * Section 3.1, Algorithm 1, the init step before the exploration loop): resets
+ * every sequence and runs the prompts through all layers. Positions 0..len-2
+ * of each prompt fill the committed KV cache; the last prompt token becomes
+ * the anchor of the first cycle (FSM state 0, Section 3.2, "Finite-state
+ * control and collapse"). `tokens` holds the
  * prompts back to back (host int32), `lens` their lengths (host, n_seqs).
  * Errors: DEX_EINVAL (n_seqs outside 1..max_batch, len < 1, token outside
  * [0, vocab)), DEX_ENOSPC (len + max_new_tokens > max_context), DEX_EHIP. */
@@ -185,8 +190,12 @@ int dex_prefill(dex_ctx* ctx, int32_t n_seqs, const int32_t* tokens, const int32
 int dex_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
 
 /* Plain autoregressive decoding with the same kernels: one full-depth token
- * per live sequence per call (branch = 0, layers = L). The reference that DEX
- * must reproduce bit for bit. Errors as dex_step (DEX_ESTATE if the context
+ * per live sequence per call (branch = 0, layers = L). DEX is lossless: every
+ * committed token is the final-depth reference, so the committed stream is
+ * the plain model's ("Depth Exploration for LLM Decoding", Section 3.2,
+ * "Commit process"; for sampling, the shared noise of Appendix C.1). This call
+ * computes that plain stream on the same batch-invariant kernels, the
+ * reference DEX must reproduce bit for bit. Errors as dex_step (DEX_ESTATE if the context
  * was stepped with dex_step since the last prefill). */
 int dex_ar_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
 

@@ -119,12 +119,27 @@ def options(mode="greedy", temperature=1.0, decs=True, max_batch=1, max_context=
     ``single_exit`` selects the single-exit ablation; ``branch_cap`` > 0 the pruned lattice
     (position children only from explorers below it); ``span_attention`` makes grouped
     attention blocks always run whole spans (same results; for tests)."""
-    return Options(SAMPLE if mode == "sample" else GREEDY, float(temperature), int(bool(decs)),
-                   max_batch, max_context, max_new_tokens,
-                   None if gumbel is None else gumbel.data_ptr(),
-                   0 if gumbel is None else gumbel.shape[1],
-                   int(bool(debug)) | (0 if graphs else 2) | (4 if span_attention else 0),
-                   int(bool(single_exit)), int(branch_cap))
+    if gumbel is not None:
+        import torch
+        if not isinstance(gumbel, torch.Tensor) or gumbel.dtype != torch.float32 or not gumbel.is_cuda:
+            raise ValueError("gumbel must be a float32 tensor on the GPU")
+        if gumbel.dim() != 3 or not gumbel.is_contiguous():
+            raise ValueError("gumbel must be a contiguous [max_batch, rows, vocab] tensor")
+        if gumbel.shape[0] < max_batch or gumbel.shape[1] < max_new_tokens:
+            raise ValueError(f"gumbel has shape {tuple(gumbel.shape)}: it needs max_batch={max_batch} "
+                             f"sequences and at least max_new_tokens={max_new_tokens} rows")
+        if gumbel.data_ptr() % 16:
+            raise ValueError("gumbel must be 16-byte aligned")
+    opt = Options(SAMPLE if mode == "sample" else GREEDY, float(temperature), int(bool(decs)),
+                  max_batch, max_context, max_new_tokens,
+                  None if gumbel is None else gumbel.data_ptr(),
+                  0 if gumbel is None else gumbel.shape[1],
+                  int(bool(debug)) | (0 if graphs else 2) | (4 if span_attention else 0),
+                  int(bool(single_exit)), int(branch_cap))
+    # The library reads the rows through the raw pointer: the options keep the
+    # tensor alive, and the context made from them keeps the options.
+    opt._gumbel = gumbel
+    return opt
 
 
 def workspace_bytes(cfg: ModelConfig, X: Sequence[int], opt: Options) -> int:
@@ -155,6 +170,14 @@ class Dex:
         self.cfg, self.opt, self.X = cfg, opt, list(X)
         self.N = len(X)
         self._keep = [opt]
+        g = getattr(opt, "_gumbel", None)
+        if opt.mode == SAMPLE and g is None and opt.gumbel:
+            raise ValueError("sampling options must come from options(), which checks and keeps the Gumbel rows")
+        if g is not None:
+            if g.shape[0] < opt.max_batch or g.shape[2] != cfg.vocab or g.shape[1] < opt.max_new_tokens + self.N - 1:
+                raise ValueError(f"gumbel has shape {tuple(g.shape)}; this context needs "
+                                 f"[>= {opt.max_batch}, >= {opt.max_new_tokens + self.N - 1}, {cfg.vocab}]")
+            self._keep.append(g)
         nbytes = workspace_bytes(cfg, X, opt)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         L = cfg.n_layers

@@ -34,6 +34,27 @@ def _dispatches(db):
     return cur.execute("select name, start, end, duration from kernels order by start").fetchall()
 
 
+def gemm_epilogue(name: str):
+    """Epilogue id of a GEMM dispatch (0 QKV, 1 residual, 2 SwiGLU, 3 exit head,
+    4/5 adapters), or None for other kernels. gemm_kernel<T, MB, NB, EPI>,
+    gemm_wide_kernel<EPI, SPLIT, WT>, gemm_split_reduce_kernel<EPI>."""
+    k = _short(name)
+    if "<" not in k:
+        return None
+    args = [a.strip() for a in k[k.index("<") + 1:k.rindex(">")].split(",")]
+    if k.startswith("dex::gemm_kernel"):
+        return int(args[3])
+    if k.startswith("dex::gemm_wide_kernel") or k.startswith("dex::gemm_split_reduce_kernel"):
+        return int(args[0])
+    return None
+
+
+def is_layer_gemm(name: str) -> bool:
+    """A stage-batched layer GEMM dispatch: QKV, O, gate/up or down (exit head
+    and adapters excluded)."""
+    return gemm_epilogue(name) in (0, 1, 2)
+
+
 def decode_window(rows):
     for i, r in enumerate(rows):
         if "sched_kernel" in r[0] or "ar_rows_kernel" in r[0]:
@@ -55,10 +76,12 @@ def trace_summary(db: str) -> str:
     for k, v in sorted(stats.items(), key=lambda kv: -sum(kv[1])):
         out.append(f"{k:<52} {len(v):>7} {sum(v) / len(v) / 1e3:>10.2f} {sum(v) / 1e6:>10.2f} "
                    f"{100.0 * sum(v) / total:>6.1f}%")
-    g = [d for k, v in stats.items() if k.startswith("dex::gemm_kernel") for d in v]
-    out.append(f"layer+head GEMM dispatches: {len(g)}, mean {sum(g) / len(g) / 1e3:.2f} us")
-    lg = [d for k, v in stats.items() if k.startswith("dex::gemm_kernel") and not k.endswith(", 3>") for d in v]
-    out.append(f"layer GEMM dispatches (exit head excluded): {len(lg)}, mean {sum(lg) / len(lg) / 1e3:.2f} us")
+    lg = [d for k, v in stats.items() if is_layer_gemm(k) for d in v]
+    out.append(f"layer GEMM dispatches (QKV, O, gate/up, down: gemm_kernel, gemm_wide_kernel and "
+               f"gemm_split_reduce_kernel): {len(lg)}, mean {sum(lg) / max(1, len(lg)) / 1e3:.2f} us, "
+               f"total {sum(lg) / 1e6:.2f} ms")
+    hg = [d for k, v in stats.items() if gemm_epilogue(k) == 3 or "head_reduce" in k for d in v]
+    out.append(f"exit-head dispatches: {len(hg)}, total {sum(hg) / 1e6:.2f} ms")
     return "\n".join(out) + "\n"
 
 
@@ -78,7 +101,7 @@ def _calibration(rows):
 
 def _gemm_window(rows):
     start = next(i for i, r in enumerate(rows) if "sched_kernel" in r[1] or "ar_rows_kernel" in r[1])
-    return [r for r in rows[start:] if "dex::gemm_kernel" in r[1] and not _short(r[1]).endswith(", 3>")]
+    return [r for r in rows[start:] if is_layer_gemm(r[1])]
 
 
 def traffic(fetch_db, write_db, bench_json, workload=None):

@@ -81,9 +81,11 @@ def ar_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = "
         rec = dict(token=yc, decoded=y, position=ev.C + 1, u=u, margins=margins,
                    b=b, layers=X[b], final_margin=m_final)
         if brute_ead:
-            cand = [decode(ev.logits(slot, l), [], mode, tau, g)[0] for l in range(1, L + 1)]
+            dec = [decode(ev.logits(slot, l), [], mode, tau, g) for l in range(1, L + 1)]
+            cand = [d[0] for d in dec]
             acc = [c == yc for c in cand]
-            rec.update(cand_by_depth=cand, ead=ead(acc), ead_stab=ead_stable(acc))
+            rec.update(cand_by_depth=cand, cand_margins=[d[1] for d in dec], ead=ead(acc),
+                       ead_stab=ead_stable(acc))
         if keep_logits:
             rec["final_logits"] = z_final
         recs.append(rec)
@@ -137,7 +139,7 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
     exists in a chain).
 
     branch_cap: a pruned lattice (the sparse lattice named as future work in
-    Section 6). The pages give no policy; the one taken here is structural:
+    Appendix E, "Expansion growth and overhead"). The pages give no policy; the one taken here is structural:
     only nodes of explorers j < branch_cap spawn position children (0: no
     pruning). Depth children are never pruned, so every anchor chain still
     reaches the final depth and the commit rule is unchanged: the output stays

@@ -24,7 +24,9 @@ activation is the backbone's, SiLU). The residual stream itself is not
 changed, and the final depth never has an adapter.
 
 Storage-dtype weights (bf16 or fp32) are upcast exactly to float64; all
-arithmetic is float64.
+arithmetic is float64. With ``resident=False`` the layer weights stay in their
+storage dtype and one layer at a time is upcast when a forward reaches it (the
+same values, so the same results), which keeps full-size models in host memory.
 """
 
 from dataclasses import dataclass
@@ -54,12 +56,17 @@ class LayerW:
     w_down: np.ndarray
 
 
+_LAYER_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
 class PlainModel:
-    def __init__(self, cfg, weights, adapters=None):
+    def __init__(self, cfg, weights, adapters=None, resident=True):
         """``cfg`` needs n_layers, d_model, n_heads, n_kv_heads, head_dim,
         d_ffn, vocab, rope_base, eps; ``weights`` is the dict produced by
         ``synthetic.weights.generate``; ``adapters`` (optional) maps a depth
-        l < L to a dict w1, b1, w2, b2, norm, alpha."""
+        l < L to a dict w1, b1, w2, b2, norm, alpha. ``resident=False`` keeps
+        the layer weights and the embedding as given and upcasts a layer (or
+        the gathered embedding rows) each time it is used."""
         self.L = cfg.n_layers
         self.d = cfg.d_model
         self.nq = cfg.n_heads
@@ -68,17 +75,45 @@ class PlainModel:
         self.V = cfg.vocab
         self.eps = float(cfg.eps)
         self.base = float(cfg.rope_base)
-        self.embed = _f64(weights["embed"])
-        self.layers: List[LayerW] = []
-        for lw in weights["layers"]:
-            self.layers.append(LayerW(**{k: _f64(lw[k]) for k in (
-                "attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")}))
+        tied = weights["lm_head"] is weights["embed"]
+        self.resident = bool(resident)
+        if self.resident:
+            self.embed = _f64(weights["embed"])
+            self.layers: Optional[List[LayerW]] = [self._upcast(lw) for lw in weights["layers"]]
+        else:
+            self.embed = weights["embed"]
+            self.layers = None
+            self._raw_layers = list(weights["layers"])
         self.final_norm = _f64(weights["final_norm"])
-        self.head = self.embed if weights["lm_head"] is weights["embed"] else _f64(weights["lm_head"])
+        if tied:
+            self.head = self.embed if self.resident else _f64(weights["embed"])
+        else:
+            self.head = _f64(weights["lm_head"])
         self.adapters = {}
         for l, a in (adapters or {}).items():
             assert 1 <= l < self.L, "adapters sit at non-final depths"
             self.adapters[int(l)] = {k: (float(v) if k == "alpha" else _f64(v)) for k, v in a.items()}
+
+    @staticmethod
+    def _upcast(lw) -> LayerW:
+        return LayerW(**{k: _f64(lw[k]) for k in _LAYER_KEYS})
+
+    def layer(self, l: int) -> LayerW:
+        """Weights of layer l (0-based) in float64."""
+        if self.layers is not None:
+            return self.layers[l]
+        return self._upcast(self._raw_layers[l])
+
+    def embed_rows(self, tokens: Sequence[int]) -> np.ndarray:
+        """E[tokens] in float64: the embedding rows of the given token ids."""
+        idx = np.asarray(tokens, dtype=np.int64)
+        if self.resident:
+            return self.embed[idx]
+        e = self.embed
+        if hasattr(e, "detach"):
+            import torch
+            return _f64(e[torch.from_numpy(idx)])
+        return _f64(np.asarray(e)[idx])
 
     # -- elementary pieces ------------------------------------------------
     def rmsnorm(self, x: np.ndarray, g: np.ndarray) -> np.ndarray:
@@ -108,6 +143,27 @@ class PlainModel:
             out[h] = p @ vh
         return out.reshape(-1)
 
+    def causal_attention(self, q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+        """All rows of a prompt at positions 0..n-1 at once: row i attends to
+        keys 0..i. q: [n, nq, hd]; k, v: [n, nkv, hd] -> [n, nq * hd].
+        Per query head, softmax(Q K^T / sqrt(hd) + M) V with M = -inf above
+        the diagonal (the same softmax as ``attend``, row by row)."""
+        import torch
+        n = q.shape[0]
+        rep = self.nq // self.nkv
+        out = np.empty((n, self.nq, self.hd))
+        future = torch.triu(torch.ones(n, n, dtype=torch.bool), diagonal=1)
+        for h in range(self.nq):
+            qh = torch.from_numpy(np.ascontiguousarray(q[:, h, :]))
+            kh = torch.from_numpy(np.ascontiguousarray(k[:, h // rep, :]))
+            vh = torch.from_numpy(np.ascontiguousarray(v[:, h // rep, :]))
+            s = (qh @ kh.T) / np.sqrt(self.hd)
+            s.masked_fill_(future, -np.inf)
+            p = torch.softmax(s, dim=-1)
+            out[:, h, :] = (p @ vh).numpy()
+            del s, p
+        return out.reshape(n, -1)
+
     def logits(self, h: np.ndarray) -> np.ndarray:
         """Shared exit head: h [..., d] -> [..., V]."""
         return self.rmsnorm(h, self.final_norm) @ self.head.T
@@ -125,31 +181,34 @@ class PlainModel:
         return self.logits(h + self.adapter_delta(h, depth))
 
     # -- forward passes ---------------------------------------------------
-    def prefill(self, tokens: Sequence[int]):
+    def prefill(self, tokens: Sequence[int], keep_hidden: bool = True):
         """Full causal forward of ``tokens`` at positions 0..n-1.
 
         Returns (K, V, hiddens): K, V as lists over layers of [n, nkv, hd];
-        hiddens [L+1, n, d] (hiddens[l] = residual stream after l layers).
+        hiddens [L+1, n, d] (hiddens[l] = residual stream after l layers), or
+        None when ``keep_hidden`` is false.
         """
         n = len(tokens)
         pos = np.arange(n)
-        h = self.embed[np.asarray(tokens, dtype=np.int64)]
-        Ks, Vs, hs = [], [], [h.copy()]
-        for lw in self.layers:
+        h = self.embed_rows(tokens)
+        Ks, Vs, hs = [], [], [h.copy()] if keep_hidden else None
+        for l in range(self.L):
+            lw = self.layer(l)
             a = self.rmsnorm(h, lw.attn_norm)
             q = self.rope((a @ lw.wq.T).reshape(n, self.nq, self.hd), pos)
             k = self.rope((a @ lw.wk.T).reshape(n, self.nkv, self.hd), pos)
             v = (a @ lw.wv.T).reshape(n, self.nkv, self.hd)
-            o = np.stack([self.attend(q[i], k[:i + 1], v[:i + 1]) for i in range(n)]) if n else \
-                np.zeros((0, self.nq * self.hd))
+            o = self.causal_attention(q, k, v) if n else np.zeros((0, self.nq * self.hd))
             h = h + o @ lw.wo.T
             f = self.rmsnorm(h, lw.ffn_norm)
             g = f @ lw.w_gate.T
             h = h + ((g / (1.0 + np.exp(-g))) * (f @ lw.w_up.T)) @ lw.w_down.T
             Ks.append(k)
             Vs.append(v)
-            hs.append(h.copy())
-        return Ks, Vs, np.stack(hs)
+            if keep_hidden:
+                hs.append(h.copy())
+            del lw
+        return Ks, Vs, (np.stack(hs) if keep_hidden else None)
 
     def extend(self, tokens: Sequence[int], positions: Sequence[int], past) -> tuple:
         """Forward independent single-token rows, each with its own past keys.
@@ -160,11 +219,12 @@ class PlainModel:
         """
         n = len(tokens)
         pos = np.asarray(positions, dtype=np.int64)
-        h = self.embed[np.asarray(tokens, dtype=np.int64)]
+        h = self.embed_rows(tokens)
         hs = [h.copy()]
         kn = np.empty((n, self.L, self.nkv, self.hd))
         vn = np.empty((n, self.L, self.nkv, self.hd))
-        for l, lw in enumerate(self.layers):
+        for l in range(self.L):
+            lw = self.layer(l)
             a = self.rmsnorm(h, lw.attn_norm)
             q = self.rope((a @ lw.wq.T).reshape(n, self.nq, self.hd), pos)
             k = self.rope((a @ lw.wk.T).reshape(n, self.nkv, self.hd), pos)
@@ -200,7 +260,7 @@ class SlotEvaluator:
 
     def begin(self, prompt: Sequence[int]):
         """Cache prompt[:-1]; the last prompt token becomes the anchor."""
-        K, V, _ = self.m.prefill(list(prompt[:-1]))
+        K, V, _ = self.m.prefill(list(prompt[:-1]), keep_hidden=False)
         self.K = [k for k in K]       # per layer [C, nkv, hd]
         self.V = [v for v in V]
         self.C = len(prompt) - 1

@@ -33,17 +33,21 @@ def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, g
     return ctx
 
 
-def run(ctx, prompts, T, ar=False, logits_at=None):
+def run(ctx, prompts, T, ar=False, logits_at=None, rows_log=None):
     """Decode T tokens per sequence. Returns per-sequence lists of records;
     each record adds u, margins and (for commit indices in ``logits_at``, or
-    all when None) the final-depth logits."""
+    all when None) the final-depth logits. ``rows_log`` (a list) receives the
+    rows each step ran per explorer."""
     ctx.prefill(prompts)
     out = [[] for _ in prompts]
     steps = 0
     while any(len(o) < T for o in out):
         recs = ctx.ar_step() if ar else ctx.step()
         steps += 1
+        if rows_log is not None:
+            rows_log.append(ctx.last_step_rows()[0])
         for r in recs:
+            r["step"] = steps
             t = len(out[r["seq"]])
             want = logits_at is None or t in logits_at
             u, m, lg = ctx.debug_anchor(r["seq"], want_logits=want)
@@ -79,3 +83,73 @@ def compare_with_oracle(gpu_recs, orc_recs, gate, logit_tol, N, check_chain=True
             worst = max(worst, err)
             assert err <= logit_tol, (err, logit_tol)
     return dict(tokens=n_tok, branches=n_b, worst_logit_err=worst)
+
+
+def gated_commit(o, gate):
+    """The commit's token and branch are decided with margins above the gate:
+    the final-depth decision and the anchor candidates u_0..u_b."""
+    return o["final_margin"] > gate and all(m > gate for m in o["margins"][:o["b"] + 1])
+
+
+def check_ead(gpu_recs, orc_recs, gate, X, decs=True):
+    """Layers per token against the depth ceiling of the stable EAD
+    ("Depth Exploration for LLM Decoding", Definition 1 eqs. (1)-(3),
+    Definition 4 eq. (6), Proposition 6): on every commit whose decisions clear
+    the gate, the GPU's layers(t) <= ceil_X(EAD_stab(t)) computed by the
+    oracle's brute force over every depth. A commit below the ceiling is a
+    transient match (the unmasked candidate at d_b already equals y although
+    a deeper layer disagrees) or, with DECS, DECS-induced (masking a shallower
+    duplicate exposed y). Returns counts: checked, agree, transient, decs."""
+    from oracle.depth import ceil_x
+    st = dict(checked=0, agree=0, transient=0, decs=0)
+    for g, o in zip(gpu_recs, orc_recs):
+        if not gated_commit(o, gate):
+            continue
+        c = ceil_x(o["ead_stab"], X)
+        assert g["layers"] <= c, (g, o["ead_stab"], c)
+        st["checked"] += 1
+        if g["layers"] == c:
+            st["agree"] += 1
+        elif o["cand_by_depth"][g["layers"] - 1] == g["token"]:
+            st["transient"] += 1
+        else:
+            assert decs, "without DECS the committed depth is the first explored depth proposing y"
+            st["decs"] += 1
+        if not decs:
+            first = min(d for d in X if o["cand_by_depth"][d - 1] == g["token"])
+            assert g["layers"] == first, (g, first)
+    return st
+
+
+def compare_lattice(gpu_recs, gpu_rows, orc_recs, orc_rows, gate, N):
+    """One sequence decoded alone on the GPU against the oracle's DEX lattice
+    forced onto its stream ("Depth Exploration for LLM Decoding", Algorithm 1,
+    Section 3.2): gated token, anchor candidates, branch and layers per
+    commit; and, while every branch agrees, the rounds between commits and the
+    rows each round ran per explorer (the lattice's node set). Returns the
+    number of rounds compared."""
+    assert len(gpu_recs) == len(orc_recs)
+    agree_upto = len(gpu_recs)
+    prev_step = 0
+    for t, (g, o) in enumerate(zip(gpu_recs, orc_recs)):
+        assert g["token"] == o["token"]
+        if o["margins"][-1] > gate:
+            assert g["token"] == o["decoded"]
+        ok = True
+        for j in range(N):
+            ok = ok and o["margins"][j] > gate
+            if ok:
+                assert g["u"][j] == o["u"][j], (t, j, g["u"], o["u"])
+        if g["branch"] != o["b"]:
+            assert not all(m > gate for m in o["margins"][:max(g["branch"], o["b"]) + 1]), (t, g, o)
+            agree_upto = min(agree_upto, t)
+        elif t <= agree_upto:
+            assert g["layers"] == o["layers"]
+        if t <= agree_upto:
+            assert g["step"] - prev_step == o["rounds"], (t, g["step"], prev_step, o["rounds"])
+        prev_step = g["step"]
+    # rounds up to (and including) the last commit whose branch history agrees
+    last = gpu_recs[min(agree_upto, len(gpu_recs) - 1)]["step"]
+    for r in range(min(last, len(orc_rows), len(gpu_rows))):
+        assert list(gpu_rows[r]) == list(orc_rows[r]), (r, gpu_rows[r], orc_rows[r])
+    return min(last, len(orc_rows), len(gpu_rows))

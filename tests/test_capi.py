@@ -96,12 +96,27 @@ def test_gumbel_rows_alignment():
     ok = buf[: rows * cfg.vocab].view(1, rows, cfg.vocab)
     bad = buf[1: 1 + rows * cfg.vocab].view(1, rows, cfg.vocab)
     assert ok.data_ptr() % 16 == 0 and bad.data_ptr() % 16 == 4
-    opt = dict(mode="sample", max_batch=1, max_new_tokens=64)
-    assert D.workspace_bytes(cfg, [2, 4, 6, 8], D.options(gumbel=ok, **opt)) > 0
+    def raw(t):
+        # the C struct filled directly, as a caller of the ABI would (the Python
+        # binding's own checks want a GPU tensor)
+        o = D.options(mode="sample", max_batch=1, max_new_tokens=64)
+        o.gumbel, o.gumbel_rows = t.data_ptr(), rows
+        return o
+    assert D.workspace_bytes(cfg, [2, 4, 6, 8], raw(ok)) > 0
     with pytest.raises(D.DexError) as e:
-        D.workspace_bytes(cfg, [2, 4, 6, 8], D.options(gumbel=bad, **opt))
+        D.workspace_bytes(cfg, [2, 4, 6, 8], raw(bad))
     assert e.value.code == D.DEX_EINVAL
     assert "16-byte aligned" in str(e.value)
+
+
+def test_gumbel_tensor_checked_by_binding():
+    """options() refuses Gumbel rows the exit head could not read safely: not
+    float32, not on the GPU, not a contiguous 3-D tensor, or too few rows."""
+    import torch
+    with pytest.raises(ValueError, match="on the GPU"):
+        D.options(mode="sample", gumbel=torch.zeros(1, 70, 2048))
+    with pytest.raises(ValueError, match="float32"):
+        D.options(mode="sample", gumbel=torch.zeros(1, 70, 2048, dtype=torch.bfloat16))
 
 
 @pytest.mark.parametrize("cap", [0, 1, 2, 3, 4])

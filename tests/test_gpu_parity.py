@@ -21,7 +21,7 @@ decoding modes. Full-size 7B runs are in test_gpu_fullsize.py.
 import numpy as np
 import pytest
 
-from oracle.decode import ar_decode
+from oracle.decode import ar_decode, dex_decode
 from oracle.model import PlainModel, SlotEvaluator
 from synthetic import get_workload
 from synthetic.adapters import generate_adapters
@@ -30,6 +30,17 @@ from synthetic.prompts import batch_prompts
 from synthetic.weights import generate
 
 pytestmark = pytest.mark.gpu
+
+# Margin gates (a decision is compared only where the oracle's top-1 minus
+# top-2 margin of the maximised quantity exceeds the gate). GATE is the one the
+# target fixes for bf16 weights; GATE2 is a second, tighter gate derived from
+# the measured logit error of the bf16 path (worst 1.5e-5 on these reduced
+# widths, 1.4e-4 at full size): a decision can only flip when the two top
+# values move by more than half the margin, and 1e-3 is over 30 times the
+# reduced-width error (7 times the full-size one), so nearly every decision is
+# compared. The fp32 path (errors ~1e-6) uses 1e-3 for both.
+GATE_BF16, GATE2_BF16, TOL_BF16 = 5e-2, 1e-3, 3e-2
+GATE_F32, TOL_F32 = 1e-3, 1e-4
 
 tiny = get_workload("tiny_f32")
 small = dict(d_model=512, n_heads=4, n_kv_heads=4, d_ffn=1376, vocab=4096)
@@ -80,6 +91,15 @@ CASES = {
         dict(T=16, span=True)),
     "tiny_N8_span": (tiny.scaled(tied=False, gamma=0.8, X=tuple(range(1, 9))), dict(T=32, span=True)),
     "qwen_gqa_long": (qwen_long, dict(T=32)),
+    # the GQA workload's 4:1 query/key-value head ratio (four query heads per
+    # attention work-item row instead of two), and a vocabulary that is not a
+    # multiple of 256 (4224 = 16 * 264: the exit head's last 16-tile column
+    # block is half full, as at V = 151936), greedy and sampled
+    "qwen_gqa4_x9_b4_narrow": (get_workload("qwen8b_x9_b16").scaled(
+        d_model=512, n_heads=8, n_kv_heads=2, d_ffn=1536, vocab=4224, batch=4, prompt_len=40), dict(T=16)),
+    "qwen_gqa4_long": (qwen_long.scaled(n_heads=8, n_kv_heads=2, vocab=4224), dict(T=24)),
+    "llama13b_x8_b16_sample_v4224_narrow": (get_workload("llama13b_x8_b8").scaled(
+        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4224, batch=16, prompt_len=48), dict(T=12)),
     "qwen_gqa_long_span": (qwen_long, dict(T=32, span=True)),
 }
 
@@ -97,7 +117,7 @@ def _max_context(w, kw):
 
 
 def _run_case(name):
-    from tests.gpu_helpers import compare_with_oracle, device_weights, make_ctx, run
+    from tests.gpu_helpers import check_ead, compare_with_oracle, device_weights, make_ctx, run
     w, kw = CASES[name]
     T = kw["T"]
     decs = kw.get("decs", True)
@@ -133,20 +153,26 @@ def _run_case(name):
     ads = dict(zip(w.X[:-1], generate_adapters(w, alpha))) if alpha is not None else None
     m = PlainModel(w, generate(w), adapters=ads)
     fp32 = w.dtype == "f32"
-    gate, tol = (1e-3, 1e-4) if fp32 else (5e-2, 3e-2)
-    stats = []
+    gate, gate2, tol = (GATE_F32, GATE_F32, TOL_F32) if fp32 else (GATE_BF16, GATE2_BF16, TOL_BF16)
+    stats, stats2, ead_st = [], [], []
     for s in range(w.batch):
         g = gum[s].numpy() if gum is not None else None
         orc = ar_decode(SlotEvaluator(m), prompts[s], T, w.X, mode=w.mode, tau=w.tau, gumbel=g,
-                        decs=decs, forced=[r["token"] for r in dex_recs[s]], brute_ead=False,
+                        decs=decs, forced=[r["token"] for r in dex_recs[s]], brute_ead=True,
                         keep_logits=True)
         stats.append(compare_with_oracle(dex_recs[s], orc, gate, tol, N))
-    print(f"[case] {name} steps={steps} oracle-compared tokens={sum(x['tokens'] for x in stats)} "
-          f"branches={sum(x['branches'] for x in stats)} worst logit err="
-          f"{max(x['worst_logit_err'] for x in stats):.3g}", flush=True)
+        stats2.append(compare_with_oracle(dex_recs[s], orc, gate2, tol, N))
+        ead_st.append(check_ead(dex_recs[s], orc, gate2, w.X, decs))
     total = sum(len(r) for r in dex_recs)
-    assert sum(x["tokens"] for x in stats) >= total // 4, "too few tokens passed the margin gate"
-    assert sum(x["branches"] for x in stats) >= total // 8, "too few branches passed the margin gate"
+    n_tok, n_b = sum(x["tokens"] for x in stats2), sum(x["branches"] for x in stats2)
+    es = {k: sum(x[k] for x in ead_st) for k in ead_st[0]}
+    print(f"[case] {name} steps={steps} commits={total} oracle-compared at {gate:g}: tokens="
+          f"{sum(x['tokens'] for x in stats)} branches={sum(x['branches'] for x in stats)}; at {gate2:g}: "
+          f"tokens={n_tok} branches={n_b}; worst logit err={max(x['worst_logit_err'] for x in stats):.3g}; "
+          f"layers vs ceil_X(EAD_stab): {es}", flush=True)
+    assert n_tok >= total // 2, "too few tokens passed the margin gate"
+    assert n_b >= total // 2, "too few branches passed the margin gate"
+    assert es["checked"] >= total // 2
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -185,7 +211,7 @@ def test_single_exit_parity(name):
         bs = [r["branch"] for r in se_recs[0]]
         assert steps == N + sum(b + 1 for b in bs[:-1])
     m = PlainModel(w, generate(w))
-    gate = 1e-3 if w.dtype == "f32" else 5e-2
+    gate = GATE_F32 if w.dtype == "f32" else GATE2_BF16
     checked = 0
     for s in range(w.batch):
         g = gum[s].numpy() if gum is not None else None
@@ -197,7 +223,7 @@ def test_single_exit_parity(name):
                 checked += 1
     total = sum(len(r) for r in se_recs)
     print(f"[case] single-exit {name} steps={steps} branches checked={checked}/{total}", flush=True)
-    assert checked >= total // 4
+    assert checked >= total // 2
 
 
 @pytest.mark.parametrize("name,cap", [("tiny", 1), ("tiny_sample", 2), ("llama7b_x8_sample_narrow", 3),
@@ -297,3 +323,38 @@ def test_graph_replay_matches_eager(name):
             for a, b in zip(eager, graph):
                 assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
                 assert a["u"] == b["u"]
+
+
+@pytest.mark.parametrize("name,cap,T", [("tiny", 0, 64), ("tiny_sample", 0, 48), ("tiny_N8", 0, 10),
+                                        ("llama7b_x8_sample_narrow", 0, 8), ("tiny", 1, 48),
+                                        ("tiny_sample", 2, 48), ("llama7b_x8_sample_narrow", 3, 12),
+                                        ("qwen_gqa_x9_b4_narrow", 2, 8), ("llama13b_x8_b4_narrow", 4, 6)])
+def test_lattice_matches_oracle(name, cap, T):
+    """The GPU lattice against the oracle's DEX lattice (Algorithm 1; with
+    cap > 0 the pruned lattice of Appendix E, "Expansion growth and
+    overhead"): the first sequence decoded alone on the GPU (the kernels are
+    batch-invariant, so its commits are those it makes inside the batch), the
+    oracle's dex_decode forced onto its stream. Per commit: the token, anchor
+    candidates, branch and layers under the margin gate, and the rounds since
+    the previous commit; per round: the rows run at each explorer."""
+    from tests.gpu_helpers import compare_lattice, device_weights, make_ctx, run
+    w, kw = CASES[name]
+    N = len(w.X)
+    print(f"[case] lattice {name} cap={cap} X={w.X} mode={w.mode} T={T}", flush=True)
+    Wd = device_weights(w)
+    prompt = batch_prompts(w)[:1]
+    gum = gumbel_rows(w.seed_g, 1, T + N, w.vocab) if w.mode == "sample" else None
+    ctx = make_ctx(w, Wd, 1, T, gumbel=gum.cuda() if gum is not None else None, branch_cap=cap)
+    rows = []
+    recs, steps = run(ctx, prompt, T, rows_log=rows)
+    ctx.close()
+    m = PlainModel(w, generate(w))
+    st = {}
+    orc = dex_decode(SlotEvaluator(m), prompt[0], T, w.X, mode=w.mode, tau=w.tau,
+                     gumbel=gum[0].numpy() if gum is not None else None,
+                     forced=[r["token"] for r in recs[0]], stats=st, branch_cap=cap)
+    gate = GATE_F32 if w.dtype == "f32" else GATE2_BF16
+    n = compare_lattice(recs[0], rows, orc, st["rows_per_round"], gate, N)
+    print(f"[case] lattice {name} cap={cap}: {steps} GPU rounds, {st['rounds']} oracle rounds, "
+          f"{n} rounds compared row for row, branches {[r['branch'] for r in recs[0]]}", flush=True)
+    assert n >= steps // 2

@@ -1,5 +1,5 @@
 """Pins of the pruned-lattice oracle (the sparse lattice that "Depth Exploration
-for LLM Decoding", Section 6, names as future work; the policy is this
+for LLM Decoding", Appendix E ("Expansion growth and overhead"), names as future work; the policy is this
 repository's: only explorers j < cap spawn position children).
 
 * Lossless: the committed stream, the selected branch, the layers and the
