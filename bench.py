@@ -119,12 +119,14 @@ def cpu_baseline(w, Wd, prompts, gpu_seq0, commits, gate, variant="dex", adapter
     ev.begin(list(prompts[0]))
     t_prefill = time.time() - t1
     log(f"[cpu] oracle prefill of {len(prompts[0]) - 1} positions: {t_prefill:.1f}s")
-    kv0 = (list(ev.K), list(ev.V), ev.C)
+    ev_ead = ev.fork()
     g = gumbel_rows(w.seed_g, 1, commits + len(w.X), w.vocab)[0].numpy() if w.mode == "sample" else None
     t2 = time.time()
     recs = dex_decode(_Prefilled(ev), prompts[0], commits, w.X, mode=w.mode, tau=w.tau, gumbel=g,
                       decs=variant != "vanilla", single_exit=variant == "single_exit",
-                      branch_cap=branch_cap if variant == "pruned" else 0)
+                      branch_cap=branch_cap if variant == "pruned" else 0,
+                      on_commit=lambda r: log(f"[cpu] oracle DEX commit at position {r['position']}: token "
+                                              f"{r['token']}, branch {r['b']} ({time.time() - t2:.1f}s)"))
     t_dec = time.time() - t2
     blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
     threads = blas[0]["num_threads"] if blas else 1
@@ -140,13 +142,11 @@ def cpu_baseline(w, Wd, prompts, gpu_seq0, commits, gate, variant="dex", adapter
             break
         agree += 1
     # stable EAD of the GPU's commits (oracle plain decoding forced onto them)
-    ev2 = SlotEvaluator(model)
-    ev2.K, ev2.V, ev2.C = list(kv0[0]), list(kv0[1]), kv0[2]
-    ev2.memo = {}
     n_ead = min(len(gpu_seq0), commits)
     t3 = time.time()
-    orc = ar_decode(_Prefilled(ev2), prompts[0], n_ead, w.X, mode=w.mode, tau=w.tau, gumbel=g,
-                    decs=variant != "vanilla", forced=[r["token"] for r in gpu_seq0[:n_ead]], brute_ead=True)
+    orc = ar_decode(_Prefilled(ev_ead), prompts[0], n_ead, w.X, mode=w.mode, tau=w.tau, gumbel=g,
+                    decs=variant != "vanilla", forced=[r["token"] for r in gpu_seq0[:n_ead]], brute_ead=True,
+                    on_commit=lambda r: log(f"[cpu] EAD_stab at position {r['position']}: {r['ead_stab']}"))
     log(f"[cpu] brute-force EAD of {n_ead} GPU commits: {time.time() - t3:.1f}s")
     ead = dict(sample=f"the first {n_ead} commits of sequence 0", commits=n_ead, agree=0, transient=0,
                decs_induced=0, gated=0, layers=[], ceil_ead_stab=[], ead_stab=[])

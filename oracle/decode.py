@@ -54,11 +54,12 @@ def _gumbel_row(gumbel, target: int, P: int, mode: str):
 def ar_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = "greedy",
               tau: float = 1.0, gumbel=None, decs: bool = True,
               forced: Optional[Sequence[int]] = None, brute_ead: bool = True,
-              keep_logits: bool = False) -> List[dict]:
+              keep_logits: bool = False, on_commit=None) -> List[dict]:
     """Plain AR decoding of T tokens; ``gumbel[j]`` is the noise row for target
     position len(prompt) + j. With ``forced`` the context follows the given
     tokens instead of the decoded ones (every reported quantity is still a
-    function of the committed prefix only)."""
+    function of the committed prefix only). ``on_commit(record)`` is called
+    after each token (progress reporting)."""
     N, L, P = len(X), X[-1], len(prompt)
     ev.begin(list(prompt))
     anchor = int(prompt[-1])
@@ -89,6 +90,8 @@ def ar_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = "
         if keep_logits:
             rec["final_logits"] = z_final
         recs.append(rec)
+        if on_commit is not None:
+            on_commit(rec)
         ev.commit(yc)
         anchor = yc
     return recs
@@ -123,11 +126,12 @@ def _subtree(n: Node) -> List[Node]:
 def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = "greedy",
                tau: float = 1.0, gumbel=None, decs: bool = True,
                forced: Optional[Sequence[int]] = None, stats: Optional[dict] = None,
-               single_exit: bool = False, branch_cap: int = 0) -> List[dict]:
+               single_exit: bool = False, branch_cap: int = 0, on_commit=None) -> List[dict]:
     """DEX decoding of T tokens. Returns one record per commit:
     token, b, layers (= d_b), u (anchor candidates), margins, rounds (rounds
     since the previous commit). ``stats`` (optional dict) receives per-round
-    node counts per explorer under "rows_per_round".
+    node counts per explorer under "rows_per_round". ``on_commit(record)`` is
+    called after each commit (progress reporting).
 
     single_exit: the single-exit ablation of "Depth Exploration for LLM
     Decoding", Section 4 (Figure 4, right-top): intermediate depth branches
@@ -216,6 +220,8 @@ def dex_decode(ev, prompt: Sequence[int], T: int, X: Sequence[int], mode: str = 
         b = next((j for j in range(N) if u[j] == y), N - 1)
         recs.append(dict(token=y, decoded=u[-1], position=ev.C + 1, u=u,
                          margins=[c.margin for c in chain], b=b, layers=X[b], rounds=since))
+        if on_commit is not None:
+            on_commit(recs[-1])
         since = 0
         if len(recs) == T:
             break

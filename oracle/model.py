@@ -213,9 +213,10 @@ class PlainModel:
     def extend(self, tokens: Sequence[int], positions: Sequence[int], past) -> tuple:
         """Forward independent single-token rows, each with its own past keys.
 
-        ``past(i, l)`` returns (K, V) arrays [n_past, nkv, hd] of the keys row i
-        attends to at layer l (positions < its own). Rows do not see each
-        other. Returns (hiddens [n, L+1, d], K [n, L, nkv, hd], V [n, L, nkv, hd]).
+        ``past(i, l, k_i, v_i)`` returns (K, V) arrays [n_keys, nkv, hd] of the
+        keys row i attends to at layer l: its past positions, then its own key
+        and value (k_i, v_i, [nkv, hd]) last. Rows do not see each other.
+        Returns (hiddens [n, L+1, d], K [n, L, nkv, hd], V [n, L, nkv, hd]).
         """
         n = len(tokens)
         pos = np.asarray(positions, dtype=np.int64)
@@ -232,9 +233,8 @@ class PlainModel:
             kn[:, l], vn[:, l] = k, v
             o = np.empty((n, self.nq * self.hd))
             for i in range(n):
-                pk, pv = past(i, l)
-                o[i] = self.attend(q[i], np.concatenate([pk, k[i:i + 1]]),
-                                   np.concatenate([pv, v[i:i + 1]]))
+                keys, vals = past(i, l, k[i], v[i])
+                o[i] = self.attend(q[i], keys, vals)
             h = h + o @ lw.wo.T
             f = self.rmsnorm(h, lw.ffn_norm)
             g = f @ lw.w_gate.T
@@ -261,10 +261,46 @@ class SlotEvaluator:
     def begin(self, prompt: Sequence[int]):
         """Cache prompt[:-1]; the last prompt token becomes the anchor."""
         K, V, _ = self.m.prefill(list(prompt[:-1]), keep_hidden=False)
-        self.K = [k for k in K]       # per layer [C, nkv, hd]
-        self.V = [v for v in V]
         self.C = len(prompt) - 1
+        # Per layer, the committed keys and values sit in rows [0, C) of a
+        # buffer; the rows after them are scratch where a row's ancestor and
+        # own entries are laid out behind the committed ones before it attends.
+        self.Kb = [np.empty((self.C + 64, self.m.nkv, self.m.hd)) for _ in range(self.m.L)]
+        self.Vb = [np.empty((self.C + 64, self.m.nkv, self.m.hd)) for _ in range(self.m.L)]
+        for l in range(self.m.L):
+            self.Kb[l][:self.C] = K[l]
+            self.Vb[l][:self.C] = V[l]
         self.memo = {}                # slot -> (hiddens [L+1, d], K [L,nkv,hd], V)
+
+    @property
+    def K(self):
+        """Committed keys per layer, [C, nkv, hd] each."""
+        return [k[:self.C] for k in self.Kb]
+
+    @property
+    def V(self):
+        return [v[:self.C] for v in self.Vb]
+
+    def _reserve(self, rows: int):
+        if rows <= self.Kb[0].shape[0]:
+            return
+        cap = 2 * rows
+        for buf in (self.Kb, self.Vb):
+            for l in range(self.m.L):
+                b = np.empty((cap, self.m.nkv, self.m.hd))
+                b[:self.C] = buf[l][:self.C]
+                buf[l] = b
+
+    def fork(self) -> "SlotEvaluator":
+        """An evaluator with a copy of this one's committed cache and an empty
+        memo (the state right after a prefill or a commit)."""
+        ev = SlotEvaluator(self.m)
+        ev.C = self.C
+        ev.Kb = [k[:self.C + 64].copy() for k in self.Kb]
+        ev.Vb = [v[:self.C + 64].copy() for v in self.Vb]
+        ev._reserve(self.C + 64)
+        ev.memo = {}
+        return ev
 
     def eval_slots(self, slots: Sequence[tuple]):
         todo = [s for s in dict.fromkeys(slots) if s not in self.memo]
@@ -274,11 +310,18 @@ class SlotEvaluator:
             for m in range(1, len(s)):
                 assert s[:m] in self.memo, "slot evaluated before its prefix"
 
-        def past(i, l):
+        self._reserve(self.C + max(len(s) for s in todo))
+
+        def past(i, l, k_self, v_self):
+            # committed keys, then the slot's earlier tokens, then its own
             s = todo[i]
-            ks = [self.K[l]] + [self.memo[s[:m]][1][l][None] for m in range(1, len(s))]
-            vs = [self.V[l]] + [self.memo[s[:m]][2][l][None] for m in range(1, len(s))]
-            return np.concatenate(ks), np.concatenate(vs)
+            C, n = self.C, len(s)
+            for m in range(1, n):
+                self.Kb[l][C + m - 1] = self.memo[s[:m]][1][l]
+                self.Vb[l][C + m - 1] = self.memo[s[:m]][2][l]
+            self.Kb[l][C + n - 1] = k_self
+            self.Vb[l][C + n - 1] = v_self
+            return self.Kb[l][:C + n], self.Vb[l][:C + n]
 
         hs, kn, vn = self.m.extend([s[-1] for s in todo],
                                    [self.C + len(s) - 1 for s in todo], past)
@@ -300,9 +343,10 @@ class SlotEvaluator:
         assert len(anchor) == 1
         a = anchor[0]
         _, k, v = self.memo[a]
+        self._reserve(self.C + 1)
         for l in range(self.m.L):
-            self.K[l] = np.concatenate([self.K[l], k[l][None]])
-            self.V[l] = np.concatenate([self.V[l], v[l][None]])
+            self.Kb[l][self.C] = k[l]
+            self.Vb[l][self.C] = v[l]
         self.C += 1
         self.memo = {s[1:]: val for s, val in self.memo.items()
                      if len(s) >= 2 and s[0] == a[0] and s[1] == y}
