@@ -77,7 +77,15 @@ struct WsPlan {
   std::vector<size_t> wqkv, wo, wgu, wdown;
   size_t total;
   int Rmax, nchunk, split_cols;
+  size_t sbytes[10];   // bytes of the per-round scratch regions (ScratchRegion order)
 };
+
+// Per-round scratch regions of the workspace: written by a round before they
+// are read and never carried to the next round (plan staging, attention and
+// GEMM partial results, exit-head tile summaries). dex_step_noalloc takes
+// them from the static device array instead.
+enum ScratchRegion { SC_ROWS, SC_PLANS, SC_ITEMS, SC_Q, SC_ATTN_OUT, SC_ACT, SC_ATTN_PART, SC_ATTN_TAIL, SC_GEMM_SPLIT,
+                     SC_HEAD_PART, SC_N };
 
 size_t esize(int dtype) { return dtype == DEX_DTYPE_BF16 ? 2 : 4; }
 
@@ -177,18 +185,29 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.dbg_m = lay.take(B * kMaxN * 4);
   w.Xd = lay.take(kMaxN * 4);
   w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
-  w.rows = lay.take(R * sizeof(RowInfo));
-  w.plans = lay.take(B * sizeof(SeqPlan));
-  w.items = lay.take(R * (sizeof(AttnItem) + 12));   // items, then the attention block lists (3 R ints)
-  w.q = lay.take(R * nq * hd * 4);
-  w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
-  w.attn_out = lay.take(R * nq * hd * 4);
-  w.act = lay.take(R * std::max(F, m) * 4);
-  w.attn_part = lay.take(R * nq * w.nchunk * (hd + 4) * 4);
-  w.attn_tail = lay.take(R * nq * attn_mix_slots() * (hd + 4) * 4);
   w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
-  w.gemm_split = lay.take((size_t)kKSplit * kSplitRows * w.split_cols * 4);
-  w.head_part = lay.take(R * (V / 16) * 3 * 4);
+  w.sbytes[SC_ROWS] = R * sizeof(RowInfo);
+  w.sbytes[SC_PLANS] = B * sizeof(SeqPlan);
+  w.sbytes[SC_ITEMS] = R * (sizeof(AttnItem) + 12);   // items, then the attention block lists (3 R ints)
+  w.sbytes[SC_Q] = R * nq * hd * 4;
+  w.sbytes[SC_ATTN_OUT] = R * nq * hd * 4;
+  w.sbytes[SC_ACT] = R * std::max(F, m) * 4;
+  w.sbytes[SC_ATTN_PART] = R * nq * w.nchunk * (hd + 4) * 4;
+  w.sbytes[SC_ATTN_TAIL] = R * nq * attn_mix_slots() * (hd + 4) * 4;
+  // the split-range partials serve the wide (bf16) GEMM only
+  w.sbytes[SC_GEMM_SPLIT] = c->dtype == DEX_DTYPE_BF16 ? (size_t)kKSplit * kSplitRows * w.split_cols * 4 : 0;
+  w.sbytes[SC_HEAD_PART] = R * (V / 16) * 3 * 4;
+  w.rows = lay.take(w.sbytes[SC_ROWS]);
+  w.plans = lay.take(w.sbytes[SC_PLANS]);
+  w.items = lay.take(w.sbytes[SC_ITEMS]);
+  w.q = lay.take(w.sbytes[SC_Q]);
+  w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
+  w.attn_out = lay.take(w.sbytes[SC_ATTN_OUT]);
+  w.act = lay.take(w.sbytes[SC_ACT]);
+  w.attn_part = lay.take(w.sbytes[SC_ATTN_PART]);
+  w.attn_tail = lay.take(w.sbytes[SC_ATTN_TAIL]);
+  w.gemm_split = lay.take(w.sbytes[SC_GEMM_SPLIT]);
+  w.head_part = lay.take(w.sbytes[SC_HEAD_PART]);
   w.total = lay.off;
   return w;
 }
@@ -315,10 +334,16 @@ constexpr int kWideRows = DEX_WIDE_ROWS;
 // split-k groups apart; wide ones only with bf16 weights); ga carries
 // everything else. A wide launch that would have few blocks runs split by k
 // range when its rows fit the scratch (split_cols: the scratch's row length).
-// Counts launches.
+// m2: 1 lets launches with N <= K (the O and down projections) take 32-row
+// blocks of 8 tiles per wave (measured on the 13B-shaped lattice rounds: O
+// 201 -> 163 us, down 552 -> 424 us per launch, while QKV and gate/up, with N
+// several times K, run faster on 64-row blocks); 2 sends every unsplit wide
+// launch there (tests); 0 never. Unsplit wide launches row-shard their groups
+// over the XCDs (gemm_wide_kernel). Counts launches.
 template <typename T>
 hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, int split_cols,
-                         hipStream_t st, int* launches) {
+                         hipStream_t st, int* launches, int m2 = 1) {
+  std::vector<GemmGroup> halves;
   for (int wide = 0; wide < 2; ++wide) {
     ga.ngroups = 0;
     int rows = 0;
@@ -327,7 +352,7 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
       const bool mine = i < groups.size() && is_wide == (wide == 1);
       const bool flush = i == groups.size() || ga.ngroups == kMaxGroups;
       if (flush && ga.ngroups) {
-        hipError_t e;
+        hipError_t e = hipSuccess;
         if (wide) {
           // blocks at 4 tiles per wave: many -> as they are; a medium launch
           // -> 2 tiles per wave (twice the blocks); few -> split by k range
@@ -335,8 +360,28 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
           int shape = WIDE_T4;
           if (blocks4 < 128 && rows <= kSplitRows && ga.N <= split_cols) shape = WIDE_SPLIT;
           else if (blocks4 < 384) shape = WIDE_T2;
-          e = launch_gemm_wide(ga, epi, shape, st);
-          *launches += shape == WIDE_SPLIT ? 2 : 1;
+          if (shape != WIDE_SPLIT && (m2 == 2 || (m2 == 1 && ga.N <= ga.K))) shape = WIDE_M2;
+          ga.xcd_rows = shape != WIDE_SPLIT;
+          if (shape == WIDE_M2) {
+            // the chunk's groups as groups of at most 32 rows, kMaxGroups a launch
+            halves.clear();
+            for (int g = 0; g < ga.ngroups; ++g)
+              for (int o = 0; o < ga.g[g].m; o += 32) {
+                GemmGroup h = ga.g[g];
+                h.row0 += o;
+                h.m = std::min(32, ga.g[g].m - o);
+                halves.push_back(h);
+              }
+            for (size_t h0 = 0; h0 < halves.size() && e == hipSuccess; h0 += kMaxGroups) {
+              ga.ngroups = (int)std::min(halves.size() - h0, (size_t)kMaxGroups);
+              for (int g = 0; g < ga.ngroups; ++g) ga.g[g] = halves[h0 + g];
+              e = launch_gemm_wide(ga, epi, shape, st);
+              ++*launches;
+            }
+          } else {
+            e = launch_gemm_wide(ga, epi, shape, st);
+            *launches += shape == WIDE_SPLIT ? 2 : 1;
+          }
         } else {
           e = launch_gemm<T>(ga, epi, st);
           ++*launches;
@@ -354,6 +399,10 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
   }
   return hipSuccess;
 }
+
+// 32-row wide GEMM blocks: where they pay (1), or for every unsplit wide
+// launch (2, options.debug bit 3).
+int m2_mode(const dex_ctx* ctx) { return (ctx->opt.debug & 8) ? 2 : 1; }
 
 // Opens a timed region of class `cls`; returns its mark index or -1.
 int prof_begin(dex_ctx* ctx, int cls) {
@@ -502,7 +551,8 @@ int run_adapters(dex_ctx* ctx, const std::vector<std::array<int, 3>>& ranges) {
     ga.N = pass ? D.d : m;
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
     int launches = 0;
-    HIPCHK(launch_groups<T>(ga, groups, pass ? EPI_ADAPT2 : EPI_ADAPT1, ctx->wp.split_cols, st, &launches));
+    HIPCHK(launch_groups<T>(ga, groups, pass ? EPI_ADAPT2 : EPI_ADAPT1, ctx->wp.split_cols, st, &launches,
+                            m2_mode(ctx)));
     bytes = (double)ranges.size() * m * D.d * es + (double)nrows * (m + D.d) * 4 * (pass ? 2 : 1);
     flops = 2.0 * nrows * m * D.d;
     prof_end(ctx, mk, launches, bytes, flops);
@@ -565,7 +615,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     }
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
     int launches = 0;
-    const hipError_t e = launch_groups<T>(ga, glist, epi, ctx->wp.split_cols, st, &launches);
+    const hipError_t e = launch_groups<T>(ga, glist, epi, ctx->wp.split_cols, st, &launches, m2_mode(ctx));
     if (e != hipSuccess) return e;
     prof_end(ctx, mk, launches, bytes, flops);
     return hipSuccess;
@@ -660,7 +710,7 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
     nrows += rg.second;
   }
   ga.split = ctx->gemm_split;
-  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches));
+  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches, m2_mode(ctx)));
   for (const auto& rg : ranges) {
     HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, rg.first, rg.second, ctx->rows, D.P, ctx->cand, ctx->margin,
                               st));

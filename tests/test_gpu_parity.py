@@ -100,6 +100,17 @@ CASES = {
     "qwen_gqa4_long": (qwen_long.scaled(n_heads=8, n_kv_heads=2, vocab=4224), dict(T=24)),
     "llama13b_x8_b16_sample_v4224_narrow": (get_workload("llama13b_x8_b8").scaled(
         d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4224, batch=16, prompt_len=48), dict(T=12)),
+    # every unsplit wide GEMM launch on 32-row blocks (m2=True; by default only
+    # launches with N <= K and many blocks, the 13B-shaped O and down
+    # projections, use them): layer GEMMs, the exit head with depth-coupled
+    # masks, noise and a half-full last column block, and the adapters
+    "llama13b_x8_b16_sample_v4224_narrow_m2": (get_workload("llama13b_x8_b8").scaled(
+        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4224, batch=16, prompt_len=48), dict(T=12, m2=True)),
+    "qwen_gqa4_x9_b4_narrow_m2": (get_workload("qwen8b_x9_b16").scaled(
+        d_model=512, n_heads=8, n_kv_heads=2, d_ffn=1536, vocab=4224, batch=4, prompt_len=40), dict(T=16, m2=True)),
+    "llama13b_x8_b4_adapters_narrow_m2": (get_workload("llama13b_x8_b8").scaled(
+        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4096, batch=4, prompt_len=48),
+        dict(T=20, adapter_alpha=0.5, m2=True)),
     "qwen_gqa_long_span": (qwen_long, dict(T=32, span=True)),
 }
 
@@ -130,11 +141,13 @@ def _run_case(name):
     gum_d = gum.cuda() if gum is not None else None
     alpha = kw.get("adapter_alpha")
     ads_d = generate_adapters(w, alpha, device="cuda") if alpha is not None else None
-    span = kw.get("span", False)
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span)
+    span, m2 = kw.get("span", False), kw.get("m2", False)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span,
+                   m2_gemm=m2)
     dex_recs, steps = run(ctx, prompts, T)
     ctx.close()
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span,
+                   m2_gemm=m2)
     ar_recs, ar_steps = run(ctx, prompts, T, ar=True)
     ctx.close()
     assert ar_steps == T
