@@ -202,6 +202,21 @@ int dex_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
  * was stepped with dex_step since the last prefill). */
 int dex_ar_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
 
+/* dex_step for callers that cannot allocate device memory (tight serving
+ * loops, harnesses that forbid hipMalloc): the same round as dex_step, with
+ * the same records and the same bits, launched eagerly (no HIP graph is
+ * captured or instantiated, no timing events are created) and with the
+ * round's scratch (row and attention plans, attention and GEMM partial
+ * results, exit-head tile summaries) in a static device array of the library
+ * instead of the workspace's scratch regions. The array is 64 MiB per GPU,
+ * held until the process ends; contexts on one GPU share it, so calls that
+ * overlap on one GPU (from any context or thread) race. Nothing in it carries
+ * from one call to the next. Can be mixed with dex_step on the same context.
+ * Errors as dex_step, plus DEX_ENOSPC when the context's per-round scratch
+ * exceeds 64 MiB (it grows with max_batch * 2^(N-1) rows, the vocabulary and
+ * max_context: small models and batches fit). */
+int dex_step_noalloc(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out);
+
 /* For sequence `seq`'s last commit: the anchor-path candidates u_0..u_{N-1}
  * and their top-1 minus top-2 margins (host arrays of N, either may be NULL),
  * and, when options.debug bit 0 is set, the final-depth logits (host array of

@@ -16,6 +16,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -214,6 +215,37 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
 
 }  // namespace
 
+// Scratch of dex_step_noalloc, for callers that cannot allocate: a file-scope
+// device array, one copy per GPU, held until the process ends. Its host-side
+// name is not a device address; host code uses the address that
+// hipGetSymbolAddress returns for the current device (g_scratch_ptr).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices] = {};
+static std::mutex g_scratch_mu;
+
+// Looks up the static scratch's device address on the current device, once
+// per device. Returns the device index, or -1 with err set.
+static int scratch_setup(std::string& err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    err = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return -1;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return dev;
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || p == nullptr) {
+    err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+    return -1;
+  }
+  g_scratch_ptr[dev] = p;
+  return dev;
+}
+
 struct dex_ctx {
   dex_model_config cfg;
   dex_options opt;
@@ -221,6 +253,8 @@ struct dex_ctx {
   int N, S, L;
   std::vector<int> X;
   bool bf16;
+  int device = -1;         // device the context was created on
+  bool no_graphs = false;  // launch this round eagerly (dex_step_noalloc)
   hipStream_t st;
   char* ws;
   WsPlan wp;
@@ -886,7 +920,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   };
   // Timed rounds run eagerly: an event recorded inside a replayed graph does
   // not wait for the kernel before it, so it cannot time that kernel.
-  const bool graphs = !(ctx->opt.debug & 2) && !ctx->prof;
+  const bool graphs = !(ctx->opt.debug & 2) && !ctx->prof && !ctx->no_graphs;
   std::string key;
   if (graphs) {
     key.reserve(16 + 3 * B);
@@ -1074,11 +1108,15 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
       rc = DEX_ENOSPC;
     }
   }
+  // the static scratch of dex_step_noalloc, looked up once per device
+  const int device = rc ? -1 : scratch_setup(err);
+  if (!rc && device < 0) rc = DEX_EHIP;
   if (rc) {
     g_create_error = err;
     return rc;
   }
   dex_ctx* ctx = new dex_ctx();
+  ctx->device = device;
   ctx->cfg = *cfg;
   ctx->opt = *opt;
   ctx->N = n_x;
@@ -1234,6 +1272,69 @@ static int step_common(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int3
 int dex_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out) { return step_common(ctx, false, out, cap, n_out); }
 
 int dex_ar_step(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out) { return step_common(ctx, true, out, cap, n_out); }
+
+int dex_step_noalloc(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out) {
+  if (!ctx) return DEX_EINVAL;
+  if (ctx->poisoned) return DEX_EHIP;
+  const WsPlan& wp = ctx->wp;
+  size_t need = 0;
+  for (int r = 0; r < SC_N; ++r) need += (wp.sbytes[r] + 255) & ~(size_t)255;
+  if (need > kStaticScratchBytes) {
+    char buf[200];
+    snprintf(buf, sizeof buf, "per-round scratch of this context (%zu bytes) exceeds the static scratch (%zu bytes)",
+             need, kStaticScratchBytes);
+    ctx->err = buf;
+    return DEX_ENOSPC;
+  }
+  char* base = (char*)g_scratch_ptr[ctx->device];
+  if (base == nullptr) {
+    ctx->err = "static scratch not set up on the context's device";
+    return DEX_EHIP;
+  }
+  size_t off[SC_N];
+  size_t o = 0;
+  for (int r = 0; r < SC_N; ++r) {
+    off[r] = o;
+    o += (wp.sbytes[r] + 255) & ~(size_t)255;
+  }
+  // the round's scratch regions point into the static array for this call only
+  RowInfo* rows = ctx->rows;
+  SeqPlan* plans = ctx->plans;
+  AttnItem* items = ctx->items;
+  int* item_list = ctx->item_list;
+  float *q = ctx->q, *attn_part = ctx->attn_part, *attn_tail = ctx->attn_tail, *gemm_split = ctx->gemm_split,
+        *head_part = ctx->head_part;
+  void *attn_out = ctx->attn_out, *act = ctx->act;
+  const bool prof = ctx->prof;
+  ctx->rows = (RowInfo*)(base + off[SC_ROWS]);
+  ctx->plans = (SeqPlan*)(base + off[SC_PLANS]);
+  ctx->items = (AttnItem*)(base + off[SC_ITEMS]);
+  ctx->item_list = (int*)(ctx->items + wp.Rmax);
+  ctx->q = (float*)(base + off[SC_Q]);
+  ctx->attn_out = base + off[SC_ATTN_OUT];
+  ctx->act = base + off[SC_ACT];
+  ctx->attn_part = (float*)(base + off[SC_ATTN_PART]);
+  ctx->attn_tail = (float*)(base + off[SC_ATTN_TAIL]);
+  ctx->gemm_split = (float*)(base + off[SC_GEMM_SPLIT]);
+  ctx->head_part = (float*)(base + off[SC_HEAD_PART]);
+  ctx->no_graphs = true;    // no graph capture or instantiation
+  ctx->prof = false;        // no timing events
+  const int rc = step_common(ctx, false, out, cap, n_out);
+  ctx->rows = rows;
+  ctx->plans = plans;
+  ctx->items = items;
+  ctx->item_list = item_list;
+  ctx->q = q;
+  ctx->attn_out = attn_out;
+  ctx->act = act;
+  ctx->attn_part = attn_part;
+  ctx->attn_tail = attn_tail;
+  ctx->gemm_split = gemm_split;
+  ctx->head_part = head_part;
+  ctx->no_graphs = false;
+  ctx->prof = prof;
+  return rc;
+}
 
 int dex_debug_anchor(dex_ctx* ctx, int32_t seq, int32_t* u, float* margins, float* logits) {
   if (!ctx) return DEX_EINVAL;

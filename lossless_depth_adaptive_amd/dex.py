@@ -17,7 +17,7 @@ LIB_PATH = os.environ.get("DEX_LIBRARY") or os.path.join(HERE, "libdex.so")
 DEX_OK, DEX_EINVAL, DEX_ENOSPC, DEX_ESTATE, DEX_EHIP = 0, -1, -2, -3, -4
 DTYPE_F32, DTYPE_BF16 = 0, 1
 GREEDY, SAMPLE = 0, 1
-EXPORTED = ["dex_workspace_bytes", "dex_create", "dex_prefill", "dex_step", "dex_ar_step",
+EXPORTED = ["dex_workspace_bytes", "dex_create", "dex_prefill", "dex_step", "dex_step_noalloc", "dex_ar_step",
             "dex_debug_anchor", "dex_last_step_rows", "dex_profile", "dex_destroy", "dex_last_error"]
 PROF_CLASSES = ["gemm", "attention", "exit_head", "row_ops", "lattice"]
 
@@ -85,6 +85,7 @@ def load_library() -> ctypes.CDLL:
     lib.dex_prefill.argtypes = [vp, i32, P(i32), P(i32)]
     lib.dex_step.argtypes = [vp, P(Commit), i32, P(i32)]
     lib.dex_ar_step.argtypes = [vp, P(Commit), i32, P(i32)]
+    lib.dex_step_noalloc.argtypes = [vp, P(Commit), i32, P(i32)]
     lib.dex_debug_anchor.argtypes = [vp, i32, P(i32), P(ctypes.c_float), P(ctypes.c_float)]
     lib.dex_last_step_rows.argtypes = [vp, P(i32), P(i32)]
     lib.dex_profile.argtypes = [vp, i32, P(KernelStats), i32]
@@ -233,6 +234,11 @@ class Dex:
 
     def step(self) -> List[dict]:
         return self._step(self.lib.dex_step)
+
+    def step_noalloc(self) -> List[dict]:
+        """dex_step with the round's scratch in the library's static device
+        array and no graph capture (allocates nothing)."""
+        return self._step(self.lib.dex_step_noalloc)
 
     def ar_step(self) -> List[dict]:
         return self._step(self.lib.dex_ar_step)

@@ -33,7 +33,7 @@ def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, g
     return ctx
 
 
-def run(ctx, prompts, T, ar=False, logits_at=None, rows_log=None):
+def run(ctx, prompts, T, ar=False, logits_at=None, rows_log=None, noalloc=False):
     """Decode T tokens per sequence. Returns per-sequence lists of records;
     each record adds u, margins and (for commit indices in ``logits_at``, or
     all when None) the final-depth logits. ``rows_log`` (a list) receives the
@@ -42,7 +42,7 @@ def run(ctx, prompts, T, ar=False, logits_at=None, rows_log=None):
     out = [[] for _ in prompts]
     steps = 0
     while any(len(o) < T for o in out):
-        recs = ctx.ar_step() if ar else ctx.step()
+        recs = ctx.ar_step() if ar else (ctx.step_noalloc() if noalloc else ctx.step())
         steps += 1
         if rows_log is not None:
             rows_log.append(ctx.last_step_rows()[0])
