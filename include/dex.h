@@ -124,10 +124,7 @@ typedef struct {
                               bit 2: grouped attention blocks always run whole spans of key
                               positions (by default a launch does so only when that still fills
                               the GPU). The results are the same bits either way; the bit lets
-                              small inputs exercise the span path;
-                              bit 3: every unsplit bf16 GEMM launch of many rows uses 32-row blocks
-                              (by default only launches whose output is no wider than their input
-                              do). Same bits; lets small inputs exercise that kernel shape. */
+                              small inputs exercise the span path. */
   int32_t single_exit;     /* 1: the single-exit ablation ("Depth Exploration for LLM Decoding",
                               Section 4, Figure 4 right-top): only explorers 0 and N-1 exit; the
                               intermediate ones run without proposing, so only explorer-0 nodes

@@ -35,29 +35,32 @@ def _hipcc():
             return c
 
 
-def _compile(src: str, outdir: str) -> str:
+def _compile(src: str, outdir: str, defines=()) -> str:
     obj = os.path.join(outdir, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *FLAGS, *SOURCE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr[-6000:]}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    outdir = os.path.join(HERE, "_build")
+def build(verbose: bool = True, lib: str = LIB, defines=()) -> str:
+    """Compile every source and link ``lib``; ``defines`` are extra -D flags
+    (tuning macros of the sources)."""
+    outdir = os.path.join(HERE, "_build" + ("_" + "_".join(d.replace("=", "") for d in defines) if defines else ""))
     os.makedirs(outdir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, outdir), SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, outdir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":

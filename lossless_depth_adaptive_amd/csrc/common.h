@@ -16,10 +16,9 @@ constexpr int kKSplit = 8;
 constexpr int kMaxMB = 4;            // 16-row MFMA blocks per GEMM group (<= 64 rows)
 constexpr int kMaxGroups = 48;       // GEMM groups per launch
 constexpr int kSplitRows = 512;      // rows of one split-range wide GEMM launch
-// Wide GEMM launch shapes: 64-row blocks with 4 column tiles per wave
-// (unsplit or split by k range) or 2 tiles per wave (unsplit); or 32-row
-// blocks with 8 tiles per wave (WIDE_M2: groups of at most 32 rows).
-enum WideShape { WIDE_T4 = 0, WIDE_SPLIT = 1, WIDE_T2 = 2, WIDE_M2 = 3 };
+// Wide GEMM launch shapes: 4 column tiles per wave (unsplit or split by k
+// range), or 2 tiles per wave (unsplit).
+enum WideShape { WIDE_T4 = 0, WIDE_SPLIT = 1, WIDE_T2 = 2 };
 constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item (one MFMA tile)
 constexpr int kKvTile = 32;          // positions per K/V cache tile = keys per attention chunk
 #ifndef DEX_ATTN_SC

@@ -368,16 +368,16 @@ constexpr int kWideRows = DEX_WIDE_ROWS;
 // split-k groups apart; wide ones only with bf16 weights); ga carries
 // everything else. A wide launch that would have few blocks runs split by k
 // range when its rows fit the scratch (split_cols: the scratch's row length).
-// m2: 1 lets launches with N <= K (the O and down projections) take 32-row
-// blocks of 8 tiles per wave (measured on the 13B-shaped lattice rounds: O
-// 201 -> 163 us, down 552 -> 424 us per launch, while QKV and gate/up, with N
-// several times K, run faster on 64-row blocks); 2 sends every unsplit wide
-// launch there (tests); 0 never. Unsplit wide launches row-shard their groups
-// over the XCDs (gemm_wide_kernel). Counts launches.
+// Unsplit wide launches row-shard their groups over the XCDs
+// (gemm_wide_kernel; the 13B-shaped batch-8 workload 326.6 -> 328.1 tokens/s,
+// two A/B passes of three runs each). Counts launches.
+#ifndef DEX_XCD_ROWS
+#define DEX_XCD_ROWS 1
+#endif
+constexpr int kXcdRows = DEX_XCD_ROWS;
 template <typename T>
 hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, int split_cols,
-                         hipStream_t st, int* launches, int m2 = 1) {
-  std::vector<GemmGroup> halves;
+                         hipStream_t st, int* launches) {
   for (int wide = 0; wide < 2; ++wide) {
     ga.ngroups = 0;
     int rows = 0;
@@ -394,28 +394,9 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
           int shape = WIDE_T4;
           if (blocks4 < 128 && rows <= kSplitRows && ga.N <= split_cols) shape = WIDE_SPLIT;
           else if (blocks4 < 384) shape = WIDE_T2;
-          if (shape != WIDE_SPLIT && (m2 == 2 || (m2 == 1 && ga.N <= ga.K))) shape = WIDE_M2;
-          ga.xcd_rows = shape != WIDE_SPLIT;
-          if (shape == WIDE_M2) {
-            // the chunk's groups as groups of at most 32 rows, kMaxGroups a launch
-            halves.clear();
-            for (int g = 0; g < ga.ngroups; ++g)
-              for (int o = 0; o < ga.g[g].m; o += 32) {
-                GemmGroup h = ga.g[g];
-                h.row0 += o;
-                h.m = std::min(32, ga.g[g].m - o);
-                halves.push_back(h);
-              }
-            for (size_t h0 = 0; h0 < halves.size() && e == hipSuccess; h0 += kMaxGroups) {
-              ga.ngroups = (int)std::min(halves.size() - h0, (size_t)kMaxGroups);
-              for (int g = 0; g < ga.ngroups; ++g) ga.g[g] = halves[h0 + g];
-              e = launch_gemm_wide(ga, epi, shape, st);
-              ++*launches;
-            }
-          } else {
-            e = launch_gemm_wide(ga, epi, shape, st);
-            *launches += shape == WIDE_SPLIT ? 2 : 1;
-          }
+          ga.xcd_rows = shape != WIDE_SPLIT && kXcdRows;
+          e = launch_gemm_wide(ga, epi, shape, st);
+          *launches += shape == WIDE_SPLIT ? 2 : 1;
         } else {
           e = launch_gemm<T>(ga, epi, st);
           ++*launches;
@@ -433,10 +414,6 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
   }
   return hipSuccess;
 }
-
-// 32-row wide GEMM blocks: where they pay (1), or for every unsplit wide
-// launch (2, options.debug bit 3).
-int m2_mode(const dex_ctx* ctx) { return (ctx->opt.debug & 8) ? 2 : 1; }
 
 // Opens a timed region of class `cls`; returns its mark index or -1.
 int prof_begin(dex_ctx* ctx, int cls) {
@@ -585,8 +562,7 @@ int run_adapters(dex_ctx* ctx, const std::vector<std::array<int, 3>>& ranges) {
     ga.N = pass ? D.d : m;
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
     int launches = 0;
-    HIPCHK(launch_groups<T>(ga, groups, pass ? EPI_ADAPT2 : EPI_ADAPT1, ctx->wp.split_cols, st, &launches,
-                            m2_mode(ctx)));
+    HIPCHK(launch_groups<T>(ga, groups, pass ? EPI_ADAPT2 : EPI_ADAPT1, ctx->wp.split_cols, st, &launches));
     bytes = (double)ranges.size() * m * D.d * es + (double)nrows * (m + D.d) * 4 * (pass ? 2 : 1);
     flops = 2.0 * nrows * m * D.d;
     prof_end(ctx, mk, launches, bytes, flops);
@@ -649,7 +625,7 @@ int run_layers(dex_ctx* ctx, int nrows, const std::vector<std::pair<int, int>>& 
     }
     const int mk = prof_begin(ctx, DEX_PROF_GEMM);
     int launches = 0;
-    const hipError_t e = launch_groups<T>(ga, glist, epi, ctx->wp.split_cols, st, &launches, m2_mode(ctx));
+    const hipError_t e = launch_groups<T>(ga, glist, epi, ctx->wp.split_cols, st, &launches);
     if (e != hipSuccess) return e;
     prof_end(ctx, mk, launches, bytes, flops);
     return hipSuccess;
@@ -744,7 +720,7 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
     nrows += rg.second;
   }
   ga.split = ctx->gemm_split;
-  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches, m2_mode(ctx)));
+  HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches));
   for (const auto& rg : ranges) {
     HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, rg.first, rg.second, ctx->rows, D.P, ctx->cand, ctx->margin,
                               st));

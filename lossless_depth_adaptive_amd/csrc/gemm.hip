@@ -649,14 +649,12 @@ __device__ __forceinline__ void resid_epilogue_wide(const GemmArgs& args, const 
   }
 }
 
-template <int EPI, bool SPLIT, int WT, int MBLK, int DEPTH>
+template <int EPI, bool SPLIT, int WT>
 __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
   constexpr int BT = 4 * WT;   // 16-column tiles per block
-  constexpr int ROWS = 16 * MBLK;   // rows per block (MBLK 16-row blocks)
-  // 32-row blocks keep the running range sums in LDS (a private slot per
-  // thread) instead of registers, so that two blocks still fit a CU
-  constexpr bool TLDS = MBLK == 2;
-  static_assert(!(SPLIT && TLDS), "the split form keeps its sums in registers");
+  constexpr int MBLK = 4;      // 16-row blocks per block (one per wave)
+  constexpr int ROWS = 16 * MBLK;
+  constexpr int DEPTH = 3;     // k-steps of loads in flight
   constexpr int KSTEP = 32;
   constexpr bool NORM = epi_norm(EPI);
   const int ntiles = args.N >> 4;
@@ -694,20 +692,15 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   // f[buf][part][mb][lane]: part 0 (hi) / 1 (lo) of row 16 mb + (lane & 15),
   // k 8 (lane >> 4) .. +7 of the k-step, the A operand of lane `lane`.
   struct Stage { u32x4_t f[2][2][MBLK][64]; };
-  struct Main {
-    Stage s;
-    f32x4_t tot[TLDS ? MBLK * WT : 1][TLDS ? kWideThreads : 1];   // [tile][thread]: conflict-free
-  };
   struct Out { float t[SPLIT ? 1 : ROWS][BT * 16 + 4]; };   // the split form stores from registers
-  __shared__ union { Main m; Out o; } sm;
+  __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[ROWS];
   __shared__ float scr[SPLIT || EPI != EPI_ADAPT2 ? 1 : ROWS][17];
 
-  // Thread (w, lane) of the first MBLK waves converts the fragment that lane
-  // `lane` of row block w reads. Rows past the group's end repeat its first
-  // row and tiles past N the last tile: their outputs are never stored.
-  const bool conv = w < MBLK;
-  const int ar = 16 * (conv ? w : 0) + col16;
+  // Thread (w, lane) converts the fragment that lane `lane` of row block w
+  // reads. Rows past the group's end repeat its first row and tiles past N the
+  // last tile: their outputs are never stored.
+  const int ar = 16 * w + col16;
   const int rr = ar < G.m ? ar : 0;
   const float* asrc = (NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
                             : (const float*)args.a + (size_t)(G.row0 + rr) * K) + 8 * kg;
@@ -734,70 +727,39 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
     for (int nb = 0; nb < WT; ++nb) p.b[nb] = bbase[((size_t)btile[nb] * KS + ks) * 64];
   };
   // One k-step from the registers of p, which then take k-step ks + DEPTH
-  // (DEPTH register sets, so each load has DEPTH - 1 k-steps of MFMAs to land
-  // in): the activation loads go out once p.a is staged, the weight loads once
-  // the MFMAs have read p.b.
+  // (three register sets, so each load has two k-steps of MFMAs to land in;
+  // a fourth set measured no faster): the activation loads go out once p.a is
+  // staged, the weight loads once the MFMAs have read p.b.
   auto step = [&](int ks, Pre& p, f32x4_t (&acc)[MBLK][WT]) {
     const int buf = ks & 1;
-    if (conv) {
-      u32x4_t hv, lv;
+    u32x4_t hv, lv;
 #pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        unsigned h0, l0, h1, l1;
-        split_bf2(p.a[x][0], p.a[x][1], h0, l0);
-        split_bf2(p.a[x][2], p.a[x][3], h1, l1);
-        hv[2 * x] = h0;
-        hv[2 * x + 1] = h1;
-        lv[2 * x] = l0;
-        lv[2 * x + 1] = l1;
-      }
-      sm.m.s.f[buf][0][w][lane] = hv;
-      sm.m.s.f[buf][1][w][lane] = lv;
-      load_a(ks + DEPTH, p);
+    for (int x = 0; x < 2; ++x) {
+      unsigned h0, l0, h1, l1;
+      split_bf2(p.a[x][0], p.a[x][1], h0, l0);
+      split_bf2(p.a[x][2], p.a[x][3], h1, l1);
+      hv[2 * x] = h0;
+      hv[2 * x + 1] = h1;
+      lv[2 * x] = l0;
+      lv[2 * x + 1] = l1;
     }
+    sm.s.f[buf][0][w][lane] = hv;
+    sm.s.f[buf][1][w][lane] = lv;
+    load_a(ks + DEPTH, p);
     __syncthreads();
-    if constexpr (MBLK == 4) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const u32x4_t ahu = sm.m.s.f[buf][0][mb][lane], alu = sm.m.s.f[buf][1][mb][lane];
-        bf16x8_t ah, al;
-        __builtin_memcpy(&ah, &ahu, 16);
-        __builtin_memcpy(&al, &alu, 16);
+    for (int mb = 0; mb < MBLK; ++mb) {
+      const u32x4_t ahu = sm.s.f[buf][0][mb][lane], alu = sm.s.f[buf][1][mb][lane];
+      bf16x8_t ah, al;
+      __builtin_memcpy(&ah, &ahu, 16);
+      __builtin_memcpy(&al, &alu, 16);
 #pragma unroll
-        for (int nb = 0; nb < WT; ++nb) {
-          bf16x8_t bv;
-          __builtin_memcpy(&bv, &p.b[nb], 16);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[mb][nb], 0, 0, 0);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[mb][nb], 0, 0, 0);
-        }
+      for (int nb = 0; nb < WT; ++nb) {
+        bf16x8_t bv;
+        __builtin_memcpy(&bv, &p.b[nb], 16);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, acc[mb][nb], 0, 0, 0);
       }
-    } else {
-      // every accumulator takes its hi product, then (MBLK * WT MFMAs later)
-      // its lo product: the same chain per output, with no back-to-back
-      // dependent pair
-      bf16x8_t ah[MBLK], al[MBLK];
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb) {
-        const u32x4_t ahu = sm.m.s.f[buf][0][mb][lane], alu = sm.m.s.f[buf][1][mb][lane];
-        __builtin_memcpy(&ah[mb], &ahu, 16);
-        __builtin_memcpy(&al[mb], &alu, 16);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < WT; ++nb) {
-          bf16x8_t bv;
-          __builtin_memcpy(&bv, &p.b[nb], 16);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah[mb], bv, acc[mb][nb], 0, 0, 0);
-        }
-#pragma unroll
-      for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < WT; ++nb) {
-          bf16x8_t bv;
-          __builtin_memcpy(&bv, &p.b[nb], 16);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al[mb], bv, acc[mb][nb], 0, 0, 0);
-        }
     }
     load_b(ks + DEPTH, p);
   };
@@ -805,14 +767,11 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   // The k ranges in order: acc takes one range, tot the range sums (the first
   // as it is, the next ones added in order); the loop walks every k-step of
   // the block's ranges with the three register sets in turn.
-  f32x4_t tot[TLDS ? 1 : MBLK][TLDS ? 1 : WT], acc[MBLK][WT];
+  f32x4_t tot[MBLK][WT], acc[MBLK][WT];
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < WT; ++nb) {
-      acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if constexpr (!TLDS) tot[mb][nb] = acc[mb][nb];
-    }
+    for (int nb = 0; nb < WT; ++nb) acc[mb][nb] = tot[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int r0 = SPLIT ? z : 0, r1 = SPLIT ? z + 1 : kKSplit;
   int ks = (KS * r0) / kKSplit;
   const int kend = (KS * r1) / kKSplit;
@@ -820,7 +779,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   Pre p[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    if (conv) load_a(ks + i, p[i]);
+    load_a(ks + i, p[i]);
     load_b(ks + i, p[i]);
   }
   auto close = [&](int k) {
@@ -829,12 +788,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
       for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
         for (int nb = 0; nb < WT; ++nb) {
-          if constexpr (TLDS) {
-            f32x4_t& t = sm.m.tot[mb * WT + nb][threadIdx.x];
-            t = r == r0 ? acc[mb][nb] : t + acc[mb][nb];
-          } else {
-            tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
-          }
+          tot[mb][nb] = r == r0 ? acc[mb][nb] : tot[mb][nb] + acc[mb][nb];
           acc[mb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
       ++r;
@@ -880,25 +834,13 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
       if (lane == 0) rs_sh[rl] = 1.0f / sqrtf(s / (float)K + args.eps);
     }
   }
-  if constexpr (TLDS) {
-    // the sums come back to registers before the output tile overwrites them
-#pragma unroll
-    for (int mb = 0; mb < MBLK; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < WT; ++nb) acc[mb][nb] = sm.m.tot[mb * WT + nb][threadIdx.x];
-  }
   __syncthreads();   // the last k-step's LDS reads are done before the outputs overwrite them
 #pragma unroll
   for (int mb = 0; mb < MBLK; ++mb)
 #pragma unroll
     for (int nb = 0; nb < WT; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v;
-        if constexpr (TLDS) v = acc[mb][nb][r];
-        else v = tot[mb][nb][r];
-        sm.o.t[mb * 16 + kg * 4 + r][(w * WT + nb) * 16 + col16] = v;
-      }
+      for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * WT + nb) * 16 + col16] = tot[mb][nb][r];
   __syncthreads();
   if constexpr (EPI == EPI_HEAD) {
     head_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
@@ -1054,11 +996,11 @@ static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
   return launch_gemm_mb<T, 1, EPI>(a, mb, st);
 }
 
-template <int EPI, bool SPLIT, int WT, int MBLK = 4, int DEPTH = 3>
+template <int EPI, bool SPLIT, int WT>
 static void wide_launch(const GemmArgs& a, hipStream_t st) {
   const int ncb = (a.N / 16 + 4 * WT - 1) / (4 * WT);
   const dim3 grid(a.ngroups * ncb * (SPLIT ? kKSplit : 1));
-  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT, WT, MBLK, DEPTH>), grid, dim3(kWideThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT, WT>), grid, dim3(kWideThreads), 0, st, a);
   if (SPLIT) {
     hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3(a.ngroups, a.N / 16), dim3(kWideThreads), 0, st, a);
   }
@@ -1074,9 +1016,6 @@ template <int EPI>
 static void wide_launch_shape(const GemmArgs& a, int shape, hipStream_t st) {
   if (shape == WIDE_SPLIT) wide_launch<EPI, true, 4>(a, st);
   else if (shape == WIDE_T2) wide_launch<EPI, false, 2>(a, st);
-  else if (shape == WIDE_M2) wide_launch<EPI, false, 8, 2>(a, st);
-  else if (shape == 4) wide_launch<EPI, false, 4, 4, 4>(a, st);
-  else if (shape == 5) wide_launch<EPI, false, 8, 2, 4>(a, st);
   else wide_launch<EPI, false, 4>(a, st);
 }
 

@@ -114,13 +114,12 @@ def model_config(n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab,
 
 def options(mode="greedy", temperature=1.0, decs=True, max_batch=1, max_context=1024,
             max_new_tokens=256, gumbel=None, debug=False, graphs=True, single_exit=False,
-            branch_cap=0, span_attention=False, m2_gemm=False) -> Options:
+            branch_cap=0, span_attention=False) -> Options:
     """``gumbel``: CUDA float32 tensor [max_batch, rows, vocab] or None. ``debug`` keeps the
     final-depth logits of each last commit; ``graphs=False`` launches every round eagerly;
     ``single_exit`` selects the single-exit ablation; ``branch_cap`` > 0 the pruned lattice
     (position children only from explorers below it); ``span_attention`` makes grouped
-    attention blocks always run whole spans (same results; for tests); ``m2_gemm`` makes every
-    unsplit bf16 GEMM launch of many rows use 32-row blocks (same results; for tests)."""
+    attention blocks always run whole spans (same results; for tests)."""
     if gumbel is not None:
         import torch
         if not isinstance(gumbel, torch.Tensor) or gumbel.dtype != torch.float32 or not gumbel.is_cuda:
@@ -136,7 +135,7 @@ def options(mode="greedy", temperature=1.0, decs=True, max_batch=1, max_context=
                   max_batch, max_context, max_new_tokens,
                   None if gumbel is None else gumbel.data_ptr(),
                   0 if gumbel is None else gumbel.shape[1],
-                  int(bool(debug)) | (0 if graphs else 2) | (4 if span_attention else 0) | (8 if m2_gemm else 0),
+                  int(bool(debug)) | (0 if graphs else 2) | (4 if span_attention else 0),
                   int(bool(single_exit)), int(branch_cap))
     # The library reads the rows through the raw pointer: the options keep the
     # tensor alive, and the context made from them keeps the options.

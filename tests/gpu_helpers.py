@@ -15,7 +15,7 @@ def device_weights(w):
 
 
 def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, gumbel=None, graphs=True,
-             single_exit=False, adapters=None, branch_cap=0, span_attention=False, m2_gemm=False):
+             single_exit=False, adapters=None, branch_cap=0, span_attention=False):
     """``adapters``: device adapter dicts (synthetic.adapters layout) or None."""
     X = list(X or w.X)
     m = adapters[0]["w1"].shape[0] if adapters else 0
@@ -26,7 +26,7 @@ def make_ctx(w, Wd, batch, T, X=None, decs=True, debug=True, max_context=None, g
     if w.mode == "sample" and gumbel is None:
         gumbel = gumbel_rows(w.seed_g, batch, T + len(X), w.vocab).cuda()
     opt = D.options(w.mode, w.tau, decs, batch, max_context, T, gumbel, debug, graphs, single_exit, branch_cap,
-                    span_attention, m2_gemm)
+                    span_attention)
     ctx = D.Dex(cfg, Wd, X, opt, adapters=adapters)
     ctx._gumbel = gumbel
     ctx._adapters = adapters

@@ -100,17 +100,6 @@ CASES = {
     "qwen_gqa4_long": (qwen_long.scaled(n_heads=8, n_kv_heads=2, vocab=4224), dict(T=24)),
     "llama13b_x8_b16_sample_v4224_narrow": (get_workload("llama13b_x8_b8").scaled(
         d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4224, batch=16, prompt_len=48), dict(T=12)),
-    # every unsplit wide GEMM launch on 32-row blocks (m2=True; by default only
-    # launches with N <= K and many blocks, the 13B-shaped O and down
-    # projections, use them): layer GEMMs, the exit head with depth-coupled
-    # masks, noise and a half-full last column block, and the adapters
-    "llama13b_x8_b16_sample_v4224_narrow_m2": (get_workload("llama13b_x8_b8").scaled(
-        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4224, batch=16, prompt_len=48), dict(T=12, m2=True)),
-    "qwen_gqa4_x9_b4_narrow_m2": (get_workload("qwen8b_x9_b16").scaled(
-        d_model=512, n_heads=8, n_kv_heads=2, d_ffn=1536, vocab=4224, batch=4, prompt_len=40), dict(T=16, m2=True)),
-    "llama13b_x8_b4_adapters_narrow_m2": (get_workload("llama13b_x8_b8").scaled(
-        d_model=640, n_heads=5, n_kv_heads=5, d_ffn=1728, vocab=4096, batch=4, prompt_len=48),
-        dict(T=20, adapter_alpha=0.5, m2=True)),
     "qwen_gqa_long_span": (qwen_long, dict(T=32, span=True)),
 }
 
@@ -141,13 +130,11 @@ def _run_case(name):
     gum_d = gum.cuda() if gum is not None else None
     alpha = kw.get("adapter_alpha")
     ads_d = generate_adapters(w, alpha, device="cuda") if alpha is not None else None
-    span, m2 = kw.get("span", False), kw.get("m2", False)
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span,
-                   m2_gemm=m2)
+    span = kw.get("span", False)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span)
     dex_recs, steps = run(ctx, prompts, T)
     ctx.close()
-    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span,
-                   m2_gemm=m2)
+    ctx = make_ctx(w, Wd, w.batch, T, decs=decs, gumbel=gum_d, adapters=ads_d, max_context=mc, span_attention=span)
     ar_recs, ar_steps = run(ctx, prompts, T, ar=True)
     ctx.close()
     assert ar_steps == T
@@ -371,3 +358,38 @@ def test_lattice_matches_oracle(name, cap, T):
     print(f"[case] lattice {name} cap={cap}: {steps} GPU rounds, {st['rounds']} oracle rounds, "
           f"{n} rounds compared row for row, branches {[r['branch'] for r in recs[0]]}", flush=True)
     assert n >= steps // 2
+
+
+@pytest.mark.parametrize("name", ["llama7b_x8_sample_narrow", "llama13b_x8_b4_narrow", "tiny_sample"])
+def test_reprefill_resumes_on_gpu(name):
+    """Recovery by re-prefill (a lost context is rebuilt from the prompt and
+    the committed tokens): dex_prefill(prompt || first k commits) followed by
+    dex_step continues every sequence with the same tokens, branches, layers,
+    anchor candidates and final-depth logit bits as the uninterrupted decode.
+    The committed prefix decides all of them (Section 3.2, "Commit process");
+    the prefill and the lattice rounds run the same batch-invariant kernels."""
+    import torch
+    from tests.gpu_helpers import device_weights, make_ctx, run
+    w, kw = CASES[name]
+    T, k = kw["T"], kw["T"] // 2
+    N = len(w.X)
+    print(f"[case] reprefill {name} T={T} k={k}", flush=True)
+    Wd = device_weights(w)
+    prompts = batch_prompts(w)
+    gum = gumbel_rows(w.seed_g, w.batch, T + N, w.vocab) if w.mode == "sample" else None
+    ctx = make_ctx(w, Wd, w.batch, T, gumbel=gum.cuda() if gum is not None else None)
+    full, _ = run(ctx, prompts, T)
+    ctx.close()
+    resumed_prompts = [list(prompts[s]) + [r["token"] for r in full[s][:k]] for s in range(w.batch)]
+    # noise row j now serves target position len(prompt) + k + j
+    gum2 = gum[:, k:, :].contiguous().cuda() if gum is not None else None
+    ctx = make_ctx(w, Wd, w.batch, T - k, gumbel=gum2, max_context=w.prompt_len + T + N + 8)
+    again, _ = run(ctx, resumed_prompts, T - k)
+    ctx.close()
+    for s in range(w.batch):
+        for a, b in zip(full[s][k:], again[s]):
+            assert (a["token"], a["position"], a["branch"], a["layers"]) == \
+                   (b["token"], b["position"], b["branch"], b["layers"]), (s, a, b)
+            assert a["u"] == b["u"]
+            assert np.array_equal(a["logits"].view(np.uint32), b["logits"].view(np.uint32))
+    print(f"[case] reprefill {name}: {w.batch} x {T - k} commits resumed bit for bit", flush=True)

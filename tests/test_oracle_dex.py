@@ -195,3 +195,22 @@ def test_real_model_single_exit(variant):
     dx = dex_decode(SlotEvaluator(m), p, T, w.X, mode=w.mode, tau=w.tau, gumbel=G, single_exit=True)
     assert [r["token"] for r in dx] == [r["token"] for r in ar]
     assert [r["b"] for r in dx] == _single_exit_expected(ar, w.X)
+
+
+@pytest.mark.parametrize("mode", ["greedy", "sample"])
+def test_reprefill_resumes_the_stream(mode):
+    """Recovery by re-prefill: a decode restarted from a prefill of
+    prompt || the first k committed tokens continues with the same tokens,
+    branches and layers (every committed quantity is a function of the
+    committed prefix, Section 3.2, "Commit process"; the Gumbel row of a
+    target position is the same whichever prefill reached it)."""
+    w, m = _real("tiny_f32", tied=False, gamma=0.8, mode=mode, seed_g=3001)
+    p = list(prompt_ids(w.prompt_dist, w.vocab, 20, w.seed_p, 0))
+    T, k = 24, 9
+    G = gumbel_rows(w.seed_g, 1, T + len(w.X) + 1, w.vocab).numpy()[0] if mode == "sample" else None
+    full = dex_decode(SlotEvaluator(m), p, T, w.X, mode=mode, tau=w.tau, gumbel=G)
+    again = dex_decode(SlotEvaluator(m), p + [r["token"] for r in full[:k]], T - k, w.X, mode=mode, tau=w.tau,
+                       gumbel=None if G is None else G[k:])
+    assert [(r["token"], r["b"], r["layers"], r["u"]) for r in full[k:]] == \
+           [(r["token"], r["b"], r["layers"], r["u"]) for r in again]
+    assert [r["position"] for r in full[k:]] == [r["position"] for r in again]
