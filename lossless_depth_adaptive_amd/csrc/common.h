@@ -16,9 +16,10 @@ constexpr int kKSplit = 8;
 constexpr int kMaxMB = 4;            // 16-row MFMA blocks per GEMM group (<= 64 rows)
 constexpr int kMaxGroups = 48;       // GEMM groups per launch
 constexpr int kSplitRows = 512;      // rows of one split-range wide GEMM launch
-// Wide GEMM launch shapes: 4 column tiles per wave (unsplit or split by k
-// range), or 2 tiles per wave (unsplit).
-enum WideShape { WIDE_T4 = 0, WIDE_SPLIT = 1, WIDE_T2 = 2 };
+// Wide GEMM launch shapes: 4-wave blocks with 4 column tiles per wave
+// (unsplit or split by k range) or 2 tiles per wave (unsplit); 8-wave blocks
+// of 4 tiles per wave (512 columns, unsplit).
+enum WideShape { WIDE_T4 = 0, WIDE_SPLIT = 1, WIDE_T2 = 2, WIDE_W8 = 3 };
 constexpr int kAttnUnits = 16;       // (row, query head) units per attention work item (one MFMA tile)
 constexpr int kKvTile = 32;          // positions per K/V cache tile = keys per attention chunk
 #ifndef DEX_ATTN_SC
@@ -134,7 +135,11 @@ struct GemmArgs {
   float tau;
   const float* gumbel;   // [batch][gumbel_rows][N]
   int gumbel_rows;
-  float* part;      // [rows][N/16][3] partial top-2 per 16-column tile
+  float* part;      // [rows][N/16][3] top-2 summaries per 16-column tile (wide blocks: per column block)
+  int* cand;        // per (sequence, node slot): the token the rule chose ...
+  float* margin;    // ... and its top-1 minus top-2 margin
+  int P;            // node slots per sequence
+  unsigned* done;   // per group of the launch: blocks finished (the last one reduces, then resets it)
   // split-range wide GEMM: per k range r, scratch rows [r][kSplitRows][N] (fp32)
   float* split;
   int xcd_rows;     // wide GEMM block order: 1 row-shards the first ngroups - ngroups % 8 groups over

@@ -31,7 +31,6 @@ hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, i
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
 hipError_t launch_gemm_wide(const GemmArgs&, int, int, hipStream_t);
-hipError_t launch_head_reduce(const float*, int, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
@@ -74,6 +73,7 @@ struct WsPlan {
   size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh, xa, ssq_head, ad_vec;
   std::vector<size_t> wad1, wad2;  // packed inducing adapters, one per non-final explorer
   size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
+  size_t head_done;   // exit-head block counters, one per GEMM group of a launch (zero between launches)
   size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq, gemm_split;
   std::vector<size_t> wqkv, wo, wgu, wdown;
   size_t total;
@@ -185,6 +185,7 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.dbg_u = lay.take(B * kMaxN * 4);
   w.dbg_m = lay.take(B * kMaxN * 4);
   w.Xd = lay.take(kMaxN * 4);
+  w.head_done = lay.take(kMaxGroups * 4);
   w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
   w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
   w.sbytes[SC_ROWS] = R * sizeof(RowInfo);
@@ -264,6 +265,7 @@ struct dex_ctx {
   float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q;
   float *attn_part, *attn_tail, *head_part, *ssq, *gemm_split;
   int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
+  unsigned* head_done;
   RowInfo* rows;
   SeqPlan* plans;
   AttnItem* items;
@@ -375,6 +377,21 @@ constexpr int kWideRows = DEX_WIDE_ROWS;
 #define DEX_XCD_ROWS 1
 #endif
 constexpr int kXcdRows = DEX_XCD_ROWS;
+// 8-wave blocks (64 rows x 512 columns, one block per CU) halve the
+// activation re-reads of the 4-wave ones (each block reads its rows'
+// activations once per K pass); a launch uses them when it still has this
+// many blocks. Measured (three runs each, library variants): 13B-shaped batch
+// 8 320.7 -> 342.5 tokens/s, GQA batch 16 179.4 -> 189.2, 7B sampled 209.2 ->
+// 213.5, 7B greedy 270.2 -> 273.6; thresholds from 1 to 128 blocks measured
+// the same, 256 and 512 less.
+#ifndef DEX_W8_MIN_BLOCKS
+#define DEX_W8_MIN_BLOCKS 128
+#endif
+constexpr int kW8MinBlocks = DEX_W8_MIN_BLOCKS;
+#ifndef DEX_W8_HEAD
+#define DEX_W8_HEAD 1
+#endif
+constexpr int kW8Head = DEX_W8_HEAD;
 template <typename T>
 hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, int split_cols,
                          hipStream_t st, int* launches) {
@@ -394,6 +411,9 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
           int shape = WIDE_T4;
           if (blocks4 < 128 && rows <= kSplitRows && ga.N <= split_cols) shape = WIDE_SPLIT;
           else if (blocks4 < 384) shape = WIDE_T2;
+          if (shape != WIDE_SPLIT && (epi != EPI_HEAD || kW8Head) &&
+              ga.ngroups * ((ga.N / 16 + 31) / 32) >= kW8MinBlocks)
+            shape = WIDE_W8;
           ga.xcd_rows = shape != WIDE_SPLIT && kXcdRows;
           e = launch_gemm_wide(ga, epi, shape, st);
           *launches += shape == WIDE_SPLIT ? 2 : 1;
@@ -710,6 +730,10 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
   ga.gumbel = ctx->opt.gumbel;
   ga.gumbel_rows = ctx->opt.gumbel_rows;
   ga.part = ctx->head_part;
+  ga.cand = ctx->cand;
+  ga.margin = ctx->margin;
+  ga.P = D.P;
+  ga.done = ctx->head_done;
   const double es = sizeof(T);
   const int mk = prof_begin(ctx, DEX_PROF_HEAD);
   int launches = 0, nrows = 0;
@@ -721,11 +745,6 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
   }
   ga.split = ctx->gemm_split;
   HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches));
-  for (const auto& rg : ranges) {
-    HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, rg.first, rg.second, ctx->rows, D.P, ctx->cand, ctx->margin,
-                              st));
-    ++launches;
-  }
   prof_end(ctx, mk, launches, (double)D.V * D.d * es + (double)nrows * D.d * 4 + (double)nrows * (D.V / 16) * 12 * 2,
            2.0 * nrows * D.V * D.d);
   return DEX_OK;
@@ -1145,6 +1164,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->dbg_u = (int*)ctx->at(wp.dbg_u);
   ctx->dbg_m = (float*)ctx->at(wp.dbg_m);
   ctx->Xd = (int*)ctx->at(wp.Xd);
+  ctx->head_done = (unsigned*)ctx->at(wp.head_done);
   ctx->dbg_logits = (opt->debug & 1) ? (float*)ctx->at(wp.dbg_logits) : nullptr;
   ctx->rows = (RowInfo*)ctx->at(wp.rows);
   ctx->plans = (SeqPlan*)ctx->at(wp.plans);
@@ -1185,9 +1205,12 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
     }
   int xd[kMaxN] = {0};
   for (int k = 0; k < n_x; ++k) xd[k] = X[k];
+  // the exit head's block counters start at zero; each launch leaves them there
+  const unsigned zeros[kMaxGroups] = {0};
   if (hipMemcpy(ctx->cosT, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->sinT, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->Xd, xd, sizeof(xd), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(ctx->head_done, zeros, sizeof(zeros), hipMemcpyHostToDevice) != hipSuccess ||
       hipStreamSynchronize(ctx->st) != hipSuccess) {
     ctx->err = "upload of tables failed";
     return fail(DEX_EHIP);

@@ -132,6 +132,59 @@ __device__ __forceinline__ void rope_pair(float x1, float x2, float cs, float sn
   o2 = fmaf(x2, cs, x1 * sn);
 }
 
+// Exact merge of two (best, index, second) summaries: ties keep the lower id.
+// The merge only compares and selects, so any order of merges gives the same
+// summary: the rule's token and margin do not depend on how the tiles are
+// grouped or which block reduces them.
+__device__ __forceinline__ void top2_merge(float& b, int& i, float& s, float b2, int i2, float s2) {
+  if (b2 > b || (b2 == b && i2 < i)) {
+    s = fmaxf(s2, b);
+    b = b2;
+    i = i2;
+  } else {
+    s = fmaxf(s, b2);
+  }
+}
+
+// End of an exit-head block. Every block of group gi has written its rows'
+// summaries (nent per row, at part[row][0 .. nent)); the block that finishes
+// last, found with a device-scope vector atomic on the group's counter, merges
+// each row's summaries into the row's token and margin (one wave per row,
+// lanes over the summaries, then a butterfly) and resets the counter for the
+// next launch. NT threads, nblocks blocks per group.
+template <int NT>
+__device__ __forceinline__ void head_finish(const GemmArgs& args, const GemmGroup& G, int gi, unsigned nblocks,
+                                            int nent) {
+  __shared__ unsigned is_last;
+  __threadfence();   // this block's summaries are visible to every block
+  __syncthreads();
+  if (threadIdx.x == 0) is_last = atomicAdd(args.done + gi, 1u) == nblocks - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!is_last) return;
+  __threadfence();   // and every other block's are visible here
+  const int ntiles = args.N >> 4, lane = threadIdx.x & 63;
+  for (int rl = threadIdx.x >> 6; rl < G.m; rl += NT / 64) {
+    const int row = G.row0 + rl;
+    const float* p = args.part + (size_t)row * ntiles * 3;
+    float b = -INFINITY, s = -INFINITY;
+    int i = 0x7fffffff;
+    for (int t = lane; t < nent; t += 64) top2_merge(b, i, s, p[3 * t], __float_as_int(p[3 * t + 1]), p[3 * t + 2]);
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float b2 = __shfl_xor(b, off);
+      const int i2 = __shfl_xor(i, off);
+      const float s2 = __shfl_xor(s, off);
+      top2_merge(b, i, s, b2, i2, s2);
+    }
+    if (lane == 0) {
+      const RowInfo& ri = args.rows[row];
+      if (i < 0 || i >= args.N) i = 0;  // unreachable for finite logits; keeps token ids in range
+      args.cand[ri.seq * args.P + ri.phys] = i;
+      args.margin[ri.seq * args.P + ri.phys] = b - s;
+    }
+  }
+  if (threadIdx.x == 0) args.done[gi] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue of one 16-column output tile for rows [0, G.m) of group G. val(rl, c)
 // is the GEMM output of row rl, tile column c (before rstd); rs[rl] the row's
@@ -412,16 +465,19 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(MB
     epilogue_tile<EPI, kGemmThreads, MB * 16>(args, G, tile0 + nb, total, rs_sh, scr);
     if (NB > 1) __syncthreads();
   }
+  if constexpr (EPI == EPI_HEAD) head_finish<kGemmThreads>(args, G, gi, gridDim.x, ntiles);
 }
 
 // ---------------------------------------------------------------------------
 // Wide GEMM for groups of many rows (bf16 weights). 1-D grid of (group, column
-// block[, k range]) blocks, block = 4 waves; a block computes 64 rows x 4 WT
-// column tiles, wave w the WT tiles from WT w (WT does not change any output's
-// bits, only the block count). Each k-step's
-// activations (64 rows x 32, fp32) are split once into bf16 (hi, lo) and
-// stored in LDS in MFMA operand order, shared by the four waves; global loads
-// run three k-steps ahead in registers. Each output is reduced exactly as in
+// block[, k range]) blocks, block = NWV waves (4, or 8 for one block of 512
+// columns per CU); a block computes 64 rows x NWV WT column tiles, wave w the
+// WT tiles from WT w (WT and NWV do not change any output's bits, only the
+// block count). Each k-step's activations (64 rows x 32, fp32) are split once
+// into bf16 (hi, lo) by the first four waves and stored in LDS in MFMA operand
+// order, shared by all waves, so a block reads its rows' activations once per
+// K pass whatever its width; global loads run three k-steps ahead in
+// registers. Each output is reduced exactly as in
 // gemm_kernel: the 8 k ranges [KS r/8, KS (r+1)/8) are accumulated from zero
 // by the same MFMA chain (hi then lo per k-step), in order, and summed in
 // range order, so a row gets the same bits from either kernel and from any
@@ -437,72 +493,86 @@ constexpr int kWideThreads = 256;
 // rows (before rstd). Lane l of each of the NW waves takes row l, and wave w
 // the tiles w, w + NW, ...: the row's data is read once, and each tile's 16
 // columns are scanned in column order exactly as in epilogue_tile (same mask,
-// noise and top-2 arithmetic, so the summaries carry the same bits). With a
-// row per lane and a row pitch of 4 banks, the 16-byte LDS reads of a wave
-// fall on distinct banks.
+// noise and top-2 arithmetic). With a row per lane and a row pitch of 4 banks,
+// the 16-byte LDS reads of a wave fall on distinct banks. The lane merges its
+// tiles' summaries, the NW waves' summaries of a row meet in LDS (hs), and the
+// block writes one summary per row, at part[row][column block]. All threads
+// call it (it synchronises).
 template <int BT, int NW>
-__device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0,
-                                                   const float (*t)[BT * 16 + 4], const float* rs) {
+__device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0, int cb,
+                                                   const float (*t)[BT * 16 + 4], const float* rs,
+                                                   float (*hs)[64][3]) {
   const int ntiles = args.N >> 4;
   const int rl = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (rl >= G.m) return;
-  const RowInfo& ri = args.rows[G.row0 + rl];
-  const bool fin = ri.final_ != 0;
-  const float rsl = rs[rl];
-  float* outp = args.out != nullptr && fin ? args.out + (size_t)ri.seq * args.N : nullptr;
-  const float* gum = args.mode == 1 ? args.gumbel + ((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N : nullptr;
-  // Whether a masked token falls in the block's columns at all (a row masks at
-  // most N - 1 tokens, so nearly every block has none).
-  const int nm = fin ? 0 : ri.n_mask;
-  bool hit = false;
-  for (int i = 0; i < nm; ++i) hit |= ri.mask[i] >= tb0 * 16 && ri.mask[i] < (tb0 + BT) * 16;
-  float* part = args.part + ((size_t)(G.row0 + rl) * ntiles) * 3;
-  for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
-    const int n0 = (tb0 + tl) * 16;
-    float s[16];
-#pragma unroll
-    for (int c = 0; c < 16; c += 4) {
-      const float4 v = *(const float4*)&t[rl][tl * 16 + c];
-      s[c] = v.x * rsl;
-      s[c + 1] = v.y * rsl;
-      s[c + 2] = v.z * rsl;
-      s[c + 3] = v.w * rsl;
-    }
-    if (outp != nullptr) {
-#pragma unroll
-      for (int c = 0; c < 16; c += 4) *(float4*)(outp + n0 + c) = float4{s[c], s[c + 1], s[c + 2], s[c + 3]};
-    }
-    if (hit) {
-      for (int i = 0; i < nm; ++i) {
-        const int m = ri.mask[i] - n0;
-#pragma unroll
-        for (int c = 0; c < 16; ++c)
-          if (m == c) s[c] = -INFINITY;
-      }
-    }
-    if (gum != nullptr) {
+  float hb = -INFINITY, hsec = -INFINITY;
+  int hi = 0x7fffffff;
+  if (rl < G.m) {
+    const RowInfo& ri = args.rows[G.row0 + rl];
+    const bool fin = ri.final_ != 0;
+    const float rsl = rs[rl];
+    float* outp = args.out != nullptr && fin ? args.out + (size_t)ri.seq * args.N : nullptr;
+    const float* gum = args.mode == 1 ? args.gumbel + ((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N : nullptr;
+    // Whether a masked token falls in the block's columns at all (a row masks at
+    // most N - 1 tokens, so nearly every block has none).
+    const int nm = fin ? 0 : ri.n_mask;
+    bool hit = false;
+    for (int i = 0; i < nm; ++i) hit |= ri.mask[i] >= tb0 * 16 && ri.mask[i] < (tb0 + BT) * 16;
+    for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
+      const int n0 = (tb0 + tl) * 16;
+      float s[16];
 #pragma unroll
       for (int c = 0; c < 16; c += 4) {
-        const float4 g = *(const float4*)(gum + n0 + c);
-        s[c] = s[c] / args.tau + g.x;
-        s[c + 1] = s[c + 1] / args.tau + g.y;
-        s[c + 2] = s[c + 2] / args.tau + g.z;
-        s[c + 3] = s[c + 3] / args.tau + g.w;
+        const float4 v = *(const float4*)&t[rl][tl * 16 + c];
+        s[c] = v.x * rsl;
+        s[c + 1] = v.y * rsl;
+        s[c + 2] = v.z * rsl;
+        s[c + 3] = v.w * rsl;
       }
-    }
-    float best = s[0], second = -INFINITY;
-    int bi = 0;
+      if (outp != nullptr) {
 #pragma unroll
-    for (int c = 1; c < 16; ++c) {
-      const bool gt = s[c] > best;
-      second = gt ? best : (s[c] > second ? s[c] : second);
-      bi = gt ? c : bi;
-      best = gt ? s[c] : best;
+        for (int c = 0; c < 16; c += 4) *(float4*)(outp + n0 + c) = float4{s[c], s[c + 1], s[c + 2], s[c + 3]};
+      }
+      if (hit) {
+        for (int i = 0; i < nm; ++i) {
+          const int m = ri.mask[i] - n0;
+#pragma unroll
+          for (int c = 0; c < 16; ++c)
+            if (m == c) s[c] = -INFINITY;
+        }
+      }
+      if (gum != nullptr) {
+#pragma unroll
+        for (int c = 0; c < 16; c += 4) {
+          const float4 g = *(const float4*)(gum + n0 + c);
+          s[c] = s[c] / args.tau + g.x;
+          s[c + 1] = s[c + 1] / args.tau + g.y;
+          s[c + 2] = s[c + 2] / args.tau + g.z;
+          s[c + 3] = s[c + 3] / args.tau + g.w;
+        }
+      }
+      float best = s[0], second = -INFINITY;
+      int bi = 0;
+#pragma unroll
+      for (int c = 1; c < 16; ++c) {
+        const bool gt = s[c] > best;
+        second = gt ? best : (s[c] > second ? s[c] : second);
+        bi = gt ? c : bi;
+        best = gt ? s[c] : best;
+      }
+      top2_merge(hb, hi, hsec, best, n0 + bi, second);
     }
-    float* p = part + (size_t)(tb0 + tl) * 3;
-    p[0] = best;
-    p[1] = __int_as_float(n0 + bi);
-    p[2] = second;
+  }
+  hs[w][rl][0] = hb;
+  hs[w][rl][1] = __int_as_float(hi);
+  hs[w][rl][2] = hsec;
+  __syncthreads();
+  if (w == 0 && rl < G.m) {
+#pragma unroll
+    for (int v = 1; v < NW; ++v) top2_merge(hb, hi, hsec, hs[v][rl][0], __float_as_int(hs[v][rl][1]), hs[v][rl][2]);
+    float* p = args.part + ((size_t)(G.row0 + rl) * ntiles + cb) * 3;
+    p[0] = hb;
+    p[1] = __int_as_float(hi);
+    p[2] = hsec;
   }
 }
 
@@ -649,10 +719,12 @@ __device__ __forceinline__ void resid_epilogue_wide(const GemmArgs& args, const 
   }
 }
 
-template <int EPI, bool SPLIT, int WT>
-__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs args) {
-  constexpr int BT = 4 * WT;   // 16-column tiles per block
-  constexpr int MBLK = 4;      // 16-row blocks per block (one per wave)
+template <int EPI, bool SPLIT, int WT, int NWV>
+__global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args) {
+  constexpr int NT = NWV * 64;  // threads: NWV waves, each WT column tiles of the block's 64 rows
+  constexpr int BT = NWV * WT;  // 16-column tiles per block
+  constexpr int MBLK = 4;      // 16-row blocks per block (the first four waves stage them)
+  static_assert(NWV == 4 || (NWV == 8 && !SPLIT), "4 waves, or 8 unsplit");
   constexpr int ROWS = 16 * MBLK;
   constexpr int DEPTH = 3;     // k-steps of loads in flight
   constexpr int KSTEP = 32;
@@ -697,10 +769,11 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   __shared__ float rs_sh[ROWS];
   __shared__ float scr[SPLIT || EPI != EPI_ADAPT2 ? 1 : ROWS][17];
 
-  // Thread (w, lane) converts the fragment that lane `lane` of row block w
-  // reads. Rows past the group's end repeat its first row and tiles past N the
-  // last tile: their outputs are never stored.
-  const int ar = 16 * w + col16;
+  // Thread (w, lane) of the first four waves converts the fragment that lane
+  // `lane` of row block w reads. Rows past the group's end repeat its first
+  // row and tiles past N the last tile: their outputs are never stored.
+  const bool conv = w < MBLK;
+  const int ar = 16 * (conv ? w : 0) + col16;
   const int rr = ar < G.m ? ar : 0;
   const float* asrc = (NORM ? args.xin + (size_t)args.rows[G.row0 + rr].hrow * K
                             : (const float*)args.a + (size_t)(G.row0 + rr) * K) + 8 * kg;
@@ -732,20 +805,22 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   // staged, the weight loads once the MFMAs have read p.b.
   auto step = [&](int ks, Pre& p, f32x4_t (&acc)[MBLK][WT]) {
     const int buf = ks & 1;
-    u32x4_t hv, lv;
+    if (conv) {
+      u32x4_t hv, lv;
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      unsigned h0, l0, h1, l1;
-      split_bf2(p.a[x][0], p.a[x][1], h0, l0);
-      split_bf2(p.a[x][2], p.a[x][3], h1, l1);
-      hv[2 * x] = h0;
-      hv[2 * x + 1] = h1;
-      lv[2 * x] = l0;
-      lv[2 * x + 1] = l1;
+      for (int x = 0; x < 2; ++x) {
+        unsigned h0, l0, h1, l1;
+        split_bf2(p.a[x][0], p.a[x][1], h0, l0);
+        split_bf2(p.a[x][2], p.a[x][3], h1, l1);
+        hv[2 * x] = h0;
+        hv[2 * x + 1] = h1;
+        lv[2 * x] = l0;
+        lv[2 * x + 1] = l1;
+      }
+      sm.s.f[buf][0][w][lane] = hv;
+      sm.s.f[buf][1][w][lane] = lv;
+      load_a(ks + DEPTH, p);
     }
-    sm.s.f[buf][0][w][lane] = hv;
-    sm.s.f[buf][1][w][lane] = lv;
-    load_a(ks + DEPTH, p);
     __syncthreads();
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
@@ -779,7 +854,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   Pre p[DEPTH];
 #pragma unroll
   for (int i = 0; i < DEPTH; ++i) {
-    load_a(ks + i, p[i]);
+    if (conv) load_a(ks + i, p[i]);
     load_b(ks + i, p[i]);
   }
   auto close = [&](int k) {
@@ -826,7 +901,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
   }
   if constexpr (NORM) {
     const int nt = K >> 4;
-    for (int rl = w; rl < G.m; rl += kWideThreads / 64) {
+    for (int rl = w; rl < G.m; rl += NWV) {
       const float* sq = args.ssq + (size_t)args.rows[G.row0 + rl].hrow * nt;
       float s = 0.f;
       for (int t = lane; t < nt; t += 64) s += sq[t];
@@ -843,15 +918,17 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(const GemmArgs 
       for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * WT + nb) * 16 + col16] = tot[mb][nb][r];
   __syncthreads();
   if constexpr (EPI == EPI_HEAD) {
-    head_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
+    __shared__ float hs[NWV][64][3];
+    head_epilogue_wide<BT, NWV>(args, G, tb0, cb, sm.o.t, rs_sh, hs);
+    head_finish<NT>(args, G, gi, (unsigned)ncb, ncb);
   } else if constexpr (EPI == EPI_RESID) {
-    resid_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t);
+    resid_epilogue_wide<BT, NWV>(args, G, tb0, sm.o.t);
   } else if constexpr (EPI == EPI_QKV) {
-    qkv_epilogue_wide<BT, kWideThreads / 64>(args, G, tb0, sm.o.t, rs_sh);
+    qkv_epilogue_wide<BT, NWV>(args, G, tb0, sm.o.t, rs_sh);
   } else {
     // Only the adapter's second layer uses scr, so only it waits between tiles.
     for (int tl = 0; tl < BT && tb0 + tl < ntiles; ++tl) {
-      epilogue_tile<EPI, kWideThreads, ROWS>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
+      epilogue_tile<EPI, NT, ROWS>(args, G, tb0 + tl, [&](int rl, int c) { return sm.o.t[rl][tl * 16 + c]; },
                                            rs_sh, scr);
       if constexpr (EPI == EPI_ADAPT2) __syncthreads();
     }
@@ -890,46 +967,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_split_reduce_kernel(const G
   }
   __syncthreads();
   epilogue_tile<EPI, kWideThreads, 64>(args, G, tile, [&](int rl, int c) { return val[rl][c]; }, rs_sh, scr);
-}
-
-// Exact merge of two (best, index, second) summaries: ties keep the lower id.
-__device__ __forceinline__ void top2_merge(float& b, int& i, float& s, float b2, int i2, float s2) {
-  if (b2 > b || (b2 == b && i2 < i)) {
-    s = fmaxf(s2, b);
-    b = b2;
-    i = i2;
-  } else {
-    s = fmaxf(s, b2);
-  }
-}
-
-// One wave per row of [row0, row0 + nrows): reduce the per-tile summaries to
-// the row's token and margin.
-__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int row0, int nrows,
-                                   const RowInfo* __restrict__ rows, int P, int* __restrict__ cand,
-                                   float* __restrict__ margin) {
-  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (idx >= nrows) return;
-  const int row = row0 + idx;
-  float b = -INFINITY, s = -INFINITY;
-  int i = 0x7fffffff;
-  for (int t = lane; t < ntiles; t += 64) {
-    const float* p = part + ((size_t)row * ntiles + t) * 3;
-    top2_merge(b, i, s, p[0], __float_as_int(p[1]), p[2]);
-  }
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float b2 = __shfl_xor(b, off);
-    const int i2 = __shfl_xor(i, off);
-    const float s2 = __shfl_xor(s, off);
-    top2_merge(b, i, s, b2, i2, s2);
-  }
-  if (lane == 0) {
-    const RowInfo& ri = rows[row];
-    if (i < 0 || i >= ntiles * 16) i = 0;  // unreachable for finite logits; keeps token ids in range
-    cand[ri.seq * P + ri.phys] = i;
-    margin[ri.seq * P + ri.phys] = b - s;
-  }
+  if constexpr (EPI == EPI_HEAD) head_finish<kWideThreads>(args, G, blockIdx.x, gridDim.y, args.N >> 4);
 }
 
 // Embedding gather for rows with tok >= 0 (prefill and autoregressive rows):
@@ -996,11 +1034,11 @@ static hipError_t launch_gemm_nb(const GemmArgs& a, int mb, hipStream_t st) {
   return launch_gemm_mb<T, 1, EPI>(a, mb, st);
 }
 
-template <int EPI, bool SPLIT, int WT>
+template <int EPI, bool SPLIT, int WT, int NWV = 4>
 static void wide_launch(const GemmArgs& a, hipStream_t st) {
-  const int ncb = (a.N / 16 + 4 * WT - 1) / (4 * WT);
+  const int ncb = (a.N / 16 + NWV * WT - 1) / (NWV * WT);
   const dim3 grid(a.ngroups * ncb * (SPLIT ? kKSplit : 1));
-  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT, WT>), grid, dim3(kWideThreads), 0, st, a);
+  hipLaunchKernelGGL((gemm_wide_kernel<EPI, SPLIT, WT, NWV>), grid, dim3(NWV * 64), 0, st, a);
   if (SPLIT) {
     hipLaunchKernelGGL((gemm_split_reduce_kernel<EPI>), dim3(a.ngroups, a.N / 16), dim3(kWideThreads), 0, st, a);
   }
@@ -1016,6 +1054,7 @@ template <int EPI>
 static void wide_launch_shape(const GemmArgs& a, int shape, hipStream_t st) {
   if (shape == WIDE_SPLIT) wide_launch<EPI, true, 4>(a, st);
   else if (shape == WIDE_T2) wide_launch<EPI, false, 2>(a, st);
+  else if (shape == WIDE_W8) wide_launch<EPI, false, 4, 8>(a, st);
   else wide_launch<EPI, false, 4>(a, st);
 }
 
@@ -1048,15 +1087,6 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 }
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
-
-hipError_t launch_head_reduce(const float* part, int ntiles, int row0, int nrows, const RowInfo* rows, int P,
-                              int* cand, float* margin, hipStream_t st) {
-  if (nrows == 0) return hipSuccess;
-  const int wpb = 4;
-  hipLaunchKernelGGL(head_reduce_kernel, dim3((nrows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, part,
-                     ntiles, row0, nrows, rows, P, cand, margin);
-  return hipGetLastError();
-}
 
 template <typename T>
 hipError_t launch_embed(const void* E, const RowInfo* rows, int row0, int nrows, float* hidden, float* xn,
