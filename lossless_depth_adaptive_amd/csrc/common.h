@@ -135,11 +135,7 @@ struct GemmArgs {
   float tau;
   const float* gumbel;   // [batch][gumbel_rows][N]
   int gumbel_rows;
-  float* part;      // [rows][N/16][3] top-2 summaries per 16-column tile (wide blocks: per column block)
-  int* cand;        // per (sequence, node slot): the token the rule chose ...
-  float* margin;    // ... and its top-1 minus top-2 margin
-  int P;            // node slots per sequence
-  unsigned* done;   // per group of the launch: blocks finished (the last one reduces, then resets it)
+  float* part;      // [rows][N/16][3] top-2 summaries per 16-column tile
   // split-range wide GEMM: per k range r, scratch rows [r][kSplitRows][N] (fp32)
   float* split;
   int xcd_rows;     // wide GEMM block order: 1 row-shards the first ngroups - ngroups % 8 groups over

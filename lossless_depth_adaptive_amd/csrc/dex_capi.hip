@@ -31,6 +31,7 @@ hipError_t launch_pack(void*, const void*, const void*, const void*, int, int, i
 template <typename T>
 hipError_t launch_gemm(const GemmArgs&, int, hipStream_t);
 hipError_t launch_gemm_wide(const GemmArgs&, int, int, hipStream_t);
+hipError_t launch_head_reduce(const float*, int, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
 int attn_chunk(int hd);
@@ -73,7 +74,6 @@ struct WsPlan {
   size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh, xa, ssq_head, ad_vec;
   std::vector<size_t> wad1, wad2;  // packed inducing adapters, one per non-final explorer
   size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
-  size_t head_done;   // exit-head block counters, one per GEMM group of a launch (zero between launches)
   size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq, gemm_split;
   std::vector<size_t> wqkv, wo, wgu, wdown;
   size_t total;
@@ -185,7 +185,6 @@ WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, cons
   w.dbg_u = lay.take(B * kMaxN * 4);
   w.dbg_m = lay.take(B * kMaxN * 4);
   w.Xd = lay.take(kMaxN * 4);
-  w.head_done = lay.take(kMaxGroups * 4);
   w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
   w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
   w.sbytes[SC_ROWS] = R * sizeof(RowInfo);
@@ -265,7 +264,6 @@ struct dex_ctx {
   float *norms, *cosT, *sinT, *hidden, *xn, *xh, *margin, *dbg_m, *dbg_logits, *q;
   float *attn_part, *attn_tail, *head_part, *ssq, *gemm_split;
   int *map, *cand, *freel, *cursor, *anchor, *anchors_in, *records, *promote, *dbg_u, *Xd;
-  unsigned* head_done;
   RowInfo* rows;
   SeqPlan* plans;
   AttnItem* items;
@@ -370,9 +368,8 @@ constexpr int kWideRows = DEX_WIDE_ROWS;
 // split-k groups apart; wide ones only with bf16 weights); ga carries
 // everything else. A wide launch that would have few blocks runs split by k
 // range when its rows fit the scratch (split_cols: the scratch's row length).
-// Unsplit wide launches row-shard their groups over the XCDs
-// (gemm_wide_kernel; the 13B-shaped batch-8 workload 326.6 -> 328.1 tokens/s,
-// two A/B passes of three runs each). Counts launches.
+// Unsplit wide launches may row-shard their groups over the XCDs (xcd_pays).
+// Counts launches.
 #ifndef DEX_XCD_ROWS
 #define DEX_XCD_ROWS 1
 #endif
@@ -392,14 +389,56 @@ constexpr int kW8MinBlocks = DEX_W8_MIN_BLOCKS;
 #define DEX_W8_HEAD 1
 #endif
 constexpr int kW8Head = DEX_W8_HEAD;
+// Groups of fewer than kWideRows rows join the wide launch when they are few
+// next to it (at most a quarter of its groups: batched rounds, where they
+// would otherwise stream their stages' weights in a serial split-k launch of
+// their own); 13B-shaped batch 8: 364 -> 373 tokens/s. Where they are many
+// (the batch-1 lattice's small stages) the split-k kernel is much cheaper:
+// merging them cost the 7B-shaped sampled workload 7%.
+#ifndef DEX_MERGE_SMALL
+#define DEX_MERGE_SMALL 1
+#endif
+
+// Whether a wide launch row-shards its groups over the XCDs (GemmArgs.xcd_rows):
+// it saves the activation re-reads of the sharded groups (each column block
+// after the first would read them again) and costs the weight reads of the
+// XCDs that hold groups of the same stage (each of them streams that stage's
+// weights). Taken when the saving is larger. Without the model, 13B-shaped
+// batch 8 preferred never (364 vs 354 tokens/s; both its layer GEMMs and its
+// exit head) and the GQA batch-16 exit head always (370 vs 403 ms per 60
+// rounds). Two passes each, tokens/s with the model / never / always: 13B
+// batch 8 373.9, 371.6 / 371.8, 372.6 / 369.0, 369.8; GQA batch 16 188.0,
+// 185.8 / 184.1, 184.4 / 187.0, 187.3.
+bool xcd_pays(const GemmArgs& ga, int bt, int es) {
+  const int Q = ga.ngroups & ~7;
+  if (Q == 0 || kXcdRows == 0) return false;
+  if (kXcdRows == 2) return true;
+  const int ncb = (ga.N / 16 + bt - 1) / bt;
+  double rows = 0;
+  for (int g = 0; g < Q; ++g) rows += ga.g[g].m;
+  const double saving = rows * ga.K * 4.0 * (ncb - 1);
+  const int gpx = Q / 8;
+  int per_xcd = 0, overall = 0;
+  for (int g = 0; g < Q; ++g) {
+    if (g == 0 || ga.g[g].w != ga.g[g - 1].w) ++overall;   // groups of a weight are consecutive
+    if (g % gpx == 0 || ga.g[g].w != ga.g[g - 1].w) ++per_xcd;
+  }
+  const double cost = (double)(per_xcd - overall) * ga.N * ga.K * es;
+  return saving > cost;
+}
+
 template <typename T>
 hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int epi, int split_cols,
                          hipStream_t st, int* launches) {
+  int nwide = 0, nsmall = 0;
+  for (const GemmGroup& g : groups) (g.m >= kWideRows ? nwide : nsmall)++;
+  const bool merge = DEX_MERGE_SMALL && std::is_same<T, bf16_t>::value && nsmall > 0 && 4 * nsmall <= nwide;
   for (int wide = 0; wide < 2; ++wide) {
     ga.ngroups = 0;
     int rows = 0;
     for (size_t i = 0; i <= groups.size(); ++i) {
-      const bool is_wide = std::is_same<T, bf16_t>::value && i < groups.size() && groups[i].m >= kWideRows;
+      const bool is_wide = std::is_same<T, bf16_t>::value && i < groups.size() &&
+                           (groups[i].m >= kWideRows || merge);
       const bool mine = i < groups.size() && is_wide == (wide == 1);
       const bool flush = i == groups.size() || ga.ngroups == kMaxGroups;
       if (flush && ga.ngroups) {
@@ -414,7 +453,8 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
           if (shape != WIDE_SPLIT && (epi != EPI_HEAD || kW8Head) &&
               ga.ngroups * ((ga.N / 16 + 31) / 32) >= kW8MinBlocks)
             shape = WIDE_W8;
-          ga.xcd_rows = shape != WIDE_SPLIT && kXcdRows;
+          ga.xcd_rows = shape != WIDE_SPLIT &&
+                        xcd_pays(ga, shape == WIDE_W8 ? 32 : shape == WIDE_T2 ? 8 : 16, (int)sizeof(T));
           e = launch_gemm_wide(ga, epi, shape, st);
           *launches += shape == WIDE_SPLIT ? 2 : 1;
         } else {
@@ -730,10 +770,6 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
   ga.gumbel = ctx->opt.gumbel;
   ga.gumbel_rows = ctx->opt.gumbel_rows;
   ga.part = ctx->head_part;
-  ga.cand = ctx->cand;
-  ga.margin = ctx->margin;
-  ga.P = D.P;
-  ga.done = ctx->head_done;
   const double es = sizeof(T);
   const int mk = prof_begin(ctx, DEX_PROF_HEAD);
   int launches = 0, nrows = 0;
@@ -745,6 +781,11 @@ int run_head(dex_ctx* ctx, const std::vector<std::pair<int, int>>& ranges) {
   }
   ga.split = ctx->gemm_split;
   HIPCHK(launch_groups<T>(ga, groups, EPI_HEAD, ctx->wp.split_cols, st, &launches));
+  for (const auto& rg : ranges) {
+    HIPCHK(launch_head_reduce(ctx->head_part, D.V / 16, rg.first, rg.second, ctx->rows, D.P, ctx->cand, ctx->margin,
+                              st));
+    ++launches;
+  }
   prof_end(ctx, mk, launches, (double)D.V * D.d * es + (double)nrows * D.d * 4 + (double)nrows * (D.V / 16) * 12 * 2,
            2.0 * nrows * D.V * D.d);
   return DEX_OK;
@@ -1164,7 +1205,6 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   ctx->dbg_u = (int*)ctx->at(wp.dbg_u);
   ctx->dbg_m = (float*)ctx->at(wp.dbg_m);
   ctx->Xd = (int*)ctx->at(wp.Xd);
-  ctx->head_done = (unsigned*)ctx->at(wp.head_done);
   ctx->dbg_logits = (opt->debug & 1) ? (float*)ctx->at(wp.dbg_logits) : nullptr;
   ctx->rows = (RowInfo*)ctx->at(wp.rows);
   ctx->plans = (SeqPlan*)ctx->at(wp.plans);
@@ -1205,12 +1245,9 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
     }
   int xd[kMaxN] = {0};
   for (int k = 0; k < n_x; ++k) xd[k] = X[k];
-  // the exit head's block counters start at zero; each launch leaves them there
-  const unsigned zeros[kMaxGroups] = {0};
   if (hipMemcpy(ctx->cosT, cs.data(), cs.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->sinT, sn.data(), sn.size() * 4, hipMemcpyHostToDevice) != hipSuccess ||
       hipMemcpy(ctx->Xd, xd, sizeof(xd), hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(ctx->head_done, zeros, sizeof(zeros), hipMemcpyHostToDevice) != hipSuccess ||
       hipStreamSynchronize(ctx->st) != hipSuccess) {
     ctx->err = "upload of tables failed";
     return fail(DEX_EHIP);

@@ -146,45 +146,6 @@ __device__ __forceinline__ void top2_merge(float& b, int& i, float& s, float b2,
   }
 }
 
-// End of an exit-head block. Every block of group gi has written its rows'
-// summaries (nent per row, at part[row][0 .. nent)); the block that finishes
-// last, found with a device-scope vector atomic on the group's counter, merges
-// each row's summaries into the row's token and margin (one wave per row,
-// lanes over the summaries, then a butterfly) and resets the counter for the
-// next launch. NT threads, nblocks blocks per group.
-template <int NT>
-__device__ __forceinline__ void head_finish(const GemmArgs& args, const GemmGroup& G, int gi, unsigned nblocks,
-                                            int nent) {
-  __shared__ unsigned is_last;
-  __threadfence();   // this block's summaries are visible to every block
-  __syncthreads();
-  if (threadIdx.x == 0) is_last = atomicAdd(args.done + gi, 1u) == nblocks - 1 ? 1u : 0u;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();   // and every other block's are visible here
-  const int ntiles = args.N >> 4, lane = threadIdx.x & 63;
-  for (int rl = threadIdx.x >> 6; rl < G.m; rl += NT / 64) {
-    const int row = G.row0 + rl;
-    const float* p = args.part + (size_t)row * ntiles * 3;
-    float b = -INFINITY, s = -INFINITY;
-    int i = 0x7fffffff;
-    for (int t = lane; t < nent; t += 64) top2_merge(b, i, s, p[3 * t], __float_as_int(p[3 * t + 1]), p[3 * t + 2]);
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float b2 = __shfl_xor(b, off);
-      const int i2 = __shfl_xor(i, off);
-      const float s2 = __shfl_xor(s, off);
-      top2_merge(b, i, s, b2, i2, s2);
-    }
-    if (lane == 0) {
-      const RowInfo& ri = args.rows[row];
-      if (i < 0 || i >= args.N) i = 0;  // unreachable for finite logits; keeps token ids in range
-      args.cand[ri.seq * args.P + ri.phys] = i;
-      args.margin[ri.seq * args.P + ri.phys] = b - s;
-    }
-  }
-  if (threadIdx.x == 0) args.done[gi] = 0u;
-}
-
 // ---------------------------------------------------------------------------
 // Epilogue of one 16-column output tile for rows [0, G.m) of group G. val(rl, c)
 // is the GEMM output of row rl, tile column c (before rstd); rs[rl] the row's
@@ -465,7 +426,6 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(MB
     epilogue_tile<EPI, kGemmThreads, MB * 16>(args, G, tile0 + nb, total, rs_sh, scr);
     if (NB > 1) __syncthreads();
   }
-  if constexpr (EPI == EPI_HEAD) head_finish<kGemmThreads>(args, G, gi, gridDim.x, ntiles);
 }
 
 // ---------------------------------------------------------------------------
@@ -493,86 +453,72 @@ constexpr int kWideThreads = 256;
 // rows (before rstd). Lane l of each of the NW waves takes row l, and wave w
 // the tiles w, w + NW, ...: the row's data is read once, and each tile's 16
 // columns are scanned in column order exactly as in epilogue_tile (same mask,
-// noise and top-2 arithmetic). With a row per lane and a row pitch of 4 banks,
-// the 16-byte LDS reads of a wave fall on distinct banks. The lane merges its
-// tiles' summaries, the NW waves' summaries of a row meet in LDS (hs), and the
-// block writes one summary per row, at part[row][column block]. All threads
-// call it (it synchronises).
+// noise and top-2 arithmetic, so the summaries carry the same bits). With a
+// row per lane and a row pitch of 4 banks, the 16-byte LDS reads of a wave
+// fall on distinct banks.
 template <int BT, int NW>
-__device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0, int cb,
-                                                   const float (*t)[BT * 16 + 4], const float* rs,
-                                                   float (*hs)[64][3]) {
+__device__ __forceinline__ void head_epilogue_wide(const GemmArgs& args, const GemmGroup& G, int tb0,
+                                                   const float (*t)[BT * 16 + 4], const float* rs) {
   const int ntiles = args.N >> 4;
   const int rl = threadIdx.x & 63, w = threadIdx.x >> 6;
-  float hb = -INFINITY, hsec = -INFINITY;
-  int hi = 0x7fffffff;
-  if (rl < G.m) {
-    const RowInfo& ri = args.rows[G.row0 + rl];
-    const bool fin = ri.final_ != 0;
-    const float rsl = rs[rl];
-    float* outp = args.out != nullptr && fin ? args.out + (size_t)ri.seq * args.N : nullptr;
-    const float* gum = args.mode == 1 ? args.gumbel + ((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N : nullptr;
-    // Whether a masked token falls in the block's columns at all (a row masks at
-    // most N - 1 tokens, so nearly every block has none).
-    const int nm = fin ? 0 : ri.n_mask;
-    bool hit = false;
-    for (int i = 0; i < nm; ++i) hit |= ri.mask[i] >= tb0 * 16 && ri.mask[i] < (tb0 + BT) * 16;
-    for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
-      const int n0 = (tb0 + tl) * 16;
-      float s[16];
+  if (rl >= G.m) return;
+  const RowInfo& ri = args.rows[G.row0 + rl];
+  const bool fin = ri.final_ != 0;
+  const float rsl = rs[rl];
+  float* outp = args.out != nullptr && fin ? args.out + (size_t)ri.seq * args.N : nullptr;
+  const float* gum = args.mode == 1 ? args.gumbel + ((size_t)ri.seq * args.gumbel_rows + ri.grow) * args.N : nullptr;
+  // Whether a masked token falls in the block's columns at all (a row masks at
+  // most N - 1 tokens, so nearly every block has none).
+  const int nm = fin ? 0 : ri.n_mask;
+  bool hit = false;
+  for (int i = 0; i < nm; ++i) hit |= ri.mask[i] >= tb0 * 16 && ri.mask[i] < (tb0 + BT) * 16;
+  float* part = args.part + ((size_t)(G.row0 + rl) * ntiles) * 3;
+  for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
+    const int n0 = (tb0 + tl) * 16;
+    float s[16];
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+      const float4 v = *(const float4*)&t[rl][tl * 16 + c];
+      s[c] = v.x * rsl;
+      s[c + 1] = v.y * rsl;
+      s[c + 2] = v.z * rsl;
+      s[c + 3] = v.w * rsl;
+    }
+    if (outp != nullptr) {
+#pragma unroll
+      for (int c = 0; c < 16; c += 4) *(float4*)(outp + n0 + c) = float4{s[c], s[c + 1], s[c + 2], s[c + 3]};
+    }
+    if (hit) {
+      for (int i = 0; i < nm; ++i) {
+        const int m = ri.mask[i] - n0;
+#pragma unroll
+        for (int c = 0; c < 16; ++c)
+          if (m == c) s[c] = -INFINITY;
+      }
+    }
+    if (gum != nullptr) {
 #pragma unroll
       for (int c = 0; c < 16; c += 4) {
-        const float4 v = *(const float4*)&t[rl][tl * 16 + c];
-        s[c] = v.x * rsl;
-        s[c + 1] = v.y * rsl;
-        s[c + 2] = v.z * rsl;
-        s[c + 3] = v.w * rsl;
+        const float4 g = *(const float4*)(gum + n0 + c);
+        s[c] = s[c] / args.tau + g.x;
+        s[c + 1] = s[c + 1] / args.tau + g.y;
+        s[c + 2] = s[c + 2] / args.tau + g.z;
+        s[c + 3] = s[c + 3] / args.tau + g.w;
       }
-      if (outp != nullptr) {
-#pragma unroll
-        for (int c = 0; c < 16; c += 4) *(float4*)(outp + n0 + c) = float4{s[c], s[c + 1], s[c + 2], s[c + 3]};
-      }
-      if (hit) {
-        for (int i = 0; i < nm; ++i) {
-          const int m = ri.mask[i] - n0;
-#pragma unroll
-          for (int c = 0; c < 16; ++c)
-            if (m == c) s[c] = -INFINITY;
-        }
-      }
-      if (gum != nullptr) {
-#pragma unroll
-        for (int c = 0; c < 16; c += 4) {
-          const float4 g = *(const float4*)(gum + n0 + c);
-          s[c] = s[c] / args.tau + g.x;
-          s[c + 1] = s[c + 1] / args.tau + g.y;
-          s[c + 2] = s[c + 2] / args.tau + g.z;
-          s[c + 3] = s[c + 3] / args.tau + g.w;
-        }
-      }
-      float best = s[0], second = -INFINITY;
-      int bi = 0;
-#pragma unroll
-      for (int c = 1; c < 16; ++c) {
-        const bool gt = s[c] > best;
-        second = gt ? best : (s[c] > second ? s[c] : second);
-        bi = gt ? c : bi;
-        best = gt ? s[c] : best;
-      }
-      top2_merge(hb, hi, hsec, best, n0 + bi, second);
     }
-  }
-  hs[w][rl][0] = hb;
-  hs[w][rl][1] = __int_as_float(hi);
-  hs[w][rl][2] = hsec;
-  __syncthreads();
-  if (w == 0 && rl < G.m) {
+    float best = s[0], second = -INFINITY;
+    int bi = 0;
 #pragma unroll
-    for (int v = 1; v < NW; ++v) top2_merge(hb, hi, hsec, hs[v][rl][0], __float_as_int(hs[v][rl][1]), hs[v][rl][2]);
-    float* p = args.part + ((size_t)(G.row0 + rl) * ntiles + cb) * 3;
-    p[0] = hb;
-    p[1] = __int_as_float(hi);
-    p[2] = hsec;
+    for (int c = 1; c < 16; ++c) {
+      const bool gt = s[c] > best;
+      second = gt ? best : (s[c] > second ? s[c] : second);
+      bi = gt ? c : bi;
+      best = gt ? s[c] : best;
+    }
+    float* p = part + (size_t)(tb0 + tl) * 3;
+    p[0] = best;
+    p[1] = __int_as_float(n0 + bi);
+    p[2] = second;
   }
 }
 
@@ -918,9 +864,7 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
       for (int r = 0; r < 4; ++r) sm.o.t[mb * 16 + kg * 4 + r][(w * WT + nb) * 16 + col16] = tot[mb][nb][r];
   __syncthreads();
   if constexpr (EPI == EPI_HEAD) {
-    __shared__ float hs[NWV][64][3];
-    head_epilogue_wide<BT, NWV>(args, G, tb0, cb, sm.o.t, rs_sh, hs);
-    head_finish<NT>(args, G, gi, (unsigned)ncb, ncb);
+    head_epilogue_wide<BT, NWV>(args, G, tb0, sm.o.t, rs_sh);
   } else if constexpr (EPI == EPI_RESID) {
     resid_epilogue_wide<BT, NWV>(args, G, tb0, sm.o.t);
   } else if constexpr (EPI == EPI_QKV) {
@@ -967,7 +911,35 @@ __global__ __launch_bounds__(kWideThreads) void gemm_split_reduce_kernel(const G
   }
   __syncthreads();
   epilogue_tile<EPI, kWideThreads, 64>(args, G, tile, [&](int rl, int c) { return val[rl][c]; }, rs_sh, scr);
-  if constexpr (EPI == EPI_HEAD) head_finish<kWideThreads>(args, G, blockIdx.x, gridDim.y, args.N >> 4);
+}
+
+// One wave per row of [row0, row0 + nrows): reduce the per-tile summaries to
+// the row's token and margin.
+__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int row0, int nrows,
+                                   const RowInfo* __restrict__ rows, int P, int* __restrict__ cand,
+                                   float* __restrict__ margin) {
+  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (idx >= nrows) return;
+  const int row = row0 + idx;
+  float b = -INFINITY, s = -INFINITY;
+  int i = 0x7fffffff;
+  for (int t = lane; t < ntiles; t += 64) {
+    const float* p = part + ((size_t)row * ntiles + t) * 3;
+    top2_merge(b, i, s, p[0], __float_as_int(p[1]), p[2]);
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float b2 = __shfl_xor(b, off);
+    const int i2 = __shfl_xor(i, off);
+    const float s2 = __shfl_xor(s, off);
+    top2_merge(b, i, s, b2, i2, s2);
+  }
+  if (lane == 0) {
+    const RowInfo& ri = rows[row];
+    if (i < 0 || i >= ntiles * 16) i = 0;  // unreachable for finite logits; keeps token ids in range
+    cand[ri.seq * P + ri.phys] = i;
+    margin[ri.seq * P + ri.phys] = b - s;
+  }
 }
 
 // Embedding gather for rows with tok >= 0 (prefill and autoregressive rows):
@@ -1087,6 +1059,15 @@ hipError_t launch_gemm(const GemmArgs& a, int epi, hipStream_t st) {
 }
 template hipError_t launch_gemm<float>(const GemmArgs&, int, hipStream_t);
 template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
+
+hipError_t launch_head_reduce(const float* part, int ntiles, int row0, int nrows, const RowInfo* rows, int P,
+                              int* cand, float* margin, hipStream_t st) {
+  if (nrows == 0) return hipSuccess;
+  const int wpb = 4;
+  hipLaunchKernelGGL(head_reduce_kernel, dim3((nrows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, part,
+                     ntiles, row0, nrows, rows, P, cand, margin);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_embed(const void* E, const RowInfo* rows, int row0, int nrows, float* hidden, float* xn,
