@@ -5,6 +5,7 @@ The shared library lands next to this file; it is git-ignored but travels with
 the source tree.
 """
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -27,6 +28,21 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
 # VGPRs: the compiler otherwise rotates them through AGPRs with copies in every
 # k-step, or spills into AGPRs.
 SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in ("gemm.hip", "layer.hip")}
+
+
+def source_digest() -> str:
+    """SHA-256 over the library's sources (every file of csrc/, the public
+    header) and its compile flags: measurements taken on one build (counter
+    summaries) name it, so a later reader can tell whether they still describe
+    the kernels in the tree."""
+    h = hashlib.sha256()
+    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
+    for path in files + [os.path.join(INCLUDE, "dex.h")]:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h.update(repr((FLAGS, sorted(SOURCE_FLAGS.items()))).encode())
+    return h.hexdigest()[:16]
 
 
 def _hipcc():

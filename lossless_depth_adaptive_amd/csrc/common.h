@@ -140,6 +140,12 @@ struct GemmArgs {
   float* split;
   int xcd_rows;     // wide GEMM block order: 1 row-shards the first ngroups - ngroups % 8 groups over
                     // the XCDs (see gemm_wide_kernel); 0 puts every group of a column block on one XCD
+  // Unsplit wide GEMM, groups that are not row-sharded: runs of consecutive
+  // groups that share a weight, run r = groups [run0[r], run0[r + 1]); the
+  // blocks of a run are consecutive (column block slowest). nrun = 0: every
+  // group of a column block, then the next column block.
+  int nrun;
+  int run0[kMaxGroups + 1];
 };
 
 struct AttnItem {

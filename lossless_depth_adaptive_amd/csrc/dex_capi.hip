@@ -395,6 +395,13 @@ constexpr int kW8Head = DEX_W8_HEAD;
 // their own); 13B-shaped batch 8: 364 -> 373 tokens/s. Where they are many
 // (the batch-1 lattice's small stages) the split-k kernel is much cheaper:
 // merging them cost the 7B-shaped sampled workload 7%.
+// Unsplit wide launches order their blocks weight by weight (GemmArgs.nrun):
+// the 13B-shaped batch-8 layer GEMMs fetch 1.14x their algorithmic bytes
+// instead of 1.39x, in the same time within a percent.
+#ifndef DEX_STAGE_MAJOR
+#define DEX_STAGE_MAJOR 1
+#endif
+constexpr bool kStageMajor = DEX_STAGE_MAJOR != 0;
 #ifndef DEX_MERGE_SMALL
 #define DEX_MERGE_SMALL 1
 #endif
@@ -455,6 +462,13 @@ hipError_t launch_groups(GemmArgs& ga, const std::vector<GemmGroup>& groups, int
             shape = WIDE_W8;
           ga.xcd_rows = shape != WIDE_SPLIT &&
                         xcd_pays(ga, shape == WIDE_W8 ? 32 : shape == WIDE_T2 ? 8 : 16, (int)sizeof(T));
+          ga.nrun = 0;
+          if (kStageMajor && shape != WIDE_SPLIT) {
+            const int q0 = ga.xcd_rows ? ga.ngroups & ~7 : 0;
+            for (int g = q0; g < ga.ngroups; ++g)
+              if (g == q0 || ga.g[g].w != ga.g[g - 1].w) ga.run0[ga.nrun++] = g;
+            ga.run0[ga.nrun] = ga.ngroups;
+          }
           e = launch_gemm_wide(ga, epi, shape, st);
           *launches += shape == WIDE_SPLIT ? 2 : 1;
         } else {

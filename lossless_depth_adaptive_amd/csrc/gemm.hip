@@ -686,7 +686,10 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
   //    XCDs whose groups need it).
   //  * The other groups: the blocks that read one weight tile (the row groups
   //    of a column block) get consecutive logical ids on one XCD, so the tile
-  //    is fetched into that XCD's L2 once.
+  //    is fetched into that XCD's L2 once. With runs (nrun > 0), the groups
+  //    of one weight take all their column blocks before the next weight's
+  //    groups start, so an XCD works on one or two weights at a time and
+  //    keeps only their groups' activations in flight, not every group's.
   const int Q = !SPLIT && args.xcd_rows ? args.ngroups & ~7 : 0;
   int gi, cb, z = 0;
   if ((int)blockIdx.x < Q * ncb) {
@@ -696,9 +699,17 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
   } else {
     const int R = args.ngroups - Q;
     const int lb = xcd_block(blockIdx.x - Q * ncb, nblk - Q * ncb);
-    gi = Q + lb % R;
-    cb = (lb / R) % ncb;
-    z = SPLIT ? lb / (R * ncb) : 0;
+    if (!SPLIT && args.nrun > 0) {
+      int r = 0;
+      while (r + 1 < args.nrun && lb >= ncb * (args.run0[r + 1] - Q)) ++r;
+      const int g0 = args.run0[r], len = args.run0[r + 1] - g0, local = lb - ncb * (g0 - Q);
+      gi = g0 + local % len;
+      cb = local / len;
+    } else {
+      gi = Q + lb % R;
+      cb = (lb / R) % ncb;
+      z = SPLIT ? lb / (R * ncb) : 0;
+    }
   }
   const GemmGroup G = args.g[gi];
   const int tb0 = cb * BT;

@@ -1,9 +1,11 @@
 """Summaries of rocprofv3 result databases (rocpd SQLite) for the lattice step.
 
-  python -m lossless_depth_adaptive_amd.profsum trace RESULTS.db
+  python -m lossless_depth_adaptive_amd.profsum trace RESULTS.db [--bench-json B --command C]
       Per-kernel statistics of the decode window (from the first schedule or
       autoregressive-row kernel to the end of the trace): calls, mean and
-      total duration, share, plus the mean over every layer-GEMM dispatch.
+      total duration, share, plus the mean over every layer-GEMM dispatch;
+      with --bench-json, a header naming the workload, the command and what
+      the traced bench.py run printed.
 
   python -m lossless_depth_adaptive_amd.profsum traffic --fetch F.db --write W.db \
         --bench-json BENCH.json --out traffic.json
@@ -14,13 +16,16 @@
       bench.py timed with HIP events (the last roofline.launches of the decode
       window; run bench.py with --no-ar) and divided by their count; compared
       with the algorithmic bytes per launch the library reported for the same
-      rounds.
+      rounds. The summary names the library sources it was measured on
+      (build.source_digest); bench.py uses it only while they are unchanged.
 """
 
 import argparse
 import json
 import sqlite3
 import sys
+
+from .build import source_digest
 
 GIB = 1 << 30
 
@@ -60,6 +65,30 @@ def decode_window(rows):
         if "sched_kernel" in r[0] or "ar_rows_kernel" in r[0]:
             return rows[i:]
     return []
+
+
+def trace_header(bench_json: str, command: str) -> str:
+    """Header lines of a trace summary: the workload, the command that made
+    the database, and what the traced bench.py run printed."""
+    d = json.loads(open(bench_json).read().strip().splitlines()[-1])
+    c, rl = d["config"], d["roofline"]
+    out = [f"# Kernel trace: lattice step, workload {c['workload']} ({c.get('layers')} layers, d {c.get('d_model')}, "
+           f"X={c.get('X')}, batch {c.get('batch')}, prompts {c.get('prompt_len')}, {c.get('mode')})",
+           f"# library sources {source_digest()}",
+           "#",
+           "# Commands (repository root, MI355X, ROCm 7.2):",
+           "#   export TMPDIR=/tmp",
+           f"#   rocprofv3 --kernel-trace --stats -d D -o bench -- {command}",
+           "#   python3 -m lossless_depth_adaptive_amd.profsum trace D/bench_results.db --bench-json B.json "
+           "--command '...'   (B.json: what the traced command printed)",
+           "#",
+           f"# Window: {d['warmup']} warmup + {d['steps']} timed rounds (replayed HIP graphs) + {d['steps']} eagerly "
+           "profiled rounds, after prefill.",
+           f"# bench.py in this traced command: {d['value']} tokens/s; layer-GEMM class by HIP events over the eager "
+           f"rounds: {rl['mean_launch_us']:.1f} us per launch, {rl['algorithmic_bytes_per_launch'] / 1e6:.1f} MB "
+           f"algorithmic per launch, {rl['achieved']:.0f} GB/s ({rl['frac']:.3f} of 8 TB/s); the events also span "
+           "launch gaps."]
+    return "\n".join(out) + "\n"
 
 
 def trace_summary(db: str) -> str:
@@ -118,7 +147,7 @@ def traffic(fetch_db, write_db, bench_json, workload=None):
                 fetch_bytes_per_launch=fetch / n, write_bytes_per_launch=write / max(1, len(wg)),
                 bytes_per_launch=fetch / n + write / max(1, len(wg)),
                 algorithmic_bytes_per_launch=rl["algorithmic_bytes_per_launch"],
-                fetch_scale=f_scale, write_scale=w_scale,
+                fetch_scale=f_scale, write_scale=w_scale, library_sources=source_digest(),
                 note="layer GEMM launches (exit head excluded) of the HIP-event-timed rounds; counters in KiB "
                      "per dispatch scaled by a 1 GiB copy read/write in the same process")
 
@@ -128,6 +157,8 @@ def main(argv=None):
     sub = ap.add_subparsers(dest="cmd", required=True)
     t = sub.add_parser("trace")
     t.add_argument("db")
+    t.add_argument("--bench-json", help="what the traced bench.py command printed (adds a header)")
+    t.add_argument("--command", default="python3 bench.py ...", help="the traced command, for the header")
     r = sub.add_parser("traffic")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
@@ -136,6 +167,8 @@ def main(argv=None):
     r.add_argument("--out")
     a = ap.parse_args(argv)
     if a.cmd == "trace":
+        if a.bench_json:
+            sys.stdout.write(trace_header(a.bench_json, a.command))
         sys.stdout.write(trace_summary(a.db))
     else:
         res = traffic(a.fetch, a.write, a.bench_json, a.workload)
