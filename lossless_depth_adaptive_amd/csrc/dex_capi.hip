@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "dex.h"
+#include "plan.h"
 
 namespace dex {
 template <typename T>
@@ -34,8 +35,6 @@ hipError_t launch_gemm_wide(const GemmArgs&, int, int, hipStream_t);
 hipError_t launch_head_reduce(const float*, int, int, int, const RowInfo*, int, int*, float*, hipStream_t);
 template <typename T>
 hipError_t launch_embed(const void*, const RowInfo*, int, int, float*, float*, float*, const float*, int, hipStream_t);
-int attn_chunk(int hd);
-int attn_mix_slots();
 hipError_t launch_attention(const AttnItem*, int, const int*, int, int, int, const RowInfo*, int, const float*,
                             const bf16_t*,
                             const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, int,
@@ -57,161 +56,8 @@ using namespace dex;
 namespace {
 
 thread_local std::string g_create_error;
-constexpr int kPrefillRows = 512;
 constexpr size_t kMaxGraphs = 256;
 
-struct Layout {
-  size_t off = 0;
-  size_t take(size_t bytes) {
-    const size_t o = off;
-    off += (bytes + 255) & ~(size_t)255;
-    return o;
-  }
-};
-
-// Every buffer of the workspace, as byte offsets.
-struct WsPlan {
-  size_t embed, head, norms, cosT, sinT, kvc, exb, hidden, xn, xh, xa, ssq_head, ad_vec;
-  std::vector<size_t> wad1, wad2;  // packed inducing adapters, one per non-final explorer
-  size_t map, cand, margin, freel, cursor, anchor, anchors_in, records, promote, dbg_u, dbg_m, Xd, dbg_logits;
-  size_t rows, plans, items, q, attn_out, act, attn_part, attn_tail, head_part, ssq, gemm_split;
-  std::vector<size_t> wqkv, wo, wgu, wdown;
-  size_t total;
-  int Rmax, nchunk, split_cols;
-  size_t sbytes[10];   // bytes of the per-round scratch regions (ScratchRegion order)
-};
-
-// Per-round scratch regions of the workspace: written by a round before they
-// are read and never carried to the next round (plan staging, attention and
-// GEMM partial results, exit-head tile summaries). dex_step_noalloc takes
-// them from the static device array instead.
-enum ScratchRegion { SC_ROWS, SC_PLANS, SC_ITEMS, SC_Q, SC_ATTN_OUT, SC_ACT, SC_ATTN_PART, SC_ATTN_TAIL, SC_GEMM_SPLIT,
-                     SC_HEAD_PART, SC_N };
-
-size_t esize(int dtype) { return dtype == DEX_DTYPE_BF16 ? 2 : 4; }
-
-int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex_options* o, std::string& err) {
-  if (!c || !X || !o) { err = "null argument"; return DEX_EINVAL; }
-  if (c->n_layers < 1 || c->d_model < 16 || c->n_heads < 1 || c->n_kv_heads < 1 || c->d_ffn < 8 || c->vocab < 16) {
-    err = "non-positive model dimension"; return DEX_EINVAL;
-  }
-  if (c->dtype != DEX_DTYPE_F32 && c->dtype != DEX_DTYPE_BF16) { err = "dtype must be F32 or BF16"; return DEX_EINVAL; }
-  if (c->head_dim != 64 && c->head_dim != 128) { err = "head_dim must be 64 or 128"; return DEX_EINVAL; }
-  if (c->n_heads % c->n_kv_heads) { err = "n_heads must be a multiple of n_kv_heads"; return DEX_EINVAL; }
-  if (c->n_heads / c->n_kv_heads > kAttnUnits) { err = "too many query heads per kv head"; return DEX_EINVAL; }
-  const int kstep = c->dtype == DEX_DTYPE_BF16 ? 32 : 16;
-  if (c->d_model % kstep || (c->n_heads * c->head_dim) % kstep || c->d_ffn % kstep) {
-    err = "d_model, n_heads*head_dim and d_ffn must be multiples of the MFMA k-step (32 bf16, 16 fp32)";
-    return DEX_EINVAL;
-  }
-  if (c->d_model % 16 || c->vocab % 16 || c->d_ffn % 8) { err = "d_model and vocab must be multiples of 16, d_ffn of 8"; return DEX_EINVAL; }
-  if (!(c->rms_eps > 0) || !(c->rope_base > 1)) { err = "rms_eps and rope_base must be positive"; return DEX_EINVAL; }
-  if (n_x < 1 || n_x > kMaxN) { err = "number of exploration depths must be 1..10"; return DEX_EINVAL; }
-  if (c->adapter_hidden < 0 || c->adapter_hidden % (c->dtype == DEX_DTYPE_BF16 ? 32 : 16)) {
-    err = "adapter_hidden must be 0 or a positive multiple of the MFMA k-step (32 bf16, 16 fp32)";
-    return DEX_EINVAL;
-  }
-  for (int k = 0; k < n_x; ++k) {
-    if (X[k] < 1 || (k > 0 && X[k] <= X[k - 1])) { err = "exploration set must be strictly increasing within [1, L]"; return DEX_EINVAL; }
-  }
-  if (X[n_x - 1] != c->n_layers) { err = "the last exploration depth must equal L"; return DEX_EINVAL; }
-  if (o->max_batch < 1 || o->max_batch > 64) { err = "max_batch must be 1..64"; return DEX_EINVAL; }
-  if (o->max_context < 2) { err = "max_context must be at least 2"; return DEX_EINVAL; }
-  if (o->max_new_tokens < 1) { err = "max_new_tokens must be positive"; return DEX_EINVAL; }
-  if (o->mode != DEX_GREEDY && o->mode != DEX_SAMPLE) { err = "mode must be GREEDY or SAMPLE"; return DEX_EINVAL; }
-  if (o->single_exit != 0 && o->single_exit != 1) { err = "single_exit must be 0 or 1"; return DEX_EINVAL; }
-  if (o->branch_cap < 0 || o->branch_cap > n_x) { err = "branch_cap must be 0..N"; return DEX_EINVAL; }
-  if (o->single_exit && o->branch_cap) { err = "branch_cap and single_exit cannot be combined"; return DEX_EINVAL; }
-  if (o->mode == DEX_SAMPLE) {
-    if (!(o->temperature > 0)) { err = "temperature must be positive"; return DEX_EINVAL; }
-    if (!o->gumbel) { err = "sampling needs Gumbel rows"; return DEX_EINVAL; }
-    if (((uintptr_t)o->gumbel & 15) != 0) { err = "gumbel must be 16-byte aligned"; return DEX_EINVAL; }
-    if (o->gumbel_rows < o->max_new_tokens + n_x - 1) { err = "gumbel_rows must be >= max_new_tokens + N - 1"; return DEX_EINVAL; }
-  }
-  return DEX_OK;
-}
-
-// Layers of the longest stage: max over j of d_j - d_{j-1} (d_{-1} = 0).
-int longest_stage(const int32_t* X, int n_x) {
-  int s = 0;
-  for (int j = 0; j < n_x; ++j) s = std::max(s, X[j] - (j ? X[j - 1] : 0));
-  return s;
-}
-
-WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_x, const dex_options* o) {
-  WsPlan w;
-  Layout lay;
-  const size_t es = esize(c->dtype);
-  const size_t L = c->n_layers, d = c->d_model, nq = c->n_heads, nkv = c->n_kv_heads, hd = c->head_dim,
-               F = c->d_ffn, V = c->vocab, B = o->max_batch, Cmax = o->max_context;
-  const int N = n_x, S = longest_stage(X, n_x), P = (1 << N) - 1;
-  w.Rmax = std::max(std::max((int)B << (N - 1), kPrefillRows), (int)B);
-  w.nchunk = (int)((Cmax + attn_chunk((int)hd) - 1) / attn_chunk((int)hd));
-  const size_t Cs = (Cmax + kKvTile - 1) / kKvTile * kKvTile;
-  const size_t R = w.Rmax;
-  w.embed = lay.take(V * d * es);
-  w.head = lay.take(V * d * es);
-  for (size_t l = 0; l < L; ++l) {
-    w.wqkv.push_back(lay.take((nq + 2 * nkv) * hd * d * es));
-    w.wo.push_back(lay.take(d * nq * hd * es));
-    w.wgu.push_back(lay.take(2 * F * d * es));
-    w.wdown.push_back(lay.take(d * F * es));
-  }
-  w.norms = lay.take((2 * L + 1) * d * 4);
-  const size_t m = c->adapter_hidden;
-  for (int k = 0; m && k < N - 1; ++k) {
-    w.wad1.push_back(lay.take(m * d * es));
-    w.wad2.push_back(lay.take(d * m * es));
-  }
-  w.ad_vec = lay.take(m ? (size_t)(N - 1) * (m + 2 * d) * 4 : 0);   // per adapter: b1 [m], b2 [d], norm [d]
-  w.cosT = lay.take(Cmax * (hd / 2) * 4);
-  w.sinT = lay.take(Cmax * (hd / 2) * 4);
-  w.kvc = lay.take(B * L * nkv * Cs * hd * 8);            // K and V as bf16 (hi, lo) pairs
-  w.exb = lay.take(B * P * S * nkv * hd * 8);
-  w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
-  w.xn = lay.take((B * P + kPrefillRows) * d * 4);
-  w.xh = lay.take((B * P + kPrefillRows) * d * 4);
-  w.xa = lay.take(m ? (B * P + kPrefillRows) * d * 4 : 0);
-  w.ssq_head = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
-  w.map = lay.take(B * P * 4);
-  w.cand = lay.take(B * P * 4);
-  w.margin = lay.take(B * P * 4);
-  w.freel = lay.take(B * P * 4);
-  w.cursor = lay.take(B * 4);
-  w.anchor = lay.take(B * 4);
-  w.anchors_in = lay.take(B * 4);
-  w.records = lay.take(B * 5 * 4);
-  w.promote = lay.take(B * kMaxN * 4);
-  w.dbg_u = lay.take(B * kMaxN * 4);
-  w.dbg_m = lay.take(B * kMaxN * 4);
-  w.Xd = lay.take(kMaxN * 4);
-  w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
-  w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
-  w.sbytes[SC_ROWS] = R * sizeof(RowInfo);
-  w.sbytes[SC_PLANS] = B * sizeof(SeqPlan);
-  w.sbytes[SC_ITEMS] = R * (sizeof(AttnItem) + 12);   // items, then the attention block lists (3 R ints)
-  w.sbytes[SC_Q] = R * nq * hd * 4;
-  w.sbytes[SC_ATTN_OUT] = R * nq * hd * 4;
-  w.sbytes[SC_ACT] = R * std::max(F, m) * 4;
-  w.sbytes[SC_ATTN_PART] = R * nq * w.nchunk * (hd + 4) * 4;
-  w.sbytes[SC_ATTN_TAIL] = R * nq * attn_mix_slots() * (hd + 4) * 4;
-  // the split-range partials serve the wide (bf16) GEMM only
-  w.sbytes[SC_GEMM_SPLIT] = c->dtype == DEX_DTYPE_BF16 ? (size_t)kKSplit * kSplitRows * w.split_cols * 4 : 0;
-  w.sbytes[SC_HEAD_PART] = R * (V / 16) * 3 * 4;
-  w.rows = lay.take(w.sbytes[SC_ROWS]);
-  w.plans = lay.take(w.sbytes[SC_PLANS]);
-  w.items = lay.take(w.sbytes[SC_ITEMS]);
-  w.q = lay.take(w.sbytes[SC_Q]);
-  w.ssq = lay.take((B * P + kPrefillRows) * (d / 16) * 4);
-  w.attn_out = lay.take(w.sbytes[SC_ATTN_OUT]);
-  w.act = lay.take(w.sbytes[SC_ACT]);
-  w.attn_part = lay.take(w.sbytes[SC_ATTN_PART]);
-  w.attn_tail = lay.take(w.sbytes[SC_ATTN_TAIL]);
-  w.gemm_split = lay.take(w.sbytes[SC_GEMM_SPLIT]);
-  w.head_part = lay.take(w.sbytes[SC_HEAD_PART]);
-  w.total = lay.off;
-  return w;
-}
 
 }  // namespace
 
@@ -319,36 +165,12 @@ struct dex_ctx {
 
 namespace {
 
-// Attention blocks: the items of one (sequence, stage) are covered in groups of
-// up to kAttnGroup consecutive items; item i of n leads a group of this size (0:
-// inside a group).
-int attn_lead(int i, int n) { return i % kAttnGroup ? 0 : std::min(kAttnGroup, n - i); }
-
-// Attention block lists of the pass's first nitems items: the items that form
-// a group of their own (the shared-role blocks of attn_kernel), then the items
-// that lead a group of several (attn_group_kernel), then, for items whose rows
-// read explore keys, one entry 4 item + q per quarter q of the item's rows
-// (the per-row chunk blocks of attn_kernel, kAttnSC rows each), so that no
-// launch has blocks without work.
+// The attention block lists of the context's first nitems host items.
 void attn_block_list(dex_ctx* ctx, int nitems) {
-  int n1 = 0, ng = 0, nt = 0;
-  for (int i = 0; i < nitems; ++i)
-    if (ctx->h_items[i].lead == 1) ctx->h_item_list[n1++] = i;
-  for (int i = 0; i < nitems; ++i)
-    if (ctx->h_items[i].lead > 1) ctx->h_item_list[n1 + ng++] = i;
-  for (int i = 0; i < nitems; ++i)
-    if (ctx->h_items[i].xc0 >= 0)
-      for (int qt = 0; qt * kAttnSC < ctx->h_items[i].nrows; ++qt) ctx->h_item_list[n1 + ng + nt++] = 4 * i + qt;
-  ctx->attn_single = n1;
-  ctx->attn_groups = ng;
-  ctx->attn_tails = nt;
-}
-
-// Node cap of the lattice (node_held): 1 for the single-exit ablation, the
-// pruned lattice's branch_cap below N, else 0 (every node).
-int node_cap(const dex_options& o, int N) {
-  if (o.single_exit) return 1;
-  return o.branch_cap > 0 && o.branch_cap < N ? o.branch_cap : 0;
+  const BlockList b = attn_block_list(ctx->h_items, nitems, ctx->h_item_list);
+  ctx->attn_single = b.single;
+  ctx->attn_groups = b.groups;
+  ctx->attn_tails = b.tails;
 }
 
 // Groups of at least this many rows go to the wide GEMM kernel, the others to
@@ -812,25 +634,13 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   const int T_ = ctx->opt.max_new_tokens;
   const int ncap = node_cap(ctx->opt, N);
   // Host plan: rows per (sequence, stage) from the FSM state alone.
-  std::vector<int> live(B), rows_seq_stage((size_t)B * N, 0);
-  int nlive = 0, ncommit = 0;
-  int stage_tot[kMaxN] = {0};
-  for (int s = 0; s < B; ++s) {
-    live[s] = ctx->commits_[s] < T_;
-    if (!live[s]) continue;
-    ++nlive;
-    const int q = ar ? 0 : ctx->q_[s];
-    if (!ar && ncap) {   // pruned lattice (single-exit: one node per explorer 0..q)
-      for (int n = (1 << q) - 1; n <= (1 << (q + 1)) - 2; ++n)
-        if (node_held(n + 1, ncap)) ++rows_seq_stage[(size_t)s * N + __builtin_ctz(n + 1)];
-    }
-    for (int j = 0; j < N; ++j) {
-      int& r = rows_seq_stage[(size_t)s * N + j];
-      if (ar) r = j == 0 ? 1 : 0;
-      else if (!ncap) r = j < q ? 1 << (q - 1 - j) : (j == q ? 1 : 0);   // full lattice
-      stage_tot[j] += r;
-    }
-  }
+  RoundShape shape;
+  round_rows(ctx->q_.data(), ctx->commits_.data(), B, N, T_, ar, ncap, shape);
+  const std::vector<int>& live = shape.live;
+  const std::vector<int>& rows_seq_stage = shape.rows;
+  const int* stage_tot = shape.stage_tot;
+  const int* stage_off = shape.stage_off;
+  const int nlive = shape.nlive;
   if (nlive == 0) {
     ctx->err = "every sequence has reached max_new_tokens";
     return DEX_ESTATE;
@@ -839,51 +649,14 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
     ctx->err = "output capacity below the number of live sequences";
     return DEX_ENOSPC;
   }
-  int stage_off[kMaxN + 1];
-  stage_off[0] = 0;
-  for (int j = 0; j < N; ++j) stage_off[j + 1] = stage_off[j] + stage_tot[j];
-  const int R = stage_off[N];
-  std::vector<int> cursor(stage_off, stage_off + N);
-  for (int s = 0; s < B; ++s) {
-    SeqPlan& p = ctx->h_plans[s];
-    std::memset(&p, 0, sizeof(p));
-    p.live = live[s];
-    p.q = ar ? 0 : ctx->q_[s];
-    p.C = ctx->C_[s];
-    p.commit = live[s] && (ar || p.q + 1 == N);
-    p.prompt_len = ctx->plen_[s];
-    ncommit += p.commit;
-    for (int j = 0; j < N; ++j) {
-      p.base[j] = cursor[j];
-      cursor[j] += rows_seq_stage[(size_t)s * N + j];
-    }
-  }
+  const int R = shape.R;
+  const int ncommit = seq_plans(shape, ctx->q_.data(), ctx->C_.data(), ctx->plen_.data(), B, N, ar, ctx->h_plans);
   // Attention work items: rows of one (sequence, stage), at most kAttnUnits units each.
-  const int rep = ctx->D.nq / ctx->D.nkv;
-  const int per_item = std::max(1, kAttnUnits / rep);
-  int nitems = 0, max_keys = 0;
-  ctx->attn_umax = 1;
-  ctx->attn_nj = 0;
-  for (int j = 0; j < N; ++j)
-    for (int s = 0; s < B; ++s) {
-      const int cnt = rows_seq_stage[(size_t)s * N + j];
-      const int mk = ctx->C_[s] + (ar ? 1 : (ctx->q_[s] - j + 1));
-      for (int o = 0; o < cnt; o += per_item) {
-        AttnItem& it = ctx->h_items[nitems++];
-        it.seq = s;
-        it.row0 = ctx->h_plans[s].base[j] + o;
-        it.nrows = std::min(per_item, cnt - o);
-        it.stage = j;
-        it.max_keys = mk;
-        // lattice rows: explore keys at [C, mk), at most two chunks
-        it.xc0 = ar ? -1 : ctx->C_[s] / kKvTile;
-        it.xc1 = ar ? -1 : (mk - 1) / kKvTile;
-        if (!ar) ctx->attn_nj = std::max(ctx->attn_nj, it.xc1 - it.xc0 + 1);
-        it.lead = attn_lead(o / per_item, (cnt + per_item - 1) / per_item);
-        max_keys = std::max(max_keys, mk);
-        ctx->attn_umax = std::max(ctx->attn_umax, it.nrows * rep);
-      }
-    }
+  const ItemStats is = round_items(shape, ctx->h_plans, ctx->q_.data(), ctx->C_.data(), B, N, ar,
+                                   ctx->D.nq / ctx->D.nkv, ctx->h_items);
+  const int nitems = is.nitems, max_keys = is.max_keys;
+  ctx->attn_umax = is.umax;
+  ctx->attn_nj = is.nj;
   attn_block_list(ctx, nitems);
   // Algorithmic attention traffic of one layer slot, per stage: each
   // (sequence, stage) group reads its committed K/V once, each row its
@@ -971,18 +744,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   // Timed rounds run eagerly: an event recorded inside a replayed graph does
   // not wait for the kernel before it, so it cannot time that kernel.
   const bool graphs = !(ctx->opt.debug & 2) && !ctx->prof && !ctx->no_graphs;
-  std::string key;
-  if (graphs) {
-    key.reserve(16 + 3 * B);
-    key += ar ? 'A' : 'D';
-    key += std::to_string((max_keys + attn_chunk(ctx->D.hd) - 1) / attn_chunk(ctx->D.hd));
-    key += ':';
-    key += (char)('0' + ctx->attn_nj);   // per-row chunk slots of the attention launch
-    for (int s = 0; s < B; ++s) {
-      key += (char)('a' + (live[s] ? ctx->h_plans[s].q : 31));
-      key += ctx->h_plans[s].commit ? 'c' : '.';
-    }
-  }
+  const std::string key = graphs ? graph_key(ar, max_keys, ctx->attn_nj, shape, ctx->h_plans, B) : std::string();
   auto found = graphs ? ctx->graphs.find(key) : ctx->graphs.end();
   if (found != ctx->graphs.end()) {
     HIPCHK(hipGraphLaunch(found->second, st));
@@ -1030,10 +792,9 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       out[n++] = c;
       ctx->C_[s] += 1;
       ctx->commits_[s] += 1;
-      // the kept subtree has done N - 1 - b rounds; a pruned branch kept nothing
-      ctx->q_[s] = ar || (ncap && c.branch >= ncap) ? 0 : N - 1 - c.branch;
+      ctx->q_[s] = next_q(ctx->q_[s], true, ar, ncap, c.branch, N);
     } else {
-      ctx->q_[s] += 1;
+      ctx->q_[s] = next_q(ctx->q_[s], false, ar, ncap, 0, N);
     }
   }
   *n_out = n;

@@ -169,7 +169,6 @@ __device__ __forceinline__ void mask_v(u32x4_t& vh, u32x4_t& vl, int nv) {
   }
 }
 
-constexpr int kMixSlots = 2 * kAttnSC;   // chunk slots of the (at most two) mixed super-chunks
 // Super-chunks per span: a row's super-chunk states are folded left to right
 // within each span of kAttnSpan, and the span states left to right.
 constexpr int kAttnSpan = 16;
@@ -723,8 +722,6 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
 // ----------------------------------------------------------------------------
 // Host launcher
 // ----------------------------------------------------------------------------
-int attn_chunk(int) { return kAttnSCKeys; }
-int attn_mix_slots() { return kMixSlots; }
 
 // list: the nsingle items that form a group of their own, then the ngroups
 // items that lead a group of several, then ntails entries 4 item + quad of
