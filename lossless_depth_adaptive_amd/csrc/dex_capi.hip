@@ -217,11 +217,13 @@ constexpr int kW8Head = DEX_W8_HEAD;
 // their own); 13B-shaped batch 8: 364 -> 373 tokens/s. Where they are many
 // (the batch-1 lattice's small stages) the split-k kernel is much cheaper:
 // merging them cost the 7B-shaped sampled workload 7%.
-// Unsplit wide launches order their blocks weight by weight (GemmArgs.nrun):
-// the 13B-shaped batch-8 layer GEMMs fetch 1.14x their algorithmic bytes
-// instead of 1.39x, in the same time within a percent.
+// 1: unsplit wide launches order their blocks weight by weight
+// (GemmArgs.nrun). The 13B-shaped batch-8 layer GEMMs then fetch 1.14x their
+// algorithmic bytes instead of 1.39x, but the workload ran 1-2% slower (200
+// rounds, median of three: 356.4 -> 348.6 tokens/s; GQA batch 16 193.2 ->
+// 188.8), so the column-block order stays the default.
 #ifndef DEX_STAGE_MAJOR
-#define DEX_STAGE_MAJOR 1
+#define DEX_STAGE_MAJOR 0
 #endif
 constexpr bool kStageMajor = DEX_STAGE_MAJOR != 0;
 #ifndef DEX_MERGE_SMALL
