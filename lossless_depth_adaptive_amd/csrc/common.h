@@ -11,6 +11,15 @@
 
 namespace dex {
 
+// k-steps the 8-wave wide GEMM stages in LDS between two barriers (1 or 2).
+// Two halve the barriers: 13B-shaped batch 8 layer GEMMs -1.5% time (382.8
+// -> 386.6 tokens/s, two passes of 60 rounds each), the other workloads the
+// same within noise.
+#ifndef DEX_WIDE_KPB
+#define DEX_WIDE_KPB 2
+#endif
+constexpr int kWideKPB = DEX_WIDE_KPB;
+
 typedef unsigned short bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));

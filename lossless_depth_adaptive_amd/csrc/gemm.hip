@@ -718,9 +718,11 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
   const int col16 = lane & 15, kg = lane >> 4;
   const int t0 = tb0 + w * WT;
 
-  // f[buf][part][mb][lane]: part 0 (hi) / 1 (lo) of row 16 mb + (lane & 15),
-  // k 8 (lane >> 4) .. +7 of the k-step, the A operand of lane `lane`.
-  struct Stage { u32x4_t f[2][2][MBLK][64]; };
+  // f[buf][slot][part][mb][lane]: part 0 (hi) / 1 (lo) of row 16 mb +
+  // (lane & 15), k 8 (lane >> 4) .. +7 of k-step `slot` of the KPB k-steps
+  // staged between two barriers, the A operand of lane `lane`.
+  constexpr int KPB = SPLIT || NWV != 8 ? 1 : kWideKPB;
+  struct Stage { u32x4_t f[2][KPB][2][MBLK][64]; };
   struct Out { float t[SPLIT ? 1 : ROWS][BT * 16 + 4]; };   // the split form stores from registers
   __shared__ union { Stage s; Out o; } sm;
   __shared__ float rs_sh[ROWS];
@@ -759,9 +761,9 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
   // One k-step from the registers of p, which then take k-step ks + DEPTH
   // (three register sets, so each load has two k-steps of MFMAs to land in;
   // a fourth set measured no faster): the activation loads go out once p.a is
-  // staged, the weight loads once the MFMAs have read p.b.
-  auto step = [&](int ks, Pre& p, f32x4_t (&acc)[MBLK][WT]) {
-    const int buf = ks & 1;
+  // staged, the weight loads once the MFMAs have read p.b. stage() before the
+  // barrier, compute() after it.
+  auto stage = [&](int ks, Pre& p, int buf, int slot) {
     if (conv) {
       u32x4_t hv, lv;
 #pragma unroll
@@ -774,14 +776,15 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
         lv[2 * x] = l0;
         lv[2 * x + 1] = l1;
       }
-      sm.s.f[buf][0][w][lane] = hv;
-      sm.s.f[buf][1][w][lane] = lv;
+      sm.s.f[buf][slot][0][w][lane] = hv;
+      sm.s.f[buf][slot][1][w][lane] = lv;
       load_a(ks + DEPTH, p);
     }
-    __syncthreads();
+  };
+  auto compute = [&](int ks, Pre& p, int buf, int slot, f32x4_t (&acc)[MBLK][WT]) {
 #pragma unroll
     for (int mb = 0; mb < MBLK; ++mb) {
-      const u32x4_t ahu = sm.s.f[buf][0][mb][lane], alu = sm.s.f[buf][1][mb][lane];
+      const u32x4_t ahu = sm.s.f[buf][slot][0][mb][lane], alu = sm.s.f[buf][slot][1][mb][lane];
       bf16x8_t ah, al;
       __builtin_memcpy(&ah, &ahu, 16);
       __builtin_memcpy(&al, &alu, 16);
@@ -827,20 +830,57 @@ __global__ __launch_bounds__(NWV * 64) void gemm_wide_kernel(const GemmArgs args
       rend = (KS * (r + 1)) / kKSplit;
     }
   };
-  for (; ks + DEPTH <= kend; ks += DEPTH) {
+  if constexpr (KPB == 1) {
+    auto step = [&](int k, Pre& pk) {
+      stage(k, pk, k & 1, 0);
+      __syncthreads();
+      compute(k, pk, k & 1, 0, acc);
+      close(k);
+    };
+    for (; ks + DEPTH <= kend; ks += DEPTH) {
 #pragma unroll
-    for (int i = 0; i < DEPTH; ++i) {
-      step(ks + i, p[i], acc);
-      close(ks + i);
+      for (int i = 0; i < DEPTH; ++i) step(ks + i, p[i]);
     }
-  }
 #pragma unroll
-  for (int i = 0; i < DEPTH - 1; ++i) {
-    if (ks < kend) {
-      step(ks, p[i], acc);
-      close(ks);
-      ++ks;
+    for (int i = 0; i < DEPTH - 1; ++i) {
+      if (ks < kend) {
+        step(ks, p[i]);
+        ++ks;
+      }
     }
+  } else {
+    // Two k-steps per barrier: k-steps k and k + 1 (when below kend) staged
+    // into buffer pi & 1, then computed in order. The register sets still
+    // take k-steps in turn (six k-steps walk the three sets twice).
+    static_assert(KPB == 2 && DEPTH == 3, "pairs of k-steps over three register sets");
+    int pi = 0;
+    auto pair = [&](int k, Pre& pa, Pre& pb) {
+      const int buf = pi & 1;
+      const bool two = k + 1 < kend;
+      stage(k, pa, buf, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (two) stage(k + 1, pb, buf, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      compute(k, pa, buf, 0, acc);
+      close(k);
+      if (two) {
+        // keep the second k-step's LDS reads below the first one's MFMAs:
+        // hoisted, they need 32 more VGPRs and spill
+        __builtin_amdgcn_sched_barrier(0);
+        compute(k + 1, pb, buf, 1, acc);
+        close(k + 1);
+      }
+      ++pi;
+    };
+    for (; ks + 2 * DEPTH <= kend; ks += 2 * DEPTH) {
+      pair(ks, p[0], p[1]);
+      pair(ks + 2, p[2], p[0]);
+      pair(ks + 4, p[1], p[2]);
+    }
+    if (ks < kend) pair(ks, p[0], p[1]);
+    if (ks + 2 < kend) pair(ks + 2, p[2], p[0]);
+    if (ks + 4 < kend) pair(ks + 4, p[1], p[2]);
   }
 
   if constexpr (SPLIT) {
