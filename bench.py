@@ -24,7 +24,8 @@ Extra fields on the JSON line:
                   decode run eagerly right after the last timed run; traffic
                   comes from rocprofv3 counter runs of this workload
                   (profiles/traffic_gemm_<workload>.json) when present and
-                  taken on the library sources in the tree (else null);
+                  taken with the library this run loads (same digest; else
+                  null);
   e2e           - end-to-end committed tokens per second of one whole
                   generation (prefill included; the pages' throughput
                   definition, Appendix D) next to the decode-only value;
@@ -53,7 +54,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-from lossless_depth_adaptive_amd.build import source_digest  # noqa: E402
+from lossless_depth_adaptive_amd.build import library_digest  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
@@ -306,10 +307,10 @@ def main():
     if os.path.exists(tpath) and not args.X and args.variant == "dex" and args.adapter_alpha is None:
         tr = json.load(open(tpath))
         if tr.get("workload") == w.name and g["launches"]:
-            if tr.get("library_sources") == source_digest():
+            if tr.get("library") == library_digest(D.LIB_PATH):
                 traffic = tr.get("bytes_per_launch")
             else:
-                log(f"[gpu] {tpath} was measured on other kernel sources: traffic left null")
+                log(f"[gpu] {tpath} was measured with another build of the library: traffic left null")
     per_launch_bytes = g["bytes"] / max(1, g["launches"])
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
@@ -397,6 +398,7 @@ def main():
                    "note": "each run prefills, then times rounds warmup+1 .. warmup+steps after the prefill; "
                            "value is the median run",
                    "tokens_per_s": [round(r["tokens_per_s"], 2) for r in runs]},
+        "library": {"path": os.path.relpath(D.LIB_PATH, ROOT), "digest": library_digest(D.LIB_PATH)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "ead": ead,

@@ -30,18 +30,14 @@ FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
 SOURCE_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form"] for src in ("gemm.hip", "layer.hip")}
 
 
-def source_digest() -> str:
-    """SHA-256 over the library's sources (every file of csrc/, the public
-    header) and its compile flags: measurements taken on one build (counter
-    summaries) name it, so a later reader can tell whether they still describe
-    the kernels in the tree."""
+def library_digest(path: str = LIB) -> str:
+    """SHA-256 (16 hex digits) of a built library file. Measurements taken
+    with one build (counter summaries) name it, so a later reader can tell
+    whether they still describe the library it loads; builds of the same
+    sources with the same flags are byte-identical."""
     h = hashlib.sha256()
-    files = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".h")))
-    for path in files + [os.path.join(INCLUDE, "dex.h")]:
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
-            h.update(f.read())
-    h.update(repr((FLAGS, sorted(SOURCE_FLAGS.items()))).encode())
+    with open(path, "rb") as f:
+        h.update(f.read())
     return h.hexdigest()[:16]
 
 

@@ -818,54 +818,24 @@ int run_prefill(dex_ctx* ctx, int n_seqs, const int32_t* tokens, const int32_t* 
   HIPCHK(hipMemcpy(ctx->anchors_in, anchors.data(), n_seqs * 4, hipMemcpyHostToDevice));
   HIPCHK(launch_reset(ctx->map, ctx->freel, ctx->cursor, ctx->anchor, ctx->anchors_in, n_seqs, ctx->D.P, st));
   const int base_h = ctx->opt.max_batch * ctx->D.P;
-  const int rep = ctx->D.nq / ctx->D.nkv;
-  const int per_item = std::max(1, kAttnUnits / rep);
-  off = 0;
-  for (int s = 0; s < n_seqs; ++s) {
-    const int npos = lens[s] - 1;  // positions 0..len-2 go to the committed cache
-    for (int p0 = 0; p0 < npos; p0 += kPrefillRows) {
-      const int R = std::min(kPrefillRows, npos - p0);
-      for (int i = 0; i < R; ++i) {
-        RowInfo& r = ctx->h_rows[i];
-        std::memset(&r, 0, sizeof(r));
-        r.seq = s;
-        r.phys = 0;
-        r.hrow = base_h + i;
-        r.stage = 0;
-        r.pos = p0 + i;
-        r.tok = tokens[off + p0 + i];
-        r.ncommit = p0 + i + 1;
-        r.kv_commit = 1;
-      }
-      int nitems = 0;
-      for (int o = 0; o < R; o += per_item) {
-        AttnItem& it = ctx->h_items[nitems++];
-        it.seq = s;
-        it.row0 = o;
-        it.nrows = std::min(per_item, R - o);
-        it.stage = 0;
-        it.max_keys = p0 + o + it.nrows;
-        it.xc0 = it.xc1 = -1;
-        it.lead = attn_lead(o / per_item, (R + per_item - 1) / per_item);
-      }
-      // A group's blocks skip super-chunks past its first item's max_keys:
-      // make that the group's largest (causal rows further down need more).
-      for (int i = 0; i < nitems; ++i)
-        for (int k = 1; k < ctx->h_items[i].lead; ++k)
-          ctx->h_items[i].max_keys = std::max(ctx->h_items[i].max_keys, ctx->h_items[i + k].max_keys);
-      HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
-      attn_block_list(ctx, nitems);
-      HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
-      HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list,
-                            (ctx->attn_single + ctx->attn_groups + ctx->attn_tails) * sizeof(int),
-                            hipMemcpyHostToDevice, st));
-      HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
-      std::vector<std::pair<int, int>> stage_rows = {{0, R}};
-      const int rc = run_layers<T>(ctx, R, stage_rows, ctx->L, 0, nitems, p0 + R, false);
-      if (rc) return rc;
-      HIPCHK(hipStreamSynchronize(st));  // host row buffers are reused by the next chunk
-    }
-    off += lens[s];
+  const int per_item = std::max(1, kAttnUnits / (ctx->D.nq / ctx->D.nkv));
+  PrefillCursor cur;
+  for (;;) {
+    int nitems = 0, max_keys = 0;
+    const int R = prefill_chunk(tokens, lens, n_seqs, base_h, per_item, cur, ctx->h_rows, ctx->h_items, nitems,
+                                max_keys);
+    if (R == 0) break;
+    HIPCHK(hipMemcpyAsync(ctx->rows, ctx->h_rows, R * sizeof(RowInfo), hipMemcpyHostToDevice, st));
+    attn_block_list(ctx, nitems);
+    HIPCHK(hipMemcpyAsync(ctx->items, ctx->h_items, nitems * sizeof(AttnItem), hipMemcpyHostToDevice, st));
+    HIPCHK(hipMemcpyAsync(ctx->item_list, ctx->h_item_list,
+                          (ctx->attn_single + ctx->attn_groups + ctx->attn_tails) * sizeof(int),
+                          hipMemcpyHostToDevice, st));
+    HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
+    std::vector<std::pair<int, int>> stage_rows = {{0, R}};
+    const int rc = run_layers<T>(ctx, R, stage_rows, ctx->L, 0, nitems, max_keys, false);
+    if (rc) return rc;
+    HIPCHK(hipStreamSynchronize(st));  // host row buffers are reused by the next chunk
   }
   HIPCHK(hipStreamSynchronize(st));
   return DEX_OK;

@@ -7,6 +7,9 @@
       with --bench-json, a header naming the workload, the command and what
       the traced bench.py run printed.
 
+  python -m lossless_depth_adaptive_amd.profsum pmc RESULTS.db
+      Per-kernel means of every counter of a --pmc run over the decode window.
+
   python -m lossless_depth_adaptive_amd.profsum traffic --fetch F.db --write W.db \
         --bench-json BENCH.json --out traffic.json
       HBM bytes of the layer GEMMs from the FETCH_SIZE and WRITE_SIZE counter
@@ -16,8 +19,8 @@
       bench.py timed with HIP events (the last roofline.launches of the decode
       window; run bench.py with --no-ar) and divided by their count; compared
       with the algorithmic bytes per launch the library reported for the same
-      rounds. The summary names the library sources it was measured on
-      (build.source_digest); bench.py uses it only while they are unchanged.
+      rounds. The summary names the library the counted run loaded (its
+      digest, from the bench line); bench.py uses it only with that library.
 """
 
 import argparse
@@ -25,7 +28,6 @@ import json
 import sqlite3
 import sys
 
-from .build import source_digest
 
 GIB = 1 << 30
 
@@ -74,7 +76,7 @@ def trace_header(bench_json: str, command: str) -> str:
     c, rl = d["config"], d["roofline"]
     out = [f"# Kernel trace: lattice step, workload {c['workload']} ({c.get('layers')} layers, d {c.get('d_model')}, "
            f"X={c.get('X')}, batch {c.get('batch')}, prompts {c.get('prompt_len')}, {c.get('mode')})",
-           f"# library sources {source_digest()}",
+           f"# library {d.get('library', {}).get('digest')}",
            "#",
            "# Commands (repository root, MI355X, ROCm 7.2):",
            "#   export TMPDIR=/tmp",
@@ -91,7 +93,7 @@ def trace_header(bench_json: str, command: str) -> str:
     return "\n".join(out) + "\n"
 
 
-def trace_summary(db: str) -> str:
+def trace_summary(db: str, bench_json: str = None) -> str:
     rows = [r for r in decode_window(_dispatches(db)) if "dex::" in r[0]]
     if not rows:
         return "no decode-window dispatches found\n"
@@ -111,6 +113,18 @@ def trace_summary(db: str) -> str:
                f"total {sum(lg) / 1e6:.2f} ms")
     hg = [d for k, v in stats.items() if gemm_epilogue(k) == 3 or "head_reduce" in k for d in v]
     out.append(f"exit-head dispatches: {len(hg)}, total {sum(hg) / 1e6:.2f} ms")
+    if bench_json:
+        # the rounds bench.py timed with HIP events: the last roofline.launches
+        # layer-GEMM dispatches of the window
+        rl = json.loads(open(bench_json).read().strip().splitlines()[-1])["roofline"]
+        n = rl["launches"]
+        last = [d for name, _, _, d in rows if is_layer_gemm(name)][-n:]
+        if last:
+            mean = sum(last) / len(last)
+            gbs = rl["algorithmic_bytes_per_launch"] / (mean * 1e-9) / 1e9
+            out.append(f"the {len(last)} layer-GEMM dispatches of the event-timed rounds: mean {mean / 1e3:.2f} us "
+                       f"(events: {rl['mean_launch_us']:.2f} us), {gbs:.0f} GB/s algorithmic, {gbs / 8000.0:.3f} "
+                       "of 8 TB/s")
     return "\n".join(out) + "\n"
 
 
@@ -147,9 +161,34 @@ def traffic(fetch_db, write_db, bench_json, workload=None):
                 fetch_bytes_per_launch=fetch / n, write_bytes_per_launch=write / max(1, len(wg)),
                 bytes_per_launch=fetch / n + write / max(1, len(wg)),
                 algorithmic_bytes_per_launch=rl["algorithmic_bytes_per_launch"],
-                fetch_scale=f_scale, write_scale=w_scale, library_sources=source_digest(),
+                fetch_scale=f_scale, write_scale=w_scale, library=bench.get("library", {}).get("digest"),
                 note="layer GEMM launches (exit head excluded) of the HIP-event-timed rounds; counters in KiB "
                      "per dispatch scaled by a 1 GiB copy read/write in the same process")
+
+
+def pmc_summary(db: str, top: int = 12) -> str:
+    """Per-kernel means of every counter in a --pmc database over the decode
+    window (the kernels with the most dispatches first)."""
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select dispatch_id, kernel_name, counter_name, value from counters_collection "
+                       "order by dispatch_id").fetchall()
+    start = next((d for d, k, _, _ in rows if "sched_kernel" in k or "ar_rows_kernel" in k), None)
+    if start is None:
+        return "no decode-window dispatches found\n"
+    acc, disp = {}, {}
+    for d, k, c, v in rows:
+        if d < start or "dex::" not in k:
+            continue
+        k = _short(k)
+        acc.setdefault(k, {}).setdefault(c, 0.0)
+        acc[k][c] += v
+        disp.setdefault(k, set()).add(d)
+    counters = sorted({c for v in acc.values() for c in v})
+    out = [f"{'kernel':<44} {'calls':>6} " + " ".join(f"{c[:18]:>18}" for c in counters)]
+    for k in sorted(acc, key=lambda k: -len(disp[k]))[:top]:
+        n = len(disp[k])
+        out.append(f"{k:<44} {n:>6} " + " ".join(f"{acc[k].get(c, 0.0) / n:>18.4g}" for c in counters))
+    return "\n".join(out) + "\n"
 
 
 def main(argv=None):
@@ -159,6 +198,8 @@ def main(argv=None):
     t.add_argument("db")
     t.add_argument("--bench-json", help="what the traced bench.py command printed (adds a header)")
     t.add_argument("--command", default="python3 bench.py ...", help="the traced command, for the header")
+    c = sub.add_parser("pmc")
+    c.add_argument("db")
     r = sub.add_parser("traffic")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
@@ -166,10 +207,12 @@ def main(argv=None):
     r.add_argument("--workload")
     r.add_argument("--out")
     a = ap.parse_args(argv)
-    if a.cmd == "trace":
+    if a.cmd == "pmc":
+        sys.stdout.write(pmc_summary(a.db))
+    elif a.cmd == "trace":
         if a.bench_json:
             sys.stdout.write(trace_header(a.bench_json, a.command))
-        sys.stdout.write(trace_summary(a.db))
+        sys.stdout.write(trace_summary(a.db, a.bench_json))
     else:
         res = traffic(a.fetch, a.write, a.bench_json, a.workload)
         txt = json.dumps(res, indent=2)

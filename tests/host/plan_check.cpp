@@ -2,7 +2,8 @@
 // AddressSanitizer and UndefinedBehaviorSanitizer (tests/test_host_plan.py):
 // configuration checks, workspace carving, rows per round against a brute
 // enumeration of the heap level, per-sequence plans, attention items and block
-// lists, the HIP-graph key and the FSM over scripted commits. Every buffer is
+// lists, the HIP-graph key, the FSM over scripted commits and the prefill
+// chunks (every prompt position once, in order). Every buffer is
 // sized exactly as the library sizes its host buffers, so a write past one is
 // an ASan report. Prints "plan checks ok" and exits 0 when every check holds.
 //
@@ -430,6 +431,94 @@ static void check_fsm(std::mt19937& rng) {
   CHECK(next_q(0, true, true, 0, 0, 4) == 0);
 }
 
+// --- prefill chunks ----------------------------------------------------------------
+static void check_prefill(std::mt19937& rng) {
+  for (int t = 0; t < 300; ++t) {
+    const int n = 1 + rng() % 16;
+    std::vector<int32_t> lens(n);
+    size_t total = 0;
+    for (int s = 0; s < n; ++s) {
+      lens[s] = 1 + (rng() % 3 == 0 ? rng() % 9000 : rng() % 700);
+      total += lens[s];
+    }
+    std::vector<int32_t> tokens(total);
+    std::vector<size_t> start(n);
+    for (int s = 0, o = 0; s < n; o += lens[s], ++s) {
+      start[s] = o;
+      for (int p = 0; p < lens[s]; ++p) tokens[o + p] = s * 10000 + p;
+    }
+    const int per_item = 16 >> (rng() % 4);
+    const int base_h = (int)(rng() % 1000);
+    const int Rmax = kPrefillRows;   // the library's host buffers hold at least this many rows and items
+    std::vector<RowInfo> rows(Rmax);
+    std::vector<AttnItem> items(Rmax);
+    std::vector<int> list(3 * (size_t)Rmax);
+    PrefillCursor cur;
+    int next_seq = 0, next_pos = 0, chunks = 0;
+    for (;;) {
+      int nitems = -1, maxk = -1;
+      const int R = prefill_chunk(tokens.data(), lens.data(), n, base_h, per_item, cur, rows.data(), items.data(),
+                                  nitems, maxk);
+      if (R == 0) break;
+      ++chunks;
+      CHECK(R <= kPrefillRows && nitems <= R);
+      int want_maxk = 0;
+      for (int i = 0; i < R; ++i) {
+        // positions in order, sequence after sequence, skipping each prompt's last token
+        while (next_seq < n && next_pos >= lens[next_seq] - 1) {
+          ++next_seq;
+          next_pos = 0;
+        }
+        CHECK(next_seq < n);
+        const RowInfo& r = rows[i];
+        CHECK(r.seq == next_seq && r.pos == next_pos);
+        CHECK(r.tok == next_seq * 10000 + next_pos);
+        CHECK(r.hrow == base_h + i && r.ncommit == r.pos + 1 && r.kv_commit == 1 && r.stage == 0);
+        want_maxk = std::max(want_maxk, r.ncommit);
+        ++next_pos;
+      }
+      CHECK(maxk == want_maxk);
+      // items: every row once, one sequence each, at most per_item rows
+      std::vector<int> cover(R, 0);
+      for (int i = 0; i < nitems; ++i) {
+        const AttnItem& it = items[i];
+        CHECK(it.nrows >= 1 && it.nrows <= per_item && it.xc0 == -1 && it.stage == 0);
+        int own = 0;
+        for (int k = 0; k < it.nrows; ++k) {
+          const int row = it.row0 + k;
+          CHECK(row >= 0 && row < R);
+          if (row < 0 || row >= R) continue;
+          ++cover[row];
+          CHECK(rows[row].seq == it.seq);
+          own = std::max(own, rows[row].ncommit);
+        }
+        if (it.lead > 1) {   // the group's first item carries its largest key count
+          int g = own;
+          for (int k = 1; k < it.lead; ++k) {
+            CHECK(i + k < nitems && items[i + k].lead == 0 && items[i + k].seq == it.seq);
+            const AttnItem& o = items[i + k];
+            g = std::max(g, rows[o.row0 + o.nrows - 1].ncommit);
+          }
+          CHECK(it.max_keys == g);
+        } else {
+          CHECK(it.max_keys == own);
+        }
+      }
+      for (int row = 0; row < R; ++row) CHECK(cover[row] == 1);
+      const BlockList b = attn_block_list(items.data(), nitems, list.data());
+      CHECK(b.tails == 0 && b.single + b.groups <= nitems);
+    }
+    while (next_seq < n && next_pos >= lens[next_seq] - 1) {
+      ++next_seq;
+      next_pos = 0;
+    }
+    CHECK(next_seq == n);   // every position went through exactly one chunk
+    size_t rows_total = 0;
+    for (int s = 0; s < n; ++s) rows_total += lens[s] - 1;
+    CHECK(chunks == (int)((rows_total + kPrefillRows - 1) / kPrefillRows));
+  }
+}
+
 int main() {
   check_validate();
   check_workspace();
@@ -444,6 +533,7 @@ int main() {
       }
   check_graph_key(rng);
   check_fsm(rng);
+  check_prefill(rng);
   if (g_fail) {
     std::fprintf(stderr, "%d plan checks failed\n", g_fail);
     return 1;
