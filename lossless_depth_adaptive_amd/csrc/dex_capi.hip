@@ -1061,7 +1061,7 @@ int dex_step_noalloc(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out)
   if (ctx->poisoned) return DEX_EHIP;
   const WsPlan& wp = ctx->wp;
   size_t need = 0;
-  for (int r = 0; r < SC_N; ++r) need += (wp.sbytes[r] + 255) & ~(size_t)255;
+  for (int r = 0; r < SC_N; ++r) need += (wp.sstep[r] + 255) & ~(size_t)255;
   if (need > kStaticScratchBytes) {
     char buf[200];
     snprintf(buf, sizeof buf, "per-round scratch of this context (%zu bytes) exceeds the static scratch (%zu bytes)",
@@ -1078,7 +1078,7 @@ int dex_step_noalloc(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out)
   size_t o = 0;
   for (int r = 0; r < SC_N; ++r) {
     off[r] = o;
-    o += (wp.sbytes[r] + 255) & ~(size_t)255;
+    o += (wp.sstep[r] + 255) & ~(size_t)255;
   }
   // the round's scratch regions point into the static array for this call only
   RowInfo* rows = ctx->rows;
@@ -1092,7 +1092,7 @@ int dex_step_noalloc(dex_ctx* ctx, dex_commit* out, int32_t cap, int32_t* n_out)
   ctx->rows = (RowInfo*)(base + off[SC_ROWS]);
   ctx->plans = (SeqPlan*)(base + off[SC_PLANS]);
   ctx->items = (AttnItem*)(base + off[SC_ITEMS]);
-  ctx->item_list = (int*)(ctx->items + wp.Rmax);
+  ctx->item_list = (int*)(ctx->items + wp.Rstep);
   ctx->q = (float*)(base + off[SC_Q]);
   ctx->attn_out = base + off[SC_ATTN_OUT];
   ctx->act = base + off[SC_ACT];

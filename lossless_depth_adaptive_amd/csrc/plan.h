@@ -48,6 +48,10 @@ struct WsPlan {
   size_t total;
   int Rmax, nchunk, split_cols;
   size_t sbytes[10];   // bytes of the per-round scratch regions (ScratchRegion order)
+  // The same regions sized for lattice and autoregressive rounds only (Rstep
+  // rows: no prefill chunk), which is all dex_step_noalloc needs.
+  int Rstep;
+  size_t sstep[10];
 };
 
 // Per-round scratch regions of the workspace: written by a round before they
@@ -156,17 +160,22 @@ inline WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_
   w.Xd = lay.take(kMaxN * 4);
   w.dbg_logits = lay.take((o->debug & 1) ? B * V * 4 : 0);
   w.split_cols = (int)std::max(std::max((nq + 2 * nkv) * hd, 2 * F), d);
-  w.sbytes[SC_ROWS] = R * sizeof(RowInfo);
-  w.sbytes[SC_PLANS] = B * sizeof(SeqPlan);
-  w.sbytes[SC_ITEMS] = R * (sizeof(AttnItem) + 12);   // items, then the attention block lists (3 R ints)
-  w.sbytes[SC_Q] = R * nq * hd * 4;
-  w.sbytes[SC_ATTN_OUT] = R * nq * hd * 4;
-  w.sbytes[SC_ACT] = R * std::max(F, m) * 4;
-  w.sbytes[SC_ATTN_PART] = R * nq * w.nchunk * (hd + 4) * 4;
-  w.sbytes[SC_ATTN_TAIL] = R * nq * kMixSlots * (hd + 4) * 4;
-  // the split-range partials serve the wide (bf16) GEMM only
-  w.sbytes[SC_GEMM_SPLIT] = c->dtype == DEX_DTYPE_BF16 ? (size_t)kKSplit * kSplitRows * w.split_cols * 4 : 0;
-  w.sbytes[SC_HEAD_PART] = R * (V / 16) * 3 * 4;
+  auto scratch_sizes = [&](size_t R, size_t* sb) {
+    sb[SC_ROWS] = R * sizeof(RowInfo);
+    sb[SC_PLANS] = B * sizeof(SeqPlan);
+    sb[SC_ITEMS] = R * (sizeof(AttnItem) + 12);   // items, then the attention block lists (3 R ints)
+    sb[SC_Q] = R * nq * hd * 4;
+    sb[SC_ATTN_OUT] = R * nq * hd * 4;
+    sb[SC_ACT] = R * std::max(F, m) * 4;
+    sb[SC_ATTN_PART] = R * nq * w.nchunk * (hd + 4) * 4;
+    sb[SC_ATTN_TAIL] = R * nq * kMixSlots * (hd + 4) * 4;
+    // the split-range partials serve the wide (bf16) GEMM only
+    sb[SC_GEMM_SPLIT] = c->dtype == DEX_DTYPE_BF16 ? (size_t)kKSplit * kSplitRows * w.split_cols * 4 : 0;
+    sb[SC_HEAD_PART] = R * (V / 16) * 3 * 4;
+  };
+  w.Rstep = std::max((int)B << (N - 1), (int)B);
+  scratch_sizes(R, w.sbytes);
+  scratch_sizes(w.Rstep, w.sstep);
   w.rows = lay.take(w.sbytes[SC_ROWS]);
   w.plans = lay.take(w.sbytes[SC_PLANS]);
   w.items = lay.take(w.sbytes[SC_ITEMS]);

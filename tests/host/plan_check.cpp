@@ -218,6 +218,10 @@ static void check_workspace() {
     CHECK(w.sbytes[SC_ROWS] >= (size_t)widest * sizeof(RowInfo));
     CHECK(w.sbytes[SC_HEAD_PART] >= (size_t)widest * (V / 16) * 12);
     CHECK(w.plans + w.sbytes[SC_PLANS] <= w.items);
+    // the allocation-free step's regions: decode rounds only, never larger
+    CHECK(w.Rstep >= k.B << (k.N - 1) && w.Rstep <= w.Rmax);
+    for (int r = 0; r < SC_N; ++r) CHECK(w.sstep[r] <= w.sbytes[r]);
+    CHECK(w.sstep[SC_HEAD_PART] >= (size_t)(k.B << (k.N - 1)) * (V / 16) * 12);
     CHECK(w.head_part + w.sbytes[SC_HEAD_PART] <= w.total);
   }
 }
