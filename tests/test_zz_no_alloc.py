@@ -55,10 +55,11 @@ def test_step_noalloc_matches_step(name):
 def test_step_noalloc_refuses_large_scratch():
     from lossless_depth_adaptive_amd import dex as D
     from tests.gpu_helpers import device_weights, make_ctx
-    # a 151936-token vocabulary: the exit head's tile summaries alone need
-    # 512 rows x 9496 tiles x 12 bytes, with the GEMM partials beyond 64 MiB
+    # a 151936-token vocabulary at batch 64: a decode round's exit-head tile
+    # summaries alone need 64 x 2^(4-1) rows x 9496 tiles x 12 bytes (58 MB),
+    # with the split-range GEMM partials (34 MB) beyond 64 MiB
     w = tiny.scaled(dtype="bf16", tied=False, vocab=151936)
-    ctx = make_ctx(w, device_weights(w), 1, 4)
+    ctx = make_ctx(w, device_weights(w), 64, 4)
     with pytest.raises(D.DexError) as e:
         ctx.step_noalloc()
     assert e.value.code == D.DEX_ENOSPC
