@@ -67,6 +67,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def counted_traffic(path: str, workload: str, lib_path: str):
+    """HBM bytes per layer-GEMM launch from a counter summary
+    (profiles/traffic_gemm_<workload>.json), or None when there is none for
+    this workload or it was counted with another build of the library."""
+    if not os.path.exists(path):
+        return None
+    tr = json.load(open(path))
+    if tr.get("workload") != workload:
+        return None
+    if tr.get("library") != library_digest(lib_path):
+        log(f"[gpu] {path} was measured with another build of the library: traffic left null")
+        return None
+    return tr.get("bytes_per_launch")
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -304,13 +319,8 @@ def main():
     achieved = g["bytes"] / (g["ms"] * 1e-3) / 1e9 if g["ms"] > 0 else 0.0
     traffic = None
     tpath = args.traffic or os.path.join(ROOT, "profiles", f"traffic_gemm_{w.name}.json")
-    if os.path.exists(tpath) and not args.X and args.variant == "dex" and args.adapter_alpha is None:
-        tr = json.load(open(tpath))
-        if tr.get("workload") == w.name and g["launches"]:
-            if tr.get("library") == library_digest(D.LIB_PATH):
-                traffic = tr.get("bytes_per_launch")
-            else:
-                log(f"[gpu] {tpath} was measured with another build of the library: traffic left null")
+    if not args.X and args.variant == "dex" and args.adapter_alpha is None and g["launches"]:
+        traffic = counted_traffic(tpath, w.name, D.LIB_PATH)
     per_launch_bytes = g["bytes"] / max(1, g["launches"])
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
