@@ -39,9 +39,8 @@ hipError_t launch_attention(const AttnItem*, int, const int*, int, int, int, con
                             const bf16_t*,
                             const bf16_t*, float*, float*, float*, const ModelDims&, int, int, int, int, int, int,
                             bool, hipStream_t);
-template <typename T>
 hipError_t launch_sched(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*, const int*, int, int, int,
-                        const void*, float*, float*, float*, const float*, int, int, int, hipStream_t);
+                        int, int, hipStream_t);
 hipError_t launch_commit(const SeqPlan*, int, int*, const int*, const float*, int*, int*, int*, int*, int*, int*,
                          float*, const int*, int, int, int, int, hipStream_t);
 hipError_t launch_promote(const SeqPlan*, int, const int*, const bf16_t*, bf16_t*, const ModelDims&, hipStream_t);
@@ -698,11 +697,13 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       HIPCHK(launch_ar_rows(ctx->plans, B, ctx->rows, ctx->anchor, ctx->D.P, st));
       HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, R, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms, ctx->D.d, st));
     } else {
-      HIPCHK(launch_sched<T>(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
-                             ctx->D.P, ctx->opt.decs, ctx->embed, ctx->hidden, ctx->xn, ctx->ssq, ctx->norms,
-                             ctx->D.d, ctx->opt.single_exit, ncap, st));
+      HIPCHK(launch_sched(ctx->plans, B, ctx->rows, ctx->map, ctx->cand, ctx->freel, ctx->cursor, ctx->anchor, N,
+                          ctx->D.P, ctx->opt.decs, ctx->opt.single_exit, ncap, st));
+      // explorer 0's rows (the round's first) start from their token's embedding
+      HIPCHK(launch_embed<T>(ctx->embed, ctx->rows, 0, stage_tot[0], ctx->hidden, ctx->xn, ctx->ssq, ctx->norms,
+                             ctx->D.d, st));
     }
-    prof_end(ctx, mk, ar ? 2 : 1, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
+    prof_end(ctx, mk, 2, (double)R * sizeof(RowInfo) + (double)stage_tot[0] * ctx->D.d * (4 + sizeof(T)), 0);
     std::vector<std::pair<int, int>> stage_rows;
     for (int j = 0; j < N; ++j) stage_rows.push_back({stage_off[j], stage_tot[j]});
     int rc = run_layers<T>(ctx, R, stage_rows, ar ? ctx->L : ctx->S, ar ? 0 : 1, nitems, max_keys, true,

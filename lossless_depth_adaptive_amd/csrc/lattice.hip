@@ -19,22 +19,18 @@
 namespace dex {
 
 // Expand: one workgroup per live sequence builds the row of every node the
-// round creates (2^q of them at state q) and gathers the embedding of the rows
-// that start a slot (explorer 0): residual, residual times the first layer's
-// attention-norm weight, and per-16-column sums of squares (the inputs of the
-// fused RMSNorm of the next GEMM).
+// round creates (2^q of them at state q). The rows that start a slot
+// (explorer 0, the first rows of the round) take their token's embedding in a
+// launch of their own (embed_kernel, a workgroup per row).
 // Pruned lattice (cap > 0): only the nodes node_held keeps are created; each
 // takes the next free slot in heap order and the next row of its explorer.
 // The single-exit ablation ("Depth Exploration for LLM Decoding", Section 4,
 // Figure 4 right-top) has the cap-1 node set, n + 1 = (2^(a+1) - 1) 2^(q-a)
 // for a = 0..q (one per explorer), and no masks.
-template <typename T>
 __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restrict__ rows,
                              int* __restrict__ map, const int* __restrict__ cand,
                              const int* __restrict__ freel, int* __restrict__ cursor,
-                             const int* __restrict__ anchor_tok, int N, int P, int decs,
-                             const T* __restrict__ E, float* __restrict__ hidden, float* __restrict__ xn,
-                             float* __restrict__ ssq, const float* __restrict__ g0, int d, int single_exit,
+                             const int* __restrict__ anchor_tok, int N, int P, int decs, int single_exit,
                              int cap) {
   const int s = blockIdx.x;
   const SeqPlan pl = plans[s];
@@ -46,11 +42,6 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
     for (int t = 0; t < total; ++t) nnew += node_held(first + t + 1, cap);
   }
   const int cur = cursor[s];
-  __shared__ int nemb;
-  __shared__ int emb_h[1 << (kMaxN - 1)];
-  __shared__ int emb_t[1 << (kMaxN - 1)];
-  if (threadIdx.x == 0) nemb = 0;
-  __syncthreads();
   int* mp = map + (size_t)s * P;
   const int* cd = cand + (size_t)s * P;
   for (int t = threadIdx.x; t < total; t += blockDim.x) {
@@ -103,31 +94,8 @@ __global__ void sched_kernel(const SeqPlan* __restrict__ plans, RowInfo* __restr
       R.n_mask = depth;
     }
     rows[pl.base[depth] + idx] = R;
-    if (R.tok >= 0) {
-      const int e = atomicAdd(&nemb, 1);
-      emb_h[e] = R.hrow;
-      emb_t[e] = R.tok;
-    }
   }
-  __syncthreads();
   if (threadIdx.x == 0) cursor[s] = cur + nnew;
-  const int nt = d >> 4;
-  for (int x = threadIdx.x; x < nemb * nt; x += blockDim.x) {
-    const int e = x / nt, t = x - e * nt;
-    const T* src = E + (size_t)emb_t[e] * d + 16 * t;
-    float* h = hidden + (size_t)emb_h[e] * d + 16 * t;
-    float* xr = xn + (size_t)emb_h[e] * d + 16 * t;
-    float v[16], ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) v[c] = to_f<T>(src[c]);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      h[c] = v[c];
-      xr[c] = v[c] * g0[16 * t + c];
-      ss = fmaf(v[c], v[c], ss);
-    }
-    ssq[(size_t)emb_h[e] * nt + t] = ss;
-  }
 }
 
 // Commit and collapse for every sequence whose round reached the final
@@ -285,21 +253,13 @@ __global__ void reset_seq_kernel(int* __restrict__ map, int* __restrict__ freel,
 }
 
 // ----------------------------------------------------------------------------
-template <typename T>
 hipError_t launch_sched(const SeqPlan* plans, int nseq, RowInfo* rows, int* map, const int* cand,
                         const int* freel, int* cursor, const int* anchor_tok, int N, int P, int decs,
-                        const void* E, float* hidden, float* xn, float* ssq, const float* g0, int d,
                         int single_exit, int cap, hipStream_t st) {
-  hipLaunchKernelGGL(sched_kernel<T>, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
-                     anchor_tok, N, P, decs, (const T*)E, hidden, xn, ssq, g0, d, single_exit, cap);
+  hipLaunchKernelGGL(sched_kernel, dim3(nseq), dim3(256), 0, st, plans, rows, map, cand, freel, cursor,
+                     anchor_tok, N, P, decs, single_exit, cap);
   return hipGetLastError();
 }
-template hipError_t launch_sched<float>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
-                                        const int*, int, int, int, const void*, float*, float*, float*, const float*,
-                                        int, int, int, hipStream_t);
-template hipError_t launch_sched<bf16_t>(const SeqPlan*, int, RowInfo*, int*, const int*, const int*, int*,
-                                         const int*, int, int, int, const void*, float*, float*, float*, const float*,
-                                         int, int, int, hipStream_t);
 
 hipError_t launch_commit(const SeqPlan* plans, int nseq, int* map, const int* cand, const float* margin,
                          int* freel, int* cursor, int* anchor_tok, int* records, int* promote_src,
