@@ -615,8 +615,9 @@ __global__ __launch_bounds__(64 * kAttnSC) __attribute__((amdgpu_waves_per_eu(2)
 // attn_group_kernel), folded here the same way. Super-chunks with
 // per-row chunks (the last ones of a row) are folded here from their chunk
 // partials, exactly as attn_kernel folds the others, and join their span's
-// fold in order. grid = (items, kv heads), block = 4 waves, one unit at a
-// time per wave.
+// fold in order. grid = (items, kv heads, kAttnUnits / 4), block = 4 waves,
+// one unit per wave (the units of an item are independent, and each one's
+// folds are a chain of dependent loads, so they run side by side).
 template <int HD>
 __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const RowInfo* __restrict__ rows,
                                     const float* __restrict__ mix, const float* __restrict__ part,
@@ -628,7 +629,9 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
   const int nq = D.nq, h = blockIdx.y, rep = nq / D.nkv, units = it.nrows * rep;
   const bool grouped = span_states && it.lead != 1;
   const int lane = threadIdx.x & 63;
-  for (int u = threadIdx.x >> 6; u < units; u += blockDim.x >> 6) {
+  {
+    const int u = blockIdx.z * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    if (u >= units) return;
     const int row = it.row0 + u / rep, qh = h * rep + u % rep;
     const RowInfo& R = rows[row];
     const int lim = R.ncommit + R.n_anc;
@@ -778,12 +781,13 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const dim3 cgrid(nitems, D.nkv, kAttnUnits / 4);
   if (D.hd == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
-                       out, D, lam, lattice, nsc_max, span_states);
+    hipLaunchKernelGGL((attn_combine_kernel<128>), cgrid, dim3(256), 0, st, items, rows, mix, part, out, D, lam,
+                       lattice, nsc_max, span_states);
   else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), dim3(nitems, D.nkv), dim3(256), 0, st, items, rows, mix, part,
-                       out, D, lam, lattice, nsc_max, span_states);
+    hipLaunchKernelGGL((attn_combine_kernel<64>), cgrid, dim3(256), 0, st, items, rows, mix, part, out, D, lam,
+                       lattice, nsc_max, span_states);
   return hipGetLastError();
 }
 
