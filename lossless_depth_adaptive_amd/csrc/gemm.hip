@@ -964,18 +964,17 @@ __global__ __launch_bounds__(kWideThreads) void gemm_split_reduce_kernel(const G
   epilogue_tile<EPI, kWideThreads, 64>(args, G, tile, [&](int rl, int c) { return val[rl][c]; }, rs_sh, scr);
 }
 
-// One wave per row of [row0, row0 + nrows): reduce the per-tile summaries to
-// the row's token and margin.
-__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int row0, int nrows,
+// One workgroup of four waves per row of [row0, row0 + nrows): reduce the
+// per-tile summaries to the row's token and margin (the merge is exact, so
+// how the tiles are split among the threads does not change the result).
+__global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, int row0,
                                    const RowInfo* __restrict__ rows, int P, int* __restrict__ cand,
                                    float* __restrict__ margin) {
-  const int idx = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (idx >= nrows) return;
-  const int row = row0 + idx;
+  const int row = row0 + blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float b = -INFINITY, s = -INFINITY;
   int i = 0x7fffffff;
-  for (int t = lane; t < ntiles; t += 64) {
+  for (int t = threadIdx.x; t < ntiles; t += blockDim.x) {
     const float* p = part + ((size_t)row * ntiles + t) * 3;
     top2_merge(b, i, s, p[0], __float_as_int(p[1]), p[2]);
   }
@@ -985,7 +984,16 @@ __global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, i
     const float s2 = __shfl_xor(s, off);
     top2_merge(b, i, s, b2, i2, s2);
   }
+  __shared__ float wb[4], ws[4];
+  __shared__ int wi[4];
   if (lane == 0) {
+    wb[w] = b;
+    wi[w] = i;
+    ws[w] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < (int)(blockDim.x >> 6); ++k) top2_merge(b, i, s, wb[k], wi[k], ws[k]);
     const RowInfo& ri = rows[row];
     if (i < 0 || i >= ntiles * 16) i = 0;  // unreachable for finite logits; keeps token ids in range
     cand[ri.seq * P + ri.phys] = i;
@@ -993,7 +1001,8 @@ __global__ void head_reduce_kernel(const float* __restrict__ part, int ntiles, i
   }
 }
 
-// Embedding gather for rows with tok >= 0 (prefill and autoregressive rows):
+// Embedding gather for rows with tok >= 0 (explorer 0 of a lattice round, prefill and
+// autoregressive rows):
 // h = E[tok] in fp32, xn = h * g0 (first layer's attention-norm weight) and the
 // per-16-column sums of squares.
 template <typename T>
@@ -1114,9 +1123,7 @@ template hipError_t launch_gemm<bf16_t>(const GemmArgs&, int, hipStream_t);
 hipError_t launch_head_reduce(const float* part, int ntiles, int row0, int nrows, const RowInfo* rows, int P,
                               int* cand, float* margin, hipStream_t st) {
   if (nrows == 0) return hipSuccess;
-  const int wpb = 4;
-  hipLaunchKernelGGL(head_reduce_kernel, dim3((nrows + wpb - 1) / wpb), dim3(64 * wpb), 0, st, part,
-                     ntiles, row0, nrows, rows, P, cand, margin);
+  hipLaunchKernelGGL(head_reduce_kernel, dim3(nrows), dim3(256), 0, st, part, ntiles, row0, rows, P, cand, margin);
   return hipGetLastError();
 }
 
