@@ -6,10 +6,11 @@
 // header alone (DEX_HD empty) under AddressSanitizer.
 //
 // The lattice is numbered as a heap (Depth Exploration for LLM Decoding,
-// Section 3.2 "Lattice structure"): round q of a tree runs heap level q, the
-// nodes 2^q - 1 .. 2^(q+1) - 2; node n belongs to explorer ctz(n + 1) and
-// reads popcount(n + 1) - 1 explore-buffer ancestors. After a commit with
-// branch b the kept subtree has done N - 1 - b rounds (Algorithm 1's collapse).
+// Section 3.2, Figure 2 and "Finite-state control and collapse"): round q of
+// a tree runs heap level q, the nodes 2^q - 1 .. 2^(q+1) - 2; node n belongs
+// to explorer ctz(n + 1) and reads popcount(n + 1) - 1 explore-buffer
+// ancestors. After a commit with branch b the kept subtree has done N - 1 - b
+// rounds (Algorithm 1's collapse).
 #pragma once
 #include <algorithm>
 #include <cstring>

@@ -7,12 +7,12 @@
 // sized exactly as the library sizes its host buffers, so a write past one is
 // an ASan report. Prints "plan checks ok" and exits 0 when every check holds.
 //
-// Facts checked (Depth Exploration for LLM Decoding, Section 3.2 "Lattice
-// structure" and "Commit process"; Algorithm 1): round q of a tree runs heap
-// level q (nodes 2^q - 1 .. 2^(q+1) - 2, explorer ctz(n + 1)); a tree commits
-// in the round that reaches the final explorer; after a commit with branch b
-// the next commit comes b + 1 rounds later, so K commits take
-// N + sum over the first K - 1 commits of (b + 1) rounds.
+// Facts checked (Depth Exploration for LLM Decoding, Section 3.2, Figure 2,
+// "Finite-state control and collapse" and "Commit process"; Algorithm 1):
+// round q of a tree runs heap level q (nodes 2^q - 1 .. 2^(q+1) - 2, explorer
+// ctz(n + 1)); a tree commits in the round that reaches the final explorer;
+// after a commit with branch b the next commit comes b + 1 rounds later, so K
+// commits take N + sum over the first K - 1 commits of (b + 1) rounds.
 #include <cstdio>
 #include <cstdlib>
 #include <map>
