@@ -44,7 +44,7 @@ def _dispatches(db):
 def gemm_epilogue(name: str):
     """Epilogue id of a GEMM dispatch (0 QKV, 1 residual, 2 SwiGLU, 3 exit head,
     4/5 adapters), or None for other kernels. gemm_kernel<T, MB, NB, EPI>,
-    gemm_wide_kernel<EPI, SPLIT, WT>, gemm_split_reduce_kernel<EPI>."""
+    gemm_wide_kernel<EPI, SPLIT, WT, NWV>, gemm_split_reduce_kernel<EPI>."""
     k = _short(name)
     if "<" not in k:
         return None
@@ -157,9 +157,9 @@ def traffic(fetch_db, write_db, bench_json, workload=None):
     fg, wg = _gemm_window(f)[-n:], _gemm_window(w)[-n:]
     fetch = sum(v for _, _, v in fg) * 1024.0 * f_scale
     write = sum(v for _, _, v in wg) * 1024.0 * w_scale
+    fpl, wpl = fetch / max(1, len(fg)), write / max(1, len(wg))
     return dict(workload=workload or bench["config"]["workload"], launches=n,
-                fetch_bytes_per_launch=fetch / n, write_bytes_per_launch=write / max(1, len(wg)),
-                bytes_per_launch=fetch / n + write / max(1, len(wg)),
+                fetch_bytes_per_launch=fpl, write_bytes_per_launch=wpl, bytes_per_launch=fpl + wpl,
                 algorithmic_bytes_per_launch=rl["algorithmic_bytes_per_launch"],
                 fetch_scale=f_scale, write_scale=w_scale, library=bench.get("library", {}).get("digest"),
                 note="layer GEMM launches (exit head excluded) of the HIP-event-timed rounds; counters in KiB "
