@@ -59,7 +59,7 @@ from lossless_depth_adaptive_amd.build import library_digest  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 # Oracle commits timed by default (about 10-30 s of host work on 16 cores).
-CPU_COMMITS = {"tiny_f32": 32, "llama7b_x4_greedy": 6, "llama7b_x8_sample": 3, "llama13b_x8_b8": 3,
+CPU_COMMITS = {"tiny_f32": 32, "llama7b_x4_greedy": 6, "llama7b_x8_sample": 3, "llama13b_x8_b8": 2,
                "qwen8b_x9_b16": 2}
 
 
