@@ -332,10 +332,10 @@ def main():
                        gb_per_s=round(v["bytes"] / (v["ms"] * 1e-3) / 1e9, 1) if v["ms"] else None,
                        tflops=round(v["flops"] / (v["ms"] * 1e-3) / 1e12, 2) if v["ms"] else None)
                for k, v in prof.items()}
-    if prof["attention"]["ms"]:
-        # the library stores each K/V value as a bf16 (hi, lo) pair, 4 bytes; at
-        # 2 bytes per value the K/V stream (all but the per-row query and output
-        # vectors, under 1% of it) is half as many bytes
+    if prof["attention"]["ms"] and w.dtype == "f32":
+        # an fp32 model's cache holds each K/V value as a bf16 (hi, lo) pair, 4
+        # bytes; at 2 bytes per value the K/V stream (all but the per-row query
+        # and output vectors, under 1% of it) is half as many bytes
         classes["attention"]["gb_per_s_kv_2_bytes"] = round(classes["attention"]["gb_per_s"] / 2, 1)
     step_bytes = sum(v["bytes"] for v in prof.values()) / args.steps
     roofline["timing"] = (f"HIP events around each launch over {args.steps} eager rounds that follow the timed "

@@ -22,6 +22,7 @@ constexpr int kWideKPB = DEX_WIDE_KPB;
 
 typedef unsigned short bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -51,7 +52,7 @@ struct GemmArgs {
   const float* cosT;
   const float* sinT;
   float* qout;      // [rows][nq][hd], pre-scaled by qscale
-  bf16_t* kvc;      // committed K/V (tiles of (hi, lo) pairs)
+  bf16_t* kvc;      // committed K/V (tiles of 16-bit planes)
   bf16_t* exb;      // explore-buffer K/V
   int lattice, lam;  // layer slot lam; layer = layer_of(dims, lattice, row's stage, lam)
   float qscale;
@@ -83,29 +84,31 @@ __device__ __forceinline__ int xcd_block(int b, int nb) {
   return x * q + (x < rem ? x : rem) + k;
 }
 
-// K/V storage. Every K or V value x is kept as a bfloat16 pair (hi, lo) with
-// hi = bf16(x) and lo = bf16(x - hi), both round-to-nearest-even, so that the
-// attention products run on bf16 MFMA with about 2^-17 relative error.
-//
+// K/V storage. Values are stored in kvp 16-bit planes, all rounded to nearest
+// even: kvp = 1 for bfloat16 models, one fp16 value (11 significant bits,
+// three more than the model's bfloat16; 2 bytes, the K/V stream of a bf16
+// cache); kvp = 2 for fp32 models, a bfloat16 pair hi = bf16(x),
+// lo = bf16(x - hi) (about 2^-17 relative, 4 bytes). Either way attention runs
+// on 16-bit MFMA operands.
 // Committed cache: per (sequence, layer, kv head) a run of Cs / kKvTile tiles
-// of 32 positions, 128 * hd bf16 each:
-//   K plane pl (0 hi, 1 lo): [pl][hd / 8][slot][8] at offset pl * 32 hd, with
-//     position k of the tile at slot 16 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3);
-//   V plane pl: [pl][hd][32 positions] at offset 64 hd + pl * 32 hd.
-// Explore entry of one (sequence, node slot, layer slot, kv head): 4 hd bf16,
-//   K hi, K lo, V hi, V lo, each [hd].
+// of 32 positions, 64 kvp hd values each:
+//   K plane pl: [hd / 8][slot][8] at offset pl * 32 hd, with position k of the
+//     tile at slot 16 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3);
+//   V plane pl: [hd][32 positions] at offset 32 kvp hd + pl * 32 hd.
+// Explore entry of one (sequence, node slot, layer slot, kv head): 2 kvp hd
+//   values, the K planes then the V planes, each [hd].
 __host__ __device__ inline int kv_slot(int k) { return 16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
 __host__ __device__ inline size_t kv_head_base(const ModelDims& D, int seq, int layer, int h) {
-  return (((size_t)seq * D.L + layer) * D.nkv + h) * (size_t)D.Cs * D.hd * 4;
+  return (((size_t)seq * D.L + layer) * D.nkv + h) * (size_t)D.Cs * D.hd * 2 * D.kvp;
 }
-__host__ __device__ inline size_t kv_elem(int hd, int pos, int kv, int plane, int d) {
-  const size_t tile = (size_t)(pos / kKvTile) * 128 * hd;
+__host__ __device__ inline size_t kv_elem(int hd, int kvp, int pos, int kv, int plane, int d) {
+  const size_t tile = (size_t)(pos / kKvTile) * 64 * kvp * hd;
   const int k = pos % kKvTile;
   return kv == 0 ? tile + (size_t)plane * 32 * hd + (d >> 3) * 256 + kv_slot(k) * 8 + (d & 7)
-                 : tile + 64 * (size_t)hd + (size_t)plane * 32 * hd + (size_t)d * 32 + k;
+                 : tile + (size_t)(kvp + plane) * 32 * hd + (size_t)d * 32 + k;
 }
 __host__ __device__ inline size_t ex_base(const ModelDims& D, int seq, int phys, int lam, int h) {
-  return ((((size_t)seq * D.P + phys) * D.S + lam) * D.nkv + h) * 4 * (size_t)D.hd;
+  return ((((size_t)seq * D.P + phys) * D.S + lam) * D.nkv + h) * 2 * D.kvp * (size_t)D.hd;
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -134,12 +137,37 @@ __device__ __forceinline__ void split_bf2(float a, float b, unsigned& hi, unsign
   hi = f2bf2(a, b);
   lo = f2bf2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
 }
-// The (hi, lo) bfloat16 pair of x described above.
-__device__ __forceinline__ void split_bf(float x, bf16_t& hi, bf16_t& lo) {
-  unsigned h, l;
-  split_bf2(x, 0.f, h, l);
-  hi = (bf16_t)(h & 0xFFFFu);
-  lo = (bf16_t)(l & 0xFFFFu);
+
+// Two floats to packed fp16 (a in the low half), round-to-nearest-even, with
+// magnitudes above the largest finite fp16 (65504) saturated to it (NaN
+// passes through). Every float-to-fp16 rounding of the library goes through
+// here.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float sat_f16(float x) { return x > 65504.f ? 65504.f : (x < -65504.f ? -65504.f : x); }
+__device__ __forceinline__ unsigned f2h2(float a, float b) {
+  const f32x2_t f = {sat_f16(a), sat_f16(b)};
+  const f16x2_t v = __builtin_convertvector(f, f16x2_t);
+  unsigned u;
+  __builtin_memcpy(&u, &v, 4);
+  return u;
+}
+__device__ __forceinline__ float h2f(unsigned bits16) {
+  _Float16 h;
+  const unsigned short b = (unsigned short)bits16;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+// The (hi, lo) fp16 pairs of two values, packed (a in the low halves).
+__device__ __forceinline__ void split_h2(float a, float b, unsigned& hi, unsigned& lo) {
+  hi = f2h2(a, b);
+  lo = f2h2(a - h2f(hi & 0xFFFFu), b - h2f(hi >> 16));
+}
+// The (hi, lo) pair of two values in the 16-bit format of kvp planes: fp16
+// (kvp = 1) or bfloat16 (kvp = 2).
+template <int KVP>
+__device__ __forceinline__ void split16(float a, float b, unsigned& hi, unsigned& lo) {
+  if constexpr (KVP == 1) split_h2(a, b, hi, lo);
+  else split_bf2(a, b, hi, lo);
 }
 
 // Host-visible kernel launchers (defined in the .hip files).

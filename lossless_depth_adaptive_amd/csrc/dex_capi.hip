@@ -664,7 +664,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
   // explore entries.
   std::vector<double> attn_bytes(N, 0.0), attn_flops(N, 0.0);
   if (ctx->prof) {
-    const double kvrow = 2.0 * ctx->D.nkv * ctx->D.hd * 4;
+    const double kvrow = 2.0 * ctx->D.nkv * ctx->D.hd * 2 * ctx->D.kvp;   // K and V, stored bytes
     for (int s = 0; s < B; ++s) {
       if (!live[s]) continue;
       const int q = ar ? 0 : ctx->q_[s];
@@ -741,7 +741,7 @@ int run_step(dex_ctx* ctx, bool ar, dex_commit* out, int32_t cap, int32_t* n_out
       HIPCHK(hipMemcpyAsync(ctx->h_records, ctx->records, (size_t)B * 5 * 4, hipMemcpyDeviceToHost, st));
     }
     prof_end(ctx, mk, ncommit ? (ar ? 1 : 2) : 0,
-             ar ? 0.0 : 2.0 * ncommit * ctx->L * 2.0 * ctx->D.nkv * ctx->D.hd * 4, 0);
+             ar ? 0.0 : 2.0 * ncommit * ctx->L * 2.0 * ctx->D.nkv * ctx->D.hd * 2 * ctx->D.kvp, 0);
     return DEX_OK;
   };
   // Timed rounds run eagerly: an event recorded inside a replayed graph does
@@ -927,6 +927,7 @@ int dex_create(const dex_model_config* cfg, const dex_weights* w, const int32_t*
   D.B = opt->max_batch;
   D.Cmax = opt->max_context;
   D.Cs = (D.Cmax + kKvTile - 1) / kKvTile * kKvTile;
+  D.kvp = kv_planes(cfg->dtype);
   D.eps = cfg->rms_eps;
   ctx->embed = ctx->at(wp.embed);
   ctx->head = ctx->at(wp.head);

@@ -221,24 +221,27 @@ __device__ __forceinline__ void epilogue_tile(const GemmArgs& args, const GemmGr
       const RowInfo& R = args.rows[row];
       const float x1 = val(rl, c) * rs[rl], x2 = val(rl, c + 8) * rs[rl];
       const int layer = layer_of(D, args.lattice, R.stage, args.lam);
-      // K/V go out as (hi, lo) bf16 pairs: committed tile or explore entry.
+      // K/V go out in the cache's format (fp16, or (hi, lo) bf16 pairs):
+      // committed tile or explore entry.
       bf16_t* kvbase = nullptr;
       int kv = 0;
+      const int kvp = D.kvp;
       if (head >= D.nq) {
         kv = head < D.nq + D.nkv ? 0 : 1;
         const int hh = head - D.nq - kv * D.nkv;
         kvbase = R.kv_commit ? args.kvc + kv_head_base(D, R.seq, layer, hh)
-                             : args.exb + ex_base(D, R.seq, R.phys, args.lam, hh) + (size_t)kv * 2 * hd;
+                             : args.exb + ex_base(D, R.seq, R.phys, args.lam, hh) + (size_t)kv * kvp * hd;
       }
       auto put = [&](int dd, float v) {
-        bf16_t hi, lo;
-        split_bf(v, hi, lo);
+        unsigned hi, lo = 0;
+        if (kvp == 1) hi = f2h2(v, 0.f);
+        else split_bf2(v, 0.f, hi, lo);
         if (R.kv_commit) {
-          kvbase[kv_elem(hd, R.pos, kv, 0, dd)] = hi;
-          kvbase[kv_elem(hd, R.pos, kv, 1, dd)] = lo;
+          kvbase[kv_elem(hd, kvp, R.pos, kv, 0, dd)] = (bf16_t)hi;
+          if (kvp == 2) kvbase[kv_elem(hd, kvp, R.pos, kv, 1, dd)] = (bf16_t)lo;
         } else {
-          kvbase[dd] = hi;
-          kvbase[hd + dd] = lo;
+          kvbase[dd] = (bf16_t)hi;
+          if (kvp == 2) kvbase[hd + dd] = (bf16_t)lo;
         }
       };
       if (kv == 1) {                         // values: natural column order
@@ -547,18 +550,21 @@ __device__ __forceinline__ void qkv_epilogue_wide(const GemmArgs& args, const Ge
   const float rsl = rs[rl];
   const float* cosr = args.cosT + (size_t)pos * half;
   const float* sinr = args.sinT + (size_t)pos * half;
-  // 8 consecutive values as (hi, lo) bf16 runs at hp and lp (16-byte aligned).
-  auto put8 = [](bf16_t* hp, bf16_t* lp, const float* v) {
+  // 8 consecutive values in the cache's format: fp16 at hp (kvp = 1), or
+  // (hi, lo) bf16 runs at hp and lp (16-byte aligned).
+  const int kvp = D.kvp;
+  auto put8 = [kvp](bf16_t* hp, bf16_t* lp, const float* v) {
     u32x4_t h, l;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       unsigned hk, lk;
-      split_bf2(v[2 * k], v[2 * k + 1], hk, lk);
+      if (kvp == 1) hk = f2h2(v[2 * k], v[2 * k + 1]), lk = 0;
+      else split_bf2(v[2 * k], v[2 * k + 1], hk, lk);
       h[k] = hk;
       l[k] = lk;
     }
     *(u32x4_t*)hp = h;
-    *(u32x4_t*)lp = l;
+    if (kvp == 2) *(u32x4_t*)lp = l;
   };
   for (int tl = w; tl < BT && tb0 + tl < ntiles; tl += NW) {
     const int tile = tb0 + tl;
@@ -577,14 +583,19 @@ __device__ __forceinline__ void qkv_epilogue_wide(const GemmArgs& args, const Ge
       if (commit) {
         bf16_t* base = args.kvc + kv_head_base(D, seq, layer, hh);
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          bf16_t hi, lo;
-          split_bf(x[c], hi, lo);
-          base[kv_elem(hd, pos, 1, 0, 16 * u + c)] = hi;
-          base[kv_elem(hd, pos, 1, 1, 16 * u + c)] = lo;
+        for (int c = 0; c < 16; c += 2) {
+          unsigned hi, lo = 0;
+          if (kvp == 1) hi = f2h2(x[c], x[c + 1]);
+          else split_bf2(x[c], x[c + 1], hi, lo);
+          base[kv_elem(hd, kvp, pos, 1, 0, 16 * u + c)] = (bf16_t)hi;
+          base[kv_elem(hd, kvp, pos, 1, 0, 16 * u + c + 1)] = (bf16_t)(hi >> 16);
+          if (kvp == 2) {
+            base[kv_elem(hd, kvp, pos, 1, 1, 16 * u + c)] = (bf16_t)lo;
+            base[kv_elem(hd, kvp, pos, 1, 1, 16 * u + c + 1)] = (bf16_t)(lo >> 16);
+          }
         }
       } else {
-        bf16_t* base = args.exb + ex_base(D, seq, phys, args.lam, hh) + 2 * (size_t)hd + 16 * u;
+        bf16_t* base = args.exb + ex_base(D, seq, phys, args.lam, hh) + (size_t)kvp * hd + 16 * u;
         put8(base, base + hd, x);
         put8(base + 8, base + hd + 8, x + 8);
       }
@@ -604,8 +615,8 @@ __device__ __forceinline__ void qkv_epilogue_wide(const GemmArgs& args, const Ge
       const int hh = head - D.nq;
       if (commit) {
         bf16_t* base = args.kvc + kv_head_base(D, seq, layer, hh);
-        put8(base + kv_elem(hd, pos, 0, 0, 8 * u), base + kv_elem(hd, pos, 0, 1, 8 * u), o1);
-        put8(base + kv_elem(hd, pos, 0, 0, 8 * u + half), base + kv_elem(hd, pos, 0, 1, 8 * u + half), o2);
+        put8(base + kv_elem(hd, kvp, pos, 0, 0, 8 * u), base + kv_elem(hd, kvp, pos, 0, 1, 8 * u), o1);
+        put8(base + kv_elem(hd, kvp, pos, 0, 0, 8 * u + half), base + kv_elem(hd, kvp, pos, 0, 1, 8 * u + half), o2);
       } else {
         bf16_t* base = args.exb + ex_base(D, seq, phys, args.lam, hh) + 8 * u;
         put8(base, base + hd, o1);

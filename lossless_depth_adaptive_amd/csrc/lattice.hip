@@ -187,9 +187,10 @@ __global__ void promote_kernel(const SeqPlan* __restrict__ plans, const int* __r
   const int phys = promote_src[s * kMaxN + j];
   const bf16_t* src = exb + ex_base(D, s, phys, lam, h);
   bf16_t* dst = kvc + kv_head_base(D, s, layer, h);
-  for (int t = threadIdx.x; t < 4 * D.hd; t += blockDim.x) {   // K hi, K lo, V hi, V lo, each [hd]
-    const int kv = t / (2 * D.hd), plane = (t / D.hd) & 1, i = t % D.hd;
-    dst[kv_elem(D.hd, pl.C, kv, plane, i)] = src[t];
+  const int kvp = D.kvp;
+  for (int t = threadIdx.x; t < 2 * kvp * D.hd; t += blockDim.x) {   // the K planes, then the V planes, each [hd]
+    const int kv = t / (kvp * D.hd), plane = (t / D.hd) % kvp, i = t % D.hd;
+    dst[kv_elem(D.hd, kvp, pl.C, kv, plane, i)] = src[t];
   }
 }
 

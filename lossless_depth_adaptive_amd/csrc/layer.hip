@@ -3,6 +3,8 @@
 // Every row is computed from that row's own inputs in a fixed order, so a node
 // of the depth-position lattice and the same context decoded autoregressively
 // produce identical bits.
+#include <type_traits>
+
 #include "common.h"
 
 namespace dex {
@@ -14,8 +16,11 @@ namespace dex {
 // explore-buffer entries of its ancestors at positions ncommit.. (its own
 // entry last). All rows of a work item share one sequence and layer.
 //
-// Products run on bf16 MFMA (v_mfma_f32_16x16x32_bf16) with every fp32
-// operand split into a bf16 pair: a.b is taken as hi.hi + hi.lo + lo.hi.
+// Products run on 16-bit MFMA in the cache's format (common.h). fp16 K/V
+// (bfloat16 models): v_mfma_f32_16x16x32_f16 with the fp32 query and softmax
+// weights split into an fp16 pair, k.q taken as k.q_hi + k.q_lo (and p.v the
+// same way). bfloat16 (hi, lo) K/V (fp32 models): v_mfma_f32_16x16x32_bf16
+// with both operands split, a.b taken as hi.hi + hi.lo + lo.hi.
 // A work item is one MFMA tile of up to 16 units (row, query head) of one kv
 // head. Scores come out transposed, S^T = K Q^T: lane (g, n) = (lane / 16,
 // lane % 16) holds unit n's scores for keys 8g .. 8g+7 of a 32-key chunk, which
@@ -53,6 +58,11 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
   __builtin_memcpy(&r, &v, 16);
   return r;
 }
+__device__ __forceinline__ f16x8_t as_f16x8(const u32x4_t& v) {
+  f16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
 
 // acc += A B^T over one 32-element k step, operands split into (hi, lo).
 __device__ __forceinline__ f32x4_t mma3(f32x4_t acc, const u32x4_t& ah, const u32x4_t& al, const u32x4_t& bh,
@@ -63,11 +73,27 @@ __device__ __forceinline__ f32x4_t mma3(f32x4_t acc, const u32x4_t& ah, const u3
   return acc;
 }
 
+// acc += A B^T over one 32-element k step in the format of KVP planes: A
+// (the cached operand) fp16 and B split into an fp16 (hi, lo) pair (KVP = 1):
+// A.B_hi, then A.B_lo; or both bfloat16 pairs (KVP = 2), mma3.
+template <int KVP>
+__device__ __forceinline__ f32x4_t mma_kv(f32x4_t acc, const u32x4_t& ah, const u32x4_t& al, const u32x4_t& bh,
+                                          const u32x4_t& bl) {
+  if constexpr (KVP == 1) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ah), as_f16x8(bh), acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(ah), as_f16x8(bl), acc, 0, 0, 0);
+  } else {
+    return mma3(acc, ah, al, bh, bl);
+  }
+}
+
+// Eight fp32 values as (hi, lo) pairs in the 16-bit format of KVP planes.
+template <int KVP>
 __device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     unsigned h, l;
-    split_bf2(x[2 * i], x[2 * i + 1], h, l);
+    split16<KVP>(x[2 * i], x[2 * i + 1], h, l);
     hi[i] = h;
     lo[i] = l;
   }
@@ -93,27 +119,15 @@ __device__ __forceinline__ void fold(float& M, float& L, float* A, float m, floa
 // (unit n, dims 32s + 8g .. 32s + 8g + 7); ksrc(t, s, hi, lo): its K operand for
 // row block t (0, 1) and 32-dim step s; vsrc(b, hi, lo): its V^T operand for
 // output dims [16b, 16b + 16), as loaded; vpost(b, hi, lo) then fixes it up
-// (masks, gathered values) once the loads have landed. valid8 bit i: key
-// 8g + i counts for this lane's unit. Out: acc[b][r] = the unit's unnormalised
-// output at dim 16b + 4g + r, and the chunk's m and l (m = -inf when no key
-// counts). EAGER: all K and V loads of the chunk are issued before the first
-// MFMA, so the chunk costs one memory latency (at the price of registers);
-// otherwise each operand is loaded where it is used. The arithmetic is the
-// same either way.
-template <int HD, bool EAGER, typename QSrc, typename KSrc, typename VSrc, typename VPost>
+// (masks, gathered values). The lo operands are read only with KVP = 2.
+// valid8 bit i: key 8g + i counts for this lane's unit. Out: acc[b][r] = the
+// unit's unnormalised output at dim 16b + 4g + r, and the chunk's m and l
+// (m = -inf when no key counts).
+template <int HD, int KVP, typename QSrc, typename KSrc, typename VSrc, typename VPost>
 __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, VPost vpost, unsigned valid8,
                                               f32x4_t* acc, float& m, float& l) {
   constexpr int NS = HD / 32, NB = HD / 16;
   u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
-  if constexpr (EAGER) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) ksrc(t, s, kh[t][s], kl[t][s]);
-#pragma unroll
-    for (int b = 0; b < NB; ++b) vsrc(b, vh[b], vl[b]);
-    __builtin_amdgcn_sched_barrier(0);
-  }
   f32x4_t st[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -121,9 +135,9 @@ __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, V
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4_t qh, ql;
-      if constexpr (!EAGER) ksrc(t, s, kh[t][s], kl[t][s]);
+      ksrc(t, s, kh[t][s], kl[t][s]);
       qsrc(s, qh, ql);
-      st[t] = mma3(st[t], kh[t][s], kl[t][s], qh, ql);
+      st[t] = mma_kv<KVP>(st[t], kh[t][s], kl[t][s], qh, ql);
     }
   }
   float sv[8];
@@ -146,25 +160,26 @@ __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, V
   m = mx;
   l = ls;
   u32x4_t ph, pl;
-  split8(p, ph, pl);
+  split8<KVP>(p, ph, pl);
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    if constexpr (!EAGER) vsrc(b, vh[b], vl[b]);
+    vsrc(b, vh[b], vl[b]);
     vpost(b, vh[b], vl[b]);
-    acc[b] = mma3(f32x4_t{0.f, 0.f, 0.f, 0.f}, vh[b], vl[b], ph, pl);
+    acc[b] = mma_kv<KVP>(f32x4_t{0.f, 0.f, 0.f, 0.f}, vh[b], vl[b], ph, pl);
   }
 }
 
 // V^T operand fix-up of the shared chunks: positions at or past vlim (the
 // largest key limit of the tile) may hold stale or never-written values; their
 // elements are zeroed so that p = 0 contributes exact zeros.
+template <int KVP>
 __device__ __forceinline__ void mask_v(u32x4_t& vh, u32x4_t& vl, int nv) {
   if (nv < 8) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const unsigned keep = (2 * i + 1 < nv ? 0xFFFF0000u : 0u) | (2 * i < nv ? 0xFFFFu : 0u);
       vh[i] &= keep;
-      vl[i] &= keep;
+      if constexpr (KVP == 2) vl[i] &= keep;
     }
   }
 }
@@ -199,13 +214,13 @@ template <int HD, int MAXT> struct AttnSmem {
       alignas(16) float red[kAttnSC][kAttnUnits][HD + 4];   // chunk partials; rows 16-byte aligned
       bf16_t qsh[MAXT][2][kAttnUnits][HD + 8];   // queries as (hi, lo), rows padded by 16 bytes
     } m;
-    bf16_t ev[kAttnSC][kMaxN][2 * HD];      // per wave: V hi, V lo of the unit's explore entries
+    bf16_t ev[kAttnSC][kMaxN][2 * HD];      // per wave: the V planes of the unit's explore entries
   };
 };
 
 // Queries of a tile of `units` units from row row0 on, split into (hi, lo),
 // into LDS rows padded by 16 bytes. Threads t0, t0 + step, ... share the work.
-template <int HD>
+template <int HD, int KVP>
 __device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], int row0, int units, int h,
                                             const float* __restrict__ q, const ModelDims& D, int t0, int step) {
   const int rep = D.nq / D.nkv;
@@ -222,7 +237,7 @@ __device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], i
       }
     }
     u32x4_t hi, lo;
-    split8(x, hi, lo);
+    split8<KVP>(x, hi, lo);
     *(u32x4_t*)&dst[0][u][d8] = hi;
     *(u32x4_t*)&dst[1][u][d8] = lo;
   }
@@ -234,7 +249,7 @@ __device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], i
 // query and are not stored), into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
 // A column's result depends only on its own query, so each unit gets the bits
 // it gets in a shared tile.
-template <int HD>
+template <int HD, int KVP>
 __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, int c, int rr,
                                 const RowInfo* __restrict__ rows, const float* __restrict__ q,
                                 const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
@@ -247,24 +262,25 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
   const RowInfo& Ru = rows[row];
   const int ncu = Ru.ncommit, limu = Ru.ncommit + Ru.n_anc;
   const bool active = rr < it.nrows && c <= it.xc1 && p0 < limu;
-  const size_t eslot = (size_t)D.S * D.nkv * 4 * HD;  // bf16 between node slots
+  const size_t eslot = (size_t)D.S * D.nkv * 2 * KVP * HD;  // 16-bit values between node slots
   const bf16_t* eb = exb + ex_base(D, it.seq, 0, lam, h);
   bf16_t (*ev)[2 * HD] = sm.ev[w];
-  if (active) {
-    for (int t = lane; t < (limu - ncu) * (HD / 4); t += 64) {
-      const int j = t / (HD / 4), o = 8 * (t % (HD / 4));
-      *(u32x4_t*)&ev[j][o] = *(const u32x4_t*)(eb + Ru.anc[j] * eslot + 2 * HD + o);
+  if (active) {   // the V planes (KVP HD values) of each explore entry, 16 bytes a thread
+    constexpr int PIECES = KVP * HD / 8;
+    for (int t = lane; t < (limu - ncu) * PIECES; t += 64) {
+      const int j = t / PIECES, o = 8 * (t % PIECES);
+      *(u32x4_t*)&ev[j][o] = *(const u32x4_t*)(eb + Ru.anc[j] * eslot + KVP * HD + o);
     }
   }
   __syncthreads();
   if (!active) return;
   const int layer = layer_of(D, lattice, it.stage, lam);
-  const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 128 * HD;
+  const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 64 * KVP * HD;
   const float* qr = q + ((size_t)row * D.nq + h * rep + min(n, rep - 1)) * HD;
   auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
     const f32x4_t a = *(const f32x4_t*)(qr + 32 * s + 8 * g), b = *(const f32x4_t*)(qr + 32 * s + 8 * g + 4);
     const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    split8(x, qh, ql);
+    split8<KVP>(x, qh, ql);
   };
   auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
     const int p = p0 + 8 * (n >> 2) + 4 * t + (n & 3);
@@ -281,14 +297,14 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
       return;
     }
     kh = *(const u32x4_t*)kp;
-    kl = *(const u32x4_t*)(kp + lo_off);
+    if constexpr (KVP == 2) kl = *(const u32x4_t*)(kp + lo_off);
   };
   auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
     const int pb = p0 + 8 * g, dd = 16 * b + n;
     if (pb < ncu) {
-      const bf16_t* vp = tb + 64 * HD + dd * 32 + 8 * g;
+      const bf16_t* vp = tb + 32 * KVP * HD + dd * 32 + 8 * g;
       vh = *(const u32x4_t*)vp;
-      vl = *(const u32x4_t*)(vp + 32 * HD);
+      if constexpr (KVP == 2) vl = *(const u32x4_t*)(vp + 32 * HD);
     } else {
       vh = vl = u32x4_t{0u, 0u, 0u, 0u};
     }
@@ -301,11 +317,14 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
     for (int i = 0; i < 8; ++i) {
       const int p = pb + i;
       if (p < ncu) continue;
-      const unsigned hv = p < limu ? ev[p - ncu][dd] : 0u, lv = p < limu ? ev[p - ncu][HD + dd] : 0u;
+      const unsigned hv = p < limu ? ev[p - ncu][dd] : 0u;
       const int sh = 16 * (i & 1);
       const unsigned keep = ~(0xFFFFu << sh);
       vh[i >> 1] = (vh[i >> 1] & keep) | (hv << sh);
-      vl[i >> 1] = (vl[i >> 1] & keep) | (lv << sh);
+      if constexpr (KVP == 2) {
+        const unsigned lv = p < limu ? ev[p - ncu][HD + dd] : 0u;
+        vl[i >> 1] = (vl[i >> 1] & keep) | (lv << sh);
+      }
     }
   };
   unsigned valid8 = 0;
@@ -313,7 +332,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
   for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < limu ? 1u : 0u) << i;
   f32x4_t acc[NB];
   float m, l;
-  chunk_partial<HD, false>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
+  chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
   if (n < rep)
     store_partial<HD>(mix + (((size_t)row * D.nq + h * rep + n) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
                       acc, m, l, g);
@@ -331,7 +350,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
 // (the first as it is, each later one that holds keys of the unit by the fold)
 // and write it to part[row][qh][span]. Super-chunks with per-row chunks come
 // last in a row's keys, so the span state covers the ones before them.
-template <int HD, int MAXT, bool SPAN>
+template <int HD, int MAXT, bool SPAN, int KVP>
 __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __restrict__ items, int first, int count,
                                    int h, int sc0, int sc1, int span, const RowInfo* __restrict__ rows,
                                    const float* __restrict__ q, const bf16_t* __restrict__ kvc,
@@ -368,7 +387,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
   }
 #pragma unroll
   for (int t = 0; t < MAXT; ++t)
-    if (t < count) load_q_tile<HD>(sm.m.qsh[t], row0[t], units[t], h, q, D, threadIdx.x, 64 * kAttnSC);
+    if (t < count) load_q_tile<HD, KVP>(sm.m.qsh[t], row0[t], units[t], h, q, D, threadIdx.x, 64 * kAttnSC);
   // Positions past every unit's limit may hold stale or never-written values:
   // their V elements are zeroed so that p = 0 contributes exact zeros. (Below
   // that limit every position holds a written key, so a unit with a smaller
@@ -397,7 +416,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
   const bool work = !unit_chunk && p0 < vlim;
 
   // The chunk's K and V operands, every load issued before the first use.
-  const bf16_t* tb = kvc + kv_head_base(D, it0.seq, layer, h) + (size_t)c * 128 * HD;
+  const bf16_t* tb = kvc + kv_head_base(D, it0.seq, layer, h) + (size_t)c * 64 * KVP * HD;
   u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
   if (work) {
 #pragma unroll
@@ -406,18 +425,18 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
       for (int s = 0; s < NS; ++s) {
         const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
         kh[t][s] = *(const u32x4_t*)kp;
-        kl[t][s] = *(const u32x4_t*)(kp + 32 * HD);
+        if constexpr (KVP == 2) kl[t][s] = *(const u32x4_t*)(kp + 32 * HD);
       }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const bf16_t* vp = tb + 64 * HD + (16 * b + n) * 32 + 8 * g;
+      const bf16_t* vp = tb + 32 * KVP * HD + (16 * b + n) * 32 + 8 * g;
       vh[b] = *(const u32x4_t*)vp;
-      vl[b] = *(const u32x4_t*)(vp + 32 * HD);
+      if constexpr (KVP == 2) vl[b] = *(const u32x4_t*)(vp + 32 * HD);
     }
     __builtin_amdgcn_sched_barrier(0);
     if (p0 + kKvTile > vlim)   // only a chunk that reaches past every limit needs the V mask
 #pragma unroll
-      for (int b = 0; b < NB; ++b) mask_v(vh[b], vl[b], vlim - (p0 + 8 * g));
+      for (int b = 0; b < NB; ++b) mask_v<KVP>(vh[b], vl[b], vlim - (p0 + 8 * g));
   }
 
 #pragma unroll
@@ -442,7 +461,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
       for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim[t] ? 1u : 0u) << i;
       f32x4_t acc[NB];
       float m, l;
-      chunk_partial<HD, false>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
+      chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
       if (n < units[t] && p0 < lim[t]) {
         if (to_mix) {
           const int row = row0[t] + n / rep, qhd = h * rep + n % rep;
@@ -542,7 +561,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 // explore keys in one item). Logical blocks from ntail: index = (k * nkv + h)
 // * nsc + sc, shared role for item list[k], the k-th of the items that form a
 // group of their own.
-template <int HD>
+template <int HD, int KVP>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
     const float* __restrict__ q, const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
@@ -565,7 +584,7 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const int e = tlist[b / D.nkv];
     const AttnItem it = items[e >> 2];
     if (it.xc0 < 0 || (lattice && lam >= stage_len(D, it.stage))) return;
-    attn_unit_chunk<HD>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * (e & 3) + (threadIdx.x >> 6), rows, q, kvc, exb, mix,
+    attn_unit_chunk<HD, KVP>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * (e & 3) + (threadIdx.x >> 6), rows, q, kvc, exb, mix,
                         D, lam, lattice);
     return;
   }
@@ -575,7 +594,7 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
   const int ii = list[b / D.nkv];
   const AttnItem it = items[ii];
   if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD, 1, false>(sm, items, ii, 1, b % D.nkv, sc, sc + 1, 0, rows, q, kvc, mix, part, D, lam,
+  attn_shared_chunks<HD, 1, false, KVP>(sm, items, ii, 1, b % D.nkv, sc, sc + 1, 0, rows, q, kvc, mix, part, D, lam,
                                    lattice, nsc_max);
 }
 
@@ -589,7 +608,7 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
 // (group, kv head), so the blocks in flight stream a few contiguous K/V
 // regions. (The single-item launch keeps the hardware order: there the remap
 // made the per-row blocks pile up on the first XCDs.)
-template <int HD, bool SPAN>
+template <int HD, bool SPAN, int KVP>
 __global__ __launch_bounds__(64 * kAttnSC) __attribute__((amdgpu_waves_per_eu(2))) void attn_group_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
     const float* __restrict__ q, const bf16_t* __restrict__ kvc, float* __restrict__ mix, float* __restrict__ part,
@@ -602,7 +621,7 @@ __global__ __launch_bounds__(64 * kAttnSC) __attribute__((amdgpu_waves_per_eu(2)
   const int nsc = (it.max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
   const int sc0 = SPAN ? bi * kAttnSpan : bi, sc1 = SPAN ? min(sc0 + kAttnSpan, nsc) : sc0 + 1;
   if (it.lead < 2 || sc0 >= nsc || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD, kAttnGroup, SPAN>(sm, items, ii, it.lead, h, sc0, sc1, bi, rows, q, kvc, mix, part, D, lam,
+  attn_shared_chunks<HD, kAttnGroup, SPAN, KVP>(sm, items, ii, it.lead, h, sc0, sc1, bi, rows, q, kvc, mix, part, D, lam,
                                            lattice, nsc_max);
 }
 
@@ -733,26 +752,17 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
 // read explore-buffer keys (lattice rows), 0 when no row does; nj: the most
 // chunks holding explore keys in one item (xc1 - xc0 + 1, at most 2). span:
 // grouped blocks run whole spans whatever their count.
-hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups, int ntails,
-                            const RowInfo* rows, int nrows, const float* q, const bf16_t* kvc, const bf16_t* exb,
-                            float* mix, float* part, float* out, const ModelDims& D, int lam, int lattice, int nsc_max,
-                            int max_keys, int umax, int nj, bool span, hipStream_t st) {
-  (void)nrows;
-  if (nitems == 0) return hipSuccess;
-  const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
-  if (nsc > nsc_max || umax > kAttnUnits || nsingle < 0 || ngroups < 0 || nsingle + ngroups > nitems || nj < 0 ||
-      nj > 2 || ntails < 0 || ntails > 4 * nitems || (ntails > 0 && nj == 0))
-    return hipErrorInvalidValue;
+template <int HD, int KVP>
+static hipError_t launch_attention_t(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups,
+                                     int ntails, const RowInfo* rows, const float* q, const bf16_t* kvc,
+                                     const bf16_t* exb, float* mix, float* part, float* out, const ModelDims& D,
+                                     int lam, int lattice, int nsc_max, int nsc, int nj, bool span, hipStream_t st) {
   const int ntail = ntails * D.nkv * nj;
   const dim3 grid(ntail + nsingle * D.nkv * nsc);
   hipError_t e = hipSuccess;
   if (grid.x > 0) {
-    if (D.hd == 128)
-      hipLaunchKernelGGL((attn_kernel<128>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
-                         part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nsc);
-    else
-      hipLaunchKernelGGL((attn_kernel<64>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
-                         part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nsc);
+    hipLaunchKernelGGL((attn_kernel<HD, KVP>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
+                       part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nsc);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -763,32 +773,43 @@ hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, 
   if (ngroups > 0 && nsc > 0) {
     const int nb = span_states ? nspan : nsc;
     const dim3 ggrid(ngroups * D.nkv * nb);
-    if (D.hd == 128) {
-      if (span_states)
-        hipLaunchKernelGGL((attn_group_kernel<128, true>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
-                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
-      else
-        hipLaunchKernelGGL((attn_group_kernel<128, false>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
-                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
-    } else {
-      if (span_states)
-        hipLaunchKernelGGL((attn_group_kernel<64, true>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
-                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
-      else
-        hipLaunchKernelGGL((attn_group_kernel<64, false>), ggrid, dim3(64 * kAttnSC), 0, st, items, list + nsingle,
-                           rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
-    }
+    if (span_states)
+      hipLaunchKernelGGL((attn_group_kernel<HD, true, KVP>), ggrid, dim3(64 * kAttnSC), 0, st, items,
+                         list + nsingle, rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
+    else
+      hipLaunchKernelGGL((attn_group_kernel<HD, false, KVP>), ggrid, dim3(64 * kAttnSC), 0, st, items,
+                         list + nsingle, rows, q, kvc, mix, part, D, lam, lattice, nsc_max, nb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 cgrid(nitems, D.nkv, kAttnUnits / 4);
-  if (D.hd == 128)
-    hipLaunchKernelGGL((attn_combine_kernel<128>), cgrid, dim3(256), 0, st, items, rows, mix, part, out, D, lam,
-                       lattice, nsc_max, span_states);
-  else
-    hipLaunchKernelGGL((attn_combine_kernel<64>), cgrid, dim3(256), 0, st, items, rows, mix, part, out, D, lam,
-                       lattice, nsc_max, span_states);
+  hipLaunchKernelGGL((attn_combine_kernel<HD>), cgrid, dim3(256), 0, st, items, rows, mix, part, out, D, lam,
+                     lattice, nsc_max, span_states);
   return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnItem* items, int nitems, const int* list, int nsingle, int ngroups, int ntails,
+                            const RowInfo* rows, int nrows, const float* q, const bf16_t* kvc, const bf16_t* exb,
+                            float* mix, float* part, float* out, const ModelDims& D, int lam, int lattice, int nsc_max,
+                            int max_keys, int umax, int nj, bool span, hipStream_t st) {
+  (void)nrows;
+  if (nitems == 0) return hipSuccess;
+  const int nsc = (max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
+  if (nsc > nsc_max || umax > kAttnUnits || nsingle < 0 || ngroups < 0 || nsingle + ngroups > nitems || nj < 0 ||
+      nj > 2 || ntails < 0 || ntails > 4 * nitems || (ntails > 0 && nj == 0) || (D.hd != 64 && D.hd != 128) ||
+      (D.kvp != 1 && D.kvp != 2))
+    return hipErrorInvalidValue;
+  auto go = [&](auto hd, auto kvp) {
+    return launch_attention_t<decltype(hd)::value, decltype(kvp)::value>(
+        items, nitems, list, nsingle, ngroups, ntails, rows, q, kvc, exb, mix, part, out, D, lam, lattice, nsc_max,
+        nsc, nj, span, st);
+  };
+  using I64 = std::integral_constant<int, 64>;
+  using I128 = std::integral_constant<int, 128>;
+  using K1 = std::integral_constant<int, 1>;
+  using K2 = std::integral_constant<int, 2>;
+  if (D.hd == 128) return D.kvp == 1 ? go(I128{}, K1{}) : go(I128{}, K2{});
+  return D.kvp == 1 ? go(I64{}, K1{}) : go(I64{}, K2{});
 }
 
 }  // namespace dex

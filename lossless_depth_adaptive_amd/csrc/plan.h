@@ -63,6 +63,9 @@ enum ScratchRegion { SC_ROWS, SC_PLANS, SC_ITEMS, SC_Q, SC_ATTN_OUT, SC_ACT, SC_
                      SC_HEAD_PART, SC_N };
 
 inline size_t esize(int dtype) { return dtype == DEX_DTYPE_BF16 ? 2 : 4; }
+// 16-bit planes per cached K or V value: fp16 for bfloat16 models, a bfloat16
+// (hi, lo) pair for fp32 models.
+inline int kv_planes(int dtype) { return dtype == DEX_DTYPE_BF16 ? 1 : 2; }
 
 inline int validate(const dex_model_config* c, const int32_t* X, int32_t n_x, const dex_options* o, std::string& err) {
   if (!c || !X || !o) { err = "null argument"; return DEX_EINVAL; }
@@ -140,8 +143,9 @@ inline WsPlan plan_workspace(const dex_model_config* c, const int32_t* X, int n_
   w.ad_vec = lay.take(m ? (size_t)(N - 1) * (m + 2 * d) * 4 : 0);   // per adapter: b1 [m], b2 [d], norm [d]
   w.cosT = lay.take(Cmax * (hd / 2) * 4);
   w.sinT = lay.take(Cmax * (hd / 2) * 4);
-  w.kvc = lay.take(B * L * nkv * Cs * hd * 8);            // K and V as bf16 (hi, lo) pairs
-  w.exb = lay.take(B * P * S * nkv * hd * 8);
+  const size_t kvb = 2 * 2 * (size_t)kv_planes(c->dtype);   // bytes of a position's K and V per dim
+  w.kvc = lay.take(B * L * nkv * Cs * hd * kvb);
+  w.exb = lay.take(B * P * S * nkv * hd * kvb);
   w.hidden = lay.take((B * P + kPrefillRows) * d * 4);
   w.xn = lay.take((B * P + kPrefillRows) * d * 4);
   w.xh = lay.take((B * P + kPrefillRows) * d * 4);

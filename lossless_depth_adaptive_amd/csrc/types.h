@@ -68,6 +68,7 @@ struct ModelDims {
   int B;            // max sequences
   int Cmax;         // max context
   int Cs;           // committed-cache positions per (sequence, layer, kv head): Cmax rounded up to kKvTile
+  int kvp;          // 16-bit planes per K or V value: 1 (fp16, bf16 models) or 2 (bf16 hi, lo: fp32 models)
   float eps;
   int lfirst[kMaxN + 1];   // explorer j runs layers [lfirst[j], lfirst[j+1]) (d_{j-1} .. d_j - 1); lfirst[N] = L
 };

@@ -210,7 +210,9 @@ static void check_workspace() {
     const size_t P = (1u << k.N) - 1, Cs = (k.Cmax + kKvTile - 1) / kKvTile * kKvTile;
     // sizes the kernels rely on, from the shapes (not from the plan)
     CHECK(w.head - w.embed >= V * d * es);
-    CHECK(w.exb - w.kvc >= (size_t)k.B * L * nkv * Cs * hd * 8);     // K and V as (hi, lo) bf16 pairs
+    // K and V: fp16 for bf16 models, (hi, lo) bf16 pairs for fp32 models
+    const size_t kvb = c.dtype == DEX_DTYPE_BF16 ? 4 : 8;
+    CHECK(w.exb - w.kvc >= (size_t)k.B * L * nkv * Cs * hd * kvb);
     CHECK(w.xn - w.hidden >= ((size_t)k.B * P + kPrefillRows) * d * 4);
     // the widest round: heap level N - 1 of every sequence, or a prefill chunk
     const int widest = std::max(k.B << (k.N - 1), kPrefillRows);
