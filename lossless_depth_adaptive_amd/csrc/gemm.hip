@@ -604,13 +604,13 @@ __device__ __forceinline__ void qkv_epilogue_wide(const GemmArgs& args, const Ge
     float o1[8], o2[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) rope_pair(x[c], x[c + 8], cosr[8 * u + c], sinr[8 * u + c], o1[c], o2[c]);
-    if (head < D.nq) {
+    if (head < D.nq) {   // 16-byte stores: dims 8u .. 8u + 7 and half + 8u .. half + 8u + 7
       float* qd = args.qout + ((size_t)row * D.nq + head) * hd + 8 * u;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        qd[c] = o1[c] * args.qscale;
-        qd[c + half] = o2[c] * args.qscale;
-      }
+      const float qs = args.qscale;
+      *(f32x4_t*)qd = f32x4_t{o1[0] * qs, o1[1] * qs, o1[2] * qs, o1[3] * qs};
+      *(f32x4_t*)(qd + 4) = f32x4_t{o1[4] * qs, o1[5] * qs, o1[6] * qs, o1[7] * qs};
+      *(f32x4_t*)(qd + half) = f32x4_t{o2[0] * qs, o2[1] * qs, o2[2] * qs, o2[3] * qs};
+      *(f32x4_t*)(qd + half + 4) = f32x4_t{o2[4] * qs, o2[5] * qs, o2[6] * qs, o2[7] * qs};
     } else {
       const int hh = head - D.nq;
       if (commit) {

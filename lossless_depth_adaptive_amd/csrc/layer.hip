@@ -189,6 +189,13 @@ __device__ __forceinline__ void mask_v(u32x4_t& vh, u32x4_t& vl, int nv) {
 constexpr int kAttnSpan = 16;
 constexpr int kSpanBlocks = 512;   // grouped blocks that fill the chip (two per CU)
 constexpr int kSpreadBlocks = 4096;   // attn_kernel launches that spread their per-row blocks
+// Super-chunks a single-item block of attn_kernel runs in turn (each one's
+// state written as a block of its own would), so that its item, rows and
+// query tile are read once for all of them.
+#ifndef DEX_ATTN_SCPB
+#define DEX_ATTN_SCPB 2
+#endif
+constexpr int kSingleSC = DEX_ATTN_SCPB;
 
 // Whether super-chunk sc of the item holds a per-row (explore) chunk.
 __device__ __forceinline__ bool sc_mixed(const AttnItem& it, int sc) {
@@ -265,7 +272,46 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
   const size_t eslot = (size_t)D.S * D.nkv * 2 * KVP * HD;  // 16-bit values between node slots
   const bf16_t* eb = exb + ex_base(D, it.seq, 0, lam, h);
   bf16_t (*ev)[2 * HD] = sm.ev[w];
-  if (active) {   // the V planes (KVP HD values) of each explore entry, 16 bytes a thread
+  const int layer = layer_of(D, lattice, it.stage, lam);
+  const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 64 * KVP * HD;
+  const float* qr = q + ((size_t)row * D.nq + h * rep + min(n, rep - 1)) * HD;
+  // Every operand load of the chunk is issued at once, ahead of the explore
+  // values' gather into LDS, so the chunk waits for memory once: K (committed
+  // tile below ncu, the ancestors' explore entries from there, zero past the
+  // limit), V of the committed positions, and the query.
+  constexpr int NS = HD / 32;
+  u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
+  f32x4_t qa[NS][2];
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const int p = p0 + 8 * (n >> 2) + 4 * t + (n & 3);
+        kh[t][s] = kl[t][s] = u32x4_t{0u, 0u, 0u, 0u};
+        if (p < limu) {
+          const bf16_t* kp =
+              p < ncu ? tb + (4 * s + g) * 256 + (16 * t + n) * 8 : eb + Ru.anc[p - ncu] * eslot + 8 * (4 * s + g);
+          kh[t][s] = *(const u32x4_t*)kp;
+          if constexpr (KVP == 2) kl[t][s] = *(const u32x4_t*)(kp + (p < ncu ? 32 * HD : HD));
+        }
+      }
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const int pb = p0 + 8 * g, dd = 16 * b + n;
+      vh[b] = vl[b] = u32x4_t{0u, 0u, 0u, 0u};
+      if (pb < ncu) {
+        const bf16_t* vp = tb + 32 * KVP * HD + dd * 32 + 8 * g;
+        vh[b] = *(const u32x4_t*)vp;
+        if constexpr (KVP == 2) vl[b] = *(const u32x4_t*)(vp + 32 * HD);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qa[s][0] = *(const f32x4_t*)(qr + 32 * s + 8 * g);
+      qa[s][1] = *(const f32x4_t*)(qr + 32 * s + 8 * g + 4);
+    }
+    // the V planes (KVP HD values) of each explore entry, 16 bytes a thread
     constexpr int PIECES = KVP * HD / 8;
     for (int t = lane; t < (limu - ncu) * PIECES; t += 64) {
       const int j = t / PIECES, o = 8 * (t % PIECES);
@@ -274,40 +320,18 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
   }
   __syncthreads();
   if (!active) return;
-  const int layer = layer_of(D, lattice, it.stage, lam);
-  const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 64 * KVP * HD;
-  const float* qr = q + ((size_t)row * D.nq + h * rep + min(n, rep - 1)) * HD;
   auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
-    const f32x4_t a = *(const f32x4_t*)(qr + 32 * s + 8 * g), b = *(const f32x4_t*)(qr + 32 * s + 8 * g + 4);
-    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const float x[8] = {qa[s][0][0], qa[s][0][1], qa[s][0][2], qa[s][0][3],
+                        qa[s][1][0], qa[s][1][1], qa[s][1][2], qa[s][1][3]};
     split8<KVP>(x, qh, ql);
   };
-  auto ksrc = [&](int t, int s, u32x4_t& kh, u32x4_t& kl) {
-    const int p = p0 + 8 * (n >> 2) + 4 * t + (n & 3);
-    const bf16_t* kp;
-    size_t lo_off;
-    if (p < ncu) {
-      kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
-      lo_off = 32 * HD;
-    } else if (p < limu) {
-      kp = eb + Ru.anc[p - ncu] * eslot + 8 * (4 * s + g);
-      lo_off = HD;
-    } else {
-      kh = kl = u32x4_t{0u, 0u, 0u, 0u};
-      return;
-    }
-    kh = *(const u32x4_t*)kp;
-    if constexpr (KVP == 2) kl = *(const u32x4_t*)(kp + lo_off);
+  auto ksrc = [&](int t, int s, u32x4_t& a, u32x4_t& b) {
+    a = kh[t][s];
+    b = kl[t][s];
   };
-  auto vsrc = [&](int b, u32x4_t& vh, u32x4_t& vl) {
-    const int pb = p0 + 8 * g, dd = 16 * b + n;
-    if (pb < ncu) {
-      const bf16_t* vp = tb + 32 * KVP * HD + dd * 32 + 8 * g;
-      vh = *(const u32x4_t*)vp;
-      if constexpr (KVP == 2) vl = *(const u32x4_t*)(vp + 32 * HD);
-    } else {
-      vh = vl = u32x4_t{0u, 0u, 0u, 0u};
-    }
+  auto vsrc = [&](int b, u32x4_t& a, u32x4_t& bb) {
+    a = vh[b];
+    bb = vl[b];
   };
   auto vpost = [&](int b, u32x4_t& vh, u32x4_t& vl) {
     const int pb = p0 + 8 * g, dd = 16 * b + n;
@@ -344,7 +368,7 @@ __device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, 
 // them. Per tile, in a super-chunk without per-row chunks the block folds the
 // chunks per unit into the super-chunk state (acc[hd], m, l); in one with them,
 // the tile's chunks go to the mix slots for the combine kernel to fold. SPAN
-// false: one super-chunk, its state written to part[row][qh][sc]. SPAN true:
+// false: each super-chunk's state written to part[row][qh][sc]. SPAN true:
 // the super-chunks of span `span` (kAttnSpan of them from sc0 = kAttnSpan
 // span); the fold threads fold the states into the span state in registers
 // (the first as it is, each later one that holds keys of the unit by the fold)
@@ -529,7 +553,7 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
         }
       }
     }
-    if (SPAN || t + 1 < count) __syncthreads();   // the fold has read red before it is written again
+    if (SPAN || t + 1 < count || sc + 1 < sc1) __syncthreads();   // the fold has read red before it is written again
   }
   }
 
@@ -559,14 +583,15 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 // chunks, index = (e * nkv + h) * nj + j for tail entry tlist[e] = 4 item +
 // quad -> chunk xc0 + j, row kAttnSC * quad + wave (nj: the most chunks with
 // explore keys in one item). Logical blocks from ntail: index = (k * nkv + h)
-// * nsc + sc, shared role for item list[k], the k-th of the items that form a
-// group of their own.
+// * nscb + i, shared role over super-chunks kSingleSC i .. kSingleSC (i + 1) - 1
+// of item list[k], the k-th of the items that form a group of their own
+// (nscb: the widest item's super-chunks in blocks of kSingleSC).
 template <int HD, int KVP>
 __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const AttnItem* __restrict__ items, const int* __restrict__ list, const RowInfo* __restrict__ rows,
     const float* __restrict__ q, const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
     float* __restrict__ mix, float* __restrict__ part, ModelDims D, int lam, int lattice, int nsc_max, int ntail,
-    const int* __restrict__ tlist, int nj, int nsc) {
+    const int* __restrict__ tlist, int nj, int nscb) {
   __shared__ AttnSmem<HD, 1> sm;
   // Hardware block x -> logical index b. In a launch of kSpreadBlocks blocks
   // or more the per-row blocks are spread evenly among the shared ones (x
@@ -589,13 +614,14 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     return;
   }
   b -= ntail;
-  const int sc = b % nsc;
-  b /= nsc;
+  const int sc0 = (b % nscb) * kSingleSC;
+  b /= nscb;
   const int ii = list[b / D.nkv];
   const AttnItem it = items[ii];
-  if (it.lead != 1 || sc * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
-  attn_shared_chunks<HD, 1, false, KVP>(sm, items, ii, 1, b % D.nkv, sc, sc + 1, 0, rows, q, kvc, mix, part, D, lam,
-                                   lattice, nsc_max);
+  if (it.lead != 1 || sc0 * kAttnSCKeys >= it.max_keys || (lattice && lam >= stage_len(D, it.stage))) return;
+  const int sc1 = min(sc0 + kSingleSC, (it.max_keys + kAttnSCKeys - 1) / kAttnSCKeys);
+  attn_shared_chunks<HD, 1, false, KVP>(sm, items, ii, 1, b % D.nkv, sc0, sc1, 0, rows, q, kvc, mix, part, D, lam,
+                                        lattice, nsc_max);
 }
 
 // Groups of several items: the shared role over up to kAttnGroup tiles. SPAN:
@@ -758,11 +784,12 @@ static hipError_t launch_attention_t(const AttnItem* items, int nitems, const in
                                      const bf16_t* exb, float* mix, float* part, float* out, const ModelDims& D,
                                      int lam, int lattice, int nsc_max, int nsc, int nj, bool span, hipStream_t st) {
   const int ntail = ntails * D.nkv * nj;
-  const dim3 grid(ntail + nsingle * D.nkv * nsc);
+  const int nscb = (nsc + kSingleSC - 1) / kSingleSC;
+  const dim3 grid(ntail + nsingle * D.nkv * nscb);
   hipError_t e = hipSuccess;
   if (grid.x > 0) {
     hipLaunchKernelGGL((attn_kernel<HD, KVP>), grid, dim3(64 * kAttnSC), 0, st, items, list, rows, q, kvc, exb, mix,
-                       part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nsc);
+                       part, D, lam, lattice, nsc_max, ntail, list + nsingle + ngroups, nj, nscb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

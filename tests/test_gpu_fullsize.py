@@ -71,9 +71,9 @@ def test_fullsize_7b(name):
     assert steps == N + sum(b + 1 for b in bs[:-1])
     print(f"[full] {name}: {T} tokens, {steps} rounds, branch histogram {np.bincount(bs, minlength=N).tolist()}",
           flush=True)
-    n, n_dec, ead = compare_golden(d, gold["seqs"]["0"], GATE, GATE2, TOL, N)
+    n, n_dec, ead, worst = compare_golden(d, gold["seqs"]["0"], GATE, GATE2, TOL, N)
     print(f"[full] {name}: {n}/{n_gold} commits equal to the oracle's, {n_dec} anchor candidates compared; "
-          f"layers vs ceil_X(EAD_stab): {ead}", flush=True)
+          f"layers vs ceil_X(EAD_stab): {ead}; worst logit err={worst:.3g}", flush=True)
 
 
 def compare_golden(gpu, gold, gate, gate2, tol, N):
@@ -81,8 +81,9 @@ def compare_golden(gpu, gold, gate, gate2, tol, N):
     The oracle followed its own stream, so the comparison runs until the first
     commit where the streams part, which is only allowed where the oracle's
     final-depth margin is below the tighter gate. Returns (commits compared,
-    decisions compared at gate2, layers-vs-EAD counts)."""
+    decisions compared at gate2, layers-vs-EAD counts, worst logit error)."""
     n = n_dec = 0
+    worst = 0.0
     ead = dict(agree=0, below=0)
     for g, o in zip(gpu, gold):
         if g["token"] != o["token"]:
@@ -103,8 +104,9 @@ def compare_golden(gpu, gold, gate, gate2, tol, N):
             for ids, vals in ((o["top_ids"], o["top_logits"]), (o["sample_ids"], o["sample_logits"])):
                 err = float(np.max(np.abs(z[ids] - np.asarray(vals))))
                 assert err <= tol, (err, tol)
+                worst = max(worst, err)
         n += 1
-    return n, n_dec, ead
+    return n, n_dec, ead, worst
 
 
 @pytest.mark.timeout(900)
@@ -137,6 +139,6 @@ def test_fullsize_batched(name):
     hist = np.bincount([r["branch"] for s in range(w.batch) for r in dex_recs[s]], minlength=N).tolist()
     print(f"[full] {name}: {w.batch} x {T} tokens equal to GPU AR; branch histogram {hist}", flush=True)
     for key, grecs in gold["seqs"].items():
-        n, n_dec, ead = compare_golden(dex_recs[int(key)], grecs, GATE, GATE2, TOL, N)
+        n, n_dec, ead, worst = compare_golden(dex_recs[int(key)], grecs, GATE, GATE2, TOL, N)
         print(f"[full] {name} seq {key}: {n}/{len(grecs)} commits equal to the oracle's, {n_dec} anchor "
-              f"candidates compared; layers vs ceil_X(EAD_stab): {ead}", flush=True)
+              f"candidates compared; layers vs ceil_X(EAD_stab): {ead}; worst logit err={worst:.3g}", flush=True)
