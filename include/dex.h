@@ -25,7 +25,9 @@
  *    own packed layout inside the workspace, after which the caller may free
  *    them.
  *  - The workspace (size from dex_workspace_bytes) is a caller-owned device
- *    buffer that the context uses until dex_destroy.
+ *    buffer that the context uses until dex_destroy. It holds the K/V cache:
+ *    fp16 values for DEX_DTYPE_BF16 models (2 bytes each), bfloat16
+ *    (hi, lo) pairs for DEX_DTYPE_F32 models (4 bytes each).
  *  - A context is bound to one HIP stream (passed as void*, a hipStream_t) and
  *    is not thread-safe. Calls that compute enqueue on that stream; dex_step,
  *    dex_ar_step and dex_prefill synchronise it before returning.
