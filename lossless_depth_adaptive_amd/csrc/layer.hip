@@ -250,116 +250,147 @@ __device__ __forceinline__ void load_q_tile(bf16_t (*dst)[kAttnUnits][HD + 8], i
   }
 }
 
-// Per-row role: wave w computes chunk c (one of xc0, xc1) for row rr of the
-// item with that row's own keys, for all rep = nq / nkv query heads of kv head
-// h at once (MFMA column n carries query head h rep + n; the others repeat a
-// query and are not stored), into mix[row][qh][c - kAttnSC (xc0 / kAttnSC)].
-// A column's result depends only on its own query, so each unit gets the bits
-// it gets in a shared tile.
+// Per-row role: the block takes rows rbase .. rbase + kTailRows - 1 of the
+// item, wave w rows rbase + w + kAttnSC r (r < kTailRowsPerWave). For each it
+// computes chunk c (one of xc0, xc1) with that row's own keys, for all
+// rep = nq / nkv query heads of kv head h at once (MFMA column n carries query
+// head h rep + n; the others repeat a query and are not stored), into
+// mix[row][qh][c - kAttnSC (xc0 / kAttnSC)]. A column's result depends only on
+// its own query, so each unit gets the bits it gets in a shared tile. The rows
+// of an item that reads explore keys are lattice rows of one sequence, which
+// share ncommit = C: the chunk's committed keys and values are the same for all
+// of them, so a wave loads those once and, per row, the row's explore keys, its
+// query and its explore values (gathered into the wave's own LDS slice), all
+// issued together so that a row waits for memory once.
 template <int HD, int KVP>
-__device__ void attn_unit_chunk(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, int c, int rr,
-                                const RowInfo* __restrict__ rows, const float* __restrict__ q,
-                                const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
-                                float* __restrict__ mix, const ModelDims& D, int lam, int lattice) {
-  constexpr int NB = HD / 16, HP = HD + 4;
+__device__ void attn_unit_rows(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, int c, int rbase,
+                               const RowInfo* __restrict__ rows, const float* __restrict__ q,
+                               const bf16_t* __restrict__ kvc, const bf16_t* __restrict__ exb,
+                               float* __restrict__ mix, const ModelDims& D, int lam, int lattice) {
+  constexpr int NB = HD / 16, NS = HD / 32, HP = HD + 4;
   const int rep = D.nq / D.nkv;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
   const int p0 = c * kKvTile;
-  const int row = it.row0 + min(rr, it.nrows - 1);
-  const RowInfo& Ru = rows[row];
-  const int ncu = Ru.ncommit, limu = Ru.ncommit + Ru.n_anc;
-  const bool active = rr < it.nrows && c <= it.xc1 && p0 < limu;
+  const int r0 = rbase + w;
+  if (r0 >= it.nrows || c > it.xc1) return;
+  const int ncu = rows[it.row0 + r0].ncommit;
   const size_t eslot = (size_t)D.S * D.nkv * 2 * KVP * HD;  // 16-bit values between node slots
   const bf16_t* eb = exb + ex_base(D, it.seq, 0, lam, h);
   bf16_t (*ev)[2 * HD] = sm.ev[w];
   const int layer = layer_of(D, lattice, it.stage, lam);
   const bf16_t* tb = kvc + kv_head_base(D, it.seq, layer, h) + (size_t)c * 64 * KVP * HD;
-  const float* qr = q + ((size_t)row * D.nq + h * rep + min(n, rep - 1)) * HD;
-  // Every operand load of the chunk is issued at once, ahead of the explore
-  // values' gather into LDS, so the chunk waits for memory once: K (committed
-  // tile below ncu, the ancestors' explore entries from there, zero past the
-  // limit), V of the committed positions, and the query.
-  constexpr int NS = HD / 32;
+  // The committed operands of the chunk (zero at and past ncu).
   u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
-  f32x4_t qa[NS][2];
-  if (active) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const int p = p0 + 8 * (n >> 2) + 4 * t + (n & 3);
+      kh[t][s] = kl[t][s] = u32x4_t{0u, 0u, 0u, 0u};
+      if (p < ncu) {
+        const bf16_t* kp = tb + (4 * s + g) * 256 + (16 * t + n) * 8;
+        kh[t][s] = *(const u32x4_t*)kp;
+        if constexpr (KVP == 2) kl[t][s] = *(const u32x4_t*)(kp + 32 * HD);
+      }
+    }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int pb = p0 + 8 * g, dd = 16 * b + n;
+    vh[b] = vl[b] = u32x4_t{0u, 0u, 0u, 0u};
+    if (pb < ncu) {
+      const bf16_t* vp = tb + 32 * KVP * HD + dd * 32 + 8 * g;
+      vh[b] = *(const u32x4_t*)vp;
+      if constexpr (KVP == 2) vl[b] = *(const u32x4_t*)(vp + 32 * HD);
+    }
+  }
+  for (int r = 0; r < kTailRowsPerWave; ++r) {
+    const int rr = r0 + kAttnSC * r;
+    if (rr >= it.nrows) break;
+    const int row = it.row0 + rr;
+    const RowInfo& Ru = rows[row];
+    const int limu = ncu + Ru.n_anc;
+    if (p0 >= limu) continue;   // no key of this row in chunk c
+    // K of this row: the lanes of positions from ncu on take its explore
+    // entries, zero past its limit (the committed lanes keep their operand)
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const int p = p0 + 8 * (n >> 2) + 4 * t + (n & 3);
-        kh[t][s] = kl[t][s] = u32x4_t{0u, 0u, 0u, 0u};
-        if (p < limu) {
-          const bf16_t* kp =
-              p < ncu ? tb + (4 * s + g) * 256 + (16 * t + n) * 8 : eb + Ru.anc[p - ncu] * eslot + 8 * (4 * s + g);
-          kh[t][s] = *(const u32x4_t*)kp;
-          if constexpr (KVP == 2) kl[t][s] = *(const u32x4_t*)(kp + (p < ncu ? 32 * HD : HD));
+        if (p >= ncu) {
+          kh[t][s] = kl[t][s] = u32x4_t{0u, 0u, 0u, 0u};
+          if (p < limu) {
+            const bf16_t* kp = eb + Ru.anc[p - ncu] * eslot + 8 * (4 * s + g);
+            kh[t][s] = *(const u32x4_t*)kp;
+            if constexpr (KVP == 2) kl[t][s] = *(const u32x4_t*)(kp + HD);
+          }
         }
       }
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int pb = p0 + 8 * g, dd = 16 * b + n;
-      vh[b] = vl[b] = u32x4_t{0u, 0u, 0u, 0u};
-      if (pb < ncu) {
-        const bf16_t* vp = tb + 32 * KVP * HD + dd * 32 + 8 * g;
-        vh[b] = *(const u32x4_t*)vp;
-        if constexpr (KVP == 2) vl[b] = *(const u32x4_t*)(vp + 32 * HD);
-      }
-    }
+    const float* qr = q + ((size_t)row * D.nq + h * rep + min(n, rep - 1)) * HD;
+    f32x4_t qa[NS][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       qa[s][0] = *(const f32x4_t*)(qr + 32 * s + 8 * g);
       qa[s][1] = *(const f32x4_t*)(qr + 32 * s + 8 * g + 4);
     }
-    // the V planes (KVP HD values) of each explore entry, 16 bytes a thread
+    // the V planes (KVP HD values) of each explore entry, 16 bytes a lane; the
+    // slice belongs to this wave, whose LDS accesses take effect in order
     constexpr int PIECES = KVP * HD / 8;
     for (int t = lane; t < (limu - ncu) * PIECES; t += 64) {
       const int j = t / PIECES, o = 8 * (t % PIECES);
       *(u32x4_t*)&ev[j][o] = *(const u32x4_t*)(eb + Ru.anc[j] * eslot + KVP * HD + o);
     }
-  }
-  __syncthreads();
-  if (!active) return;
-  auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
-    const float x[8] = {qa[s][0][0], qa[s][0][1], qa[s][0][2], qa[s][0][3],
-                        qa[s][1][0], qa[s][1][1], qa[s][1][2], qa[s][1][3]};
-    split8<KVP>(x, qh, ql);
-  };
-  auto ksrc = [&](int t, int s, u32x4_t& a, u32x4_t& b) {
-    a = kh[t][s];
-    b = kl[t][s];
-  };
-  auto vsrc = [&](int b, u32x4_t& a, u32x4_t& bb) {
-    a = vh[b];
-    bb = vl[b];
-  };
-  auto vpost = [&](int b, u32x4_t& vh, u32x4_t& vl) {
-    const int pb = p0 + 8 * g, dd = 16 * b + n;
-    if (pb + 7 < ncu) return;
-    // Positions from ncu on: the explore entry's value, or 0 past the limit.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    auto qsrc = [&](int s, u32x4_t& qh, u32x4_t& ql) {
+      const float x[8] = {qa[s][0][0], qa[s][0][1], qa[s][0][2], qa[s][0][3],
+                          qa[s][1][0], qa[s][1][1], qa[s][1][2], qa[s][1][3]};
+      split8<KVP>(x, qh, ql);
+    };
+    // V of this row: positions from ncu on take its explore entry's value,
+    // or 0 past its limit (every such element is rewritten for each row)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int p = pb + i;
-      if (p < ncu) continue;
-      const unsigned hv = p < limu ? ev[p - ncu][dd] : 0u;
-      const int sh = 16 * (i & 1);
-      const unsigned keep = ~(0xFFFFu << sh);
-      vh[i >> 1] = (vh[i >> 1] & keep) | (hv << sh);
-      if constexpr (KVP == 2) {
-        const unsigned lv = p < limu ? ev[p - ncu][HD + dd] : 0u;
-        vl[i >> 1] = (vl[i >> 1] & keep) | (lv << sh);
+    for (int b = 0; b < NB; ++b) {
+      const int pb = p0 + 8 * g, dd = 16 * b + n;
+      if (pb + 7 < ncu) continue;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = pb + i;
+        if (p < ncu) continue;
+        const unsigned hv = p < limu ? ev[p - ncu][dd] : 0u;
+        const int sh = 16 * (i & 1);
+        const unsigned keep = ~(0xFFFFu << sh);
+        vh[b][i >> 1] = (vh[b][i >> 1] & keep) | (hv << sh);
+        if constexpr (KVP == 2) {
+          const unsigned lv = p < limu ? ev[p - ncu][HD + dd] : 0u;
+          vl[b][i >> 1] = (vl[b][i >> 1] & keep) | (lv << sh);
+        }
       }
     }
-  };
-  unsigned valid8 = 0;
+    auto ksrc = [&](int t, int s, u32x4_t& a, u32x4_t& b) {
+      a = kh[t][s];
+      b = kl[t][s];
+    };
+    auto vsrc = [&](int b, u32x4_t& a, u32x4_t& bb) {
+      a = vh[b];
+      bb = vl[b];
+    };
+    auto vpost = [&](int, u32x4_t&, u32x4_t&) {};
+    unsigned valid8 = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < limu ? 1u : 0u) << i;
-  f32x4_t acc[NB];
-  float m, l;
-  chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
-  if (n < rep)
-    store_partial<HD>(mix + (((size_t)row * D.nq + h * rep + n) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
-                      acc, m, l, g);
+    for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < limu ? 1u : 0u) << i;
+    f32x4_t acc[NB];
+    float m, l;
+    chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
+    if (n < rep)
+      store_partial<HD>(mix + (((size_t)row * D.nq + h * rep + n) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
+                        acc, m, l, g);
+    // the next row's gather writes the slice only after this row's reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
 }
 
 // Shared role over super-chunks sc0 .. sc1 - 1, in order: for each, wave w
@@ -581,8 +612,8 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
 
 // One launch, block = kAttnSC waves. Logical blocks [0, ntail): per-row
 // chunks, index = (e * nkv + h) * nj + j for tail entry tlist[e] = 4 item +
-// quad -> chunk xc0 + j, row kAttnSC * quad + wave (nj: the most chunks with
-// explore keys in one item). Logical blocks from ntail: index = (k * nkv + h)
+// q -> chunk xc0 + j, rows kTailRows q .. kTailRows (q + 1) - 1 (nj: the most
+// chunks with explore keys in one item). Logical blocks from ntail: index = (k * nkv + h)
 // * nscb + i, shared role over super-chunks kSingleSC i .. kSingleSC (i + 1) - 1
 // of item list[k], the k-th of the items that form a group of their own
 // (nscb: the widest item's super-chunks in blocks of kSingleSC).
@@ -609,8 +640,8 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
     const int e = tlist[b / D.nkv];
     const AttnItem it = items[e >> 2];
     if (it.xc0 < 0 || (lattice && lam >= stage_len(D, it.stage))) return;
-    attn_unit_chunk<HD, KVP>(sm, it, b % D.nkv, it.xc0 + j, kAttnSC * (e & 3) + (threadIdx.x >> 6), rows, q, kvc, exb, mix,
-                        D, lam, lattice);
+    attn_unit_rows<HD, KVP>(sm, it, b % D.nkv, it.xc0 + j, kTailRows * (e & 3), rows, q, kvc, exb, mix, D, lam,
+                            lattice);
     return;
   }
   b -= ntail;
@@ -772,8 +803,9 @@ __global__ void attn_combine_kernel(const AttnItem* __restrict__ items, const Ro
 // ----------------------------------------------------------------------------
 
 // list: the nsingle items that form a group of their own, then the ngroups
-// items that lead a group of several, then ntails entries 4 item + quad of
-// the 4-row quarters of items whose rows read explore keys (0 when none do).
+// items that lead a group of several, then ntails entries 4 item + q of the
+// runs of kTailRows rows of items whose rows read explore keys (0 when none
+// do).
 // umax: most units of an item whose rows
 // read explore-buffer keys (lattice rows), 0 when no row does; nj: the most
 // chunks holding explore keys in one item (xc1 - xc0 + 1, at most 2). span:

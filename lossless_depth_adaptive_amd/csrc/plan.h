@@ -312,10 +312,11 @@ inline ItemStats round_items(const RoundShape& r, const SeqPlan* plans, const in
 // Attention block lists of the first nitems items: the items that form a
 // group of their own (the shared-role blocks of attn_kernel), then the items
 // that lead a group of several (attn_group_kernel), then, for items whose rows
-// read explore keys, one entry 4 item + q per quarter q of the item's rows
-// (the per-row chunk blocks of attn_kernel, kAttnSC rows each), so that no
-// launch has blocks without work. list receives at most nitems plus the sum
-// over items with explore keys of ceil(nrows / kAttnSC) entries.
+// read explore keys, one entry 4 item + q per run q of kTailRows of the item's
+// rows (the per-row chunk blocks of attn_kernel; an item has at most
+// kAttnUnits rows, so q < 4), so that no launch has blocks without work. list
+// receives at most nitems plus the sum over items with explore keys of
+// ceil(nrows / kTailRows) entries.
 struct BlockList {
   int single = 0, groups = 0, tails = 0;
 };
@@ -328,7 +329,7 @@ inline BlockList attn_block_list(const AttnItem* items, int nitems, int* list) {
     if (items[i].lead > 1) list[b.single + b.groups++] = i;
   for (int i = 0; i < nitems; ++i)
     if (items[i].xc0 >= 0)
-      for (int qt = 0; qt * kAttnSC < items[i].nrows; ++qt) list[b.single + b.groups + b.tails++] = 4 * i + qt;
+      for (int qt = 0; qt * kTailRows < items[i].nrows; ++qt) list[b.single + b.groups + b.tails++] = 4 * i + qt;
   return b;
 }
 

@@ -31,6 +31,14 @@ constexpr int kAttnSC = DEX_ATTN_SC;  // chunks per attention super-chunk (= wav
 constexpr int kAttnGroup = 4;        // unit tiles (items) of one sequence and stage per grouped attention block
 constexpr int kAttnSCKeys = kKvTile * kAttnSC;
 constexpr int kMixSlots = 2 * kAttnSC;   // chunk slots of the (at most two) mixed super-chunks
+// Rows of an item whose explore keys one per-row attention block computes:
+// kTailRowsPerWave rows in each of its kAttnSC waves.
+#ifndef DEX_TAIL_RPW
+#define DEX_TAIL_RPW 2
+#endif
+constexpr int kTailRowsPerWave = DEX_TAIL_RPW;
+constexpr int kTailRows = kAttnSC * kTailRowsPerWave;
+static_assert(kAttnUnits <= 4 * kTailRows, "a tail entry 4 item + q needs q < 4");
 
 // One lattice (or autoregressive, or prefill) row of a step.
 struct RowInfo {

@@ -341,7 +341,7 @@ static void check_round(std::mt19937& rng, int N, int B, int rep, int ncap, bool
       CHECK(it.xc0 * kKvTile <= C[it.seq] && (it.xc1 + 1) * kKvTile >= mk);
       CHECK(it.xc1 - it.xc0 <= 1);
       nj = std::max(nj, it.xc1 - it.xc0 + 1);
-      tails += (it.nrows + kAttnSC - 1) / kAttnSC;
+      tails += (it.nrows + kTailRows - 1) / kTailRows;
     } else {
       CHECK(it.xc0 == -1);
     }
@@ -373,7 +373,7 @@ static void check_round(std::mt19937& rng, int N, int B, int rep, int ncap, bool
   std::set<int> tail_entries;
   for (int e = b.single + b.groups; e < b.single + b.groups + b.tails; ++e) {
     const int i = list[e] / 4, qt = list[e] % 4;
-    CHECK(i < st.nitems && qt * kAttnSC < items[i].nrows);
+    CHECK(i < st.nitems && qt * kTailRows < items[i].nrows);
     CHECK(tail_entries.insert(list[e]).second);
   }
 }
