@@ -196,6 +196,11 @@ constexpr int kSpreadBlocks = 4096;   // attn_kernel launches that spread their 
 #define DEX_ATTN_SCPB 2
 #endif
 constexpr int kSingleSC = DEX_ATTN_SCPB;
+// The same for a grouped block that runs super-chunks (not whole spans).
+#ifndef DEX_GROUP_SCPB
+#define DEX_GROUP_SCPB 2
+#endif
+constexpr int kGroupSC = DEX_GROUP_SCPB;
 
 // Whether super-chunk sc of the item holds a per-row (explore) chunk.
 __device__ __forceinline__ bool sc_mixed(const AttnItem& it, int sc) {
@@ -657,9 +662,10 @@ __global__ __launch_bounds__(64 * kAttnSC) void attn_kernel(
 
 // Groups of several items: the shared role over up to kAttnGroup tiles. SPAN:
 // block (group, h, span) runs the super-chunks of one span and writes span
-// states; otherwise block (group, h, sc) runs one super-chunk and writes its
-// state, and the combine kernel folds those into span states in the same
-// order (the launch picks SPAN when it has blocks enough to fill the chip).
+// states; otherwise block (group, h, b) runs super-chunks kGroupSC b ..
+// kGroupSC (b + 1) - 1 and writes each one's state, and the combine kernel
+// folds those into span states in the same order (the launch picks SPAN when
+// it has blocks enough to fill the chip).
 // 1-D grid, logical index (xcd_block) = (k * nkv + h) * nb + b for the group
 // led by item list[k]: each XCD walks consecutive super-chunks or spans of one
 // (group, kv head), so the blocks in flight stream a few contiguous K/V
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(64 * kAttnSC) __attribute__((amdgpu_waves_per_eu(2)
   const int ii = list[ih / D.nkv], h = ih % D.nkv;
   const AttnItem it = items[ii];
   const int nsc = (it.max_keys + kAttnSCKeys - 1) / kAttnSCKeys;
-  const int sc0 = SPAN ? bi * kAttnSpan : bi, sc1 = SPAN ? min(sc0 + kAttnSpan, nsc) : sc0 + 1;
+  const int sc0 = SPAN ? bi * kAttnSpan : bi * kGroupSC, sc1 = min(sc0 + (SPAN ? kAttnSpan : kGroupSC), nsc);
   if (it.lead < 2 || sc0 >= nsc || (lattice && lam >= stage_len(D, it.stage))) return;
   attn_shared_chunks<HD, kAttnGroup, SPAN, KVP>(sm, items, ii, it.lead, h, sc0, sc1, bi, rows, q, kvc, mix, part, D, lam,
                                            lattice, nsc_max);
@@ -830,7 +836,7 @@ static hipError_t launch_attention_t(const AttnItem* items, int nitems, const in
   const int nspan = (nsc + kAttnSpan - 1) / kAttnSpan;
   const int span_states = ngroups > 0 && (span || ngroups * D.nkv * nspan >= kSpanBlocks);
   if (ngroups > 0 && nsc > 0) {
-    const int nb = span_states ? nspan : nsc;
+    const int nb = span_states ? nspan : (nsc + kGroupSC - 1) / kGroupSC;
     const dim3 ggrid(ngroups * D.nkv * nb);
     if (span_states)
       hipLaunchKernelGGL((attn_group_kernel<HD, true, KVP>), ggrid, dim3(64 * kAttnSC), 0, st, items,
