@@ -116,6 +116,33 @@ struct AttnItem {
                     // attention block of this item covers; 0: covered by an earlier item
 };
 
+// K/V storage. Values are stored in kvp 16-bit planes, all rounded to nearest
+// even: kvp = 1 for bfloat16 models, one fp16 value (11 significant bits,
+// three more than the model's bfloat16; 2 bytes, the K/V stream of a bf16
+// cache); kvp = 2 for fp32 models, a bfloat16 pair hi = bf16(x),
+// lo = bf16(x - hi) (about 2^-17 relative, 4 bytes). Either way attention runs
+// on 16-bit MFMA operands.
+// Committed cache: per (sequence, layer, kv head) a run of Cs / kKvTile tiles
+// of 32 positions, 64 kvp hd values each:
+//   K plane pl: [hd / 8][slot][8] at offset pl * 32 hd, with position k of the
+//     tile at slot 16 ((k >> 2) & 1) + 4 (k >> 3) + (k & 3);
+//   V plane pl: [hd][32 positions] at offset 32 kvp hd + pl * 32 hd.
+// Explore entry of one (sequence, node slot, layer slot, kv head): 2 kvp hd
+//   values, the K planes then the V planes, each [hd].
+DEX_HD inline int kv_slot(int k) { return 16 * ((k >> 2) & 1) + 4 * (k >> 3) + (k & 3); }
+DEX_HD inline size_t kv_head_base(const ModelDims& D, int seq, int layer, int h) {
+  return (((size_t)seq * D.L + layer) * D.nkv + h) * (size_t)D.Cs * D.hd * 2 * D.kvp;
+}
+DEX_HD inline size_t kv_elem(int hd, int kvp, int pos, int kv, int plane, int d) {
+  const size_t tile = (size_t)(pos / kKvTile) * 64 * kvp * hd;
+  const int k = pos % kKvTile;
+  return kv == 0 ? tile + (size_t)plane * 32 * hd + (d >> 3) * 256 + kv_slot(k) * 8 + (d & 7)
+                 : tile + (size_t)(kvp + plane) * 32 * hd + (size_t)d * 32 + k;
+}
+DEX_HD inline size_t ex_base(const ModelDims& D, int seq, int phys, int lam, int h) {
+  return ((((size_t)seq * D.P + phys) * D.S + lam) * D.nkv + h) * 2 * D.kvp * (size_t)D.hd;
+}
+
 // Pruned lattice: whether heap node n (n1 = n + 1) is created when only nodes
 // of explorers below `cap` spawn position children (cap 0: every node). The
 // bits of n1 after its leading 1 are the node's path from the root (0 = depth

@@ -2,8 +2,9 @@
 // AddressSanitizer and UndefinedBehaviorSanitizer (tests/test_host_plan.py):
 // configuration checks, workspace carving, rows per round against a brute
 // enumeration of the heap level, per-sequence plans, attention items and block
-// lists, the HIP-graph key, the FSM over scripted commits and the prefill
-// chunks (every prompt position once, in order). Every buffer is
+// lists, the HIP-graph key, the FSM over scripted commits, the prefill
+// chunks (every prompt position once, in order) and the K/V tile layout that
+// the cache writers and the attention kernels share. Every buffer is
 // sized exactly as the library sizes its host buffers, so a write past one is
 // an ASan report. Prints "plan checks ok" and exits 0 when every check holds.
 //
@@ -225,7 +226,62 @@ static void check_workspace() {
     for (int r = 0; r < SC_N; ++r) CHECK(w.sstep[r] <= w.sbytes[r]);
     CHECK(w.sstep[SC_HEAD_PART] >= (size_t)(k.B << (k.N - 1)) * (V / 16) * 12);
     CHECK(w.head_part + w.sbytes[SC_HEAD_PART] <= w.total);
+    // the K/V addressing the kernels use stays inside the carved regions: the
+    // last (sequence, layer, kv head) run of committed tiles, and the last
+    // explore entry (16-bit elements)
+    ModelDims D{};
+    D.L = c.n_layers;
+    D.nkv = c.n_kv_heads;
+    D.hd = c.head_dim;
+    D.S = longest_stage(X.data(), k.N);
+    D.N = k.N;
+    D.P = (int)P;
+    D.B = k.B;
+    D.Cs = (int)Cs;
+    D.kvp = kv_planes(c.dtype);
+    CHECK(kv_head_base(D, k.B - 1, D.L - 1, D.nkv - 1) + (size_t)D.Cs * D.hd * 2 * D.kvp <= (w.exb - w.kvc) / 2);
+    CHECK(kv_head_base(D, 0, 0, 1) == (size_t)D.Cs * D.hd * 2 * D.kvp || D.nkv == 1);
+    CHECK(ex_base(D, k.B - 1, D.P - 1, D.S - 1, D.nkv - 1) + 2 * (size_t)D.kvp * D.hd <= (w.hidden - w.exb) / 2);
   }
+}
+
+// K/V tile layout: kv_elem (the writers: QKV epilogues, promotion) maps the
+// 64 kvp hd values of a 32-position tile one to one onto the tile, and the
+// attention kernels' own operand addressing reads the same element: K lane
+// (g, n) of MFMA row block t and 32-dim step s takes 16 bytes at
+// (4 s + g) 256 + (16 t + n) 8 (position 8 (n / 4) + 4 t + n % 4, dims
+// 8 (4 s + g) ..), V^T lane (g, n) of output block b takes 16 bytes at
+// 32 kvp hd + (16 b + n) 32 + 8 g (dim 16 b + n, positions 8 g ..); the lo
+// plane of a pair sits 32 hd further.
+static void check_kv_layout() {
+  for (int kvp : {1, 2})
+    for (int hd : {64, 128}) {
+      const size_t tile = (size_t)64 * kvp * hd;
+      std::vector<int> seen(tile, 0);
+      for (int pos = 0; pos < kKvTile; ++pos)
+        for (int kv = 0; kv < 2; ++kv)
+          for (int pl = 0; pl < kvp; ++pl)
+            for (int d = 0; d < hd; ++d) {
+              const size_t e = kv_elem(hd, kvp, pos, kv, pl, d);
+              CHECK(e < tile);
+              if (e < tile) ++seen[e];
+              CHECK(kv_elem(hd, kvp, pos + 3 * kKvTile, kv, pl, d) == e + 3 * tile);
+            }
+      for (size_t e = 0; e < tile; ++e) CHECK(seen[e] == 1);
+      for (int lane = 0; lane < 64; ++lane) {
+        const int g = lane >> 4, n = lane & 15;
+        for (int pl = 0; pl < kvp; ++pl)
+          for (int i = 0; i < 8; ++i) {
+            for (int t = 0; t < 2; ++t)
+              for (int st = 0; st < hd / 32; ++st)
+                CHECK((size_t)(4 * st + g) * 256 + (16 * t + n) * 8 + (size_t)pl * 32 * hd + i ==
+                      kv_elem(hd, kvp, 8 * (n >> 2) + 4 * t + (n & 3), 0, pl, 8 * (4 * st + g) + i));
+            for (int b = 0; b < hd / 16; ++b)
+              CHECK((size_t)32 * kvp * hd + (16 * b + n) * 32 + 8 * g + (size_t)pl * 32 * hd + i ==
+                    kv_elem(hd, kvp, 8 * g + i, 1, pl, 16 * b + n));
+          }
+      }
+    }
 }
 
 // --- one round's plan ------------------------------------------------------------
@@ -528,6 +584,7 @@ static void check_prefill(std::mt19937& rng) {
 int main() {
   check_validate();
   check_workspace();
+  check_kv_layout();
   std::mt19937 rng(11);
   for (int N = 1; N <= kMaxN; ++N)
     for (int rep : {1, 2, 4, 8})
