@@ -36,9 +36,10 @@ pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 # The target's margin gate and logit bound for bf16 weights, and a tighter
-# second gate for the decisions compared: three times the worst full-size
-# logit error of the fp16 K/V cache (6-7e-3 when the oracle itself rounds K/V
-# to fp16 on the 7B and 13B shapes).
+# second gate for the decisions compared: over three times the worst full-size
+# logit error of the path with its fp16 K/V cache (measured 4.1e-3 on the 7B
+# workloads, 4.0e-3 on 13B, 6.0e-3 on the GQA one; 6-7e-3 when the oracle
+# itself rounds K/V to fp16 on the 7B and 13B shapes).
 GATE, GATE2, TOL = 5e-2, 2e-2, 3e-2
 
 
