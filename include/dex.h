@@ -244,7 +244,8 @@ typedef struct {
   double ms;        /* summed GPU time between HIP events around the class's launches */
   int64_t launches; /* kernel launches timed */
   double bytes;     /* algorithmic HBM bytes of those launches (each weight matrix, KV entry,
-                       activation row read or written once) */
+                       activation row read or written once; KV values at their stored size,
+                       2 bytes for DEX_DTYPE_BF16 models, 4 for DEX_DTYPE_F32) */
   double flops;     /* algorithmic floating-point operations */
 } dex_kernel_stats;
 
