@@ -113,12 +113,14 @@ __device__ __forceinline__ void split_bf2(float a, float b, unsigned& hi, unsign
 
 // Two floats to packed fp16 (a in the low half), round-to-nearest-even, with
 // magnitudes above the largest finite fp16 (65504) saturated to it (NaN
-// passes through). Every float-to-fp16 rounding of the library goes through
-// here.
+// passes through). SAT = false leaves out the saturation where the values are
+// known to lie in range (softmax weights in [0, 1]), with the same results.
+// Every float-to-fp16 rounding of the library goes through here.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float sat_f16(float x) { return x > 65504.f ? 65504.f : (x < -65504.f ? -65504.f : x); }
+template <bool SAT = true>
 __device__ __forceinline__ unsigned f2h2(float a, float b) {
-  const f32x2_t f = {sat_f16(a), sat_f16(b)};
+  const f32x2_t f = SAT ? f32x2_t{sat_f16(a), sat_f16(b)} : f32x2_t{a, b};
   const f16x2_t v = __builtin_convertvector(f, f16x2_t);
   unsigned u;
   __builtin_memcpy(&u, &v, 4);
@@ -131,15 +133,16 @@ __device__ __forceinline__ float h2f(unsigned bits16) {
   return (float)h;
 }
 // The (hi, lo) fp16 pairs of two values, packed (a in the low halves).
+template <bool SAT = true>
 __device__ __forceinline__ void split_h2(float a, float b, unsigned& hi, unsigned& lo) {
-  hi = f2h2(a, b);
-  lo = f2h2(a - h2f(hi & 0xFFFFu), b - h2f(hi >> 16));
+  hi = f2h2<SAT>(a, b);
+  lo = f2h2<SAT>(a - h2f(hi & 0xFFFFu), b - h2f(hi >> 16));
 }
 // The (hi, lo) pair of two values in the 16-bit format of kvp planes: fp16
 // (kvp = 1) or bfloat16 (kvp = 2).
-template <int KVP>
+template <int KVP, bool SAT = true>
 __device__ __forceinline__ void split16(float a, float b, unsigned& hi, unsigned& lo) {
-  if constexpr (KVP == 1) split_h2(a, b, hi, lo);
+  if constexpr (KVP == 1) split_h2<SAT>(a, b, hi, lo);
   else split_bf2(a, b, hi, lo);
 }
 

@@ -87,13 +87,14 @@ __device__ __forceinline__ f32x4_t mma_kv(f32x4_t acc, const u32x4_t& ah, const 
   }
 }
 
-// Eight fp32 values as (hi, lo) pairs in the 16-bit format of KVP planes.
-template <int KVP>
+// Eight fp32 values as (hi, lo) pairs in the 16-bit format of KVP planes
+// (SAT as for f2h2).
+template <int KVP, bool SAT = true>
 __device__ __forceinline__ void split8(const float* x, u32x4_t& hi, u32x4_t& lo) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     unsigned h, l;
-    split16<KVP>(x[2 * i], x[2 * i + 1], h, l);
+    split16<KVP, SAT>(x[2 * i], x[2 * i + 1], h, l);
     hi[i] = h;
     lo[i] = l;
   }
@@ -160,7 +161,7 @@ __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, V
   m = mx;
   l = ls;
   u32x4_t ph, pl;
-  split8<KVP>(p, ph, pl);
+  split8<KVP, false>(p, ph, pl);   // softmax weights lie in [0, 1]
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     vsrc(b, vh[b], vl[b]);
