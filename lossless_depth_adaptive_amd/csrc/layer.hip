@@ -116,16 +116,25 @@ __device__ __forceinline__ void fold(float& M, float& L, float* A, float m, floa
   M = Mn;
 }
 
+// Bits 0 .. min(max(nv, 0), 8) - 1 set: the keys of a lane's eight that lie
+// below its unit's limit (nv = limit - first key of the eight).
+__device__ __forceinline__ unsigned key_bits(int nv) {
+  nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
+  return (1u << nv) - 1u;
+}
+
 // One 32-key chunk for the tile. qsrc(s, hi, lo): this lane's query operand
 // (unit n, dims 32s + 8g .. 32s + 8g + 7); ksrc(t, s, hi, lo): its K operand for
 // row block t (0, 1) and 32-dim step s; vsrc(b, hi, lo): its V^T operand for
 // output dims [16b, 16b + 16), as loaded; vpost(b, hi, lo) then fixes it up
 // (masks, gathered values). The lo operands are read only with KVP = 2.
-// valid8 bit i: key 8g + i counts for this lane's unit. Out: acc[b][r] = the
+// valid8 bit i: key 8g + i counts for this lane's unit; `full` (the same in
+// every lane): every key of the chunk counts for every unit of the tile, which
+// skips the selects (same values). Out: acc[b][r] = the
 // unit's unnormalised output at dim 16b + 4g + r, and the chunk's m and l
 // (m = -inf when no key counts).
 template <int HD, int KVP, typename QSrc, typename KSrc, typename VSrc, typename VPost>
-__device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, VPost vpost, unsigned valid8,
+__device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, VPost vpost, unsigned valid8, bool full,
                                               f32x4_t* acc, float& m, float& l) {
   constexpr int NS = HD / 32, NB = HD / 16;
   u32x4_t kh[2][NS], kl[2][NS], vh[NB], vl[NB];
@@ -141,18 +150,25 @@ __device__ __forceinline__ void chunk_partial(QSrc qsrc, KSrc ksrc, VSrc vsrc, V
       st[t] = mma_kv<KVP>(st[t], kh[t][s], kl[t][s], qh, ql);
     }
   }
-  float sv[8];
+  // The chunk's max and softmax weights, in a masked and an unmasked copy
+  // (a branch on `full`, not a select per key).
+  float p[8], mx;
+  auto weights = [&](auto masked) {
+    constexpr bool MASKED = decltype(masked)::value;
+    float sv[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) sv[i] = (valid8 >> i) & 1 ? st[i >> 2][i & 3] : -INFINITY;
-  float mx = sv[0];
+    for (int i = 0; i < 8; ++i) sv[i] = !MASKED || (valid8 >> i) & 1 ? st[i >> 2][i & 3] : -INFINITY;
+    mx = sv[0];
 #pragma unroll
-  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float msafe = mx == -INFINITY ? 0.f : mx;
-  float p[8];
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, sv[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float msafe = mx == -INFINITY ? 0.f : mx;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = (valid8 >> i) & 1 ? exp2_hw(sv[i] - msafe) : 0.f;
+    for (int i = 0; i < 8; ++i) p[i] = !MASKED || (valid8 >> i) & 1 ? exp2_hw(sv[i] - msafe) : 0.f;
+  };
+  if (full) weights(std::false_type{});
+  else weights(std::true_type{});
   float ls = p[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) ls += p[i];
@@ -383,12 +399,10 @@ __device__ void attn_unit_rows(AttnSmem<HD, 1>& sm, const AttnItem& it, int h, i
       bb = vl[b];
     };
     auto vpost = [&](int, u32x4_t&, u32x4_t&) {};
-    unsigned valid8 = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < limu ? 1u : 0u) << i;
+    const unsigned valid8 = key_bits(limu - (p0 + 8 * g));
     f32x4_t acc[NB];
     float m, l;
-    chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
+    chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, p0 + kKvTile <= limu, acc, m, l);
     if (n < rep)
       store_partial<HD>(mix + (((size_t)row * D.nq + h * rep + n) * kMixSlots + c - kAttnSC * (it.xc0 / kAttnSC)) * HP,
                         acc, m, l, g);
@@ -458,6 +472,14 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
   for (int t = 0; t < MAXT; ++t) vlim = max(vlim, lim[t]);
   for (int off = 32; off >= 1; off >>= 1) vlim = max(vlim, __shfl_xor(vlim, off));
   vlim = __builtin_amdgcn_readfirstlane(vlim);   // the same in every lane
+  // the smallest limit of each tile's units (the same in every lane)
+  int tmin[MAXT];
+#pragma unroll
+  for (int t = 0; t < MAXT; ++t) {
+    int v = n < units[t] ? lim[t] : 0x7fffffff;
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+    tmin[t] = __builtin_amdgcn_readfirstlane(v);
+  }
   __syncthreads();
 
   // Span state of fold thread fu's unit per tile (elements 4 fs + 64 q + e).
@@ -517,12 +539,10 @@ __device__ void attn_shared_chunks(AttnSmem<HD, MAXT>& sm, const AttnItem* __res
         bb = vl[b];
       };
       auto vpost = [&](int, u32x4_t&, u32x4_t&) {};
-      unsigned valid8 = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) valid8 |= (p0 + 8 * g + i < lim[t] ? 1u : 0u) << i;
+      const unsigned valid8 = key_bits(lim[t] - (p0 + 8 * g));
       f32x4_t acc[NB];
       float m, l;
-      chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, acc, m, l);
+      chunk_partial<HD, KVP>(qsrc, ksrc, vsrc, vpost, valid8, p0 + kKvTile <= tmin[t], acc, m, l);
       if (n < units[t] && p0 < lim[t]) {
         if (to_mix) {
           const int row = row0[t] + n / rep, qhd = h * rep + n % rep;
